@@ -1,0 +1,152 @@
+/*
+ * falcon.h -- C ABI of the MI355X (gfx950) implementation of Falcon
+ * fast-weight attention: the chunk-parallel forward pass and the single-token
+ * recurrent step.
+ *
+ * Sources, cited by page title and section:
+ *   [P1] zhouql-dev.github.io, "把状态更新写成一条学习规则：Falcon 家族重新对齐
+ *        fast-weight 记忆": sections 本质 (prefix alignment), Falcon家族 (the
+ *        family and the NLMS step), 三种等价形式 (recurrent / masked-parallel /
+ *        chunked forms, positive-decay renormalisation), Figures 3 and 4.
+ *   [P2] 59188saintaubert.com, "给记忆装一个“及时纠错”的开关：Falcon让循环模型
+ *        学会边写边改": sections 一个被忽略的时间差, 把记忆更新变成一次梯度下降,
+ *        六个变体, 正衰减钳制, 三种视角.
+ *
+ * What both entry points compute, per sequence (b, h) and step t = 1..T:
+ *   x_t   = phi(k_{t-1})                  prefix-aligned key ([P1] 本质); x_1 = x_prev
+ *   lam_t = max(exp(g_t), eps_gamma)      positive-decay clamp ([P2] 正衰减钳制)
+ *   eta_t = beta_t / (eps_eta + |x_t|^2)  NLMS step ([P1] Falcon家族; [P2] 梯度下降)
+ *   F1 : S_t = lam_t S_{t-1} + eta_t (v_t - S_{t-1} x_t) x_t^T
+ *   F2 : as F1 with eta_t a vector over value channels (rows of S)
+ *   F3 : S_t = lam_t S_{t-1} + (eta_t / Bw) sum_{j=t-Bw+1..t} (v_j - S_{t-1} x_j) x_j^T
+ *   F1A/F2A/F3A: the same with the additive write (v_j instead of the residual)
+ *   o_t   = S_t phi(q_t)                  read after write
+ *   phi(a) = a / sqrt(|a|^2 + eps_phi)
+ * The step definitions are [P1] Falcon家族 and [P2] 六个变体; the chunked
+ * evaluation is [P1] 三种等价形式 form C / Figure 4-C (per-chunk Gram and WY
+ * factors with a triangular solve) and [P2] 三种视角.
+ *
+ * Conventions shared by every entry point
+ *   Layout   all arrays are dense, C order, no strides:
+ *              q, k   [B, T, H, dk]   dtype (fp32 or bf16)
+ *              v, o   [B, T, H, dv]   dtype
+ *              beta   [B, T, H]  fp32, or [B, T, H, dv] for F2/F2A
+ *              log_lambda (g) [B, T, H] fp32; any value <= 0 incl. -inf
+ *              S      [B, H, dv, dk]  fp32, row i = value channel i
+ *              x_prev [B, H, dk]      fp32
+ *              win_x  [B, H, Bw-1, dk], win_v [B, H, Bw-1, dv] fp32, oldest first
+ *            The single-step entry point drops the T axis.
+ *   Memory   every pointer except `shape` and the state struct itself is a
+ *            device pointer (hipMalloc / torch CUDA tensor).  The caller owns
+ *            all memory; the library never allocates, frees, synchronises or
+ *            keeps a pointer after the call returns.  Device pointers must be
+ *            16-byte aligned.
+ *   Streams  work is enqueued on `stream` (a hipStream_t, NULL = the null
+ *            stream) and the call returns without waiting.  Buffers must stay
+ *            alive until the stream reaches the work.
+ *   Errors   the return value is a falcon_status_t.  Argument validation is
+ *            done on the host before any HIP call, so an invalid call never
+ *            touches the device.  A failed kernel launch returns
+ *            FALCON_ERR_HIP; a fault inside a kernel shows up at the caller's
+ *            next synchronisation.  NaN/Inf in the inputs are not checked;
+ *            lam > 1 is outside the contract.
+ *   Threads  no global mutable state: calls may be made from several threads.
+ */
+#ifndef FALCON_H
+#define FALCON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FALCON_ABI_VERSION 1
+
+typedef enum {
+  FALCON_1 = 1,   /* scalar NLMS step, residual write            */
+  FALCON_1A = 2,  /* scalar step, additive (inner-product) write  */
+  FALCON_2 = 3,   /* per-value-channel step, residual write       */
+  FALCON_2A = 4,  /* per-value-channel step, additive write       */
+  FALCON_3 = 5,   /* window of Bw pairs, averaged residuals       */
+  FALCON_3A = 6   /* window of Bw pairs, averaged additive write  */
+} falcon_variant_t;
+
+typedef enum { FALCON_F32 = 0, FALCON_BF16 = 1 } falcon_dtype_t;  /* of q, k, v, o */
+
+typedef enum {
+  FALCON_OK = 0,
+  FALCON_ERR_INVALID_ARG = 1,  /* null pointer, bad enum, non-positive size, ... */
+  FALCON_ERR_UNSUPPORTED = 2,  /* valid but not built: head dim, chunk, window, dtype */
+  FALCON_ERR_WORKSPACE = 3,    /* workspace smaller than falcon_chunk_fwd_workspace() */
+  FALCON_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} falcon_status_t;
+
+typedef struct {
+  int32_t variant;   /* falcon_variant_t */
+  int32_t dtype;     /* falcon_dtype_t   */
+  int32_t batch;     /* B >= 1 */
+  int32_t seqlen;    /* T >= 1 (ignored by falcon_recurrent_step) */
+  int32_t heads;     /* H >= 1 */
+  int32_t dk;        /* key/query head dim: 32, 64 or 128 */
+  int32_t dv;        /* value head dim:     32, 64 or 128 (fp32: 32 or 64) */
+  int32_t chunk;     /* chunk length C: 16, 32 or 64; T need not be a multiple */
+  int32_t window;    /* Bw: 1..8 for F3/F3A (Bw divides 64), must be 1 otherwise */
+  float eps_gamma;   /* decay floor, in (0, 1]; the pages' workloads use 1e-3 */
+  float eps_phi;     /* feature-map epsilon, >= 0 (1e-6) */
+  float eps_eta;     /* NLMS epsilon, >= 0 (1e-6) */
+} falcon_shape_t;
+
+typedef struct {
+  float *S;       /* [B, H, dv, dk]; required                                 */
+  float *x_prev;  /* [B, H, dk] = phi(k) of the last consumed token; required  */
+  float *win_x;   /* [B, H, Bw-1, dk], F3/F3A with Bw > 1 only, else ignored  */
+  float *win_v;   /* [B, H, Bw-1, dv]                                         */
+} falcon_state_t;
+
+/* ABI version of the loaded library (FALCON_ABI_VERSION). */
+int falcon_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *falcon_status_string(int status);
+
+/* Bytes of device workspace falcon_chunk_fwd needs for this shape (0 when it
+ * needs none).  Returns 0 for an invalid shape as well; validation is the
+ * forward call's job. */
+size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape);
+
+/* Chunked forward pass over T tokens ([P1] 三种等价形式 form C, Figure 4-C;
+ * [P2] 三种视角).
+ *   init         NULL: fresh sequences (S = 0, x_prev = 0, zero window).
+ *                Otherwise S and x_prev (and the window for F3/F3A, Bw > 1)
+ *                are read.  May alias final_state (in-place continuation).
+ *   final_state  NULL: not written.  Otherwise receives S_T, x_prev =
+ *                phi(k_T) and the last Bw-1 pairs.
+ *   o            [B, T, H, dv] in dtype; must not alias any input.
+ *   chunk_states NULL, or [B, H, ceil(T/C), dv, dk] fp32: S at the end of
+ *                every chunk (the last one equals S_T).
+ *   workspace    may be NULL when falcon_chunk_fwd_workspace() is 0.
+ * Results are deterministic: the same inputs give bit-identical outputs. */
+int falcon_chunk_fwd(const falcon_shape_t *shape,
+                     const void *q, const void *k, const void *v,
+                     const float *beta, const float *log_lambda,
+                     const falcon_state_t *init, falcon_state_t *final_state,
+                     void *o, float *chunk_states,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* One token of the recurrent form ([P1] 三种等价形式 form A; [P2] 三种视角):
+ * reads q, k [B, H, dk], v [B, H, dv], beta [B, H] (F2/F2A: [B, H, dv]) and
+ * log_lambda [B, H]; updates `state` in place (S, x_prev and, for F3/F3A with
+ * Bw > 1, the window) and writes o [B, H, dv] in dtype.  shape->seqlen and
+ * shape->chunk are ignored. */
+int falcon_recurrent_step(const falcon_shape_t *shape,
+                          const void *q, const void *k, const void *v,
+                          const float *beta, const float *log_lambda,
+                          falcon_state_t *state, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FALCON_H */

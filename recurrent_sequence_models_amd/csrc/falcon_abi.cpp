@@ -1,0 +1,186 @@
+// C ABI of the Falcon fast-weight attention library (declared in include/falcon.h).
+//
+// Host side only: every argument is validated here before the first HIP call,
+// so an invalid call returns a status without touching the device.  The
+// kernels live in falcon_fwd.hip, falcon_fwd3.hip and falcon_step.hip.
+#include "falcon.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "falcon_kernels.h"
+
+namespace {
+
+using falcon::FwdArgs;
+using falcon::StepArgs;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool windowed(int v) { return v == FALCON_3 || v == FALCON_3A; }
+bool per_channel(int v) { return v == FALCON_2 || v == FALCON_2A; }
+bool finite(float x) { return std::isfinite(x); }
+
+// Shape checks shared by both entry points.  `step` skips seqlen/chunk.
+int check_shape(const falcon_shape_t *s, bool step) {
+  if (!s) return FALCON_ERR_INVALID_ARG;
+  if (s->variant < FALCON_1 || s->variant > FALCON_3A) return FALCON_ERR_INVALID_ARG;
+  if (s->dtype != FALCON_F32 && s->dtype != FALCON_BF16) return FALCON_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->heads < 1 || s->dk < 1 || s->dv < 1) return FALCON_ERR_INVALID_ARG;
+  if (!step && (s->seqlen < 1 || s->chunk < 1)) return FALCON_ERR_INVALID_ARG;
+  if (!finite(s->eps_gamma) || !finite(s->eps_phi) || !finite(s->eps_eta)) return FALCON_ERR_INVALID_ARG;
+  if (!(s->eps_gamma > 0.f && s->eps_gamma <= 1.f)) return FALCON_ERR_INVALID_ARG;
+  if (s->eps_phi < 0.f || !(s->eps_eta > 0.f)) return FALCON_ERR_INVALID_ARG;
+  if (s->window < 1) return FALCON_ERR_INVALID_ARG;
+  if (!windowed(s->variant) && s->window != 1) return FALCON_ERR_INVALID_ARG;
+  if (windowed(s->variant) && s->window > 8) return FALCON_ERR_UNSUPPORTED;
+  if (s->dk != s->dv) return FALCON_ERR_UNSUPPORTED;
+  if (s->dk != 32 && s->dk != 64 && s->dk != 128) return FALCON_ERR_UNSUPPORTED;
+  if (!step) {
+    if (s->chunk != 16 && s->chunk != 32 && s->chunk != 64) return FALCON_ERR_UNSUPPORTED;
+    if (s->dtype == FALCON_F32 && s->dk > 64) return FALCON_ERR_UNSUPPORTED;
+    if (windowed(s->variant) && 64 % s->window != 0) return FALCON_ERR_UNSUPPORTED;
+    if ((int64_t)s->batch * s->seqlen > INT32_MAX) return FALCON_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)s->batch * s->heads > INT32_MAX / 2) return FALCON_ERR_UNSUPPORTED;
+  return FALCON_OK;
+}
+
+int check_state(const falcon_state_t *st, const falcon_shape_t *s) {
+  if (!st->S || !st->x_prev) return FALCON_ERR_INVALID_ARG;
+  if (!aligned16(st->S) || !aligned16(st->x_prev)) return FALCON_ERR_INVALID_ARG;
+  if (windowed(s->variant) && s->window > 1) {
+    if (!st->win_x || !st->win_v) return FALCON_ERR_INVALID_ARG;
+    if (!aligned16(st->win_x) || !aligned16(st->win_v)) return FALCON_ERR_INVALID_ARG;
+  }
+  return FALCON_OK;
+}
+
+int check_io(const void *q, const void *k, const void *v, const float *beta, const float *g, const void *o) {
+  if (!q || !k || !v || !beta || !g || !o) return FALCON_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(beta))
+    return FALCON_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(g) & 3u) != 0) return FALCON_ERR_INVALID_ARG;
+  return FALCON_OK;
+}
+
+}  // namespace
+
+namespace falcon {
+hipError_t launch_chunk_fwd_rows(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
+                                 const FwdArgs &a, hipStream_t s);
+hipError_t launch_chunk_fwd_window(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
+                                   const FwdArgs &a, hipStream_t s);
+
+int choose_nsplit(int variant, bool bf16, int dk, int dv, int chunk, int batch_heads) {
+  (void)bf16; (void)chunk; (void)dk;
+  int n = 1;
+  // F2 keeps per-channel steps in LDS: at 128 channels a workgroup takes 64 of them.
+  if (per_channel(variant) && dv == 128) n = 2;
+  // Few sequences: split the value channels over more workgroups (rows of S are
+  // independent given the keys), so more compute units take part.
+  while (batch_heads * n < 128 && dv / (2 * n) >= 16 && n < 8) n *= 2;
+  return n;
+}
+
+hipError_t launch_chunk_fwd(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
+                            const FwdArgs &a, hipStream_t s) {
+  if (windowed(variant)) return launch_chunk_fwd_window(variant, bf16, dk, dv, chunk, nsplit, a, s);
+  return launch_chunk_fwd_rows(variant, bf16, dk, dv, chunk, nsplit, a, s);
+}
+}  // namespace falcon
+
+extern "C" {
+
+int falcon_abi_version(void) { return FALCON_ABI_VERSION; }
+
+const char *falcon_status_string(int status) {
+  switch (status) {
+    case FALCON_OK: return "FALCON_OK";
+    case FALCON_ERR_INVALID_ARG: return "FALCON_ERR_INVALID_ARG: invalid argument";
+    case FALCON_ERR_UNSUPPORTED: return "FALCON_ERR_UNSUPPORTED: valid but unsupported shape or option";
+    case FALCON_ERR_WORKSPACE: return "FALCON_ERR_WORKSPACE: workspace too small";
+    case FALCON_ERR_HIP: return "FALCON_ERR_HIP: HIP launch or runtime error";
+  }
+  return "unknown falcon status";
+}
+
+size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape) {
+  (void)shape;
+  return 0;  // the fused kernels keep all intermediates on chip
+}
+
+int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, const void *v,
+                     const float *beta, const float *log_lambda, const falcon_state_t *init,
+                     falcon_state_t *final_state, void *o, float *chunk_states, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  int st = check_shape(s, false);
+  if (st != FALCON_OK) return st;
+  if ((st = check_io(q, k, v, beta, log_lambda, o)) != FALCON_OK) return st;
+  if (init && (st = check_state(init, s)) != FALCON_OK) return st;
+  if (final_state && (st = check_state(final_state, s)) != FALCON_OK) return st;
+  if (chunk_states && !aligned16(chunk_states)) return FALCON_ERR_INVALID_ARG;
+  if (windowed(s->variant)) return FALCON_ERR_UNSUPPORTED;  // chunked Falcon-3 not built yet
+  if (workspace_bytes < falcon_chunk_fwd_workspace(s)) return FALCON_ERR_WORKSPACE;
+  (void)workspace;
+
+  const bool bf16 = s->dtype == FALCON_BF16;
+  const bool win = windowed(s->variant) && s->window > 1;
+  const int nsplit = falcon::choose_nsplit(s->variant, bf16, s->dk, s->dv, s->chunk, s->batch * s->heads);
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = log_lambda;
+  a.S0 = init ? init->S : nullptr;
+  a.xprev0 = init ? init->x_prev : nullptr;
+  a.winx0 = (init && win) ? init->win_x : nullptr;
+  a.winv0 = (init && win) ? init->win_v : nullptr;
+  a.S_out = final_state ? final_state->S : nullptr;
+  a.xprev_out = final_state ? final_state->x_prev : nullptr;
+  a.winx_out = (final_state && win) ? final_state->win_x : nullptr;
+  a.winv_out = (final_state && win) ? final_state->win_v : nullptr;
+  a.o = o;
+  a.chunk_states = chunk_states;
+  a.B = s->batch; a.T = s->seqlen; a.H = s->heads;
+  a.nchunks = (s->seqlen + s->chunk - 1) / s->chunk;
+  a.window = windowed(s->variant) ? s->window : 1;
+  a.log_eps_gamma = std::log(s->eps_gamma);
+  a.eps_phi = s->eps_phi;
+  a.eps_eta = s->eps_eta;
+  // The main kernel writes x_prev itself only when one workgroup owns the whole
+  // sequence (then it has read the incoming x_prev before, even when aliased).
+  a.write_tail = (final_state && nsplit == 1 && !win) ? 1 : 0;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (falcon::launch_chunk_fwd(s->variant, bf16, s->dk, s->dv, s->chunk, nsplit, a, hs) != hipSuccess)
+    return FALCON_ERR_HIP;
+  if (final_state && !a.write_tail) {
+    if (falcon::launch_tail(s->variant, bf16, s->dk, s->dv, a, hs) != hipSuccess) return FALCON_ERR_HIP;
+  }
+  return FALCON_OK;
+}
+
+int falcon_recurrent_step(const falcon_shape_t *s, const void *q, const void *k, const void *v,
+                          const float *beta, const float *log_lambda, falcon_state_t *state, void *o,
+                          void *stream) {
+  int st = check_shape(s, true);
+  if (st != FALCON_OK) return st;
+  if ((st = check_io(q, k, v, beta, log_lambda, o)) != FALCON_OK) return st;
+  if (!state) return FALCON_ERR_INVALID_ARG;
+  if ((st = check_state(state, s)) != FALCON_OK) return st;
+  const bool win = windowed(s->variant) && s->window > 1;
+  StepArgs a{};
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = log_lambda;
+  a.S = state->S; a.xprev = state->x_prev;
+  a.winx = win ? state->win_x : nullptr;
+  a.winv = win ? state->win_v : nullptr;
+  a.o = o;
+  a.B = s->batch; a.H = s->heads;
+  a.window = windowed(s->variant) ? s->window : 1;
+  a.log_eps_gamma = std::log(s->eps_gamma);
+  a.eps_phi = s->eps_phi;
+  a.eps_eta = s->eps_eta;
+  if (falcon::launch_step(s->variant, s->dtype == FALCON_BF16, s->dk, s->dv, a,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FALCON_ERR_HIP;
+  return FALCON_OK;
+}
+
+}  // extern "C"

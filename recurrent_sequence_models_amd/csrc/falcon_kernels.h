@@ -1,0 +1,48 @@
+// Internal launch interface between the C ABI (falcon_abi.cpp) and the HIP
+// kernels.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace falcon {
+
+// Everything a forward launch needs, already validated by the host.
+struct FwdArgs {
+  const void *q, *k, *v;         // [B,T,H,dk|dv] in the input dtype
+  const float *beta;             // [B,T,H] or [B,T,H,dv]
+  const float *g;                // [B,T,H] log-decay (unclamped)
+  const float *S0;               // [B,H,dv,dk] or null (zeros)
+  const float *xprev0;           // [B,H,dk] or null (zeros)
+  const float *winx0, *winv0;    // [B,H,Bw-1,dk|dv] or null (zeros)
+  float *S_out;                  // [B,H,dv,dk] or null
+  float *xprev_out;              // [B,H,dk] or null (written by the kernel only when write_tail)
+  float *winx_out, *winv_out;    // [B,H,Bw-1,dk|dv] or null
+  void *o;                       // [B,T,H,dv]
+  float *chunk_states;           // [B,H,NC,dv,dk] or null
+  int B, T, H, nchunks, window;
+  float log_eps_gamma, eps_phi, eps_eta;
+  int write_tail;                // 1: the main kernel writes x_prev / window itself
+};
+
+struct StepArgs {
+  const void *q, *k, *v;
+  const float *beta, *g;
+  float *S, *xprev, *winx, *winv;
+  void *o;
+  int B, H, window;
+  float log_eps_gamma, eps_phi, eps_eta;
+};
+
+// Return hipSuccess or the launch error.  `variant` is falcon_variant_t,
+// `bf16` selects the input dtype.  Unsupported combinations return
+// hipErrorInvalidValue (the host validates first, so this is a safety net).
+hipError_t launch_chunk_fwd(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
+                            const FwdArgs &a, hipStream_t stream);
+hipError_t launch_tail(int variant, bool bf16, int dk, int dv, const FwdArgs &a, hipStream_t stream);
+hipError_t launch_step(int variant, bool bf16, int dk, int dv, const StepArgs &a, hipStream_t stream);
+
+// The per-shape d_v split of the forward kernel (channels per workgroup = dv / nsplit).
+int choose_nsplit(int variant, bool bf16, int dk, int dv, int chunk, int batch_heads);
+
+}  // namespace falcon

@@ -1,0 +1,255 @@
+// Single-token recurrent step of Falcon fast-weight attention on gfx950
+// (recurrent form: [P1] 三种等价形式 form A; [P2] 三种视角), and the small
+// kernel that writes the carried key / window of a chunked call.
+// ([P1] = zhouql-dev.github.io "把状态更新写成一条学习规则：Falcon 家族重新对齐
+// fast-weight 记忆"; [P2] = 59188saintaubert.com "给记忆装一个“及时纠错”的开关：
+// Falcon让循环模型学会边写边改".)
+//
+// The step is row-local: for value channel i, with x = x_prev (= phi(k_{t-1})),
+// q^ = phi(q_t), lam = max(e^g, eps_gamma), eta = beta / (eps_eta + |x|^2) and the
+// window pairs (x_j, v_j) (just (x, v_t) unless Falcon-3):
+//   e_ij  = v_j[i] - s_i . x_j           (regression family; v_j[i] for the A variants)
+//   s_i  <- lam s_i + (eta_i / Bw) sum_j e_ij x_j
+//   o_i   = lam (s_i . q^) + (eta_i / Bw) sum_j e_ij (x_j . q^)    (= s_i_new . q^)
+// so each row of S is read once and written once, in place: the kernel is a
+// single HBM stream over the state.
+#include "falcon_kernels.h"
+#include "mfma_frag.h"
+
+namespace falcon {
+
+namespace {
+
+enum { V_F1 = 1, V_F1A = 2, V_F2 = 3, V_F2A = 4, V_F3 = 5, V_F3A = 6 };
+constexpr int MAXW = 8;
+
+__device__ __forceinline__ float ld1(const __bf16 *p) { return (float)*p; }
+__device__ __forceinline__ float ld1(const float *p) { return *p; }
+__device__ __forceinline__ void st1(__bf16 *p, float x) { *p = (__bf16)x; }
+__device__ __forceinline__ void st1(float *p, float x) { *p = x; }
+
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {  // sum over the LPR lanes of one row
+#pragma unroll
+  for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ float dot4(const f4 &a, const f4 &b) {
+  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+}
+
+template <int VAR, typename IT, int DK, int DV>
+__global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
+  constexpr int LPR = DK / 4;          // lanes per row of S (float4 per lane)
+  constexpr int RPW = 64 / LPR;        // rows per wave pass
+  constexpr bool PERCH = (VAR == V_F2 || VAR == V_F2A);
+  constexpr bool WIN = (VAR == V_F3 || VAR == V_F3A);
+  constexpr bool DELTA = (VAR == V_F1 || VAR == V_F2 || VAR == V_F3);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int part = lane % LPR, rsub = lane / LPR;
+  const int bh = blockIdx.x;
+  const int BW = WIN ? a.window : 1;
+  const IT *qp = static_cast<const IT *>(a.q);
+  const IT *kp = static_cast<const IT *>(a.k);
+  const IT *vp = static_cast<const IT *>(a.v);
+  IT *op = static_cast<IT *>(a.o);
+
+  // per-sequence scalars, computed redundantly by every row group
+  f4 x = *reinterpret_cast<const f4 *>(a.xprev + (size_t)bh * DK + 4 * part);
+  f4 qv, kv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    qv[e] = ld1(qp + (size_t)bh * DK + 4 * part + e);
+    kv[e] = ld1(kp + (size_t)bh * DK + 4 * part + e);
+  }
+  const float qn = row_sum<LPR>(dot4(qv, qv));
+  const f4 qh = qv * (qn + a.eps_phi > 0.f ? rsqrtf(qn + a.eps_phi) : 0.f);
+  const float xn2 = row_sum<LPR>(dot4(x, x));
+  const float xq = row_sum<LPR>(dot4(x, qh));
+  const float lam = __expf(fmaxf(a.g[bh], a.log_eps_gamma));
+  const float etas = PERCH ? 0.f : a.beta[bh] / (a.eps_eta + xn2);
+  const float inv_e = 1.f / (a.eps_eta + xn2);
+
+  f4 wx[MAXW - 1];
+  float wxq[MAXW - 1];
+  if (WIN) {
+#pragma unroll
+    for (int j = 0; j < MAXW - 1; ++j) {
+      if (j < BW - 1) {
+        wx[j] = *reinterpret_cast<const f4 *>(a.winx + ((size_t)bh * (BW - 1) + j) * DK + 4 * part);
+        wxq[j] = row_sum<LPR>(dot4(wx[j], qh));
+      } else {
+        wx[j] = zero4();
+        wxq[j] = 0.f;
+      }
+    }
+  }
+
+  for (int row0 = 0; row0 < DV; row0 += 4 * RPW) {
+    const int row = row0 + wv * RPW + rsub;
+    const bool ok = row < DV;  // uniform per row group
+    f4 s = ok ? *reinterpret_cast<const f4 *>(a.S + ((size_t)bh * DV + row) * DK + 4 * part) : zero4();
+    const float vi = ok ? ld1(vp + (size_t)bh * DV + row) : 0.f;
+    const float eta = PERCH ? (ok ? a.beta[(size_t)bh * DV + row] * inv_e : 0.f) : etas;
+    const float sq = row_sum<LPR>(dot4(s, qh));
+    float o;
+    f4 snew = s * lam;
+    if (!WIN) {
+      const float e = DELTA ? vi - row_sum<LPR>(dot4(s, x)) : vi;
+      snew += x * (eta * e);
+      o = lam * sq + eta * e * xq;
+    } else {
+      const float w = eta / (float)BW;
+      float acc_o = 0.f;
+#pragma unroll
+      for (int j = 0; j < MAXW - 1; ++j) {
+        if (j < BW - 1) {
+          const float vj = ok ? a.winv[((size_t)bh * (BW - 1) + j) * DV + row] : 0.f;
+          const float e = DELTA ? vj - row_sum<LPR>(dot4(s, wx[j])) : vj;
+          snew += wx[j] * (w * e);
+          acc_o += e * wxq[j];
+        }
+      }
+      const float e = DELTA ? vi - row_sum<LPR>(dot4(s, x)) : vi;
+      snew += x * (w * e);
+      acc_o += e * xq;
+      o = lam * sq + w * acc_o;
+    }
+    if (ok) {
+      *reinterpret_cast<f4 *>(a.S + ((size_t)bh * DV + row) * DK + 4 * part) = snew;
+      if (part == 0) st1(op + (size_t)bh * DV + row, o);
+    }
+  }
+
+  // every lane has read x_prev and the window; now they may be replaced
+  __syncthreads();
+  if (wv == 0 && rsub == 0) {
+    const float kn = row_sum<LPR>(dot4(kv, kv));
+    const f4 xn = kv * (kn + a.eps_phi > 0.f ? rsqrtf(kn + a.eps_phi) : 0.f);
+    if (WIN && BW > 1) {
+      // shift the window: drop the oldest pair, append (x, v)
+#pragma unroll
+      for (int j = 0; j < MAXW - 2; ++j)
+        if (j < BW - 2) *reinterpret_cast<f4 *>(a.winx + ((size_t)bh * (BW - 1) + j) * DK + 4 * part) = wx[j + 1];
+      *reinterpret_cast<f4 *>(a.winx + ((size_t)bh * (BW - 1) + BW - 2) * DK + 4 * part) = x;
+    }
+    *reinterpret_cast<f4 *>(a.xprev + (size_t)bh * DK + 4 * part) = xn;
+  }
+  if (WIN && BW > 1) {
+    // value window: each thread moves whole columns (oldest first, so no overwrite before read)
+    for (int row = tid; row < DV; row += 256) {
+      float* wvp = a.winv + (size_t)bh * (BW - 1) * DV + row;
+      for (int j = 0; j + 1 < BW - 1; ++j) wvp[(size_t)j * DV] = wvp[(size_t)(j + 1) * DV];
+      wvp[(size_t)(BW - 2) * DV] = ld1(vp + (size_t)bh * DV + row);
+    }
+  }
+}
+
+// x_prev = phi(k_{T-1}) and, for a window, the last Bw-1 pairs (x_s, v_s),
+// s = T-Bw+1..T-1, where x_s = phi(k_{s-1}) for s >= 1, x_0 = the incoming x_prev
+// and s < 0 are pairs of the incoming window.  One workgroup per sequence;
+// every old value it needs is read before anything is written, so the
+// outputs may alias the incoming state.
+template <typename IT, int DK, int DV>
+__global__ __launch_bounds__(256) void tail_kernel(FwdArgs a) {
+  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x;
+  const int T = a.T, H = a.H, BW = a.window;
+  const IT *kp = static_cast<const IT *>(a.k);
+  const IT *vp = static_cast<const IT *>(a.v);
+  __shared__ float sx[MAXW][DK];   // new window keys, then x_prev
+  __shared__ float sv[MAXW][DV];
+  __shared__ float snorm[MAXW];
+  // slot j = 0..BW-2 is pair s = T - BW + 1 + j; slot BW-1 is phi(k_{T-1})
+  for (int j = 0; j < BW; ++j) {
+    const int s = T - BW + 1 + j;     // pair index (slot BW-1 reuses the formula with s = T)
+    for (int e = tid; e < DK; e += 256) {
+      float x;
+      if (s >= 1) x = ld1(kp + ((size_t)(b * T + s - 1) * H + h) * DK + e);
+      else if (s == 0) x = a.xprev0 ? a.xprev0[(size_t)bh * DK + e] : 0.f;
+      else x = a.winx0 ? a.winx0[((size_t)bh * (BW - 1) + (BW - 1 + s)) * DK + e] : 0.f;
+      sx[j][e] = x;
+    }
+    if (j < BW - 1) {
+      for (int e = tid; e < DV; e += 256) {
+        float v;
+        if (s >= 0) v = ld1(vp + ((size_t)(b * T + s) * H + h) * DV + e);
+        else v = a.winv0 ? a.winv0[((size_t)bh * (BW - 1) + (BW - 1 + s)) * DV + e] : 0.f;
+        sv[j][e] = v;
+      }
+    }
+  }
+  __syncthreads();
+  for (int j = tid >> 6; j < BW; j += 4) {   // wave w normalises slots w, w+4 when they came from a key
+    const int lane = tid & 63;
+    const int s = T - BW + 1 + j;
+    float ss = 0.f;
+    for (int e = lane; e < DK; e += 64) ss += sx[j][e] * sx[j][e];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if (lane == 0) snorm[j] = (s >= 1) ? (ss + a.eps_phi > 0.f ? rsqrtf(ss + a.eps_phi) : 0.f) : 1.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < DK; e += 256) a.xprev_out[(size_t)bh * DK + e] = sx[BW - 1][e] * snorm[BW - 1];
+  if (BW > 1 && a.winx_out) {
+    for (int j = 0; j < BW - 1; ++j) {
+      for (int e = tid; e < DK; e += 256)
+        a.winx_out[((size_t)bh * (BW - 1) + j) * DK + e] = sx[j][e] * snorm[j];
+      for (int e = tid; e < DV; e += 256) a.winv_out[((size_t)bh * (BW - 1) + j) * DV + e] = sv[j][e];
+    }
+  }
+}
+
+template <int VAR, typename IT>
+hipError_t step_dims(int dk, int dv, const StepArgs &a, hipStream_t s) {
+  const int nblk = a.B * a.H;
+#define FALCON_STEP(DK_, DV_)                                                                  \
+  if (dk == DK_ && dv == DV_) {                                                                \
+    hipLaunchKernelGGL((step_kernel<VAR, IT, DK_, DV_>), dim3(nblk), dim3(256), 0, s, a);      \
+    return hipGetLastError();                                                                  \
+  }
+  FALCON_STEP(32, 32)
+  FALCON_STEP(64, 64)
+  FALCON_STEP(128, 128)
+#undef FALCON_STEP
+  return hipErrorInvalidValue;
+}
+
+template <typename IT>
+hipError_t tail_dims(int dk, int dv, const FwdArgs &a, hipStream_t s) {
+  const int nblk = a.B * a.H;
+#define FALCON_TAIL(DK_, DV_)                                                             \
+  if (dk == DK_ && dv == DV_) {                                                           \
+    hipLaunchKernelGGL((tail_kernel<IT, DK_, DV_>), dim3(nblk), dim3(256), 0, s, a);      \
+    return hipGetLastError();                                                             \
+  }
+  FALCON_TAIL(32, 32)
+  FALCON_TAIL(64, 64)
+  FALCON_TAIL(128, 128)
+#undef FALCON_TAIL
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_step(int variant, bool bf16, int dk, int dv, const StepArgs &a, hipStream_t s) {
+#define FALCON_V(VV) return bf16 ? step_dims<VV, __bf16>(dk, dv, a, s) : step_dims<VV, float>(dk, dv, a, s)
+  switch (variant) {
+    case V_F1: FALCON_V(V_F1);
+    case V_F1A: FALCON_V(V_F1A);
+    case V_F2: FALCON_V(V_F2);
+    case V_F2A: FALCON_V(V_F2A);
+    case V_F3: FALCON_V(V_F3);
+    case V_F3A: FALCON_V(V_F3A);
+  }
+#undef FALCON_V
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_tail(int variant, bool bf16, int dk, int dv, const FwdArgs &a, hipStream_t s) {
+  (void)variant;
+  return bf16 ? tail_dims<__bf16>(dk, dv, a, s) : tail_dims<float>(dk, dv, a, s);
+}
+
+}  // namespace falcon

@@ -1,0 +1,75 @@
+// 16x16 MFMA fragments for gfx950 (CDNA4, wave64).
+//
+// Every 16x16 tile lives in one uniform per-lane layout of 4 values, with
+// lane l = 16*g + c (g = l / 16 in 0..3, c = l % 16):
+//
+//   C-layout of M : lane holds M[4g + i][c],  i = 0..3     (accumulators, B operand)
+//   A-layout of M : lane holds M[c][4g + i]                (= C-layout of M^T)
+//
+// mma16(D, a, b) adds A(16x16) * B(16x16) to D, with A given in A-layout and B
+// in C-layout.  Because the result D comes out in C-layout, which is exactly
+// the B-operand layout, a product can feed the next product without a trip
+// through LDS; and the C-layout of M^T is the A-layout of M.
+//
+//  * bf16: one v_mfma_f32_16x16x16_bf16 (k-slots 4g..4g+3 of the lane).
+//  * fp32: four v_mfma_f32_16x16x4_f32, instruction i taking k = 4g + i.
+// mma32 sums two k-blocks of 16.  For bf16 it is one v_mfma_f32_16x16x32_bf16
+// whose 8 k-slots per lane are filled with the lane's 4 k of each block; the
+// assignment of actual k to slots only has to be the same for A and B, which
+// it is by construction.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace falcon {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct Op;
+template <> struct Op<float> { typedef f4 frag; };
+template <> struct Op<__bf16> { typedef bf4 frag; };
+
+__device__ __forceinline__ bf4 to_op(const f4 &x, __bf16) {
+  bf4 r;
+  r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
+  return r;
+}
+__device__ __forceinline__ f4 to_op(const f4 &x, float) { return x; }
+
+template <typename OpT>
+__device__ __forceinline__ typename Op<OpT>::frag cvt(const f4 &x) { return to_op(x, OpT()); }
+
+__device__ __forceinline__ void mma16(f4 &d, const bf4 &a, const bf4 &b) {
+  d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), d, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f4 &d, const f4 &a, const f4 &b) {
+  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], d, 0, 0, 0);
+  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], d, 0, 0, 0);
+  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], d, 0, 0, 0);
+  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], d, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f4 &d, const bf4 &a0, const bf4 &a1, const bf4 &b0, const bf4 &b1) {
+  bf8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  bf8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, d, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f4 &d, const f4 &a0, const f4 &a1, const f4 &b0, const f4 &b1) {
+  mma16(d, a0, b0);
+  mma16(d, a1, b1);
+}
+
+// Four consecutive operands from LDS (8-byte aligned for bf16, 16 for fp32).
+__device__ __forceinline__ bf4 ld4(const __bf16 *p) { return *reinterpret_cast<const bf4 *>(p); }
+__device__ __forceinline__ f4 ld4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+
+// A-layout fragment of the 16x16 block at (r0, c0) of a row-major LDS matrix.
+template <typename OpT>
+__device__ __forceinline__ typename Op<OpT>::frag lda(const OpT *m, int ld, int r0, int c0, int lane) {
+  return ld4(m + (r0 + (lane & 15)) * ld + c0 + 4 * (lane >> 4));
+}
+
+__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace falcon

@@ -1,0 +1,138 @@
+"""CPU tests of the C ABI: the library loads, exports what include/falcon.h
+declares, and rejects invalid calls on the host before any HIP call.
+
+No kernel is launched here.  Every call below is invalid by construction;
+pointer arguments that are never dereferenced use a fake aligned address, so
+the tests are skipped on a machine that has a GPU (a validation bug must never
+be able to launch a kernel on a fake pointer)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from recurrent_sequence_models_amd import falcon as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "falcon.h")
+FAKE = ctypes.c_void_p(0x10000)    # aligned, never dereferenced
+
+
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+cpu_only = pytest.mark.skipif(not _no_gpu(), reason="invalid-call tests run only where no GPU is visible")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(falcon_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    L = F.lib()
+    names = declared_functions()
+    assert set(names) == set(F.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    L = F.lib()
+    assert L.falcon_abi_version() == 1
+    for code in range(5):
+        s = F.status_string(code)
+        assert s.startswith("FALCON_")
+    assert "unknown" in F.status_string(99)
+
+
+def good_shape(**kw):
+    d = dict(variant="F1", dtype="bf16", batch=2, seqlen=100, heads=3, dk=64, dv=64, chunk=64, window=1)
+    d.update(kw)
+    return F.make_shape(**d)
+
+
+def call_fwd(shape, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, init=None, final=None, o=FAKE,
+             cs=None, ws=None, wsb=0):
+    L = F.lib()
+    return L.falcon_chunk_fwd(ctypes.byref(shape) if shape is not None else None, q, k, v, beta, g,
+                              ctypes.byref(init) if init else None, ctypes.byref(final) if final else None,
+                              o, cs, ws, wsb, None)
+
+
+def call_step(shape, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, state=None, o=FAKE):
+    L = F.lib()
+    return L.falcon_recurrent_step(ctypes.byref(shape) if shape is not None else None, q, k, v, beta, g,
+                                   ctypes.byref(state) if state else None, o, None)
+
+
+def test_workspace_is_zero():
+    assert F.lib().falcon_chunk_fwd_workspace(ctypes.byref(good_shape())) == 0
+
+
+INVALID_SHAPES = [
+    dict(variant=0), dict(variant=7), dict(dtype=2), dict(batch=0), dict(seqlen=0), dict(heads=0),
+    dict(dk=0), dict(chunk=0), dict(window=0), dict(variant="F1", window=2),
+    dict(eps_gamma=0.0), dict(eps_gamma=1.5), dict(eps_gamma=float("nan")), dict(eps_phi=-1.0),
+    dict(eps_eta=0.0), dict(eps_eta=float("inf")),
+]
+UNSUPPORTED_SHAPES = [
+    dict(dk=48, dv=48), dict(dk=64, dv=32), dict(dk=256, dv=256), dict(chunk=8), dict(chunk=128),
+    dict(dtype="fp32", dk=128, dv=128), dict(variant="F3", window=3), dict(variant="F3", window=16),
+]
+
+
+@cpu_only
+@pytest.mark.parametrize("kw", INVALID_SHAPES)
+def test_invalid_shape(kw):
+    assert call_fwd(good_shape(**kw)) == F.ERR_INVALID_ARG
+    if "seqlen" not in kw and "chunk" not in kw:
+        assert call_step(good_shape(**kw), state=F.State(FAKE.value, FAKE.value, None, None)) == F.ERR_INVALID_ARG
+
+
+@cpu_only
+@pytest.mark.parametrize("kw", UNSUPPORTED_SHAPES)
+def test_unsupported_shape(kw):
+    assert call_fwd(good_shape(**kw)) == F.ERR_UNSUPPORTED
+
+
+@cpu_only
+def test_null_shape_and_pointers():
+    assert call_fwd(None) == F.ERR_INVALID_ARG
+    for name in ("q", "k", "v", "beta", "g", "o"):
+        assert call_fwd(good_shape(), **{name: None}) == F.ERR_INVALID_ARG, name
+    assert call_step(good_shape(), state=None) == F.ERR_INVALID_ARG
+
+
+@cpu_only
+def test_misaligned_pointers():
+    bad = ctypes.c_void_p(0x10004)
+    for name in ("q", "k", "v", "o", "beta"):
+        assert call_fwd(good_shape(), **{name: bad}) == F.ERR_INVALID_ARG, name
+    assert call_fwd(good_shape(), g=ctypes.c_void_p(0x10002)) == F.ERR_INVALID_ARG
+    assert call_fwd(good_shape(), cs=bad) == F.ERR_INVALID_ARG
+
+
+@cpu_only
+def test_incomplete_states():
+    half = F.State(FAKE.value, None, None, None)
+    assert call_fwd(good_shape(), init=half) == F.ERR_INVALID_ARG
+    assert call_fwd(good_shape(), final=half) == F.ERR_INVALID_ARG
+    no_window = F.State(FAKE.value, FAKE.value, None, None)
+    sh = good_shape(variant="F3", window=4)
+    assert call_fwd(sh, init=no_window) == F.ERR_INVALID_ARG
+    assert call_step(sh, state=no_window) == F.ERR_INVALID_ARG
+    assert call_step(good_shape(), state=F.State(FAKE.value, 0x10008, None, None)) == F.ERR_INVALID_ARG
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(F, "_LIB", None)
+    monkeypatch.setattr(F, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        F.lib()

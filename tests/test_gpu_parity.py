@@ -1,0 +1,157 @@
+"""GPU parity of falcon_chunk_fwd against the fp64 oracle (through the C ABI).
+
+Bar: rel-L2 <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs, on the
+outputs o and on every state the call writes (S, x_prev, window, chunk states).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import TOL, oracle_subset, rel_l2, state_to_dev, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+ROW_VARIANTS = ("F1", "F1A", "F2", "F2A")
+
+
+def run_gpu(variant, inp, dtype, chunk, window=1, init=None, chunk_states=False, final=True):
+    import torch
+    from recurrent_sequence_models_amd import chunk_fwd
+    d = to_dev(inp, dtype)
+    st = state_to_dev(init) if init is not None else None
+    o, fin, cs = chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=chunk,
+                           window=window, init=st, final=final, chunk_states=chunk_states)
+    torch.cuda.synchronize()
+    out = {"o": to_np(o)}
+    if fin is not None:
+        out.update({n: to_np(t) for n, t in fin.items()})
+    if cs is not None:
+        out["chunk_states"] = to_np(cs)
+    return out
+
+
+def check(variant, w, seed, window=1, init=False, chunk=None, chunk_states=False):
+    inp = W.make_inputs(w, variant, seed=seed)
+    st = W.make_state(w, seed + 1000, window) if init else None
+    chunk = chunk or w.chunk
+    g = run_gpu(variant, inp, w.dtype, chunk, window, st, chunk_states)
+    r = oracle.recurrent(variant, **inp, window=window, state=st, return_states=chunk_states)
+    tol = TOL[w.dtype]
+    errs = {"o": rel_l2(g["o"], r["o"]), "S": rel_l2(g["S"], r["S"]), "x_prev": rel_l2(g["x_prev"], r["x_prev"])}
+    if window > 1:
+        errs["win_x"] = rel_l2(g["win_x"], r["win_x"])
+        errs["win_v"] = rel_l2(g["win_v"], r["win_v"])
+    if chunk_states:
+        T = w.seqlen
+        ends = [min(T, c0 + chunk) - 1 for c0 in range(0, T, chunk)]
+        ref = np.moveaxis(r["states"][:, ends], 2, 1)           # [B,H,NC,dv,dk]
+        errs["chunk_states"] = rel_l2(g["chunk_states"], ref)
+    print(variant, w.name, seed, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+    return errs
+
+
+TINY = W.WORKLOADS["tiny_fp32"]
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+@pytest.mark.parametrize("seed", [101, 102, 103])
+def test_tiny_fp32(variant, seed):
+    """The tiny fp32 workload (B1 H2 T256 d32, chunk 16): recurrent oracle vs chunked GPU."""
+    check(variant, TINY, seed)
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_fp32_chunks_ragged_with_state(variant, chunk):
+    w = TINY.replace(batch=2, heads=3, seqlen=203, dk=64, dv=64, chunk=chunk, gates="softplus")
+    check(variant, w, 7, init=True, chunk_states=True)
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_bf16_ragged(variant, d):
+    w = W.WORKLOADS["layer130m"].replace(batch=2, heads=3, seqlen=200, dk=d, dv=d)
+    check(variant, w, 11, init=True, chunk_states=True)
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65])
+def test_short_sequences(variant, T):
+    w = TINY.replace(batch=1, heads=2, seqlen=T, dk=32, dv=32, chunk=16)
+    check(variant, w, 13)
+    w = W.WORKLOADS["layer130m"].replace(batch=1, heads=2, seqlen=T)
+    check(variant, w, 14, init=True)
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+def test_floor_decay_long_chunks(variant):
+    """~5% of steps below the eps_gamma floor (clamped), d = 128, several chunks."""
+    w = W.WORKLOADS["long_t65536"].replace(heads=4, seqlen=640)
+    check(variant, w, 505)
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+def test_correlated_keys(variant):
+    """k_t = k_{t-1} + 0.1 noise: ill-conditioned Gram blocks stress the triangular solve."""
+    w = TINY.replace(batch=1, heads=2, seqlen=130, dk=64, dv=64, chunk=64, gates="softplus")
+    inp = W.make_inputs(w, variant, seed=21)
+    k = inp["k"].copy()
+    for t in range(1, k.shape[1]):
+        k[:, t] = k[:, t - 1] + 0.1 * inp["k"][:, t]
+    inp["k"] = k.astype(np.float32)
+    g = run_gpu(variant, inp, "fp32", 64)
+    r = oracle.recurrent(variant, **inp)
+    assert rel_l2(g["o"], r["o"]) <= TOL["fp32"]
+    assert rel_l2(g["S"], r["S"]) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+def test_split_continuation_in_place(variant):
+    """Two calls, the second continuing in place from the first one's state."""
+    import torch
+    from recurrent_sequence_models_amd import chunk_fwd, new_state
+    w = W.WORKLOADS["layer130m"].replace(batch=2, heads=2, seqlen=300)
+    inp = W.make_inputs(w, variant, seed=31)
+    d = to_dev(inp, "bf16")
+    st = new_state(2, 2, 64, 64)
+    o1, _, _ = chunk_fwd(variant, *(d[n][:, :137].contiguous() for n in ("q", "k", "v", "beta", "log_lambda")),
+                         init=st, final=st)
+    o2, _, _ = chunk_fwd(variant, *(d[n][:, 137:].contiguous() for n in ("q", "k", "v", "beta", "log_lambda")),
+                         init=st, final=st)
+    torch.cuda.synchronize()
+    r = oracle.recurrent(variant, **inp)
+    o = np.concatenate([to_np(o1), to_np(o2)], axis=1)
+    assert rel_l2(o, r["o"]) <= TOL["bf16"]
+    assert rel_l2(to_np(st["S"]), r["S"]) <= TOL["bf16"]
+    assert rel_l2(to_np(st["x_prev"]), r["x_prev"]) <= 1e-6
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+def test_deterministic(variant):
+    w = W.WORKLOADS["layer130m"].replace(batch=2, heads=3, seqlen=256)
+    inp = W.make_inputs(w, variant, seed=41)
+    a = run_gpu(variant, inp, "bf16", 64)
+    b = run_gpu(variant, inp, "bf16", 64)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("name,variant", [("layer130m", "F1"), ("layer130m", "F1A"), ("layer130m_f2", "F2")])
+def test_full_size_sampled(name, variant):
+    """The full 130M-layer workload (B8 H12 T2048 d64, bf16, chunk 64) in the launch
+    configuration the benchmark times; the oracle checks a sample of sequences."""
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, variant, seed=w.seed)
+    g = run_gpu(variant, inp, w.dtype, w.chunk)
+    seqs = [(0, 0), (3, 7), (7, 11)]
+    refs = oracle_subset(variant, inp, seqs)
+    for (b, h), r in zip(seqs, refs):
+        eo = rel_l2(g["o"][b, :, h], r["o"][0, :, 0])
+        es = rel_l2(g["S"][b, h], r["S"][0, 0])
+        print(variant, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    assert np.all(np.isfinite(g["o"]))

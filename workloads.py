@@ -150,10 +150,9 @@ def make_state(w: Workload, seed: int, window: int = 1, zero: bool = False) -> d
 def make_decode_inputs(batch: int, heads: int, dk: int, dv: int, variant: str, seed: int,
                        window: int = 1, dtype: str = "bf16", gates: str = "floor5") -> dict:
     """One decode step's inputs ([B,H,d] each) plus a random incoming state."""
-    w = Workload("decode", batch, 1, heads, dk, dv, dtype, 1, gates, seed)
-    # Draw as a length-1 sequence with heads on the H axis.
-    inp = make_inputs(w.replace(seqlen=1, heads=heads), variant, seed)
-    st = make_state(w.replace(heads=heads), seed + 7919, window)
+    w = Workload("decode", batch=batch, heads=heads, seqlen=1, dk=dk, dv=dv, dtype=dtype,
+                 chunk=1, gates=gates, seed=seed)
+    inp = make_inputs(w, variant, seed)
     out = {n: a[:, 0] for n, a in inp.items()}
-    out.update(st)
+    out.update(make_state(w, seed + 7919, window))
     return out
