@@ -1,0 +1,190 @@
+"""Benchmark of the Falcon chunked forward pass on one MI355X.
+
+Default workload: Falcon-1, the layer shape of the pages' 124-130M models
+(batch 8, 12 heads, head dim 64, T = 2048, bf16 q/k/v, fp32 state, chunk 64),
+synthetic N(0,1) inputs.  One step = one falcon_chunk_fwd call over one batch
+(gates, outputs o, final S and x_prev included).  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant V]
+
+Timing: three rotating input sets (more bytes than the 256 MB MALL), W untimed
+calls, then K timed calls bracketed by torch.cuda.synchronize().  Each call is
+also bracketed by HIP events on the stream it is launched on, which gives the
+average duration of the forward kernel used for the roofline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec, Falcon-1 chunked fwd (H=12,d=64,T=2048) + % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def alg_bytes(w, variant):
+    """Algorithmic HBM bytes of one call: q, k, v, o in the input dtype, the fp32
+    gates (beta is per channel for F2/F2A), the final S and x_prev."""
+    e = 2 if w.dtype == "bf16" else 4
+    per_th = (2 * w.dk + 2 * w.dv) * e + 8 + (4 * w.dv - 4 if variant in ("F2", "F2A") else 0)
+    per_seq = w.dv * w.dk * 4 + w.dk * 4
+    return w.batch * w.heads * (w.seqlen * per_th + per_seq)
+
+
+def ref_flops(w, variant):
+    """Fixed reference flop count of the chunked form at the configured chunk C."""
+    C, dk, dv = w.chunk, w.dk, w.dv
+    per_chunk = {
+        "F1": 2 * C * C * (3 * dk + 2 * dv) + 6 * C * dk * dv + C ** 3 / 3,
+        "F1A": 2 * C * C * (dk + dv) + 4 * C * dk * dv,
+        "F2": 4 * C * C * dk + 6 * C * dk * dv + 2 * C * C * dv + C * C * dv,
+        "F2A": 2 * C * C * (dk + dv) + 4 * C * dk * dv,
+    }[variant]
+    nch = -(-w.seqlen // C)
+    return w.batch * w.heads * nch * per_chunk
+
+
+def cpu_baseline(w, variant, budget_s=20.0):
+    """Time the fp64 oracle (as it stands) on a prefix of the same workload, on
+    one host core; scaled to tokens/s of the full batch."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    import oracle
+    import workloads as W
+    inp = W.make_inputs(w, variant, seed=w.seed)
+    # calibrate on a short prefix, then run a prefix sized for the time budget
+    t_probe = 32
+    t0 = time.perf_counter()
+    oracle.recurrent(variant, **{n: a[:, :t_probe] for n, a in inp.items()})
+    per_step = (time.perf_counter() - t0) / t_probe
+    T_s = int(max(t_probe, min(w.seqlen, budget_s / max(per_step, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.recurrent(variant, **{n: a[:, :T_s] for n, a in inp.items()})
+    dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    return {"value": w.batch * T_s / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 NumPy step loop over all {w.batch * w.heads} sequences of the workload, "
+                      f"first {T_s} of {w.seqlen} steps ({dt:.1f} s on 1 host core)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="layer130m")
+    ap.add_argument("--variant", default="F1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every (b, h) sequence is independent: more GPUs would each run their own share)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    from recurrent_sequence_models_amd import chunk_fwd, new_state
+
+    w = W.WORKLOADS[args.workload]
+    variant = args.variant
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    # three rotating input sets, each with its own outputs and final state
+    sets = []
+    for i in range(3):
+        inp = W.make_inputs(w, variant, seed=w.seed + i)
+        d = {n: torch.from_numpy(a).to(dev) for n, a in inp.items()}
+        for n in ("q", "k", "v"):
+            d[n] = d[n].to(tdt).contiguous()
+        d["o"] = torch.empty(w.batch, w.seqlen, w.heads, w.dv, dtype=tdt, device=dev)
+        d["final"] = new_state(w.batch, w.heads, w.dk, w.dv, device=dev)
+        sets.append(d)
+    del inp
+    stream = torch.cuda.current_stream()
+
+    def call(d):
+        chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk,
+                  final=d["final"], out=d["o"], stream=stream)
+
+    for i in range(args.warmup):
+        call(sets[i % 3])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        call(sets[i % 3])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_kernel_s = sum(kern_ms) / K / 1e3
+    ms_per_step = wall / K * 1e3
+    tokens = w.batch * w.seqlen
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    nbytes = alg_bytes(w, variant)
+    flops = ref_flops(w, variant)
+    achieved = nbytes / avg_kernel_s / 1e9
+    mfma_tfs = flops / avg_kernel_s / 1e12
+    bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFS * 1e12) else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "chunk_fwd_rows"
+    roof["kernel_us"] = {"mean": round(avg_kernel_s * 1e6, 2), "p10": round(kern_ms[K // 10] * 1e3, 2),
+                         "p50": round(kern_ms[K // 2] * 1e3, 2), "p90": round(kern_ms[(9 * K) // 10] * 1e3, 2)}
+    roof["alg_bytes"] = nbytes
+    roof["ref_flops"] = flops
+    roof["mfma_frac"] = round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"Falcon-{variant[1:]} chunked forward, {w.name}: B{w.batch} H{w.heads} "
+                               f"T{w.seqlen} d{w.dk} chunk {w.chunk}, {w.dtype} q/k/v/o, fp32 state",
+                   "variant": variant, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
+                   "head_dim": w.dk, "chunk": w.chunk},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, variant)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

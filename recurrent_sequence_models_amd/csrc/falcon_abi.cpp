@@ -144,9 +144,11 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   a.log_eps_gamma = std::log(s->eps_gamma);
   a.eps_phi = s->eps_phi;
   a.eps_eta = s->eps_eta;
-  // The main kernel writes x_prev itself only when one workgroup owns the whole
-  // sequence (then it has read the incoming x_prev before, even when aliased).
-  a.write_tail = (final_state && nsplit == 1 && !win) ? 1 : 0;
+  // The main kernel writes x_prev itself when that cannot race with another
+  // workgroup still reading the incoming x_prev: one workgroup per sequence, or
+  // the two buffers are distinct.  Otherwise (and for windows) a tail kernel does.
+  const bool xprev_alias = init && final_state && init->x_prev == final_state->x_prev;
+  a.write_tail = (final_state && !win && (nsplit == 1 || !xprev_alias)) ? 1 : 0;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (falcon::launch_chunk_fwd(s->variant, bf16, s->dk, s->dv, s->chunk, nsplit, a, hs) != hipSuccess)
