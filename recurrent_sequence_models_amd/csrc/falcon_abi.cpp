@@ -74,6 +74,8 @@ hipError_t launch_chunk_fwd_window(int variant, bool bf16, int dk, int dv, int c
 int choose_nsplit(int variant, bool bf16, int dk, int dv, int chunk, int batch_heads) {
   (void)bf16; (void)chunk; (void)dk;
   int n = 1;
+  // Falcon-3: one workgroup takes up to 64 value channels.
+  if (windowed(variant)) return dv == 128 ? 2 : 1;
   // F2 keeps per-channel steps in LDS: at 128 channels a workgroup takes 64 of them.
   if (per_channel(variant) && dv == 128) n = 2;
   // Few sequences: split the value channels over more workgroups (rows of S are
@@ -119,7 +121,6 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   if (init && (st = check_state(init, s)) != FALCON_OK) return st;
   if (final_state && (st = check_state(final_state, s)) != FALCON_OK) return st;
   if (chunk_states && !aligned16(chunk_states)) return FALCON_ERR_INVALID_ARG;
-  if (windowed(s->variant)) return FALCON_ERR_UNSUPPORTED;  // chunked Falcon-3 not built yet
   if (workspace_bytes < falcon_chunk_fwd_workspace(s)) return FALCON_ERR_WORKSPACE;
   (void)workspace;
 

@@ -155,3 +155,70 @@ def test_full_size_sampled(name, variant):
         print(variant, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
     assert np.all(np.isfinite(g["o"]))
+
+
+# ---- Falcon-3 / 3A: window of Bw pairs --------------------------------------------
+WIN_CASES = [("F3", 2), ("F3", 4), ("F3", 8), ("F3A", 2), ("F3A", 4), ("F3A", 8), ("F3", 1), ("F3A", 1)]
+
+
+@pytest.mark.parametrize("variant,bw", WIN_CASES)
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_window_fp32(variant, bw, chunk):
+    w = TINY.replace(batch=2, heads=2, seqlen=150, chunk=chunk)
+    check(variant, w, 61, window=bw, init=True, chunk_states=True)
+
+
+@pytest.mark.parametrize("variant,bw", WIN_CASES)
+def test_window_tiny_workload(variant, bw):
+    """The tiny fp32 workload itself (B1 H2 T256 d32, chunk 16), fresh sequences."""
+    check(variant, TINY, 101, window=bw)
+
+
+@pytest.mark.parametrize("variant,bw", WIN_CASES)
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_window_bf16(variant, bw, d):
+    w = W.WORKLOADS["window_t4096"].replace(batch=2, heads=2, seqlen=203, dk=d, dv=d)
+    check(variant, w, 62, window=bw, init=True, chunk_states=True)
+
+
+@pytest.mark.parametrize("variant,bw", [("F3", 4), ("F3", 8), ("F3A", 8)])
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 9, 33])
+def test_window_short(variant, bw, T):
+    """Sequences shorter than the window: the final window mixes carried and new pairs."""
+    w = TINY.replace(batch=1, heads=2, seqlen=T, dk=32, dv=32, chunk=16)
+    check(variant, w, 63, window=bw, init=True)
+
+
+@pytest.mark.parametrize("variant,bw", [("F3", 4), ("F3A", 4), ("F3", 8)])
+def test_window_split_continuation_in_place(variant, bw):
+    import torch
+    from recurrent_sequence_models_amd import chunk_fwd, new_state
+    w = W.WORKLOADS["window_t4096"].replace(batch=2, heads=2, seqlen=300)
+    inp = W.make_inputs(w, variant, seed=64)
+    d = to_dev(inp, "bf16")
+    st = new_state(2, 2, 64, 64, window=bw)
+    outs = []
+    for sl in (slice(0, 5), slice(5, 141), slice(141, 300)):
+        o, _, _ = chunk_fwd(variant, *(d[n][:, sl].contiguous() for n in ("q", "k", "v", "beta", "log_lambda")),
+                            window=bw, init=st, final=st)
+        outs.append(to_np(o))
+    torch.cuda.synchronize()
+    r = oracle.recurrent(variant, **inp, window=bw)
+    assert rel_l2(np.concatenate(outs, axis=1), r["o"]) <= TOL["bf16"]
+    for n in ("S", "x_prev", "win_x", "win_v"):
+        assert rel_l2(to_np(st[n]), r[n]) <= TOL["bf16"], n
+
+
+@pytest.mark.parametrize("variant,bw", [("F3", 4), ("F3", 8), ("F3A", 4), ("F3A", 8)])
+def test_window_full_size_sampled(variant, bw):
+    """The full window workload (B4 H12 T4096 d64, bf16, chunk 64); sampled sequences."""
+    w = W.WORKLOADS["window_t4096"]
+    inp = W.make_inputs(w, variant, seed=w.seed)
+    g = run_gpu(variant, inp, w.dtype, w.chunk, window=bw)
+    seqs = [(0, 0), (3, 11)]
+    refs = oracle_subset(variant, inp, seqs, window=bw)
+    for (b, h), r in zip(seqs, refs):
+        eo = rel_l2(g["o"][b, :, h], r["o"][0, :, 0])
+        es = rel_l2(g["S"][b, h], r["S"][0, 0])
+        print(variant, bw, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
