@@ -70,10 +70,12 @@ hipError_t launch_chunk_fwd_rows(int variant, bool bf16, int dk, int dv, int chu
                                  const FwdArgs &a, hipStream_t s);
 hipError_t launch_chunk_fwd_window(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
                                    const FwdArgs &a, hipStream_t s);
+bool chunk_fwd_pipe_supported(int variant, bool bf16, int dk, int dv, int chunk);
 
 int choose_nsplit(int variant, bool bf16, int dk, int dv, int chunk, int batch_heads) {
-  (void)bf16; (void)chunk; (void)dk;
   int n = 1;
+  // whole sequences per workgroup on the software-pipelined kernel when it fits
+  if (!windowed(variant) && chunk_fwd_pipe_supported(variant, bf16, dk, dv, chunk)) return 1;
   // Falcon-3: one workgroup takes up to 64 value channels.
   if (windowed(variant)) return dv == 128 ? 2 : 1;
   // F2 keeps per-channel steps in LDS: at 128 channels a workgroup takes 64 of them.

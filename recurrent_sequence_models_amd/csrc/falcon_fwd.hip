@@ -498,8 +498,15 @@ hipError_t by_dims(int dk, int dv, int nsplit, int chunk, const FwdArgs &a, hipS
 
 }  // namespace
 
+bool chunk_fwd_pipe_supported(int variant, bool bf16, int dk, int dv, int chunk);
+hipError_t launch_chunk_fwd_pipe(int variant, bool bf16, int dk, int dv, int chunk, const FwdArgs &a,
+                                 hipStream_t s);
+
 hipError_t launch_chunk_fwd_rows(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
                                  const FwdArgs &a, hipStream_t s) {
+  // the software-pipelined kernel takes whole sequences whenever its LDS footprint fits
+  if (nsplit == 1 && chunk_fwd_pipe_supported(variant, bf16, dk, dv, chunk))
+    return launch_chunk_fwd_pipe(variant, bf16, dk, dv, chunk, a, s);
 #define FALCON_DISPATCH(VV)                                                         \
   return bf16 ? by_dims<VV, __bf16>(dk, dv, nsplit, chunk, a, s)                   \
               : by_dims<VV, float>(dk, dv, nsplit, chunk, a, s)
