@@ -11,20 +11,22 @@
 // One workgroup per sequence (b, h), D/16 + 4 waves:
 //   consumer waves (one per 16 value channels) keep S^T in registers and, for
 //     chunk c, compute X S0^T, Q^ S0^T, the residuals E (blocked solve), the
-//     outputs and the state update;
+//     outputs and the state update.  They read their values (and Falcon-2's
+//     per-channel gains) straight from HBM in MFMA fragment layout, one chunk
+//     ahead.
 //   producer waves, in the same iteration, build the key-side tiles of chunk
 //     c+1 (decayed Gram A with the step folded in, scores P, diagonal-block
-//     inverses T_pp), stage the normalised inputs of chunk c+2 in LDS and
+//     inverses T_pp), stage the normalised keys/queries of chunk c+2 in LDS and
 //     prefetch the raw inputs of chunk c+3 into registers.
 // One workgroup barrier per chunk.  Input tiles are triple-buffered, key-side
-// tiles double-buffered.  Nothing the consumers need is computed on their
-// chain except what depends on S.
+// tiles double-buffered.  Every k axis an MFMA reduces over is stored permuted
+// in LDS (kperm) so that one 16-byte read fills a 16x16x32 operand.
 //
-// Falcon-2 (per-channel step): the 16x16 diagonal block of each channel's
-// system (I + A_pp diag(eta_c)) e = r is solved by a block-Jacobi sweep over
-// 4x4 sub-blocks: each lane solves its own 4 rows exactly, and the coupling
-// between sub-blocks (strictly block-lower, hence nilpotent) is one MFMA with
-// the shared matrix A_pp per sweep; three sweeps make the solution exact.
+// Diagonal blocks: T_pp = (I + N)^{-1} with N strictly lower 16x16, and
+// Falcon-2's per-channel systems (I + A_pp diag(eta_c)) e = r, are both solved
+// by a block-Jacobi sweep over 4x4 sub-blocks: each lane group solves its own
+// 4 rows exactly, and the coupling between sub-blocks (strictly block-lower,
+// hence nilpotent) is one 16x16 MFMA per sweep; three sweeps are exact.
 #include "falcon_kernels.h"
 #include "mfma_frag.h"
 
@@ -93,49 +95,55 @@ struct Pipe {
   static constexpr bool PERCH = (VAR == V_F2 || VAR == V_F2A);
   static constexpr bool DELTA = (VAR == V_F1 || VAR == V_F2);
   static constexpr int NB = C / 16, NA = D / 16;
-  static constexpr int NCW = D / 16, NPW = 4, NWAVES = NCW + NPW, NT = 64 * NWAVES;
-  static constexpr int NPT = 64 * NPW;                   // producer threads
-  static constexpr int LX = D + 4, LT = C + 4, LV = D + 16 / (int)sizeof(IT);
-  static constexpr int NOFF = NB * (NB - 1) / 2, NPB = NB * (NB + 1) / 2;
-  static constexpr int VEC = 16 / sizeof(IT);
-  static constexpr int LO = 16 + VEC;                    // output staging row (16 channels + pad)
-  static constexpr int TPR = D / VEC;                    // producer threads per input row
-  static constexpr int RPP = NPT / TPR;                  // rows per producer pass
+  static constexpr int NCW = D / 16, NPW = 4, NT = 64 * (NCW + NPW);
+  static constexpr int NPT = 64 * NPW;                       // producer threads
+  static constexpr int PADE = 16 / (int)sizeof(IT);          // elements in 16 bytes
+  static constexpr int LX = D + PADE;                        // X, Q rows (k = dk, permuted)
+  static constexpr int LT = C + PADE;                        // XT, Ao, P rows (k = chunk row)
+  static constexpr int LTB = 16 + PADE;                      // T_pp / inner-block rows
+  static constexpr int LO = 16 + PADE;                       // output staging rows
+  static constexpr int VEC = PADE;
+  static constexpr int TPR = D / VEC;                        // producer threads per input row
+  static constexpr int RPP = NPT / TPR;                      // rows per producer pass
   static constexpr int NPASS = (C + RPP - 1) / RPP;
+  static constexpr int NOFF = NB * (NB - 1) / 2, NPB = NB * (NB + 1) / 2;
   static constexpr size_t lds_bytes() {
-    return sizeof(IT) * (3 * (2 * C * LX + D * LT + C * LV) + 2 * ((NOFF ? NOFF : 1) * 320 + NB * 320 + NPB * 320)) +
-           sizeof(IT) * NCW * C * LO +
+    return sizeof(IT) * (3 * (2 * C * LX + D * LT) + 2 * (2 * C * LT + NB * 16 * LTB) + NCW * C * LO) +
            4 * (3 * G_N * C + 3 + (PERCH ? 2 * NB * 272 : 0) + (VAR == V_F1 ? NPW * 272 : 0) + 2 * D + 2);
   }
-  static constexpr bool fits() { return lds_bytes() + 512 <= 160 * 1024; }
+  static constexpr bool fits() { return lds_bytes() + 256 <= 160 * 1024; }
 };
+
+// position of chunk-row k in a row whose k axis is a chunk (permuted when C >= 32)
+template <int C>
+__device__ __forceinline__ int kc(int k) { return (C % 32 == 0) ? kperm(k) : k; }
 
 template <int VAR, typename IT, int D, int C>
 __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
   using P = Pipe<VAR, IT, D, C>;
   using OpT = IT;
   using Frag = typename Op<OpT>::frag;
+  using Pr = Pair<OpT>;
   constexpr int NB = P::NB, NA = P::NA, NCW = P::NCW, NPW = P::NPW;
-  constexpr int LX = P::LX, LT = P::LT, LV = P::LV, VEC = P::VEC, TPR = P::TPR, RPP = P::RPP, NPASS = P::NPASS;
+  constexpr int LX = P::LX, LT = P::LT, LTB = P::LTB, VEC = P::VEC, TPR = P::TPR, RPP = P::RPP, NPASS = P::NPASS;
   constexpr bool PERCH = P::PERCH, DELTA = P::DELTA;
-  constexpr int NOFF1 = P::NOFF ? P::NOFF : 1;
 
-  __shared__ __attribute__((aligned(16))) OpT sX[3][C * LX];
-  __shared__ __attribute__((aligned(16))) OpT sQ[3][C * LX];
-  __shared__ __attribute__((aligned(16))) OpT sXT[3][D * LT];
-  __shared__ __attribute__((aligned(16))) IT sV[3][C * LV];
-  __shared__ float sG[3][G_N * C];
+  __shared__ __attribute__((aligned(16))) OpT sX[3][C * LX];      // x_i = phi(k_{i-1}), dk permuted
+  __shared__ __attribute__((aligned(16))) OpT sQ[3][C * LX];      // q^_i, dk permuted
+  __shared__ __attribute__((aligned(16))) OpT sXT[3][D * LT];     // X^T, chunk row permuted
+  __shared__ __attribute__((aligned(16))) float sG[3][G_N * C];
   __shared__ float sLam[3];
-  __shared__ __attribute__((aligned(16))) OpT sAo[2][NOFF1 * 320];    // off-diagonal blocks of A, 16 x 20
-  __shared__ __attribute__((aligned(16))) OpT sTb[2][NB * 320];       // F1: T_pp; F2: A_pp minus its 4x4 diagonal
-  __shared__ __attribute__((aligned(16))) OpT sP[2][P::NPB * 320];    // score blocks (p, q <= p)
-  __shared__ float sAd2[PERCH ? 2 : 1][PERCH ? NB * 272 : 1];         // F2: diagonal blocks of A, fp32
+  __shared__ __attribute__((aligned(16))) OpT sAo[2][C * LT];     // strictly-lower blocks of A (k permuted)
+  __shared__ __attribute__((aligned(16))) OpT sP[2][C * LT];      // lower blocks of P (k permuted)
+  __shared__ __attribute__((aligned(16))) OpT sTb[2][NB * 16 * LTB];  // F1: T_pp; F2: A_pp minus its 4x4 diagonal
+  __shared__ float sAd2[PERCH ? 2 : 1][PERCH ? NB * 272 : 1];     // F2: diagonal blocks of A, fp32
   __shared__ float sAdT[VAR == V_F1 ? NPW : 1][VAR == V_F1 ? 272 : 1];  // F1: producer scratch
   __shared__ float sCarry[2][D];
   __shared__ float sCarryN2[2];
   __shared__ __attribute__((aligned(16))) IT sOst[NCW][C * P::LO];   // consumer output staging
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = tid >> 6;
   const int g4 = lane >> 4, cl = lane & 15;
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int T = a.T, H = a.H, NC = a.nchunks;
@@ -149,8 +157,8 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
   const IT *vp = static_cast<const IT *>(a.v);
   IT *op = static_cast<IT *>(a.o);
 
-  // ---------------- producer helpers ----------------
-  uint4 rk[NPASS], rq[NPASS], rv[NPASS];   // raw input rows of one chunk
+  // ================= producers =================
+  uint4 rk[NPASS], rq[NPASS];              // raw key / query rows of one chunk
   float rg = 0.f, rb = 0.f;                // raw gate of row `lane` (producer wave NPW-1)
 
   auto prefetch = [&](int c) {             // global -> registers, chunk c
@@ -159,10 +167,9 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     for (int ps = 0; ps < NPASS; ++ps) {
       const int r = ps * RPP + ptid / TPR, part = ptid % TPR, t = c0 + r;
       const bool ok = r < C && t < T;
-      const size_t rowq = ((size_t)(b * T + t) * H + h);
-      rk[ps] = ok ? *reinterpret_cast<const uint4 *>(kp + rowq * D + part * VEC) : uint4{0, 0, 0, 0};
-      rq[ps] = ok ? *reinterpret_cast<const uint4 *>(qp + rowq * D + part * VEC) : uint4{0, 0, 0, 0};
-      rv[ps] = ok ? *reinterpret_cast<const uint4 *>(vp + rowq * D + part * VEC) : uint4{0, 0, 0, 0};
+      const size_t row = ((size_t)(b * T + t) * H + h) * D + part * VEC;
+      rk[ps] = ok ? *reinterpret_cast<const uint4 *>(kp + row) : uint4{0, 0, 0, 0};
+      rq[ps] = ok ? *reinterpret_cast<const uint4 *>(qp + row) : uint4{0, 0, 0, 0};
     }
     if (pw == NPW - 1) {
       const int t = c0 + lane;
@@ -172,16 +179,27 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     }
   };
 
+  // write 4 consecutive logical columns starting at k0 (multiple of 4) of a dk-permuted row
+  auto put4 = [&](OpT *row, int k0, const float *v) {
+    OpT *dst = row + kperm(k0);
+    if constexpr (sizeof(OpT) == 2) {
+      bf4 w;
+      w[0] = (__bf16)v[0]; w[1] = (__bf16)v[1]; w[2] = (__bf16)v[2]; w[3] = (__bf16)v[3];
+      *reinterpret_cast<bf4 *>(dst) = w;
+    } else {
+      *reinterpret_cast<f4 *>(dst) = f4{v[0], v[1], v[2], v[3]};
+    }
+  };
+
   auto stage = [&](int c) {                // registers -> normalised LDS tiles of chunk c
     const int s = c % 3;
     const int cin = (c + 1) & 1, cprev = c & 1;   // carry written for chunk c+1, read from chunk c-1
     OpT *X = sX[s], *Q = sQ[s], *XT = sXT[s];
-    IT *V = sV[s];
     float *G = sG[s];
     for (int e = ptid; e < D; e += P::NPT) {
       const float x = sCarry[cprev][e];
-      X[e] = (OpT)x;
-      XT[e * LT] = (OpT)x;
+      X[kperm(e)] = (OpT)x;
+      XT[e * LT + kc<C>(0)] = (OpT)x;
     }
     if (ptid == 0) G[G_XN2 * C + 0] = sCarryN2[cprev];
 #pragma unroll
@@ -196,29 +214,27 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
       sk = group_sum<TPR>(sk);
       sq = group_sum<TPR>(sq);
       const float ik = safe_rsqrt(sk + a.eps_phi), iq = safe_rsqrt(sq + a.eps_phi);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) { xv[e] *= ik; qv[e] *= iq; }
       if (r + 1 < C) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const OpT xo = (OpT)(xv[e] * ik);
-          X[(r + 1) * LX + part * VEC + e] = xo;
-          XT[(part * VEC + e) * LT + r + 1] = xo;
-        }
+        for (int e = 0; e < VEC; e += 4) put4(X + (r + 1) * LX, part * VEC + e, xv + e);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) XT[(part * VEC + e) * LT + kc<C>(r + 1)] = (OpT)xv[e];
         if (part == 0) G[G_XN2 * C + r + 1] = sk * ik * ik;
       } else if (r + 1 == C) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) sCarry[cin][part * VEC + e] = xv[e] * ik;
+        for (int e = 0; e < VEC; ++e) sCarry[cin][part * VEC + e] = xv[e];
         if (part == 0) sCarryN2[cin] = sk * ik * ik;
       }
       if (r < C) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) Q[r * LX + part * VEC + e] = (OpT)(qv[e] * iq);
-        *reinterpret_cast<uint4 *>(V + r * LV + part * VEC) = rv[ps];
+        for (int e = 0; e < VEC; e += 4) put4(Q + r * LX, part * VEC + e, qv + e);
       }
     }
     if (pw == NPW - 1) {   // clamp in log space, chunk-local inclusive scan
-      const float gg = fmaxf(rg, a.log_eps_gamma);
       const bool ok = lane < C && c * C + lane < T;
-      const float g2 = ok ? gg : 0.f;
+      const float g2 = ok ? fmaxf(rg, a.log_eps_gamma) : 0.f;
       const float L = wave_inclusive_scan(g2);
       if (lane < C) {
         G[G_LC * C + lane] = L;
@@ -233,33 +249,36 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     const OpT *X = sX[s], *Q = sQ[s];
     float *G = sG[s];
     auto wcol = [&](int col) { return PERCH ? 1.f : G[G_BETA * C + col] / (a.eps_eta + G[G_XN2 * C + col]); };
+    auto gram = [&](const OpT *Am, int p, int q) {   // 16x16 block (p, q) of Am X^T
+      f4 acc = zero4();
+#pragma unroll
+      for (int a2 = 0; a2 < NA / 2; ++a2)
+        mmap(acc, ldp(Am + (16 * p + cl) * LX + 32 * a2 + 8 * g4), ldp(X + (16 * q + cl) * LX + 32 * a2 + 8 * g4));
+      return acc;
+    };
     // diagonal Gram block pw (F1: T_pp; F2: A_pp)
     if (DELTA && pw < NB) {
       const int p = pw;
-      f4 acc = zero4();
-#pragma unroll
-      for (int aa = 0; aa < NA; aa += 2)
-        mma32(acc, lda(X, LX, 16 * p, 16 * aa, lane), lda(X, LX, 16 * p, 16 * aa + 16, lane),
-              lda(X, LX, 16 * p, 16 * aa, lane), lda(X, LX, 16 * p, 16 * aa + 16, lane));
+      const f4 acc = gram(X, p, p);
       const int col = 16 * p + cl;
       const float Lcol = G[G_LC * C + col], wc = wcol(col);
+      const f4 Lmr = *reinterpret_cast<const f4 *>(G + G_LM * C + 16 * p + 4 * g4);
       f4 N;   // C-layout: N[4 g4 + i][cl] of the diagonal block (A with the step folded in for F1)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * p + 4 * g4 + i;
-        N[i] = (col < row) ? acc[i] * __expf(G[G_LM * C + row] - Lcol) * wc : 0.f;
+        const float v = acc[i] * __expf(Lmr[i] - Lcol) * wc;
+        N[i] = (cl < 4 * g4 + i) ? v : 0.f;
       }
+      const int r0 = 4 * g4;
       if (VAR == V_F1) {
-        // T_pp = (I + N)^{-1} by block Jacobi over 4x4 sub-blocks (lane group g4 owns rows 4 g4..+3):
-        // T <- (I + N_d)^{-1} (I - N_o T), exact after 3 sweeps because N_o is block-strictly-lower.
+        // T_pp = (I + N)^{-1}: T <- (I + N_d)^{-1} (I - N_o T), exact after 3 sweeps.
         float *Ad = sAdT[pw];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Ad[(4 * g4 + i) * 17 + cl] = N[i];
+        for (int i = 0; i < 4; ++i) Ad[(r0 + i) * 17 + cl] = N[i];
         wave_lds_sync();
         f4 No;   // A-layout of N without its 4x4 diagonal sub-blocks: N[cl][4 g4 + i]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) No[i] = ((cl >> 2) == g4) ? 0.f : Ad[cl * 17 + 4 * g4 + i];
-        const int r0 = 4 * g4;
+        for (int i = 0; i < 4; ++i) No[i] = ((cl >> 2) == g4) ? 0.f : Ad[cl * 17 + r0 + i];
         const float n10 = Ad[(r0 + 1) * 17 + r0], n20 = Ad[(r0 + 2) * 17 + r0], n21 = Ad[(r0 + 2) * 17 + r0 + 1];
         const float n30 = Ad[(r0 + 3) * 17 + r0], n31 = Ad[(r0 + 3) * 17 + r0 + 1], n32 = Ad[(r0 + 3) * 17 + r0 + 2];
         f4 Z, Y;
@@ -279,13 +298,12 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
           local(Z - cpl);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sTb[ds][p * 320 + (r0 + i) * 20 + cl] = (OpT)Y[i];
+        for (int i = 0; i < 4; ++i) sTb[ds][(p * 16 + r0 + i) * LTB + cl] = (OpT)Y[i];
       } else {  // F2: full diagonal block (fp32) and its part outside the 4x4 diagonal sub-blocks
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rl = 4 * g4 + i;
-          sAd2[ds][p * 272 + rl * 17 + cl] = N[i];
-          sTb[ds][p * 320 + rl * 20 + cl] = (OpT)((rl >> 2) == (cl >> 2) ? 0.f : N[i]);
+          sAd2[ds][p * 272 + (r0 + i) * 17 + cl] = N[i];
+          sTb[ds][(p * 16 + r0 + i) * LTB + cl] = (OpT)((cl >> 2) == g4 ? 0.f : N[i]);
         }
       }
     }
@@ -295,36 +313,30 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
 #pragma unroll
     for (int jj = 0; jj < (NJOB + NPW - 1) / NPW; ++jj) {
       const int job = pw + jj * NPW;
-      if (job >= NJOB) break;
-      const bool isP = job >= NG;
-      const int pj = isP ? job - NG : job;
-      int p, q;
-      if (isP) {
-        p = 0;
-        while ((p + 1) * (p + 2) / 2 <= pj) ++p;
-        q = pj - p * (p + 1) / 2;
-      } else {
-        p = 1;
-        while (p * (p + 1) / 2 <= pj) ++p;
-        q = pj - p * (p - 1) / 2;
-      }
-      const OpT *Am = isP ? Q : X;
-      f4 acc = zero4();
-#pragma unroll
-      for (int aa = 0; aa < NA; aa += 2)
-        mma32(acc, lda(Am, LX, 16 * p, 16 * aa, lane), lda(Am, LX, 16 * p, 16 * aa + 16, lane),
-              lda(X, LX, 16 * q, 16 * aa, lane), lda(X, LX, 16 * q, 16 * aa + 16, lane));
-      const int col = 16 * q + cl;
-      const float Lcol = G[G_LC * C + col], wc = wcol(col);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * p + 4 * g4 + i;
+      if (job < NJOB) {
+        const bool isP = job >= NG;
+        const int pj = isP ? job - NG : job;
+        int p, q;
         if (isP) {
-          const float val = (col <= row) ? acc[i] * __expf(G[G_LC * C + row] - Lcol) * wc : 0.f;
-          sP[ds][pj * 320 + (4 * g4 + i) * 20 + cl] = (OpT)val;
+          p = 0;
+          while ((p + 1) * (p + 2) / 2 <= pj) ++p;
+          q = pj - p * (p + 1) / 2;
         } else {
-          const float val = acc[i] * __expf(G[G_LM * C + row] - Lcol) * wc;   // q < p: always below
-          sAo[ds][pj * 320 + (4 * g4 + i) * 20 + cl] = (OpT)val;
+          p = 1;
+          while (p * (p + 1) / 2 <= pj) ++p;
+          q = pj - p * (p - 1) / 2;
+        }
+        const f4 acc = gram(isP ? Q : X, p, q);
+        const int col = 16 * q + cl;
+        const float Lcol = G[G_LC * C + col], wc = wcol(col);
+        // decay to the row: e^{L_i - L_j} for scores, e^{L_{i-1} - L_j} for the Gram
+        const f4 Lr = *reinterpret_cast<const f4 *>(G + (isP ? G_LC : G_LM) * C + 16 * p + 4 * g4);
+        OpT *dst = (isP ? sP[ds] : sAo[ds]) + kc<C>(col);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * p + 4 * g4 + i;
+          const float v = acc[i] * __expf(Lr[i] - Lcol) * wc;
+          dst[row * LT] = (OpT)((p > q || cl <= 4 * g4 + i) ? v : 0.f);   // Gram blocks have q < p
         }
       }
     }
@@ -342,65 +354,78 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     }
   };
 
-  // ---------------- consumer state ----------------
-  f4 sT[NA];
-  float rbeta[NB][4];                       // F2/F2A: beta of the next chunk, C-layout
+  // ================= consumers =================
+  f4 sT[NA];                 // S^T of this wave's 16 channels, C-layout per dk block
+  IT rv[NB][4];              // values of the next chunk, C-layout
+  float rbeta[NB][4];        // F2/F2A: per-channel gains of the next chunk
   if (consumer) {
 #pragma unroll
     for (int aa = 0; aa < NA; ++aa)
       sT[aa] = a.S0 ? *reinterpret_cast<const f4 *>(a.S0 + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) : zero4();
   }
-  auto prefetch_beta = [&](int c) {
+  auto prefetch_v = [&](int c) {
 #pragma unroll
     for (int p = 0; p < NB; ++p)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = c * C + 16 * p + 4 * g4 + i;
-        rbeta[p][i] = (t < T) ? a.beta[((size_t)(b * T + t) * H + h) * D + chW] : 0.f;
+        const size_t idx = ((size_t)(b * T + t) * H + h) * D + chW;
+        rv[p][i] = (t < T) ? vp[idx] : (IT)0.f;
+        if (PERCH) rbeta[p][i] = (t < T) ? a.beta[idx] : 0.f;
       }
   };
 
   auto consume = [&](int c) {
     const int s = c % 3, ds = c & 1, c0 = c * C;
     const OpT *X = sX[s], *Q = sQ[s], *XT = sXT[s];
-    const IT *V = sV[s];
     const float *G = sG[s];
-    Frag Sb[NA];
+    const OpT *Ao = sAo[ds], *Pm = sP[ds], *Tb = sTb[ds];
+    Pr Sp[NA / 2];
 #pragma unroll
-    for (int aa = 0; aa < NA; ++aa) Sb[aa] = cvt<OpT>(sT[aa]);
+    for (int a2 = 0; a2 < NA / 2; ++a2) Sp[a2] = mkp(cvt<OpT>(sT[2 * a2]), cvt<OpT>(sT[2 * a2 + 1]));
     f4 QS[NB], XS[NB];
 #pragma unroll
     for (int p = 0; p < NB; ++p) {
       QS[p] = zero4();
       XS[p] = zero4();
 #pragma unroll
-      for (int aa = 0; aa < NA; aa += 2) {
-        if (DELTA)
-          mma32(XS[p], lda(X, LX, 16 * p, 16 * aa, lane), lda(X, LX, 16 * p, 16 * aa + 16, lane), Sb[aa], Sb[aa + 1]);
-        mma32(QS[p], lda(Q, LX, 16 * p, 16 * aa, lane), lda(Q, LX, 16 * p, 16 * aa + 16, lane), Sb[aa], Sb[aa + 1]);
+      for (int a2 = 0; a2 < NA / 2; ++a2) {
+        if (DELTA) mmap(XS[p], ldp(X + (16 * p + cl) * LX + 32 * a2 + 8 * g4), Sp[a2]);
+        mmap(QS[p], ldp(Q + (16 * p + cl) * LX + 32 * a2 + 8 * g4), Sp[a2]);
       }
     }
+    // A-layout operand of the 16x16 block (row block p, k block q) of a C x C tile
+    auto blk1 = [&](const OpT *M, int p, int q) -> Frag {
+      const int k0 = (C % 32 == 0) ? (32 * (q >> 1) + 8 * g4 + 4 * (q & 1)) : (16 * q + 4 * g4);
+      return ld4(M + (16 * p + cl) * LT + k0);
+    };
+    auto blk2 = [&](const OpT *M, int p, int q) -> Pr {   // k blocks q, q+1 (q even)
+      return ldp(M + (16 * p + cl) * LT + 32 * (q >> 1) + 8 * g4);
+    };
     Frag Eb[NB];
     f4 Ef[NB];
 #pragma unroll
     for (int p = 0; p < NB; ++p) {
+      const f4 gam = *reinterpret_cast<const f4 *>(G + G_GAM * C + 16 * p + 4 * g4);
       f4 R, eta4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * p + 4 * g4 + i;
-        R[i] = to_f(V[row * LV + chW]);
-        if (DELTA) R[i] -= G[G_GAM * C + row] * XS[p][i];
-        if (PERCH) eta4[i] = rbeta[p][i] * G[G_ETA * C + row];
+      for (int i = 0; i < 4; ++i) R[i] = to_f(rv[p][i]);
+      if (DELTA) R -= gam * XS[p];
+      if (PERCH) {
+        const f4 inv = *reinterpret_cast<const f4 *>(G + G_ETA * C + 16 * p + 4 * g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eta4[i] = rbeta[p][i] * inv[i];
       }
-      if (DELTA) {
+      if (DELTA) {   // R -= sum_{q<p} A_pq E_q   (E_q = eta (.) E for F2)
         f4 acc = zero4();
 #pragma unroll
-        for (int q = 0; q < p; ++q) mma16(acc, lda(sAo[ds], 20, 16 * (p * (p - 1) / 2 + q), 0, lane), Eb[q]);
+        for (int q = 0; q + 1 < p; q += 2) mmap(acc, blk2(Ao, p, q), mkp(Eb[q], Eb[q + 1]));
+        if (p & 1) mma16(acc, blk1(Ao, p, p - 1), Eb[p - 1]);
         R -= acc;
       }
       if (VAR == V_F1) {
         f4 E = zero4();
-        mma16(E, lda(sTb[ds], 20, 16 * p, 0, lane), cvt<OpT>(R));
+        mma16(E, ld4(Tb + (16 * p + cl) * LTB + 4 * g4), cvt<OpT>(R));
         Ef[p] = E;
         Eb[p] = cvt<OpT>(E);
       } else if (VAR == V_F2) {
@@ -409,7 +434,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
         const int r0 = 4 * g4;
         const float a10 = Ad[(r0 + 1) * 17 + r0], a20 = Ad[(r0 + 2) * 17 + r0], a21 = Ad[(r0 + 2) * 17 + r0 + 1];
         const float a30 = Ad[(r0 + 3) * 17 + r0], a31 = Ad[(r0 + 3) * 17 + r0 + 1], a32 = Ad[(r0 + 3) * 17 + r0 + 2];
-        const Frag Ao = lda(sTb[ds], 20, 16 * p, 0, lane);
+        const Frag Ain = ld4(Tb + (16 * p + cl) * LTB + 4 * g4);
         f4 E, F;
         auto local = [&](const f4 &z) {
           E[0] = z[0];
@@ -425,7 +450,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
 #pragma unroll
         for (int it = 0; it < 3; ++it) {
           f4 cpl = zero4();
-          mma16(cpl, Ao, cvt<OpT>(F));
+          mma16(cpl, Ain, cvt<OpT>(F));
           local(R - cpl);
         }
         Ef[p] = F;                 // eta (.) E feeds the state update and the outputs
@@ -439,14 +464,13 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
         Eb[p] = cvt<OpT>(F);
       }
     }
-    // outputs
+    // outputs o = e^{L} Q^ S0^T + P E'
 #pragma unroll
     for (int p = 0; p < NB; ++p) {
-      f4 O;
+      f4 O = *reinterpret_cast<const f4 *>(G + G_EL * C + 16 * p + 4 * g4) * QS[p];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) O[i] = G[G_EL * C + 16 * p + 4 * g4 + i] * QS[p][i];
-#pragma unroll
-      for (int q = 0; q <= p; ++q) mma16(O, lda(sP[ds], 20, 16 * (p * (p + 1) / 2 + q), 0, lane), Eb[q]);
+      for (int q = 0; q + 1 <= p; q += 2) mmap(O, blk2(Pm, p, q), mkp(Eb[q], Eb[q + 1]));
+      if (!(p & 1)) mma16(O, blk1(Pm, p, p), Eb[p]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sOst[wv][(16 * p + 4 * g4 + i) * P::LO + cl] = (IT)O[i];
     }
@@ -462,23 +486,21 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
               *reinterpret_cast<const uint4 *>(&sOst[wv][r * P::LO + j * VEC]);
       }
     }
-    // state
+    // state: S^T <- e^{L_last} S^T + X^T diag(cst) E'
     Frag CE[NB];
 #pragma unroll
-    for (int p = 0; p < NB; ++p) {
-      f4 x;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = G[G_CST * C + 16 * p + 4 * g4 + i] * Ef[p][i];
-      CE[p] = cvt<OpT>(x);
-    }
+    for (int p = 0; p < NB; ++p) CE[p] = cvt<OpT>(*reinterpret_cast<const f4 *>(G + G_CST * C + 16 * p + 4 * g4) * Ef[p]);
     const float lamtot = sLam[s];
 #pragma unroll
     for (int aa = 0; aa < NA; ++aa) {
       f4 acc = sT[aa] * lamtot;
+      if constexpr (NB == 1) {
+        mma16(acc, ld4(XT + (16 * aa + cl) * LT + 4 * g4), CE[0]);
+      } else {
 #pragma unroll
-      for (int p = 0; p + 1 < NB; p += 2)
-        mma32(acc, lda(XT, LT, 16 * aa, 16 * p, lane), lda(XT, LT, 16 * aa, 16 * p + 16, lane), CE[p], CE[p + 1]);
-      if (NB & 1) mma16(acc, lda(XT, LT, 16 * aa, 16 * (NB - 1), lane), CE[NB - 1]);
+        for (int p = 0; p < NB; p += 2)
+          mmap(acc, ldp(XT + (16 * aa + cl) * LT + 32 * (p >> 1) + 8 * g4), mkp(CE[p], CE[p + 1]));
+      }
       sT[aa] = acc;
     }
     if (a.chunk_states) {
@@ -493,17 +515,15 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     // the carry slot read by chunk 0 is slot 0 (chunk -1's key = the incoming x_prev)
     for (int e = ptid; e < D; e += P::NPT) sCarry[0][e] = a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f;
     prefetch(0);
+  } else {
+    prefetch_v(0);
   }
-  if (consumer && PERCH) prefetch_beta(0);
   __syncthreads();
-  if (!consumer) {
-    if (pw == 0) {
-      float s = 0.f;
-      for (int e = lane; e < D; e += 64) s += sCarry[0][e] * sCarry[0][e];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-      if (lane == 0) sCarryN2[0] = s;
-    }
+  if (pw == 0) {
+    float s = 0.f;
+    for (int e = lane; e < D; e += 64) s += sCarry[0][e] * sCarry[0][e];
+    s = group_sum<64>(s);
+    if (lane == 0) sCarryN2[0] = s;
   }
   __syncthreads();
   if (!consumer) {
@@ -517,7 +537,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     if (consumer) {
       if (i >= 1) {
         consume(i - 1);
-        if (PERCH && i < NC) prefetch_beta(i);
+        if (i < NC) prefetch_v(i);
       }
     } else {
       if (i + 1 < NC) {
@@ -535,15 +555,13 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
       *reinterpret_cast<f4 *>(a.S_out + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) = sT[aa];
   }
   if (a.write_tail && a.xprev_out && pw == 0) {
-    float s = 0.f, xv[2] = {0.f, 0.f};
+    float xv[2] = {0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int e = lane + 64 * j;
       if (e < D) xv[j] = to_f(kp[((size_t)(b * T + T - 1) * H + h) * D + e]);
-      s += xv[j] * xv[j];
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    const float s = group_sum<64>(xv[0] * xv[0] + xv[1] * xv[1]);
     const float inv = safe_rsqrt(s + a.eps_phi);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {

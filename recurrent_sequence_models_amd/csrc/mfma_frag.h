@@ -72,4 +72,31 @@ __device__ __forceinline__ typename Op<OpT>::frag lda(const OpT *m, int ld, int 
 
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
+// ---- Pairs of k-blocks --------------------------------------------------------
+// A "pair" holds a lane's operands for two k-blocks of 16 (k = 4g+i of block 0 in
+// `lo`, of block 1 in `hi`).  In LDS a pair is 8 consecutive elements when the k
+// axis is stored permuted within groups of 32: logical k = 16h + 4g + i lives at
+// position 8g + 4h + i (kperm), so one 16-byte read fills a 16x16x32 operand.
+__device__ __forceinline__ int kperm(int k) { return (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3); }
+
+template <typename T> struct Pair;
+template <> struct Pair<__bf16> { bf8 v; };
+template <> struct Pair<float> { f4 lo, hi; };
+
+__device__ __forceinline__ Pair<__bf16> ldp(const __bf16 *p) { return {*reinterpret_cast<const bf8 *>(p)}; }
+__device__ __forceinline__ Pair<float> ldp(const float *p) {
+  return {*reinterpret_cast<const f4 *>(p), *reinterpret_cast<const f4 *>(p + 4)};
+}
+__device__ __forceinline__ Pair<__bf16> mkp(const bf4 &lo, const bf4 &hi) {
+  return {bf8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}};
+}
+__device__ __forceinline__ Pair<float> mkp(const f4 &lo, const f4 &hi) { return {lo, hi}; }
+__device__ __forceinline__ void mmap(f4 &d, const Pair<__bf16> &a, const Pair<__bf16> &b) {
+  d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, d, 0, 0, 0);
+}
+__device__ __forceinline__ void mmap(f4 &d, const Pair<float> &a, const Pair<float> &b) {
+  mma16(d, a.lo, b.lo);
+  mma16(d, a.hi, b.hi);
+}
+
 }  // namespace falcon
