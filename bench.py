@@ -38,20 +38,101 @@ def alg_bytes(w, variant):
     return w.batch * w.heads * (w.seqlen * per_th + per_seq)
 
 
-def ref_flops(w, variant):
-    """Fixed reference flop count of the chunked form at the configured chunk C."""
+def ref_flops(w, variant, window=1):
+    """Fixed reference flop count of the chunked form at the configured chunk C
+    (Falcon-3: per WY system of C/Bw steps and C virtual rows)."""
     C, dk, dv = w.chunk, w.dk, w.dv
+    if variant == "F3" and window > 1:
+        cs, m = C // window, C
+        per_sub = (2 * m * m * (2 * dk + dv) + m ** 3 / 3 + 4 * m * dk * dv + 2 * cs * m * (dk + dv)
+                   + 2 * cs * dk * dv)
+        return w.batch * w.heads * (-(-w.seqlen // cs)) * per_sub
     per_chunk = {
         "F1": 2 * C * C * (3 * dk + 2 * dv) + 6 * C * dk * dv + C ** 3 / 3,
         "F1A": 2 * C * C * (dk + dv) + 4 * C * dk * dv,
         "F2": 4 * C * C * dk + 6 * C * dk * dv + 2 * C * C * dv + C * C * dv,
         "F2A": 2 * C * C * (dk + dv) + 4 * C * dk * dv,
+        "F3": 2 * C * C * (3 * dk + 2 * dv) + 6 * C * dk * dv + C ** 3 / 3,
+        "F3A": 2 * C * C * (dk + dv) + 4 * C * dk * dv,
     }[variant]
     nch = -(-w.seqlen // C)
     return w.batch * w.heads * nch * per_chunk
 
 
-def cpu_baseline(w, variant, budget_s=20.0):
+DECODE = dict(batch=256, heads=16, d=128)   # the long-context workload's decode step
+
+
+def bench_decode(args):
+    """One falcon_recurrent_step over batch 256 x 16 heads x 128x128 fp32 states
+    (bf16 q/k/v/o): HBM-bound, the state is read and written once."""
+    import torch
+    import workloads as W
+    from recurrent_sequence_models_amd import recurrent_step
+    B, H, d = DECODE["batch"], DECODE["heads"], DECODE["d"]
+    dev = torch.device("cuda:0")
+    bw = args.window if args.variant in ("F3", "F3A") else 1
+    sets = []
+    for i in range(3):
+        inp = W.make_decode_inputs(B, H, d, d, args.variant, seed=505 + i, window=bw, dtype="bf16")
+        dd = {n: torch.from_numpy(a).to(dev) for n, a in inp.items()}
+        for n in ("q", "k", "v"):
+            dd[n] = dd[n].to(torch.bfloat16).contiguous()
+        sets.append(dd)
+    stream = torch.cuda.current_stream()
+
+    def call(dd):
+        recurrent_step(args.variant, dd["q"], dd["k"], dd["v"], dd["beta"], dd["log_lambda"], dd,
+                       window=bw, stream=stream)
+
+    for i in range(args.warmup):
+        call(sets[i % 3])
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        call(sets[i % 3])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_s = sum(a.elapsed_time(b) for a, b in ev) / K / 1e3
+    per_state = 2 * d * d * 4 + 2 * d * 4 + (2 * d + 2 * d) * 2 + 8 + (2 * (bw - 1) * 2 * d * 4 if bw > 1 else 0)
+    nbytes = B * H * per_state
+    ach = nbytes / kern_s / 1e9
+    return {
+        "metric": "decode steps/sec (batch 256 x 16 heads x 128x128 fp32 states)",
+        "value": round(B / (wall / K), 1), "unit": "sequences/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"Falcon-{args.variant[1:]} recurrent step, B{B} H{H} d{d}, fp32 state, bf16 q/k/v/o",
+                   "variant": args.variant, "window": bw},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "step_kernel",
+                     "kernel_us": {"mean": round(kern_s * 1e6, 2)}, "alg_bytes": nbytes},
+    }
+
+
+KERNEL_SOURCES = ("falcon_fwd_pipe.hip", "mfma_frag.h", "falcon_kernels.h")
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed counter record, or None when the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "recurrent_sequence_models_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return round(rec["bytes_per_launch"]) if h.hexdigest() == rec["source_sha256"] else None
+
+
+def cpu_baseline(w, variant, window=1, budget_s=20.0):
     """Time the fp64 oracle (as it stands) on a prefix of the same workload, on
     one host core; scaled to tokens/s of the full batch."""
     import numpy as np
@@ -66,11 +147,11 @@ def cpu_baseline(w, variant, budget_s=20.0):
     # calibrate on a short prefix, then run a prefix sized for the time budget
     t_probe = 32
     t0 = time.perf_counter()
-    oracle.recurrent(variant, **{n: a[:, :t_probe] for n, a in inp.items()})
+    oracle.recurrent(variant, **{n: a[:, :t_probe] for n, a in inp.items()}, window=window)
     per_step = (time.perf_counter() - t0) / t_probe
     T_s = int(max(t_probe, min(w.seqlen, budget_s / max(per_step, 1e-9))))
     t0 = time.perf_counter()
-    oracle.recurrent(variant, **{n: a[:, :T_s] for n, a in inp.items()})
+    oracle.recurrent(variant, **{n: a[:, :T_s] for n, a in inp.items()}, window=window)
     dt = time.perf_counter() - t0
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
@@ -86,6 +167,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="layer130m")
     ap.add_argument("--variant", default="F1")
+    ap.add_argument("--window", type=int, default=4, help="Falcon-3/3A window (pairs)")
+    ap.add_argument("--decode", action="store_true", help="time the single-token step instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter calibration)")
@@ -96,12 +179,17 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.decode:
+        print(json.dumps(bench_decode(args)), flush=True)
+        return
+
     import torch
     import workloads as W
     from recurrent_sequence_models_amd import chunk_fwd, new_state
 
     w = W.WORKLOADS[args.workload]
     variant = args.variant
+    window = args.window if variant in ("F3", "F3A") else 1
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
@@ -113,13 +201,13 @@ def main():
         for n in ("q", "k", "v"):
             d[n] = d[n].to(tdt).contiguous()
         d["o"] = torch.empty(w.batch, w.seqlen, w.heads, w.dv, dtype=tdt, device=dev)
-        d["final"] = new_state(w.batch, w.heads, w.dk, w.dv, device=dev)
+        d["final"] = new_state(w.batch, w.heads, w.dk, w.dv, window=window, device=dev)
         sets.append(d)
     del inp
     stream = torch.cuda.current_stream()
 
     def call(d):
-        chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk,
+        chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk, window=window,
                   final=d["final"], out=d["o"], stream=stream)
 
     for i in range(args.warmup):
@@ -147,8 +235,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    nbytes = alg_bytes(w, variant)
-    flops = ref_flops(w, variant)
+    nbytes = alg_bytes(w, variant) + (w.batch * w.heads * (window - 1) * (w.dk + w.dv) * 4 if window > 1 else 0)
+    flops = ref_flops(w, variant, window)
     achieved = nbytes / avg_kernel_s / 1e9
     mfma_tfs = flops / avg_kernel_s / 1e12
     bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFS * 1e12) else "mfma"
@@ -158,8 +246,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
-    roof["traffic"] = None
-    roof["kernel"] = "chunk_fwd_rows"
+    roof["traffic"] = measured_traffic(f"chunk_fwd_pipe {variant} {w.name}")
+    roof["kernel"] = ("chunk_fwd_window" if window > 1 else
+                      "chunk_fwd_pipe" if w.dk <= 64 else "chunk_fwd_rows")
     roof["kernel_us"] = {"mean": round(avg_kernel_s * 1e6, 2), "p10": round(kern_ms[K // 10] * 1e3, 2),
                          "p50": round(kern_ms[K // 2] * 1e3, 2), "p90": round(kern_ms[(9 * K) // 10] * 1e3, 2)}
     roof["alg_bytes"] = nbytes
@@ -176,13 +265,14 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": f"Falcon-{variant[1:]} chunked forward, {w.name}: B{w.batch} H{w.heads} "
-                               f"T{w.seqlen} d{w.dk} chunk {w.chunk}, {w.dtype} q/k/v/o, fp32 state",
+                               f"T{w.seqlen} d{w.dk} chunk {w.chunk}" + (f" window {window}" if window > 1 else "")
+                               + f", {w.dtype} q/k/v/o, fp32 state",
                    "variant": variant, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
-                   "head_dim": w.dk, "chunk": w.chunk},
+                   "head_dim": w.dk, "chunk": w.chunk, "window": window},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, variant)
+        line["cpu_baseline"] = cpu_baseline(w, variant, window)
     print(json.dumps(line), flush=True)
 
 
