@@ -11,22 +11,27 @@
 // One workgroup per sequence (b, h), D/16 + 4 waves:
 //   consumer waves (one per 16 value channels) keep S^T in registers and, for
 //     chunk c, compute X S0^T, Q^ S0^T, the residuals E (blocked solve), the
-//     outputs and the state update.  They read their values (and Falcon-2's
-//     per-channel gains) straight from HBM in MFMA fragment layout, one chunk
-//     ahead.
+//     outputs and the state update;
 //   producer waves, in the same iteration, build the key-side tiles of chunk
 //     c+1 (decayed Gram A with the step folded in, scores P, diagonal-block
-//     inverses T_pp), stage the normalised keys/queries of chunk c+2 in LDS and
-//     prefetch the raw inputs of chunk c+3 into registers.
+//     inverses T_pp), stage the raw keys / queries / values of chunk c+2 in LDS
+//     and prefetch those of chunk c+3 into registers.
 // One workgroup barrier per chunk.  Input tiles are triple-buffered, key-side
-// tiles double-buffered.  Every k axis an MFMA reduces over is stored permuted
-// in LDS (kperm) so that one 16-byte read fills a 16x16x32 operand.
+// tiles double-buffered.
 //
-// Diagonal blocks: T_pp = (I + N)^{-1} with N strictly lower 16x16, and
-// Falcon-2's per-channel systems (I + A_pp diag(eta_c)) e = r, are both solved
-// by a block-Jacobi sweep over 4x4 sub-blocks: each lane group solves its own
-// 4 rows exactly, and the coupling between sub-blocks (strictly block-lower,
-// hence nilpotent) is one 16x16 MFMA per sweep; three sweeps are exact.
+// Operands are the raw (unnormalised) inputs: the feature map phi only scales
+// rows, so its factors 1/sqrt(|k|^2 + eps) and 1/sqrt(|q|^2 + eps) are folded
+// into the per-row decay / output / state factors and into the Gram and score
+// tiles.  The producers compute the key-side tiles transposed, so each lane's
+// MFMA result is exactly the consumer's A-operand fragment and is stored
+// fragment-native (8 or 16 bytes per lane, no bank conflicts).  The consumers
+// read X^T and the values in fragment layout with the transposing LDS read.
+//
+// Diagonal blocks: T_pp = (I + N)^{-1} (N strictly lower 16x16) and Falcon-2's
+// per-channel systems (I + A_pp diag(eta_c)) e = r are solved by block-Jacobi
+// sweeps over 4x4 sub-blocks: each lane group solves its own 4 rows or columns
+// exactly, and the coupling between sub-blocks (strictly block-lower, hence
+// nilpotent) is one 16x16 MFMA per sweep; three sweeps are exact.
 #include "falcon_kernels.h"
 #include "mfma_frag.h"
 
@@ -36,8 +41,24 @@ namespace {
 
 enum { V_F1 = 1, V_F1A = 2, V_F2 = 3, V_F2A = 4 };
 
-// gate arrays of an input slot
-enum { G_LC = 0, G_LM, G_XN2, G_BETA, G_GAM, G_EL, G_ETA, G_CST, G_N };
+// per-row arrays of an input slot
+enum {
+  G_LC = 0,   // L_i, chunk-local inclusive log-decay sum
+  G_LM,       // L_{i-1}
+  G_XN2,      // |x_i|^2 (normalised key)
+  G_BETA,     // beta_i (scalar-step variants)
+  G_IK,       // 1/sqrt(|k|^2 + eps) of the raw key in row i of X
+  G_IQ,       // 1/sqrt(|q|^2 + eps)
+  G_GAM,      // e^{L_{i-1}} * IK_i           (consumers)
+  G_EL,       // e^{L_i} * IQ_i               (consumers)
+  G_ETA,      // eta_i (F1/F1A) or 1/(eps + |x_i|^2) (F2/F2A)
+  G_CST,      // e^{L_last - L_i} * IK_i * (eta_i for F1/F1A)
+  G_N
+};
+
+__device__ __forceinline__ float safe_rsqrt(float s) { return s > 0.f ? rsqrtf(s) : 0.f; }
+__device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
 
 __device__ __forceinline__ void unpack(const uint4 &u, __bf16, float *out) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -51,9 +72,6 @@ __device__ __forceinline__ void unpack(const uint4 &u, float, float *out) {
   out[0] = __uint_as_float(u.x); out[1] = __uint_as_float(u.y);
   out[2] = __uint_as_float(u.z); out[3] = __uint_as_float(u.w);
 }
-__device__ __forceinline__ float safe_rsqrt(float s) { return s > 0.f ? rsqrtf(s) : 0.f; }
-__device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
-__device__ __forceinline__ float to_f(float x) { return x; }
 
 // Completes this wave's outstanding LDS operations, so that values one lane wrote
 // are visible to the other lanes of the same wave; also a compiler barrier.
@@ -90,33 +108,48 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   return x;
 }
 
+// A-layout fragment of the transposed 16x16 block of a row-major matrix M:
+// rows r0..r0+15 of M are the k axis, columns c0..c0+15 (given as the 4-column
+// groups' physical offsets by `col4`) the M axis.  Lane (g, c) receives
+// M[r0 + 4g + m][c0 + c], m = 0..3.
+template <typename ColFn>
+__device__ __forceinline__ bf4 ldT(const __bf16 *M, int ld, int r0, ColFn col4, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  return ldtr(M + (r0 + 4 * g + (j >> 2)) * ld + col4(j & 3));
+}
+template <typename ColFn>
+__device__ __forceinline__ f4 ldT(const float *M, int ld, int r0, ColFn col4, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const int col = col4(c >> 2) + (c & 3);
+  f4 r;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) r[m] = M[(r0 + 4 * g + m) * ld + col];
+  return r;
+}
+
 template <int VAR, typename IT, int D, int C>
 struct Pipe {
   static constexpr bool PERCH = (VAR == V_F2 || VAR == V_F2A);
   static constexpr bool DELTA = (VAR == V_F1 || VAR == V_F2);
   static constexpr int NB = C / 16, NA = D / 16;
+  static constexpr int SP = NB > 1 ? NB / 2 : 1;            // fragment pairs per tile row
   static constexpr int NCW = D / 16, NPW = 4, NT = 64 * (NCW + NPW);
   static constexpr int NPT = 64 * NPW;                       // producer threads
   static constexpr int PADE = 16 / (int)sizeof(IT);          // elements in 16 bytes
-  static constexpr int LX = D + PADE;                        // X, Q rows (k = dk, permuted)
-  static constexpr int LT = C + PADE;                        // XT, Ao, P rows (k = chunk row)
-  static constexpr int LTB = 16 + PADE;                      // T_pp / inner-block rows
+  static constexpr int LX = D + PADE;                        // X, Q rows (dk permuted), V rows
   static constexpr int LO = 16 + PADE;                       // output staging rows
   static constexpr int VEC = PADE;
   static constexpr int TPR = D / VEC;                        // producer threads per input row
   static constexpr int RPP = NPT / TPR;                      // rows per producer pass
   static constexpr int NPASS = (C + RPP - 1) / RPP;
   static constexpr int NOFF = NB * (NB - 1) / 2, NPB = NB * (NB + 1) / 2;
+  static constexpr int FRAG = 64 * 8;                        // elements of one fragment pair
   static constexpr size_t lds_bytes() {
-    return sizeof(IT) * (3 * (2 * C * LX + D * LT) + 2 * (2 * C * LT + NB * 16 * LTB) + NCW * C * LO) +
-           4 * (3 * G_N * C + 3 + (PERCH ? 2 * NB * 272 : 0) + (VAR == V_F1 ? NPW * 272 : 0) + 2 * D + 2);
+    return sizeof(IT) * (3 * 3 * C * LX + 2 * (2 * NB * SP * FRAG + NB * 64 * 4) + NCW * C * LO) +
+           4 * (3 * G_N * C + 3 + (PERCH ? 2 * NB * 272 : 0) + NPW * 272 + 2 * D + 4);
   }
   static constexpr bool fits() { return lds_bytes() + 256 <= 160 * 1024; }
 };
-
-// position of chunk-row k in a row whose k axis is a chunk (permuted when C >= 32)
-template <int C>
-__device__ __forceinline__ int kc(int k) { return (C % 32 == 0) ? kperm(k) : k; }
 
 template <int VAR, typename IT, int D, int C>
 __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
@@ -124,26 +157,25 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
   using OpT = IT;
   using Frag = typename Op<OpT>::frag;
   using Pr = Pair<OpT>;
-  constexpr int NB = P::NB, NA = P::NA, NCW = P::NCW, NPW = P::NPW;
-  constexpr int LX = P::LX, LT = P::LT, LTB = P::LTB, VEC = P::VEC, TPR = P::TPR, RPP = P::RPP, NPASS = P::NPASS;
+  constexpr int NB = P::NB, NA = P::NA, NCW = P::NCW, NPW = P::NPW, SP = P::SP;
+  constexpr int LX = P::LX, VEC = P::VEC, TPR = P::TPR, RPP = P::RPP, NPASS = P::NPASS;
   constexpr bool PERCH = P::PERCH, DELTA = P::DELTA;
 
-  __shared__ __attribute__((aligned(16))) OpT sX[3][C * LX];      // x_i = phi(k_{i-1}), dk permuted
-  __shared__ __attribute__((aligned(16))) OpT sQ[3][C * LX];      // q^_i, dk permuted
-  __shared__ __attribute__((aligned(16))) OpT sXT[3][D * LT];     // X^T, chunk row permuted
+  __shared__ __attribute__((aligned(16))) OpT sX[3][C * LX];      // raw x_i = k_{i-1}, dk permuted
+  __shared__ __attribute__((aligned(16))) OpT sQ[3][C * LX];      // raw q_i, dk permuted
+  __shared__ __attribute__((aligned(16))) IT sV[3][C * LX];       // raw v_i, natural channel order
   __shared__ __attribute__((aligned(16))) float sG[3][G_N * C];
   __shared__ float sLam[3];
-  __shared__ __attribute__((aligned(16))) OpT sAo[2][C * LT];     // strictly-lower blocks of A (k permuted)
-  __shared__ __attribute__((aligned(16))) OpT sP[2][C * LT];      // lower blocks of P (k permuted)
-  __shared__ __attribute__((aligned(16))) OpT sTb[2][NB * 16 * LTB];  // F1: T_pp; F2: A_pp minus its 4x4 diagonal
-  __shared__ float sAd2[PERCH ? 2 : 1][PERCH ? NB * 272 : 1];     // F2: diagonal blocks of A, fp32
-  __shared__ float sAdT[VAR == V_F1 ? NPW : 1][VAR == V_F1 ? 272 : 1];  // F1: producer scratch
-  __shared__ float sCarry[2][D];
-  __shared__ float sCarryN2[2];
-  __shared__ __attribute__((aligned(16))) IT sOst[NCW][C * P::LO];   // consumer output staging
+  __shared__ __attribute__((aligned(16))) OpT sAo[2][NB * SP * P::FRAG];  // A_pq (q < p), fragment pairs
+  __shared__ __attribute__((aligned(16))) OpT sP[2][NB * SP * P::FRAG];   // P_pq (q <= p), fragment pairs
+  __shared__ __attribute__((aligned(16))) OpT sTb[2][NB * 64 * 4];        // F1: T_pp; F2: A_pp off its 4x4 diagonal
+  __shared__ float sAd2[PERCH ? 2 : 1][PERCH ? NB * 272 : 1];             // F2: diagonal blocks of A (C-layout)
+  __shared__ float sNd[NPW][272];                                          // producer scratch
+  __shared__ __attribute__((aligned(16))) OpT sCarry[2][D];               // raw key carried to the next chunk
+  __shared__ float sCarryIK[2], sCarryXN2[2];
+  __shared__ __attribute__((aligned(16))) IT sOst[NCW][C * P::LO];        // consumer output staging
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, cl = lane & 15;
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int T = a.T, H = a.H, NC = a.nchunks;
@@ -157,8 +189,11 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
   const IT *vp = static_cast<const IT *>(a.v);
   IT *op = static_cast<IT *>(a.o);
 
+  // fragment-native offset of tile (p, q) of a pair buffer; pairs are tiles (2s, 2s+1)
+  auto fragoff = [&](int p, int q) { return ((p * SP + (q >> 1)) * 64 + lane) * 8 + (q & 1) * 4; };
+
   // ================= producers =================
-  uint4 rk[NPASS], rq[NPASS];              // raw key / query rows of one chunk
+  uint4 rk[NPASS], rq[NPASS], rv[NPASS];   // raw key / query / value rows of one chunk
   float rg = 0.f, rb = 0.f;                // raw gate of row `lane` (producer wave NPW-1)
 
   auto prefetch = [&](int c) {             // global -> registers, chunk c
@@ -170,6 +205,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
       const size_t row = ((size_t)(b * T + t) * H + h) * D + part * VEC;
       rk[ps] = ok ? *reinterpret_cast<const uint4 *>(kp + row) : uint4{0, 0, 0, 0};
       rq[ps] = ok ? *reinterpret_cast<const uint4 *>(qp + row) : uint4{0, 0, 0, 0};
+      rv[ps] = ok ? *reinterpret_cast<const uint4 *>(vp + row) : uint4{0, 0, 0, 0};
     }
     if (pw == NPW - 1) {
       const int t = c0 + lane;
@@ -179,29 +215,28 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     }
   };
 
-  // write 4 consecutive logical columns starting at k0 (multiple of 4) of a dk-permuted row
-  auto put4 = [&](OpT *row, int k0, const float *v) {
-    OpT *dst = row + kperm(k0);
-    if constexpr (sizeof(OpT) == 2) {
-      bf4 w;
-      w[0] = (__bf16)v[0]; w[1] = (__bf16)v[1]; w[2] = (__bf16)v[2]; w[3] = (__bf16)v[3];
-      *reinterpret_cast<bf4 *>(dst) = w;
+  // store VEC raw elements (one 16-byte vector) of logical columns k0..k0+VEC-1 in a dk-permuted row
+  auto put_perm = [&](OpT *row, int k0, const uint4 &u) {
+    if constexpr (sizeof(OpT) == 2) {   // 8 elements = two groups of 4, each contiguous after kperm
+      *reinterpret_cast<uint2 *>(row + kperm(k0)) = uint2{u.x, u.y};
+      *reinterpret_cast<uint2 *>(row + kperm(k0 + 4)) = uint2{u.z, u.w};
     } else {
-      *reinterpret_cast<f4 *>(dst) = f4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<uint4 *>(row + kperm(k0)) = u;
     }
   };
 
-  auto stage = [&](int c) {                // registers -> normalised LDS tiles of chunk c
+  auto stage = [&](int c) {                // registers -> raw LDS tiles of chunk c, row norms
     const int s = c % 3;
     const int cin = (c + 1) & 1, cprev = c & 1;   // carry written for chunk c+1, read from chunk c-1
-    OpT *X = sX[s], *Q = sQ[s], *XT = sXT[s];
+    OpT *X = sX[s], *Q = sQ[s];
+    IT *V = sV[s];
     float *G = sG[s];
-    for (int e = ptid; e < D; e += P::NPT) {
-      const float x = sCarry[cprev][e];
-      X[kperm(e)] = (OpT)x;
-      XT[e * LT + kc<C>(0)] = (OpT)x;
+    for (int e = ptid; e < D / 4; e += P::NPT)
+      *reinterpret_cast<Frag *>(X + kperm(4 * e)) = *reinterpret_cast<const Frag *>(&sCarry[cprev][4 * e]);
+    if (ptid == 0) {
+      G[G_IK * C] = sCarryIK[cprev];
+      G[G_XN2 * C] = sCarryXN2[cprev];
     }
-    if (ptid == 0) G[G_XN2 * C + 0] = sCarryN2[cprev];
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int r = ps * RPP + ptid / TPR, part = ptid % TPR;
@@ -214,22 +249,23 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
       sk = group_sum<TPR>(sk);
       sq = group_sum<TPR>(sq);
       const float ik = safe_rsqrt(sk + a.eps_phi), iq = safe_rsqrt(sq + a.eps_phi);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) { xv[e] *= ik; qv[e] *= iq; }
       if (r + 1 < C) {
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4) put4(X + (r + 1) * LX, part * VEC + e, xv + e);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) XT[(part * VEC + e) * LT + kc<C>(r + 1)] = (OpT)xv[e];
-        if (part == 0) G[G_XN2 * C + r + 1] = sk * ik * ik;
+        put_perm(X + (r + 1) * LX, part * VEC, rk[ps]);
+        if (part == 0) {
+          G[G_IK * C + r + 1] = ik;
+          G[G_XN2 * C + r + 1] = sk * ik * ik;
+        }
       } else if (r + 1 == C) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) sCarry[cin][part * VEC + e] = xv[e];
-        if (part == 0) sCarryN2[cin] = sk * ik * ik;
+        *reinterpret_cast<uint4 *>(&sCarry[cin][part * VEC]) = rk[ps];
+        if (part == 0) {
+          sCarryIK[cin] = ik;
+          sCarryXN2[cin] = sk * ik * ik;
+        }
       }
       if (r < C) {
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4) put4(Q + r * LX, part * VEC + e, qv + e);
+        put_perm(Q + r * LX, part * VEC, rq[ps]);
+        *reinterpret_cast<uint4 *>(V + r * LX + part * VEC) = rv[ps];
+        if (part == 0) G[G_IQ * C + r] = iq;
       }
     }
     if (pw == NPW - 1) {   // clamp in log space, chunk-local inclusive scan
@@ -248,66 +284,84 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     const int s = c % 3, ds = c & 1;
     const OpT *X = sX[s], *Q = sQ[s];
     float *G = sG[s];
-    auto wcol = [&](int col) { return PERCH ? 1.f : G[G_BETA * C + col] / (a.eps_eta + G[G_XN2 * C + col]); };
-    auto gram = [&](const OpT *Am, int p, int q) {   // 16x16 block (p, q) of Am X^T
+    // 16x16 block of (rows of block qa of Am) . (rows of block pb of Bm)^T, raw operands:
+    // lane (g, c) gets <Am_{16 qa + 4g + i}, Bm_{16 pb + c}>.
+    auto gram = [&](const OpT *Am, int qa, const OpT *Bm, int pb) {
       f4 acc = zero4();
 #pragma unroll
       for (int a2 = 0; a2 < NA / 2; ++a2)
-        mmap(acc, ldp(Am + (16 * p + cl) * LX + 32 * a2 + 8 * g4), ldp(X + (16 * q + cl) * LX + 32 * a2 + 8 * g4));
+        mmap(acc, ldp(Am + (16 * qa + cl) * LX + 32 * a2 + 8 * g4), ldp(Bm + (16 * pb + cl) * LX + 32 * a2 + 8 * g4));
       return acc;
     };
-    // diagonal Gram block pw (F1: T_pp; F2: A_pp)
+    // column factors of a block of columns: IK_j * (eta_j or 1)
+    auto colfac = [&](int j0) {
+      const f4 ik = *reinterpret_cast<const f4 *>(G + G_IK * C + j0);
+      if (PERCH) return ik;
+      const f4 bt = *reinterpret_cast<const f4 *>(G + G_BETA * C + j0);
+      const f4 xn = *reinterpret_cast<const f4 *>(G + G_XN2 * C + j0);
+      f4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = ik[i] * bt[i] / (a.eps_eta + xn[i]);
+      return r;
+    };
+    // diagonal block pw: F1 -> T_pp (A-layout), F2 -> A_pp (fp32, C-layout) and A_pp off its 4x4 diagonal
     if (DELTA && pw < NB) {
-      const int p = pw;
-      const f4 acc = gram(X, p, p);
-      const int col = 16 * p + cl;
-      const float Lcol = G[G_LC * C + col], wc = wcol(col);
-      const f4 Lmr = *reinterpret_cast<const f4 *>(G + G_LM * C + 16 * p + 4 * g4);
-      f4 N;   // C-layout: N[4 g4 + i][cl] of the diagonal block (A with the step folded in for F1)
+      const int p = pw, r0 = 4 * g4;
+      const f4 acc = gram(X, p, X, p);     // symmetric: <x_{16p+4g+i}, x_{16p+c}>
+      const f4 cf = colfac(16 * p + r0);   // factors of columns 16p + 4g + i
+      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + G_LC * C + 16 * p + r0);
+      const f4 Lm4 = *reinterpret_cast<const f4 *>(G + G_LM * C + 16 * p + r0);
+      const float Lc1 = G[G_LC * C + 16 * p + cl], Lm1 = G[G_LM * C + 16 * p + cl];
+      const float ik1 = G[G_IK * C + 16 * p + cl];
+      const float cf1 = PERCH ? ik1 : ik1 * G[G_BETA * C + 16 * p + cl] / (a.eps_eta + G[G_XN2 * C + 16 * p + cl]);
+      f4 NA4, NC4;   // N[16p+c][16p+4g+i] (A-layout) and N[16p+4g+i][16p+c] (C-layout)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float v = acc[i] * __expf(Lmr[i] - Lcol) * wc;
-        N[i] = (cl < 4 * g4 + i) ? v : 0.f;
+        const float va = acc[i] * __expf(Lm1 - Lc4[i]) * ik1 * cf[i];
+        const float vc = acc[i] * __expf(Lm4[i] - Lc1) * G[G_IK * C + 16 * p + r0 + i] * cf1;
+        NA4[i] = (r0 + i < cl) ? va : 0.f;
+        NC4[i] = (cl < r0 + i) ? vc : 0.f;
       }
-      const int r0 = 4 * g4;
-      if (VAR == V_F1) {
-        // T_pp = (I + N)^{-1}: T <- (I + N_d)^{-1} (I - N_o T), exact after 3 sweeps.
-        float *Ad = sAdT[pw];
+      if constexpr (VAR == V_F1) {
+        // row-oriented: T (I + N) = I, so T <- (I - T N_o)(I + N_d)^{-1}, exact after 3 sweeps;
+        // Y holds T in A-layout (row c, columns 4g..4g+3 of the block).
+        float *Nd = sNd[pw];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Ad[(r0 + i) * 17 + cl] = N[i];
+        for (int i = 0; i < 4; ++i) Nd[cl * 17 + r0 + i] = NA4[i];   // Nd[row][col]
         wave_lds_sync();
-        f4 No;   // A-layout of N without its 4x4 diagonal sub-blocks: N[cl][4 g4 + i]
+        const float n10 = Nd[(r0 + 1) * 17 + r0], n20 = Nd[(r0 + 2) * 17 + r0], n21 = Nd[(r0 + 2) * 17 + r0 + 1];
+        const float n30 = Nd[(r0 + 3) * 17 + r0], n31 = Nd[(r0 + 3) * 17 + r0 + 1], n32 = Nd[(r0 + 3) * 17 + r0 + 2];
+        f4 NoC;   // C-layout of N without its 4x4 diagonal sub-blocks
 #pragma unroll
-        for (int i = 0; i < 4; ++i) No[i] = ((cl >> 2) == g4) ? 0.f : Ad[cl * 17 + r0 + i];
-        const float n10 = Ad[(r0 + 1) * 17 + r0], n20 = Ad[(r0 + 2) * 17 + r0], n21 = Ad[(r0 + 2) * 17 + r0 + 1];
-        const float n30 = Ad[(r0 + 3) * 17 + r0], n31 = Ad[(r0 + 3) * 17 + r0 + 1], n32 = Ad[(r0 + 3) * 17 + r0 + 2];
+        for (int i = 0; i < 4; ++i) NoC[i] = ((cl >> 2) == g4) ? 0.f : NC4[i];
         f4 Z, Y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) Z[i] = (r0 + i == cl) ? 1.f : 0.f;
-        auto local = [&](const f4 &z) {
-          Y[0] = z[0];
-          Y[1] = z[1] - n10 * Y[0];
-          Y[2] = z[2] - n20 * Y[0] - n21 * Y[1];
-          Y[3] = z[3] - n30 * Y[0] - n31 * Y[1] - n32 * Y[2];
+        auto local = [&](const f4 &w) {     // t (I + N_gg) = w, t a row of 4
+          Y[3] = w[3];
+          Y[2] = w[2] - Y[3] * n32;
+          Y[1] = w[1] - Y[2] * n21 - Y[3] * n31;
+          Y[0] = w[0] - Y[1] * n10 - Y[2] * n20 - Y[3] * n30;
         };
         local(Z);
 #pragma unroll
         for (int it = 0; it < 3; ++it) {
           f4 cpl = zero4();
-          mma16(cpl, No, Y);     // fp32 MFMA
+          mma16(cpl, NoC, Y);   // fp32: C-layout of N_o^T Y^T = A-layout of Y N_o
           local(Z - cpl);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sTb[ds][(p * 16 + r0 + i) * LTB + cl] = (OpT)Y[i];
-      } else {  // F2: full diagonal block (fp32) and its part outside the 4x4 diagonal sub-blocks
+        *reinterpret_cast<Frag *>(&sTb[ds][(p * 64 + lane) * 4]) = cvt<OpT>(Y);
+      } else {
+        f4 NoA;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sAd2[ds][p * 272 + (r0 + i) * 17 + cl] = N[i];
-          sTb[ds][(p * 16 + r0 + i) * LTB + cl] = (OpT)((cl >> 2) == g4 ? 0.f : N[i]);
+          sAd2[ds][p * 272 + (r0 + i) * 17 + cl] = NC4[i];
+          NoA[i] = ((cl >> 2) == g4) ? 0.f : NA4[i];
         }
+        *reinterpret_cast<Frag *>(&sTb[ds][(p * 64 + lane) * 4]) = cvt<OpT>(NoA);
       }
     }
-    // off-diagonal A blocks and score blocks, a static round robin over producer waves
+    // off-diagonal A blocks and score blocks, transposed, a static round robin over producer waves
     constexpr int NG = DELTA ? P::NOFF : 0;
     constexpr int NJOB = NG + P::NPB;
 #pragma unroll
@@ -326,58 +380,59 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
           while (p * (p + 1) / 2 <= pj) ++p;
           q = pj - p * (p - 1) / 2;
         }
-        const f4 acc = gram(isP ? Q : X, p, q);
-        const int col = 16 * q + cl;
-        const float Lcol = G[G_LC * C + col], wc = wcol(col);
-        // decay to the row: e^{L_i - L_j} for scores, e^{L_{i-1} - L_j} for the Gram
-        const f4 Lr = *reinterpret_cast<const f4 *>(G + (isP ? G_LC : G_LM) * C + 16 * p + 4 * g4);
-        OpT *dst = (isP ? sP[ds] : sAo[ds]) + kc<C>(col);
+        // lane (g, c): element (row 16p + c, col 16q + 4g + i)
+        const f4 acc = gram(X, q, isP ? Q : X, p);
+        const f4 cf = colfac(16 * q + 4 * g4);
+        const f4 Lc4 = *reinterpret_cast<const f4 *>(G + G_LC * C + 16 * q + 4 * g4);
+        const int row = 16 * p + cl;
+        const float Lrow = G[(isP ? G_LC : G_LM) * C + row];
+        const float rf = G[(isP ? G_IQ : G_IK) * C + row];
+        f4 val;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 16 * p + 4 * g4 + i;
-          const float v = acc[i] * __expf(Lr[i] - Lcol) * wc;
-          dst[row * LT] = (OpT)((p > q || cl <= 4 * g4 + i) ? v : 0.f);   // Gram blocks have q < p
+          const float v = acc[i] * __expf(Lrow - Lc4[i]) * rf * cf[i];
+          val[i] = (p > q || 4 * g4 + i <= cl) ? v : 0.f;   // Gram blocks have q < p
         }
+        *reinterpret_cast<Frag *>(&(isP ? sP[ds] : sAo[ds])[fragoff(p, q)]) = cvt<OpT>(val);
       }
     }
     // per-row factors the consumers use
     if (pw == NPW - 1 && lane < C) {
       const float L = G[G_LC * C + lane], Lm = G[G_LM * C + lane];
       const float Llast = G[G_LC * C + C - 1];
+      const float ik = G[G_IK * C + lane];
       const float inv = 1.f / (a.eps_eta + G[G_XN2 * C + lane]);
       const float eta = PERCH ? inv : G[G_BETA * C + lane] * inv;
-      G[G_GAM * C + lane] = __expf(Lm);
-      G[G_EL * C + lane] = __expf(L);
+      G[G_GAM * C + lane] = __expf(Lm) * ik;
+      G[G_EL * C + lane] = __expf(L) * G[G_IQ * C + lane];
       G[G_ETA * C + lane] = eta;
-      G[G_CST * C + lane] = __expf(Llast - L) * (PERCH ? 1.f : eta);
+      G[G_CST * C + lane] = __expf(Llast - L) * ik * (PERCH ? 1.f : eta);
       if (lane == 0) sLam[s] = __expf(Llast);
     }
   };
 
   // ================= consumers =================
   f4 sT[NA];                 // S^T of this wave's 16 channels, C-layout per dk block
-  IT rv[NB][4];              // values of the next chunk, C-layout
   float rbeta[NB][4];        // F2/F2A: per-channel gains of the next chunk
   if (consumer) {
 #pragma unroll
     for (int aa = 0; aa < NA; ++aa)
       sT[aa] = a.S0 ? *reinterpret_cast<const f4 *>(a.S0 + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) : zero4();
   }
-  auto prefetch_v = [&](int c) {
+  auto prefetch_beta = [&](int c) {
 #pragma unroll
     for (int p = 0; p < NB; ++p)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = c * C + 16 * p + 4 * g4 + i;
-        const size_t idx = ((size_t)(b * T + t) * H + h) * D + chW;
-        rv[p][i] = (t < T) ? vp[idx] : (IT)0.f;
-        if (PERCH) rbeta[p][i] = (t < T) ? a.beta[idx] : 0.f;
+        rbeta[p][i] = (t < T) ? a.beta[((size_t)(b * T + t) * H + h) * D + chW] : 0.f;
       }
   };
 
   auto consume = [&](int c) {
     const int s = c % 3, ds = c & 1, c0 = c * C;
-    const OpT *X = sX[s], *Q = sQ[s], *XT = sXT[s];
+    const OpT *X = sX[s], *Q = sQ[s];
+    const IT *V = sV[s];
     const float *G = sG[s];
     const OpT *Ao = sAo[ds], *Pm = sP[ds], *Tb = sTb[ds];
     Pr Sp[NA / 2];
@@ -394,23 +449,14 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
         mmap(QS[p], ldp(Q + (16 * p + cl) * LX + 32 * a2 + 8 * g4), Sp[a2]);
       }
     }
-    // A-layout operand of the 16x16 block (row block p, k block q) of a C x C tile
-    auto blk1 = [&](const OpT *M, int p, int q) -> Frag {
-      const int k0 = (C % 32 == 0) ? (32 * (q >> 1) + 8 * g4 + 4 * (q & 1)) : (16 * q + 4 * g4);
-      return ld4(M + (16 * p + cl) * LT + k0);
-    };
-    auto blk2 = [&](const OpT *M, int p, int q) -> Pr {   // k blocks q, q+1 (q even)
-      return ldp(M + (16 * p + cl) * LT + 32 * (q >> 1) + 8 * g4);
-    };
+    auto vcol = [&](int j4) { return 16 * wv + 4 * j4; };
     Frag Eb[NB];
     f4 Ef[NB];
 #pragma unroll
     for (int p = 0; p < NB; ++p) {
-      const f4 gam = *reinterpret_cast<const f4 *>(G + G_GAM * C + 16 * p + 4 * g4);
-      f4 R, eta4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) R[i] = to_f(rv[p][i]);
-      if (DELTA) R -= gam * XS[p];
+      f4 R = to_f4(ldT(V, LX, 16 * p, vcol, lane));   // C-layout values of this wave's channels
+      if (DELTA) R -= *reinterpret_cast<const f4 *>(G + G_GAM * C + 16 * p + 4 * g4) * XS[p];
+      f4 eta4;
       if (PERCH) {
         const f4 inv = *reinterpret_cast<const f4 *>(G + G_ETA * C + 16 * p + 4 * g4);
 #pragma unroll
@@ -419,22 +465,22 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
       if (DELTA) {   // R -= sum_{q<p} A_pq E_q   (E_q = eta (.) E for F2)
         f4 acc = zero4();
 #pragma unroll
-        for (int q = 0; q + 1 < p; q += 2) mmap(acc, blk2(Ao, p, q), mkp(Eb[q], Eb[q + 1]));
-        if (p & 1) mma16(acc, blk1(Ao, p, p - 1), Eb[p - 1]);
+        for (int q = 0; q + 1 < p; q += 2) mmap(acc, ldp(Ao + fragoff(p, q)), mkp(Eb[q], Eb[q + 1]));
+        if (p & 1) mma16(acc, ld4(Ao + fragoff(p, p - 1)), Eb[p - 1]);
         R -= acc;
       }
-      if (VAR == V_F1) {
+      if constexpr (VAR == V_F1) {
         f4 E = zero4();
-        mma16(E, ld4(Tb + (16 * p + cl) * LTB + 4 * g4), cvt<OpT>(R));
+        mma16(E, ld4(Tb + (p * 64 + lane) * 4), cvt<OpT>(R));
         Ef[p] = E;
         Eb[p] = cvt<OpT>(E);
-      } else if (VAR == V_F2) {
+      } else if constexpr (VAR == V_F2) {
         // rows 4g4..4g4+3 of block p: exact 4x4 solves, coupled by A_pp minus its 4x4 diagonal
         const float *Ad = sAd2[ds] + p * 272;
         const int r0 = 4 * g4;
         const float a10 = Ad[(r0 + 1) * 17 + r0], a20 = Ad[(r0 + 2) * 17 + r0], a21 = Ad[(r0 + 2) * 17 + r0 + 1];
         const float a30 = Ad[(r0 + 3) * 17 + r0], a31 = Ad[(r0 + 3) * 17 + r0 + 1], a32 = Ad[(r0 + 3) * 17 + r0 + 2];
-        const Frag Ain = ld4(Tb + (16 * p + cl) * LTB + 4 * g4);
+        const Frag Ain = ld4(Tb + (p * 64 + lane) * 4);
         f4 E, F;
         auto local = [&](const f4 &z) {
           E[0] = z[0];
@@ -455,7 +501,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
         }
         Ef[p] = F;                 // eta (.) E feeds the state update and the outputs
         Eb[p] = cvt<OpT>(F);
-      } else if (VAR == V_F1A) {
+      } else if constexpr (VAR == V_F1A) {
         Ef[p] = R;
         Eb[p] = cvt<OpT>(R);
       } else {
@@ -469,13 +515,12 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     for (int p = 0; p < NB; ++p) {
       f4 O = *reinterpret_cast<const f4 *>(G + G_EL * C + 16 * p + 4 * g4) * QS[p];
 #pragma unroll
-      for (int q = 0; q + 1 <= p; q += 2) mmap(O, blk2(Pm, p, q), mkp(Eb[q], Eb[q + 1]));
-      if (!(p & 1)) mma16(O, blk1(Pm, p, p), Eb[p]);
+      for (int q = 0; q + 1 <= p; q += 2) mmap(O, ldp(Pm + fragoff(p, q)), mkp(Eb[q], Eb[q + 1]));
+      if (!(p & 1)) mma16(O, ld4(Pm + fragoff(p, p)), Eb[p]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sOst[wv][(16 * p + 4 * g4 + i) * P::LO + cl] = (IT)O[i];
     }
     wave_lds_sync();
-    // each lane stores one step's 16 channels of this wave
 #pragma unroll
     for (int r = lane; r < C; r += 64) {
       const int t = c0 + r;
@@ -486,20 +531,21 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
               *reinterpret_cast<const uint4 *>(&sOst[wv][r * P::LO + j * VEC]);
       }
     }
-    // state: S^T <- e^{L_last} S^T + X^T diag(cst) E'
+    // state: S^T <- e^{L_last} S^T + X~^T diag(cst) E'   (X~ raw keys; cst carries their norm)
     Frag CE[NB];
 #pragma unroll
     for (int p = 0; p < NB; ++p) CE[p] = cvt<OpT>(*reinterpret_cast<const f4 *>(G + G_CST * C + 16 * p + 4 * g4) * Ef[p]);
     const float lamtot = sLam[s];
 #pragma unroll
     for (int aa = 0; aa < NA; ++aa) {
+      auto dkcol = [&](int j4) { return kperm(16 * aa + 4 * j4); };
       f4 acc = sT[aa] * lamtot;
       if constexpr (NB == 1) {
-        mma16(acc, ld4(XT + (16 * aa + cl) * LT + 4 * g4), CE[0]);
+        mma16(acc, ldT(X, LX, 0, dkcol, lane), CE[0]);
       } else {
 #pragma unroll
         for (int p = 0; p < NB; p += 2)
-          mmap(acc, ldp(XT + (16 * aa + cl) * LT + 32 * (p >> 1) + 8 * g4), mkp(CE[p], CE[p + 1]));
+          mmap(acc, mkp(ldT(X, LX, 16 * p, dkcol, lane), ldT(X, LX, 16 * p + 16, dkcol, lane)), mkp(CE[p], CE[p + 1]));
       }
       sT[aa] = acc;
     }
@@ -512,18 +558,24 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
 
   // ---------------- prologue ----------------
   if (!consumer) {
-    // the carry slot read by chunk 0 is slot 0 (chunk -1's key = the incoming x_prev)
-    for (int e = ptid; e < D; e += P::NPT) sCarry[0][e] = a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f;
+    // chunk 0's first key is the incoming x_prev (already a feature: factor 1)
+    for (int e = ptid; e < D; e += P::NPT) sCarry[0][e] = (OpT)(a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f);
     prefetch(0);
-  } else {
-    prefetch_v(0);
+  } else if (PERCH) {
+    prefetch_beta(0);
   }
   __syncthreads();
   if (pw == 0) {
     float s = 0.f;
-    for (int e = lane; e < D; e += 64) s += sCarry[0][e] * sCarry[0][e];
+    for (int e = lane; e < D; e += 64) {
+      const float x = a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f;
+      s += x * x;
+    }
     s = group_sum<64>(s);
-    if (lane == 0) sCarryN2[0] = s;
+    if (lane == 0) {
+      sCarryIK[0] = 1.f;
+      sCarryXN2[0] = s;
+    }
   }
   __syncthreads();
   if (!consumer) {
@@ -537,7 +589,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     if (consumer) {
       if (i >= 1) {
         consume(i - 1);
-        if (i < NC) prefetch_v(i);
+        if (PERCH && i < NC) prefetch_beta(i);
       }
     } else {
       if (i + 1 < NC) {

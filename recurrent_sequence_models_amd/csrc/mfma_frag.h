@@ -37,6 +37,8 @@ __device__ __forceinline__ bf4 to_op(const f4 &x, __bf16) {
   return r;
 }
 __device__ __forceinline__ f4 to_op(const f4 &x, float) { return x; }
+__device__ __forceinline__ f4 to_f4(const bf4 &x) { return f4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
+__device__ __forceinline__ f4 to_f4(const f4 &x) { return x; }
 
 template <typename OpT>
 __device__ __forceinline__ typename Op<OpT>::frag cvt(const f4 &x) { return to_op(x, OpT()); }
@@ -97,6 +99,17 @@ __device__ __forceinline__ void mmap(f4 &d, const Pair<__bf16> &a, const Pair<__
 __device__ __forceinline__ void mmap(f4 &d, const Pair<float> &a, const Pair<float> &b) {
   mma16(d, a.lo, b.lo);
   mma16(d, a.hi, b.hi);
+}
+
+// ---- Transposing LDS read (gfx950 ds_read_b64_tr_b16) ---------------------------
+// Within each group of 16 lanes, lane j names 4 consecutive 16-bit elements of
+// row j/4 (columns 4(j%4)..+3) of a 4x16 block; lane c receives column c of that
+// block (its 4 rows).  Pointed at rows r0..r0+3 of a row-major matrix, it yields
+// the A-layout fragment of the transposed 16x4 slice, or the C-layout fragment
+// of a 4x16 slice, without a transposed copy in LDS.
+__device__ __forceinline__ bf4 ldtr(const __bf16 *p) {
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)(p));
+  return __builtin_bit_cast(bf4, v);
 }
 
 }  // namespace falcon
