@@ -32,6 +32,8 @@
 // sweeps over 4x4 sub-blocks: each lane group solves its own 4 rows or columns
 // exactly, and the coupling between sub-blocks (strictly block-lower, hence
 // nilpotent) is one 16x16 MFMA per sweep; three sweeps are exact.
+#include <type_traits>
+
 #include "falcon_kernels.h"
 #include "mfma_frag.h"
 
@@ -45,18 +47,20 @@ enum { V_F1 = 1, V_F1A = 2, V_F2 = 3, V_F2A = 4 };
 enum {
   G_LC = 0,   // L_i, chunk-local inclusive log-decay sum
   G_LM,       // L_{i-1}
-  G_XN2,      // |x_i|^2 (normalised key)
-  G_BETA,     // beta_i (scalar-step variants)
   G_IK,       // 1/sqrt(|k|^2 + eps) of the raw key in row i of X
   G_IQ,       // 1/sqrt(|q|^2 + eps)
+  G_CF,       // column factor of the Gram and score tiles: IK_i * eta_i (F1/F1A) or IK_i (F2/F2A)
+  G_ETA,      // eta_i (F1/F1A) or 1/(eps + |x_i|^2) (F2/F2A)
   G_GAM,      // e^{L_{i-1}} * IK_i           (consumers)
   G_EL,       // e^{L_i} * IQ_i               (consumers)
-  G_ETA,      // eta_i (F1/F1A) or 1/(eps + |x_i|^2) (F2/F2A)
-  G_CST,      // e^{L_last - L_i} * IK_i * (eta_i for F1/F1A)
+  G_CST,      // e^{L_last - L_i} * CF_i      (consumers)
   G_N
 };
 
-__device__ __forceinline__ float safe_rsqrt(float s) { return s > 0.f ? rsqrtf(s) : 0.f; }
+// Hardware reciprocal square root / reciprocal (about 1 ulp); arguments are
+// bounded away from zero and denormals by eps_phi and eps_eta.
+__device__ __forceinline__ float safe_rsqrt(float s) { return s > 0.f ? __builtin_amdgcn_rsqf(s) : 0.f; }
+__device__ __forceinline__ float fast_rcp(float s) { return __builtin_amdgcn_rcpf(s); }
 __device__ __forceinline__ float to_f(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
 
@@ -127,6 +131,57 @@ __device__ __forceinline__ f4 ldT(const float *M, int ld, int r0, ColFn col4, in
   return r;
 }
 
+// Key-side tiles of one chunk, split over the four producer waves.  A wave
+// gets the diagonal block `diag` (T_pp or A_pp, -1 if none) and up to four
+// 16x16 tiles: Gram blocks A_pq (q < p) and score blocks P_pq (q <= p).  The
+// tiles of a wave share few column blocks q, whose key rows are the left MFMA
+// operand, and the diagonal block uses the same rows for both operands.
+struct JobList {
+  int diag, n;
+  int isP[4], p[4], q[4];
+};
+constexpr JobList make_jobs(int nb, bool delta, int w) {
+  JobList J{-1, 0, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  // (isP, p, q) triples per wave
+  int t[4][4][3] = {};
+  int n[4] = {0, 0, 0, 0};
+  int dg[4] = {-1, -1, -1, -1};
+  auto put = [&](int wv, int isP, int p, int q) { t[wv][n[wv]][0] = isP; t[wv][n[wv]][1] = p; t[wv][n[wv]][2] = q; ++n[wv]; };
+  if (nb == 4) {
+    if (delta) {
+      dg[0] = 0; put(0, 0, 1, 0); put(0, 0, 2, 0); put(0, 0, 3, 0); put(0, 1, 0, 0);
+      dg[1] = 3; put(1, 1, 1, 0); put(1, 1, 2, 0); put(1, 1, 3, 0); put(1, 1, 3, 3);
+      dg[2] = 1; put(2, 0, 2, 1); put(2, 0, 3, 1); put(2, 1, 1, 1); put(2, 1, 2, 1);
+      dg[3] = 2; put(3, 1, 3, 1); put(3, 0, 3, 2); put(3, 1, 2, 2); put(3, 1, 3, 2);
+    } else {
+      put(0, 1, 0, 0); put(0, 1, 1, 0); put(0, 1, 2, 0);
+      put(1, 1, 3, 0); put(1, 1, 3, 3);
+      put(2, 1, 1, 1); put(2, 1, 2, 1); put(2, 1, 3, 1);
+      put(3, 1, 2, 2); put(3, 1, 3, 2);
+    }
+  } else if (nb == 2) {
+    if (delta) {
+      dg[0] = 0; put(0, 0, 1, 0);
+      dg[1] = 1; put(1, 1, 1, 1);
+      put(2, 1, 0, 0);
+      put(3, 1, 1, 0);
+    } else {
+      put(0, 1, 0, 0); put(1, 1, 1, 0); put(2, 1, 1, 1);
+    }
+  } else {
+    if (delta) dg[0] = 0;
+    put(1, 1, 0, 0);
+  }
+  J.diag = dg[w];
+  J.n = n[w];
+  for (int j = 0; j < n[w]; ++j) {
+    J.isP[j] = t[w][j][0];
+    J.p[j] = t[w][j][1];
+    J.q[j] = t[w][j][2];
+  }
+  return J;
+}
+
 template <int VAR, typename IT, int D, int C>
 struct Pipe {
   static constexpr bool PERCH = (VAR == V_F2 || VAR == V_F2A);
@@ -146,7 +201,7 @@ struct Pipe {
   static constexpr int FRAG = 64 * 8;                        // elements of one fragment pair
   static constexpr size_t lds_bytes() {
     return sizeof(IT) * (3 * 3 * C * LX + 2 * (2 * NB * SP * FRAG + NB * 64 * 4) + NCW * C * LO) +
-           4 * (3 * G_N * C + 3 + (PERCH ? 2 * NB * 272 : 0) + NPW * 272 + 2 * D + 4);
+           4 * (3 * G_N * C + 3 + (PERCH ? 2 * NB * 272 : 0) + 2 * D + 6);
   }
   static constexpr bool fits() { return lds_bytes() + 256 <= 160 * 1024; }
 };
@@ -170,9 +225,8 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) OpT sP[2][NB * SP * P::FRAG];   // P_pq (q <= p), fragment pairs
   __shared__ __attribute__((aligned(16))) OpT sTb[2][NB * 64 * 4];        // F1: T_pp; F2: A_pp off its 4x4 diagonal
   __shared__ float sAd2[PERCH ? 2 : 1][PERCH ? NB * 272 : 1];             // F2: diagonal blocks of A (C-layout)
-  __shared__ float sNd[NPW][272];                                          // producer scratch
   __shared__ __attribute__((aligned(16))) OpT sCarry[2][D];               // raw key carried to the next chunk
-  __shared__ float sCarryIK[2], sCarryXN2[2];
+  __shared__ float sCarryF[2][3];                                         // its IK, CF, ETA
   __shared__ __attribute__((aligned(16))) IT sOst[NCW][C * P::LO];        // consumer output staging
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -194,25 +248,24 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
 
   // ================= producers =================
   uint4 rk[NPASS], rq[NPASS], rv[NPASS];   // raw key / query / value rows of one chunk
-  float rg = 0.f, rb = 0.f;                // raw gate of row `lane` (producer wave NPW-1)
+  float rb1[NPASS];                        // beta of the row after (the step of x_{r+1} = phi(k_r))
+  float rg = 0.f;                          // raw gate of row `lane` (producer wave NPW-1)
 
-  auto prefetch = [&](int c) {             // global -> registers, chunk c
+  // global -> registers, chunk c.  Rows past the end are clamped to the last
+  // token (always in bounds) and zeroed when staged.
+  auto prefetch = [&](int c) {
     const int c0 = c * C;
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
-      const int r = ps * RPP + ptid / TPR, part = ptid % TPR, t = c0 + r;
-      const bool ok = r < C && t < T;
+      const int r = ps * RPP + ptid / TPR, part = ptid % TPR;
+      const int t = min(c0 + r, T - 1);
       const size_t row = ((size_t)(b * T + t) * H + h) * D + part * VEC;
-      rk[ps] = ok ? *reinterpret_cast<const uint4 *>(kp + row) : uint4{0, 0, 0, 0};
-      rq[ps] = ok ? *reinterpret_cast<const uint4 *>(qp + row) : uint4{0, 0, 0, 0};
-      rv[ps] = ok ? *reinterpret_cast<const uint4 *>(vp + row) : uint4{0, 0, 0, 0};
+      rk[ps] = *reinterpret_cast<const uint4 *>(kp + row);
+      rq[ps] = *reinterpret_cast<const uint4 *>(qp + row);
+      rv[ps] = *reinterpret_cast<const uint4 *>(vp + row);
+      if (!PERCH) rb1[ps] = a.beta[(size_t)(b * T + min(c0 + r + 1, T - 1)) * H + h];
     }
-    if (pw == NPW - 1) {
-      const int t = c0 + lane;
-      const bool ok = lane < C && t < T;
-      rg = ok ? a.g[(size_t)(b * T + t) * H + h] : 0.f;
-      rb = (ok && !PERCH) ? a.beta[(size_t)(b * T + t) * H + h] : 0.f;
-    }
+    if (pw == NPW - 1) rg = a.g[(size_t)(b * T + min(c0 + lane, T - 1)) * H + h];
   };
 
   // store VEC raw elements (one 16-byte vector) of logical columns k0..k0+VEC-1 in a dk-permuted row
@@ -225,8 +278,9 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     }
   };
 
-  auto stage = [&](int c) {                // registers -> raw LDS tiles of chunk c, row norms
-    const int s = c % 3;
+  // registers -> raw LDS tiles of chunk c, with the per-row norms and step factors
+  auto stage = [&](int c) {
+    const int s = c % 3, c0 = c * C;
     const int cin = (c + 1) & 1, cprev = c & 1;   // carry written for chunk c+1, read from chunk c-1
     OpT *X = sX[s], *Q = sQ[s];
     IT *V = sV[s];
@@ -234,103 +288,118 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     for (int e = ptid; e < D / 4; e += P::NPT)
       *reinterpret_cast<Frag *>(X + kperm(4 * e)) = *reinterpret_cast<const Frag *>(&sCarry[cprev][4 * e]);
     if (ptid == 0) {
-      G[G_IK * C] = sCarryIK[cprev];
-      G[G_XN2 * C] = sCarryXN2[cprev];
+      G[G_IK * C] = sCarryF[cprev][0];
+      G[G_CF * C] = sCarryF[cprev][1];
+      G[G_ETA * C] = sCarryF[cprev][2];
     }
 #pragma unroll
     for (int ps = 0; ps < NPASS; ++ps) {
       const int r = ps * RPP + ptid / TPR, part = ptid % TPR;
+      const bool ok = c0 + r < T;
+      const uint4 z{0, 0, 0, 0};
+      const uint4 k4 = ok ? rk[ps] : z, q4 = ok ? rq[ps] : z, v4 = ok ? rv[ps] : z;
       float xv[VEC], qv[VEC];
-      unpack(rk[ps], IT(), xv);
-      unpack(rq[ps], IT(), qv);
+      unpack(k4, IT(), xv);
+      unpack(q4, IT(), qv);
       float sk = 0.f, sq = 0.f;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) { sk += xv[e] * xv[e]; sq += qv[e] * qv[e]; }
       sk = group_sum<TPR>(sk);
       sq = group_sum<TPR>(sq);
       const float ik = safe_rsqrt(sk + a.eps_phi), iq = safe_rsqrt(sq + a.eps_phi);
+      // key k_{c0+r} becomes x_{c0+r+1}: its step eta uses beta_{c0+r+1}
+      const float inv = fast_rcp(a.eps_eta + sk * ik * ik);
+      const float eta = PERCH ? inv : (c0 + r + 1 < T ? rb1[ps] : 0.f) * inv;
+      const float cf = PERCH ? ik : ik * eta;
       if (r + 1 < C) {
-        put_perm(X + (r + 1) * LX, part * VEC, rk[ps]);
+        put_perm(X + (r + 1) * LX, part * VEC, k4);
         if (part == 0) {
           G[G_IK * C + r + 1] = ik;
-          G[G_XN2 * C + r + 1] = sk * ik * ik;
+          G[G_CF * C + r + 1] = cf;
+          G[G_ETA * C + r + 1] = eta;
         }
       } else if (r + 1 == C) {
-        *reinterpret_cast<uint4 *>(&sCarry[cin][part * VEC]) = rk[ps];
+        *reinterpret_cast<uint4 *>(&sCarry[cin][part * VEC]) = k4;
         if (part == 0) {
-          sCarryIK[cin] = ik;
-          sCarryXN2[cin] = sk * ik * ik;
+          sCarryF[cin][0] = ik;
+          sCarryF[cin][1] = cf;
+          sCarryF[cin][2] = eta;
         }
       }
       if (r < C) {
-        put_perm(Q + r * LX, part * VEC, rq[ps]);
-        *reinterpret_cast<uint4 *>(V + r * LX + part * VEC) = rv[ps];
+        put_perm(Q + r * LX, part * VEC, q4);
+        *reinterpret_cast<uint4 *>(V + r * LX + part * VEC) = v4;
         if (part == 0) G[G_IQ * C + r] = iq;
       }
     }
     if (pw == NPW - 1) {   // clamp in log space, chunk-local inclusive scan
-      const bool ok = lane < C && c * C + lane < T;
+      const bool ok = lane < C && c0 + lane < T;
       const float g2 = ok ? fmaxf(rg, a.log_eps_gamma) : 0.f;
       const float L = wave_inclusive_scan(g2);
       if (lane < C) {
         G[G_LC * C + lane] = L;
         G[G_LM * C + lane] = L - g2;
-        G[G_BETA * C + lane] = rb;
       }
     }
   };
 
-  auto derive = [&](int c) {               // key-side tiles of chunk c (needs its staged inputs)
+  // key-side tiles of chunk c (needs its staged inputs)
+  auto derive = [&](int c) {
     const int s = c % 3, ds = c & 1;
     const OpT *X = sX[s], *Q = sQ[s];
     float *G = sG[s];
-    // 16x16 block of (rows of block qa of Am) . (rows of block pb of Bm)^T, raw operands:
-    // lane (g, c) gets <Am_{16 qa + 4g + i}, Bm_{16 pb + c}>.
-    auto gram = [&](const OpT *Am, int qa, const OpT *Bm, int pb) {
+    // A-operand fragments of rows 16 blk .. 16 blk + 15 of M (raw, dk permuted)
+    auto rows16 = [&](const OpT *M, int blk, Pr (&out)[NA / 2]) {
+#pragma unroll
+      for (int a2 = 0; a2 < NA / 2; ++a2) out[a2] = ldp(M + (16 * blk + cl) * LX + 32 * a2 + 8 * g4);
+    };
+    // lane (g, c) of the result: <Am_{4g+i}, Bm_c> for the two 16-row blocks
+    auto tile = [&](const Pr (&Am)[NA / 2], const Pr (&Bm)[NA / 2]) {
       f4 acc = zero4();
 #pragma unroll
-      for (int a2 = 0; a2 < NA / 2; ++a2)
-        mmap(acc, ldp(Am + (16 * qa + cl) * LX + 32 * a2 + 8 * g4), ldp(Bm + (16 * pb + cl) * LX + 32 * a2 + 8 * g4));
+      for (int a2 = 0; a2 < NA / 2; ++a2) mmap(acc, Am[a2], Bm[a2]);
       return acc;
     };
-    // column factors of a block of columns: IK_j * (eta_j or 1)
-    auto colfac = [&](int j0) {
-      const f4 ik = *reinterpret_cast<const f4 *>(G + G_IK * C + j0);
-      if (PERCH) return ik;
-      const f4 bt = *reinterpret_cast<const f4 *>(G + G_BETA * C + j0);
-      const f4 xn = *reinterpret_cast<const f4 *>(G + G_XN2 * C + j0);
-      f4 r;
+    // Gram (isP = 0) or score (isP = 1) block (p, q), transposed: lane (g, c) holds
+    // element (row 16p + c, col 16q + 4g + i), the consumers' A-operand fragment.
+    auto finish = [&](const f4 &acc, int isP, int p, int q) {
+      const f4 cf = *reinterpret_cast<const f4 *>(G + G_CF * C + 16 * q + 4 * g4);
+      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + G_LC * C + 16 * q + 4 * g4);
+      const int row = 16 * p + cl;
+      const float Lrow = G[(isP ? G_LC : G_LM) * C + row];
+      const float rf = G[(isP ? G_IQ : G_IK) * C + row];
+      f4 val;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = ik[i] * bt[i] / (a.eps_eta + xn[i]);
-      return r;
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] * __expf(Lrow - Lc4[i]) * rf * cf[i];
+        val[i] = (p > q || 4 * g4 + i <= cl) ? v : 0.f;
+      }
+      *reinterpret_cast<Frag *>(&(isP ? sP[ds] : sAo[ds])[fragoff(p, q)]) = cvt<OpT>(val);
     };
-    // diagonal block pw: F1 -> T_pp (A-layout), F2 -> A_pp (fp32, C-layout) and A_pp off its 4x4 diagonal
-    if (DELTA && pw < NB) {
-      const int p = pw, r0 = 4 * g4;
-      const f4 acc = gram(X, p, X, p);     // symmetric: <x_{16p+4g+i}, x_{16p+c}>
-      const f4 cf = colfac(16 * p + r0);   // factors of columns 16p + 4g + i
+    // diagonal block p: F1 -> T_pp (A-layout), F2 -> A_pp (fp32, C-layout) and A_pp off its 4x4 diagonal
+    auto diag = [&](const f4 &acc, int p) {   // acc: <x_{16p+4g+i}, x_{16p+c}> (symmetric)
+      const int r0 = 4 * g4;
+      const f4 cf4 = *reinterpret_cast<const f4 *>(G + G_CF * C + 16 * p + r0);
+      const f4 ik4 = *reinterpret_cast<const f4 *>(G + G_IK * C + 16 * p + r0);
       const f4 Lc4 = *reinterpret_cast<const f4 *>(G + G_LC * C + 16 * p + r0);
       const f4 Lm4 = *reinterpret_cast<const f4 *>(G + G_LM * C + 16 * p + r0);
       const float Lc1 = G[G_LC * C + 16 * p + cl], Lm1 = G[G_LM * C + 16 * p + cl];
-      const float ik1 = G[G_IK * C + 16 * p + cl];
-      const float cf1 = PERCH ? ik1 : ik1 * G[G_BETA * C + 16 * p + cl] / (a.eps_eta + G[G_XN2 * C + 16 * p + cl]);
+      const float ik1 = G[G_IK * C + 16 * p + cl], cf1 = G[G_CF * C + 16 * p + cl];
       f4 NA4, NC4;   // N[16p+c][16p+4g+i] (A-layout) and N[16p+4g+i][16p+c] (C-layout)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float va = acc[i] * __expf(Lm1 - Lc4[i]) * ik1 * cf[i];
-        const float vc = acc[i] * __expf(Lm4[i] - Lc1) * G[G_IK * C + 16 * p + r0 + i] * cf1;
+        const float va = acc[i] * __expf(Lm1 - Lc4[i]) * ik1 * cf4[i];
+        const float vc = acc[i] * __expf(Lm4[i] - Lc1) * ik4[i] * cf1;
         NA4[i] = (r0 + i < cl) ? va : 0.f;
         NC4[i] = (cl < r0 + i) ? vc : 0.f;
       }
       if constexpr (VAR == V_F1) {
         // row-oriented: T (I + N) = I, so T <- (I - T N_o)(I + N_d)^{-1}, exact after 3 sweeps;
         // Y holds T in A-layout (row c, columns 4g..4g+3 of the block).
-        float *Nd = sNd[pw];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Nd[cl * 17 + r0 + i] = NA4[i];   // Nd[row][col]
-        wave_lds_sync();
-        const float n10 = Nd[(r0 + 1) * 17 + r0], n20 = Nd[(r0 + 2) * 17 + r0], n21 = Nd[(r0 + 2) * 17 + r0 + 1];
-        const float n30 = Nd[(r0 + 3) * 17 + r0], n31 = Nd[(r0 + 3) * 17 + r0 + 1], n32 = Nd[(r0 + 3) * 17 + r0 + 2];
+        // n_ab = N[4g+a][4g+b] sits in lane (g, 4g+a), entry b of NA4.
+        const int src = 16 * g4 + r0;
+        const float n10 = __shfl(NA4[0], src + 1), n20 = __shfl(NA4[0], src + 2), n21 = __shfl(NA4[1], src + 2);
+        const float n30 = __shfl(NA4[0], src + 3), n31 = __shfl(NA4[1], src + 3), n32 = __shfl(NA4[2], src + 3);
         f4 NoC;   // C-layout of N without its 4x4 diagonal sub-blocks
 #pragma unroll
         for (int i = 0; i < 4; ++i) NoC[i] = ((cl >> 2) == g4) ? 0.f : NC4[i];
@@ -360,55 +429,42 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
         }
         *reinterpret_cast<Frag *>(&sTb[ds][(p * 64 + lane) * 4]) = cvt<OpT>(NoA);
       }
-    }
-    // off-diagonal A blocks and score blocks, transposed, a static round robin over producer waves
-    constexpr int NG = DELTA ? P::NOFF : 0;
-    constexpr int NJOB = NG + P::NPB;
-#pragma unroll
-    for (int jj = 0; jj < (NJOB + NPW - 1) / NPW; ++jj) {
-      const int job = pw + jj * NPW;
-      if (job < NJOB) {
-        const bool isP = job >= NG;
-        const int pj = isP ? job - NG : job;
-        int p, q;
-        if (isP) {
-          p = 0;
-          while ((p + 1) * (p + 2) / 2 <= pj) ++p;
-          q = pj - p * (p + 1) / 2;
-        } else {
-          p = 1;
-          while (p * (p + 1) / 2 <= pj) ++p;
-          q = pj - p * (p - 1) / 2;
-        }
-        // lane (g, c): element (row 16p + c, col 16q + 4g + i)
-        const f4 acc = gram(X, q, isP ? Q : X, p);
-        const f4 cf = colfac(16 * q + 4 * g4);
-        const f4 Lc4 = *reinterpret_cast<const f4 *>(G + G_LC * C + 16 * q + 4 * g4);
-        const int row = 16 * p + cl;
-        const float Lrow = G[(isP ? G_LC : G_LM) * C + row];
-        const float rf = G[(isP ? G_IQ : G_IK) * C + row];
-        f4 val;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = acc[i] * __expf(Lrow - Lc4[i]) * rf * cf[i];
-          val[i] = (p > q || 4 * g4 + i <= cl) ? v : 0.f;   // Gram blocks have q < p
-        }
-        *reinterpret_cast<Frag *>(&(isP ? sP[ds] : sAo[ds])[fragoff(p, q)]) = cvt<OpT>(val);
-      }
-    }
+    };
     // per-row factors the consumers use
-    if (pw == NPW - 1 && lane < C) {
-      const float L = G[G_LC * C + lane], Lm = G[G_LM * C + lane];
-      const float Llast = G[G_LC * C + C - 1];
-      const float ik = G[G_IK * C + lane];
-      const float inv = 1.f / (a.eps_eta + G[G_XN2 * C + lane]);
-      const float eta = PERCH ? inv : G[G_BETA * C + lane] * inv;
-      G[G_GAM * C + lane] = __expf(Lm) * ik;
-      G[G_EL * C + lane] = __expf(L) * G[G_IQ * C + lane];
-      G[G_ETA * C + lane] = eta;
-      G[G_CST * C + lane] = __expf(Llast - L) * ik * (PERCH ? 1.f : eta);
-      if (lane == 0) sLam[s] = __expf(Llast);
-    }
+    auto rowfac = [&]() {
+      if (lane < C) {
+        const float L = G[G_LC * C + lane], Lm = G[G_LM * C + lane];
+        const float Llast = G[G_LC * C + C - 1];
+        G[G_GAM * C + lane] = __expf(Lm) * G[G_IK * C + lane];
+        G[G_EL * C + lane] = __expf(L) * G[G_IQ * C + lane];
+        G[G_CST * C + lane] = __expf(Llast - L) * G[G_CF * C + lane];
+        if (lane == 0) sLam[s] = __expf(Llast);
+      }
+    };
+    auto run = [&](auto wc) {
+      constexpr int w = decltype(wc)::value;
+      constexpr JobList J = make_jobs(NB, DELTA, w);
+      constexpr int NJ = J.n > 0 ? J.n : 1;
+      Pr Dop[NA / 2], Aop[NJ][NA / 2], Bop[NJ][NA / 2];
+      if constexpr (J.diag >= 0) rows16(X, J.diag, Dop);
+#pragma unroll
+      for (int j = 0; j < J.n; ++j) {
+        rows16(X, J.q[j], Aop[j]);
+        rows16(J.isP[j] ? Q : X, J.p[j], Bop[j]);
+      }
+      f4 dacc, acc[NJ];
+      if constexpr (J.diag >= 0) dacc = tile(Dop, Dop);
+#pragma unroll
+      for (int j = 0; j < J.n; ++j) acc[j] = tile(Aop[j], Bop[j]);
+      if constexpr (J.diag >= 0) diag(dacc, J.diag);
+#pragma unroll
+      for (int j = 0; j < J.n; ++j) finish(acc[j], J.isP[j], J.p[j], J.q[j]);
+      if constexpr (w == NPW - 1) rowfac();
+    };
+    if (pw == 0) run(std::integral_constant<int, 0>());
+    else if (pw == 1) run(std::integral_constant<int, 1>());
+    else if (pw == 2) run(std::integral_constant<int, 2>());
+    else run(std::integral_constant<int, 3>());
   };
 
   // ================= consumers =================
@@ -564,7 +620,6 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
   } else if (PERCH) {
     prefetch_beta(0);
   }
-  __syncthreads();
   if (pw == 0) {
     float s = 0.f;
     for (int e = lane; e < D; e += 64) {
@@ -573,8 +628,11 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     }
     s = group_sum<64>(s);
     if (lane == 0) {
-      sCarryIK[0] = 1.f;
-      sCarryXN2[0] = s;
+      const float inv = fast_rcp(a.eps_eta + s);
+      const float eta = PERCH ? inv : a.beta[(size_t)(b * T) * H + h] * inv;
+      sCarryF[0][0] = 1.f;
+      sCarryF[0][1] = PERCH ? 1.f : eta;
+      sCarryF[0][2] = eta;
     }
   }
   __syncthreads();

@@ -11,12 +11,19 @@
 // the B-operand layout, a product can feed the next product without a trip
 // through LDS; and the C-layout of M^T is the A-layout of M.
 //
-//  * bf16: one v_mfma_f32_16x16x16_bf16 (k-slots 4g..4g+3 of the lane).
+//  * bf16: one v_mfma_f32_16x16x32_bf16 whose upper four k-slots per lane are
+//    zero (see below).
 //  * fp32: four v_mfma_f32_16x16x4_f32, instruction i taking k = 4g + i.
 // mma32 sums two k-blocks of 16.  For bf16 it is one v_mfma_f32_16x16x32_bf16
 // whose 8 k-slots per lane are filled with the lane's 4 k of each block; the
 // assignment of actual k to slots only has to be the same for A and B, which
 // it is by construction.
+//
+// All bf16 products use the one 16x16x32 opcode.  On gfx950 a 16x16x16 bf16
+// MFMA that accumulates into the result of an immediately preceding 16x16x32
+// bf16 MFMA read a stale accumulator (measured: wrong sums with the wait
+// states the compiler inserts), while same-opcode accumulation chains are
+// exact.  A padded 16x16x32 issues at the same rate as 16x16x16.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -44,7 +51,9 @@ template <typename OpT>
 __device__ __forceinline__ typename Op<OpT>::frag cvt(const f4 &x) { return to_op(x, OpT()); }
 
 __device__ __forceinline__ void mma16(f4 &d, const bf4 &a, const bf4 &b) {
-  d = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), d, 0, 0, 0);
+  const bf8 a8 = {a[0], a[1], a[2], a[3], (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+  const bf8 b8 = {b[0], b[1], b[2], b[3], (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+  d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, d, 0, 0, 0);
 }
 __device__ __forceinline__ void mma16(f4 &d, const f4 &a, const f4 &b) {
   d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], d, 0, 0, 0);
