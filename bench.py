@@ -10,7 +10,10 @@ synthetic N(0,1) inputs.  One step = one falcon_chunk_fwd call over one batch
 Timing: three rotating input sets (more bytes than the 256 MB MALL), W untimed
 calls, then K timed calls bracketed by torch.cuda.synchronize().  Each call is
 also bracketed by HIP events on the stream it is launched on, which gives the
-average duration of the forward kernel used for the roofline.
+average device time of the forward path used for the roofline: the prep kernel
+over all chunks plus the state scan (chunk-parallel path, the default when the
+shape has a workspace, allocated once outside the timed region), or the one
+fused kernel (--fused, or shapes without a workspace).
 """
 
 from __future__ import annotations
@@ -113,7 +116,7 @@ def bench_decode(args):
     }
 
 
-KERNEL_SOURCES = ("falcon_fwd_pipe.hip", "mfma_frag.h", "falcon_kernels.h")
+KERNEL_SOURCES = ("falcon_fwd_split.hip", "falcon_fwd_pipe.hip", "chunk_common.h", "mfma_frag.h", "falcon_kernels.h")
 
 
 def measured_traffic(key):
@@ -170,6 +173,7 @@ def main():
     ap.add_argument("--window", type=int, default=4, help="Falcon-3/3A window (pairs)")
     ap.add_argument("--decode", action="store_true", help="time the single-token step instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", action="store_true", help="run the fused single-kernel path (no workspace)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -186,6 +190,7 @@ def main():
     import torch
     import workloads as W
     from recurrent_sequence_models_amd import chunk_fwd, new_state
+    from recurrent_sequence_models_amd.falcon import workspace_bytes
 
     w = W.WORKLOADS[args.workload]
     variant = args.variant
@@ -205,10 +210,14 @@ def main():
         sets.append(d)
     del inp
     stream = torch.cuda.current_stream()
+    ws_bytes = 0 if args.fused else workspace_bytes(variant, w.dtype, w.batch, w.seqlen, w.heads, w.dk, w.dv,
+                                                    w.chunk, window)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else False
+    path = "split" if ws_bytes else "fused"
 
     def call(d):
         chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk, window=window,
-                  final=d["final"], out=d["o"], stream=stream)
+                  final=d["final"], out=d["o"], stream=stream, workspace=ws)
 
     for i in range(args.warmup):
         call(sets[i % 3])
@@ -246,9 +255,11 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
-    roof["traffic"] = measured_traffic(f"chunk_fwd_pipe {variant} {w.name}")
-    roof["kernel"] = ("chunk_fwd_window" if window > 1 else
+    roof["traffic"] = measured_traffic(f"{path} {variant} {w.name}")
+    roof["kernel"] = ("chunk_prep + chunk_scan" if path == "split" else "chunk_fwd_window" if window > 1 else
                       "chunk_fwd_pipe" if w.dk <= 64 else "chunk_fwd_rows")
+    roof["path"] = path
+    roof["workspace_bytes"] = ws_bytes
     roof["kernel_us"] = {"mean": round(avg_kernel_s * 1e6, 2), "p10": round(kern_ms[K // 10] * 1e3, 2),
                          "p50": round(kern_ms[K // 2] * 1e3, 2), "p90": round(kern_ms[(9 * K) // 10] * 1e3, 2)}
     roof["alg_bytes"] = nbytes

@@ -111,9 +111,13 @@ int falcon_abi_version(void);
 /* Static, human-readable name of a status code (never NULL). */
 const char *falcon_status_string(int status);
 
-/* Bytes of device workspace falcon_chunk_fwd needs for this shape (0 when it
- * needs none).  Returns 0 for an invalid shape as well; validation is the
- * forward call's job. */
+/* Bytes of device workspace that enable the chunk-parallel path of
+ * falcon_chunk_fwd for this shape; 0 when that path does not apply (the
+ * forward then runs a fused kernel that needs no workspace).  The workspace
+ * holds, per chunk, the key-side factors (Gram / score blocks, diagonal-block
+ * inverses, per-row factors) that a prep kernel over all chunks writes and the
+ * state scan reads; its contents are scratch and need no initialisation.
+ * Returns 0 for an invalid shape as well; validation is the forward call's job. */
 size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape);
 
 /* Chunked forward pass over T tokens ([P1] 三种等价形式 form C, Figure 4-C;
@@ -126,7 +130,13 @@ size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape);
  *   o            [B, T, H, dv] in dtype; must not alias any input.
  *   chunk_states NULL, or [B, H, ceil(T/C), dv, dk] fp32: S at the end of
  *                every chunk (the last one equals S_T).
- *   workspace    may be NULL when falcon_chunk_fwd_workspace() is 0.
+ *   workspace    caller-owned device scratch, 16-byte aligned, or NULL.  NULL
+ *                (or a shape whose workspace size is 0) selects the fused
+ *                path; otherwise workspace_bytes must be at least
+ *                falcon_chunk_fwd_workspace(shape) (else FALCON_ERR_WORKSPACE)
+ *                and the chunk-parallel path runs.  Both paths compute the
+ *                same function; calls that share one workspace on different
+ *                streams race.
  * Results are deterministic: the same inputs give bit-identical outputs. */
 int falcon_chunk_fwd(const falcon_shape_t *shape,
                      const void *q, const void *k, const void *v,

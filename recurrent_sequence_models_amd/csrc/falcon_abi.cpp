@@ -71,6 +71,10 @@ hipError_t launch_chunk_fwd_rows(int variant, bool bf16, int dk, int dv, int chu
 hipError_t launch_chunk_fwd_window(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
                                    const FwdArgs &a, hipStream_t s);
 bool chunk_fwd_pipe_supported(int variant, bool bf16, int dk, int dv, int chunk);
+bool chunk_fwd_split_supported(int variant, bool bf16, int dk, int dv, int chunk);
+size_t chunk_fwd_split_workspace(int variant, bool bf16, int dk, int dv, int chunk, int bhc);
+hipError_t launch_chunk_fwd_split(int variant, bool bf16, int dk, int dv, int chunk, const FwdArgs &a, void *ws,
+                                  hipStream_t s);
 
 int choose_nsplit(int variant, bool bf16, int dk, int dv, int chunk, int batch_heads) {
   int n = 1;
@@ -109,8 +113,12 @@ const char *falcon_status_string(int status) {
 }
 
 size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape) {
-  (void)shape;
-  return 0;  // the fused kernels keep all intermediates on chip
+  if (check_shape(shape, false) != FALCON_OK) return 0;
+  if (windowed(shape->variant)) return 0;
+  const int64_t bhc = (int64_t)shape->batch * shape->heads * ((shape->seqlen + shape->chunk - 1) / shape->chunk);
+  if (bhc > INT32_MAX) return 0;
+  return falcon::chunk_fwd_split_workspace(shape->variant, shape->dtype == FALCON_BF16, shape->dk, shape->dv,
+                                           shape->chunk, (int)bhc);
 }
 
 int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, const void *v,
@@ -123,8 +131,10 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   if (init && (st = check_state(init, s)) != FALCON_OK) return st;
   if (final_state && (st = check_state(final_state, s)) != FALCON_OK) return st;
   if (chunk_states && !aligned16(chunk_states)) return FALCON_ERR_INVALID_ARG;
-  if (workspace_bytes < falcon_chunk_fwd_workspace(s)) return FALCON_ERR_WORKSPACE;
-  (void)workspace;
+  const size_t ws_need = falcon_chunk_fwd_workspace(s);
+  const bool split = workspace != nullptr && ws_need > 0;
+  if (split && workspace_bytes < ws_need) return FALCON_ERR_WORKSPACE;
+  if (split && !aligned16(workspace)) return FALCON_ERR_INVALID_ARG;
 
   const bool bf16 = s->dtype == FALCON_BF16;
   const bool win = windowed(s->variant) && s->window > 1;
@@ -151,9 +161,14 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   // workgroup still reading the incoming x_prev: one workgroup per sequence, or
   // the two buffers are distinct.  Otherwise (and for windows) a tail kernel does.
   const bool xprev_alias = init && final_state && init->x_prev == final_state->x_prev;
-  a.write_tail = (final_state && !win && (nsplit == 1 || !xprev_alias)) ? 1 : 0;
+  a.write_tail = (final_state && !win && (split || nsplit == 1 || !xprev_alias)) ? 1 : 0;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (split) {   // prep over all chunks, then one scan workgroup per sequence
+    return falcon::launch_chunk_fwd_split(s->variant, bf16, s->dk, s->dv, s->chunk, a, workspace, hs) == hipSuccess
+               ? FALCON_OK
+               : FALCON_ERR_HIP;
+  }
   if (falcon::launch_chunk_fwd(s->variant, bf16, s->dk, s->dv, s->chunk, nsplit, a, hs) != hipSuccess)
     return FALCON_ERR_HIP;
   if (final_state && !a.write_tail) {

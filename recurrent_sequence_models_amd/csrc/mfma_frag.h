@@ -38,11 +38,9 @@ template <typename T> struct Op;
 template <> struct Op<float> { typedef f4 frag; };
 template <> struct Op<__bf16> { typedef bf4 frag; };
 
-__device__ __forceinline__ bf4 to_op(const f4 &x, __bf16) {
-  bf4 r;
-  r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
-  return r;
-}
+// Round-to-nearest-even fp32 -> bf16 as one vector conversion (two packed
+// v_cvt_pk_bf16_f32), not four scalar conversions that then need repacking.
+__device__ __forceinline__ bf4 to_op(const f4 &x, __bf16) { return __builtin_convertvector(x, bf4); }
 __device__ __forceinline__ f4 to_op(const f4 &x, float) { return x; }
 __device__ __forceinline__ f4 to_f4(const bf4 &x) { return f4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]}; }
 __device__ __forceinline__ f4 to_f4(const f4 &x) { return x; }

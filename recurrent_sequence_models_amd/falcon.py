@@ -121,16 +121,26 @@ def new_state(batch, heads, dk, dv, window=1, device="cuda"):
     return st
 
 
+def workspace_bytes(variant, dtype, batch, seqlen, heads, dk, dv, chunk=64, window=1, eps_gamma=1e-3,
+                    eps_phi=1e-6, eps_eta=1e-6):
+    """falcon_chunk_fwd_workspace for a shape: bytes of scratch that enable the
+    chunk-parallel path (0: the shape runs the fused path)."""
+    shape = make_shape(variant, dtype, batch, seqlen, heads, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta)
+    return int(lib().falcon_chunk_fwd_workspace(ctypes.byref(shape)))
+
+
 def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=None,
               final=True, chunk_states=False, eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6,
-              out=None, stream=None):
+              out=None, stream=None, workspace=True):
     """falcon_chunk_fwd on torch tensors.
 
     q, k [B,T,H,dk] and v [B,T,H,dv] in float32 or bfloat16; beta [B,T,H] (or
     [B,T,H,dv] for F2/F2A) and log_lambda [B,T,H] float32.  ``init``: None or a
     state dict (S, x_prev, win_x, win_v).  ``final``: True (allocate), a state
-    dict to write into (may be ``init``), or False.  Returns (o, final_state,
-    chunk_states)."""
+    dict to write into (may be ``init``), or False.  ``workspace``: True
+    allocates the scratch of the chunk-parallel path when the shape has one,
+    False runs the fused path (no scratch), or a uint8 device tensor to use.
+    Returns (o, final_state, chunk_states)."""
     import torch
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -155,8 +165,14 @@ def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=No
     cs = torch.empty(B, H, nch, dv, dk, dtype=torch.float32, device=dev) if chunk_states else None
     shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta)
     L = lib()
-    ws_bytes = L.falcon_chunk_fwd_workspace(ctypes.byref(shape))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if workspace is True:
+        ws_bytes = L.falcon_chunk_fwd_workspace(ctypes.byref(shape))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    elif workspace is False or workspace is None:
+        ws, ws_bytes = None, 0
+    else:
+        _check_tensor("workspace", workspace, torch.uint8, (workspace.numel(),), dev)
+        ws, ws_bytes = workspace, workspace.numel()
     st_in, st_out = _state(init), _state(final)
     status = L.falcon_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_lambda),
                                 ctypes.byref(st_in) if st_in else None,

@@ -72,8 +72,28 @@ def call_step(shape, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, state=None, o=FA
                                    ctypes.byref(state) if state else None, o, None)
 
 
-def test_workspace_is_zero():
-    assert F.lib().falcon_chunk_fwd_workspace(ctypes.byref(good_shape())) == 0
+def workspace(**kw):
+    return F.lib().falcon_chunk_fwd_workspace(ctypes.byref(good_shape(**kw)))
+
+
+def test_workspace_size():
+    """The chunk-parallel path keeps one image per (sequence, chunk): the size is a
+    multiple of 16 bytes proportional to B*H*ceil(T/C); windowed variants, d = 128
+    and invalid shapes need none."""
+    w1, w2 = workspace(seqlen=100), workspace(seqlen=200)   # 2 and 4 chunks of 64
+    assert w1 > 0 and w1 % 16 == 0 and w2 == 2 * w1
+    assert workspace(batch=4, seqlen=100) == 2 * w1
+    assert workspace(variant="F1A") < w1                    # no Gram / T blocks
+    assert workspace(variant="F3", window=4) == 0
+    assert workspace(dk=128, dv=128) == 0
+    assert workspace(batch=0) == 0 and workspace(dk=48, dv=48) == 0
+
+
+@cpu_only
+def test_workspace_too_small_or_misaligned():
+    need = workspace()
+    assert call_fwd(good_shape(), ws=FAKE, wsb=need - 16) == F.ERR_WORKSPACE
+    assert call_fwd(good_shape(), ws=ctypes.c_void_p(0x10008), wsb=need) == F.ERR_INVALID_ARG
 
 
 INVALID_SHAPES = [

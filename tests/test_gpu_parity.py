@@ -16,13 +16,13 @@ pytestmark = pytest.mark.gpu
 ROW_VARIANTS = ("F1", "F1A", "F2", "F2A")
 
 
-def run_gpu(variant, inp, dtype, chunk, window=1, init=None, chunk_states=False, final=True):
+def run_gpu(variant, inp, dtype, chunk, window=1, init=None, chunk_states=False, final=True, workspace=True):
     import torch
     from recurrent_sequence_models_amd import chunk_fwd
     d = to_dev(inp, dtype)
     st = state_to_dev(init) if init is not None else None
     o, fin, cs = chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=chunk,
-                           window=window, init=st, final=final, chunk_states=chunk_states)
+                           window=window, init=st, final=final, chunk_states=chunk_states, workspace=workspace)
     torch.cuda.synchronize()
     out = {"o": to_np(o)}
     if fin is not None:
@@ -32,11 +32,11 @@ def run_gpu(variant, inp, dtype, chunk, window=1, init=None, chunk_states=False,
     return out
 
 
-def check(variant, w, seed, window=1, init=False, chunk=None, chunk_states=False):
+def check(variant, w, seed, window=1, init=False, chunk=None, chunk_states=False, workspace=True):
     inp = W.make_inputs(w, variant, seed=seed)
     st = W.make_state(w, seed + 1000, window) if init else None
     chunk = chunk or w.chunk
-    g = run_gpu(variant, inp, w.dtype, chunk, window, st, chunk_states)
+    g = run_gpu(variant, inp, w.dtype, chunk, window, st, chunk_states, workspace=workspace)
     r = oracle.recurrent(variant, **inp, window=window, state=st, return_states=chunk_states)
     tol = TOL[w.dtype]
     errs = {"o": rel_l2(g["o"], r["o"]), "S": rel_l2(g["S"], r["S"]), "x_prev": rel_l2(g["x_prev"], r["x_prev"])}
@@ -76,6 +76,29 @@ def test_fp32_chunks_ragged_with_state(variant, chunk):
 def test_bf16_ragged(variant, d):
     w = W.WORKLOADS["layer130m"].replace(batch=2, heads=3, seqlen=200, dk=d, dv=d)
     check(variant, w, 11, init=True, chunk_states=True)
+
+
+# The default calls above take the chunk-parallel path (prep over all chunks +
+# state scan) wherever a workspace applies; these run the fused path (no
+# workspace) on the same cases, and check that the two paths agree.
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+@pytest.mark.parametrize("dtype,d,chunk", [("fp32", 64, 16), ("fp32", 32, 64), ("bf16", 32, 64), ("bf16", 64, 32),
+                                           ("bf16", 64, 64)])
+def test_fused_path(variant, dtype, d, chunk):
+    w = W.WORKLOADS["layer130m"].replace(batch=2, heads=3, seqlen=203, dk=d, dv=d, chunk=chunk, dtype=dtype)
+    check(variant, w, 17, init=True, chunk_states=True, workspace=False)
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+def test_fused_and_split_paths_agree(variant):
+    w = W.WORKLOADS["layer130m"].replace(batch=2, heads=3, seqlen=333)
+    inp = W.make_inputs(w, variant, seed=19)
+    st = W.make_state(w, 1019)
+    a = run_gpu(variant, inp, "bf16", 64, init=st, chunk_states=True, workspace=True)
+    b = run_gpu(variant, inp, "bf16", 64, init=st, chunk_states=True, workspace=False)
+    for k in a:
+        e = rel_l2(a[k], b[k])
+        assert e <= 5e-3, (k, e)   # same arithmetic up to accumulation order and bf16 rounding of tiles
 
 
 @pytest.mark.parametrize("variant", ROW_VARIANTS)
