@@ -86,15 +86,26 @@ struct Split {
   static constexpr int RPP = NPT / TPR, NPASS = (C + RPP - 1) / RPP;
   static constexpr int LDT = C + 4;                          // fp32 rows of the prep's A and T
   static constexpr size_t prep_lds() { return (size_t)SZ * 2 * C * LX + 4 * R_N * C + (TFULL ? 8 * C * LDT : 0); }
-  // scan kernel: D/16 consumer waves + 4 copy waves
-  static constexpr int NCW = D / 16, NSW = 4, NT = 64 * (NCW + NSW), NST = 64 * NSW;
-  static constexpr int RPC = NST / TPR, NPK = (C + RPC - 1) / RPC;
-  static constexpr int NPI = (NU + NST - 1) / NST;
-  static constexpr size_t scan_lds() {
-    return (size_t)SZ * 2 * 4 * C * LX + 2 * (size_t)IMG;
-  }
-  static constexpr bool fits() { return scan_lds() + 256 <= 160 * 1024 && prep_lds() + 256 <= 64 * 1024; }
   static size_t workspace(int bhc) { return (size_t)bhc * IMG; }
+};
+
+// The scan of one sequence is split over NS workgroups by value channel (rows
+// of S evolve independently given the keys): each takes D/NS channels with
+// one consumer wave per 16 of them, plus 4 (d = 128: 8) copy waves that stage the shared
+// key / query rows and chunk image and its own value columns.
+template <int VAR, typename IT, int D, int C, int NS>
+struct Scan {
+  using S = Split<VAR, IT, D, C>;
+  static constexpr int DS = D / NS;                          // value channels per workgroup
+  static constexpr int NCW = DS / 16, NSW = D == 128 ? 8 : 4, NT = 64 * (NCW + NSW), NST = 64 * NSW;
+  static constexpr int LXV = DS + S::PADE;                   // V rows (this workgroup's channels)
+  static constexpr int RPC = NST / S::TPR, NPK = (C + RPC - 1) / RPC;   // key / query rows per copy pass
+  static constexpr int TPV = DS / S::VEC, RPV = NST / TPV, NPV = (C + RPV - 1) / RPV;
+  static constexpr int NPI = (S::NU + NST - 1) / NST;
+  static constexpr size_t lds() { return (size_t)S::SZ * 2 * (3 * C * S::LX + C * LXV) + 2 * (size_t)S::IMG; }
+  static constexpr bool fits() {
+    return DS >= 16 && D % NS == 0 && lds() + 256 <= 160 * 1024 && S::prep_lds() + 256 <= 64 * 1024;
+  }
 };
 
 // fragment-native element offset of tile (.., q) in a pair buffer whose row of pairs starts at slot `base`
@@ -389,29 +400,42 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
 }
 
 // ============================== scan kernel ==============================
-template <int VAR, typename IT, int D, int C>
-__global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_scan(FwdArgs a, const unsigned char *ws) {
+template <int VAR, typename IT, int D, int C, int NS>
+__global__ __launch_bounds__(64 * (D / 16 / NS + (D == 128 ? 8 : 4))) void chunk_scan(FwdArgs a, const unsigned char *ws) {
   using S = Split<VAR, IT, D, C>;
+  using Z = Scan<VAR, IT, D, C, NS>;
   using OpT = IT;
   using Frag = typename Op<OpT>::frag;
   using Pr = Pair<OpT>;
-  constexpr int NB = S::NB, NA = S::NA, NCW = S::NCW, LX = S::LX, VEC = S::VEC, TPR = S::TPR, RPC = S::RPC;
+  constexpr int NB = S::NB, NA = S::NA, NCW = Z::NCW, LX = S::LX, VEC = S::VEC, TPR = S::TPR, RPC = Z::RPC;
+  constexpr int LXV = Z::LXV, TPV = Z::TPV, RPV = Z::RPV;
   constexpr bool PERCH = S::PERCH, DELTA = S::DELTA;
 
   // Operands with the per-row factors folded in (dk permuted), from x_i = k_{i-1} and q_i:
   __shared__ __attribute__((aligned(16))) OpT sXg[2][C * LX];  // GAM_i x_i   (residuals)
   __shared__ __attribute__((aligned(16))) OpT sXc[2][C * LX];  // CST_i x_i   (state update)
   __shared__ __attribute__((aligned(16))) OpT sQe[2][C * LX];  // EL_i q_i    (outputs)
-  __shared__ __attribute__((aligned(16))) IT sV[2][C * LX];    // raw v_i, natural channel order
+  __shared__ __attribute__((aligned(16))) IT sV[2][C * LXV];   // raw v_i, this workgroup's channels
   __shared__ __attribute__((aligned(16))) unsigned char sImg[2][S::IMG];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, cl = lane & 15;
-  const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  // workgroup -> (sequence, channel slice).  The NS slices of a sequence get ids
+  // that are equal mod 8, i.e. the same XCD, so its L2 serves their shared reads.
+  int bh, sp;
+  if (NS > 1 && (a.B * a.H) % 8 == 0) {
+    const int rest = blockIdx.x >> 3;
+    sp = rest % NS;
+    bh = (rest / NS) * 8 + (blockIdx.x & 7);
+  } else {
+    bh = blockIdx.x / NS;
+    sp = blockIdx.x % NS;
+  }
+  const int b = bh / a.H, h = bh % a.H;
   const int T = a.T, H = a.H, NC = a.nchunks;
   const bool consumer = wv < NCW;
   const int ctid = tid - 64 * NCW;         // copy thread index
-  const int chW = 16 * wv + cl;            // consumer lane's value channel
+  const int chW = Z::DS * sp + 16 * wv + cl;   // consumer lane's value channel
 
   const IT *qp = static_cast<const IT *>(a.q);
   const IT *kp = static_cast<const IT *>(a.k);
@@ -423,19 +447,24 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_scan(FwdArgs a, const
   // Two register sets: chunk c lands in set c & 1, two chunks ahead of its use,
   // so a load has two scan iterations to arrive.
   struct Regs {
-    uint4 k[S::NPK], q[S::NPK], v[S::NPK], img[S::NPI];
-    float fg[S::NPK], fc[S::NPK], fe[S::NPK];   // GAM, CST of the row's x; EL of its q
+    uint4 k[Z::NPK], q[Z::NPK], v[Z::NPV], img[Z::NPI];
+    float fg[Z::NPK], fc[Z::NPK], fe[Z::NPK];   // GAM, CST of the row's x; EL of its q
   };
   Regs reg[2];
   auto prefetch = [&](int c, Regs &R) __attribute__((always_inline)) {    // global -> registers, chunk c (rows clamped in bounds)
     const int c0 = c * C;
 #pragma unroll
-    for (int ps = 0; ps < S::NPK; ++ps) {
+    for (int ps = 0; ps < Z::NPV; ++ps) {
+      const int r = min(ps * RPV + ctid / TPV, C - 1), part = ctid % TPV;
+      const int tq = min(c0 + r, T - 1);
+      R.v[ps] = *reinterpret_cast<const uint4 *>(vp + ((size_t)(b * T + tq) * H + h) * D + Z::DS * sp + part * VEC);
+    }
+#pragma unroll
+    for (int ps = 0; ps < Z::NPK; ++ps) {
       const int r = min(ps * RPC + ctid / TPR, C - 1), part = ctid % TPR;
       const int tk = min(max(c0 + r - 1, 0), T - 1), tq = min(c0 + r, T - 1);
       R.k[ps] = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tk) * H + h) * D + part * VEC);
       R.q[ps] = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tq) * H + h) * D + part * VEC);
-      R.v[ps] = *reinterpret_cast<const uint4 *>(vp + ((size_t)(b * T + tq) * H + h) * D + part * VEC);
       const float *Fg = reinterpret_cast<const float *>(wsq + (size_t)c * S::IMG + S::OFF_F);
       R.fg[ps] = Fg[F_GAM * C + r];
       R.fc[ps] = Fg[F_CST * C + r];
@@ -443,12 +472,17 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_scan(FwdArgs a, const
     }
     const uint4 *src = reinterpret_cast<const uint4 *>(wsq + (size_t)c * S::IMG);
 #pragma unroll
-    for (int j = 0; j < S::NPI; ++j) R.img[j] = src[min(ctid + j * S::NST, S::NU - 1)];
+    for (int j = 0; j < Z::NPI; ++j) R.img[j] = src[min(ctid + j * Z::NST, S::NU - 1)];
   };
   auto stage = [&](int c, const Regs &R) __attribute__((always_inline)) { // registers -> LDS slot c & 1
     const int s = c & 1, c0 = c * C;
 #pragma unroll
-    for (int ps = 0; ps < S::NPK; ++ps) {
+    for (int ps = 0; ps < Z::NPV; ++ps) {
+      const int r = ps * RPV + ctid / TPV, part = ctid % TPV;
+      if (r < C) *reinterpret_cast<uint4 *>(sV[s] + r * LXV + part * VEC) = keep_or_zero(c0 + r < T, R.v[ps]);
+    }
+#pragma unroll
+    for (int ps = 0; ps < Z::NPK; ++ps) {
       const int r = ps * RPC + ctid / TPR, part = ctid % TPR;
       if (r < C) {
         float xv[VEC], qv[VEC];
@@ -462,12 +496,11 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_scan(FwdArgs a, const
         put_perm(sXg[s] + r * LX, part * VEC, scale_pack<OpT, VEC>(xv, R.fg[ps]));
         put_perm(sXc[s] + r * LX, part * VEC, scale_pack<OpT, VEC>(xv, R.fc[ps]));
         put_perm(sQe[s] + r * LX, part * VEC, scale_pack<OpT, VEC>(qv, R.fe[ps]));
-        *reinterpret_cast<uint4 *>(sV[s] + r * LX + part * VEC) = keep_or_zero(okq, R.v[ps]);
       }
     }
 #pragma unroll
-    for (int j = 0; j < S::NPI; ++j) {
-      const int u = ctid + j * S::NST;
+    for (int j = 0; j < Z::NPI; ++j) {
+      const int u = ctid + j * Z::NST;
       if (u < S::NU) *reinterpret_cast<uint4 *>(sImg[s] + 16 * u) = R.img[j];
     }
   };
@@ -524,7 +557,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_scan(FwdArgs a, const
       Frag Rb[NB];
 #pragma unroll
       for (int q = 0; q < NB; ++q)
-        Rb[q] = cvt<OpT>(to_f4(ldT(V, LX, 16 * q, vcol, lane)) - XS[q]);
+        Rb[q] = cvt<OpT>(to_f4(ldT(V, LXV, 16 * q, vcol, lane)) - XS[q]);
 #pragma unroll
       for (int p = 0; p < NB; ++p) {
         f4 E = zero4();
@@ -536,7 +569,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_scan(FwdArgs a, const
     }
 #pragma unroll
     for (int p = 0; p < NB && !(VAR == V_F1 && S::TFULL); ++p) {
-      f4 R = to_f4(ldT(V, LX, 16 * p, vcol, lane));   // C-layout values of this wave's channels
+      f4 R = to_f4(ldT(V, LXV, 16 * p, vcol, lane));  // C-layout values of this wave's channels
       if (DELTA) R -= XS[p];
       f4 eta4;
       if (PERCH) {
@@ -596,7 +629,7 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_scan(FwdArgs a, const
       for (int q = 0; q + 1 <= p; q += 2) mmap(O, mkp(Eb[q], Eb[q + 1]), ldp(Pm + frag_off(pslot_base(p), q, lane)));
       if (!(p & 1)) mma16(O, Eb[p], ld4(Pm + frag_off(pslot_base(p), p, lane)));
       const int t = c0 + 16 * p + cl;
-      if (t < T) *reinterpret_cast<Frag *>(op + ((size_t)(b * T + t) * H + h) * D + 16 * wv + 4 * g4) = cvt<OpT>(O);
+      if (t < T) *reinterpret_cast<Frag *>(op + ((size_t)(b * T + t) * H + h) * D + Z::DS * sp + 16 * wv + 4 * g4) = cvt<OpT>(O);
     }
     // state: S^T <- e^{L_last} S^T + (diag(CST) X)^T E'
     const Frag *CE = Eb;
@@ -621,79 +654,114 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_scan(FwdArgs a, const
     }
   };
 
-  // ---------------- prologue ----------------
-  if (!consumer) {
+  // ---------------- scan: iteration i consumes chunk i and stages chunk i+1 ----------------
+  // Each role runs its own loop, so neither keeps the other's loop-carried
+  // registers live; both pass the same number of workgroup barriers (one per
+  // chunk after a prologue barrier), which is what the barrier counts.
+  if (consumer) {
+    if (PERCH) prefetch_beta(0);
+    __syncthreads();
+    for (int i = 0; i < NC; ++i) {
+      consume(i);
+      if (PERCH && i + 1 < NC) prefetch_beta(i + 1);
+      __syncthreads();
+    }
+    if (a.S_out) {
+#pragma unroll
+      for (int aa = 0; aa < NA; ++aa)
+        *reinterpret_cast<f4 *>(a.S_out + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) = sT[aa];
+    }
+  } else {
     prefetch(0, reg[0]);
     if (NC > 1) prefetch(1, reg[1]);
     stage(0, reg[0]);
     if (NC > 2) prefetch(2, reg[0]);
-  } else if (PERCH) {
-    prefetch_beta(0);
-  }
-  __syncthreads();
-
-  // ---------------- scan: iteration i consumes chunk i and stages chunk i+1 ----------------
-  // (the register sets are indexed with compile-time parity: two iterations per trip)
-  auto copy_step = [&](int i, Regs &Rnext) __attribute__((always_inline)) {   // Rnext holds chunk i+1; refilled with chunk i+3
-    if (i + 1 < NC) {
-      stage(i + 1, Rnext);
-      if (i + 3 < NC) prefetch(i + 3, Rnext);
-    }
-  };
-  for (int i = 0; i < NC; i += 2) {
-    if (consumer) {
-      consume(i);
-      if (PERCH && i + 1 < NC) prefetch_beta(i + 1);
-    } else {
-      copy_step(i, reg[1]);
-    }
     __syncthreads();
-    if (i + 1 < NC) {
-      if (consumer) {
-        consume(i + 1);
-        if (PERCH && i + 2 < NC) prefetch_beta(i + 2);
-      } else {
-        copy_step(i + 1, reg[0]);
+    // the register sets are indexed with compile-time parity: two iterations per trip;
+    // Rnext holds chunk i+1 and is refilled with chunk i+3
+    auto copy_step = [&](int i, Regs &Rnext) __attribute__((always_inline)) {
+      if (i + 1 < NC) {
+        stage(i + 1, Rnext);
+        if (i + 3 < NC) prefetch(i + 3, Rnext);
       }
+    };
+    for (int i = 0; i < NC; i += 2) {
+      copy_step(i, reg[1]);
       __syncthreads();
+      if (i + 1 < NC) {
+        copy_step(i + 1, reg[0]);
+        __syncthreads();
+      }
+    }
+    if (a.write_tail && a.xprev_out && wv == NCW && sp == 0) {
+      float xv[2] = {0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = lane + 64 * j;
+        if (e < D) xv[j] = to_f(kp[((size_t)(b * T + T - 1) * H + h) * D + e]);
+      }
+      const float ss = group_sum<64>(xv[0] * xv[0] + xv[1] * xv[1]);
+      const float inv = safe_rsqrt(ss + a.eps_phi);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = lane + 64 * j;
+        if (e < D) a.xprev_out[(size_t)bh * D + e] = xv[j] * inv;
+      }
     }
   }
+}
 
-  if (consumer && a.S_out) {
-#pragma unroll
-    for (int aa = 0; aa < NA; ++aa)
-      *reinterpret_cast<f4 *>(a.S_out + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) = sT[aa];
+// Channel splits built per shape: fp32 keeps whole sequences; bf16 takes 1 or
+// 2 slices at d <= 64 and 2, 4 or 8 at d = 128 (whose values do not fit whole).
+template <typename IT, int D>
+constexpr bool ns_built(int ns) {
+  if (sizeof(IT) == 4) return ns == 1;
+  return D <= 64 ? (ns == 1 || ns == 2) : (ns == 2 || ns == 4 || ns == 8);
+}
+template <int VAR, typename IT, int D, int C, int NS>
+constexpr bool scan_ok() { return ns_built<IT, D>(NS) && Scan<VAR, IT, D, C, NS>::fits(); }
+
+// Smallest built split that fits and gives at least 128 scan workgroups (else
+// the largest that fits); 0 when none fits.
+template <int VAR, typename IT, int D, int C>
+int pick_ns(int bh) {
+  const bool ok[4] = {scan_ok<VAR, IT, D, C, 1>(), scan_ok<VAR, IT, D, C, 2>(), scan_ok<VAR, IT, D, C, 4>(),
+                      scan_ok<VAR, IT, D, C, 8>()};
+  int best = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (!ok[i]) continue;
+    best = 1 << i;
+    if (bh * best >= 128) break;
   }
-  if (a.write_tail && a.xprev_out && wv == NCW) {
-    float xv[2] = {0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = lane + 64 * j;
-      if (e < D) xv[j] = to_f(kp[((size_t)(b * T + T - 1) * H + h) * D + e]);
-    }
-    const float ss = group_sum<64>(xv[0] * xv[0] + xv[1] * xv[1]);
-    const float inv = safe_rsqrt(ss + a.eps_phi);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = lane + 64 * j;
-      if (e < D) a.xprev_out[(size_t)bh * D + e] = xv[j] * inv;
-    }
+  return best;
+}
+
+template <int VAR, typename IT, int D, int C, int NS>
+hipError_t launch_scan(const FwdArgs &a, const unsigned char *w, hipStream_t st) {
+  if constexpr (scan_ok<VAR, IT, D, C, NS>()) {
+    hipLaunchKernelGGL((chunk_scan<VAR, IT, D, C, NS>), dim3(a.B * a.H * NS), dim3(Scan<VAR, IT, D, C, NS>::NT), 0,
+                       st, a, w);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
   }
 }
 
 template <int VAR, typename IT, int D, int C>
 hipError_t launch_split(const FwdArgs &a, void *ws, hipStream_t st) {
-  using S = Split<VAR, IT, D, C>;
-  if constexpr (S::fits()) {
-    unsigned char *w = static_cast<unsigned char *>(ws);
-    hipLaunchKernelGGL((chunk_prep<VAR, IT, D, C>), dim3(a.B * a.H * a.nchunks), dim3(256), 0, st, a, w);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_scan<VAR, IT, D, C>), dim3(a.B * a.H), dim3(S::NT), 0, st, a, (const unsigned char *)w);
-    return hipGetLastError();
-  } else {
-    return hipErrorInvalidValue;
+  const int ns = pick_ns<VAR, IT, D, C>(a.B * a.H);
+  if (ns == 0) return hipErrorInvalidValue;
+  unsigned char *w = static_cast<unsigned char *>(ws);
+  hipLaunchKernelGGL((chunk_prep<VAR, IT, D, C>), dim3(a.B * a.H * a.nchunks), dim3(256), 0, st, a, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (ns) {
+    case 1: return launch_scan<VAR, IT, D, C, 1>(a, w, st);
+    case 2: return launch_scan<VAR, IT, D, C, 2>(a, w, st);
+    case 4: return launch_scan<VAR, IT, D, C, 4>(a, w, st);
+    case 8: return launch_scan<VAR, IT, D, C, 8>(a, w, st);
   }
+  return hipErrorInvalidValue;
 }
 
 // Compile-time dispatch over (variant, dtype, d, chunk): `fn` receives the
@@ -714,6 +782,9 @@ auto dispatch_split(int variant, bool bf16, int d, int chunk, Fn &&fn) -> declty
   auto by_d = [&](auto v, auto *t) -> R {
     if (d == 32) return by_chunk(v, t, std::integral_constant<int, 32>());
     if (d == 64) return by_chunk(v, t, std::integral_constant<int, 64>());
+    if constexpr (sizeof(*t) == 2) {
+      if (d == 128) return by_chunk(v, t, std::integral_constant<int, 128>());
+    }
     return R();
   };
   auto by_type = [&](auto v) -> R {
@@ -735,7 +806,7 @@ bool chunk_fwd_split_supported(int variant, bool bf16, int dk, int dv, int chunk
   if (dk != dv) return false;
   return dispatch_split(variant, bf16, dk, chunk, [](auto v, auto *t, auto dd, auto cc) -> bool {
     using IT = std::remove_pointer_t<decltype(t)>;
-    return Split<decltype(v)::value, IT, decltype(dd)::value, decltype(cc)::value>::fits();
+    return pick_ns<decltype(v)::value, IT, decltype(dd)::value, decltype(cc)::value>(1) > 0;
   });
 }
 

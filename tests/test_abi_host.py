@@ -78,14 +78,15 @@ def workspace(**kw):
 
 def test_workspace_size():
     """The chunk-parallel path keeps one image per (sequence, chunk): the size is a
-    multiple of 16 bytes proportional to B*H*ceil(T/C); windowed variants, d = 128
-    and invalid shapes need none."""
+    multiple of 16 bytes proportional to B*H*ceil(T/C); windowed variants, fp32 at
+    d = 128 and invalid shapes need none."""
     w1, w2 = workspace(seqlen=100), workspace(seqlen=200)   # 2 and 4 chunks of 64
     assert w1 > 0 and w1 % 16 == 0 and w2 == 2 * w1
     assert workspace(batch=4, seqlen=100) == 2 * w1
     assert workspace(variant="F1A") < w1                    # no Gram / T blocks
     assert workspace(variant="F3", window=4) == 0
-    assert workspace(dk=128, dv=128) == 0
+    assert workspace(dk=128, dv=128) == w1                  # d = 128 (bf16) too; tiles are C x C
+    assert workspace(dtype="fp32", dk=128, dv=128) == 0
     assert workspace(batch=0) == 0 and workspace(dk=48, dv=48) == 0
 
 

@@ -101,6 +101,27 @@ def test_fused_and_split_paths_agree(variant):
         assert e <= 5e-3, (k, e)   # same arithmetic up to accumulation order and bf16 rounding of tiles
 
 
+# The state scan splits the value channels of a sequence over NS workgroups,
+# chosen from B*H (smallest split giving >= 128 workgroups among those built);
+# when B*H is a multiple of 8 the slices of a sequence share an XCD.  These
+# shapes reach every built split and both workgroup mappings.
+SPLIT_SHAPES = [
+    (64, 8, 16, 130),    # B*H = 128: NS = 1
+    (64, 4, 8, 130),     # B*H = 32: NS = 2, XCD-grouped
+    (64, 1, 5, 130),     # B*H = 5: NS = 2, plain mapping
+    (128, 2, 32, 100),   # NS = 2, XCD-grouped
+    (128, 4, 8, 100),    # NS = 4
+    (128, 1, 6, 100),    # NS = 8, plain mapping
+]
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+@pytest.mark.parametrize("d,B,H,T", SPLIT_SHAPES)
+def test_scan_channel_splits(variant, d, B, H, T):
+    w = W.WORKLOADS["layer130m"].replace(batch=B, heads=H, seqlen=T, dk=d, dv=d)
+    check(variant, w, 23, init=True, chunk_states=True)
+
+
 @pytest.mark.parametrize("variant", ROW_VARIANTS)
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65])
 def test_short_sequences(variant, T):
