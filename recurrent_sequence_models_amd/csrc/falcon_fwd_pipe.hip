@@ -482,71 +482,71 @@ __global__ __launch_bounds__(64 * (D / 16 + 4)) void chunk_fwd_pipe(FwdArgs a) {
     }
   };
 
-  // ---------------- prologue ----------------
-  if (!consumer) {
-    // chunk 0's first key is the incoming x_prev (already a feature: factor 1)
-    for (int e = ptid; e < D; e += P::NPT) sCarry[0][e] = (OpT)(a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f);
-    prefetch(0);
-  } else if (PERCH) {
-    prefetch_beta(0);
-  }
-  if (pw == 0) {
-    float s = 0.f;
-    for (int e = lane; e < D; e += 64) {
-      const float x = a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f;
-      s += x * x;
-    }
-    s = group_sum<64>(s);
-    if (lane == 0) {
-      const float inv = fast_rcp(a.eps_eta + s);
-      const float eta = PERCH ? inv : a.beta[(size_t)(b * T) * H + h] * inv;
-      sCarryF[0][0] = 1.f;
-      sCarryF[0][1] = PERCH ? 1.f : eta;
-      sCarryF[0][2] = eta;
-    }
-  }
-  __syncthreads();
-  if (!consumer) {
-    stage(0);
-    if (NC > 1) prefetch(1);
-  }
-  __syncthreads();
-
-  // ---------------- pipeline: iteration i derives chunk i, stages i+1, consumes i-1 ----------------
-  for (int i = 0; i <= NC; ++i) {
-    if (consumer) {
+  // Each role runs its own loop, so neither keeps the other's loop-carried
+  // registers live; both pass the same number of workgroup barriers (two in the
+  // prologue, then one per iteration), which is what the barrier counts.
+  if (consumer) {
+    if (PERCH) prefetch_beta(0);
+    __syncthreads();
+    __syncthreads();
+    // iteration i consumes chunk i-1 while the producers derive chunk i and stage i+1
+    for (int i = 0; i <= NC; ++i) {
       if (i >= 1) {
         consume(i - 1);
         if (PERCH && i < NC) prefetch_beta(i);
       }
-    } else {
+      __syncthreads();
+    }
+    if (a.S_out) {
+#pragma unroll
+      for (int aa = 0; aa < NA; ++aa)
+        *reinterpret_cast<f4 *>(a.S_out + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) = sT[aa];
+    }
+  } else {
+    // chunk 0's first key is the incoming x_prev (already a feature: factor 1)
+    for (int e = ptid; e < D; e += P::NPT) sCarry[0][e] = (OpT)(a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f);
+    prefetch(0);
+    if (pw == 0) {
+      float s = 0.f;
+      for (int e = lane; e < D; e += 64) {
+        const float x = a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f;
+        s += x * x;
+      }
+      s = group_sum<64>(s);
+      if (lane == 0) {
+        const float inv = fast_rcp(a.eps_eta + s);
+        const float eta = PERCH ? inv : a.beta[(size_t)(b * T) * H + h] * inv;
+        sCarryF[0][0] = 1.f;
+        sCarryF[0][1] = PERCH ? 1.f : eta;
+        sCarryF[0][2] = eta;
+      }
+    }
+    __syncthreads();
+    stage(0);
+    if (NC > 1) prefetch(1);
+    __syncthreads();
+    for (int i = 0; i <= NC; ++i) {
       if (i + 1 < NC) {
         stage(i + 1);
         if (i + 2 < NC) prefetch(i + 2);
       }
       if (i < NC) derive(i);
+      __syncthreads();
     }
-    __syncthreads();
-  }
-
-  if (consumer && a.S_out) {
+    if (a.write_tail && a.xprev_out && pw == 0) {
+      float xv[2] = {0.f, 0.f};
 #pragma unroll
-    for (int aa = 0; aa < NA; ++aa)
-      *reinterpret_cast<f4 *>(a.S_out + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) = sT[aa];
-  }
-  if (a.write_tail && a.xprev_out && pw == 0) {
-    float xv[2] = {0.f, 0.f};
+      for (int j = 0; j < 2; ++j) {
+        const int e = lane + 64 * j;
+        if (e < D) xv[j] = to_f(kp[((size_t)(b * T + T - 1) * H + h) * D + e]);
+      }
+      const float s = group_sum<64>(xv[0] * xv[0] + xv[1] * xv[1]);
+      const float inv = safe_rsqrt(s + a.eps_phi);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = lane + 64 * j;
-      if (e < D) xv[j] = to_f(kp[((size_t)(b * T + T - 1) * H + h) * D + e]);
-    }
-    const float s = group_sum<64>(xv[0] * xv[0] + xv[1] * xv[1]);
-    const float inv = safe_rsqrt(s + a.eps_phi);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int e = lane + 64 * j;
-      if (e < D) a.xprev_out[(size_t)bh * D + e] = xv[j] * inv;
+      for (int j = 0; j < 2; ++j) {
+        const int e = lane + 64 * j;
+        if (e < D) a.xprev_out[(size_t)bh * D + e] = xv[j] * inv;
+      }
     }
   }
 }
