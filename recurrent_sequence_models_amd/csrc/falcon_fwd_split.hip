@@ -9,9 +9,10 @@
 //   * the residuals, outputs and the state update of chunk c need S at its start.
 // The prep kernel runs one workgroup per chunk over the whole device and writes
 // the first group, per chunk, as an "image": the exact LDS layout the scan
-// reads.  The scan kernel runs one workgroup per sequence: copy waves stream
-// the raw q / k / v rows and the chunk image into double-buffered LDS one chunk
-// ahead, and one consumer wave per 16 value channels carries S^T in registers.
+// reads.  The scan kernel runs one to eight workgroups per sequence (slices of
+// the value channels): copy waves stream the key / query rows, the slice's
+// values and the chunk image into double-buffered LDS one chunk ahead, and one
+// consumer wave per 16 value channels carries S^T in registers.
 // ([P1] = zhouql-dev.github.io "把状态更新写成一条学习规则：Falcon 家族重新对齐
 // fast-weight 记忆"; [P2] = 59188saintaubert.com "给记忆装一个“及时纠错”的开关：
 // Falcon让循环模型学会边写边改".)
@@ -34,7 +35,14 @@ namespace falcon {
 namespace {
 
 // per-row arrays of the prep kernel
-enum { R_LC = 0, R_LM, R_IK, R_IQ, R_CF, R_ETA, R_N };
+enum {
+  R_LC = 0, R_LM, R_IK, R_IQ, R_CF, R_ETA,
+  // separable decay factors around L_ref = L_last / 2 (used while |L_last| <= 160):
+  R_EP,   // e^{L_i - L_ref} IQ_i       rows of score blocks
+  R_EA,   // e^{L_{i-1} - L_ref} IK_i   rows of Gram blocks
+  R_EC,   // e^{L_ref - L_j} CF_j       columns of both
+  R_N
+};
 // per-row factors in the image (consumers)
 enum {
   F_GAM = 0,  // e^{L_{i-1}} * IK_i
@@ -91,13 +99,13 @@ struct Split {
 
 // The scan of one sequence is split over NS workgroups by value channel (rows
 // of S evolve independently given the keys): each takes D/NS channels with
-// one consumer wave per 16 of them, plus 4 (d = 128: 8) copy waves that stage the shared
+// one consumer wave per 16 of them, plus 8 copy waves that stage the shared
 // key / query rows and chunk image and its own value columns.
 template <int VAR, typename IT, int D, int C, int NS>
 struct Scan {
   using S = Split<VAR, IT, D, C>;
   static constexpr int DS = D / NS;                          // value channels per workgroup
-  static constexpr int NCW = DS / 16, NSW = D == 128 ? 8 : 4, NT = 64 * (NCW + NSW), NST = 64 * NSW;
+  static constexpr int NCW = DS / 16, NSW = 8, NT = 64 * (NCW + NSW), NST = 64 * NSW;
   static constexpr int LXV = DS + S::PADE;                   // V rows (this workgroup's channels)
   static constexpr int RPC = NST / S::TPR, NPK = (C + RPC - 1) / RPC;   // key / query rows per copy pass
   static constexpr int TPV = DS / S::VEC, RPV = NST / TPV, NPV = (C + RPV - 1) / RPV;
@@ -229,6 +237,19 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
     }
   }
   __syncthreads();
+  // e^{L_i - L_j} = e^{L_i - L_ref} e^{L_ref - L_j}: each factor stays within
+  // e^{+-80} while the chunk's total log-decay is >= -160, so both are normal
+  // fp32 numbers and the product keeps fp32 relative accuracy; deeper decays
+  // (a long run of floored steps) keep the per-element exponential.
+  const float Llast = sR[R_LC * C + C - 1];
+  const bool sep = Llast >= -160.f;
+  if (sep && pw == 0 && lane < C) {
+    const float Lref = 0.5f * Llast;
+    sR[R_EP * C + lane] = __expf(sR[R_LC * C + lane] - Lref) * sR[R_IQ * C + lane];
+    sR[R_EA * C + lane] = __expf(sR[R_LM * C + lane] - Lref) * sR[R_IK * C + lane];
+    sR[R_EC * C + lane] = __expf(Lref - sR[R_LC * C + lane]) * sR[R_CF * C + lane];
+  }
+  __syncthreads();
 
   const OpT *X = sX, *Q = sQ;
   const float *G = sR;
@@ -245,16 +266,26 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
   // Gram (isP = 0) or score (isP = 1) block (p, q), transposed: lane (g, c) holds
   // element (row 16p + c, col 16q + 4g + i), the consumers' A-operand fragment.
   auto finish = [&](const f4 &acc, int isP, int p, int q) {
-    const f4 cf = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * q + 4 * g4);
-    const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * q + 4 * g4);
     const int row = 16 * p + cl;
-    const float Lrow = G[(isP ? R_LC : R_LM) * C + row];
-    const float rf = G[(isP ? R_IQ : R_IK) * C + row];
     f4 val;
+    if (sep) {
+      const f4 ec = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * q + 4 * g4);
+      const float er = G[(isP ? R_EP : R_EA) * C + row];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = acc[i] * __expf(Lrow - Lc4[i]) * rf * cf[i];
-      val[i] = (p > q || 4 * g4 + i <= cl) ? v : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] * er * ec[i];
+        val[i] = (p > q || 4 * g4 + i <= cl) ? v : 0.f;
+      }
+    } else {
+      const f4 cf = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * q + 4 * g4);
+      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * q + 4 * g4);
+      const float Lrow = G[(isP ? R_LC : R_LM) * C + row];
+      const float rf = G[(isP ? R_IQ : R_IK) * C + row];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] * __expf(Lrow - Lc4[i]) * rf * cf[i];
+        val[i] = (p > q || 4 * g4 + i <= cl) ? v : 0.f;
+      }
     }
     if (S::TFULL && !isP) {   // F1 keeps A in fp32 for the inverse
 #pragma unroll
@@ -267,19 +298,30 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
   // diagonal block p: F1 -> T_pp (A-layout); F2 -> the 4x4 diagonal coefficients and A_pp without them
   auto diag = [&](const f4 &acc, int p) {   // acc: <x_{16p+4g+i}, x_{16p+c}> (symmetric)
     const int r0 = 4 * g4;
-    const f4 cf4 = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * p + r0);
-    const f4 ik4 = *reinterpret_cast<const f4 *>(G + R_IK * C + 16 * p + r0);
-    const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * p + r0);
-    const f4 Lm4 = *reinterpret_cast<const f4 *>(G + R_LM * C + 16 * p + r0);
-    const float Lc1 = G[R_LC * C + 16 * p + cl], Lm1 = G[R_LM * C + 16 * p + cl];
-    const float ik1 = G[R_IK * C + 16 * p + cl], cf1 = G[R_CF * C + 16 * p + cl];
     f4 NA4, NC4;   // N[16p+c][16p+4g+i] (A-layout) and N[16p+4g+i][16p+c] (C-layout)
+    if (sep) {
+      const f4 ea4 = *reinterpret_cast<const f4 *>(G + R_EA * C + 16 * p + r0);
+      const f4 ec4 = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * p + r0);
+      const float ea1 = G[R_EA * C + 16 * p + cl], ec1 = G[R_EC * C + 16 * p + cl];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float va = acc[i] * __expf(Lm1 - Lc4[i]) * ik1 * cf4[i];
-      const float vc = acc[i] * __expf(Lm4[i] - Lc1) * ik4[i] * cf1;
-      NA4[i] = (r0 + i < cl) ? va : 0.f;
-      NC4[i] = (cl < r0 + i) ? vc : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        NA4[i] = (r0 + i < cl) ? acc[i] * ea1 * ec4[i] : 0.f;
+        NC4[i] = (cl < r0 + i) ? acc[i] * ea4[i] * ec1 : 0.f;
+      }
+    } else {
+      const f4 cf4 = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * p + r0);
+      const f4 ik4 = *reinterpret_cast<const f4 *>(G + R_IK * C + 16 * p + r0);
+      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * p + r0);
+      const f4 Lm4 = *reinterpret_cast<const f4 *>(G + R_LM * C + 16 * p + r0);
+      const float Lc1 = G[R_LC * C + 16 * p + cl], Lm1 = G[R_LM * C + 16 * p + cl];
+      const float ik1 = G[R_IK * C + 16 * p + cl], cf1 = G[R_CF * C + 16 * p + cl];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float va = acc[i] * __expf(Lm1 - Lc4[i]) * ik1 * cf4[i];
+        const float vc = acc[i] * __expf(Lm4[i] - Lc1) * ik4[i] * cf1;
+        NA4[i] = (r0 + i < cl) ? va : 0.f;
+        NC4[i] = (cl < r0 + i) ? vc : 0.f;
+      }
     }
     if constexpr (VAR == V_F1) {
       // row-oriented block Jacobi: T (I + N) = I, so T <- (I - T N_o)(I + N_d)^{-1},
@@ -401,7 +443,7 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
 
 // ============================== scan kernel ==============================
 template <int VAR, typename IT, int D, int C, int NS>
-__global__ __launch_bounds__(64 * (D / 16 / NS + (D == 128 ? 8 : 4))) void chunk_scan(FwdArgs a, const unsigned char *ws) {
+__global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, const unsigned char *ws) {
   using S = Split<VAR, IT, D, C>;
   using Z = Scan<VAR, IT, D, C, NS>;
   using OpT = IT;
