@@ -116,7 +116,8 @@ def bench_decode(args):
     }
 
 
-KERNEL_SOURCES = ("falcon_fwd_split.hip", "falcon_fwd_pipe.hip", "chunk_common.h", "mfma_frag.h", "falcon_kernels.h")
+KERNEL_SOURCES = ("split_impl.h", "falcon_fwd_split.hip", "falcon_fwd_split_win.hip", "falcon_fwd_pipe.hip",
+                  "chunk_common.h", "mfma_frag.h", "falcon_kernels.h")
 
 
 def measured_traffic(key):

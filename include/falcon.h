@@ -114,9 +114,13 @@ const char *falcon_status_string(int status);
 /* Bytes of device workspace that enable the chunk-parallel path of
  * falcon_chunk_fwd for this shape; 0 when that path does not apply (the
  * forward then runs a fused kernel that needs no workspace).  The workspace
- * holds, per chunk, the key-side factors (Gram / score blocks, diagonal-block
- * inverses, per-row factors) that a prep kernel over all chunks writes and the
- * state scan reads; its contents are scratch and need no initialisation.
+ * holds, per system of rows (a chunk of C steps; for F3/F3A with Bw > 1,
+ * C/Bw steps of Bw pairs each), the key-side factors (Gram / score blocks,
+ * diagonal-block inverses, per-row factors) that a prep kernel over all
+ * systems writes and the state scan reads, plus a copy of each sequence's
+ * incoming x_prev and window; its contents are scratch and need no
+ * initialisation.  The path covers F1/F1A/F2/F2A (chunk 16, 32, 64) and
+ * F3/F3A with Bw = 2, 4, 8 at chunk 64; d = 32, 64 (fp32, bf16), 128 (bf16).
  * Returns 0 for an invalid shape as well; validation is the forward call's job. */
 size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape);
 

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfalcon.so")
 
-SOURCES = ["falcon_abi.cpp", "falcon_fwd.hip", "falcon_fwd_pipe.hip", "falcon_fwd_split.hip", "falcon_fwd3.hip",
+SOURCES = ["falcon_abi.cpp", "falcon_fwd.hip", "falcon_fwd_pipe.hip", "falcon_fwd_split.hip", "falcon_fwd_split_win.hip",
+           "falcon_fwd3.hip",
            "falcon_step.hip"]
 ARCH = "gfx950"
 FLAGS = [

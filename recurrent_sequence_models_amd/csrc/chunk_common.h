@@ -12,7 +12,7 @@
 namespace falcon {
 namespace {
 
-enum { V_F1 = 1, V_F1A = 2, V_F2 = 3, V_F2A = 4 };
+enum { V_F1 = 1, V_F1A = 2, V_F2 = 3, V_F2A = 4, V_F3 = 5, V_F3A = 6 };
 
 // Hardware reciprocal square root / reciprocal (about 1 ulp); arguments are
 // bounded away from zero and denormals by eps_phi and eps_eta.
@@ -136,6 +136,54 @@ constexpr JobList make_jobs(int nb, bool delta, int w) {
     if (delta) dg[0] = 0;
     put(1, 1, 0, 0);
   }
+  J.diag = dg[w];
+  J.n = n[w];
+  for (int j = 0; j < n[w]; ++j) {
+    J.isP[j] = t[w][j][0];
+    J.p[j] = t[w][j][1];
+    J.q[j] = t[w][j][2];
+  }
+  return J;
+}
+
+// Score blocks with a window of bw pairs per step: the rows are the cs steps of a
+// system (blocks of 16), the columns its 16*nb virtual rows (step r / bw).  Row
+// block ps sees columns up to its last step, i.e. column blocks 0..score_qmax.
+// With bw = 1 this is q <= ps.
+constexpr int score_qmax(int ps, int nb, int cs, int bw) {
+  const int smax = (16 * ps + 15 < cs - 1) ? 16 * ps + 15 : cs - 1;
+  const int q = (smax * bw + bw - 1) / 16;
+  return q < nb - 1 ? q : nb - 1;
+}
+// first fragment-pair slot of score-block row ps (pairs of column blocks)
+constexpr int score_base(int ps, int nb, int cs, int bw) {
+  int b = 0;
+  for (int i = 0; i < ps; ++i) b += score_qmax(i, nb, cs, bw) / 2 + 1;
+  return b;
+}
+
+// Tiles of a windowed system (nb <= 4 virtual-row blocks): one diagonal block per
+// wave, then Gram and score tiles each to the least loaded wave.
+constexpr JobList make_jobs_win(int nb, int cs, int bw, bool delta, int w) {
+  JobList J{-1, 0, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  int t[4][4][3] = {};
+  int n[4] = {0, 0, 0, 0}, load[4] = {0, 0, 0, 0};
+  int dg[4] = {-1, -1, -1, -1};
+  auto put = [&](int isP, int p, int q) {
+    int k = 0;
+    for (int i = 1; i < 4; ++i)
+      if (load[i] < load[k]) k = i;
+    t[k][n[k]][0] = isP; t[k][n[k]][1] = p; t[k][n[k]][2] = q;
+    ++n[k];
+    ++load[k];
+  };
+  if (delta) {
+    for (int p = 0; p < nb; ++p) { dg[p] = p; load[p] = 1; }
+    for (int p = 1; p < nb; ++p)
+      for (int q = 0; q < p; ++q) put(0, p, q);
+  }
+  for (int ps = 0; ps < (cs + 15) / 16; ++ps)
+    for (int q = 0; q <= score_qmax(ps, nb, cs, bw); ++q) put(1, ps, q);
   J.diag = dg[w];
   J.n = n[w];
   for (int j = 0; j < n[w]; ++j) {

@@ -71,10 +71,10 @@ hipError_t launch_chunk_fwd_rows(int variant, bool bf16, int dk, int dv, int chu
 hipError_t launch_chunk_fwd_window(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
                                    const FwdArgs &a, hipStream_t s);
 bool chunk_fwd_pipe_supported(int variant, bool bf16, int dk, int dv, int chunk);
-bool chunk_fwd_split_supported(int variant, bool bf16, int dk, int dv, int chunk);
-size_t chunk_fwd_split_workspace(int variant, bool bf16, int dk, int dv, int chunk, int bhc);
-hipError_t launch_chunk_fwd_split(int variant, bool bf16, int dk, int dv, int chunk, const FwdArgs &a, void *ws,
-                                  hipStream_t s);
+bool chunk_fwd_split_supported(int variant, bool bf16, int dk, int dv, int chunk, int window);
+size_t chunk_fwd_split_workspace(int variant, bool bf16, int dk, int dv, int chunk, int window, int bh, int T);
+hipError_t launch_chunk_fwd_split(int variant, bool bf16, int dk, int dv, int chunk, int window, const FwdArgs &a,
+                                  void *ws, hipStream_t s);
 
 int choose_nsplit(int variant, bool bf16, int dk, int dv, int chunk, int batch_heads) {
   int n = 1;
@@ -114,11 +114,11 @@ const char *falcon_status_string(int status) {
 
 size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape) {
   if (check_shape(shape, false) != FALCON_OK) return 0;
-  if (windowed(shape->variant)) return 0;
-  const int64_t bhc = (int64_t)shape->batch * shape->heads * ((shape->seqlen + shape->chunk - 1) / shape->chunk);
-  if (bhc > INT32_MAX) return 0;
+  // one image per system of rows (at least one step each) must have an int index
+  const int64_t bhs = (int64_t)shape->batch * shape->heads * shape->seqlen;
+  if (bhs > INT32_MAX) return 0;
   return falcon::chunk_fwd_split_workspace(shape->variant, shape->dtype == FALCON_BF16, shape->dk, shape->dv,
-                                           shape->chunk, (int)bhc);
+                                           shape->chunk, shape->window, shape->batch * shape->heads, shape->seqlen);
 }
 
 int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, const void *v,
@@ -157,15 +157,17 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   a.log_eps_gamma = std::log(s->eps_gamma);
   a.eps_phi = s->eps_phi;
   a.eps_eta = s->eps_eta;
-  // The main kernel writes x_prev itself when that cannot race with another
-  // workgroup still reading the incoming x_prev: one workgroup per sequence, or
-  // the two buffers are distinct.  Otherwise (and for windows) a tail kernel does.
+  // The main kernel writes x_prev (and the window) itself when that cannot race
+  // with another workgroup still reading the incoming state: on the split path
+  // (its scan reads a copy the prep kernel made), with one workgroup per
+  // sequence, or when the two buffers are distinct.  Otherwise a tail kernel does.
   const bool xprev_alias = init && final_state && init->x_prev == final_state->x_prev;
-  a.write_tail = (final_state && !win && (split || nsplit == 1 || !xprev_alias)) ? 1 : 0;
+  a.write_tail = (final_state && (split || (!win && (nsplit == 1 || !xprev_alias)))) ? 1 : 0;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (split) {   // prep over all chunks, then one scan workgroup per sequence
-    return falcon::launch_chunk_fwd_split(s->variant, bf16, s->dk, s->dv, s->chunk, a, workspace, hs) == hipSuccess
+  if (split) {   // prep over all systems, then the scan workgroups of each sequence
+    return falcon::launch_chunk_fwd_split(s->variant, bf16, s->dk, s->dv, s->chunk, a.window, a, workspace, hs) ==
+                   hipSuccess
                ? FALCON_OK
                : FALCON_ERR_HIP;
   }

@@ -1,0 +1,915 @@
+// Chunk-parallel ("split") forward pass of Falcon-1 / 1A / 2 / 2A / 3 / 3A on
+// gfx950: the two kernels and their launch templates.  falcon_fwd_split.hip
+// instantiates them with one pair per step, falcon_fwd_split_win.hip with the
+// Falcon-3 windows.
+//
+// The chunked form ([P1] 三种等价形式 form C and Figure 4-C; [P2] 三种视角)
+// separates what depends on the carried state from what does not:
+//   * everything built from keys, queries and gates of one system of rows -- the
+//     decayed Gram blocks A_pq, the score blocks P_pq, the diagonal-block
+//     inverses T_pp (F1 / F3) or the Falcon-2 diagonal blocks, and the per-row
+//     decay / norm / step factors -- is independent across systems;
+//   * the residuals, outputs and the state update of a system need S at its start.
+// The prep kernel runs one workgroup per system over the whole device and writes
+// the first group, per system, as an "image": the exact LDS layout the scan
+// reads.  The scan kernel runs one to eight workgroups per sequence (slices of
+// the value channels): copy waves stream the key / query rows, the slice's
+// values and the image into double-buffered LDS one system ahead, and one
+// consumer wave per 16 value channels carries S^T in registers.
+//
+// Windows (Falcon-3 / 3A, [P1] Falcon家族, [P2] 六个变体): step s writes the Bw
+// pairs j = s-Bw+1..s, each weighted w_s = eta_s / Bw and each with a residual
+// against S_{s-1}.  A system then has C "virtual rows" r = (s, j), s = r / Bw,
+// j = s - Bw + 1 + r % Bw, covering CS = C / Bw steps: Gram blocks run over
+// virtual rows with the mask s(r') < s(r), score blocks over (step, virtual
+// row) with s(r') <= s, and the state update over virtual rows.  Bw = 1 is the
+// one-pair case (CS = C, r = s = j).  The public chunk (chunk_states cadence) is
+// C steps, i.e. Bw systems.
+// ([P1] = zhouql-dev.github.io "把状态更新写成一条学习规则：Falcon 家族重新对齐
+// fast-weight 记忆"; [P2] = 59188saintaubert.com "给记忆装一个“及时纠错”的开关：
+// Falcon让循环模型学会边写边改".)
+//
+// Image of one system (bytes, tiles in the input dtype, fragment pairs of 64
+// lanes x 8 elements; slots hold only the tiles that exist):
+//   A   : A_pq, q < p (F1 / F2 / F3)  -- pair slot aslot_base(p) + q/2, half q&1
+//   P   : P_pq (step block p, virtual-row block q <= qmax(p))
+//                                      -- pair slot pbase(p) + q/2, half q&1
+//   T   : F1 / F3: T_pp = (I + A_pp)^{-1}; F2: A_pp without its 4x4 diagonal
+//         sub-blocks; one fragment per diagonal block
+//   AD  : F2 only, the 6 coefficients of each 4x4 diagonal sub-block (8 floats)
+//   F   : per-row GAM, EL, CST, ETA (fp32, C each) and e^{L_last}
+// After the images, one "carry" block per sequence holds the incoming x_prev
+// (and window): the scan reads that copy, never the caller's incoming state,
+// which the outgoing state may alias.
+#pragma once
+#include "chunk_common.h"
+#include "falcon_kernels.h"
+
+namespace falcon {
+
+namespace {
+
+// per-row arrays of the prep kernel (index: virtual row r, or step row s)
+enum {
+  R_LC = 0,  // L_{s(r)}            inclusive log-decay of the row's step
+  R_LM,      // L_{s(r)-1}
+  R_IK,      // 1/|k| of the row's key (1 for carried features)
+  R_IQ,      // 1/|q_s|             step rows
+  R_CF,      // IK_r w_{s(r)} (F1/F3), IK_r (F2/F2A), IK_r (F1A/F3A: w folded too)
+  R_ETA,     // w_{s(r)}, or 1/(eps + |x_r|^2) for F2/F2A
+  // separable decay factors around L_ref = L_last / 2 (used while L_last >= -160):
+  R_EP,      // e^{L_s - L_ref} IQ_s      step rows of score blocks
+  R_EA,      // e^{L_{s(r)-1} - L_ref} IK_r   rows of Gram blocks
+  R_EC,      // e^{L_ref - L_{s(r)}} CF_r     columns of both
+  // windows only:
+  R_LQ,      // L_s                       step rows
+  R_GQ,      // clamped log-decay of step s
+  R_E2,      // |x_r|^2 of the normalised key
+  R_BQ,      // beta_s
+  R_N
+};
+// per-row factors in the image (consumers)
+enum {
+  F_GAM = 0,  // e^{L_{s(r)-1}} * IK_r        virtual rows
+  F_EL,       // e^{L_s} * IQ_s               step rows
+  F_CST,      // e^{L_last - L_{s(r)}} * CF_r virtual rows
+  F_ETA,      // 1/(eps + |x_r|^2)  (Falcon-2 / 2A)
+  F_N
+};
+
+constexpr int aslot_base(int p) {
+  int b = 0;
+  for (int i = 1; i < p; ++i) b += (i - 1) / 2 + 1;
+  return b;
+}
+
+template <int VAR, typename IT, int D, int C, int BW>
+struct Split {
+  static_assert(16 % BW == 0 && C % 16 == 0, "steps must not straddle 16-row blocks");
+  static constexpr bool PERCH = (VAR == V_F2 || VAR == V_F2A);
+  static constexpr bool DELTA = (VAR == V_F1 || VAR == V_F2 || VAR == V_F3);
+  static constexpr bool SDELTA = (VAR == V_F1 || VAR == V_F3);   // scalar step: T_pp per block
+  static constexpr int NB = C / 16, NA = D / 16;
+  static constexpr int CS = C / BW;                          // steps per system
+  static constexpr int NBS = (CS + 15) / 16, CSP = 16 * NBS; // step rows, whole tiles
+  static constexpr int RLQ = BW == 1 ? R_LC : R_LQ;          // L of a step row
+  static constexpr int qmax(int ps) { return score_qmax(ps, NB, CS, BW); }
+  static constexpr int pbase(int ps) { return score_base(ps, NB, CS, BW); }
+  static constexpr int FRAG = 64 * 8;                        // elements of one fragment pair
+  static constexpr int SZ = (int)sizeof(IT);
+  static constexpr int NSP = pbase(NBS), NSA = DELTA ? aslot_base(NB) : 0;
+  static constexpr int OFF_A = 0;
+  static constexpr int OFF_P = OFF_A + NSA * FRAG * SZ;
+  static constexpr int OFF_T = OFF_P + NSP * FRAG * SZ;
+  static constexpr int OFF_AD = OFF_T + (DELTA ? NB * 256 * SZ : 0);
+  static constexpr int OFF_F = OFF_AD + (VAR == V_F2 ? NB * 32 * 4 : 0);
+  static constexpr int IMG = ((OFF_F + (F_N * C + 4) * 4) + 15) / 16 * 16;
+  static constexpr int NU = IMG / 16;                        // 16-byte units of the image
+  // carry block: x_prev [D], window keys [BW-1][D], window values [BW-1][D] (fp32)
+  static constexpr int CARRY = ((2 * BW - 1) * D * 4 + 15) / 16 * 16;
+  // shared
+  static constexpr int PADE = 16 / SZ, VEC = PADE;
+  static constexpr int LX = D + PADE;                        // X, Q rows (dk permuted), V rows
+  static constexpr int TPR = D / VEC;                        // threads per input row
+  // prep kernel: 4 waves, one system
+  static constexpr int NPW = 4, NPT = 256;
+  static constexpr int RPP = NPT / TPR, NPASS = (C + RPP - 1) / RPP;
+  static constexpr size_t prep_lds() { return (size_t)SZ * (C + CSP) * LX + 4 * R_N * C; }
+  __host__ __device__ static int nsys(int T) { return (T + CS - 1) / CS; }
+  static size_t workspace(int bh, int T) { return (size_t)bh * nsys(T) * IMG + (size_t)bh * CARRY; }
+};
+
+// The scan of one sequence is split over NS workgroups by value channel (rows
+// of S evolve independently given the keys): each takes D/NS channels with
+// one consumer wave per 16 of them, plus 8 copy waves that stage the shared
+// key / query rows and system image and its own value columns.
+template <int VAR, typename IT, int D, int C, int BW, int NS>
+struct Scan {
+  using S = Split<VAR, IT, D, C, BW>;
+  static constexpr int DS = D / NS;                          // value channels per workgroup
+  static constexpr int NCW = DS / 16, NSW = 8, NT = 64 * (NCW + NSW), NST = 64 * NSW;
+  static constexpr int LXV = DS + S::PADE;                   // V rows (this workgroup's channels)
+  static constexpr int RPC = NST / S::TPR, NPK = (C + RPC - 1) / RPC;   // key / query rows per copy pass
+  static constexpr int TPV = DS / S::VEC, RPV = NST / TPV, NPV = (C + RPV - 1) / RPV;
+  static constexpr int NPI = (S::NU + NST - 1) / NST;
+  static constexpr size_t lds() {
+    return (size_t)S::SZ * 2 * ((2 * C + S::CSP) * S::LX + C * LXV) + 2 * (size_t)S::IMG;
+  }
+  static constexpr bool fits() {
+    return DS >= 16 && D % NS == 0 && lds() + 256 <= 160 * 1024 && S::prep_lds() + 256 <= 64 * 1024;
+  }
+};
+
+// fragment-native element offset of tile (.., q) in a pair buffer whose row of pairs starts at slot `base`
+__device__ __forceinline__ int frag_off(int base, int q, int lane) { return ((base + (q >> 1)) * 64 + lane) * 8 + (q & 1) * 4; }
+
+// store VEC raw elements (one 16-byte vector) of logical columns k0..k0+VEC-1 in a dk-permuted row
+template <typename OpT>
+__device__ __forceinline__ void put_perm(OpT *row, int k0, const uint4 &u) {
+  if constexpr (sizeof(OpT) == 2) {   // 8 elements = two groups of 4, each contiguous after kperm
+    *reinterpret_cast<uint2 *>(row + kperm(k0)) = uint2{u.x, u.y};
+    *reinterpret_cast<uint2 *>(row + kperm(k0 + 4)) = uint2{u.z, u.w};
+  } else {
+    *reinterpret_cast<uint4 *>(row + kperm(k0)) = u;
+  }
+}
+
+// VEC fp32 values of a carried feature, converted to the operand type
+template <typename OpT, int VEC>
+__device__ __forceinline__ uint4 pack_feature(const float *x, float &ss) {
+  OpT tmp[VEC];
+  ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    tmp[e] = (OpT)x[e];
+    ss += x[e] * x[e];
+  }
+  return *reinterpret_cast<const uint4 *>(tmp);
+}
+
+// VEC raw values scaled by f, in the operand type (one 16-byte vector)
+template <typename OpT, int VEC>
+__device__ __forceinline__ uint4 scale_pack(const float *x, float f) {
+  OpT tmp[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) tmp[e] = (OpT)(x[e] * f);
+  return *reinterpret_cast<const uint4 *>(tmp);
+}
+
+// ============================== prep kernel ==============================
+template <int VAR, typename IT, int D, int C, int BW>
+__global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) {
+  using S = Split<VAR, IT, D, C, BW>;
+  using OpT = IT;
+  using Frag = typename Op<OpT>::frag;
+  using Pr = Pair<OpT>;
+  constexpr int NB = S::NB, NA = S::NA, LX = S::LX, VEC = S::VEC, TPR = S::TPR, RPP = S::RPP;
+  constexpr int CS = S::CS, CSP = S::CSP, RLQ = S::RLQ;
+  constexpr bool PERCH = S::PERCH, DELTA = S::DELTA;
+
+  __shared__ __attribute__((aligned(16))) OpT sX[C * LX];     // raw key of each virtual row, dk permuted
+  __shared__ __attribute__((aligned(16))) OpT sQ[CSP * LX];   // raw q of each step row, dk permuted
+  __shared__ __attribute__((aligned(16))) float sR[R_N * C];
+
+  const int tid = threadIdx.x, lane = tid & 63, pw = tid >> 6;
+  const int g4 = lane >> 4, cl = lane & 15;
+  const int T = a.T, H = a.H, NSYS = S::nsys(T);
+  const int bh = blockIdx.x / NSYS, c = blockIdx.x % NSYS, b = bh / H, h = bh % H, c0 = c * CS;
+  const IT *qp = static_cast<const IT *>(a.q);
+  const IT *kp = static_cast<const IT *>(a.k);
+  unsigned char *img = ws + (size_t)blockIdx.x * S::IMG;
+  OpT *gA = reinterpret_cast<OpT *>(img + S::OFF_A);
+  OpT *gP = reinterpret_cast<OpT *>(img + S::OFF_P);
+  OpT *gT = reinterpret_cast<OpT *>(img + S::OFF_T);
+  float *gAd = reinterpret_cast<float *>(img + S::OFF_AD);
+  float *gF = reinterpret_cast<float *>(img + S::OFF_F);
+
+  if (c == 0) {   // the sequence's carry block
+    float *carry = reinterpret_cast<float *>(ws + (size_t)a.B * H * NSYS * S::IMG + (size_t)bh * S::CARRY);
+    for (int e = tid; e < D; e += S::NPT) carry[e] = a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f;
+    for (int e = tid; e < (BW - 1) * D; e += S::NPT) {
+      carry[D + e] = a.winx0 ? a.winx0[(size_t)bh * (BW - 1) * D + e] : 0.f;
+      carry[BW * D + e] = a.winv0 ? a.winv0[(size_t)bh * (BW - 1) * D + e] : 0.f;
+    }
+  }
+
+  if constexpr (BW == 1) {
+    // X row r holds k_{c0+r-1} (x_prev for the first row of the sequence), Q row r holds q_{c0+r}
+#pragma unroll
+    for (int ps = 0; ps < S::NPASS; ++ps) {
+      const int r = ps * RPP + tid / TPR, part = tid % TPR;
+      if (r < C) {
+        const int tk = c0 + r - 1, tq = c0 + r;
+        // loads use in-bounds (clamped) rows; rows outside the sequence are zeroed after the load
+        const int tkc = min(max(tk, 0), T - 1), tqc = min(tq, T - 1);
+        const uint4 kraw = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tkc) * H + h) * D + part * VEC);
+        const uint4 qraw = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tqc) * H + h) * D + part * VEC);
+        uint4 k4 = keep_or_zero(tk >= 0 && tk < T, kraw);
+        const uint4 q4 = keep_or_zero(tq < T, qraw);
+        float xv[VEC], qv[VEC];
+        float sk = 0.f, sq = 0.f;
+        if (tk < 0) {   // the carried feature phi(k_{-1}): fp32, already normalised
+          float xf[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xf[e] = a.xprev0 ? a.xprev0[(size_t)bh * D + part * VEC + e] : 0.f;
+          k4 = pack_feature<OpT, VEC>(xf, sk);
+        } else {
+          unpack(k4, IT(), xv);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sk += xv[e] * xv[e];
+        }
+        unpack(q4, IT(), qv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sq += qv[e] * qv[e];
+        sk = group_sum<TPR>(sk);
+        sq = group_sum<TPR>(sq);
+        const float ik = tk < 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
+        const float iq = safe_rsqrt(sq + a.eps_phi);
+        const float inv = fast_rcp(a.eps_eta + sk * ik * ik);
+        const float braw = PERCH ? 0.f : a.beta[(size_t)(b * T + tqc) * H + h];
+        const float eta = PERCH ? inv : (tq < T ? braw : 0.f) * inv;
+        put_perm(sX + r * LX, part * VEC, k4);
+        put_perm(sQ + r * LX, part * VEC, q4);
+        if (part == 0) {
+          sR[R_IK * C + r] = ik;
+          sR[R_IQ * C + r] = iq;
+          sR[R_CF * C + r] = PERCH ? ik : ik * eta;
+          sR[R_ETA * C + r] = eta;
+        }
+      }
+    }
+  } else {
+    // virtual row r: step c0 + r/BW, pair j = step - BW + 1 + r%BW with key x_j = phi(k_{j-1})
+    // (x_prev for j = 0, the carried window for j < 0); step row s holds q_{c0+s}
+#pragma unroll
+    for (int ps = 0; ps < S::NPASS; ++ps) {
+      const int r = ps * RPP + tid / TPR, part = tid % TPR;
+      if (r < C) {
+        const int st = c0 + r / BW, j = st - BW + 1 + r % BW, tk = j - 1;
+        const int tkc = min(max(tk, 0), T - 1);
+        const uint4 kraw = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tkc) * H + h) * D + part * VEC);
+        uint4 k4 = keep_or_zero(tk >= 0 && st < T, kraw);
+        float sk = 0.f;
+        if (j <= 0 && st < T) {   // carried feature (fp32, already normalised)
+          const float *src = j == 0 ? (a.xprev0 ? a.xprev0 + (size_t)bh * D : nullptr)
+                                    : (a.winx0 ? a.winx0 + ((size_t)bh * (BW - 1) + j + BW - 1) * D : nullptr);
+          float xf[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xf[e] = src ? src[part * VEC + e] : 0.f;
+          k4 = pack_feature<OpT, VEC>(xf, sk);
+        } else {
+          float xv[VEC];
+          unpack(k4, IT(), xv);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sk += xv[e] * xv[e];
+        }
+        sk = group_sum<TPR>(sk);
+        const float ik = j <= 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
+        put_perm(sX + r * LX, part * VEC, k4);
+        if (part == 0) {
+          sR[R_IK * C + r] = ik;
+          sR[R_E2 * C + r] = sk * ik * ik;
+        }
+      }
+      if (r < CSP) {
+        const int tq = c0 + r;
+        const bool okq = r < CS && tq < T;
+        const int tqc = min(tq, T - 1);
+        const uint4 qraw = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tqc) * H + h) * D + part * VEC);
+        const uint4 q4 = keep_or_zero(okq, qraw);
+        float qv[VEC], sq = 0.f;
+        unpack(q4, IT(), qv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sq += qv[e] * qv[e];
+        sq = group_sum<TPR>(sq);
+        put_perm(sQ + r * LX, part * VEC, q4);
+        if (part == 0) {
+          const float braw = a.beta[(size_t)(b * T + tqc) * H + h];
+          sR[R_IQ * C + r] = okq ? safe_rsqrt(sq + a.eps_phi) : 0.f;
+          sR[R_BQ * C + r] = okq ? braw : 0.f;
+        }
+      }
+    }
+  }
+  if (pw == S::NPW - 1) {   // clamp in log space, inclusive scan over the system's steps
+    const bool ok = lane < CS && c0 + lane < T;
+    const float graw = a.g[(size_t)(b * T + min(c0 + lane, T - 1)) * H + h];
+    const float g2 = ok ? fmaxf(graw, a.log_eps_gamma) : 0.f;
+    const float L = wave_inclusive_scan(g2);
+    if (BW == 1) {
+      if (lane < C) {
+        sR[R_LC * C + lane] = L;
+        sR[R_LM * C + lane] = L - g2;
+      }
+    } else if (lane < CSP) {
+      sR[R_LQ * C + lane] = L;
+      sR[R_GQ * C + lane] = g2;
+    }
+  }
+  __syncthreads();
+  // e^{L_a - L_b} = e^{L_a - L_ref} e^{L_ref - L_b}: each factor stays within
+  // e^{+-80} while the system's total log-decay is >= -160, so both are normal
+  // fp32 numbers and the product keeps fp32 relative accuracy; deeper decays
+  // (a long run of floored steps) keep the per-element exponential.
+  const float Llast = sR[RLQ * C + CS - 1];
+  const bool sep = Llast >= -160.f;
+  const float Lref = 0.5f * Llast;
+  if constexpr (BW == 1) {
+    if (sep && pw == 0 && lane < C) {
+      sR[R_EP * C + lane] = __expf(sR[R_LC * C + lane] - Lref) * sR[R_IQ * C + lane];
+      sR[R_EA * C + lane] = __expf(sR[R_LM * C + lane] - Lref) * sR[R_IK * C + lane];
+      sR[R_EC * C + lane] = __expf(Lref - sR[R_LC * C + lane]) * sR[R_CF * C + lane];
+    }
+  } else {
+    if (tid < C) {   // virtual-row values from their step (the step's own pair is its newest row)
+      const int r = tid, s = r / BW;
+      const float Ls = sR[R_LQ * C + s], Lm = Ls - sR[R_GQ * C + s], ik = sR[R_IK * C + r];
+      const float w = sR[R_BQ * C + s] * fast_rcp(a.eps_eta + sR[R_E2 * C + s * BW + BW - 1]) * (1.f / BW);
+      const float cf = ik * w;
+      sR[R_LC * C + r] = Ls;
+      sR[R_LM * C + r] = Lm;
+      sR[R_CF * C + r] = cf;
+      sR[R_ETA * C + r] = w;
+      if (sep) {
+        sR[R_EA * C + r] = __expf(Lm - Lref) * ik;
+        sR[R_EC * C + r] = __expf(Lref - Ls) * cf;
+      }
+    } else if (sep && tid >= 64 && tid < 64 + CSP) {
+      const int s = tid - 64;
+      sR[R_EP * C + s] = __expf(sR[R_LQ * C + s] - Lref) * sR[R_IQ * C + s];
+    }
+  }
+  __syncthreads();
+
+  const OpT *X = sX, *Q = sQ;
+  const float *G = sR;
+  auto rows16 = [&](const OpT *M, int blk, Pr (&out)[NA / 2]) {
+#pragma unroll
+    for (int a2 = 0; a2 < NA / 2; ++a2) out[a2] = ldp(M + (16 * blk + cl) * LX + 32 * a2 + 8 * g4);
+  };
+  auto tile = [&](const Pr (&Am)[NA / 2], const Pr (&Bm)[NA / 2]) {
+    f4 acc = zero4();
+#pragma unroll
+    for (int a2 = 0; a2 < NA / 2; ++a2) mmap(acc, Am[a2], Bm[a2]);
+    return acc;
+  };
+  // Gram (isP = 0, virtual rows 16p + c) or score (isP = 1, step rows 16p + c)
+  // block (p, q), transposed: lane (g, c) holds element (row 16p + c, virtual-row
+  // column 16q + 4g + i), the consumers' A-operand fragment.  Off-diagonal Gram
+  // blocks are wholly visible (steps do not straddle blocks); score blocks see
+  // the columns whose step is at most the row's.
+  auto finish = [&](const f4 &acc, int isP, int p, int q) {
+    const int row = 16 * p + cl;
+    f4 val;
+    if (sep) {
+      const f4 ec = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * q + 4 * g4);
+      const float er = G[(isP ? R_EP : R_EA) * C + row];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] * er * ec[i];
+        val[i] = (!isP || (16 * q + 4 * g4 + i) / BW <= row) ? v : 0.f;
+      }
+    } else {
+      const f4 cf = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * q + 4 * g4);
+      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * q + 4 * g4);
+      const float Lrow = G[(isP ? RLQ : R_LM) * C + row];
+      const float rf = G[(isP ? R_IQ : R_IK) * C + row];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] * __expf(Lrow - Lc4[i]) * rf * cf[i];
+        val[i] = (!isP || (16 * q + 4 * g4 + i) / BW <= row) ? v : 0.f;
+      }
+    }
+    OpT *dst = isP ? gP + frag_off(S::pbase(p), q, lane) : gA + frag_off(aslot_base(p), q, lane);
+    *reinterpret_cast<Frag *>(dst) = cvt<OpT>(val);
+  };
+  // diagonal block p: F1/F3 -> T_pp (A-layout); F2 -> the 4x4 diagonal coefficients and A_pp without them
+  auto diag = [&](const f4 &acc, int p) {   // acc: <x_{16p+4g+i}, x_{16p+c}> (symmetric)
+    const int r0 = 4 * g4;
+    f4 NA4, NC4;   // N[16p+c][16p+4g+i] (A-layout) and N[16p+4g+i][16p+c] (C-layout), strictly earlier steps
+    if (sep) {
+      const f4 ea4 = *reinterpret_cast<const f4 *>(G + R_EA * C + 16 * p + r0);
+      const f4 ec4 = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * p + r0);
+      const float ea1 = G[R_EA * C + 16 * p + cl], ec1 = G[R_EC * C + 16 * p + cl];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        NA4[i] = ((r0 + i) / BW < cl / BW) ? acc[i] * ea1 * ec4[i] : 0.f;
+        NC4[i] = (cl / BW < (r0 + i) / BW) ? acc[i] * ea4[i] * ec1 : 0.f;
+      }
+    } else {
+      const f4 cf4 = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * p + r0);
+      const f4 ik4 = *reinterpret_cast<const f4 *>(G + R_IK * C + 16 * p + r0);
+      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * p + r0);
+      const f4 Lm4 = *reinterpret_cast<const f4 *>(G + R_LM * C + 16 * p + r0);
+      const float Lc1 = G[R_LC * C + 16 * p + cl], Lm1 = G[R_LM * C + 16 * p + cl];
+      const float ik1 = G[R_IK * C + 16 * p + cl], cf1 = G[R_CF * C + 16 * p + cl];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float va = acc[i] * __expf(Lm1 - Lc4[i]) * ik1 * cf4[i];
+        const float vc = acc[i] * __expf(Lm4[i] - Lc1) * ik4[i] * cf1;
+        NA4[i] = ((r0 + i) / BW < cl / BW) ? va : 0.f;
+        NC4[i] = (cl / BW < (r0 + i) / BW) ? vc : 0.f;
+      }
+    }
+    if constexpr (S::SDELTA) {
+      // row-oriented block Jacobi: T (I + N) = I, so T <- (I - T N_o)(I + N_d)^{-1},
+      // exact after 3 sweeps; Y holds T in A-layout (row c, columns 4g..4g+3).
+      // n_ab = N[4g+a][4g+b] sits in lane (g, 4g+a), entry b of NA4.
+      const int src = 16 * g4 + r0;
+      const float n10 = __shfl(NA4[0], src + 1), n20 = __shfl(NA4[0], src + 2), n21 = __shfl(NA4[1], src + 2);
+      const float n30 = __shfl(NA4[0], src + 3), n31 = __shfl(NA4[1], src + 3), n32 = __shfl(NA4[2], src + 3);
+      f4 NoC;   // C-layout of N without its 4x4 diagonal sub-blocks
+#pragma unroll
+      for (int i = 0; i < 4; ++i) NoC[i] = ((cl >> 2) == g4) ? 0.f : NC4[i];
+      f4 Z, Y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Z[i] = (r0 + i == cl) ? 1.f : 0.f;
+      auto local = [&](const f4 &w) {     // t (I + N_gg) = w, t a row of 4
+        Y[3] = w[3];
+        Y[2] = w[2] - Y[3] * n32;
+        Y[1] = w[1] - Y[2] * n21 - Y[3] * n31;
+        Y[0] = w[0] - Y[1] * n10 - Y[2] * n20 - Y[3] * n30;
+      };
+      local(Z);
+#pragma unroll
+      for (int it = 0; it < 3; ++it) {
+        f4 cpl = zero4();
+        mma16(cpl, NoC, Y);   // fp32: C-layout of N_o^T Y^T = A-layout of Y N_o
+        local(Z - cpl);
+      }
+      *reinterpret_cast<Frag *>(gT + (p * 64 + lane) * 4) = cvt<OpT>(Y);
+    } else {
+      // lane (g, 4g+b) holds N[4g+a][4g+b] in NC4[a]; slots: 10 20 21 30 31 32
+      if ((cl >> 2) == g4) {
+        float *ad = gAd + (p * 4 + g4) * 8;
+        const int bb = cl - r0;
+        if (bb == 0) { ad[0] = NC4[1]; ad[1] = NC4[2]; ad[3] = NC4[3]; }
+        if (bb == 1) { ad[2] = NC4[2]; ad[4] = NC4[3]; }
+        if (bb == 2) ad[5] = NC4[3];
+      }
+      f4 NoA;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) NoA[i] = ((cl >> 2) == g4) ? 0.f : NA4[i];
+      *reinterpret_cast<Frag *>(gT + (p * 64 + lane) * 4) = cvt<OpT>(NoA);
+    }
+  };
+  auto rowfac = [&]() {
+    if (lane < C) {
+      const float L = G[R_LC * C + lane], Lm = G[R_LM * C + lane];
+      gF[F_GAM * C + lane] = __expf(Lm) * G[R_IK * C + lane];
+      gF[F_EL * C + lane] = lane < CSP ? __expf(G[RLQ * C + lane]) * G[R_IQ * C + lane] : 0.f;
+      gF[F_CST * C + lane] = __expf(Llast - L) * G[R_CF * C + lane];
+      gF[F_ETA * C + lane] = G[R_ETA * C + lane];
+      if (lane == 0) gF[F_N * C] = __expf(Llast);
+    }
+  };
+  auto run = [&](auto wc) {
+    constexpr int w = decltype(wc)::value;
+    constexpr JobList J = BW == 1 ? make_jobs(NB, DELTA, w) : make_jobs_win(NB, CS, BW, DELTA, w);
+    constexpr int NJ = J.n > 0 ? J.n : 1;
+    Pr Dop[NA / 2], Aop[NJ][NA / 2], Bop[NJ][NA / 2];
+    if constexpr (J.diag >= 0) rows16(X, J.diag, Dop);
+#pragma unroll
+    for (int j = 0; j < J.n; ++j) {
+      rows16(X, J.q[j], Aop[j]);
+      rows16(J.isP[j] ? Q : X, J.p[j], Bop[j]);
+    }
+    f4 dacc, acc[NJ];
+    if constexpr (J.diag >= 0) dacc = tile(Dop, Dop);
+#pragma unroll
+    for (int j = 0; j < J.n; ++j) acc[j] = tile(Aop[j], Bop[j]);
+    if constexpr (J.diag >= 0) diag(dacc, J.diag);
+#pragma unroll
+    for (int j = 0; j < J.n; ++j) finish(acc[j], J.isP[j], J.p[j], J.q[j]);
+    if constexpr (w == S::NPW - 1) rowfac();
+  };
+  if (pw == 0) run(std::integral_constant<int, 0>());
+  else if (pw == 1) run(std::integral_constant<int, 1>());
+  else if (pw == 2) run(std::integral_constant<int, 2>());
+  else run(std::integral_constant<int, 3>());
+}
+
+// ============================== scan kernel ==============================
+template <int VAR, typename IT, int D, int C, int BW, int NS>
+__global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, const unsigned char *ws) {
+  using S = Split<VAR, IT, D, C, BW>;
+  using Z = Scan<VAR, IT, D, C, BW, NS>;
+  using OpT = IT;
+  using Frag = typename Op<OpT>::frag;
+  using Pr = Pair<OpT>;
+  constexpr int NB = S::NB, NA = S::NA, NCW = Z::NCW, LX = S::LX, VEC = S::VEC, TPR = S::TPR, RPC = Z::RPC;
+  constexpr int LXV = Z::LXV, TPV = Z::TPV, RPV = Z::RPV;
+  constexpr int CS = S::CS, CSP = S::CSP, NBS = S::NBS;
+  constexpr bool PERCH = S::PERCH, DELTA = S::DELTA;
+
+  // Operands with the per-row factors folded in (dk permuted):
+  __shared__ __attribute__((aligned(16))) OpT sXg[2][C * LX];    // GAM_r x_r   (residuals)
+  __shared__ __attribute__((aligned(16))) OpT sXc[2][C * LX];    // CST_r x_r   (state update)
+  __shared__ __attribute__((aligned(16))) OpT sQe[2][CSP * LX];  // EL_s q_s    (outputs)
+  __shared__ __attribute__((aligned(16))) IT sV[2][C * LXV];     // raw v of each virtual row, this workgroup's channels
+  __shared__ __attribute__((aligned(16))) unsigned char sImg[2][S::IMG];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g4 = lane >> 4, cl = lane & 15;
+  // workgroup -> (sequence, channel slice).  The NS slices of a sequence get ids
+  // that are equal mod 8, i.e. the same XCD, so its L2 serves their shared reads.
+  int bh, sp;
+  if (NS > 1 && (a.B * a.H) % 8 == 0) {
+    const int rest = blockIdx.x >> 3;
+    sp = rest % NS;
+    bh = (rest / NS) * 8 + (blockIdx.x & 7);
+  } else {
+    bh = blockIdx.x / NS;
+    sp = blockIdx.x % NS;
+  }
+  const int b = bh / a.H, h = bh % a.H;
+  const int T = a.T, H = a.H, NC = a.nchunks, NSYS = S::nsys(T);
+  const bool consumer = wv < NCW;
+  const int ctid = tid - 64 * NCW;         // copy thread index
+  const int chW = Z::DS * sp + 16 * wv + cl;   // consumer lane's value channel
+
+  const IT *qp = static_cast<const IT *>(a.q);
+  const IT *kp = static_cast<const IT *>(a.k);
+  const IT *vp = static_cast<const IT *>(a.v);
+  IT *op = static_cast<IT *>(a.o);
+  const unsigned char *wsq = ws + (size_t)bh * NSYS * S::IMG;
+  const float *carry = reinterpret_cast<const float *>(ws + (size_t)a.B * H * NSYS * S::IMG + (size_t)bh * S::CARRY);
+  // step and pair index of virtual row r of the system starting at step c0
+  auto step_of = [](int c0, int r) { return c0 + r / BW; };
+  auto pair_of = [](int c0, int r) { return BW == 1 ? c0 + r : c0 + r / BW - BW + 1 + r % BW; };
+
+  // ================= copy waves =================
+  // Two register sets: system c lands in set c & 1, two systems ahead of its use,
+  // so a load has two scan iterations to arrive.
+  struct Regs {
+    uint4 k[Z::NPK], q[Z::NPK], v[Z::NPV], img[Z::NPI];
+    float fg[Z::NPK], fc[Z::NPK], fe[Z::NPK];   // GAM, CST of the row's key; EL of step row r
+  };
+  Regs reg[2];
+  auto prefetch = [&](int c, Regs &R) __attribute__((always_inline)) {    // global -> registers, system c (rows clamped in bounds)
+    const int c0 = c * CS;
+#pragma unroll
+    for (int ps = 0; ps < Z::NPV; ++ps) {
+      const int r = min(ps * RPV + ctid / TPV, C - 1), part = ctid % TPV;
+      const int tv = min(max(pair_of(c0, r), 0), T - 1);
+      R.v[ps] = *reinterpret_cast<const uint4 *>(vp + ((size_t)(b * T + tv) * H + h) * D + Z::DS * sp + part * VEC);
+    }
+#pragma unroll
+    for (int ps = 0; ps < Z::NPK; ++ps) {
+      const int r = min(ps * RPC + ctid / TPR, C - 1), part = ctid % TPR;
+      const int tk = min(max(pair_of(c0, r) - 1, 0), T - 1), tq = min(c0 + r, T - 1);
+      R.k[ps] = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tk) * H + h) * D + part * VEC);
+      R.q[ps] = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tq) * H + h) * D + part * VEC);
+      const float *Fg = reinterpret_cast<const float *>(wsq + (size_t)c * S::IMG + S::OFF_F);
+      R.fg[ps] = Fg[F_GAM * C + r];
+      R.fc[ps] = Fg[F_CST * C + r];
+      R.fe[ps] = Fg[F_EL * C + r];
+    }
+    const uint4 *src = reinterpret_cast<const uint4 *>(wsq + (size_t)c * S::IMG);
+#pragma unroll
+    for (int j = 0; j < Z::NPI; ++j) R.img[j] = src[min(ctid + j * Z::NST, S::NU - 1)];
+  };
+  auto stage = [&](int c, const Regs &R) __attribute__((always_inline)) { // registers -> LDS slot c & 1
+    const int s = c & 1, c0 = c * CS;
+#pragma unroll
+    for (int ps = 0; ps < Z::NPV; ++ps) {
+      const int r = ps * RPV + ctid / TPV, part = ctid % TPV;
+      if (r < C) {
+        const int j = pair_of(c0, r);
+        const bool live = step_of(c0, r) < T;
+        uint4 vv = keep_or_zero(live && j >= 0, R.v[ps]);
+        if (BW > 1 && live && j < 0) {   // a carried window value (fp32)
+          float vf[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) vf[e] = carry[(j + 2 * BW - 1) * D + Z::DS * sp + part * VEC + e];
+          vv = scale_pack<IT, VEC>(vf, 1.f);
+        }
+        *reinterpret_cast<uint4 *>(sV[s] + r * LXV + part * VEC) = vv;
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < Z::NPK; ++ps) {
+      const int r = ps * RPC + ctid / TPR, part = ctid % TPR;
+      if (r < C) {
+        const int j = pair_of(c0, r);
+        const bool live = step_of(c0, r) < T;
+        float xv[VEC];
+        unpack(keep_or_zero(live && j >= 1, R.k[ps]), IT(), xv);
+        if (live && j <= 0) {   // a carried feature (fp32, normalised): x_prev, or window key j
+          const float *src = carry + (j == 0 ? 0 : (j + BW) * D) + part * VEC;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xv[e] = src[e];
+        }
+        put_perm(sXg[s] + r * LX, part * VEC, scale_pack<OpT, VEC>(xv, R.fg[ps]));
+        put_perm(sXc[s] + r * LX, part * VEC, scale_pack<OpT, VEC>(xv, R.fc[ps]));
+        if (r < CSP) {
+          float qv[VEC];
+          unpack(keep_or_zero(r < CS && c0 + r < T, R.q[ps]), IT(), qv);
+          put_perm(sQe[s] + r * LX, part * VEC, scale_pack<OpT, VEC>(qv, R.fe[ps]));
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < Z::NPI; ++j) {
+      const int u = ctid + j * Z::NST;
+      if (u < S::NU) *reinterpret_cast<uint4 *>(sImg[s] + 16 * u) = R.img[j];
+    }
+  };
+
+  // ================= consumers =================
+  f4 sT[NA];                 // S^T of this wave's 16 channels, C-layout per dk block
+  float rbeta[NB][4];        // F2/F2A: per-channel gains of the next chunk
+  if (consumer) {
+#pragma unroll
+    for (int aa = 0; aa < NA; ++aa)
+      sT[aa] = a.S0 ? *reinterpret_cast<const f4 *>(a.S0 + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) : zero4();
+  }
+  auto prefetch_beta = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < NB; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = c * CS + 16 * p + 4 * g4 + i;   // zero past the end: padded rows must not write
+        const float braw = a.beta[((size_t)(b * T + min(t, T - 1)) * H + h) * D + chW];
+        rbeta[p][i] = t < T ? braw : 0.f;
+      }
+  };
+
+  auto consume = [&](int c) __attribute__((always_inline)) {
+    const int s = c & 1, c0 = c * CS;
+    const OpT *Xg = sXg[s], *Xc = sXc[s], *Qe = sQe[s];
+    const IT *V = sV[s];
+    const float *F = reinterpret_cast<const float *>(sImg[s] + S::OFF_F);
+    const OpT *Ao = reinterpret_cast<const OpT *>(sImg[s] + S::OFF_A);
+    const OpT *Pm = reinterpret_cast<const OpT *>(sImg[s] + S::OFF_P);
+    const OpT *Tb = reinterpret_cast<const OpT *>(sImg[s] + S::OFF_T);
+    Pr Sp[NA / 2];
+#pragma unroll
+    for (int a2 = 0; a2 < NA / 2; ++a2) Sp[a2] = mkp(cvt<OpT>(sT[2 * a2]), cvt<OpT>(sT[2 * a2 + 1]));
+    // XS = diag(GAM) X S0^T: C-layout (virtual rows 16p+4g+i, channel c).
+    // QSt = (diag(EL) Q^ S0^T)^T: C-layout with channel rows 16w+4g+i and step
+    // column 16p+c (S fragments as the left operand).
+    f4 QSt[NBS], XS[NB];
+#pragma unroll
+    for (int p = 0; p < NB; ++p) {
+      if (p < NBS) QSt[p] = zero4();
+      XS[p] = zero4();
+#pragma unroll
+      for (int a2 = 0; a2 < NA / 2; ++a2) {
+        if (DELTA) mmap(XS[p], ldp(Xg + (16 * p + cl) * LX + 32 * a2 + 8 * g4), Sp[a2]);
+        if (p < NBS) mmap(QSt[p], Sp[a2], ldp(Qe + (16 * p + cl) * LX + 32 * a2 + 8 * g4));
+      }
+    }
+    auto vcol = [&](int j4) { return 16 * wv + 4 * j4; };
+    Frag Eb[NB];               // E' = E (F1/F3), eta (.) E (F2), V (F1A/F3A), eta (.) V (F2A)
+#pragma unroll
+    for (int p = 0; p < NB; ++p) {
+      f4 R = to_f4(ldT(V, LXV, 16 * p, vcol, lane));  // C-layout values of this wave's channels
+      if (DELTA) R -= XS[p];
+      f4 eta4;
+      if (PERCH) {
+        const f4 inv = *reinterpret_cast<const f4 *>(F + F_ETA * C + 16 * p + 4 * g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eta4[i] = rbeta[p][i] * inv[i];
+      }
+      if (DELTA) {   // R -= sum_{q<p} A_pq E_q   (E_q = eta (.) E for F2)
+        f4 acc = zero4();
+#pragma unroll
+        for (int q = 0; q + 1 < p; q += 2) mmap(acc, ldp(Ao + frag_off(aslot_base(p), q, lane)), mkp(Eb[q], Eb[q + 1]));
+        if (p & 1) mma16(acc, ld4(Ao + frag_off(aslot_base(p), p - 1, lane)), Eb[p - 1]);
+        R -= acc;
+      }
+      if constexpr (S::SDELTA) {
+        f4 E = zero4();
+        mma16(E, ld4(Tb + (p * 64 + lane) * 4), cvt<OpT>(R));
+        Eb[p] = cvt<OpT>(E);
+      } else if constexpr (VAR == V_F2) {
+        // rows 4g4..4g4+3 of block p: exact 4x4 solves, coupled by A_pp minus its 4x4 diagonal
+        const float *Ad = reinterpret_cast<const float *>(sImg[s] + S::OFF_AD) + (p * 4 + g4) * 8;
+        const f4 c0v = *reinterpret_cast<const f4 *>(Ad), c1v = *reinterpret_cast<const f4 *>(Ad + 4);
+        const float a10 = c0v[0], a20 = c0v[1], a21 = c0v[2], a30 = c0v[3], a31 = c1v[0], a32 = c1v[1];
+        const Frag Ain = ld4(Tb + (p * 64 + lane) * 4);
+        f4 E, Fv;
+        auto local = [&](const f4 &zz) {
+          E[0] = zz[0];
+          Fv[0] = eta4[0] * E[0];
+          E[1] = zz[1] - a10 * Fv[0];
+          Fv[1] = eta4[1] * E[1];
+          E[2] = zz[2] - a20 * Fv[0] - a21 * Fv[1];
+          Fv[2] = eta4[2] * E[2];
+          E[3] = zz[3] - a30 * Fv[0] - a31 * Fv[1] - a32 * Fv[2];
+          Fv[3] = eta4[3] * E[3];
+        };
+        local(R);
+#pragma unroll
+        for (int it = 0; it < 3; ++it) {
+          f4 cpl = zero4();
+          mma16(cpl, Ain, cvt<OpT>(Fv));
+          local(R - cpl);
+        }
+        Eb[p] = cvt<OpT>(Fv);      // eta (.) E feeds the state update and the outputs
+      } else if constexpr (VAR == V_F2A) {
+        Eb[p] = cvt<OpT>(eta4 * R);
+      } else {
+        Eb[p] = cvt<OpT>(R);
+      }
+    }
+    // outputs, transposed: o^T = e^{L} (S0 Q^^T) + E'^T P^T.  The C-layout fragments of
+    // E' are the left operands and the stored score fragments the right ones; lane
+    // (g, c) ends with channels 16w+4g..16w+4g+3 of step 16p+c and stores them.
+#pragma unroll
+    for (int p = 0; p < NBS; ++p) {
+      const int qm = S::qmax(p);
+      f4 O = QSt[p];
+#pragma unroll
+      for (int q = 0; q + 1 <= qm; q += 2) mmap(O, mkp(Eb[q], Eb[q + 1]), ldp(Pm + frag_off(S::pbase(p), q, lane)));
+      if (!(qm & 1)) mma16(O, Eb[qm], ld4(Pm + frag_off(S::pbase(p), qm, lane)));
+      const int srow = 16 * p + cl, t = c0 + srow;
+      if (srow < CS && t < T)
+        *reinterpret_cast<Frag *>(op + ((size_t)(b * T + t) * H + h) * D + Z::DS * sp + 16 * wv + 4 * g4) = cvt<OpT>(O);
+    }
+    // state: S^T <- e^{L_last} S^T + (diag(CST) X)^T E'
+    const Frag *CE = Eb;
+    const float lamtot = F[F_N * C];
+#pragma unroll
+    for (int aa = 0; aa < NA; ++aa) {
+      auto dkcol = [&](int j4) { return kperm(16 * aa + 4 * j4); };
+      f4 acc = sT[aa] * lamtot;
+      if constexpr (NB == 1) {
+        mma16(acc, ldT(Xc, LX, 0, dkcol, lane), CE[0]);
+      } else {
+#pragma unroll
+        for (int p = 0; p < NB; p += 2)
+          mmap(acc, mkp(ldT(Xc, LX, 16 * p, dkcol, lane), ldT(Xc, LX, 16 * p + 16, dkcol, lane)), mkp(CE[p], CE[p + 1]));
+      }
+      sT[aa] = acc;
+    }
+    if (a.chunk_states && ((c + 1) % BW == 0 || c == NSYS - 1)) {   // every C steps
+      const int ci = c / BW;
+#pragma unroll
+      for (int aa = 0; aa < NA; ++aa)
+        *reinterpret_cast<f4 *>(a.chunk_states + (((size_t)bh * NC + ci) * D + chW) * D + 16 * aa + 4 * g4) = sT[aa];
+    }
+  };
+
+  // ---------------- scan: iteration i consumes system i and stages system i+1 ----------------
+  // Each role runs its own loop, so neither keeps the other's loop-carried
+  // registers live; both pass the same number of workgroup barriers (one per
+  // system after a prologue barrier), which is what the barrier counts.
+  if (consumer) {
+    if (PERCH) prefetch_beta(0);
+    __syncthreads();
+    for (int i = 0; i < NSYS; ++i) {
+      consume(i);
+      if (PERCH && i + 1 < NSYS) prefetch_beta(i + 1);
+      __syncthreads();
+    }
+    if (a.S_out) {
+#pragma unroll
+      for (int aa = 0; aa < NA; ++aa)
+        *reinterpret_cast<f4 *>(a.S_out + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) = sT[aa];
+    }
+  } else {
+    prefetch(0, reg[0]);
+    if (NSYS > 1) prefetch(1, reg[1]);
+    stage(0, reg[0]);
+    if (NSYS > 2) prefetch(2, reg[0]);
+    __syncthreads();
+    // the register sets are indexed with compile-time parity: two iterations per trip;
+    // Rnext holds system i+1 and is refilled with system i+3
+    auto copy_step = [&](int i, Regs &Rnext) __attribute__((always_inline)) {
+      if (i + 1 < NSYS) {
+        stage(i + 1, Rnext);
+        if (i + 3 < NSYS) prefetch(i + 3, Rnext);
+      }
+    };
+    for (int i = 0; i < NSYS; i += 2) {
+      copy_step(i, reg[1]);
+      __syncthreads();
+      if (i + 1 < NSYS) {
+        copy_step(i + 1, reg[0]);
+        __syncthreads();
+      }
+    }
+    if (a.write_tail) {
+      // outgoing x_prev = phi(k_{T-1}) and, for windows, the last Bw-1 pairs
+      // j = T-Bw+1..T-1 (keys phi(k_{j-1}), values v_j; carried ones for j <= 0)
+      const int w8 = wv - NCW;
+      auto key_row = [&](int j, float *dst) {   // normalised key of pair j into dst[0..D)
+        float xv[2] = {0.f, 0.f};
+        if (j >= 1) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const int e = lane + 64 * m;
+            if (e < D) xv[m] = to_f(kp[((size_t)(b * T + j - 1) * H + h) * D + e]);
+          }
+          const float inv = safe_rsqrt(group_sum<64>(xv[0] * xv[0] + xv[1] * xv[1]) + a.eps_phi);
+          xv[0] *= inv;
+          xv[1] *= inv;
+        } else {
+          const float *src = carry + (j == 0 ? 0 : (j + BW) * D);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const int e = lane + 64 * m;
+            if (e < D) xv[m] = src[e];
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int e = lane + 64 * m;
+          if (e < D) dst[e] = xv[m];
+        }
+      };
+      if (w8 == BW - 1) {
+        if (sp == 0 && a.xprev_out) key_row(T, a.xprev_out + (size_t)bh * D);
+      } else if (BW > 1 && w8 < BW - 1) {
+        const int j = T - BW + 1 + w8;
+        if (sp == 0 && a.winx_out) key_row(j, a.winx_out + ((size_t)bh * (BW - 1) + w8) * D);
+        if (a.winv_out) {
+          for (int e = lane; e < Z::DS; e += 64) {
+            const int ch = Z::DS * sp + e;
+            a.winv_out[((size_t)bh * (BW - 1) + w8) * D + ch] =
+                j >= 0 ? to_f(vp[((size_t)(b * T + j) * H + h) * D + ch]) : carry[(j + 2 * BW - 1) * D + ch];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Channel splits built per shape: fp32 keeps whole sequences; bf16 takes 1 or
+// 2 slices at d <= 64 and 2, 4 or 8 at d = 128 (whose values do not fit whole).
+template <typename IT, int D>
+constexpr bool ns_built(int ns) {
+  if (sizeof(IT) == 4) return ns == 1;
+  return D <= 64 ? (ns == 1 || ns == 2) : (ns == 2 || ns == 4 || ns == 8);
+}
+template <int VAR, typename IT, int D, int C, int BW, int NS>
+constexpr bool scan_ok() { return ns_built<IT, D>(NS) && Scan<VAR, IT, D, C, BW, NS>::fits(); }
+
+// Smallest built split that fits and gives at least 128 scan workgroups (else
+// the largest that fits); 0 when none fits.
+template <int VAR, typename IT, int D, int C, int BW>
+int pick_ns(int bh) {
+  const bool ok[4] = {scan_ok<VAR, IT, D, C, BW, 1>(), scan_ok<VAR, IT, D, C, BW, 2>(),
+                      scan_ok<VAR, IT, D, C, BW, 4>(), scan_ok<VAR, IT, D, C, BW, 8>()};
+  int best = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (!ok[i]) continue;
+    best = 1 << i;
+    if (bh * best >= 128) break;
+  }
+  return best;
+}
+
+template <int VAR, typename IT, int D, int C, int BW, int NS>
+hipError_t launch_scan(const FwdArgs &a, const unsigned char *w, hipStream_t st) {
+  if constexpr (scan_ok<VAR, IT, D, C, BW, NS>()) {
+    hipLaunchKernelGGL((chunk_scan<VAR, IT, D, C, BW, NS>), dim3(a.B * a.H * NS),
+                       dim3(Scan<VAR, IT, D, C, BW, NS>::NT), 0, st, a, w);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <int VAR, typename IT, int D, int C, int BW>
+hipError_t launch_split(const FwdArgs &a, void *ws, hipStream_t st) {
+  const int ns = pick_ns<VAR, IT, D, C, BW>(a.B * a.H);
+  if (ns == 0) return hipErrorInvalidValue;
+  unsigned char *w = static_cast<unsigned char *>(ws);
+  const int nsys = Split<VAR, IT, D, C, BW>::nsys(a.T);
+  hipLaunchKernelGGL((chunk_prep<VAR, IT, D, C, BW>), dim3(a.B * a.H * nsys), dim3(256), 0, st, a, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (ns) {
+    case 1: return launch_scan<VAR, IT, D, C, BW, 1>(a, w, st);
+    case 2: return launch_scan<VAR, IT, D, C, BW, 2>(a, w, st);
+    case 4: return launch_scan<VAR, IT, D, C, BW, 4>(a, w, st);
+    case 8: return launch_scan<VAR, IT, D, C, BW, 8>(a, w, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace falcon

@@ -77,17 +77,28 @@ def workspace(**kw):
 
 
 def test_workspace_size():
-    """The chunk-parallel path keeps one image per (sequence, chunk): the size is a
-    multiple of 16 bytes proportional to B*H*ceil(T/C); windowed variants, fp32 at
-    d = 128 and invalid shapes need none."""
-    w1, w2 = workspace(seqlen=100), workspace(seqlen=200)   # 2 and 4 chunks of 64
-    assert w1 > 0 and w1 % 16 == 0 and w2 == 2 * w1
-    assert workspace(batch=4, seqlen=100) == 2 * w1
+    """The chunk-parallel path keeps one image per (sequence, system of rows) plus
+    one carry block per sequence: the size is a multiple of 16 bytes, linear in
+    B*H and, per sequence, affine in the number of systems (ceil(T/C) steps of C
+    for one pair per step, ceil(T/(C/Bw)) for a window of Bw pairs).  Fp32 at
+    d = 128, windows on chunks other than 64 and invalid shapes need none."""
+    w1, w2, w3 = workspace(seqlen=100), workspace(seqlen=200), workspace(seqlen=300)   # 2, 4, 5 systems
+    img = w3 - w2
+    assert w1 > 0 and w1 % 16 == 0 and img > 0 and img % 16 == 0 and w2 - w1 == 2 * img
+    assert workspace(batch=4) == 2 * w1
     assert workspace(variant="F1A") < w1                    # no Gram / T blocks
-    assert workspace(variant="F3", window=4) == 0
-    assert workspace(dk=128, dv=128) == w1                  # d = 128 (bf16) too; tiles are C x C
+    assert workspace(variant="F3", window=1) == w1          # a one-pair window is Falcon-1
+    assert workspace(dk=128, dv=128) > w1                   # d = 128 (bf16): larger carry block only
+    assert workspace(dk=128, dv=128) - w1 < img
     assert workspace(dtype="fp32", dk=128, dv=128) == 0
     assert workspace(batch=0) == 0 and workspace(dk=48, dv=48) == 0
+    # windows: systems of 64 / Bw steps
+    f4 = [workspace(variant="F3", window=4, seqlen=t) for t in (100, 116, 132)]   # 7, 8, 9 systems
+    assert f4[0] > 0 and f4[1] - f4[0] == f4[2] - f4[1] > 0
+    assert workspace(variant="F3A", window=4) < f4[0]       # no Gram / T blocks
+    w8 = [workspace(variant="F3", window=8, seqlen=t) for t in (100, 108)]       # 13, 14 systems
+    assert w8[1] - w8[0] == f4[1] - f4[0]                   # same image size: one 16-row score block
+    assert workspace(variant="F3", window=4, chunk=32) == 0   # the windowed kernel, no scratch
 
 
 @cpu_only

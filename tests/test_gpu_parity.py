@@ -225,6 +225,53 @@ def test_window_bf16(variant, bw, d):
     check(variant, w, 62, window=bw, init=True, chunk_states=True)
 
 
+@pytest.mark.parametrize("variant,bw", [("F3", 4), ("F3A", 8)])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_window_kernel_bf16(variant, bw, d):
+    """The windowed kernel (no workspace) on the shapes the chunk-parallel path also takes."""
+    w = W.WORKLOADS["window_t4096"].replace(batch=2, heads=2, seqlen=203, dk=d, dv=d)
+    check(variant, w, 66, window=bw, init=True, chunk_states=True, workspace=False)
+
+
+@pytest.mark.parametrize("variant,bw", [("F3", 2), ("F3", 4), ("F3", 8), ("F3A", 2), ("F3A", 4), ("F3A", 8)])
+def test_window_split_and_window_kernel_agree(variant, bw):
+    w = W.WORKLOADS["window_t4096"].replace(batch=2, heads=3, seqlen=333)
+    inp = W.make_inputs(w, variant, seed=67)
+    st = W.make_state(w, 1067, bw)
+    a = run_gpu(variant, inp, "bf16", 64, window=bw, init=st, chunk_states=True, workspace=True)
+    b = run_gpu(variant, inp, "bf16", 64, window=bw, init=st, chunk_states=True, workspace=False)
+    for k in a:
+        e = rel_l2(a[k], b[k])
+        assert e <= 5e-3, (k, e)   # same arithmetic up to accumulation order and bf16 rounding of tiles
+
+
+# Windowed systems hold 64 / Bw steps; these shapes reach every built channel
+# split of the scan (as for one pair per step) with several windows.
+WIN_SPLIT_SHAPES = [
+    (64, 8, 16, 70),     # B*H = 128: NS = 1
+    (64, 1, 5, 70),      # NS = 2, plain mapping
+    (128, 2, 32, 50),    # NS = 2, XCD-grouped
+    (128, 4, 8, 50),     # NS = 4
+    (128, 1, 6, 50),     # NS = 8, plain mapping
+]
+
+
+@pytest.mark.parametrize("variant,bw", [("F3", 2), ("F3", 8), ("F3A", 4)])
+@pytest.mark.parametrize("d,B,H,T", WIN_SPLIT_SHAPES)
+def test_window_scan_channel_splits(variant, bw, d, B, H, T):
+    w = W.WORKLOADS["window_t4096"].replace(batch=B, heads=H, seqlen=T, dk=d, dv=d)
+    check(variant, w, 68, window=bw, init=True, chunk_states=True)
+
+
+@pytest.mark.parametrize("variant,bw", [("F3", 2), ("F3", 4), ("F3", 8), ("F3A", 4), ("F3A", 8)])
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 9, 17, 33])
+def test_window_short_systems(variant, bw, T):
+    """Chunk 64 (systems of 64 / Bw steps) with sequences about the window's
+    length: the first system's rows mix carried and new pairs, the last is ragged."""
+    w = TINY.replace(batch=1, heads=2, seqlen=T, dk=32, dv=32, chunk=64)
+    check(variant, w, 65, window=bw, init=True, chunk_states=True)
+
+
 @pytest.mark.parametrize("variant,bw", [("F3", 4), ("F3", 8), ("F3A", 8)])
 @pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 9, 33])
 def test_window_short(variant, bw, T):
