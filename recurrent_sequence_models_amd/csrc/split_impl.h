@@ -120,20 +120,25 @@ struct Split {
 };
 
 // The scan of one sequence is split over NS workgroups by value channel (rows
-// of S evolve independently given the keys): each takes D/NS channels with
-// one consumer wave per 16 of them, plus 8 copy waves that stage the shared
-// key / query rows and system image and its own value columns.
+// of S evolve independently given the keys).  A workgroup takes D/NS channels:
+// per 16 of them one state wave (the chain S -> residuals -> S, system by system)
+// and one output wave (the outputs of the previous system, from the S and E'
+// fragments the state wave leaves in LDS), plus 8 copy waves that stage the
+// shared key / query rows, the system image and the slice's value columns.
 template <int VAR, typename IT, int D, int C, int BW, int NS>
 struct Scan {
   using S = Split<VAR, IT, D, C, BW>;
   static constexpr int DS = D / NS;                          // value channels per workgroup
-  static constexpr int NCW = DS / 16, NSW = 8, NT = 64 * (NCW + NSW), NST = 64 * NSW;
+  static constexpr int NCW = DS / 16, NSW = 8, NT = 64 * (2 * NCW + NSW), NST = 64 * NSW;
   static constexpr int LXV = DS + S::PADE;                   // V rows (this workgroup's channels)
   static constexpr int RPC = NST / S::TPR, NPK = (C + RPC - 1) / RPC;   // key / query rows per copy pass
   static constexpr int TPV = DS / S::VEC, RPV = NST / TPV, NPV = (C + RPV - 1) / RPV;
   static constexpr int NPI = (S::NU + NST - 1) / NST;
+  // keys and values: 2 slots (state waves); queries and images: 3 (output waves lag one
+  // system); S and E' fragments handed to the output waves: 2
   static constexpr size_t lds() {
-    return (size_t)S::SZ * 2 * ((2 * C + S::CSP) * S::LX + C * LXV) + 2 * (size_t)S::IMG;
+    return (size_t)S::SZ * (2 * C * S::LX + 3 * S::CSP * S::LX + 2 * C * LXV) + 3 * (size_t)S::IMG +
+           2 * (size_t)NCW * 64 * S::SZ * (8 * (S::NA / 2) + 4 * S::NB);
   }
   static constexpr bool fits() {
     return DS >= 16 && D % NS == 0 && lds() + 256 <= 160 * 1024 && S::prep_lds() + 256 <= 64 * 1024;
@@ -511,7 +516,7 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
 
 // ============================== scan kernel ==============================
 template <int VAR, typename IT, int D, int C, int BW, int NS>
-__global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, const unsigned char *ws) {
+__global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdArgs a, const unsigned char *ws) {
   using S = Split<VAR, IT, D, C, BW>;
   using Z = Scan<VAR, IT, D, C, BW, NS>;
   using OpT = IT;
@@ -522,12 +527,15 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
   constexpr int CS = S::CS, CSP = S::CSP, NBS = S::NBS;
   constexpr bool PERCH = S::PERCH, DELTA = S::DELTA;
 
-  // Operands with the per-row factors folded in (dk permuted):
-  __shared__ __attribute__((aligned(16))) OpT sXg[2][C * LX];    // GAM_r x_r   (residuals)
-  __shared__ __attribute__((aligned(16))) OpT sXc[2][C * LX];    // CST_r x_r   (state update)
-  __shared__ __attribute__((aligned(16))) OpT sQe[2][CSP * LX];  // EL_s q_s    (outputs)
+  // Raw operands (dk permuted); the per-row factors are applied to the products,
+  // so copy waves only move bytes and take few issue slots from the other waves:
+  __shared__ __attribute__((aligned(16))) OpT sX[2][C * LX];     // key of each virtual row
   __shared__ __attribute__((aligned(16))) IT sV[2][C * LXV];     // raw v of each virtual row, this workgroup's channels
-  __shared__ __attribute__((aligned(16))) unsigned char sImg[2][S::IMG];
+  __shared__ __attribute__((aligned(16))) OpT sQ[3][CSP * LX];   // q of each step row
+  __shared__ __attribute__((aligned(16))) unsigned char sImg[3][S::IMG];
+  // handed from each state wave to its output wave: S at the system's start, E'
+  __shared__ Pr sSp[2][NCW][NA / 2][64];
+  __shared__ Frag sEb[2][NCW][NB][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, cl = lane & 15;
@@ -544,9 +552,10 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
   }
   const int b = bh / a.H, h = bh % a.H;
   const int T = a.T, H = a.H, NC = a.nchunks, NSYS = S::nsys(T);
-  const bool consumer = wv < NCW;
-  const int ctid = tid - 64 * NCW;         // copy thread index
-  const int chW = Z::DS * sp + 16 * wv + cl;   // consumer lane's value channel
+  const int role = wv < NCW ? 0 : wv < 2 * NCW ? 1 : 2;    // state, output, copy
+  const int cw = role == 1 ? wv - NCW : wv;                // channel group of a state / output wave
+  const int ctid = tid - 64 * 2 * NCW;                     // copy thread index
+  const int chW = Z::DS * sp + 16 * cw + cl;               // the lane's value channel
 
   const IT *qp = static_cast<const IT *>(a.q);
   const IT *kp = static_cast<const IT *>(a.k);
@@ -563,7 +572,6 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
   // so a load has two scan iterations to arrive.
   struct Regs {
     uint4 k[Z::NPK], q[Z::NPK], v[Z::NPV], img[Z::NPI];
-    float fg[Z::NPK], fc[Z::NPK], fe[Z::NPK];   // GAM, CST of the row's key; EL of step row r
   };
   Regs reg[2];
   auto prefetch = [&](int c, Regs &R) __attribute__((always_inline)) {    // global -> registers, system c (rows clamped in bounds)
@@ -580,17 +588,13 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
       const int tk = min(max(pair_of(c0, r) - 1, 0), T - 1), tq = min(c0 + r, T - 1);
       R.k[ps] = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tk) * H + h) * D + part * VEC);
       R.q[ps] = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tq) * H + h) * D + part * VEC);
-      const float *Fg = reinterpret_cast<const float *>(wsq + (size_t)c * S::IMG + S::OFF_F);
-      R.fg[ps] = Fg[F_GAM * C + r];
-      R.fc[ps] = Fg[F_CST * C + r];
-      R.fe[ps] = Fg[F_EL * C + r];
     }
     const uint4 *src = reinterpret_cast<const uint4 *>(wsq + (size_t)c * S::IMG);
 #pragma unroll
     for (int j = 0; j < Z::NPI; ++j) R.img[j] = src[min(ctid + j * Z::NST, S::NU - 1)];
   };
-  auto stage = [&](int c, const Regs &R) __attribute__((always_inline)) { // registers -> LDS slot c & 1
-    const int s = c & 1, c0 = c * CS;
+  auto stage = [&](int c, const Regs &R) __attribute__((always_inline)) { // registers -> LDS slots of system c
+    const int s2 = c & 1, s3 = c % 3, c0 = c * CS;
 #pragma unroll
     for (int ps = 0; ps < Z::NPV; ++ps) {
       const int r = ps * RPV + ctid / TPV, part = ctid % TPV;
@@ -604,7 +608,7 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
           for (int e = 0; e < VEC; ++e) vf[e] = carry[(j + 2 * BW - 1) * D + Z::DS * sp + part * VEC + e];
           vv = scale_pack<IT, VEC>(vf, 1.f);
         }
-        *reinterpret_cast<uint4 *>(sV[s] + r * LXV + part * VEC) = vv;
+        *reinterpret_cast<uint4 *>(sV[s2] + r * LXV + part * VEC) = vv;
       }
     }
 #pragma unroll
@@ -613,33 +617,29 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
       if (r < C) {
         const int j = pair_of(c0, r);
         const bool live = step_of(c0, r) < T;
-        float xv[VEC];
-        unpack(keep_or_zero(live && j >= 1, R.k[ps]), IT(), xv);
+        uint4 kk = keep_or_zero(live && j >= 1, R.k[ps]);
         if (live && j <= 0) {   // a carried feature (fp32, normalised): x_prev, or window key j
           const float *src = carry + (j == 0 ? 0 : (j + BW) * D) + part * VEC;
+          float xv[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) xv[e] = src[e];
+          kk = scale_pack<OpT, VEC>(xv, 1.f);
         }
-        put_perm(sXg[s] + r * LX, part * VEC, scale_pack<OpT, VEC>(xv, R.fg[ps]));
-        put_perm(sXc[s] + r * LX, part * VEC, scale_pack<OpT, VEC>(xv, R.fc[ps]));
-        if (r < CSP) {
-          float qv[VEC];
-          unpack(keep_or_zero(r < CS && c0 + r < T, R.q[ps]), IT(), qv);
-          put_perm(sQe[s] + r * LX, part * VEC, scale_pack<OpT, VEC>(qv, R.fe[ps]));
-        }
+        put_perm(sX[s2] + r * LX, part * VEC, kk);
+        if (r < CSP) put_perm(sQ[s3] + r * LX, part * VEC, keep_or_zero(r < CS && c0 + r < T, R.q[ps]));
       }
     }
 #pragma unroll
     for (int j = 0; j < Z::NPI; ++j) {
       const int u = ctid + j * Z::NST;
-      if (u < S::NU) *reinterpret_cast<uint4 *>(sImg[s] + 16 * u) = R.img[j];
+      if (u < S::NU) *reinterpret_cast<uint4 *>(sImg[s3] + 16 * u) = R.img[j];
     }
   };
 
-  // ================= consumers =================
+  // ================= state waves =================
   f4 sT[NA];                 // S^T of this wave's 16 channels, C-layout per dk block
-  float rbeta[NB][4];        // F2/F2A: per-channel gains of the next chunk
-  if (consumer) {
+  float rbeta[NB][4];        // F2/F2A: per-channel gains of the next system
+  if (role == 0) {
 #pragma unroll
     for (int aa = 0; aa < NA; ++aa)
       sT[aa] = a.S0 ? *reinterpret_cast<const f4 *>(a.S0 + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) : zero4();
@@ -656,32 +656,37 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
   };
 
   auto consume = [&](int c) __attribute__((always_inline)) {
-    const int s = c & 1, c0 = c * CS;
-    const OpT *Xg = sXg[s], *Xc = sXc[s], *Qe = sQe[s];
-    const IT *V = sV[s];
-    const float *F = reinterpret_cast<const float *>(sImg[s] + S::OFF_F);
-    const OpT *Ao = reinterpret_cast<const OpT *>(sImg[s] + S::OFF_A);
-    const OpT *Pm = reinterpret_cast<const OpT *>(sImg[s] + S::OFF_P);
-    const OpT *Tb = reinterpret_cast<const OpT *>(sImg[s] + S::OFF_T);
+    const int s2 = c & 1, s3 = c % 3;
+    const OpT *X = sX[s2];
+    const IT *V = sV[s2];
+    const float *F = reinterpret_cast<const float *>(sImg[s3] + S::OFF_F);
+    const OpT *Ao = reinterpret_cast<const OpT *>(sImg[s3] + S::OFF_A);
+    const OpT *Tb = reinterpret_cast<const OpT *>(sImg[s3] + S::OFF_T);
     Pr Sp[NA / 2];
 #pragma unroll
-    for (int a2 = 0; a2 < NA / 2; ++a2) Sp[a2] = mkp(cvt<OpT>(sT[2 * a2]), cvt<OpT>(sT[2 * a2 + 1]));
-    // XS = diag(GAM) X S0^T: C-layout (virtual rows 16p+4g+i, channel c).
-    // QSt = (diag(EL) Q^ S0^T)^T: C-layout with channel rows 16w+4g+i and step
-    // column 16p+c (S fragments as the left operand).
-    f4 QSt[NBS], XS[NB];
+    for (int a2 = 0; a2 < NA / 2; ++a2) {
+      Sp[a2] = mkp(cvt<OpT>(sT[2 * a2]), cvt<OpT>(sT[2 * a2 + 1]));
+      sSp[s2][cw][a2][lane] = Sp[a2];
+    }
+    // XS = diag(GAM) X S0^T: C-layout (virtual rows 16p+4g+i, channel c), the row
+    // factor applied to the product
+    f4 XS[NB];
+    if constexpr (DELTA) {
 #pragma unroll
-    for (int p = 0; p < NB; ++p) {
-      if (p < NBS) QSt[p] = zero4();
-      XS[p] = zero4();
+      for (int p = 0; p < NB; ++p) {
+        XS[p] = zero4();
 #pragma unroll
-      for (int a2 = 0; a2 < NA / 2; ++a2) {
-        if (DELTA) mmap(XS[p], ldp(Xg + (16 * p + cl) * LX + 32 * a2 + 8 * g4), Sp[a2]);
-        if (p < NBS) mmap(QSt[p], Sp[a2], ldp(Qe + (16 * p + cl) * LX + 32 * a2 + 8 * g4));
+        for (int a2 = 0; a2 < NA / 2; ++a2) mmap(XS[p], ldp(X + (16 * p + cl) * LX + 32 * a2 + 8 * g4), Sp[a2]);
+        XS[p] *= *reinterpret_cast<const f4 *>(F + F_GAM * C + 16 * p + 4 * g4);
       }
     }
-    auto vcol = [&](int j4) { return 16 * wv + 4 * j4; };
+    // state: S^T <- e^{L_last} S^T + X^T diag(CST) E', accumulated as row blocks finish
+    const float lamtot = F[F_N * C];
+#pragma unroll
+    for (int aa = 0; aa < NA; ++aa) sT[aa] *= lamtot;
+    auto vcol = [&](int j4) { return 16 * cw + 4 * j4; };
     Frag Eb[NB];               // E' = E (F1/F3), eta (.) E (F2), V (F1A/F3A), eta (.) V (F2A)
+    Frag Ec[NB];               // diag(CST) E', the state update's right operand
 #pragma unroll
     for (int p = 0; p < NB; ++p) {
       f4 R = to_f4(ldT(V, LXV, 16 * p, vcol, lane));  // C-layout values of this wave's channels
@@ -699,70 +704,55 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
         if (p & 1) mma16(acc, ld4(Ao + frag_off(aslot_base(p), p - 1, lane)), Eb[p - 1]);
         R -= acc;
       }
+      f4 Ef;                   // E' in fp32
       if constexpr (S::SDELTA) {
-        f4 E = zero4();
-        mma16(E, ld4(Tb + (p * 64 + lane) * 4), cvt<OpT>(R));
-        Eb[p] = cvt<OpT>(E);
+        Ef = zero4();
+        mma16(Ef, ld4(Tb + (p * 64 + lane) * 4), cvt<OpT>(R));
       } else if constexpr (VAR == V_F2) {
         // rows 4g4..4g4+3 of block p: exact 4x4 solves, coupled by A_pp minus its 4x4 diagonal
-        const float *Ad = reinterpret_cast<const float *>(sImg[s] + S::OFF_AD) + (p * 4 + g4) * 8;
+        const float *Ad = reinterpret_cast<const float *>(sImg[s3] + S::OFF_AD) + (p * 4 + g4) * 8;
         const f4 c0v = *reinterpret_cast<const f4 *>(Ad), c1v = *reinterpret_cast<const f4 *>(Ad + 4);
         const float a10 = c0v[0], a20 = c0v[1], a21 = c0v[2], a30 = c0v[3], a31 = c1v[0], a32 = c1v[1];
         const Frag Ain = ld4(Tb + (p * 64 + lane) * 4);
-        f4 E, Fv;
+        f4 E;
         auto local = [&](const f4 &zz) {
           E[0] = zz[0];
-          Fv[0] = eta4[0] * E[0];
-          E[1] = zz[1] - a10 * Fv[0];
-          Fv[1] = eta4[1] * E[1];
-          E[2] = zz[2] - a20 * Fv[0] - a21 * Fv[1];
-          Fv[2] = eta4[2] * E[2];
-          E[3] = zz[3] - a30 * Fv[0] - a31 * Fv[1] - a32 * Fv[2];
-          Fv[3] = eta4[3] * E[3];
+          Ef[0] = eta4[0] * E[0];
+          E[1] = zz[1] - a10 * Ef[0];
+          Ef[1] = eta4[1] * E[1];
+          E[2] = zz[2] - a20 * Ef[0] - a21 * Ef[1];
+          Ef[2] = eta4[2] * E[2];
+          E[3] = zz[3] - a30 * Ef[0] - a31 * Ef[1] - a32 * Ef[2];
+          Ef[3] = eta4[3] * E[3];
         };
         local(R);
 #pragma unroll
         for (int it = 0; it < 3; ++it) {
           f4 cpl = zero4();
-          mma16(cpl, Ain, cvt<OpT>(Fv));
+          mma16(cpl, Ain, cvt<OpT>(Ef));
           local(R - cpl);
         }
-        Eb[p] = cvt<OpT>(Fv);      // eta (.) E feeds the state update and the outputs
       } else if constexpr (VAR == V_F2A) {
-        Eb[p] = cvt<OpT>(eta4 * R);
+        Ef = eta4 * R;
       } else {
-        Eb[p] = cvt<OpT>(R);
+        Ef = R;
       }
-    }
-    // outputs, transposed: o^T = e^{L} (S0 Q^^T) + E'^T P^T.  The C-layout fragments of
-    // E' are the left operands and the stored score fragments the right ones; lane
-    // (g, c) ends with channels 16w+4g..16w+4g+3 of step 16p+c and stores them.
+      Eb[p] = cvt<OpT>(Ef);
+      sEb[s2][cw][p][lane] = Eb[p];
+      Ec[p] = cvt<OpT>(Ef * *reinterpret_cast<const f4 *>(F + F_CST * C + 16 * p + 4 * g4));
+      // a finished pair of row blocks (or the last, unpaired one) goes into the state
+      if ((p & 1) || p == NB - 1) {
+        const bool pair = p & 1;
+        const int q0 = pair ? p - 1 : p;
 #pragma unroll
-    for (int p = 0; p < NBS; ++p) {
-      const int qm = S::qmax(p);
-      f4 O = QSt[p];
-#pragma unroll
-      for (int q = 0; q + 1 <= qm; q += 2) mmap(O, mkp(Eb[q], Eb[q + 1]), ldp(Pm + frag_off(S::pbase(p), q, lane)));
-      if (!(qm & 1)) mma16(O, Eb[qm], ld4(Pm + frag_off(S::pbase(p), qm, lane)));
-      const int srow = 16 * p + cl, t = c0 + srow;
-      if (srow < CS && t < T)
-        *reinterpret_cast<Frag *>(op + ((size_t)(b * T + t) * H + h) * D + Z::DS * sp + 16 * wv + 4 * g4) = cvt<OpT>(O);
-    }
-    // state: S^T <- e^{L_last} S^T + (diag(CST) X)^T E'
-    const Frag *CE = Eb;
-    const float lamtot = F[F_N * C];
-#pragma unroll
-    for (int aa = 0; aa < NA; ++aa) {
-      auto dkcol = [&](int j4) { return kperm(16 * aa + 4 * j4); };
-      f4 acc = sT[aa] * lamtot;
-      if constexpr (NB == 1) {
-        mma16(acc, ldT(Xc, LX, 0, dkcol, lane), CE[0]);
-      } else {
-#pragma unroll
-        for (int p = 0; p < NB; p += 2)
-          mmap(acc, mkp(ldT(Xc, LX, 16 * p, dkcol, lane), ldT(Xc, LX, 16 * p + 16, dkcol, lane)), mkp(CE[p], CE[p + 1]));
+        for (int aa = 0; aa < NA; ++aa) {
+          auto dkcol = [&](int j4) { return kperm(16 * aa + 4 * j4); };
+          if (pair)
+            mmap(sT[aa], mkp(ldT(X, LX, 16 * q0, dkcol, lane), ldT(X, LX, 16 * p, dkcol, lane)), mkp(Ec[q0], Ec[p]));
+          else
+            mma16(sT[aa], ldT(X, LX, 16 * q0, dkcol, lane), Ec[q0]);
+        }
       }
-      sT[aa] = acc;
     }
     if (a.chunk_states && ((c + 1) % BW == 0 || c == NSYS - 1)) {   // every C steps
       const int ci = c / BW;
@@ -772,11 +762,43 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
     }
   };
 
-  // ---------------- scan: iteration i consumes system i and stages system i+1 ----------------
-  // Each role runs its own loop, so neither keeps the other's loop-carried
-  // registers live; both pass the same number of workgroup barriers (one per
-  // system after a prologue barrier), which is what the barrier counts.
-  if (consumer) {
+  // ================= output waves =================
+  // outputs of system c, transposed: o^T = (diag(EL) Q^ S0^T)^T + E'^T P^T.  The
+  // S fragments are the left operands of the first product; the C-layout
+  // fragments of E' the left operands, the stored score fragments the right ones,
+  // of the second.  Lane (g, c) ends with channels 16w+4g..16w+4g+3 of step 16p+c.
+  auto output = [&](int c) __attribute__((always_inline)) {
+    const int s2 = c & 1, s3 = c % 3, c0 = c * CS;
+    const OpT *Q = sQ[s3];
+    const float *F = reinterpret_cast<const float *>(sImg[s3] + S::OFF_F);
+    const OpT *Pm = reinterpret_cast<const OpT *>(sImg[s3] + S::OFF_P);
+    Pr Sp[NA / 2];
+    Frag Eb[NB];
+#pragma unroll
+    for (int a2 = 0; a2 < NA / 2; ++a2) Sp[a2] = sSp[s2][cw][a2][lane];
+#pragma unroll
+    for (int p = 0; p < NB; ++p) Eb[p] = sEb[s2][cw][p][lane];
+#pragma unroll
+    for (int ps = 0; ps < NBS; ++ps) {
+      f4 O = zero4();
+#pragma unroll
+      for (int a2 = 0; a2 < NA / 2; ++a2) mmap(O, Sp[a2], ldp(Q + (16 * ps + cl) * LX + 32 * a2 + 8 * g4));
+      O *= F[F_EL * C + 16 * ps + cl];
+      const int qm = S::qmax(ps);
+#pragma unroll
+      for (int q = 0; q + 1 <= qm; q += 2) mmap(O, mkp(Eb[q], Eb[q + 1]), ldp(Pm + frag_off(S::pbase(ps), q, lane)));
+      if (!(qm & 1)) mma16(O, Eb[qm], ld4(Pm + frag_off(S::pbase(ps), qm, lane)));
+      const int srow = 16 * ps + cl, t = c0 + srow;
+      if (srow < CS && t < T)
+        *reinterpret_cast<Frag *>(op + ((size_t)(b * T + t) * H + h) * D + Z::DS * sp + 16 * cw + 4 * g4) = cvt<OpT>(O);
+    }
+  };
+
+  // ---------------- scan: iteration i works on system i (state), i-1 (outputs), i+1 (staging) ----------------
+  // Each role runs its own loop, so none keeps another's loop-carried registers
+  // live; all pass the same number of workgroup barriers (a prologue barrier,
+  // then one per iteration, NSYS + 1 iterations), which is what the barrier counts.
+  if (role == 0) {
     if (PERCH) prefetch_beta(0);
     __syncthreads();
     for (int i = 0; i < NSYS; ++i) {
@@ -784,10 +806,18 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
       if (PERCH && i + 1 < NSYS) prefetch_beta(i + 1);
       __syncthreads();
     }
+    __syncthreads();
     if (a.S_out) {
 #pragma unroll
       for (int aa = 0; aa < NA; ++aa)
         *reinterpret_cast<f4 *>(a.S_out + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) = sT[aa];
+    }
+  } else if (role == 1) {
+    __syncthreads();
+    __syncthreads();
+    for (int i = 1; i <= NSYS; ++i) {
+      output(i - 1);
+      __syncthreads();
     }
   } else {
     prefetch(0, reg[0]);
@@ -811,10 +841,11 @@ __global__ __launch_bounds__(64 * (D / 16 / NS + 8)) void chunk_scan(FwdArgs a, 
         __syncthreads();
       }
     }
+    __syncthreads();
     if (a.write_tail) {
       // outgoing x_prev = phi(k_{T-1}) and, for windows, the last Bw-1 pairs
       // j = T-Bw+1..T-1 (keys phi(k_{j-1}), values v_j; carried ones for j <= 0)
-      const int w8 = wv - NCW;
+      const int w8 = wv - 2 * NCW;
       auto key_row = [&](int j, float *dst) {   // normalised key of pair j into dst[0..D)
         float xv[2] = {0.f, 0.f};
         if (j >= 1) {
