@@ -10,10 +10,12 @@ synthetic N(0,1) inputs.  One step = one falcon_chunk_fwd call over one batch
 Timing: three rotating input sets (more bytes than the 256 MB MALL), W untimed
 calls, then K timed calls bracketed by torch.cuda.synchronize().  Each call is
 also bracketed by HIP events on the stream it is launched on, which gives the
-average device time of the forward path used for the roofline: the prep kernel
-over all chunks plus the state scan (chunk-parallel path, the default when the
-shape has a workspace, allocated once outside the timed region), or the one
-fused kernel (--fused, or shapes without a workspace).
+average device time of the forward path used for the roofline.  Paths
+(--path): "onepass" calls without a workspace (the one-pass kernel where it is
+built, else the fused kernel); "split" passes a workspace (allocated once
+outside the timed region): the prep kernel over all systems, then the state
+scan.  "auto" (default) takes the faster one measured per shape class: split
+for Falcon-3 windows and head dim 128, one-pass otherwise.
 """
 
 from __future__ import annotations
@@ -174,7 +176,8 @@ def main():
     ap.add_argument("--window", type=int, default=4, help="Falcon-3/3A window (pairs)")
     ap.add_argument("--decode", action="store_true", help="time the single-token step instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fused", action="store_true", help="run the fused single-kernel path (no workspace)")
+    ap.add_argument("--path", choices=("auto", "onepass", "split"), default="auto",
+                    help="forward path: one-pass (no workspace), split (workspace), or auto")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -211,10 +214,11 @@ def main():
         sets.append(d)
     del inp
     stream = torch.cuda.current_stream()
-    ws_bytes = 0 if args.fused else workspace_bytes(variant, w.dtype, w.batch, w.seqlen, w.heads, w.dk, w.dv,
-                                                    w.chunk, window)
+    split_bytes = workspace_bytes(variant, w.dtype, w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk, window)
+    want = args.path if args.path != "auto" else ("split" if (window > 1 or w.dk >= 128) else "onepass")
+    ws_bytes = split_bytes if want == "split" else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else False
-    path = "split" if ws_bytes else "fused"
+    path = "split" if ws_bytes else "onepass"
 
     def call(d):
         chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk, window=window,
@@ -257,7 +261,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
     roof["traffic"] = measured_traffic(f"{path} {variant} {w.name}")
-    roof["kernel"] = ("chunk_prep + chunk_scan" if path == "split" else "chunk_fwd_window" if window > 1 else
+    roof["kernel"] = ("chunk_prep + chunk_scan" if path == "split" else
+                      "chunk_scan (one-pass)" if (w.dtype == "bf16" and w.dk <= 64 and w.chunk <= 64) else
                       "chunk_fwd_pipe" if w.dk <= 64 else "chunk_fwd_rows")
     roof["path"] = path
     roof["workspace_bytes"] = ws_bytes

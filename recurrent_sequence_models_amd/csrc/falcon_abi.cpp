@@ -75,6 +75,9 @@ bool chunk_fwd_split_supported(int variant, bool bf16, int dk, int dv, int chunk
 size_t chunk_fwd_split_workspace(int variant, bool bf16, int dk, int dv, int chunk, int window, int bh, int T);
 hipError_t launch_chunk_fwd_split(int variant, bool bf16, int dk, int dv, int chunk, int window, const FwdArgs &a,
                                   void *ws, hipStream_t s);
+int chunk_fwd_onepass_ns(int variant, bool bf16, int dk, int dv, int chunk, int window, int bh);
+hipError_t launch_chunk_fwd_onepass(int variant, bool bf16, int dk, int dv, int chunk, int window, const FwdArgs &a,
+                                    hipStream_t s);
 
 int choose_nsplit(int variant, bool bf16, int dk, int dv, int chunk, int batch_heads) {
   int n = 1;
@@ -165,6 +168,21 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   a.write_tail = (final_state && (split || (!win && (nsplit == 1 || !xprev_alias)))) ? 1 : 0;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  // Without a workspace: the one-pass kernel where it is built for the shape.
+  const int onepass = split ? 0 : falcon::chunk_fwd_onepass_ns(s->variant, bf16, s->dk, s->dv, s->chunk, a.window,
+                                                                s->batch * s->heads);
+  if (onepass) {
+    const bool alias = init && final_state &&
+                       (init->x_prev == final_state->x_prev ||
+                        (win && (init->win_x == final_state->win_x || init->win_v == final_state->win_v)));
+    a.write_tail = (final_state && (onepass == 1 || !alias)) ? 1 : 0;
+    if (falcon::launch_chunk_fwd_onepass(s->variant, bf16, s->dk, s->dv, s->chunk, a.window, a, hs) != hipSuccess)
+      return FALCON_ERR_HIP;
+    if (final_state && !a.write_tail) {
+      if (falcon::launch_tail(s->variant, bf16, s->dk, s->dv, a, hs) != hipSuccess) return FALCON_ERR_HIP;
+    }
+    return FALCON_OK;
+  }
   if (split) {   // prep over all systems, then the scan workgroups of each sequence
     return falcon::launch_chunk_fwd_split(s->variant, bf16, s->dk, s->dv, s->chunk, a.window, a, workspace, hs) ==
                    hipSuccess

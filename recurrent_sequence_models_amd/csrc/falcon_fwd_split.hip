@@ -10,6 +10,9 @@ bool chunk_fwd_split_win_supported(int variant, bool bf16, int d, int chunk, int
 size_t chunk_fwd_split_win_workspace(int variant, bool bf16, int d, int chunk, int window, int bh, int T);
 hipError_t launch_chunk_fwd_split_win(int variant, bool bf16, int d, int chunk, int window, const FwdArgs &a,
                                       void *ws, hipStream_t st);
+int chunk_fwd_onepass_win_ns(int variant, bool bf16, int d, int chunk, int window, int bh);
+hipError_t launch_chunk_fwd_onepass_win(int variant, bool bf16, int d, int chunk, int window, const FwdArgs &a,
+                                        hipStream_t st);
 
 namespace {
 
@@ -79,6 +82,26 @@ hipError_t launch_chunk_fwd_split(int variant, bool bf16, int dk, int dv, int ch
   return dispatch_split(one_pair(variant), bf16, dk, chunk, [&](auto v, auto *t, auto dd, auto cc) -> hipError_t {
     using IT = std::remove_pointer_t<decltype(t)>;
     return launch_split<decltype(v)::value, IT, decltype(dd)::value, decltype(cc)::value, 1>(a, ws, st);
+  });
+}
+
+// One-pass form (no workspace): channel split it would use for bh sequences, 0 if not built.
+int chunk_fwd_onepass_ns(int variant, bool bf16, int dk, int dv, int chunk, int window, int bh) {
+  if (dk != dv) return 0;
+  if (window > 1) return chunk_fwd_onepass_win_ns(variant, bf16, dk, chunk, window, bh);
+  return dispatch_split(one_pair(variant), bf16, dk, chunk, [bh](auto v, auto *t, auto dd, auto cc) -> int {
+    using IT = std::remove_pointer_t<decltype(t)>;
+    return pick_ns<decltype(v)::value, IT, decltype(dd)::value, decltype(cc)::value, 1, true>(bh);
+  });
+}
+
+hipError_t launch_chunk_fwd_onepass(int variant, bool bf16, int dk, int dv, int chunk, int window, const FwdArgs &a,
+                                    hipStream_t st) {
+  if (chunk_fwd_onepass_ns(variant, bf16, dk, dv, chunk, window, a.B * a.H) == 0) return hipErrorInvalidValue;
+  if (window > 1) return launch_chunk_fwd_onepass_win(variant, bf16, dk, chunk, window, a, st);
+  return dispatch_split(one_pair(variant), bf16, dk, chunk, [&](auto v, auto *t, auto dd, auto cc) -> hipError_t {
+    using IT = std::remove_pointer_t<decltype(t)>;
+    return launch_onepass<decltype(v)::value, IT, decltype(dd)::value, decltype(cc)::value, 1>(a, st);
   });
 }
 

@@ -66,4 +66,19 @@ hipError_t launch_chunk_fwd_split_win(int variant, bool bf16, int d, int chunk, 
   });
 }
 
+int chunk_fwd_onepass_win_ns(int variant, bool bf16, int d, int chunk, int window, int bh) {
+  return dispatch_win(variant, bf16, d, chunk, window, [bh](auto v, auto *t, auto dd, auto w) -> int {
+    using IT = std::remove_pointer_t<decltype(t)>;
+    return pick_ns<decltype(v)::value, IT, decltype(dd)::value, 64, decltype(w)::value, true>(bh);
+  });
+}
+
+hipError_t launch_chunk_fwd_onepass_win(int variant, bool bf16, int d, int chunk, int window, const FwdArgs &a,
+                                        hipStream_t st) {
+  return dispatch_win(variant, bf16, d, chunk, window, [&](auto v, auto *t, auto dd, auto w) -> hipError_t {
+    using IT = std::remove_pointer_t<decltype(t)>;
+    return launch_onepass<decltype(v)::value, IT, decltype(dd)::value, 64, decltype(w)::value>(a, st);
+  });
+}
+
 }  // namespace falcon

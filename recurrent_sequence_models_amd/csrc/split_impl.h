@@ -123,25 +123,36 @@ struct Split {
 // of S evolve independently given the keys).  A workgroup takes D/NS channels:
 // per 16 of them one state wave (the chain S -> residuals -> S, system by system)
 // and one output wave (the outputs of the previous system, from the S and E'
-// fragments the state wave leaves in LDS), plus 8 copy waves that stage the
-// shared key / query rows, the system image and the slice's value columns.
-template <int VAR, typename IT, int D, int C, int BW, int NS>
+// fragments the state wave leaves in LDS), plus copy waves that stage the shared
+// key / query rows and the slice's value columns.  Two-kernel form (ONE =
+// false): 8 copy waves also stage the system image the prep kernel wrote.
+// One-pass form (ONE = true): 4 derive waves build each image in LDS one system
+// ahead (the prep kernel's tiles, from the staged rows), and 4 copy waves stage
+// rows, their squared norms and the gates.
+template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false>
 struct Scan {
   using S = Split<VAR, IT, D, C, BW>;
   static constexpr int DS = D / NS;                          // value channels per workgroup
-  static constexpr int NCW = DS / 16, NSW = 8, NT = 64 * (2 * NCW + NSW), NST = 64 * NSW;
+  // one-pass derive waves (8 measured slower than 4: every role shares the CU's SIMDs)
+  static constexpr int NDW = ONE ? S::NPW : 0;
+  static constexpr int NCW = DS / 16, NSW = ONE ? 4 : 8;
+  static constexpr int RG = BW == 1 ? R_EC + 1 : R_N;        // per-row arrays a derive wave uses
+  static constexpr int NT = 64 * (2 * NCW + NDW + NSW), NST = 64 * NSW;
   static constexpr int LXV = DS + S::PADE;                   // V rows (this workgroup's channels)
   static constexpr int RPC = NST / S::TPR, NPK = (C + RPC - 1) / RPC;   // key / query rows per copy pass
   static constexpr int TPV = DS / S::VEC, RPV = NST / TPV, NPV = (C + RPV - 1) / RPV;
-  static constexpr int NPI = (S::NU + NST - 1) / NST;
-  // keys and values: 2 slots (state waves); queries and images: 3 (output waves lag one
-  // system); S and E' fragments handed to the output waves: 2
+  static constexpr int NPI = ONE ? 1 : (S::NU + NST - 1) / NST;
+  // LDS slots: keys and values 2 (3 one-pass: derive waves read one system ahead),
+  // queries 3 (4), images 3 (output waves lag one system); S and E' fragments 2
+  static constexpr int NXS = ONE ? 3 : 2, NQS = ONE ? 4 : 3;
   static constexpr size_t lds() {
-    return (size_t)S::SZ * (2 * C * S::LX + 3 * S::CSP * S::LX + 2 * C * LXV) + 3 * (size_t)S::IMG +
-           2 * (size_t)NCW * 64 * S::SZ * (8 * (S::NA / 2) + 4 * S::NB);
+    return (size_t)S::SZ * (NXS * C * S::LX + NQS * S::CSP * S::LX + NXS * C * LXV) + 3 * (size_t)S::IMG +
+           2 * (size_t)NCW * 64 * S::SZ * (8 * (S::NA / 2) + 4 * S::NB) +
+           (ONE ? (size_t)4 * (3 * 4 * C + NDW * RG * C) : 0);
   }
   static constexpr bool fits() {
-    return DS >= 16 && D % NS == 0 && lds() + 256 <= 160 * 1024 && S::prep_lds() + 256 <= 64 * 1024;
+    return DS >= 16 && D % NS == 0 && C <= 64 && NT <= 1024 && lds() + 256 <= 160 * 1024 &&
+           (ONE || S::prep_lds() + 256 <= 64 * 1024);
   }
 };
 
@@ -181,6 +192,174 @@ __device__ __forceinline__ uint4 scale_pack(const float *x, float f) {
   return *reinterpret_cast<const uint4 *>(tmp);
 }
 
+// Key-side tiles of one system from its raw rows X (virtual rows) and Q (step
+// rows), dk permuted, and its per-row arrays G (R_* layout, C entries each):
+// wave w of 4 computes its share of the Gram and score blocks and of the
+// diagonal blocks, finishes them with the decay / norm / step factors and
+// writes them, with the per-row factors (wave 3), into the image at img (global
+// memory for the prep kernel, LDS for the one-pass kernel).
+template <int VAR, typename IT, int D, int C, int BW>
+__device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const float *G, unsigned char *img, bool sep,
+                                             float Llast, int w, int lane) {
+  using S = Split<VAR, IT, D, C, BW>;
+  using OpT = IT;
+  using Frag = typename Op<OpT>::frag;
+  using Pr = Pair<OpT>;
+  constexpr int NB = S::NB, NA = S::NA, LX = S::LX, CS = S::CS, CSP = S::CSP, RLQ = S::RLQ;
+  constexpr bool DELTA = S::DELTA;
+  const int g4 = lane >> 4, cl = lane & 15;
+  OpT *gA = reinterpret_cast<OpT *>(img + S::OFF_A);
+  OpT *gP = reinterpret_cast<OpT *>(img + S::OFF_P);
+  OpT *gT = reinterpret_cast<OpT *>(img + S::OFF_T);
+  float *gAd = reinterpret_cast<float *>(img + S::OFF_AD);
+  float *gF = reinterpret_cast<float *>(img + S::OFF_F);
+  (void)CS;
+  auto rows16 = [&](const OpT *M, int blk, Pr (&out)[NA / 2]) {
+#pragma unroll
+    for (int a2 = 0; a2 < NA / 2; ++a2) out[a2] = ldp(M + (16 * blk + cl) * LX + 32 * a2 + 8 * g4);
+  };
+  auto tile = [&](const Pr (&Am)[NA / 2], const Pr (&Bm)[NA / 2]) {
+    f4 acc = zero4();
+#pragma unroll
+    for (int a2 = 0; a2 < NA / 2; ++a2) mmap(acc, Am[a2], Bm[a2]);
+    return acc;
+  };
+  // Gram (isP = 0, virtual rows 16p + c) or score (isP = 1, step rows 16p + c)
+  // block (p, q), transposed: lane (g, c) holds element (row 16p + c, virtual-row
+  // column 16q + 4g + i), the consumers' A-operand fragment.  Off-diagonal Gram
+  // blocks are wholly visible (steps do not straddle blocks); score blocks see
+  // the columns whose step is at most the row's.
+  auto finish = [&](const f4 &acc, int isP, int p, int q) {
+    const int row = 16 * p + cl;
+    f4 val;
+    if (sep) {
+      const f4 ec = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * q + 4 * g4);
+      const float er = G[(isP ? R_EP : R_EA) * C + row];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] * er * ec[i];
+        val[i] = (!isP || (16 * q + 4 * g4 + i) / BW <= row) ? v : 0.f;
+      }
+    } else {
+      const f4 cf = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * q + 4 * g4);
+      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * q + 4 * g4);
+      const float Lrow = G[(isP ? RLQ : R_LM) * C + row];
+      const float rf = G[(isP ? R_IQ : R_IK) * C + row];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] * __expf(Lrow - Lc4[i]) * rf * cf[i];
+        val[i] = (!isP || (16 * q + 4 * g4 + i) / BW <= row) ? v : 0.f;
+      }
+    }
+    OpT *dst = isP ? gP + frag_off(S::pbase(p), q, lane) : gA + frag_off(aslot_base(p), q, lane);
+    *reinterpret_cast<Frag *>(dst) = cvt<OpT>(val);
+  };
+  // diagonal block p: F1/F3 -> T_pp (A-layout); F2 -> the 4x4 diagonal coefficients and A_pp without them
+  auto diag = [&](const f4 &acc, int p) {   // acc: <x_{16p+4g+i}, x_{16p+c}> (symmetric)
+    const int r0 = 4 * g4;
+    f4 NA4, NC4;   // N[16p+c][16p+4g+i] (A-layout) and N[16p+4g+i][16p+c] (C-layout), strictly earlier steps
+    if (sep) {
+      const f4 ea4 = *reinterpret_cast<const f4 *>(G + R_EA * C + 16 * p + r0);
+      const f4 ec4 = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * p + r0);
+      const float ea1 = G[R_EA * C + 16 * p + cl], ec1 = G[R_EC * C + 16 * p + cl];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        NA4[i] = ((r0 + i) / BW < cl / BW) ? acc[i] * ea1 * ec4[i] : 0.f;
+        NC4[i] = (cl / BW < (r0 + i) / BW) ? acc[i] * ea4[i] * ec1 : 0.f;
+      }
+    } else {
+      const f4 cf4 = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * p + r0);
+      const f4 ik4 = *reinterpret_cast<const f4 *>(G + R_IK * C + 16 * p + r0);
+      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * p + r0);
+      const f4 Lm4 = *reinterpret_cast<const f4 *>(G + R_LM * C + 16 * p + r0);
+      const float Lc1 = G[R_LC * C + 16 * p + cl], Lm1 = G[R_LM * C + 16 * p + cl];
+      const float ik1 = G[R_IK * C + 16 * p + cl], cf1 = G[R_CF * C + 16 * p + cl];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float va = acc[i] * __expf(Lm1 - Lc4[i]) * ik1 * cf4[i];
+        const float vc = acc[i] * __expf(Lm4[i] - Lc1) * ik4[i] * cf1;
+        NA4[i] = ((r0 + i) / BW < cl / BW) ? va : 0.f;
+        NC4[i] = (cl / BW < (r0 + i) / BW) ? vc : 0.f;
+      }
+    }
+    if constexpr (S::SDELTA) {
+      // row-oriented block Jacobi: T (I + N) = I, so T <- (I - T N_o)(I + N_d)^{-1},
+      // exact after 3 sweeps; Y holds T in A-layout (row c, columns 4g..4g+3).
+      // n_ab = N[4g+a][4g+b] sits in lane (g, 4g+a), entry b of NA4.
+      const int src = 16 * g4 + r0;
+      const float n10 = __shfl(NA4[0], src + 1), n20 = __shfl(NA4[0], src + 2), n21 = __shfl(NA4[1], src + 2);
+      const float n30 = __shfl(NA4[0], src + 3), n31 = __shfl(NA4[1], src + 3), n32 = __shfl(NA4[2], src + 3);
+      f4 NoC;   // C-layout of N without its 4x4 diagonal sub-blocks
+#pragma unroll
+      for (int i = 0; i < 4; ++i) NoC[i] = ((cl >> 2) == g4) ? 0.f : NC4[i];
+      f4 Z, Y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Z[i] = (r0 + i == cl) ? 1.f : 0.f;
+      auto local = [&](const f4 &w) {     // t (I + N_gg) = w, t a row of 4
+        Y[3] = w[3];
+        Y[2] = w[2] - Y[3] * n32;
+        Y[1] = w[1] - Y[2] * n21 - Y[3] * n31;
+        Y[0] = w[0] - Y[1] * n10 - Y[2] * n20 - Y[3] * n30;
+      };
+      local(Z);
+#pragma unroll
+      for (int it = 0; it < 3; ++it) {
+        f4 cpl = zero4();
+        mma16(cpl, NoC, Y);   // fp32: C-layout of N_o^T Y^T = A-layout of Y N_o
+        local(Z - cpl);
+      }
+      *reinterpret_cast<Frag *>(gT + (p * 64 + lane) * 4) = cvt<OpT>(Y);
+    } else {
+      // lane (g, 4g+b) holds N[4g+a][4g+b] in NC4[a]; slots: 10 20 21 30 31 32
+      if ((cl >> 2) == g4) {
+        float *ad = gAd + (p * 4 + g4) * 8;
+        const int bb = cl - r0;
+        if (bb == 0) { ad[0] = NC4[1]; ad[1] = NC4[2]; ad[3] = NC4[3]; }
+        if (bb == 1) { ad[2] = NC4[2]; ad[4] = NC4[3]; }
+        if (bb == 2) ad[5] = NC4[3];
+      }
+      f4 NoA;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) NoA[i] = ((cl >> 2) == g4) ? 0.f : NA4[i];
+      *reinterpret_cast<Frag *>(gT + (p * 64 + lane) * 4) = cvt<OpT>(NoA);
+    }
+  };
+  auto rowfac = [&]() {
+    if (lane < C) {
+      const float L = G[R_LC * C + lane], Lm = G[R_LM * C + lane];
+      gF[F_GAM * C + lane] = __expf(Lm) * G[R_IK * C + lane];
+      gF[F_EL * C + lane] = lane < CSP ? __expf(G[RLQ * C + lane]) * G[R_IQ * C + lane] : 0.f;
+      gF[F_CST * C + lane] = __expf(Llast - L) * G[R_CF * C + lane];
+      gF[F_ETA * C + lane] = G[R_ETA * C + lane];
+      if (lane == 0) gF[F_N * C] = __expf(Llast);
+    }
+  };
+  auto run = [&](auto wc) {
+    constexpr int w = decltype(wc)::value;
+    constexpr JobList J = BW == 1 ? make_jobs(NB, DELTA, w) : make_jobs_win(NB, CS, BW, DELTA, w);
+    constexpr int NJ = J.n > 0 ? J.n : 1;
+    Pr Dop[NA / 2], Aop[NJ][NA / 2], Bop[NJ][NA / 2];
+    if constexpr (J.diag >= 0) rows16(X, J.diag, Dop);
+#pragma unroll
+    for (int j = 0; j < J.n; ++j) {
+      rows16(X, J.q[j], Aop[j]);
+      rows16(J.isP[j] ? Q : X, J.p[j], Bop[j]);
+    }
+    f4 dacc, acc[NJ];
+    if constexpr (J.diag >= 0) dacc = tile(Dop, Dop);
+#pragma unroll
+    for (int j = 0; j < J.n; ++j) acc[j] = tile(Aop[j], Bop[j]);
+    if constexpr (J.diag >= 0) diag(dacc, J.diag);
+#pragma unroll
+    for (int j = 0; j < J.n; ++j) finish(acc[j], J.isP[j], J.p[j], J.q[j]);
+    if constexpr (w == S::NPW - 1) rowfac();
+  };
+  if (w == 0) run(std::integral_constant<int, 0>());
+  else if (w == 1) run(std::integral_constant<int, 1>());
+  else if (w == 2) run(std::integral_constant<int, 2>());
+  else run(std::integral_constant<int, 3>());
+}
+
 // ============================== prep kernel ==============================
 template <int VAR, typename IT, int D, int C, int BW>
 __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) {
@@ -203,11 +382,6 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
   const IT *qp = static_cast<const IT *>(a.q);
   const IT *kp = static_cast<const IT *>(a.k);
   unsigned char *img = ws + (size_t)blockIdx.x * S::IMG;
-  OpT *gA = reinterpret_cast<OpT *>(img + S::OFF_A);
-  OpT *gP = reinterpret_cast<OpT *>(img + S::OFF_P);
-  OpT *gT = reinterpret_cast<OpT *>(img + S::OFF_T);
-  float *gAd = reinterpret_cast<float *>(img + S::OFF_AD);
-  float *gF = reinterpret_cast<float *>(img + S::OFF_F);
 
   if (c == 0) {   // the sequence's carry block
     float *carry = reinterpret_cast<float *>(ws + (size_t)a.B * H * NSYS * S::IMG + (size_t)bh * S::CARRY);
@@ -366,176 +540,37 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
   }
   __syncthreads();
 
-  const OpT *X = sX, *Q = sQ;
-  const float *G = sR;
-  auto rows16 = [&](const OpT *M, int blk, Pr (&out)[NA / 2]) {
-#pragma unroll
-    for (int a2 = 0; a2 < NA / 2; ++a2) out[a2] = ldp(M + (16 * blk + cl) * LX + 32 * a2 + 8 * g4);
-  };
-  auto tile = [&](const Pr (&Am)[NA / 2], const Pr (&Bm)[NA / 2]) {
-    f4 acc = zero4();
-#pragma unroll
-    for (int a2 = 0; a2 < NA / 2; ++a2) mmap(acc, Am[a2], Bm[a2]);
-    return acc;
-  };
-  // Gram (isP = 0, virtual rows 16p + c) or score (isP = 1, step rows 16p + c)
-  // block (p, q), transposed: lane (g, c) holds element (row 16p + c, virtual-row
-  // column 16q + 4g + i), the consumers' A-operand fragment.  Off-diagonal Gram
-  // blocks are wholly visible (steps do not straddle blocks); score blocks see
-  // the columns whose step is at most the row's.
-  auto finish = [&](const f4 &acc, int isP, int p, int q) {
-    const int row = 16 * p + cl;
-    f4 val;
-    if (sep) {
-      const f4 ec = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * q + 4 * g4);
-      const float er = G[(isP ? R_EP : R_EA) * C + row];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = acc[i] * er * ec[i];
-        val[i] = (!isP || (16 * q + 4 * g4 + i) / BW <= row) ? v : 0.f;
-      }
-    } else {
-      const f4 cf = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * q + 4 * g4);
-      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * q + 4 * g4);
-      const float Lrow = G[(isP ? RLQ : R_LM) * C + row];
-      const float rf = G[(isP ? R_IQ : R_IK) * C + row];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = acc[i] * __expf(Lrow - Lc4[i]) * rf * cf[i];
-        val[i] = (!isP || (16 * q + 4 * g4 + i) / BW <= row) ? v : 0.f;
-      }
-    }
-    OpT *dst = isP ? gP + frag_off(S::pbase(p), q, lane) : gA + frag_off(aslot_base(p), q, lane);
-    *reinterpret_cast<Frag *>(dst) = cvt<OpT>(val);
-  };
-  // diagonal block p: F1/F3 -> T_pp (A-layout); F2 -> the 4x4 diagonal coefficients and A_pp without them
-  auto diag = [&](const f4 &acc, int p) {   // acc: <x_{16p+4g+i}, x_{16p+c}> (symmetric)
-    const int r0 = 4 * g4;
-    f4 NA4, NC4;   // N[16p+c][16p+4g+i] (A-layout) and N[16p+4g+i][16p+c] (C-layout), strictly earlier steps
-    if (sep) {
-      const f4 ea4 = *reinterpret_cast<const f4 *>(G + R_EA * C + 16 * p + r0);
-      const f4 ec4 = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * p + r0);
-      const float ea1 = G[R_EA * C + 16 * p + cl], ec1 = G[R_EC * C + 16 * p + cl];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        NA4[i] = ((r0 + i) / BW < cl / BW) ? acc[i] * ea1 * ec4[i] : 0.f;
-        NC4[i] = (cl / BW < (r0 + i) / BW) ? acc[i] * ea4[i] * ec1 : 0.f;
-      }
-    } else {
-      const f4 cf4 = *reinterpret_cast<const f4 *>(G + R_CF * C + 16 * p + r0);
-      const f4 ik4 = *reinterpret_cast<const f4 *>(G + R_IK * C + 16 * p + r0);
-      const f4 Lc4 = *reinterpret_cast<const f4 *>(G + R_LC * C + 16 * p + r0);
-      const f4 Lm4 = *reinterpret_cast<const f4 *>(G + R_LM * C + 16 * p + r0);
-      const float Lc1 = G[R_LC * C + 16 * p + cl], Lm1 = G[R_LM * C + 16 * p + cl];
-      const float ik1 = G[R_IK * C + 16 * p + cl], cf1 = G[R_CF * C + 16 * p + cl];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float va = acc[i] * __expf(Lm1 - Lc4[i]) * ik1 * cf4[i];
-        const float vc = acc[i] * __expf(Lm4[i] - Lc1) * ik4[i] * cf1;
-        NA4[i] = ((r0 + i) / BW < cl / BW) ? va : 0.f;
-        NC4[i] = (cl / BW < (r0 + i) / BW) ? vc : 0.f;
-      }
-    }
-    if constexpr (S::SDELTA) {
-      // row-oriented block Jacobi: T (I + N) = I, so T <- (I - T N_o)(I + N_d)^{-1},
-      // exact after 3 sweeps; Y holds T in A-layout (row c, columns 4g..4g+3).
-      // n_ab = N[4g+a][4g+b] sits in lane (g, 4g+a), entry b of NA4.
-      const int src = 16 * g4 + r0;
-      const float n10 = __shfl(NA4[0], src + 1), n20 = __shfl(NA4[0], src + 2), n21 = __shfl(NA4[1], src + 2);
-      const float n30 = __shfl(NA4[0], src + 3), n31 = __shfl(NA4[1], src + 3), n32 = __shfl(NA4[2], src + 3);
-      f4 NoC;   // C-layout of N without its 4x4 diagonal sub-blocks
-#pragma unroll
-      for (int i = 0; i < 4; ++i) NoC[i] = ((cl >> 2) == g4) ? 0.f : NC4[i];
-      f4 Z, Y;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Z[i] = (r0 + i == cl) ? 1.f : 0.f;
-      auto local = [&](const f4 &w) {     // t (I + N_gg) = w, t a row of 4
-        Y[3] = w[3];
-        Y[2] = w[2] - Y[3] * n32;
-        Y[1] = w[1] - Y[2] * n21 - Y[3] * n31;
-        Y[0] = w[0] - Y[1] * n10 - Y[2] * n20 - Y[3] * n30;
-      };
-      local(Z);
-#pragma unroll
-      for (int it = 0; it < 3; ++it) {
-        f4 cpl = zero4();
-        mma16(cpl, NoC, Y);   // fp32: C-layout of N_o^T Y^T = A-layout of Y N_o
-        local(Z - cpl);
-      }
-      *reinterpret_cast<Frag *>(gT + (p * 64 + lane) * 4) = cvt<OpT>(Y);
-    } else {
-      // lane (g, 4g+b) holds N[4g+a][4g+b] in NC4[a]; slots: 10 20 21 30 31 32
-      if ((cl >> 2) == g4) {
-        float *ad = gAd + (p * 4 + g4) * 8;
-        const int bb = cl - r0;
-        if (bb == 0) { ad[0] = NC4[1]; ad[1] = NC4[2]; ad[3] = NC4[3]; }
-        if (bb == 1) { ad[2] = NC4[2]; ad[4] = NC4[3]; }
-        if (bb == 2) ad[5] = NC4[3];
-      }
-      f4 NoA;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) NoA[i] = ((cl >> 2) == g4) ? 0.f : NA4[i];
-      *reinterpret_cast<Frag *>(gT + (p * 64 + lane) * 4) = cvt<OpT>(NoA);
-    }
-  };
-  auto rowfac = [&]() {
-    if (lane < C) {
-      const float L = G[R_LC * C + lane], Lm = G[R_LM * C + lane];
-      gF[F_GAM * C + lane] = __expf(Lm) * G[R_IK * C + lane];
-      gF[F_EL * C + lane] = lane < CSP ? __expf(G[RLQ * C + lane]) * G[R_IQ * C + lane] : 0.f;
-      gF[F_CST * C + lane] = __expf(Llast - L) * G[R_CF * C + lane];
-      gF[F_ETA * C + lane] = G[R_ETA * C + lane];
-      if (lane == 0) gF[F_N * C] = __expf(Llast);
-    }
-  };
-  auto run = [&](auto wc) {
-    constexpr int w = decltype(wc)::value;
-    constexpr JobList J = BW == 1 ? make_jobs(NB, DELTA, w) : make_jobs_win(NB, CS, BW, DELTA, w);
-    constexpr int NJ = J.n > 0 ? J.n : 1;
-    Pr Dop[NA / 2], Aop[NJ][NA / 2], Bop[NJ][NA / 2];
-    if constexpr (J.diag >= 0) rows16(X, J.diag, Dop);
-#pragma unroll
-    for (int j = 0; j < J.n; ++j) {
-      rows16(X, J.q[j], Aop[j]);
-      rows16(J.isP[j] ? Q : X, J.p[j], Bop[j]);
-    }
-    f4 dacc, acc[NJ];
-    if constexpr (J.diag >= 0) dacc = tile(Dop, Dop);
-#pragma unroll
-    for (int j = 0; j < J.n; ++j) acc[j] = tile(Aop[j], Bop[j]);
-    if constexpr (J.diag >= 0) diag(dacc, J.diag);
-#pragma unroll
-    for (int j = 0; j < J.n; ++j) finish(acc[j], J.isP[j], J.p[j], J.q[j]);
-    if constexpr (w == S::NPW - 1) rowfac();
-  };
-  if (pw == 0) run(std::integral_constant<int, 0>());
-  else if (pw == 1) run(std::integral_constant<int, 1>());
-  else if (pw == 2) run(std::integral_constant<int, 2>());
-  else run(std::integral_constant<int, 3>());
+  derive_image<VAR, IT, D, C, BW>(sX, sQ, sR, img, sep, Llast, pw, lane);
 }
 
 // ============================== scan kernel ==============================
-template <int VAR, typename IT, int D, int C, int BW, int NS>
+template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE>
 __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdArgs a, const unsigned char *ws) {
   using S = Split<VAR, IT, D, C, BW>;
-  using Z = Scan<VAR, IT, D, C, BW, NS>;
+  using Z = Scan<VAR, IT, D, C, BW, NS, ONE>;
+  static_assert(Z::NT == 64 * (2 * (D / 16 / NS) + 8), "launch bounds");
   using OpT = IT;
   using Frag = typename Op<OpT>::frag;
   using Pr = Pair<OpT>;
   constexpr int NB = S::NB, NA = S::NA, NCW = Z::NCW, LX = S::LX, VEC = S::VEC, TPR = S::TPR, RPC = Z::RPC;
   constexpr int LXV = Z::LXV, TPV = Z::TPV, RPV = Z::RPV;
-  constexpr int CS = S::CS, CSP = S::CSP, NBS = S::NBS;
+  constexpr int CS = S::CS, CSP = S::CSP, NBS = S::NBS, NXS = Z::NXS, NQS = Z::NQS, NDW = Z::NDW;
   constexpr bool PERCH = S::PERCH, DELTA = S::DELTA;
 
   // Raw operands (dk permuted); the per-row factors are applied to the products,
   // so copy waves only move bytes and take few issue slots from the other waves:
-  __shared__ __attribute__((aligned(16))) OpT sX[2][C * LX];     // key of each virtual row
-  __shared__ __attribute__((aligned(16))) IT sV[2][C * LXV];     // raw v of each virtual row, this workgroup's channels
-  __shared__ __attribute__((aligned(16))) OpT sQ[3][CSP * LX];   // q of each step row
+  __shared__ __attribute__((aligned(16))) OpT sX[NXS][C * LX];     // key of each virtual row
+  __shared__ __attribute__((aligned(16))) IT sV[NXS][C * LXV];     // raw v of each virtual row, this workgroup's channels
+  __shared__ __attribute__((aligned(16))) OpT sQ[NQS][CSP * LX];   // q of each step row
   __shared__ __attribute__((aligned(16))) unsigned char sImg[3][S::IMG];
   // handed from each state wave to its output wave: S at the system's start, E'
   __shared__ Pr sSp[2][NCW][NA / 2][64];
   __shared__ Frag sEb[2][NCW][NB][64];
+  // one-pass: squared norms of key / query rows, clamped log-decays and gains of
+  // the steps (staged with the rows), and each derive wave's per-row arrays
+  __shared__ float sNrm[ONE ? 3 : 1][2][ONE ? C : 1];
+  __shared__ float sGB[ONE ? 3 : 1][2][ONE ? C : 1];
+  __shared__ __attribute__((aligned(16))) float sG[ONE ? NDW : 1][ONE ? Z::RG * C : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g4 = lane >> 4, cl = lane & 15;
@@ -552,17 +587,37 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
   }
   const int b = bh / a.H, h = bh % a.H;
   const int T = a.T, H = a.H, NC = a.nchunks, NSYS = S::nsys(T);
-  const int role = wv < NCW ? 0 : wv < 2 * NCW ? 1 : 2;    // state, output, copy
+  const int role = wv < NCW ? 0 : wv < 2 * NCW ? 1 : wv < 2 * NCW + NDW ? 3 : 2;   // state, output, derive, copy
   const int cw = role == 1 ? wv - NCW : wv;                // channel group of a state / output wave
-  const int ctid = tid - 64 * 2 * NCW;                     // copy thread index
+  const int dw = wv - 2 * NCW;                             // derive wave index
+  const int ctid = tid - 64 * (2 * NCW + NDW);             // copy thread index
   const int chW = Z::DS * sp + 16 * cw + cl;               // the lane's value channel
 
   const IT *qp = static_cast<const IT *>(a.q);
   const IT *kp = static_cast<const IT *>(a.k);
   const IT *vp = static_cast<const IT *>(a.v);
   IT *op = static_cast<IT *>(a.o);
-  const unsigned char *wsq = ws + (size_t)bh * NSYS * S::IMG;
-  const float *carry = reinterpret_cast<const float *>(ws + (size_t)a.B * H * NSYS * S::IMG + (size_t)bh * S::CARRY);
+  const unsigned char *wsq = ONE ? nullptr : ws + (size_t)bh * NSYS * S::IMG;
+  const float *carry =
+      ONE ? nullptr : reinterpret_cast<const float *>(ws + (size_t)a.B * H * NSYS * S::IMG + (size_t)bh * S::CARRY);
+  // carried features / window values: the prep kernel's copy (two-kernel form) or the
+  // caller's incoming state (one-pass form; then the outgoing state is written by the
+  // tail kernel when it may alias and other workgroups read it)
+  auto carried_key = [&](int j, int e) -> float {   // element e of the key of pair j <= 0
+    if constexpr (ONE) {
+      const float *src = j == 0 ? a.xprev0 : a.winx0;
+      return src ? src[(j == 0 ? (size_t)bh : (size_t)bh * (BW - 1) + j + BW - 1) * D + e] : 0.f;
+    } else {
+      return carry[(j == 0 ? 0 : (j + BW) * D) + e];
+    }
+  };
+  auto carried_val = [&](int j, int ch) -> float {  // channel ch of the value of pair j < 0
+    if constexpr (ONE) {
+      return a.winv0 ? a.winv0[((size_t)bh * (BW - 1) + j + BW - 1) * D + ch] : 0.f;
+    } else {
+      return carry[(j + 2 * BW - 1) * D + ch];
+    }
+  };
   // step and pair index of virtual row r of the system starting at step c0
   auto step_of = [](int c0, int r) { return c0 + r / BW; };
   auto pair_of = [](int c0, int r) { return BW == 1 ? c0 + r : c0 + r / BW - BW + 1 + r % BW; };
@@ -572,6 +627,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
   // so a load has two scan iterations to arrive.
   struct Regs {
     uint4 k[Z::NPK], q[Z::NPK], v[Z::NPV], img[Z::NPI];
+    float g, bt;   // one-pass: log-decay and gain of step ctid
   };
   Regs reg[2];
   auto prefetch = [&](int c, Regs &R) __attribute__((always_inline)) {    // global -> registers, system c (rows clamped in bounds)
@@ -589,12 +645,18 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
       R.k[ps] = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tk) * H + h) * D + part * VEC);
       R.q[ps] = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tq) * H + h) * D + part * VEC);
     }
-    const uint4 *src = reinterpret_cast<const uint4 *>(wsq + (size_t)c * S::IMG);
+    if constexpr (ONE) {
+      const int t = min(c0 + min(ctid, CSP - 1), T - 1);
+      R.g = a.g[(size_t)(b * T + t) * H + h];
+      R.bt = PERCH ? 0.f : a.beta[(size_t)(b * T + t) * H + h];
+    } else {
+      const uint4 *src = reinterpret_cast<const uint4 *>(wsq + (size_t)c * S::IMG);
 #pragma unroll
-    for (int j = 0; j < Z::NPI; ++j) R.img[j] = src[min(ctid + j * Z::NST, S::NU - 1)];
+      for (int j = 0; j < Z::NPI; ++j) R.img[j] = src[min(ctid + j * Z::NST, S::NU - 1)];
+    }
   };
   auto stage = [&](int c, const Regs &R) __attribute__((always_inline)) { // registers -> LDS slots of system c
-    const int s2 = c & 1, s3 = c % 3, c0 = c * CS;
+    const int s2 = c % NXS, s3 = c % NQS, si = c % 3, c0 = c * CS;
 #pragma unroll
     for (int ps = 0; ps < Z::NPV; ++ps) {
       const int r = ps * RPV + ctid / TPV, part = ctid % TPV;
@@ -605,7 +667,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
         if (BW > 1 && live && j < 0) {   // a carried window value (fp32)
           float vf[VEC];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) vf[e] = carry[(j + 2 * BW - 1) * D + Z::DS * sp + part * VEC + e];
+          for (int e = 0; e < VEC; ++e) vf[e] = carried_val(j, Z::DS * sp + part * VEC + e);
           vv = scale_pack<IT, VEC>(vf, 1.f);
         }
         *reinterpret_cast<uint4 *>(sV[s2] + r * LXV + part * VEC) = vv;
@@ -618,21 +680,53 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
         const int j = pair_of(c0, r);
         const bool live = step_of(c0, r) < T;
         uint4 kk = keep_or_zero(live && j >= 1, R.k[ps]);
+        float sk = 0.f;   // one-pass: squared norm of the row, for the derive waves
         if (live && j <= 0) {   // a carried feature (fp32, normalised): x_prev, or window key j
-          const float *src = carry + (j == 0 ? 0 : (j + BW) * D) + part * VEC;
           float xv[VEC];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) xv[e] = src[e];
+          for (int e = 0; e < VEC; ++e) xv[e] = carried_key(j, part * VEC + e);
           kk = scale_pack<OpT, VEC>(xv, 1.f);
+          if constexpr (ONE) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) sk += xv[e] * xv[e];
+          }
+        } else if constexpr (ONE) {
+          float xv[VEC];
+          unpack(kk, IT(), xv);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) sk += xv[e] * xv[e];
         }
         put_perm(sX[s2] + r * LX, part * VEC, kk);
-        if (r < CSP) put_perm(sQ[s3] + r * LX, part * VEC, keep_or_zero(r < CS && c0 + r < T, R.q[ps]));
+        if constexpr (ONE) {
+          sk = group_sum<TPR>(sk);
+          if (ctid % TPR == 0) sNrm[si][0][r] = sk;
+        }
+        if (r < CSP) {
+          const uint4 qq = keep_or_zero(r < CS && c0 + r < T, R.q[ps]);
+          put_perm(sQ[s3] + r * LX, part * VEC, qq);
+          if constexpr (ONE) {
+            float qv[VEC], sq = 0.f;
+            unpack(qq, IT(), qv);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) sq += qv[e] * qv[e];
+            sq = group_sum<TPR>(sq);
+            if (ctid % TPR == 0) sNrm[si][1][r] = sq;
+          }
+        }
       }
     }
+    if constexpr (ONE) {
+      if (ctid < CSP) {   // steps past the system or the sequence decay and write nothing
+        const bool ok = ctid < CS && c0 + ctid < T;
+        sGB[si][0][ctid] = ok ? fmaxf(R.g, a.log_eps_gamma) : 0.f;
+        sGB[si][1][ctid] = ok ? R.bt : 0.f;
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < Z::NPI; ++j) {
-      const int u = ctid + j * Z::NST;
-      if (u < S::NU) *reinterpret_cast<uint4 *>(sImg[s3] + 16 * u) = R.img[j];
+      for (int j = 0; j < Z::NPI; ++j) {
+        const int u = ctid + j * Z::NST;
+        if (u < S::NU) *reinterpret_cast<uint4 *>(sImg[si] + 16 * u) = R.img[j];
+      }
     }
   };
 
@@ -657,8 +751,8 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
 
   auto consume = [&](int c) __attribute__((always_inline)) {
     const int s2 = c & 1, s3 = c % 3;
-    const OpT *X = sX[s2];
-    const IT *V = sV[s2];
+    const OpT *X = sX[c % NXS];
+    const IT *V = sV[c % NXS];
     const float *F = reinterpret_cast<const float *>(sImg[s3] + S::OFF_F);
     const OpT *Ao = reinterpret_cast<const OpT *>(sImg[s3] + S::OFF_A);
     const OpT *Tb = reinterpret_cast<const OpT *>(sImg[s3] + S::OFF_T);
@@ -769,7 +863,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
   // of the second.  Lane (g, c) ends with channels 16w+4g..16w+4g+3 of step 16p+c.
   auto output = [&](int c) __attribute__((always_inline)) {
     const int s2 = c & 1, s3 = c % 3, c0 = c * CS;
-    const OpT *Q = sQ[s3];
+    const OpT *Q = sQ[c % NQS];
     const float *F = reinterpret_cast<const float *>(sImg[s3] + S::OFF_F);
     const OpT *Pm = reinterpret_cast<const OpT *>(sImg[s3] + S::OFF_P);
     Pr Sp[NA / 2];
@@ -794,13 +888,81 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
     }
   };
 
+  // ================= derive waves (one-pass form) =================
+  // Per-row arrays of system c from the staged norms and gates (lane = row; each
+  // derive wave keeps its own copy), then the wave's share of the image tiles.
+  auto derive = [&](int c) __attribute__((always_inline)) {
+    const int si = c % 3, c0 = c * CS;
+    float *G = sG[ONE ? dw : 0];
+    const float *nk = sNrm[si][0], *nq = sNrm[si][1], *gg = sGB[si][0], *gb = sGB[si][1];
+    const float g2 = lane < CSP ? gg[lane] : 0.f;     // lane = step
+    const float L = wave_inclusive_scan(g2);
+    const float Llast = __shfl(L, CS - 1);
+    const bool sep = Llast >= -160.f;
+    const float Lref = 0.5f * Llast;
+    if (lane >= C) {
+      // rows past the system: no per-row entries
+    } else if constexpr (BW == 1) {   // lane = row = step
+      const bool carried = c0 + lane == 0;
+      const float sk = nk[lane], sq = nq[lane];
+      const float ik = carried ? 1.f : safe_rsqrt(sk + a.eps_phi);
+      const float iq = safe_rsqrt(sq + a.eps_phi);
+      const float inv = fast_rcp(a.eps_eta + sk * ik * ik);
+      const float eta = PERCH ? inv : gb[lane] * inv;
+      const float cf = PERCH ? ik : ik * eta;
+      G[R_LC * C + lane] = L;
+      G[R_LM * C + lane] = L - g2;
+      G[R_IK * C + lane] = ik;
+      G[R_IQ * C + lane] = iq;
+      G[R_CF * C + lane] = cf;
+      G[R_ETA * C + lane] = eta;
+      if (sep) {
+        G[R_EP * C + lane] = __expf(L - Lref) * iq;
+        G[R_EA * C + lane] = __expf(L - g2 - Lref) * ik;
+        G[R_EC * C + lane] = __expf(Lref - L) * cf;
+      }
+    } else {   // lane = virtual row r (step r / BW); step values come from lane = step
+      const int st = lane / BW, j = c0 + st - BW + 1 + lane % BW;
+      const float sk = nk[lane];
+      const float ik = j <= 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
+      const float e2 = sk * ik * ik;
+      const float e2new = __shfl(e2, st * BW + BW - 1);   // the step's own (newest) pair
+      const float bq = lane < CSP ? gb[lane] : 0.f;
+      const float Ls = __shfl(L, st), gs = __shfl(g2, st), bs = __shfl(bq, st);
+      const float w = bs * fast_rcp(a.eps_eta + e2new) * (1.f / BW);
+      const float cf = ik * w;
+      G[R_LC * C + lane] = Ls;
+      G[R_LM * C + lane] = Ls - gs;
+      G[R_IK * C + lane] = ik;
+      G[R_CF * C + lane] = cf;
+      G[R_ETA * C + lane] = w;
+      if (sep) {
+        G[R_EA * C + lane] = __expf(Ls - gs - Lref) * ik;
+        G[R_EC * C + lane] = __expf(Lref - Ls) * cf;
+      }
+      if (lane < CSP) {
+        const float iq = (lane < CS && c0 + lane < T) ? safe_rsqrt(nq[lane] + a.eps_phi) : 0.f;
+        G[R_IQ * C + lane] = iq;
+        G[R_LQ * C + lane] = L;
+        G[R_GQ * C + lane] = g2;
+        if (sep) G[R_EP * C + lane] = __expf(L - Lref) * iq;
+      }
+    }
+    wave_lds_sync();
+    derive_image<VAR, IT, D, C, BW>(sX[c % NXS], sQ[c % NQS], G, sImg[si], sep, Llast, dw, lane);
+  };
+
   // ---------------- scan: iteration i works on system i (state), i-1 (outputs), i+1 (staging) ----------------
   // Each role runs its own loop, so none keeps another's loop-carried registers
   // live; all pass the same number of workgroup barriers (a prologue barrier,
   // then one per iteration, NSYS + 1 iterations), which is what the barrier counts.
+  // One-pass form: iteration k = -1..NSYS stages system k+2, derives k+1, runs the
+  // state of k and the outputs of k-1, so every role passes NSYS + 3 barriers.
+  constexpr int PRE = ONE ? 1 : 0;   // pipeline stages ahead of the state waves
   if (role == 0) {
     if (PERCH) prefetch_beta(0);
     __syncthreads();
+    if (ONE) __syncthreads();
     for (int i = 0; i < NSYS; ++i) {
       consume(i);
       if (PERCH && i + 1 < NSYS) prefetch_beta(i + 1);
@@ -814,11 +976,20 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
     }
   } else if (role == 1) {
     __syncthreads();
+    if (ONE) __syncthreads();
     __syncthreads();
     for (int i = 1; i <= NSYS; ++i) {
       output(i - 1);
       __syncthreads();
     }
+  } else if (role == 3) {
+    __syncthreads();
+    for (int i = -1; i < NSYS - 1; ++i) {
+      derive(i + 1);
+      __syncthreads();
+    }
+    __syncthreads();
+    __syncthreads();
   } else {
     prefetch(0, reg[0]);
     if (NSYS > 1) prefetch(1, reg[1]);
@@ -826,14 +997,14 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
     if (NSYS > 2) prefetch(2, reg[0]);
     __syncthreads();
     // the register sets are indexed with compile-time parity: two iterations per trip;
-    // Rnext holds system i+1 and is refilled with system i+3
+    // Rnext holds system i+1+PRE and is refilled with system i+3+PRE
     auto copy_step = [&](int i, Regs &Rnext) __attribute__((always_inline)) {
-      if (i + 1 < NSYS) {
-        stage(i + 1, Rnext);
-        if (i + 3 < NSYS) prefetch(i + 3, Rnext);
+      if (i + 1 + PRE < NSYS) {
+        stage(i + 1 + PRE, Rnext);
+        if (i + 3 + PRE < NSYS) prefetch(i + 3 + PRE, Rnext);
       }
     };
-    for (int i = 0; i < NSYS; i += 2) {
+    for (int i = -PRE; i < NSYS; i += 2) {
       copy_step(i, reg[1]);
       __syncthreads();
       if (i + 1 < NSYS) {
@@ -845,7 +1016,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
     if (a.write_tail) {
       // outgoing x_prev = phi(k_{T-1}) and, for windows, the last Bw-1 pairs
       // j = T-Bw+1..T-1 (keys phi(k_{j-1}), values v_j; carried ones for j <= 0)
-      const int w8 = wv - 2 * NCW;
+      const int w8 = wv - 2 * NCW - NDW;
       auto key_row = [&](int j, float *dst) {   // normalised key of pair j into dst[0..D)
         float xv[2] = {0.f, 0.f};
         if (j >= 1) {
@@ -858,11 +1029,10 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
           xv[0] *= inv;
           xv[1] *= inv;
         } else {
-          const float *src = carry + (j == 0 ? 0 : (j + BW) * D);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             const int e = lane + 64 * m;
-            if (e < D) xv[m] = src[e];
+            if (e < D) xv[m] = carried_key(j, e);
           }
         }
 #pragma unroll
@@ -871,16 +1041,18 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
           if (e < D) dst[e] = xv[m];
         }
       };
-      if (w8 == BW - 1) {
-        if (sp == 0 && a.xprev_out) key_row(T, a.xprev_out + (size_t)bh * D);
-      } else if (BW > 1 && w8 < BW - 1) {
-        const int j = T - BW + 1 + w8;
-        if (sp == 0 && a.winx_out) key_row(j, a.winx_out + ((size_t)bh * (BW - 1) + w8) * D);
-        if (a.winv_out) {
-          for (int e = lane; e < Z::DS; e += 64) {
-            const int ch = Z::DS * sp + e;
-            a.winv_out[((size_t)bh * (BW - 1) + w8) * D + ch] =
-                j >= 0 ? to_f(vp[((size_t)(b * T + j) * H + h) * D + ch]) : carry[(j + 2 * BW - 1) * D + ch];
+      for (int u = w8; u < BW; u += Z::NSW) {   // window pairs 0..BW-2, then x_prev
+        if (u == BW - 1) {
+          if (sp == 0 && a.xprev_out) key_row(T, a.xprev_out + (size_t)bh * D);
+        } else {
+          const int j = T - BW + 1 + u;
+          if (sp == 0 && a.winx_out) key_row(j, a.winx_out + ((size_t)bh * (BW - 1) + u) * D);
+          if (a.winv_out) {
+            for (int e = lane; e < Z::DS; e += 64) {
+              const int ch = Z::DS * sp + e;
+              a.winv_out[((size_t)bh * (BW - 1) + u) * D + ch] =
+                  j >= 0 ? to_f(vp[((size_t)(b * T + j) * H + h) * D + ch]) : carried_val(j, ch);
+            }
           }
         }
       }
@@ -895,15 +1067,15 @@ constexpr bool ns_built(int ns) {
   if (sizeof(IT) == 4) return ns == 1;
   return D <= 64 ? (ns == 1 || ns == 2) : (ns == 2 || ns == 4 || ns == 8);
 }
-template <int VAR, typename IT, int D, int C, int BW, int NS>
-constexpr bool scan_ok() { return ns_built<IT, D>(NS) && Scan<VAR, IT, D, C, BW, NS>::fits(); }
+template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false>
+constexpr bool scan_ok() { return ns_built<IT, D>(NS) && Scan<VAR, IT, D, C, BW, NS, ONE>::fits(); }
 
 // Smallest built split that fits and gives at least 128 scan workgroups (else
 // the largest that fits); 0 when none fits.
-template <int VAR, typename IT, int D, int C, int BW>
+template <int VAR, typename IT, int D, int C, int BW, bool ONE = false>
 int pick_ns(int bh) {
-  const bool ok[4] = {scan_ok<VAR, IT, D, C, BW, 1>(), scan_ok<VAR, IT, D, C, BW, 2>(),
-                      scan_ok<VAR, IT, D, C, BW, 4>(), scan_ok<VAR, IT, D, C, BW, 8>()};
+  const bool ok[4] = {scan_ok<VAR, IT, D, C, BW, 1, ONE>(), scan_ok<VAR, IT, D, C, BW, 2, ONE>(),
+                      scan_ok<VAR, IT, D, C, BW, 4, ONE>(), scan_ok<VAR, IT, D, C, BW, 8, ONE>()};
   int best = 0;
   for (int i = 0; i < 4; ++i) {
     if (!ok[i]) continue;
@@ -913,15 +1085,27 @@ int pick_ns(int bh) {
   return best;
 }
 
-template <int VAR, typename IT, int D, int C, int BW, int NS>
+template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false>
 hipError_t launch_scan(const FwdArgs &a, const unsigned char *w, hipStream_t st) {
-  if constexpr (scan_ok<VAR, IT, D, C, BW, NS>()) {
-    hipLaunchKernelGGL((chunk_scan<VAR, IT, D, C, BW, NS>), dim3(a.B * a.H * NS),
-                       dim3(Scan<VAR, IT, D, C, BW, NS>::NT), 0, st, a, w);
+  if constexpr (scan_ok<VAR, IT, D, C, BW, NS, ONE>()) {
+    hipLaunchKernelGGL((chunk_scan<VAR, IT, D, C, BW, NS, ONE>), dim3(a.B * a.H * NS),
+                       dim3(Scan<VAR, IT, D, C, BW, NS, ONE>::NT), 0, st, a, w);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
   }
+}
+
+// One-pass form: a single launch, no workspace.
+template <int VAR, typename IT, int D, int C, int BW>
+hipError_t launch_onepass(const FwdArgs &a, hipStream_t st) {
+  switch (pick_ns<VAR, IT, D, C, BW, true>(a.B * a.H)) {
+    case 1: return launch_scan<VAR, IT, D, C, BW, 1, true>(a, nullptr, st);
+    case 2: return launch_scan<VAR, IT, D, C, BW, 2, true>(a, nullptr, st);
+    case 4: return launch_scan<VAR, IT, D, C, BW, 4, true>(a, nullptr, st);
+    case 8: return launch_scan<VAR, IT, D, C, BW, 8, true>(a, nullptr, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int VAR, typename IT, int D, int C, int BW>

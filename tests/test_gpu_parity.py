@@ -201,6 +201,70 @@ def test_full_size_sampled(name, variant):
     assert np.all(np.isfinite(g["o"]))
 
 
+# ---- one-pass kernel (calls without a workspace) ------------------------------------
+# One launch per call: derive waves build each system's Gram / score blocks in LDS
+# one system ahead of the state waves.  Shapes reach both channel splits it builds
+# (d = 32: 1 or 2 slices; d = 64: 2) and both workgroup mappings, with windows.
+ONEPASS_SHAPES = [
+    (32, 8, 16, 130, 1),     # B*H = 128: one slice
+    (32, 1, 5, 130, 1),      # two slices, plain mapping
+    (64, 4, 8, 130, 1),      # two slices, XCD-grouped
+    (64, 1, 3, 70, 4),       # window of 4
+    (64, 2, 4, 70, 8),       # window of 8
+    (32, 1, 2, 33, 2),       # window of 2, short
+]
+
+
+ONEPASS_CASES = [(v, *shape) for shape in ONEPASS_SHAPES
+                 for v in (("F3", "F3A") if shape[-1] > 1 else ("F1", "F1A", "F2", "F2A", "F3", "F3A"))]
+
+
+@pytest.mark.parametrize("variant,d,B,H,T,bw", ONEPASS_CASES)
+def test_onepass_shapes(variant, d, B, H, T, bw):
+    w = W.WORKLOADS["layer130m"].replace(batch=B, heads=H, seqlen=T, dk=d, dv=d)
+    check(variant, w, 71, window=bw, init=True, chunk_states=True, workspace=False)
+
+
+@pytest.mark.parametrize("variant,bw", [("F1", 1), ("F2", 1), ("F1A", 1), ("F3", 4), ("F3A", 8)])
+def test_onepass_continuation_in_place(variant, bw):
+    """Calls continuing in place without a workspace: with two channel slices per
+    sequence the outgoing x_prev / window goes through the tail kernel."""
+    import torch
+    from recurrent_sequence_models_amd import chunk_fwd, new_state
+    w = W.WORKLOADS["layer130m"].replace(batch=2, heads=2, seqlen=300)
+    inp = W.make_inputs(w, variant, seed=72)
+    d = to_dev(inp, "bf16")
+    st = new_state(2, 2, 64, 64, window=bw)
+    outs = []
+    for sl in (slice(0, 5), slice(5, 141), slice(141, 300)):
+        o, _, _ = chunk_fwd(variant, *(d[n][:, sl].contiguous() for n in ("q", "k", "v", "beta", "log_lambda")),
+                            window=bw, init=st, final=st, workspace=False)
+        outs.append(to_np(o))
+    torch.cuda.synchronize()
+    r = oracle.recurrent(variant, **inp, window=bw)
+    assert rel_l2(np.concatenate(outs, axis=1), r["o"]) <= TOL["bf16"]
+    names = ("S", "x_prev", "win_x", "win_v") if bw > 1 else ("S", "x_prev")
+    for n in names:
+        assert rel_l2(to_np(st[n]), r[n]) <= TOL["bf16"], n
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+def test_onepass_full_size_sampled(variant):
+    """The full 130M-layer workloads through the one-pass kernel (the benchmark's
+    default path for them); the oracle checks a sample of sequences."""
+    w = W.WORKLOADS["layer130m_f2" if variant in ("F2", "F2A") else "layer130m"]
+    inp = W.make_inputs(w, variant, seed=w.seed)
+    g = run_gpu(variant, inp, w.dtype, w.chunk, workspace=False)
+    seqs = [(0, 0), (5, 9)]
+    refs = oracle_subset(variant, inp, seqs)
+    for (b, h), r in zip(seqs, refs):
+        eo = rel_l2(g["o"][b, :, h], r["o"][0, :, 0])
+        es = rel_l2(g["S"][b, h], r["S"][0, 0])
+        print(variant, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    assert np.all(np.isfinite(g["o"]))
+
+
 # ---- Falcon-3 / 3A: window of Bw pairs --------------------------------------------
 WIN_CASES = [("F3", 2), ("F3", 4), ("F3", 8), ("F3A", 2), ("F3A", 4), ("F3A", 8), ("F3", 1), ("F3A", 1)]
 
