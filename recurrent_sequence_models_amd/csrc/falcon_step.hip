@@ -86,12 +86,27 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     }
   }
 
-  for (int row0 = 0; row0 < DV; row0 += 4 * RPW) {
-    const int row = row0 + wv * RPW + rsub;
+  // All of this workgroup's state rows are read up front (one 16-byte vector per
+  // lane and pass), so every load of the stream is in flight at once; then each
+  // pass reduces, updates and writes its rows.
+  constexpr int NP = (DV + 4 * RPW - 1) / (4 * RPW);   // passes of 4 waves x RPW rows
+  f4 srow[NP];
+  float vrow[NP], brow[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int row = p * 4 * RPW + wv * RPW + rsub;
     const bool ok = row < DV;  // uniform per row group
-    f4 s = ok ? *reinterpret_cast<const f4 *>(a.S + ((size_t)bh * DV + row) * DK + 4 * part) : zero4();
-    const float vi = ok ? ld1(vp + (size_t)bh * DV + row) : 0.f;
-    const float eta = PERCH ? (ok ? a.beta[(size_t)bh * DV + row] * inv_e : 0.f) : etas;
+    srow[p] = ok ? *reinterpret_cast<const f4 *>(a.S + ((size_t)bh * DV + row) * DK + 4 * part) : zero4();
+    vrow[p] = ok ? ld1(vp + (size_t)bh * DV + row) : 0.f;
+    brow[p] = (PERCH && ok) ? a.beta[(size_t)bh * DV + row] : 0.f;
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int row = p * 4 * RPW + wv * RPW + rsub;
+    const bool ok = row < DV;
+    const f4 s = srow[p];
+    const float vi = vrow[p];
+    const float eta = PERCH ? brow[p] * inv_e : etas;
     const float sq = row_sum<LPR>(dot4(s, qh));
     float o;
     f4 snew = s * lam;
