@@ -183,6 +183,21 @@ __device__ __forceinline__ uint4 pack_feature(const float *x, float &ss) {
   return *reinterpret_cast<const uint4 *>(tmp);
 }
 
+// sum of squares of one 16-byte vector of raw inputs (bf16: paired dot products)
+__device__ __forceinline__ float sumsq(const uint4 &u, __bf16) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  float s = 0.f;
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), __builtin_bit_cast(bf2, u.x), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), __builtin_bit_cast(bf2, u.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), __builtin_bit_cast(bf2, u.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), __builtin_bit_cast(bf2, u.w), s, false);
+  return s;
+}
+__device__ __forceinline__ float sumsq(const uint4 &u, float) {
+  const float a = __uint_as_float(u.x), b = __uint_as_float(u.y), c = __uint_as_float(u.z), d = __uint_as_float(u.w);
+  return a * a + b * b + c * c + d * d;
+}
+
 // VEC raw values scaled by f, in the operand type (one 16-byte vector)
 template <typename OpT, int VEC>
 __device__ __forceinline__ uint4 scale_pack(const float *x, float f) {
@@ -630,8 +645,37 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
     float g, bt;   // one-pass: log-decay and gain of step ctid
   };
   Regs reg[2];
+  // A system is "interior" when every row's pair index is >= 1 and every step is
+  // inside the sequence: its rows are then plain strided reads, with no clamps,
+  // masks or carried features.
+  auto interior = [&](int c) { return c * CS >= BW && (c + 1) * CS <= T; };
+  const long long rstride = (long long)H * D;   // elements between consecutive tokens
   auto prefetch = [&](int c, Regs &R) __attribute__((always_inline)) {    // global -> registers, system c (rows clamped in bounds)
     const int c0 = c * CS;
+    if (interior(c)) {
+      const long long base = ((long long)b * T + c0) * rstride + (long long)h * D;   // token c0 of the sequence
+#pragma unroll
+      for (int ps = 0; ps < Z::NPV; ++ps) {
+        const int r = min(ps * RPV + ctid / TPV, C - 1), part = ctid % TPV;
+        R.v[ps] = *reinterpret_cast<const uint4 *>(vp + base + pair_of(0, r) * rstride + Z::DS * sp + part * VEC);
+      }
+#pragma unroll
+      for (int ps = 0; ps < Z::NPK; ++ps) {
+        const int r = min(ps * RPC + ctid / TPR, C - 1), part = ctid % TPR;
+        R.k[ps] = *reinterpret_cast<const uint4 *>(kp + base + (pair_of(0, r) - 1) * rstride + part * VEC);
+        R.q[ps] = *reinterpret_cast<const uint4 *>(qp + base + min(r, CS - 1) * rstride + part * VEC);
+      }
+      if constexpr (ONE) {
+        const size_t gi = ((size_t)b * T + c0 + min(ctid, CS - 1)) * H + h;
+        R.g = a.g[gi];
+        R.bt = PERCH ? 0.f : a.beta[gi];
+      } else {
+        const uint4 *src = reinterpret_cast<const uint4 *>(wsq + (size_t)c * S::IMG);
+#pragma unroll
+        for (int j = 0; j < Z::NPI; ++j) R.img[j] = src[min(ctid + j * Z::NST, S::NU - 1)];
+      }
+      return;
+    }
 #pragma unroll
     for (int ps = 0; ps < Z::NPV; ++ps) {
       const int r = min(ps * RPV + ctid / TPV, C - 1), part = ctid % TPV;
@@ -657,6 +701,46 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
   };
   auto stage = [&](int c, const Regs &R) __attribute__((always_inline)) { // registers -> LDS slots of system c
     const int s2 = c % NXS, s3 = c % NQS, si = c % 3, c0 = c * CS;
+    if (interior(c)) {
+#pragma unroll
+      for (int ps = 0; ps < Z::NPV; ++ps) {
+        const int r = ps * RPV + ctid / TPV, part = ctid % TPV;
+        if (r < C) *reinterpret_cast<uint4 *>(sV[s2] + r * LXV + part * VEC) = R.v[ps];
+      }
+#pragma unroll
+      for (int ps = 0; ps < Z::NPK; ++ps) {
+        const int r = ps * RPC + ctid / TPR, part = ctid % TPR;
+        if (r < C) {
+          put_perm(sX[s2] + r * LX, part * VEC, R.k[ps]);
+          if constexpr (ONE) {
+            const float sk = group_sum<TPR>(sumsq(R.k[ps], IT()));
+            if (part == 0) sNrm[si][0][r] = sk;
+          }
+          if (r < CSP) {
+            const uint4 qq = CSP > CS ? keep_or_zero(r < CS, R.q[ps]) : R.q[ps];
+            put_perm(sQ[s3] + r * LX, part * VEC, qq);
+            if constexpr (ONE) {
+              const float sq = group_sum<TPR>(sumsq(qq, IT()));
+              if (part == 0) sNrm[si][1][r] = sq;
+            }
+          }
+        }
+      }
+      if constexpr (ONE) {
+        if (ctid < CSP) {
+          const bool ok = ctid < CS;
+          sGB[si][0][ctid] = ok ? fmaxf(R.g, a.log_eps_gamma) : 0.f;
+          sGB[si][1][ctid] = ok ? R.bt : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < Z::NPI; ++j) {
+          const int u = ctid + j * Z::NST;
+          if (u < S::NU) *reinterpret_cast<uint4 *>(sImg[si] + 16 * u) = R.img[j];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int ps = 0; ps < Z::NPV; ++ps) {
       const int r = ps * RPV + ctid / TPV, part = ctid % TPV;
@@ -691,10 +775,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
             for (int e = 0; e < VEC; ++e) sk += xv[e] * xv[e];
           }
         } else if constexpr (ONE) {
-          float xv[VEC];
-          unpack(kk, IT(), xv);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) sk += xv[e] * xv[e];
+          sk = sumsq(kk, IT());
         }
         put_perm(sX[s2] + r * LX, part * VEC, kk);
         if constexpr (ONE) {
@@ -705,11 +786,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
           const uint4 qq = keep_or_zero(r < CS && c0 + r < T, R.q[ps]);
           put_perm(sQ[s3] + r * LX, part * VEC, qq);
           if constexpr (ONE) {
-            float qv[VEC], sq = 0.f;
-            unpack(qq, IT(), qv);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) sq += qv[e] * qv[e];
-            sq = group_sum<TPR>(sq);
+            const float sq = group_sum<TPR>(sumsq(qq, IT()));
             if (ctid % TPR == 0) sNrm[si][1][r] = sq;
           }
         }
