@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FALCON_ABI_VERSION 1
+#define FALCON_ABI_VERSION 2
 
 typedef enum {
   FALCON_1 = 1,   /* scalar NLMS step, residual write            */
@@ -74,6 +74,15 @@ typedef enum {
 } falcon_variant_t;
 
 typedef enum { FALCON_F32 = 0, FALCON_BF16 = 1 } falcon_dtype_t;  /* of q, k, v, o */
+
+/* Which key the pair written at step t carries ([P1] 本质; [P2] 一个被忽略的时间差):
+ * the prefix pair (phi(k_{t-1}), v_t), the method's alignment, or the same-step
+ * pair (phi(k_t), v_t) the pages contrast it with.  Same-step calls do not read
+ * the carried x_prev (they still write x_prev = phi(k_T)); window pairs are
+ * (phi(k_j), v_j).  Same-step runs on the chunk-parallel kernels (with or without
+ * a workspace where they are built) and on the decode step; other shapes return
+ * FALCON_ERR_UNSUPPORTED. */
+typedef enum { FALCON_ALIGN_PREFIX = 0, FALCON_ALIGN_SAME = 1 } falcon_align_t;
 
 typedef enum {
   FALCON_OK = 0,
@@ -96,6 +105,7 @@ typedef struct {
   float eps_gamma;   /* decay floor, in (0, 1]; the pages' workloads use 1e-3 */
   float eps_phi;     /* feature-map epsilon, >= 0 (1e-6) */
   float eps_eta;     /* NLMS epsilon, >= 0 (1e-6) */
+  int32_t align;     /* falcon_align_t */
 } falcon_shape_t;
 
 typedef struct {

@@ -23,6 +23,10 @@ What is computed (page keys [P1] [P2] [P3] are defined in ``oracle/__init__``):
 * Positive-decay clamp -- [P1] 三种等价形式, [P2] 正衰减钳制:
   lam_t = max(exp(g_t), eps_gamma) for the input log-decay g_t.
 * Read -- o_t = S_t phi(q_t) (read after write), phi(a) = a / sqrt(|a|^2 + eps_phi).
+* Same-step alignment (``align="same"``) -- the contrast the pages draw against
+  prefix alignment ([P1] 本质, [P2] 一个被忽略的时间差): the pair written at step t
+  is (phi(k_t), v_t), i.e. x_t = phi(k_t); the carried x_prev is not read, and
+  window pairs are (phi(k_j), v_j).  The outgoing x_prev is phi(k_T) either way.
 
 Readings where the pages are silent (also listed in the design notes):
   R3 x_1 = 0 for a fresh sequence (o_1 = 0); a continued sequence passes x_prev.
@@ -55,7 +59,12 @@ def phi(a, eps_phi=1e-6):
     return a / np.sqrt(np.sum(a * a, axis=-1, keepdims=True) + eps_phi)
 
 
-def _check(variant, window):
+ALIGNS = ("prefix", "same")
+
+
+def _check(variant, window, align="prefix"):
+    if align not in ALIGNS:
+        raise ValueError(f"unknown alignment {align!r}")
     if variant not in VARIANTS:
         raise ValueError(f"unknown variant {variant!r}")
     if window < 1:
@@ -128,12 +137,12 @@ def _step(variant, window, S, x, v, beta, g, qh, wx, wv, eps_gamma, eps_eta):
 
 
 def recurrent(variant, q, k, v, beta, log_lambda, *, window=1, state=None,
-              eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, return_states=False):
+              eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, return_states=False, align="prefix"):
     """Recurrent form, one step at a time ([P1] 三种等价形式 form A; [P2] 三种视角).
 
     Returns dict(o [B,T,H,dv], S, x_prev, win_x, win_v) and, if requested,
     ``states`` [B,T,H,dv,dk] = S_t after every step."""
-    _check(variant, window)
+    _check(variant, window, align)
     q = np.asarray(q)
     B, T, H, dk = q.shape
     dv = np.asarray(v).shape[-1]
@@ -144,7 +153,7 @@ def recurrent(variant, q, k, v, beta, log_lambda, *, window=1, state=None,
     O = np.zeros((N, T, dv))
     states = np.zeros((N, T, dv, dk)) if return_states else None
     for t in range(T):
-        x = xp
+        x = xp if align == "prefix" else phi(K[:, t], eps_phi)
         S, O[:, t] = _step(variant, window, S, x, V[:, t], Bt[:, t], G[:, t],
                            phi(Q[:, t], eps_phi), wx, wv, eps_gamma, eps_eta)
         if states is not None:
@@ -163,14 +172,14 @@ def recurrent(variant, q, k, v, beta, log_lambda, *, window=1, state=None,
 
 
 def decode_step(variant, q, k, v, beta, log_lambda, state, *, window=1,
-                eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6):
+                eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix"):
     """One token of the recurrent form for a batch of sequences.
 
     q, k [B,H,dk], v [B,H,dv], beta [B,H] or [B,H,dv], log_lambda [B,H];
     ``state`` holds S, x_prev (and the window for F3/F3A).  Returns o [B,H,dv]
     and the new state (x_prev becomes phi(k))."""
     ins = [np.asarray(a)[:, None] for a in (q, k, v, beta, log_lambda)]
-    r = recurrent(variant, *ins, window=window, state=state, eps_gamma=eps_gamma,
+    r = recurrent(variant, *ins, window=window, state=state, eps_gamma=eps_gamma, align=align,
                   eps_phi=eps_phi, eps_eta=eps_eta)
     r["o"] = r["o"][:, 0]
     return r
@@ -239,9 +248,9 @@ def _masked_parallel_one(variant, window, Qh, X, V, beta, g, S0, wx, wv,
 
 
 def masked_parallel(variant, q, k, v, beta, log_lambda, *, window=1, state=None,
-                    eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6):
+                    eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix"):
     """Masked-parallel form over the whole sequence (quadratic; small T only)."""
-    _check(variant, window)
+    _check(variant, window, align)
     q = np.asarray(q)
     B, T, H, dk = q.shape
     dv = np.asarray(v).shape[-1]
@@ -255,7 +264,10 @@ def masked_parallel(variant, q, k, v, beta, log_lambda, *, window=1, state=None,
     nwx = np.zeros_like(wx)
     nwv = np.zeros_like(wv)
     for n in range(N):
-        X = np.concatenate([xp[n][None], Kf[n, :-1]], axis=0)      # x_t = phi(k_{t-1})
+        if align == "prefix":
+            X = np.concatenate([xp[n][None], Kf[n, :-1]], axis=0)  # x_t = phi(k_{t-1})
+        else:
+            X = Kf[n]                                               # x_t = phi(k_t)
         O[n], ST[n], PX, PV = _masked_parallel_one(variant, window, Qh[n], X, V[n], Bt[n], G[n],
                                                    S[n], wx[n], wv[n], eps_gamma, eps_eta)
         if window > 1:
@@ -270,7 +282,7 @@ def masked_parallel(variant, q, k, v, beta, log_lambda, *, window=1, state=None,
 
 
 def chunked(variant, q, k, v, beta, log_lambda, *, chunk, window=1, state=None,
-            eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6):
+            eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix"):
     """Chunked form ([P1] 三种等价形式 form C, [P2] 三种视角): the masked-parallel
     form applied chunk by chunk, with the state (S, x_prev, window) handed from
     one chunk to the next.  chunk = 1 is the recurrent form, chunk >= T the
@@ -281,7 +293,7 @@ def chunked(variant, q, k, v, beta, log_lambda, *, chunk, window=1, state=None,
     for c0 in range(0, T, chunk):
         sl = slice(c0, min(T, c0 + chunk))
         r = masked_parallel(variant, q[:, sl], k[:, sl], v[:, sl], beta[:, sl],
-                            log_lambda[:, sl], window=window, state=st,
+                            log_lambda[:, sl], window=window, state=st, align=align,
                             eps_gamma=eps_gamma, eps_phi=eps_phi, eps_eta=eps_eta)
         outs.append(r["o"])
         st = {n: r[n] for n in ("S", "x_prev", "win_x", "win_v") if n in r}

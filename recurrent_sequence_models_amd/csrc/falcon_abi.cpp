@@ -31,6 +31,7 @@ int check_shape(const falcon_shape_t *s, bool step) {
   if (!(s->eps_gamma > 0.f && s->eps_gamma <= 1.f)) return FALCON_ERR_INVALID_ARG;
   if (s->eps_phi < 0.f || !(s->eps_eta > 0.f)) return FALCON_ERR_INVALID_ARG;
   if (s->window < 1) return FALCON_ERR_INVALID_ARG;
+  if (s->align != FALCON_ALIGN_PREFIX && s->align != FALCON_ALIGN_SAME) return FALCON_ERR_INVALID_ARG;
   if (!windowed(s->variant) && s->window != 1) return FALCON_ERR_INVALID_ARG;
   if (windowed(s->variant) && s->window > 8) return FALCON_ERR_UNSUPPORTED;
   if (s->dk != s->dv) return FALCON_ERR_UNSUPPORTED;
@@ -157,6 +158,7 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   a.B = s->batch; a.T = s->seqlen; a.H = s->heads;
   a.nchunks = (s->seqlen + s->chunk - 1) / s->chunk;
   a.window = windowed(s->variant) ? s->window : 1;
+  a.align = s->align;
   a.log_eps_gamma = std::log(s->eps_gamma);
   a.eps_phi = s->eps_phi;
   a.eps_eta = s->eps_eta;
@@ -183,6 +185,8 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
     }
     return FALCON_OK;
   }
+  // same-step pairs run only on the chunk-parallel kernels
+  if (!split && s->align != FALCON_ALIGN_PREFIX) return FALCON_ERR_UNSUPPORTED;
   if (split) {   // prep over all systems, then the scan workgroups of each sequence
     return falcon::launch_chunk_fwd_split(s->variant, bf16, s->dk, s->dv, s->chunk, a.window, a, workspace, hs) ==
                    hipSuccess
@@ -214,6 +218,7 @@ int falcon_recurrent_step(const falcon_shape_t *s, const void *q, const void *k,
   a.o = o;
   a.B = s->batch; a.H = s->heads;
   a.window = windowed(s->variant) ? s->window : 1;
+  a.align = s->align;
   a.log_eps_gamma = std::log(s->eps_gamma);
   a.eps_phi = s->eps_phi;
   a.eps_eta = s->eps_eta;

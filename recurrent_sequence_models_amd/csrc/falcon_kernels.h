@@ -21,6 +21,7 @@ struct FwdArgs {
   void *o;                       // [B,T,H,dv]
   float *chunk_states;           // [B,H,NC,dv,dk] or null
   int B, T, H, nchunks, window;
+  int align;                     // 0: pair (phi(k_{t-1}), v_t); 1: pair (phi(k_t), v_t)
   float log_eps_gamma, eps_phi, eps_eta;
   int write_tail;                // 1: the main kernel writes x_prev / window itself
 };
@@ -31,6 +32,7 @@ struct StepArgs {
   float *S, *xprev, *winx, *winv;
   void *o;
   int B, H, window;
+  int align;                     // 0: pair (x_prev, v_t); 1: pair (phi(k_t), v_t)
   float log_eps_gamma, eps_phi, eps_eta;
 };
 

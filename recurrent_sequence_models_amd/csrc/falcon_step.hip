@@ -56,13 +56,16 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   IT *op = static_cast<IT *>(a.o);
 
   // per-sequence scalars, computed redundantly by every row group
-  f4 x = *reinterpret_cast<const f4 *>(a.xprev + (size_t)bh * DK + 4 * part);
   f4 qv, kv;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     qv[e] = ld1(qp + (size_t)bh * DK + 4 * part + e);
     kv[e] = ld1(kp + (size_t)bh * DK + 4 * part + e);
   }
+  const float kn = row_sum<LPR>(dot4(kv, kv));
+  const f4 xk = kv * (kn + a.eps_phi > 0.f ? rsqrtf(kn + a.eps_phi) : 0.f);   // phi(k_t)
+  // the key of this step's pair: the carried phi(k_{t-1}), or phi(k_t) with same-step pairs
+  const f4 x = a.align ? xk : *reinterpret_cast<const f4 *>(a.xprev + (size_t)bh * DK + 4 * part);
   const float qn = row_sum<LPR>(dot4(qv, qv));
   const f4 qh = qv * (qn + a.eps_phi > 0.f ? rsqrtf(qn + a.eps_phi) : 0.f);
   const float xn2 = row_sum<LPR>(dot4(x, x));
@@ -140,8 +143,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   // every lane has read x_prev and the window; now they may be replaced
   __syncthreads();
   if (wv == 0 && rsub == 0) {
-    const float kn = row_sum<LPR>(dot4(kv, kv));
-    const f4 xn = kv * (kn + a.eps_phi > 0.f ? rsqrtf(kn + a.eps_phi) : 0.f);
+    const f4 xn = xk;
     if (WIN && BW > 1) {
       // shift the window: drop the oldest pair, append (x, v)
 #pragma unroll
@@ -176,12 +178,15 @@ __global__ __launch_bounds__(256) void tail_kernel(FwdArgs a) {
   __shared__ float sx[MAXW][DK];   // new window keys, then x_prev
   __shared__ float sv[MAXW][DV];
   __shared__ float snorm[MAXW];
-  // slot j = 0..BW-2 is pair s = T - BW + 1 + j; slot BW-1 is phi(k_{T-1})
+  // slot j = 0..BW-2 is pair s = T - BW + 1 + j, whose key is k_{s-1+align} (carried
+  // when that index is negative: x_prev for s = 0, the window for s < 0); slot BW-1
+  // is phi(k_{T-1})
+  auto key_index = [&](int j) { return j == BW - 1 ? T - 1 : T - BW + j + a.align; };
   for (int j = 0; j < BW; ++j) {
-    const int s = T - BW + 1 + j;     // pair index (slot BW-1 reuses the formula with s = T)
+    const int s = T - BW + 1 + j, t = key_index(j);
     for (int e = tid; e < DK; e += 256) {
       float x;
-      if (s >= 1) x = ld1(kp + ((size_t)(b * T + s - 1) * H + h) * DK + e);
+      if (t >= 0) x = ld1(kp + ((size_t)(b * T + t) * H + h) * DK + e);
       else if (s == 0) x = a.xprev0 ? a.xprev0[(size_t)bh * DK + e] : 0.f;
       else x = a.winx0 ? a.winx0[((size_t)bh * (BW - 1) + (BW - 1 + s)) * DK + e] : 0.f;
       sx[j][e] = x;
@@ -198,12 +203,11 @@ __global__ __launch_bounds__(256) void tail_kernel(FwdArgs a) {
   __syncthreads();
   for (int j = tid >> 6; j < BW; j += 4) {   // wave w normalises slots w, w+4 when they came from a key
     const int lane = tid & 63;
-    const int s = T - BW + 1 + j;
     float ss = 0.f;
     for (int e = lane; e < DK; e += 64) ss += sx[j][e] * sx[j][e];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if (lane == 0) snorm[j] = (s >= 1) ? (ss + a.eps_phi > 0.f ? rsqrtf(ss + a.eps_phi) : 0.f) : 1.f;
+    if (lane == 0) snorm[j] = (key_index(j) >= 0) ? (ss + a.eps_phi > 0.f ? rsqrtf(ss + a.eps_phi) : 0.f) : 1.f;
   }
   __syncthreads();
   for (int e = tid; e < DK; e += 256) a.xprev_out[(size_t)bh * DK + e] = sx[BW - 1][e] * snorm[BW - 1];

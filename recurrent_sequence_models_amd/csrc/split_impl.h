@@ -408,12 +408,13 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
   }
 
   if constexpr (BW == 1) {
-    // X row r holds k_{c0+r-1} (x_prev for the first row of the sequence), Q row r holds q_{c0+r}
+    // X row r holds k_{c0+r-1} (x_prev for the first row of the sequence; k_{c0+r}
+    // with same-step pairs), Q row r holds q_{c0+r}
 #pragma unroll
     for (int ps = 0; ps < S::NPASS; ++ps) {
       const int r = ps * RPP + tid / TPR, part = tid % TPR;
       if (r < C) {
-        const int tk = c0 + r - 1, tq = c0 + r;
+        const int tk = c0 + r - 1 + a.align, tq = c0 + r;
         // loads use in-bounds (clamped) rows; rows outside the sequence are zeroed after the load
         const int tkc = min(max(tk, 0), T - 1), tqc = min(tq, T - 1);
         const uint4 kraw = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tkc) * H + h) * D + part * VEC);
@@ -459,12 +460,12 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
     for (int ps = 0; ps < S::NPASS; ++ps) {
       const int r = ps * RPP + tid / TPR, part = tid % TPR;
       if (r < C) {
-        const int st = c0 + r / BW, j = st - BW + 1 + r % BW, tk = j - 1;
+        const int st = c0 + r / BW, j = st - BW + 1 + r % BW, tk = j - 1 + a.align;
         const int tkc = min(max(tk, 0), T - 1);
         const uint4 kraw = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tkc) * H + h) * D + part * VEC);
         uint4 k4 = keep_or_zero(tk >= 0 && st < T, kraw);
         float sk = 0.f;
-        if (j <= 0 && st < T) {   // carried feature (fp32, already normalised)
+        if (tk < 0 && st < T) {   // carried feature (fp32, already normalised): x_prev (j = 0) or window
           const float *src = j == 0 ? (a.xprev0 ? a.xprev0 + (size_t)bh * D : nullptr)
                                     : (a.winx0 ? a.winx0 + ((size_t)bh * (BW - 1) + j + BW - 1) * D : nullptr);
           float xf[VEC];
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
           for (int e = 0; e < VEC; ++e) sk += xv[e] * xv[e];
         }
         sk = group_sum<TPR>(sk);
-        const float ik = j <= 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
+        const float ik = tk < 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
         put_perm(sX + r * LX, part * VEC, k4);
         if (part == 0) {
           sR[R_IK * C + r] = ik;
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
   // A system is "interior" when every row's pair index is >= 1 and every step is
   // inside the sequence: its rows are then plain strided reads, with no clamps,
   // masks or carried features.
-  auto interior = [&](int c) { return c * CS >= BW && (c + 1) * CS <= T; };
+  auto interior = [&](int c) { return c * CS >= BW - a.align && (c + 1) * CS <= T; };
   const long long rstride = (long long)H * D;   // elements between consecutive tokens
   auto prefetch = [&](int c, Regs &R) __attribute__((always_inline)) {    // global -> registers, system c (rows clamped in bounds)
     const int c0 = c * CS;
@@ -662,7 +663,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
 #pragma unroll
       for (int ps = 0; ps < Z::NPK; ++ps) {
         const int r = min(ps * RPC + ctid / TPR, C - 1), part = ctid % TPR;
-        R.k[ps] = *reinterpret_cast<const uint4 *>(kp + base + (pair_of(0, r) - 1) * rstride + part * VEC);
+        R.k[ps] = *reinterpret_cast<const uint4 *>(kp + base + (pair_of(0, r) - 1 + a.align) * rstride + part * VEC);
         R.q[ps] = *reinterpret_cast<const uint4 *>(qp + base + min(r, CS - 1) * rstride + part * VEC);
       }
       if constexpr (ONE) {
@@ -685,7 +686,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
 #pragma unroll
     for (int ps = 0; ps < Z::NPK; ++ps) {
       const int r = min(ps * RPC + ctid / TPR, C - 1), part = ctid % TPR;
-      const int tk = min(max(pair_of(c0, r) - 1, 0), T - 1), tq = min(c0 + r, T - 1);
+      const int tk = min(max(pair_of(c0, r) - 1 + a.align, 0), T - 1), tq = min(c0 + r, T - 1);
       R.k[ps] = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tk) * H + h) * D + part * VEC);
       R.q[ps] = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tq) * H + h) * D + part * VEC);
     }
@@ -763,9 +764,10 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
       if (r < C) {
         const int j = pair_of(c0, r);
         const bool live = step_of(c0, r) < T;
-        uint4 kk = keep_or_zero(live && j >= 1, R.k[ps]);
+        const bool carried = j - 1 + a.align < 0;   // key before the sequence: x_prev (j = 0) or window
+        uint4 kk = keep_or_zero(live && !carried, R.k[ps]);
         float sk = 0.f;   // one-pass: squared norm of the row, for the derive waves
-        if (live && j <= 0) {   // a carried feature (fp32, normalised): x_prev, or window key j
+        if (live && carried) {   // a carried feature (fp32, normalised)
           float xv[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) xv[e] = carried_key(j, part * VEC + e);
@@ -980,7 +982,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
     if (lane >= C) {
       // rows past the system: no per-row entries
     } else if constexpr (BW == 1) {   // lane = row = step
-      const bool carried = c0 + lane == 0;
+      const bool carried = c0 + lane - 1 + a.align < 0;
       const float sk = nk[lane], sq = nq[lane];
       const float ik = carried ? 1.f : safe_rsqrt(sk + a.eps_phi);
       const float iq = safe_rsqrt(sq + a.eps_phi);
@@ -1001,7 +1003,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
     } else {   // lane = virtual row r (step r / BW); step values come from lane = step
       const int st = lane / BW, j = c0 + st - BW + 1 + lane % BW;
       const float sk = nk[lane];
-      const float ik = j <= 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
+      const float ik = j - 1 + a.align < 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
       const float e2 = sk * ik * ik;
       const float e2new = __shfl(e2, st * BW + BW - 1);   // the step's own (newest) pair
       const float bq = lane < CSP ? gb[lane] : 0.f;
@@ -1094,13 +1096,14 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
       // outgoing x_prev = phi(k_{T-1}) and, for windows, the last Bw-1 pairs
       // j = T-Bw+1..T-1 (keys phi(k_{j-1}), values v_j; carried ones for j <= 0)
       const int w8 = wv - 2 * NCW - NDW;
-      auto key_row = [&](int j, float *dst) {   // normalised key of pair j into dst[0..D)
+      // normalised key k_t (t >= 0) or carried key of pair j (t = j - 1 + align < 0) into dst[0..D)
+      auto key_row = [&](int t, int j, float *dst) {
         float xv[2] = {0.f, 0.f};
-        if (j >= 1) {
+        if (t >= 0) {
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             const int e = lane + 64 * m;
-            if (e < D) xv[m] = to_f(kp[((size_t)(b * T + j - 1) * H + h) * D + e]);
+            if (e < D) xv[m] = to_f(kp[((size_t)(b * T + t) * H + h) * D + e]);
           }
           const float inv = safe_rsqrt(group_sum<64>(xv[0] * xv[0] + xv[1] * xv[1]) + a.eps_phi);
           xv[0] *= inv;
@@ -1120,10 +1123,10 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
       };
       for (int u = w8; u < BW; u += Z::NSW) {   // window pairs 0..BW-2, then x_prev
         if (u == BW - 1) {
-          if (sp == 0 && a.xprev_out) key_row(T, a.xprev_out + (size_t)bh * D);
+          if (sp == 0 && a.xprev_out) key_row(T - 1, 0, a.xprev_out + (size_t)bh * D);
         } else {
           const int j = T - BW + 1 + u;
-          if (sp == 0 && a.winx_out) key_row(j, a.winx_out + ((size_t)bh * (BW - 1) + u) * D);
+          if (sp == 0 && a.winx_out) key_row(j - 1 + a.align, j, a.winx_out + ((size_t)bh * (BW - 1) + u) * D);
           if (a.winv_out) {
             for (int e = lane; e < Z::DS; e += 64) {
               const int ch = Z::DS * sp + e;

@@ -29,7 +29,7 @@ class Shape(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("eps_gamma", ctypes.c_float),
-                ("eps_phi", ctypes.c_float), ("eps_eta", ctypes.c_float)]
+                ("eps_phi", ctypes.c_float), ("eps_eta", ctypes.c_float), ("align", ctypes.c_int32)]
 
 
 class State(ctypes.Structure):
@@ -73,11 +73,15 @@ def status_string(status: int) -> str:
     return lib().falcon_status_string(int(status)).decode()
 
 
+ALIGNS = {"prefix": 0, "same": 1}
+
+
 def make_shape(variant, dtype, batch, seqlen, heads, dk, dv, chunk=64, window=1,
-               eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6) -> Shape:
+               eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix") -> Shape:
     return Shape(VARIANTS.get(variant, variant) if isinstance(variant, str) else variant,
                  DTYPES.get(dtype, dtype) if isinstance(dtype, str) else dtype,
-                 batch, seqlen, heads, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta)
+                 batch, seqlen, heads, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta,
+                 ALIGNS.get(align, align) if isinstance(align, str) else align)
 
 
 def _ptr(t):
@@ -122,24 +126,27 @@ def new_state(batch, heads, dk, dv, window=1, device="cuda"):
 
 
 def workspace_bytes(variant, dtype, batch, seqlen, heads, dk, dv, chunk=64, window=1, eps_gamma=1e-3,
-                    eps_phi=1e-6, eps_eta=1e-6):
+                    eps_phi=1e-6, eps_eta=1e-6, align="prefix"):
     """falcon_chunk_fwd_workspace for a shape: bytes of scratch that enable the
-    chunk-parallel path (0: the shape runs the fused path)."""
-    shape = make_shape(variant, dtype, batch, seqlen, heads, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta)
+    two-kernel chunk-parallel path (0: that path is not built for the shape)."""
+    shape = make_shape(variant, dtype, batch, seqlen, heads, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta,
+                       align)
     return int(lib().falcon_chunk_fwd_workspace(ctypes.byref(shape)))
 
 
 def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=None,
               final=True, chunk_states=False, eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6,
-              out=None, stream=None, workspace=True):
+              out=None, stream=None, workspace=True, align="prefix"):
     """falcon_chunk_fwd on torch tensors.
 
     q, k [B,T,H,dk] and v [B,T,H,dv] in float32 or bfloat16; beta [B,T,H] (or
     [B,T,H,dv] for F2/F2A) and log_lambda [B,T,H] float32.  ``init``: None or a
     state dict (S, x_prev, win_x, win_v).  ``final``: True (allocate), a state
     dict to write into (may be ``init``), or False.  ``workspace``: True
-    allocates the scratch of the chunk-parallel path when the shape has one,
-    False runs the fused path (no scratch), or a uint8 device tensor to use.
+    allocates the scratch of the two-kernel chunk-parallel path when the shape
+    has one, False runs the one-pass (or fused) kernel without scratch, or a
+    uint8 device tensor to use.  ``align``: "prefix" (the pair written at step t
+    is (phi(k_{t-1}), v_t)) or "same" ((phi(k_t), v_t)).
     Returns (o, final_state, chunk_states)."""
     import torch
     B, T, H, dk = q.shape
@@ -163,7 +170,7 @@ def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=No
         final = None
     nch = (T + chunk - 1) // chunk
     cs = torch.empty(B, H, nch, dv, dk, dtype=torch.float32, device=dev) if chunk_states else None
-    shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta)
+    shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
     L = lib()
     if workspace is True:
         ws_bytes = L.falcon_chunk_fwd_workspace(ctypes.byref(shape))
@@ -184,7 +191,7 @@ def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=No
 
 
 def recurrent_step(variant, q, k, v, beta, log_lambda, state, *, window=1, eps_gamma=1e-3,
-                   eps_phi=1e-6, eps_eta=1e-6, out=None, stream=None):
+                   eps_phi=1e-6, eps_eta=1e-6, out=None, stream=None, align="prefix"):
     """falcon_recurrent_step: one token for every (b, h); ``state`` is updated in place.
 
     q, k [B,H,dk], v [B,H,dv] (float32 or bfloat16); beta [B,H] (or [B,H,dv]),
@@ -205,7 +212,7 @@ def recurrent_step(variant, q, k, v, beta, log_lambda, state, *, window=1, eps_g
     _check_tensor("x_prev", state["x_prev"], torch.float32, (B, H, dk), dev)
     if out is None:
         out = torch.empty(B, H, dv, dtype=q.dtype, device=dev)
-    shape = make_shape(variant, dt, B, 1, H, dk, dv, 64, window, eps_gamma, eps_phi, eps_eta)
+    shape = make_shape(variant, dt, B, 1, H, dk, dv, 64, window, eps_gamma, eps_phi, eps_eta, align)
     st = _state(state)
     status = lib().falcon_recurrent_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                          _ptr(log_lambda), ctypes.byref(st), _ptr(out), _stream(stream))

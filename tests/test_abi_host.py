@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = F.lib()
-    assert L.falcon_abi_version() == 1
+    assert L.falcon_abi_version() == 2
     for code in range(5):
         s = F.status_string(code)
         assert s.startswith("FALCON_")
@@ -112,11 +112,12 @@ INVALID_SHAPES = [
     dict(variant=0), dict(variant=7), dict(dtype=2), dict(batch=0), dict(seqlen=0), dict(heads=0),
     dict(dk=0), dict(chunk=0), dict(window=0), dict(variant="F1", window=2),
     dict(eps_gamma=0.0), dict(eps_gamma=1.5), dict(eps_gamma=float("nan")), dict(eps_phi=-1.0),
-    dict(eps_eta=0.0), dict(eps_eta=float("inf")),
+    dict(eps_eta=0.0), dict(eps_eta=float("inf")), dict(align=2), dict(align=-1),
 ]
 UNSUPPORTED_SHAPES = [
     dict(dk=48, dv=48), dict(dk=64, dv=32), dict(dk=256, dv=256), dict(chunk=8), dict(chunk=128),
     dict(dtype="fp32", dk=128, dv=128), dict(variant="F3", window=3), dict(variant="F3", window=16),
+    dict(align="same", variant="F3", window=4, chunk=32),   # same-step pairs: chunk-parallel kernels only
 ]
 
 

@@ -84,3 +84,34 @@ def test_decode_full_size_sampled():
                                {"S": sub["S"], "x_prev": sub["x_prev"]})
         assert rel_l2(o[b], r["o"][0]) <= TOL["bf16"]
         assert rel_l2(to_np(st["S"][b]), r["S"][0]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("variant,window", CASES)
+@pytest.mark.parametrize("d,dtype", [(32, "fp32"), (128, "bf16")])
+def test_decode_same_step_pairs(variant, window, d, dtype):
+    """Same-step pairs (phi(k_t), v_t): consecutive steps vs the oracle; x_prev is not read."""
+    from recurrent_sequence_models_amd import recurrent_step
+    import torch
+    inp = W.make_decode_inputs(4, 3, d, d, variant, seed=56, window=window, dtype=dtype)
+    st0 = {n: inp[n] for n in ("S", "x_prev", "win_x", "win_v") if n in inp}
+    st_dev = state_to_dev(st0)
+    st_ref = st0
+    rng = np.random.default_rng(4)
+    for t in range(6):
+        x = {n: inp[n] for n in ("q", "k", "v", "beta", "log_lambda")}
+        if t:
+            x = {n: (a + 0.1 * rng.standard_normal(a.shape)).astype(np.float32) if n in ("q", "k", "v") else a
+                 for n, a in x.items()}
+            if dtype == "bf16":
+                x = {n: W.round_bf16(a) if n in ("q", "k", "v") else a for n, a in x.items()}
+        dd = to_dev(x, dtype)
+        o = recurrent_step(variant, dd["q"], dd["k"], dd["v"], dd["beta"], dd["log_lambda"], st_dev, window=window,
+                           align="same")
+        torch.cuda.synchronize()
+        r = oracle.decode_step(variant, x["q"], x["k"], x["v"], x["beta"], x["log_lambda"], st_ref, window=window,
+                               align="same")
+        st_ref = {n: r[n] for n in st0}
+        assert rel_l2(to_np(o), r["o"]) <= TOL[dtype], (t, rel_l2(to_np(o), r["o"]))
+    for n in st0:
+        e = rel_l2(to_np(st_dev[n]), st_ref[n])
+        assert e <= TOL[dtype], (n, e)

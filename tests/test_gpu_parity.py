@@ -16,13 +16,15 @@ pytestmark = pytest.mark.gpu
 ROW_VARIANTS = ("F1", "F1A", "F2", "F2A")
 
 
-def run_gpu(variant, inp, dtype, chunk, window=1, init=None, chunk_states=False, final=True, workspace=True):
+def run_gpu(variant, inp, dtype, chunk, window=1, init=None, chunk_states=False, final=True, workspace=True,
+            align="prefix"):
     import torch
     from recurrent_sequence_models_amd import chunk_fwd
     d = to_dev(inp, dtype)
     st = state_to_dev(init) if init is not None else None
     o, fin, cs = chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=chunk,
-                           window=window, init=st, final=final, chunk_states=chunk_states, workspace=workspace)
+                           window=window, init=st, final=final, chunk_states=chunk_states, workspace=workspace,
+                           align=align)
     torch.cuda.synchronize()
     out = {"o": to_np(o)}
     if fin is not None:
@@ -32,12 +34,12 @@ def run_gpu(variant, inp, dtype, chunk, window=1, init=None, chunk_states=False,
     return out
 
 
-def check(variant, w, seed, window=1, init=False, chunk=None, chunk_states=False, workspace=True):
+def check(variant, w, seed, window=1, init=False, chunk=None, chunk_states=False, workspace=True, align="prefix"):
     inp = W.make_inputs(w, variant, seed=seed)
     st = W.make_state(w, seed + 1000, window) if init else None
     chunk = chunk or w.chunk
-    g = run_gpu(variant, inp, w.dtype, chunk, window, st, chunk_states, workspace=workspace)
-    r = oracle.recurrent(variant, **inp, window=window, state=st, return_states=chunk_states)
+    g = run_gpu(variant, inp, w.dtype, chunk, window, st, chunk_states, workspace=workspace, align=align)
+    r = oracle.recurrent(variant, **inp, window=window, state=st, return_states=chunk_states, align=align)
     tol = TOL[w.dtype]
     errs = {"o": rel_l2(g["o"], r["o"]), "S": rel_l2(g["S"], r["S"]), "x_prev": rel_l2(g["x_prev"], r["x_prev"])}
     if window > 1:
@@ -263,6 +265,50 @@ def test_onepass_full_size_sampled(variant):
         print(variant, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
     assert np.all(np.isfinite(g["o"]))
+
+
+# ---- same-step pairs (phi(k_t), v_t): the pages' contrast to the prefix pair -----------
+SAME_CASES = [(v, 1) for v in ROW_VARIANTS] + [("F3", 2), ("F3", 4), ("F3", 8), ("F3A", 4), ("F3A", 8)]
+
+
+SAME_SHAPES = [(v, bw, "bf16", 64, 203, 64) for v, bw in SAME_CASES] + \
+              [(v, 1, "fp32", 32, 150, 32) for v in ROW_VARIANTS]
+
+
+@pytest.mark.parametrize("variant,bw,dtype,d,T,chunk", SAME_SHAPES)
+@pytest.mark.parametrize("workspace", [True, False])
+def test_same_step_pairs(variant, bw, dtype, d, T, chunk, workspace):
+    """Both chunk-parallel forms, carried state (x_prev present but not read), chunk states."""
+    w = W.WORKLOADS["layer130m"].replace(batch=2, heads=3, seqlen=T, dk=d, dv=d, dtype=dtype, chunk=chunk)
+    check(variant, w, 81, window=bw, init=True, chunk_states=True, workspace=workspace, align="same")
+
+
+@pytest.mark.parametrize("variant,bw", [("F1", 1), ("F2", 1), ("F3", 4), ("F3A", 2)])
+@pytest.mark.parametrize("d,B,H,T", [(128, 1, 6, 100), (64, 8, 16, 70), (32, 1, 5, 9)])
+def test_same_step_splits_and_short(variant, bw, d, B, H, T):
+    w = W.WORKLOADS["layer130m"].replace(batch=B, heads=H, seqlen=T, dk=d, dv=d)
+    check(variant, w, 82, window=bw, init=True, chunk_states=True, align="same")
+
+
+@pytest.mark.parametrize("variant,bw,workspace", [("F1", 1, False), ("F1", 1, True), ("F3", 4, True),
+                                                  ("F3", 8, False)])
+def test_same_step_continuation_in_place(variant, bw, workspace):
+    import torch
+    from recurrent_sequence_models_amd import chunk_fwd, new_state
+    w = W.WORKLOADS["layer130m"].replace(batch=2, heads=2, seqlen=300)
+    inp = W.make_inputs(w, variant, seed=83)
+    d = to_dev(inp, "bf16")
+    st = new_state(2, 2, 64, 64, window=bw)
+    outs = []
+    for sl in (slice(0, 5), slice(5, 141), slice(141, 300)):
+        o, _, _ = chunk_fwd(variant, *(d[n][:, sl].contiguous() for n in ("q", "k", "v", "beta", "log_lambda")),
+                            window=bw, init=st, final=st, workspace=workspace, align="same")
+        outs.append(to_np(o))
+    torch.cuda.synchronize()
+    r = oracle.recurrent(variant, **inp, window=bw, align="same")
+    assert rel_l2(np.concatenate(outs, axis=1), r["o"]) <= TOL["bf16"]
+    for n in (("S", "x_prev", "win_x", "win_v") if bw > 1 else ("S", "x_prev")):
+        assert rel_l2(to_np(st[n]), r[n]) <= TOL["bf16"], n
 
 
 # ---- Falcon-3 / 3A: window of Bw pairs --------------------------------------------

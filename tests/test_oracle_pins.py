@@ -366,3 +366,62 @@ def test_p10_fresh_sequence_by_hand(variant):
     np.testing.assert_allclose(r["states"][0, 1, 0], S2, rtol=1e-14, atol=1e-15)
     np.testing.assert_allclose(r["o"][0, 1, 0], (x2 @ qh2) * eta2 * v2 / bw, rtol=1e-13, atol=1e-15)
     np.testing.assert_allclose(r["x_prev"][0, 0], unit(inp["k"][0, 1, 0]), rtol=1e-15)
+
+
+# -- P11: same-step alignment, the pages' contrast to the prefix pair ([P1] 本质;
+# [P2] 一个被忽略的时间差): x_t = phi(k_t) ------------------------------------------------
+@pytest.mark.parametrize("variant,bw", CASES)
+@pytest.mark.parametrize("carry", [False, True])
+def test_p11_same_step_recurrent_equals_masked_parallel(variant, bw, carry):
+    w, inp = small(T=17, variant=variant, gates="softplus")
+    st = W.make_state(w, 3, bw) if carry else None
+    r = oracle.recurrent(variant, **inp, window=bw, state=st, align="same")
+    m = oracle.masked_parallel(variant, **inp, window=bw, state=st, align="same")
+    for key in ("o", "S", "x_prev") + (("win_x", "win_v") if bw > 1 else ()):
+        np.testing.assert_allclose(r[key], m[key], rtol=0, atol=1e-12, err_msg=key)
+
+
+@pytest.mark.parametrize("variant,bw", CASES)
+def test_p11_same_step_is_prefix_on_keys_one_step_ahead(variant, bw):
+    """Writing (phi(k_t), v_t) at step t is the prefix rule fed the keys one step
+    ahead (k'_{t-1} = k_t), with phi(k_1) as the carried feature."""
+    w, inp = small(T=15, variant=variant, gates="softplus")
+    st = W.make_state(w, 4, bw)
+    same = oracle.recurrent(variant, **inp, window=bw, state=st, align="same")
+    shifted = dict(inp)
+    k = np.asarray(inp["k"])
+    shifted["k"] = np.concatenate([k[:, 1:], k[:, -1:]], axis=1)   # the last key only feeds x_prev
+    st2 = dict(st)
+    st2["x_prev"] = unit(k[:, 0])
+    pre = oracle.recurrent(variant, **shifted, window=bw, state=st2)
+    np.testing.assert_allclose(same["o"], pre["o"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(same["S"], pre["S"], rtol=0, atol=1e-12)
+    if bw > 1:
+        np.testing.assert_allclose(same["win_x"], pre["win_x"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(same["win_v"], pre["win_v"], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", VARS)
+def test_p11_same_step_first_write_by_hand(variant):
+    bw = 3 if variant in ("F3", "F3A") else 1
+    w, inp = small(T=1, dk=4, dv=3, B=1, H=1, variant=variant)
+    r = oracle.recurrent(variant, **inp, window=bw, align="same")
+    x1 = unit(inp["k"][0, 0, 0])
+    qh1 = unit(inp["q"][0, 0, 0])
+    beta1 = np.asarray(inp["beta"][0, 0, 0], np.float64)
+    eta1 = beta1 / (1e-6 + x1 @ x1)
+    v1 = inp["v"][0, 0, 0].astype(np.float64)
+    S1 = (eta1 * v1)[:, None] * x1[None, :] / bw       # from S_0 = 0 the decay has nothing to act on
+    np.testing.assert_allclose(r["S"][0, 0], S1, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(r["o"][0, 0, 0], S1 @ qh1, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("variant,bw", CASES)
+def test_p11_same_step_chunk_invariance(variant, bw):
+    w, inp = small(T=19, variant=variant, gates="softplus")
+    st = W.make_state(w, 5, bw)
+    ref = oracle.recurrent(variant, **inp, window=bw, state=st, align="same")
+    for C in (1, 3, 16, 40):
+        c = oracle.chunked(variant, **inp, window=bw, state=st, chunk=C, align="same")
+        np.testing.assert_allclose(c["o"], ref["o"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(c["S"], ref["S"], rtol=0, atol=1e-12)
