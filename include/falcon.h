@@ -159,6 +159,27 @@ int falcon_chunk_fwd(const falcon_shape_t *shape,
                      void *o, float *chunk_states,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Chunked forward pass over a packed batch of sequences of different lengths
+ * (the same computation as falcon_chunk_fwd, one sequence per entry):
+ *   shape->batch  = N, the number of sequences; shape->seqlen = the total
+ *                   number of tokens, cu_seqlens[N].
+ *   cu_seqlens    device int32 [N + 1]: sequence n holds tokens
+ *                   cu_seqlens[n] .. cu_seqlens[n+1] - 1 (non-decreasing,
+ *                   cu_seqlens[0] = 0; read on the device, not checked).
+ *   q, k [total, H, dk], v, o [total, H, dv] in dtype; beta [total, H] (F2/F2A:
+ *   [total, H, dv]) and log_lambda [total, H] fp32; the state arrays are per
+ *   sequence ([N, H, ...]) as in falcon_chunk_fwd.
+ * Sequence n starts from init (its own S, x_prev and window) and ends in
+ * final_state.  A sequence of length 0 is skipped: its final state is not
+ * written.  No workspace and no per-chunk states; it runs on the one-pass
+ * kernel, so shapes that kernel does not build return FALCON_ERR_UNSUPPORTED.
+ * Same aliasing and stream rules as falcon_chunk_fwd. */
+int falcon_chunk_fwd_varlen(const falcon_shape_t *shape, const int32_t *cu_seqlens,
+                            const void *q, const void *k, const void *v,
+                            const float *beta, const float *log_lambda,
+                            const falcon_state_t *init, falcon_state_t *final_state,
+                            void *o, void *stream);
+
 /* One token of the recurrent form ([P1] 三种等价形式 form A; [P2] 三种视角):
  * reads q, k [B, H, dk], v [B, H, dv], beta [B, H] (F2/F2A: [B, H, dv]) and
  * log_lambda [B, H]; updates `state` in place (S, x_prev and, for F3/F3A with

@@ -1,5 +1,5 @@
 """Falcon fast-weight attention on MI355X (gfx950): chunked forward pass and
 single-token recurrent step behind a C ABI (include/falcon.h)."""
 
-from .falcon import (VARIANTS, FalconError, chunk_fwd, recurrent_step, new_state, lib,  # noqa: F401
+from .falcon import (VARIANTS, FalconError, chunk_fwd, chunk_fwd_varlen, recurrent_step, new_state, lib,  # noqa: F401
                      make_shape, status_string)

@@ -201,6 +201,53 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   return FALCON_OK;
 }
 
+int falcon_chunk_fwd_varlen(const falcon_shape_t *s, const int32_t *cu_seqlens, const void *q, const void *k,
+                            const void *v, const float *beta, const float *log_lambda, const falcon_state_t *init,
+                            falcon_state_t *final_state, void *o, void *stream) {
+  int st = check_shape(s, false);
+  if (st != FALCON_OK) return st;
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return FALCON_ERR_INVALID_ARG;
+  if ((st = check_io(q, k, v, beta, log_lambda, o)) != FALCON_OK) return st;
+  if (init && (st = check_state(init, s)) != FALCON_OK) return st;
+  if (final_state && (st = check_state(final_state, s)) != FALCON_OK) return st;
+  const bool bf16 = s->dtype == FALCON_BF16;
+  const bool win = windowed(s->variant) && s->window > 1;
+  const int window = windowed(s->variant) ? s->window : 1;
+  const int ns = falcon::chunk_fwd_onepass_ns(s->variant, bf16, s->dk, s->dv, s->chunk, window, s->batch * s->heads);
+  if (ns == 0) return FALCON_ERR_UNSUPPORTED;
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = log_lambda;
+  a.S0 = init ? init->S : nullptr;
+  a.xprev0 = init ? init->x_prev : nullptr;
+  a.winx0 = (init && win) ? init->win_x : nullptr;
+  a.winv0 = (init && win) ? init->win_v : nullptr;
+  a.S_out = final_state ? final_state->S : nullptr;
+  a.xprev_out = final_state ? final_state->x_prev : nullptr;
+  a.winx_out = (final_state && win) ? final_state->win_x : nullptr;
+  a.winv_out = (final_state && win) ? final_state->win_v : nullptr;
+  a.o = o;
+  a.chunk_states = nullptr;
+  a.cu = cu_seqlens;
+  a.B = s->batch; a.T = s->seqlen; a.H = s->heads;
+  a.nchunks = 1;
+  a.window = window;
+  a.align = s->align;
+  a.log_eps_gamma = std::log(s->eps_gamma);
+  a.eps_phi = s->eps_phi;
+  a.eps_eta = s->eps_eta;
+  const bool alias = init && final_state &&
+                     (init->x_prev == final_state->x_prev ||
+                      (win && (init->win_x == final_state->win_x || init->win_v == final_state->win_v)));
+  a.write_tail = (final_state && (ns == 1 || !alias)) ? 1 : 0;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (falcon::launch_chunk_fwd_onepass(s->variant, bf16, s->dk, s->dv, s->chunk, window, a, hs) != hipSuccess)
+    return FALCON_ERR_HIP;
+  if (final_state && !a.write_tail) {
+    if (falcon::launch_tail(s->variant, bf16, s->dk, s->dv, a, hs) != hipSuccess) return FALCON_ERR_HIP;
+  }
+  return FALCON_OK;
+}
+
 int falcon_recurrent_step(const falcon_shape_t *s, const void *q, const void *k, const void *v,
                           const float *beta, const float *log_lambda, falcon_state_t *state, void *o,
                           void *stream) {

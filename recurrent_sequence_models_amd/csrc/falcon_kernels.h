@@ -20,6 +20,7 @@ struct FwdArgs {
   float *winx_out, *winv_out;    // [B,H,Bw-1,dk|dv] or null
   void *o;                       // [B,T,H,dv]
   float *chunk_states;           // [B,H,NC,dv,dk] or null
+  const int *cu;                 // packed sequences: [B+1] token offsets (q, k, v, o are [cu[B], H, d]), or null
   int B, T, H, nchunks, window;
   int align;                     // 0: pair (phi(k_{t-1}), v_t); 1: pair (phi(k_t), v_t)
   float log_eps_gamma, eps_phi, eps_eta;

@@ -172,7 +172,11 @@ template <typename IT, int DK, int DV>
 __global__ __launch_bounds__(256) void tail_kernel(FwdArgs a) {
   const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x;
-  const int T = a.T, H = a.H, BW = a.window;
+  // token range: row b of a dense batch, or the packed tokens cu[b] .. cu[b+1]
+  const long long tok0 = a.cu ? (long long)a.cu[b] : (long long)b * a.T;
+  const int T = a.cu ? a.cu[b + 1] - a.cu[b] : a.T, H = a.H, BW = a.window;
+  if (T <= 0) return;   // empty packed sequence: skipped
+
   const IT *kp = static_cast<const IT *>(a.k);
   const IT *vp = static_cast<const IT *>(a.v);
   __shared__ float sx[MAXW][DK];   // new window keys, then x_prev
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(256) void tail_kernel(FwdArgs a) {
     const int s = T - BW + 1 + j, t = key_index(j);
     for (int e = tid; e < DK; e += 256) {
       float x;
-      if (t >= 0) x = ld1(kp + ((size_t)(b * T + t) * H + h) * DK + e);
+      if (t >= 0) x = ld1(kp + ((size_t)(tok0 + t) * H + h) * DK + e);
       else if (s == 0) x = a.xprev0 ? a.xprev0[(size_t)bh * DK + e] : 0.f;
       else x = a.winx0 ? a.winx0[((size_t)bh * (BW - 1) + (BW - 1 + s)) * DK + e] : 0.f;
       sx[j][e] = x;
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(256) void tail_kernel(FwdArgs a) {
     if (j < BW - 1) {
       for (int e = tid; e < DV; e += 256) {
         float v;
-        if (s >= 0) v = ld1(vp + ((size_t)(b * T + s) * H + h) * DV + e);
+        if (s >= 0) v = ld1(vp + ((size_t)(tok0 + s) * H + h) * DV + e);
         else v = a.winv0 ? a.winv0[((size_t)bh * (BW - 1) + (BW - 1 + s)) * DV + e] : 0.f;
         sv[j][e] = v;
       }

@@ -602,7 +602,12 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
     sp = blockIdx.x % NS;
   }
   const int b = bh / a.H, h = bh % a.H;
-  const int T = a.T, H = a.H, NC = a.nchunks, NSYS = S::nsys(T);
+  // token range of the sequence: row b of a dense [B, T] batch, or the packed
+  // tokens cu[b] .. cu[b+1] (one-pass form); an empty sequence is skipped whole
+  const long long tok0 = a.cu ? (long long)a.cu[b] : (long long)b * a.T;
+  const int T = a.cu ? a.cu[b + 1] - a.cu[b] : a.T;
+  if (T <= 0) return;
+  const int H = a.H, NC = a.nchunks, NSYS = S::nsys(T);
   const int role = wv < NCW ? 0 : wv < 2 * NCW ? 1 : wv < 2 * NCW + NDW ? 3 : 2;   // state, output, derive, copy
   const int cw = role == 1 ? wv - NCW : wv;                // channel group of a state / output wave
   const int dw = wv - 2 * NCW;                             // derive wave index
@@ -654,7 +659,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
   auto prefetch = [&](int c, Regs &R) __attribute__((always_inline)) {    // global -> registers, system c (rows clamped in bounds)
     const int c0 = c * CS;
     if (interior(c)) {
-      const long long base = ((long long)b * T + c0) * rstride + (long long)h * D;   // token c0 of the sequence
+      const long long base = (tok0 + c0) * rstride + (long long)h * D;   // token c0 of the sequence
 #pragma unroll
       for (int ps = 0; ps < Z::NPV; ++ps) {
         const int r = min(ps * RPV + ctid / TPV, C - 1), part = ctid % TPV;
@@ -667,7 +672,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
         R.q[ps] = *reinterpret_cast<const uint4 *>(qp + base + min(r, CS - 1) * rstride + part * VEC);
       }
       if constexpr (ONE) {
-        const size_t gi = ((size_t)b * T + c0 + min(ctid, CS - 1)) * H + h;
+        const size_t gi = ((size_t)(tok0 + c0 + min(ctid, CS - 1))) * H + h;
         R.g = a.g[gi];
         R.bt = PERCH ? 0.f : a.beta[gi];
       } else {
@@ -681,19 +686,19 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
     for (int ps = 0; ps < Z::NPV; ++ps) {
       const int r = min(ps * RPV + ctid / TPV, C - 1), part = ctid % TPV;
       const int tv = min(max(pair_of(c0, r), 0), T - 1);
-      R.v[ps] = *reinterpret_cast<const uint4 *>(vp + ((size_t)(b * T + tv) * H + h) * D + Z::DS * sp + part * VEC);
+      R.v[ps] = *reinterpret_cast<const uint4 *>(vp + ((size_t)(tok0 + tv) * H + h) * D + Z::DS * sp + part * VEC);
     }
 #pragma unroll
     for (int ps = 0; ps < Z::NPK; ++ps) {
       const int r = min(ps * RPC + ctid / TPR, C - 1), part = ctid % TPR;
       const int tk = min(max(pair_of(c0, r) - 1 + a.align, 0), T - 1), tq = min(c0 + r, T - 1);
-      R.k[ps] = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tk) * H + h) * D + part * VEC);
-      R.q[ps] = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tq) * H + h) * D + part * VEC);
+      R.k[ps] = *reinterpret_cast<const uint4 *>(kp + ((size_t)(tok0 + tk) * H + h) * D + part * VEC);
+      R.q[ps] = *reinterpret_cast<const uint4 *>(qp + ((size_t)(tok0 + tq) * H + h) * D + part * VEC);
     }
     if constexpr (ONE) {
       const int t = min(c0 + min(ctid, CSP - 1), T - 1);
-      R.g = a.g[(size_t)(b * T + t) * H + h];
-      R.bt = PERCH ? 0.f : a.beta[(size_t)(b * T + t) * H + h];
+      R.g = a.g[(size_t)(tok0 + t) * H + h];
+      R.bt = PERCH ? 0.f : a.beta[(size_t)(tok0 + t) * H + h];
     } else {
       const uint4 *src = reinterpret_cast<const uint4 *>(wsq + (size_t)c * S::IMG);
 #pragma unroll
@@ -823,7 +828,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = c * CS + 16 * p + 4 * g4 + i;   // zero past the end: padded rows must not write
-        const float braw = a.beta[((size_t)(b * T + min(t, T - 1)) * H + h) * D + chW];
+        const float braw = a.beta[((size_t)(tok0 + min(t, T - 1)) * H + h) * D + chW];
         rbeta[p][i] = t < T ? braw : 0.f;
       }
   };
@@ -963,7 +968,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
       if (!(qm & 1)) mma16(O, Eb[qm], ld4(Pm + frag_off(S::pbase(ps), qm, lane)));
       const int srow = 16 * ps + cl, t = c0 + srow;
       if (srow < CS && t < T)
-        *reinterpret_cast<Frag *>(op + ((size_t)(b * T + t) * H + h) * D + Z::DS * sp + 16 * cw + 4 * g4) = cvt<OpT>(O);
+        *reinterpret_cast<Frag *>(op + ((size_t)(tok0 + t) * H + h) * D + Z::DS * sp + 16 * cw + 4 * g4) = cvt<OpT>(O);
     }
   };
 
@@ -1103,7 +1108,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             const int e = lane + 64 * m;
-            if (e < D) xv[m] = to_f(kp[((size_t)(b * T + t) * H + h) * D + e]);
+            if (e < D) xv[m] = to_f(kp[((size_t)(tok0 + t) * H + h) * D + e]);
           }
           const float inv = safe_rsqrt(group_sum<64>(xv[0] * xv[0] + xv[1] * xv[1]) + a.eps_phi);
           xv[0] *= inv;
@@ -1131,7 +1136,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
             for (int e = lane; e < Z::DS; e += 64) {
               const int ch = Z::DS * sp + e;
               a.winv_out[((size_t)bh * (BW - 1) + u) * D + ch] =
-                  j >= 0 ? to_f(vp[((size_t)(b * T + j) * H + h) * D + ch]) : carried_val(j, ch);
+                  j >= 0 ? to_f(vp[((size_t)(tok0 + j) * H + h) * D + ch]) : carried_val(j, ch);
             }
           }
         }

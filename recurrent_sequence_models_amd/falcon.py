@@ -21,7 +21,7 @@ PER_CHANNEL = ("F2", "F2A")
 WINDOWED = ("F3", "F3A")
 
 EXPORTS = ("falcon_abi_version", "falcon_status_string", "falcon_chunk_fwd_workspace",
-           "falcon_chunk_fwd", "falcon_recurrent_step")
+           "falcon_chunk_fwd", "falcon_chunk_fwd_varlen", "falcon_recurrent_step")
 
 
 class Shape(ctypes.Structure):
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.falcon_chunk_fwd_workspace.argtypes = [P(Shape)]
         L.falcon_chunk_fwd.restype = I
         L.falcon_chunk_fwd.argtypes = [P(Shape), V, V, V, V, V, P(State), P(State), V, V, V, S, V]
+        L.falcon_chunk_fwd_varlen.restype = I
+        L.falcon_chunk_fwd_varlen.argtypes = [P(Shape), V, V, V, V, V, V, P(State), P(State), V, V]
         L.falcon_recurrent_step.restype = I
         L.falcon_recurrent_step.argtypes = [P(Shape), V, V, V, V, V, P(State), V, V]
         _LIB = L
@@ -188,6 +190,48 @@ def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=No
     if status != OK:
         raise FalconError(status, "falcon_chunk_fwd")
     return out, final, cs
+
+
+def chunk_fwd_varlen(variant, q, k, v, beta, log_lambda, cu_seqlens, *, chunk=64, window=1, init=None,
+                     final=True, eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, out=None, stream=None,
+                     align="prefix"):
+    """falcon_chunk_fwd_varlen on torch tensors: N packed sequences.
+
+    q, k [total,H,dk] and v [total,H,dv] (float32 or bfloat16); beta [total,H]
+    (or [total,H,dv] for F2/F2A) and log_lambda [total,H] float32; cu_seqlens an
+    int32 device tensor [N+1] of token offsets.  ``init`` / ``final`` as for
+    chunk_fwd, with N sequences.  Returns (o, final_state)."""
+    import torch
+    total, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    N = cu_seqlens.numel() - 1
+    dt = {torch.float32: "fp32", torch.bfloat16: "bf16"}.get(q.dtype)
+    if dt is None:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    _check_tensor("q", q, q.dtype, (total, H, dk), dev)
+    _check_tensor("k", k, q.dtype, (total, H, dk), dev)
+    _check_tensor("v", v, q.dtype, (total, H, dv), dev)
+    _check_tensor("beta", beta, torch.float32, (total, H, dv) if variant in PER_CHANNEL else (total, H), dev)
+    _check_tensor("log_lambda", log_lambda, torch.float32, (total, H), dev)
+    _check_tensor("cu_seqlens", cu_seqlens, torch.int32, (N + 1,), dev)
+    if out is None:
+        out = torch.empty(total, H, dv, dtype=q.dtype, device=dev)
+    _check_tensor("o", out, q.dtype, (total, H, dv), dev)
+    if final is True:
+        final = new_state(N, H, dk, dv, window if variant in WINDOWED else 1, dev)
+    elif final is False:
+        final = None
+    shape = make_shape(variant, dt, N, total, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
+    st_in, st_out = _state(init), _state(final)
+    status = lib().falcon_chunk_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(beta), _ptr(log_lambda),
+                                           ctypes.byref(st_in) if st_in else None,
+                                           ctypes.byref(st_out) if st_out else None,
+                                           _ptr(out), _stream(stream))
+    if status != OK:
+        raise FalconError(status, "falcon_chunk_fwd_varlen")
+    return out, final
 
 
 def recurrent_step(variant, q, k, v, beta, log_lambda, state, *, window=1, eps_gamma=1e-3,

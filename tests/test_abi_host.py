@@ -169,3 +169,23 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(F, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         F.lib()
+
+
+def call_varlen(shape, cu=FAKE, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, init=None, final=None, o=FAKE):
+    L = F.lib()
+    return L.falcon_chunk_fwd_varlen(ctypes.byref(shape) if shape is not None else None, cu, q, k, v, beta, g,
+                                     ctypes.byref(init) if init else None, ctypes.byref(final) if final else None,
+                                     o, None)
+
+
+@cpu_only
+def test_varlen_rejects_on_host():
+    """Packed-sequence calls: the offsets pointer must be present and 4-byte aligned;
+    shapes without a one-pass kernel are unsupported; all before any HIP call."""
+    assert call_varlen(good_shape(seqlen=500), cu=None) == F.ERR_INVALID_ARG
+    assert call_varlen(good_shape(seqlen=500), cu=ctypes.c_void_p(0x10002)) == F.ERR_INVALID_ARG
+    assert call_varlen(good_shape(seqlen=500), q=None) == F.ERR_INVALID_ARG
+    assert call_varlen(good_shape(seqlen=500, batch=0)) == F.ERR_INVALID_ARG
+    assert call_varlen(good_shape(seqlen=500, dtype="fp32", dk=64, dv=64, chunk=64)) == F.ERR_UNSUPPORTED
+    assert call_varlen(good_shape(seqlen=500, dk=128, dv=128)) == F.ERR_UNSUPPORTED
+    assert call_varlen(good_shape(seqlen=500, variant="F3", window=4, chunk=32)) == F.ERR_UNSUPPORTED

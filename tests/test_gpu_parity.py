@@ -311,6 +311,78 @@ def test_same_step_continuation_in_place(variant, bw, workspace):
         assert rel_l2(to_np(st[n]), r[n]) <= TOL["bf16"], n
 
 
+# ---- packed sequences of different lengths (cu_seqlens) ---------------------------
+def run_varlen(variant, lens, dtype, d, chunk, bw, seed, init=True, in_place=False, align="prefix"):
+    """Pack len(lens) independent sequences (H = 3), run falcon_chunk_fwd_varlen and
+    the oracle per sequence; returns the rel-L2 errors per sequence and name."""
+    import torch
+    from recurrent_sequence_models_amd import chunk_fwd_varlen, new_state
+    H = 3
+    seqs, refs, states = [], [], []
+    for n, T in enumerate(lens):
+        w = W.WORKLOADS["layer130m"].replace(batch=1, heads=H, seqlen=max(T, 1), dk=d, dv=d, dtype=dtype, chunk=chunk)
+        inp = W.make_inputs(w, variant, seed=seed + n)
+        inp = {k: a[:, :T] for k, a in inp.items()}
+        st = W.make_state(w, seed + 100 + n, bw) if init else None
+        seqs.append(inp)
+        states.append(st)
+        refs.append(oracle.recurrent(variant, **inp, window=bw, state=st, align=align) if T > 0 else None)
+    cat = {k: np.concatenate([x[k][0] for x in seqs], axis=0) for k in seqs[0]}   # [total, H, ...]
+    d_in = to_dev(cat, dtype)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+    st_dev = None
+    if init:
+        st_dev = state_to_dev({k: np.concatenate([s[k] for s in states], axis=0) for k in states[0]})
+    fin = st_dev if in_place else True
+    o, fin = chunk_fwd_varlen(variant, d_in["q"], d_in["k"], d_in["v"], d_in["beta"], d_in["log_lambda"], cu,
+                              chunk=chunk, window=bw, init=st_dev, final=fin, align=align)
+    torch.cuda.synchronize()
+    o = to_np(o)
+    fin = {k: to_np(t) for k, t in fin.items()}
+    errs = []
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    for n, r in enumerate(refs):
+        if r is None:
+            continue
+        e = {"o": rel_l2(o[offs[n]:offs[n + 1]], r["o"][0]), "S": rel_l2(fin["S"][n], r["S"][0]),
+             "x_prev": rel_l2(fin["x_prev"][n], r["x_prev"][0])}
+        if bw > 1:
+            e["win_x"] = rel_l2(fin["win_x"][n], r["win_x"][0])
+            e["win_v"] = rel_l2(fin["win_v"][n], r["win_v"][0])
+        errs.append(e)
+    return errs
+
+
+VARLEN_CASES = [(v, 1) for v in ROW_VARIANTS] + [("F3", 4), ("F3A", 8), ("F3", 2)]
+
+
+@pytest.mark.parametrize("variant,bw", VARLEN_CASES)
+@pytest.mark.parametrize("in_place", [False, True])
+def test_varlen_bf16(variant, bw, in_place):
+    errs = run_varlen(variant, [1, 17, 64, 65, 130, 200, 7], "bf16", 64, 64, bw, 91, in_place=in_place)
+    for e in errs:
+        for k, x in e.items():
+            assert x <= TOL["bf16"], (k, x, e)
+
+
+@pytest.mark.parametrize("variant", ROW_VARIANTS)
+def test_varlen_fp32(variant):
+    errs = run_varlen(variant, [3, 50, 33, 1], "fp32", 32, 32, 1, 92)
+    for e in errs:
+        for k, x in e.items():
+            assert x <= TOL["fp32"], (k, x, e)
+
+
+@pytest.mark.parametrize("variant,bw", [("F1", 1), ("F3", 4)])
+def test_varlen_empty_and_same_step(variant, bw):
+    """A zero-length sequence in the pack is skipped; same-step pairs on packed sequences."""
+    errs = run_varlen(variant, [40, 0, 90], "bf16", 64, 64, bw, 93, align="same")
+    assert len(errs) == 2
+    for e in errs:
+        for k, x in e.items():
+            assert x <= TOL["bf16"], (k, x, e)
+
+
 # ---- Falcon-3 / 3A: window of Bw pairs --------------------------------------------
 WIN_CASES = [("F3", 2), ("F3", 4), ("F3", 8), ("F3A", 2), ("F3A", 4), ("F3A", 8), ("F3", 1), ("F3A", 1)]
 
