@@ -29,6 +29,7 @@ parity is unpinned by the pages and fixed only by the readings.
 """
 
 from .falcon_oracle import (VARIANTS, recurrent, masked_parallel, chunked,
-                            decode_step, phi)
+                            decode_step, phi, recurrent_backward)
 
-__all__ = ["VARIANTS", "recurrent", "masked_parallel", "chunked", "decode_step", "phi"]
+__all__ = ["VARIANTS", "recurrent", "masked_parallel", "chunked", "decode_step", "phi",
+           "recurrent_backward"]

@@ -300,3 +300,115 @@ def chunked(variant, q, k, v, beta, log_lambda, *, chunk, window=1, state=None,
     res = dict(st)
     res["o"] = np.concatenate(outs, axis=1)
     return res
+
+
+_BACKWARD_VARIANTS = ("F1", "F1A", "F2", "F2A")
+
+
+def _phi_backward(a, da, eps_phi):
+    """Adjoint of phi(a) = a / n, n = sqrt(|a|^2 + eps_phi): J^T da = da/n - a (a.da)/n^3."""
+    n = np.sqrt(np.sum(a * a, axis=-1, keepdims=True) + eps_phi)
+    return da / n - a * np.sum(a * da, axis=-1, keepdims=True) / n ** 3
+
+
+def recurrent_backward(variant, q, k, v, beta, log_lambda, do, *, state=None, dS_T=None,
+                       eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix"):
+    """Gradients of the recurrent form by reverse-time accumulation (the adjoint of
+    the step written out), for the chunked form's use in training ([P1] 三种等价形式:
+    the chunk-parallel form is the one a training framework runs).
+
+    The scalar being differentiated is <do, o> + <dS_T, S_T> for the forward of
+    :func:`recurrent` from ``state`` (S, x_prev; zeros when absent).  The outgoing
+    x_prev takes no gradient.  Differentiation conventions (readings):
+      * lam = max(exp(g), eps_gamma): dg = dlam * lam where exp(g) > eps_gamma,
+        else 0 (at the floor the decay does not depend on g);
+      * eta = beta / (eps_eta + |x|^2) depends on x through |x|^2;
+      * phi is differentiated as written (with eps_phi inside the root).
+
+    Per step t, going backwards, with G the gradient of the scalar w.r.t. S_t:
+        G += do_t qh_t^T;  dqh_t = S_t^T do_t;  dlam_t = <G, S_{t-1}>;  u = G x_t
+        regression (F1/F2): e = v_t - S_{t-1} x_t, deta = e * u, dv_t = eta * u,
+            dx_t = G^T (eta e) - S_{t-1}^T (eta u),  G <- lam G - (eta u) x_t^T
+        additive (F1A/F2A): e = v_t, same deta/dv_t, dx_t = G^T (eta v_t),  G <- lam G
+    (``eta * u`` is a scalar times a vector for F1/F1A and elementwise for F2/F2A.)
+    Then dx_t gains -2 x_t sum(deta * eta)/(eps_eta + |x_t|^2), dbeta_t = deta/(eps_eta + |x_t|^2),
+    and dx_t flows through phi to k_{t-1} (prefix; x_1 of the prefix form is the
+    carried x_prev, so its gradient is dx_prev0) or to k_t (same step).
+
+    Returns dict(dq, dk, dv [B,T,H,d], dbeta (shape of beta), dg [B,T,H],
+    dS0 [B,H,dv,dk], dx_prev0 [B,H,dk])."""
+    _check(variant, 1, align)
+    if variant not in _BACKWARD_VARIANTS:
+        raise ValueError("the backward covers F1, F1A, F2, F2A")
+    q = np.asarray(q)
+    B, T, H, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    N = B * H
+    Q, K, V = _to_seq(q), _to_seq(k), _to_seq(v)
+    Bt, G_in, dO = _to_seq(beta), _to_seq(log_lambda), _to_seq(do)
+    S0, xp0, _, _ = _initial(state, N, B, H, dk, dv, 1)
+    delta = variant in _DELTA
+    vector = variant in _VECTOR_ETA
+
+    # Forward pass, keeping every state and every x_t.
+    fwd = recurrent(variant, q, k, v, beta, log_lambda, state=state, eps_gamma=eps_gamma,
+                    eps_phi=eps_phi, eps_eta=eps_eta, return_states=True, align=align)
+    states = _to_seq(fwd["states"])                                     # [N,T,dv,dk], S_t
+    Kh = phi(K, eps_phi)
+    Qh = phi(Q, eps_phi)
+    if align == "prefix":
+        X = np.concatenate([xp0[:, None, :], Kh[:, :-1]], axis=1)      # x_t = phi(k_{t-1})
+    else:
+        X = Kh.copy()
+
+    dQh = np.zeros_like(Qh)
+    dX = np.zeros_like(X)
+    dV = np.zeros_like(V)
+    dBt = np.zeros_like(Bt)
+    dGl = np.zeros((N, T))
+    G = np.zeros((N, dv, dk)) if dS_T is None else np.asarray(dS_T, np.float64).reshape(N, dv, dk).copy()
+    for t in range(T - 1, -1, -1):
+        S_prev = states[:, t - 1] if t > 0 else S0
+        S_t = states[:, t]
+        x = X[:, t]
+        energy = eps_eta + np.sum(x * x, axis=-1)                       # [N]
+        b = Bt[:, t]
+        eta = b / energy[:, None] if vector else b / energy              # [N,dv] or [N]
+        lam = np.maximum(np.exp(G_in[:, t]), eps_gamma)
+        G = G + dO[:, t][:, :, None] * Qh[:, t][:, None, :]
+        dQh[:, t] = np.einsum("nij,ni->nj", S_t, dO[:, t])
+        dlam = np.einsum("nij,nij->n", G, S_prev)
+        u = np.einsum("nij,nj->ni", G, x)                               # G x_t
+        e = V[:, t] - np.einsum("nij,nj->ni", S_prev, x) if delta else V[:, t]
+        eta_v = eta if vector else eta[:, None]                          # broadcast over rows
+        deta_rows = e * u                                                # per value channel
+        dV[:, t] = eta_v * u
+        dx = np.einsum("nij,ni->nj", G, eta_v * e)
+        if delta:
+            dx = dx - np.einsum("nij,ni->nj", S_prev, eta_v * u)
+            G = lam[:, None, None] * G - (eta_v * u)[:, :, None] * x[:, None, :]
+        else:
+            G = lam[:, None, None] * G
+        if vector:
+            deta = deta_rows                                             # [N,dv]
+            dBt[:, t] = deta / energy[:, None]
+            denergy = -np.sum(deta * eta, axis=-1) / energy
+        else:
+            deta = np.sum(deta_rows, axis=-1)                            # [N]
+            dBt[:, t] = deta / energy
+            denergy = -deta * eta / energy
+        dX[:, t] = dx + 2.0 * denergy[:, None] * x
+        dGl[:, t] = np.where(np.exp(G_in[:, t]) > eps_gamma, dlam * lam, 0.0)
+
+    dQ = _phi_backward(Q, dQh, eps_phi)
+    dK = np.zeros_like(K)
+    dxp0 = np.zeros((N, dk))
+    if align == "prefix":
+        dK[:, :-1] = _phi_backward(K[:, :-1], dX[:, 1:], eps_phi)
+        dxp0 = dX[:, 0]
+    else:
+        dK = _phi_backward(K, dX, eps_phi)
+    out = dict(dq=_from_seq(dQ, B, H), dk=_from_seq(dK, B, H), dv=_from_seq(dV, B, H),
+               dbeta=_from_seq(dBt, B, H), dg=_from_seq(dGl, B, H),
+               dS0=G.reshape(B, H, dv, dk), dx_prev0=dxp0.reshape(B, H, dk))
+    return out

@@ -156,3 +156,19 @@ def make_decode_inputs(batch: int, heads: int, dk: int, dv: int, variant: str, s
     out = {n: a[:, 0] for n, a in inp.items()}
     out.update(make_state(w, seed + 7919, window))
     return out
+
+
+def make_cotangents(w: Workload, seed: int, final: bool = True) -> dict:
+    """Output gradients for a backward pass: do ~ N(0,1) [B,T,H,dv] (bf16-rounded
+    for bf16 workloads, since it is stored in the input type) and, if ``final``,
+    dS_T ~ N(0,1)/sqrt(dk) [B,H,dv,dk] fp32."""
+    rng = np.random.default_rng(seed)
+    B, T, H, dk, dv = w.batch, w.seqlen, w.heads, w.dk, w.dv
+    do = rng.standard_normal((B, T, H, dv), dtype=np.float32)
+    if w.dtype == "bf16":
+        do = round_bf16(do)
+    out = dict(do=do, dS_T=None)
+    if final:
+        out["dS_T"] = (rng.standard_normal((B, H, dv, dk), dtype=np.float32)
+                       / math.sqrt(dk)).astype(np.float32)
+    return out
