@@ -1,7 +1,7 @@
 /*
  * falcon.h -- C ABI of the MI355X (gfx950) implementation of Falcon
  * fast-weight attention: the chunk-parallel forward pass and the single-token
- * recurrent step.
+ * recurrent step, and the backward pass of the chunked form.
  *
  * Sources, cited by page title and section:
  *   [P1] zhouql-dev.github.io, "把状态更新写成一条学习规则：Falcon 家族重新对齐
@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FALCON_ABI_VERSION 2
+#define FALCON_ABI_VERSION 3
 
 typedef enum {
   FALCON_1 = 1,   /* scalar NLMS step, residual write            */
@@ -189,6 +189,46 @@ int falcon_recurrent_step(const falcon_shape_t *shape,
                           const void *q, const void *k, const void *v,
                           const float *beta, const float *log_lambda,
                           falcon_state_t *state, void *o, void *stream);
+
+/* Bytes of device workspace falcon_chunk_bwd needs for this shape; 0 when the
+ * backward pass is not built for it (or the shape is invalid).  Built: F1 and
+ * F1A, d_k = d_v = 64, chunk 64, fp32 or bf16 inputs, either pairing.  The
+ * workspace holds, per chunk, the keys, the scaled WY factor, the state
+ * gradient the chunk's outputs inject and the state gradient at the chunk's
+ * end (4 x 16 KiB + 4 bytes); it needs no initialisation. */
+size_t falcon_chunk_bwd_workspace(const falcon_shape_t *shape);
+
+/* Backward pass of the chunked form ([P1] 三种等价形式 form C / Figure 4-C: the
+ * form a training framework runs): the gradients of the scalar
+ *     <d_o, o> + <d_final_S, S_T>
+ * for the forward pass falcon_chunk_fwd(shape, q, k, v, beta, log_lambda, init)
+ * with respect to q, k, v, beta, log_lambda and the initial state.  The
+ * outgoing x_prev takes no gradient.  The decay clamp passes no gradient where
+ * exp(g) <= eps_gamma (there the decay does not depend on g).
+ *   init         as given to the forward pass (NULL = fresh sequences); S and
+ *                x_prev are read.
+ *   chunk_states [B, H, ceil(T/64), 64, 64] fp32: the per-chunk states the
+ *                forward pass wrote for these inputs (chunk 64).
+ *   d_o          [B, T, H, 64] in dtype.
+ *   d_final_S    [B, H, 64, 64] fp32, or NULL for a zero gradient on S_T.
+ *   dq, dk, dv   [B, T, H, 64] fp32, written whole (under the prefix pairing
+ *                dk of the last token is 0).
+ *   dbeta, dg    [B, T, H] fp32.
+ *   d_init       NULL, or S [B, H, 64, 64] and x_prev [B, H, 64] fp32 that
+ *                receive the gradients w.r.t. the initial state (x_prev: 0
+ *                under the same-step pairing, which does not read it).
+ *   workspace    at least falcon_chunk_bwd_workspace(shape) bytes, else
+ *                FALCON_ERR_WORKSPACE; calls sharing a workspace race.
+ * Outputs must not alias inputs.  Other shapes return FALCON_ERR_UNSUPPORTED.
+ * Results are deterministic. */
+int falcon_chunk_bwd(const falcon_shape_t *shape,
+                     const void *q, const void *k, const void *v,
+                     const float *beta, const float *log_lambda,
+                     const falcon_state_t *init, const float *chunk_states,
+                     const void *d_o, const float *d_final_S,
+                     float *dq, float *dk, float *dv, float *dbeta, float *dg,
+                     falcon_state_t *d_init,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -12,6 +12,7 @@
 
 namespace {
 
+using falcon::BwdArgs;
 using falcon::FwdArgs;
 using falcon::StepArgs;
 
@@ -271,6 +272,50 @@ int falcon_recurrent_step(const falcon_shape_t *s, const void *q, const void *k,
   a.eps_eta = s->eps_eta;
   if (falcon::launch_step(s->variant, s->dtype == FALCON_BF16, s->dk, s->dv, a,
                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FALCON_ERR_HIP;
+  return FALCON_OK;
+}
+
+size_t falcon_chunk_bwd_workspace(const falcon_shape_t *s) {
+  if (check_shape(s, false) != FALCON_OK) return 0;
+  if (!falcon::chunk_bwd_supported(s->variant, s->dk, s->dv, s->chunk, s->window)) return 0;
+  return falcon::chunk_bwd_workspace(s->batch, s->heads, s->seqlen);
+}
+
+int falcon_chunk_bwd(const falcon_shape_t *s, const void *q, const void *k, const void *v, const float *beta,
+                     const float *log_lambda, const falcon_state_t *init, const float *chunk_states,
+                     const void *d_o, const float *d_final_S, float *dq, float *dk, float *dv, float *dbeta,
+                     float *dg, falcon_state_t *d_init, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_shape(s, false);
+  if (st != FALCON_OK) return st;
+  if ((st = check_io(q, k, v, beta, log_lambda, d_o)) != FALCON_OK) return st;
+  if (!chunk_states || !dq || !dk || !dv || !dbeta || !dg || !workspace) return FALCON_ERR_INVALID_ARG;
+  if (!aligned16(chunk_states) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FALCON_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(dbeta) & 3u) != 0 || (reinterpret_cast<uintptr_t>(dg) & 3u) != 0)
+    return FALCON_ERR_INVALID_ARG;
+  if (d_final_S && !aligned16(d_final_S)) return FALCON_ERR_INVALID_ARG;
+  if (init && (st = check_state(init, s)) != FALCON_OK) return st;
+  if (d_init && (st = check_state(d_init, s)) != FALCON_OK) return st;
+  if (!falcon::chunk_bwd_supported(s->variant, s->dk, s->dv, s->chunk, s->window)) return FALCON_ERR_UNSUPPORTED;
+  if (workspace_bytes < falcon::chunk_bwd_workspace(s->batch, s->heads, s->seqlen)) return FALCON_ERR_WORKSPACE;
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.dO = d_o; a.beta = beta; a.g = log_lambda;
+  a.S0 = init ? init->S : nullptr;
+  a.xprev0 = init ? init->x_prev : nullptr;
+  a.chunk_states = chunk_states;
+  a.dST = d_final_S;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dg = dg;
+  a.dS0 = d_init ? d_init->S : nullptr;
+  a.dxprev0 = d_init ? d_init->x_prev : nullptr;
+  a.ws = static_cast<float *>(workspace);
+  a.B = s->batch; a.T = s->seqlen; a.H = s->heads;
+  a.NC = (s->seqlen + s->chunk - 1) / s->chunk;
+  a.align = s->align;
+  a.log_eps_gamma = std::log(s->eps_gamma);
+  a.eps_phi = s->eps_phi;
+  a.eps_eta = s->eps_eta;
+  if (falcon::launch_chunk_bwd(s->variant, s->dtype == FALCON_BF16, a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return FALCON_ERR_HIP;
   return FALCON_OK;
 }

@@ -1,0 +1,768 @@
+// Backward pass of the chunk-parallel form for Falcon-1 / 1A (scalar NLMS step,
+// one pair per step), d_k = d_v = 64, chunks of 64 steps.
+//
+// It differentiates the scalar <do, o> + <dS_T, S_T> with respect to q, k, v,
+// beta, the log-decay g and the incoming state, reading the per-chunk states the
+// forward pass wrote ([P1] 三种等价形式 form C / Figure 4-C: the chunked form is
+// the one a training framework runs, so it is the one differentiated here).
+//
+// Chunk-local notation (steps i = 0..63 of a chunk, rows past T are identity
+// steps: x = q = v = 0, eta = 0, log-decay 0):
+//   L_i = sum_{s<=i} l_s with l = max(g, log eps_gamma); Lm_i = L_{i-1} (Lm_0 = 0)
+//   A = strict-tril(X X^T o e^{Lm_i - L_j}),  P = tril(Qh X^T o e^{L_i - L_j})
+//   M = I + A diag(eta),  R = V - diag(e^{Lm}) X S0^T,  E = M^-1 R  (F1A: E = V)
+//   O = diag(e^L) Qh S0^T + P diag(eta) E,   S_C = e^{L_C} S0 + E^T diag(b) X,
+//   b_i = eta_i e^{L_C - L_i}.
+// With G the gradient at the chunk's end state, the gradient at its start is
+//   G0 = e^{L_C} G - (G X^T) diag(b) W + do^T (diag(e^L) Qh - P diag(eta) W),
+//   W = M^-1 diag(e^{Lm}) X   (F1A: W = 0),
+// a reverse recurrence of the same shape as the forward state recurrence.
+//
+// Three launches, all fp32 MFMA (v_mfma_f32_16x16x4f32, mfma_frag.h layouts):
+//   bwd_prep   one workgroup per chunk: X, Wb = diag(b) W and
+//              Z = do^T (diag(e^L) Qh - P diag(eta) W) into the workspace.
+//   bwd_scan   one workgroup per 16 value channels of a sequence (rows of G are
+//              independent), chunks in reverse: writes G at every chunk end and
+//              the gradient of the initial S.
+//   bwd_chunk  one workgroup per chunk: recomputes A, P, E from the chunk's
+//              incoming state and takes the adjoint of every product above.
+//
+// Layout of a workgroup (256 threads = 4 waves): C x 64 matrices whose columns
+// are value or key channels are held by waves in 16-column tiles (wave w owns
+// columns 16w..16w+15 of every row tile), so a triangular solve along the
+// chunk runs inside one wave with no barrier; C x C matrices are computed one
+// 16-row tile per wave and staged in LDS.  LDS rows have a pitch of 68 floats,
+// which makes both the 16-byte row reads and the 4-byte column reads of the
+// fragment loads free of bank conflicts.
+#include "falcon_kernels.h"
+#include "mfma_frag.h"
+
+namespace falcon {
+
+namespace {
+
+constexpr int D = 64;    // d_k = d_v
+constexpr int C = 64;    // steps per chunk
+constexpr int LD = 68;   // LDS pitch of a 64-wide matrix (floats)
+constexpr int TL = 20;   // LDS pitch of a 16x16 diagonal-block inverse
+constexpr int NT = 256;  // threads per workgroup
+constexpr int MAT = C * LD;
+
+// ---- fragments (lane l = 16g + c) ---------------------------------------------
+// A-layout of the 16x16 block at (r0, k0) of row-major M: M[r0 + c][k0 + 4g + i].
+__device__ __forceinline__ f4 a_rm(const float *m, int ld, int r0, int k0, int lane) {
+  return *reinterpret_cast<const f4 *>(m + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
+}
+// A-layout of the block at (r0, k0) of M^T: M[k0 + 4g + i][r0 + c].
+__device__ __forceinline__ f4 a_tr(const float *m, int ld, int r0, int k0, int lane) {
+  const float *p = m + (k0 + 4 * (lane >> 4)) * ld + r0 + (lane & 15);
+  return f4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+// C-layout (B operand) of the block at (k0, c0) of M: M[k0 + 4g + i][c0 + c].
+__device__ __forceinline__ f4 b_rm(const float *m, int ld, int k0, int c0, int lane) {
+  return a_tr(m, ld, c0, k0, lane);
+}
+// C-layout of the block at (k0, c0) of M^T: M[c0 + c][k0 + 4g + i].
+__device__ __forceinline__ f4 b_tr(const float *m, int ld, int k0, int c0, int lane) {
+  return a_rm(m, ld, c0, k0, lane);
+}
+// Store a C-layout tile into the block at (r0, c0) of row-major M.
+__device__ __forceinline__ void st_c(float *m, int ld, int r0, int c0, int lane, const f4 &v) {
+  float *p = m + (r0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
+  p[0] = v[0];
+  p[ld] = v[1];
+  p[2 * ld] = v[2];
+  p[3 * ld] = v[3];
+}
+
+// Sum over the 16 lanes that share a row of a C-layout tile.
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+// Sum over the 4 lane groups that share a column of a C-layout tile.
+__device__ __forceinline__ float sum4g(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+__device__ __forceinline__ float sum64(float x) { return sum4g(sum16(x)); }
+
+template <typename IT>
+__device__ __forceinline__ void load16(const IT *p, float (&v)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = (float)p[j];
+}
+
+// The chunk's rows in LDS: keys x_i (features), queries qh_i and the per-row
+// scalars.  Thread (row r = tid / 4, quarter p = tid % 4) takes 16 channels.
+struct RowScalars {
+  float L[C], Lm[C], eta[C], en[C];  // L_i, L_{i-1}, eta_i, eps_eta + |x_i|^2
+};
+
+template <typename IT>
+__device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, RowScalars &rs) {
+  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3, lane = tid & 63;
+  const int b = n / a.H, h = n % a.H;
+  const int t = c * C + r;
+  const int kt = t - 1 + a.align;  // key index of the pair written at step t
+  const bool live = t < a.T;
+  float x[16], q[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) x[j] = q[j] = 0.f;
+  const bool key_row = live && kt >= 0;
+  if (key_row) load16((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + 16 * p, x);
+  else if (live && a.xprev0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = a.xprev0[(size_t)n * D + 16 * p + j];  // the carried feature
+  }
+  if (live) load16((const IT *)a.q + ((size_t)(b * a.T + t) * a.H + h) * D + 16 * p, q);
+  float sx = 0.f, sq = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    sx += x[j] * x[j];
+    sq += q[j] * q[j];
+  }
+  sx += __shfl_xor(sx, 1);
+  sx += __shfl_xor(sx, 2);
+  sq += __shfl_xor(sq, 1);
+  sq += __shfl_xor(sq, 2);
+  const float ix = key_row ? 1.f / sqrtf(sx + a.eps_phi) : 1.f;
+  const float iq = 1.f / sqrtf(sq + a.eps_phi);
+  float e = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    x[j] *= ix;
+    q[j] = live ? q[j] * iq : 0.f;
+    e += x[j] * x[j];
+  }
+  e += __shfl_xor(e, 1);
+  e += __shfl_xor(e, 2);
+#pragma unroll
+  for (int j = 0; j < 16; j += 4) {
+    *reinterpret_cast<f4 *>(sX + r * LD + 16 * p + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+    *reinterpret_cast<f4 *>(sQ + r * LD + 16 * p + j) = f4{q[j], q[j + 1], q[j + 2], q[j + 3]};
+  }
+  if (p == 0) {
+    const size_t gi = (size_t)(b * a.T + t) * a.H + h;
+    const float en = a.eps_eta + e;
+    rs.en[r] = en;
+    rs.eta[r] = live ? a.beta[gi] / en : 0.f;
+    rs.L[r] = live ? fmaxf(a.g[gi], a.log_eps_gamma) : 0.f;  // log-decay, summed below
+  }
+  __syncthreads();
+  if (tid < 64) {  // inclusive prefix sum of the log-decays along the chunk
+    float l = rs.L[lane];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(l, o);
+      if (lane >= o) l += y;
+    }
+    const float lm = __shfl_up(l, 1);
+    rs.L[lane] = l;
+    rs.Lm[lane] = lane ? lm : 0.f;
+  }
+  __syncthreads();
+}
+
+// A (row tile w; zero for F1A) and P (row tile w) into LDS, with their masks.
+template <bool ADD>
+__device__ void gram_tiles(const float *sX, const float *sQ, float *sA, float *sP, const RowScalars &rs, int w,
+                           int lane) {
+  const int g = lane >> 4, cc = lane & 15;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    f4 pa = zero4(), pp = zero4();
+    if (ct <= w) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f4 xb = b_tr(sX, LD, 16 * kb, 16 * ct, lane);
+        if (!ADD) mma16(pa, a_rm(sX, LD, 16 * w, 16 * kb, lane), xb);
+        mma16(pp, a_rm(sQ, LD, 16 * w, 16 * kb, lane), xb);
+      }
+    }
+    const int col = 16 * ct + cc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * w + 4 * g + i;
+      pa[i] = col < row ? __expf(rs.Lm[row] - rs.L[col]) * pa[i] : 0.f;
+      pp[i] = col <= row ? __expf(rs.L[row] - rs.L[col]) * pp[i] : 0.f;
+    }
+    if (!ADD) st_c(sA, LD, 16 * w, 16 * ct, lane, pa);
+    st_c(sP, LD, 16 * w, 16 * ct, lane, pp);
+  }
+}
+
+// Inverse of the unit lower-triangular diagonal block w of M = I + A diag(eta),
+// by forward substitution: lane j < 16 solves for column j.
+__device__ void diag_inverse(const float *sA, float *sT, const RowScalars &rs, int w, int lane) {
+  if (lane < 16) {
+    const int base = 16 * w;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = r == lane ? 1.f : 0.f;
+#pragma unroll
+      for (int q = 0; q < r; ++q) s -= sA[(base + r) * LD + base + q] * rs.eta[base + q] * t[q];
+      t[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[w * 16 * TL + r * TL + lane] = t[r];
+  }
+}
+
+// Y <- M^-1 Y for one 16-column tile held by a wave (blocked forward substitution).
+__device__ void solve_lower(f4 (&y)[4], const float *sA, const float *sT, const RowScalars &rs, int lane) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f4 s = zero4();
+#pragma unroll
+    for (int bp = 0; bp < b; ++bp) {
+      f4 af = a_rm(sA, LD, 16 * b, 16 * bp, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] *= rs.eta[16 * bp + 4 * g + i];
+      mma16(s, af, y[bp]);
+    }
+    const f4 r = y[b] - s;
+    y[b] = zero4();
+    mma16(y[b], a_rm(sT + b * 16 * TL, TL, 0, 0, lane), r);
+  }
+}
+
+// Y <- M^-T Y (blocked backward substitution).
+__device__ void solve_upper(f4 (&y)[4], const float *sA, const float *sT, const RowScalars &rs, int lane) {
+  const int cc = lane & 15;
+#pragma unroll
+  for (int b = 3; b >= 0; --b) {
+    f4 s = zero4();
+#pragma unroll
+    for (int bp = b + 1; bp < 4; ++bp) {
+      f4 af = a_tr(sA, LD, 16 * b, 16 * bp, lane);
+      af *= rs.eta[16 * b + cc];
+      mma16(s, af, y[bp]);
+    }
+    const f4 r = y[b] - s;
+    y[b] = zero4();
+    mma16(y[b], a_tr(sT + b * 16 * TL, TL, 0, 0, lane), r);
+  }
+}
+
+// Rows 0..63 of a [C][64] input-typed array (rows past T are zero) into LDS as fp32.
+template <typename IT>
+__device__ void load_mat(const IT *base, size_t row_stride, int rows_live, float *dst) {
+  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
+  float v[16];
+  if (r < rows_live) load16(base + (size_t)r * row_stride + 16 * p, v);
+  else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; j += 4)
+    *reinterpret_cast<f4 *>(dst + r * LD + 16 * p + j) = f4{v[j], v[j + 1], v[j + 2], v[j + 3]};
+}
+
+// Workspace arrays of one chunk.
+struct WsPtr {
+  float *X, *W, *Z, *G, *dec;
+};
+__device__ __forceinline__ WsPtr ws_of(const BwdArgs &a, size_t chunk_id) {
+  const size_t nch = (size_t)a.B * a.H * a.NC;
+  float *base = a.ws;
+  WsPtr p;
+  p.X = base + chunk_id * C * D;
+  p.W = base + nch * C * D + chunk_id * C * D;
+  p.Z = base + 2 * nch * C * D + chunk_id * D * D;
+  p.G = base + 3 * nch * C * D + chunk_id * D * D;
+  p.dec = base + 4 * nch * C * D + chunk_id;
+  return p;
+}
+
+// ---- bwd_prep -------------------------------------------------------------------
+template <typename IT, bool ADD>
+__global__ __launch_bounds__(NT) void bwd_prep(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[MAT], sP[MAT], sO[MAT];
+  __shared__ __attribute__((aligned(16))) float sT[4 * 16 * TL];
+  __shared__ RowScalars rs;
+  const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
+  const int b = n / a.H, h = n % a.H;
+  const int live = min(C, a.T - c * C);
+  load_mat((const IT *)a.dO + ((size_t)(b * a.T + c * C) * a.H + h) * D, (size_t)a.H * D, live, sO);
+  load_rows<IT>(a, n, c, sX, sQ, rs);  // ends with a barrier
+  const WsPtr ws = ws_of(a, blockIdx.x);
+  const float LC = rs.L[C - 1];
+
+  f4 qe[4];  // diag(e^L) Qh - P diag(eta) W, column tile w (key channels)
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    qe[rt] = b_rm(sQ, LD, 16 * rt, 16 * w, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qe[rt][i] *= __expf(rs.L[16 * rt + 4 * g + i]);
+  }
+  if (!ADD) {
+    gram_tiles<false>(sX, sQ, sA, sP, rs, w, lane);
+    __syncthreads();
+    diag_inverse(sA, sT, rs, w, lane);
+    __syncthreads();
+    f4 W[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      W[rt] = b_rm(sX, LD, 16 * rt, 16 * w, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) W[rt][i] *= __expf(rs.Lm[16 * rt + 4 * g + i]);
+    }
+    solve_lower(W, sA, sT, rs, lane);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f4 s = zero4();
+#pragma unroll
+      for (int kb = 0; kb <= rt; ++kb) {
+        f4 af = a_rm(sP, LD, 16 * rt, 16 * kb, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] *= rs.eta[16 * kb + 4 * g + i];
+        mma16(s, af, W[kb]);
+      }
+      qe[rt] -= s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * rt + 4 * g + i;
+        ws.W[row * D + 16 * w + cc] = rs.eta[row] * __expf(LC - rs.L[row]) * W[rt][i];
+      }
+    }
+  }
+  // Z = do^T qe: value-channel rows, key-channel column tile w.
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f4 z = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mma16(z, a_tr(sO, LD, 16 * rt, 16 * kb, lane), qe[kb]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.Z[(16 * rt + 4 * g + i) * D + 16 * w + cc] = z[i];
+  }
+  if (!ADD) {
+    const int r = threadIdx.x >> 2, p = threadIdx.x & 3;
+#pragma unroll
+    for (int j = 0; j < 16; j += 4)
+      *reinterpret_cast<f4 *>(ws.X + r * D + 16 * p + j) = *reinterpret_cast<const f4 *>(sX + r * LD + 16 * p + j);
+  }
+  if (threadIdx.x == 0) *ws.dec = __expf(LC);
+}
+
+// ---- bwd_scan -------------------------------------------------------------------
+// Workgroup (sequence n, value rows 16s..16s+15); wave w holds key columns 16w..+15.
+template <bool ADD>
+__global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[MAT], sW[MAT], sG[16 * LD], sY[16 * LD];
+  const int n = blockIdx.x >> 2, s = blockIdx.x & 3;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
+  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
+  const size_t tile = (size_t)(16 * s + 4 * g) * D + 16 * w + cc;  // + i * D
+  f4 G = zero4();
+  if (a.dST) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) G[i] = a.dST[(size_t)n * D * D + tile + i * D];
+  }
+  for (int c = a.NC - 1; c >= 0; --c) {
+    const WsPtr ws = ws_of(a, (size_t)n * a.NC + c);
+    f4 Z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ws.G[tile + i * D] = G[i];  // gradient at the end of chunk c
+      Z[i] = ws.Z[tile + i * D];
+    }
+    const float dec = *ws.dec;
+    if (ADD) {
+      G = dec * G + Z;
+      continue;
+    }
+    __syncthreads();  // the previous chunk's readers are done with sX, sW, sG, sY
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      *reinterpret_cast<f4 *>(sX + r * LD + 16 * p + j) = *reinterpret_cast<const f4 *>(ws.X + r * D + 16 * p + j);
+      *reinterpret_cast<f4 *>(sW + r * LD + 16 * p + j) = *reinterpret_cast<const f4 *>(ws.W + r * D + 16 * p + j);
+    }
+    st_c(sG, LD, 0, 16 * w, lane, G);
+    __syncthreads();
+    f4 y = zero4();  // (G X^T) tile: chunk rows 16w..16w+15
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mma16(y, a_rm(sG, LD, 0, 16 * kb, lane), b_tr(sX, LD, 16 * kb, 16 * w, lane));
+    st_c(sY, LD, 0, 16 * w, lane, y);
+    __syncthreads();
+    f4 u = zero4();  // (G X^T) diag(b) W
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mma16(u, a_rm(sY, LD, 0, 16 * kb, lane), b_rm(sW, LD, 16 * kb, 16 * w, lane));
+    G = dec * G - u + Z;
+  }
+  if (a.dS0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a.dS0[(size_t)n * D * D + tile + i * D] = G[i];
+  }
+}
+
+// ---- bwd_chunk ------------------------------------------------------------------
+template <typename IT, bool ADD>
+__global__ __launch_bounds__(NT) void bwd_chunk(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[MAT], sP[MAT], sE[MAT],
+      sO[MAT];
+  __shared__ __attribute__((aligned(16))) float sT[4 * 16 * TL];
+  __shared__ RowScalars rs;
+  __shared__ float pL[4][C], pE[4][C], pC[4], sCoef[C];
+  const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
+  const int b = n / a.H, h = n % a.H;
+  const int live = min(C, a.T - c * C);
+  const size_t row0 = (size_t)(b * a.T + c * C) * a.H + h;  // (b, t0, h)
+  const WsPtr ws = ws_of(a, blockIdx.x);
+
+  // Phase 0: rows, the incoming state S0, the end-state gradient G, do.
+  load_mat((const IT *)a.dO + row0 * D, (size_t)a.H * D, live, sO);
+  {
+    const float *S0 = c ? a.chunk_states + ((size_t)n * a.NC + c - 1) * D * D : (a.S0 ? a.S0 + (size_t)n * D * D : nullptr);
+    const int r = tid >> 2, p = tid & 3;
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      *reinterpret_cast<f4 *>(sS + r * LD + 16 * p + j) =
+          S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 16 * p + j) : zero4();
+      *reinterpret_cast<f4 *>(sG + r * LD + 16 * p + j) = *reinterpret_cast<const f4 *>(ws.G + r * D + 16 * p + j);
+    }
+    pL[w][lane] = 0.f;
+    pE[w][lane] = 0.f;
+  }
+  f4 V[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      V[rt][i] = row < live ? (float)((const IT *)a.v)[(row0 + (size_t)row * a.H) * D + 16 * w + cc] : 0.f;
+    }
+  }
+  load_rows<IT>(a, n, c, sX, sQ, rs);  // ends with a barrier
+  const float LC = rs.L[C - 1];
+  float lc = 0.f;  // this lane's share of dL_C
+
+  {  // e^{L_C} <G, S0>
+    const int r = tid >> 2, p = tid & 3;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += sG[r * LD + 16 * p + j] * sS[r * LD + 16 * p + j];
+    lc += __expf(LC) * s;
+  }
+
+  // Phase 1: A and P; R = V - diag(e^Lm) X S0^T; dQh from the first read term; Y = X G^T.
+  gram_tiles<ADD>(sX, sQ, sA, sP, rs, w, lane);
+  f4 dO[4], E[4], dQ[4], Y[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) dO[rt] = b_rm(sO, LD, 16 * rt, 16 * w, lane);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f4 xs = zero4(), dq = zero4(), y = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f4 xa = a_rm(sX, LD, 16 * rt, 16 * kb, lane);
+      if (!ADD) mma16(xs, xa, b_tr(sS, LD, 16 * kb, 16 * w, lane));
+      mma16(y, xa, b_tr(sG, LD, 16 * kb, 16 * w, lane));
+      mma16(dq, a_rm(sO, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * w, lane));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      E[rt][i] = ADD ? V[rt][i] : V[rt][i] - __expf(rs.Lm[row]) * xs[i];
+      dQ[rt][i] = __expf(rs.L[row]) * dq[i];
+      const float part = sum16(sQ[row * LD + 16 * w + cc] * dQ[rt][i]);  // qh_i . dQh_i
+      if (cc == 0) pL[w][row] += part;
+    }
+    Y[rt] = y;
+  }
+
+  // Phase 2-3: E = M^-1 R.
+  if (!ADD) {
+    __syncthreads();
+    diag_inverse(sA, sT, rs, w, lane);
+    __syncthreads();
+    solve_lower(E, sA, sT, rs, lane);
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    st_c(sE, LD, 16 * rt, 16 * w, lane, E[rt]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // db_i = E_i . (G x_i): into d eta_i, dL_i and dL_C
+      const int row = 16 * rt + 4 * g + i;
+      const float db = sum16(E[rt][i] * Y[rt][i]);
+      const float f = __expf(LC - rs.L[row]);
+      if (cc == 0) {
+        pE[w][row] += db * f;
+        pL[w][row] -= db * rs.eta[row] * f;
+        lc += db * rs.eta[row] * f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Phase 4: Z = P^T do; dE = diag(b) Y + diag(eta) Z; dX = diag(b) E G.
+  f4 dE[4], dX[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f4 z = zero4(), u = zero4();
+#pragma unroll
+    for (int kb = rt; kb < 4; ++kb) mma16(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), dO[kb]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mma16(u, a_rm(sE, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * w, lane));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      const float bb = rs.eta[row] * __expf(LC - rs.L[row]);
+      dE[rt][i] = bb * Y[rt][i] + rs.eta[row] * z[i];
+      dX[rt][i] = bb * u[i];
+      const float de = sum16(z[i] * E[rt][i]);
+      if (cc == 0) pE[w][row] += de;
+    }
+  }
+
+  // Phase 5: dR = M^-T dE (= dv); F1A: dv = dE.
+  if (!ADD) solve_upper(dE, sA, sT, rs, lane);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      if (row < live) a.dv[(row0 + (size_t)row * a.H) * D + 16 * w + cc] = dE[rt][i];
+    }
+  }
+  __syncthreads();  // every wave is done reading G and A
+  if (!ADD) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) st_c(sG, LD, 16 * rt, 16 * w, lane, dE[rt]);  // sG now holds dR
+  }
+  __syncthreads();
+
+  // Phase 6: dR S0 (into dX and dL_{i-1}); dA from dR E^T; dP from do (diag(eta) E)^T.
+  if (!ADD) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f4 s = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma16(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * w, lane));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * rt + 4 * g + i;
+        const float am = __expf(rs.Lm[row]);
+        dX[rt][i] -= am * s[i];
+        const float part = sum16(sX[row * LD + 16 * w + cc] * s[i]);
+        if (cc == 0 && row > 0) pL[w][row - 1] -= am * part;
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    if (ct > w) continue;
+    f4 t = zero4(), u = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f4 eb = b_tr(sE, LD, 16 * kb, 16 * ct, lane);
+      if (!ADD) mma16(t, a_rm(sG, LD, 16 * w, 16 * kb, lane), eb);
+      mma16(u, a_rm(sO, LD, 16 * w, 16 * kb, lane), eb);
+    }
+    const int col = 16 * ct + cc;
+    const float etac = rs.eta[col];
+    float colL = 0.f, colE = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * w + 4 * g + i;
+      float rowL = 0.f, rowLm = 0.f;
+      if (!ADD) {
+        const float Aij = sA[row * LD + col];
+        const float dM = col < row ? -t[i] : 0.f;
+        colE += Aij * dM;
+        const float dA = dM * etac;
+        const float H = dA * Aij;
+        rowLm += H;
+        colL -= H;
+        sA[row * LD + col] = col < row ? dA * __expf(rs.Lm[row] - rs.L[col]) : 0.f;
+      }
+      const float dP = col <= row ? u[i] * etac : 0.f;
+      const float HP = dP * sP[row * LD + col];
+      rowL += HP;
+      colL -= HP;
+      sP[row * LD + col] = col <= row ? dP * __expf(rs.L[row] - rs.L[col]) : 0.f;
+      rowL = sum16(rowL);
+      rowLm = sum16(rowLm);
+      if (cc == 0) {
+        pL[w][row] += rowL;
+        if (row > 0) pL[w][row - 1] += rowLm;
+      }
+    }
+    colL = sum4g(colL);
+    colE = sum4g(colE);
+    if (g == 0) {
+      pL[w][col] += colL;
+      pE[w][col] += colE;
+    }
+  }
+  __syncthreads();
+
+  // Phase 7: dQh += dPD X; dX += dPD^T Qh + dAG X + dAG^T X.
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f4 xb = b_rm(sX, LD, 16 * kb, 16 * w, lane);
+      if (kb <= rt) {
+        mma16(dQ[rt], a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
+        if (!ADD) mma16(dX[rt], a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
+      }
+      if (kb >= rt) {
+        mma16(dX[rt], a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * w, lane));
+        if (!ADD) mma16(dX[rt], a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
+      }
+    }
+  }
+  lc = sum64(lc);
+  if (lane == 0) pC[w] = lc;
+  __syncthreads();
+
+  // Phase 8: per-row totals; dL -> d(log-decay) by a reverse sum; beta and the |x|^2 term.
+  if (w == 0) {
+    const int i = lane;
+    const float de = pE[0][i] + pE[1][i] + pE[2][i] + pE[3][i];
+    float dl = pL[0][i] + pL[1][i] + pL[2][i] + pL[3][i];
+    if (i == C - 1) dl += pC[0] + pC[1] + pC[2] + pC[3];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_down(dl, o);
+      if (i + o < 64) dl += y;
+    }
+    if (i < live) {
+      const size_t gi = row0 + (size_t)i * a.H;
+      a.dbeta[gi] = de / rs.en[i];
+      a.dg[gi] = a.g[gi] > a.log_eps_gamma ? dl : 0.f;
+    }
+    sCoef[i] = -2.f * de * rs.eta[i] / rs.en[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      dX[rt][i] += sCoef[row] * sX[row * LD + 16 * w + cc];
+    }
+    st_c(sO, LD, 16 * rt, 16 * w, lane, dQ[rt]);
+    st_c(sE, LD, 16 * rt, 16 * w, lane, dX[rt]);
+  }
+  __syncthreads();
+
+  // Through the feature map: dq_t for t < T; dk of the key row i carries.
+  {
+    const int r = tid >> 2, p = tid & 3;
+    const int t = c * C + r;
+    float v[16], d[16];
+    if (t < a.T) {
+      load16((const IT *)a.q + (row0 + (size_t)r * a.H) * D + 16 * p, v);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) d[j] = sO[r * LD + 16 * p + j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = d[j] = 0.f;
+    }
+    float nn = 0.f, dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      nn += v[j] * v[j];
+      dot += v[j] * d[j];
+    }
+    nn += __shfl_xor(nn, 1);
+    nn += __shfl_xor(nn, 2);
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    float inv = 1.f / sqrtf(nn + a.eps_phi);
+    float inv3 = inv * inv * inv;
+    if (t < a.T) {
+      float *dst = a.dq + (row0 + (size_t)r * a.H) * D + 16 * p;
+#pragma unroll
+      for (int j = 0; j < 16; j += 4)
+        *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
+                                              d[j + 2] * inv - v[j + 2] * dot * inv3,
+                                              d[j + 3] * inv - v[j + 3] * dot * inv3};
+    }
+    // key of row r: k_{t-1+align}; rows at t == T (prefix) carry k_{T-1}, whose gradient is 0.
+    const int kt = t - 1 + a.align;
+    const bool key_row = kt >= 0 && kt < a.T && t <= a.T - a.align;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) d[j] = sE[r * LD + 16 * p + j];
+    if (key_row) load16((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + 16 * p, v);
+    else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = 0.f;
+    }
+    nn = 0.f;
+    dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      nn += v[j] * v[j];
+      dot += v[j] * d[j];
+    }
+    nn += __shfl_xor(nn, 1);
+    nn += __shfl_xor(nn, 2);
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    inv = 1.f / sqrtf(nn + a.eps_phi);
+    inv3 = inv * inv * inv;
+    if (key_row) {
+      float *dst = a.dk + ((size_t)(b * a.T + kt) * a.H + h) * D + 16 * p;
+#pragma unroll
+      for (int j = 0; j < 16; j += 4)
+        *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
+                                              d[j + 2] * inv - v[j + 2] * dot * inv3,
+                                              d[j + 3] * inv - v[j + 3] * dot * inv3};
+    }
+    if (t == 0 && a.dxprev0) {  // the carried feature x_prev enters row 0 directly (prefix); unread (same step)
+      float *dst = a.dxprev0 + (size_t)n * D + 16 * p;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dst[j] = a.align ? 0.f : d[j];
+    }
+    // Prefix pairing with T a multiple of C: k_{T-1} has no row here; its gradient is 0.
+    if (!a.align && c == a.NC - 1 && a.T % C == 0 && r == 0) {
+      float *dst = a.dk + ((size_t)(b * a.T + a.T - 1) * a.H + h) * D + 16 * p;
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) *reinterpret_cast<f4 *>(dst + j) = zero4();
+    }
+  }
+}
+
+template <typename IT, bool ADD>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
+  const unsigned nch = (unsigned)a.B * a.H * a.NC;
+  hipLaunchKernelGGL((bwd_prep<IT, ADD>), dim3(nch), dim3(NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_scan<ADD>), dim3((unsigned)a.B * a.H * 4), dim3(NT), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_chunk<IT, ADD>), dim3(nch), dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunk_bwd_supported(int variant, int dk, int dv, int chunk, int window) {
+  return (variant == 1 || variant == 2) && dk == D && dv == D && chunk == C && window == 1;
+}
+
+size_t chunk_bwd_workspace(int B, int H, int T) {
+  const size_t nch = (size_t)B * H * ((T + C - 1) / C);
+  return (4 * nch * C * D + nch) * sizeof(float);
+}
+
+hipError_t launch_chunk_bwd(int variant, bool bf16, const BwdArgs &a, hipStream_t st) {
+  const bool add = variant == 2;
+  if (bf16) return add ? launch_bwd_t<__bf16, true>(a, st) : launch_bwd_t<__bf16, false>(a, st);
+  return add ? launch_bwd_t<float, true>(a, st) : launch_bwd_t<float, false>(a, st);
+}
+
+}  // namespace falcon

@@ -37,6 +37,23 @@ struct StepArgs {
   float log_eps_gamma, eps_phi, eps_eta;
 };
 
+// Everything the backward pass of the chunked form needs (F1 / F1A, d = 64,
+// chunk 64), already validated by the host.
+struct BwdArgs {
+  const void *q, *k, *v, *dO;    // [B,T,H,64] in the input dtype
+  const float *beta, *g;         // [B,T,H]
+  const float *S0, *xprev0;      // incoming S [B,H,64,64] and x_prev [B,H,64], or null (zeros)
+  const float *chunk_states;     // [B,H,NC,64,64]: S at the end of every chunk (the forward's)
+  const float *dST;              // [B,H,64,64] gradient w.r.t. S_T, or null (zero)
+  float *dq, *dk, *dv;           // [B,T,H,64] fp32
+  float *dbeta, *dg;             // [B,T,H] fp32
+  float *dS0, *dxprev0;          // [B,H,64,64], [B,H,64] or null
+  float *ws;                     // chunk_bwd_workspace(B, H, T) bytes
+  int B, T, H, NC;
+  int align;
+  float log_eps_gamma, eps_phi, eps_eta;
+};
+
 // Return hipSuccess or the launch error.  `variant` is falcon_variant_t,
 // `bf16` selects the input dtype.  Unsupported combinations return
 // hipErrorInvalidValue (the host validates first, so this is a safety net).
@@ -44,6 +61,10 @@ hipError_t launch_chunk_fwd(int variant, bool bf16, int dk, int dv, int chunk, i
                             const FwdArgs &a, hipStream_t stream);
 hipError_t launch_tail(int variant, bool bf16, int dk, int dv, const FwdArgs &a, hipStream_t stream);
 hipError_t launch_step(int variant, bool bf16, int dk, int dv, const StepArgs &a, hipStream_t stream);
+
+bool chunk_bwd_supported(int variant, int dk, int dv, int chunk, int window);
+size_t chunk_bwd_workspace(int B, int H, int T);
+hipError_t launch_chunk_bwd(int variant, bool bf16, const BwdArgs &a, hipStream_t stream);
 
 // The per-shape d_v split of the forward kernel (channels per workgroup = dv / nsplit).
 int choose_nsplit(int variant, bool bf16, int dk, int dv, int chunk, int batch_heads);

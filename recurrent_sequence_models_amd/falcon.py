@@ -21,7 +21,8 @@ PER_CHANNEL = ("F2", "F2A")
 WINDOWED = ("F3", "F3A")
 
 EXPORTS = ("falcon_abi_version", "falcon_status_string", "falcon_chunk_fwd_workspace",
-           "falcon_chunk_fwd", "falcon_chunk_fwd_varlen", "falcon_recurrent_step")
+           "falcon_chunk_fwd", "falcon_chunk_fwd_varlen", "falcon_recurrent_step",
+           "falcon_chunk_bwd_workspace", "falcon_chunk_bwd")
 
 
 class Shape(ctypes.Structure):
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.falcon_chunk_fwd_varlen.argtypes = [P(Shape), V, V, V, V, V, V, P(State), P(State), V, V]
         L.falcon_recurrent_step.restype = I
         L.falcon_recurrent_step.argtypes = [P(Shape), V, V, V, V, V, P(State), V, V]
+        L.falcon_chunk_bwd_workspace.restype = S
+        L.falcon_chunk_bwd_workspace.argtypes = [P(Shape)]
+        L.falcon_chunk_bwd.restype = I
+        L.falcon_chunk_bwd.argtypes = [P(Shape), V, V, V, V, V, P(State), V, V, V, V, V, V, V, V, P(State),
+                                       V, S, V]
         _LIB = L
     return _LIB
 
@@ -263,3 +269,70 @@ def recurrent_step(variant, q, k, v, beta, log_lambda, state, *, window=1, eps_g
     if status != OK:
         raise FalconError(status, "falcon_recurrent_step")
     return out
+
+
+def bwd_workspace_bytes(variant, dtype, batch, seqlen, heads, dk, dv, chunk=64, eps_gamma=1e-3, eps_phi=1e-6,
+                        eps_eta=1e-6, align="prefix"):
+    """falcon_chunk_bwd_workspace for a shape (0: the backward pass is not built for it)."""
+    shape = make_shape(variant, dtype, batch, seqlen, heads, dk, dv, chunk, 1, eps_gamma, eps_phi, eps_eta, align)
+    return int(lib().falcon_chunk_bwd_workspace(ctypes.byref(shape)))
+
+
+def chunk_bwd(variant, q, k, v, beta, log_lambda, do, chunk_states, *, init=None, dS_T=None, chunk=64,
+              eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix", d_init=True, out=None,
+              workspace=None, stream=None):
+    """falcon_chunk_bwd on torch tensors: gradients of <do, o> + <dS_T, S_T>.
+
+    ``chunk_states`` is what ``chunk_fwd(..., chunk_states=True)`` returned for
+    the same inputs and ``init``.  ``do`` has the dtype of q; ``dS_T`` is None or
+    [B,H,dv,dk] float32.  ``d_init``: True (allocate), a state dict to write, or
+    False.  ``out``: None or a dict of preallocated dq, dk, dv, dbeta, dg.
+    ``workspace``: None (allocate) or a uint8 device tensor.
+    Returns dict(dq, dk, dv, dbeta, dg, dS0, dx_prev0) (the last two None when
+    ``d_init`` is False)."""
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = {torch.float32: "fp32", torch.bfloat16: "bf16"}.get(q.dtype)
+    if dt is None:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    _check_tensor("q", q, q.dtype, (B, T, H, dk), dev)
+    _check_tensor("k", k, q.dtype, (B, T, H, dk), dev)
+    _check_tensor("v", v, q.dtype, (B, T, H, dv), dev)
+    _check_tensor("do", do, q.dtype, (B, T, H, dv), dev)
+    _check_tensor("beta", beta, torch.float32, (B, T, H), dev)
+    _check_tensor("log_lambda", log_lambda, torch.float32, (B, T, H), dev)
+    nch = (T + chunk - 1) // chunk
+    _check_tensor("chunk_states", chunk_states, torch.float32, (B, H, nch, dv, dk), dev)
+    if dS_T is not None:
+        _check_tensor("dS_T", dS_T, torch.float32, (B, H, dv, dk), dev)
+    if out is None:
+        out = dict(dq=torch.empty(B, T, H, dk, device=dev), dk=torch.empty(B, T, H, dk, device=dev),
+                   dv=torch.empty(B, T, H, dv, device=dev), dbeta=torch.empty(B, T, H, device=dev),
+                   dg=torch.empty(B, T, H, device=dev))
+    for name, shp in (("dq", (B, T, H, dk)), ("dk", (B, T, H, dk)), ("dv", (B, T, H, dv)),
+                      ("dbeta", (B, T, H)), ("dg", (B, T, H))):
+        _check_tensor(name, out[name], torch.float32, shp, dev)
+    if d_init is True:
+        d_init = new_state(B, H, dk, dv, 1, dev)
+    elif d_init is False:
+        d_init = None
+    shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, 1, eps_gamma, eps_phi, eps_eta, align)
+    L = lib()
+    need = int(L.falcon_chunk_bwd_workspace(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check_tensor("workspace", workspace, torch.uint8, (workspace.numel(),), dev)
+    st_in, st_d = _state(init), _state(d_init)
+    status = L.falcon_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_lambda),
+                                ctypes.byref(st_in) if st_in else None, _ptr(chunk_states), _ptr(do), _ptr(dS_T),
+                                _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+                                _ptr(out["dg"]), ctypes.byref(st_d) if st_d else None,
+                                _ptr(workspace), workspace.numel(), _stream(stream))
+    if status != OK:
+        raise FalconError(status, "falcon_chunk_bwd")
+    res = dict(out)
+    res["dS0"] = d_init["S"] if d_init else None
+    res["dx_prev0"] = d_init["x_prev"] if d_init else None
+    return res

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = F.lib()
-    assert L.falcon_abi_version() == 2
+    assert L.falcon_abi_version() == 3
     for code in range(5):
         s = F.status_string(code)
         assert s.startswith("FALCON_")
@@ -189,3 +189,48 @@ def test_varlen_rejects_on_host():
     assert call_varlen(good_shape(seqlen=500, dtype="fp32", dk=64, dv=64, chunk=64)) == F.ERR_UNSUPPORTED
     assert call_varlen(good_shape(seqlen=500, dk=128, dv=128)) == F.ERR_UNSUPPORTED
     assert call_varlen(good_shape(seqlen=500, variant="F3", window=4, chunk=32)) == F.ERR_UNSUPPORTED
+
+
+def bwd_workspace(**kw):
+    return F.lib().falcon_chunk_bwd_workspace(ctypes.byref(good_shape(**kw)))
+
+
+def call_bwd(shape, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, init=None, cs=FAKE, do=FAKE, dST=None,
+             dq=FAKE, dk=FAKE, dv=FAKE, dbeta=FAKE, dg=FAKE, d_init=None, ws=FAKE, wsb=1 << 40):
+    L = F.lib()
+    return L.falcon_chunk_bwd(ctypes.byref(shape) if shape is not None else None, q, k, v, beta, g,
+                              ctypes.byref(init) if init else None, cs, do, dST, dq, dk, dv, dbeta, dg,
+                              ctypes.byref(d_init) if d_init else None, ws, wsb, None)
+
+
+def test_bwd_workspace_size():
+    """Per chunk of 64 steps: keys, the scaled WY factor, the injected state
+    gradient and the end-of-chunk state gradient (4 x 64 x 64 fp32) plus the
+    chunk's decay; F1 and F1A at d = 64, chunk 64 only."""
+    per_chunk = 4 * 64 * 64 * 4 + 4
+    assert bwd_workspace(seqlen=64, batch=1, heads=1) == per_chunk
+    assert bwd_workspace(seqlen=100) == 2 * 3 * 2 * per_chunk
+    assert bwd_workspace(seqlen=129, variant="F1A", dtype="fp32") == 2 * 3 * 3 * per_chunk
+    for kw in (dict(variant="F2"), dict(variant="F2A"), dict(variant="F3", window=2), dict(variant="F3A"),
+               dict(dk=32, dv=32), dict(dk=128, dv=128), dict(chunk=32), dict(batch=0)):
+        assert bwd_workspace(**kw) == 0, kw
+
+
+@cpu_only
+def test_bwd_rejects_on_host():
+    ok = good_shape()
+    assert call_bwd(None) == F.ERR_INVALID_ARG
+    for kw in INVALID_SHAPES:
+        assert call_bwd(good_shape(**kw)) == F.ERR_INVALID_ARG, kw
+    for name in ("q", "k", "v", "beta", "g", "cs", "do", "dq", "dk", "dv", "dbeta", "dg", "ws"):
+        assert call_bwd(ok, **{name: None}) == F.ERR_INVALID_ARG, name
+    for name in ("q", "k", "v", "do", "cs", "dq", "dk", "dv", "dST", "ws"):
+        assert call_bwd(ok, **{name: ctypes.c_void_p(0x10008)}) == F.ERR_INVALID_ARG, name
+    for name in ("g", "dbeta", "dg"):
+        assert call_bwd(ok, **{name: ctypes.c_void_p(0x10002)}) == F.ERR_INVALID_ARG, name
+    assert call_bwd(ok, d_init=F.State(FAKE.value, None, None, None)) == F.ERR_INVALID_ARG
+    assert call_bwd(ok, init=F.State(None, FAKE.value, None, None)) == F.ERR_INVALID_ARG
+    for kw in (dict(variant="F2"), dict(variant="F3", window=2), dict(dk=32, dv=32), dict(chunk=32),
+               dict(dk=128, dv=128)):
+        assert call_bwd(good_shape(**kw)) == F.ERR_UNSUPPORTED, kw
+    assert call_bwd(ok, wsb=bwd_workspace() - 1) == F.ERR_WORKSPACE
