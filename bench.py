@@ -16,6 +16,10 @@ built, else the fused kernel); "split" passes a workspace (allocated once
 outside the timed region): the prep kernel over all systems, then the state
 scan.  "auto" (default) takes the faster one measured per shape class: split
 for Falcon-3 windows and head dim 128, one-pass otherwise.
+
+--backward times falcon_chunk_bwd instead (Falcon-1 or 1A at the 130M-layer
+shape): the gradients of every input from the forward's per-chunk states,
+which are computed once outside the timed region.
 """
 
 from __future__ import annotations
@@ -118,6 +122,141 @@ def bench_decode(args):
     }
 
 
+MFMA_FP32_PEAK_TFS = 157.3    # MI355X dense fp32 MFMA
+
+
+def bwd_flops(w, variant):
+    """Algorithmic flops of one backward call, per chunk of C steps: the chunked
+    products of the adjoint (a triangular C x C product counts half).  With
+    u = 2 C d^2 (C = d): F1 = 15 u (prep 3, scan 2, per-chunk adjoint 10);
+    F1A = 6.5 u (prep 1, adjoint 5.5)."""
+    C, d = w.chunk, w.dk
+    u = 2 * C * d * d
+    per_chunk = {"F1": 15 * u, "F1A": 6.5 * u}[variant]
+    return w.batch * w.heads * (-(-w.seqlen // C)) * per_chunk
+
+
+def bwd_bytes(w):
+    """Algorithmic HBM bytes of one backward call: q, k, v, do in the input
+    dtype, beta and g, the per-chunk states, the fp32 gradients of q, k, v,
+    beta and g, and the final-state gradient and initial-state gradients."""
+    e = 2 if w.dtype == "bf16" else 4
+    nch = -(-w.seqlen // w.chunk)
+    per_th = 4 * w.dk * e + 8 + 3 * w.dk * 4 + 8
+    per_seq = nch * w.dv * w.dk * 4 + 2 * w.dv * w.dk * 4 + w.dk * 4
+    return w.batch * w.heads * (w.seqlen * per_th + per_seq)
+
+
+def cpu_baseline_bwd(w, variant, budget_s=20.0):
+    """Time the oracle's backward (as it stands) on a prefix of the same workload,
+    on one host core; scaled to tokens/s of the full batch."""
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    import oracle
+    import workloads as W
+    inp = W.make_inputs(w, variant, seed=w.seed)
+    cot = W.make_cotangents(w, w.seed + 1)
+    t_probe = 16
+    t0 = time.perf_counter()
+    oracle.recurrent_backward(variant, **{n: a[:, :t_probe] for n, a in inp.items()}, do=cot["do"][:, :t_probe],
+                              dS_T=cot["dS_T"])
+    per_step = (time.perf_counter() - t0) / t_probe
+    T_s = int(max(t_probe, min(w.seqlen, budget_s / max(per_step, 1e-9))))
+    t0 = time.perf_counter()
+    oracle.recurrent_backward(variant, **{n: a[:, :T_s] for n, a in inp.items()}, do=cot["do"][:, :T_s],
+                              dS_T=cot["dS_T"])
+    dt = time.perf_counter() - t0
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    return {"value": w.batch * T_s / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 NumPy reverse-time adjoint (with its forward) over all {w.batch * w.heads} "
+                      f"sequences of the workload, first {T_s} of {w.seqlen} steps ({dt:.1f} s on 1 host core)"}
+
+
+def bench_backward(args):
+    """K timed falcon_chunk_bwd calls over three rotating input sets (inputs,
+    cotangents and the forward's per-chunk states resident in HBM)."""
+    import torch
+    import workloads as W
+    from recurrent_sequence_models_amd import chunk_bwd, chunk_fwd
+    from recurrent_sequence_models_amd.falcon import bwd_workspace_bytes
+    w = W.WORKLOADS[args.workload]
+    variant = args.variant
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    sets = []
+    for i in range(3):
+        inp = W.make_inputs(w, variant, seed=w.seed + i)
+        cot = W.make_cotangents(w, w.seed + 10 + i)
+        d = {n: torch.from_numpy(a).to(dev) for n, a in inp.items()}
+        for n in ("q", "k", "v"):
+            d[n] = d[n].to(tdt).contiguous()
+        d["do"] = torch.from_numpy(cot["do"]).to(dev).to(tdt).contiguous()
+        d["dS_T"] = torch.from_numpy(cot["dS_T"]).to(dev)
+        _, _, d["cs"] = chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk,
+                                  final=False, chunk_states=True)
+        d["out"] = dict(dq=torch.empty(w.batch, w.seqlen, w.heads, w.dk, device=dev),
+                        dk=torch.empty(w.batch, w.seqlen, w.heads, w.dk, device=dev),
+                        dv=torch.empty(w.batch, w.seqlen, w.heads, w.dv, device=dev),
+                        dbeta=torch.empty(w.batch, w.seqlen, w.heads, device=dev),
+                        dg=torch.empty(w.batch, w.seqlen, w.heads, device=dev))
+        d["d_init"] = dict(S=torch.empty(w.batch, w.heads, w.dv, w.dk, device=dev),
+                           x_prev=torch.empty(w.batch, w.heads, w.dk, device=dev))
+        sets.append(d)
+    ws_bytes = bwd_workspace_bytes(variant, w.dtype, w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call(d):
+        chunk_bwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], d["do"], d["cs"], dS_T=d["dS_T"],
+                  chunk=w.chunk, d_init=d["d_init"], out=d["out"], workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        call(sets[i % 3])
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        call(sets[i % 3])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_s = sum(kern_ms) / K / 1e3
+    flops = bwd_flops(w, variant)
+    nbytes = bwd_bytes(w)
+    tfs = flops / avg_s / 1e12
+    line = {
+        "metric": f"tokens/sec, Falcon-{variant[1:]} chunked backward (H={w.heads},d={w.dk},T={w.seqlen}) "
+                  "+ % fp32 MFMA roofline",
+        "value": round(w.batch * w.seqlen / (wall / K), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"Falcon-{variant[1:]} chunked backward, {w.name}: B{w.batch} H{w.heads} "
+                               f"T{w.seqlen} d{w.dk} chunk {w.chunk}, {w.dtype} q/k/v/do, fp32 gradients",
+                   "variant": variant, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
+                   "head_dim": w.dk, "chunk": w.chunk},
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_FP32_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4), "traffic": None,
+                     "kernel": "bwd_prep + bwd_scan + bwd_chunk",
+                     "kernel_us": {"mean": round(avg_s * 1e6, 2), "p10": round(kern_ms[K // 10] * 1e3, 2),
+                                   "p50": round(kern_ms[K // 2] * 1e3, 2),
+                                   "p90": round(kern_ms[(9 * K) // 10] * 1e3, 2)},
+                     "alg_flops": flops, "alg_bytes": nbytes,
+                     "hbm_frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "workspace_bytes": ws_bytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bwd(w, variant)
+    return line
+
+
 KERNEL_SOURCES = ("split_impl.h", "falcon_fwd_split.hip", "falcon_fwd_split_win.hip", "falcon_fwd_pipe.hip",
                   "chunk_common.h", "mfma_frag.h", "falcon_kernels.h")
 
@@ -175,6 +314,7 @@ def main():
     ap.add_argument("--variant", default="F1")
     ap.add_argument("--window", type=int, default=4, help="Falcon-3/3A window (pairs)")
     ap.add_argument("--decode", action="store_true", help="time the single-token step instead")
+    ap.add_argument("--backward", action="store_true", help="time the chunked backward pass instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=("auto", "onepass", "split"), default="auto",
                     help="forward path: one-pass (no workspace), split (workspace), or auto")
@@ -189,6 +329,9 @@ def main():
 
     if args.decode:
         print(json.dumps(bench_decode(args)), flush=True)
+        return
+    if args.backward:
+        print(json.dumps(bench_backward(args)), flush=True)
         return
 
     import torch

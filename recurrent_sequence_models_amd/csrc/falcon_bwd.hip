@@ -27,11 +27,11 @@
 //   bwd_chunk  one workgroup per chunk: recomputes A, P, E from the chunk's
 //              incoming state and takes the adjoint of every product above.
 //
-// Layout of a workgroup (256 threads = 4 waves): C x 64 matrices whose columns
-// are value or key channels are held by waves in 16-column tiles (wave w owns
-// columns 16w..16w+15 of every row tile), so a triangular solve along the
-// chunk runs inside one wave with no barrier; C x C matrices are computed one
-// 16-row tile per wave and staged in LDS.  LDS rows have a pitch of 68 floats,
+// Layout of a workgroup: C x 64 matrices whose columns are value or key channels
+// are held by waves in 16-column tiles, so a triangular solve along the chunk
+// runs inside a wave (or a pair of waves) with few barriers; C x C matrices are
+// computed in 16x16 tiles spread over the waves and staged in LDS.  LDS rows
+// have a pitch of 68 floats,
 // which makes both the 16-byte row reads and the 4-byte column reads of the
 // fragment loads free of bank conflicts.
 #include "falcon_kernels.h"
@@ -45,7 +45,6 @@ constexpr int D = 64;    // d_k = d_v
 constexpr int C = 64;    // steps per chunk
 constexpr int LD = 68;   // LDS pitch of a 64-wide matrix (floats)
 constexpr int TL = 20;   // LDS pitch of a 16x16 diagonal-block inverse
-constexpr int NT = 256;  // threads per workgroup
 constexpr int MAT = C * LD;
 
 // ---- fragments (lane l = 16g + c) ---------------------------------------------
@@ -91,60 +90,63 @@ __device__ __forceinline__ float sum4g(float x) {
 }
 __device__ __forceinline__ float sum64(float x) { return sum4g(sum16(x)); }
 
-template <typename IT>
-__device__ __forceinline__ void load16(const IT *p, float (&v)[16]) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = (float)p[j];
-}
-
 // The chunk's rows in LDS: keys x_i (features), queries qh_i and the per-row
-// scalars.  Thread (row r = tid / 4, quarter p = tid % 4) takes 16 channels.
+// scalars.  With NTH threads, thread (row r = tid / NP, part p = tid % NP) takes
+// 64 / NP channels, NP = NTH / 64.
 struct RowScalars {
   float L[C], Lm[C], eta[C], en[C];  // L_i, L_{i-1}, eta_i, eps_eta + |x_i|^2
 };
 
-template <typename IT>
+template <int NP>
+__device__ __forceinline__ float sum_parts(float x) {
+#pragma unroll
+  for (int o = 1; o < NP; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+template <typename IT, int E>
+__device__ __forceinline__ void load_e(const IT *p, float (&v)[E]) {
+#pragma unroll
+  for (int j = 0; j < E; ++j) v[j] = (float)p[j];
+}
+
+template <typename IT, int NTH>
 __device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, RowScalars &rs) {
-  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3, lane = tid & 63;
+  constexpr int NP = NTH / 64, E = 64 / NP;
+  const int tid = threadIdx.x, r = tid / NP, p = tid % NP, lane = tid & 63;
   const int b = n / a.H, h = n % a.H;
   const int t = c * C + r;
   const int kt = t - 1 + a.align;  // key index of the pair written at step t
   const bool live = t < a.T;
-  float x[16], q[16];
+  float x[E], q[E];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) x[j] = q[j] = 0.f;
+  for (int j = 0; j < E; ++j) x[j] = q[j] = 0.f;
   const bool key_row = live && kt >= 0;
-  if (key_row) load16((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + 16 * p, x);
-  else if (live && a.xprev0) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = a.xprev0[(size_t)n * D + 16 * p + j];  // the carried feature
-  }
-  if (live) load16((const IT *)a.q + ((size_t)(b * a.T + t) * a.H + h) * D + 16 * p, q);
+  if (key_row) load_e<IT, E>((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + E * p, x);
+  else if (live && a.xprev0) load_e<float, E>(a.xprev0 + (size_t)n * D + E * p, x);  // the carried feature
+  if (live) load_e<IT, E>((const IT *)a.q + ((size_t)(b * a.T + t) * a.H + h) * D + E * p, q);
   float sx = 0.f, sq = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < E; ++j) {
     sx += x[j] * x[j];
     sq += q[j] * q[j];
   }
-  sx += __shfl_xor(sx, 1);
-  sx += __shfl_xor(sx, 2);
-  sq += __shfl_xor(sq, 1);
-  sq += __shfl_xor(sq, 2);
+  sx = sum_parts<NP>(sx);
+  sq = sum_parts<NP>(sq);
   const float ix = key_row ? 1.f / sqrtf(sx + a.eps_phi) : 1.f;
   const float iq = 1.f / sqrtf(sq + a.eps_phi);
   float e = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < E; ++j) {
     x[j] *= ix;
     q[j] = live ? q[j] * iq : 0.f;
     e += x[j] * x[j];
   }
-  e += __shfl_xor(e, 1);
-  e += __shfl_xor(e, 2);
+  e = sum_parts<NP>(e);
 #pragma unroll
-  for (int j = 0; j < 16; j += 4) {
-    *reinterpret_cast<f4 *>(sX + r * LD + 16 * p + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
-    *reinterpret_cast<f4 *>(sQ + r * LD + 16 * p + j) = f4{q[j], q[j + 1], q[j + 2], q[j + 3]};
+  for (int j = 0; j < E; j += 4) {
+    *reinterpret_cast<f4 *>(sX + r * LD + E * p + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+    *reinterpret_cast<f4 *>(sQ + r * LD + E * p + j) = f4{q[j], q[j + 1], q[j + 2], q[j + 3]};
   }
   if (p == 0) {
     const size_t gi = (size_t)(b * a.T + t) * a.H + h;
@@ -168,34 +170,36 @@ __device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, 
   __syncthreads();
 }
 
-// A (row tile w; zero for F1A) and P (row tile w) into LDS, with their masks.
+// One 16x16 tile (rt, ct <= rt) of A (skipped for F1A) and P into LDS, with
+// their masks (strict / causal) and decays.
 template <bool ADD>
-__device__ void gram_tiles(const float *sX, const float *sQ, float *sA, float *sP, const RowScalars &rs, int w,
-                           int lane) {
+__device__ void gram_tile(const float *sX, const float *sQ, float *sA, float *sP, const RowScalars &rs, int rt,
+                          int ct, int lane) {
   const int g = lane >> 4, cc = lane & 15;
+  f4 pa = zero4(), pp = zero4();
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    f4 pa = zero4(), pp = zero4();
-    if (ct <= w) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f4 xb = b_tr(sX, LD, 16 * kb, 16 * ct, lane);
-        if (!ADD) mma16(pa, a_rm(sX, LD, 16 * w, 16 * kb, lane), xb);
-        mma16(pp, a_rm(sQ, LD, 16 * w, 16 * kb, lane), xb);
-      }
-    }
-    const int col = 16 * ct + cc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * w + 4 * g + i;
-      pa[i] = col < row ? __expf(rs.Lm[row] - rs.L[col]) * pa[i] : 0.f;
-      pp[i] = col <= row ? __expf(rs.L[row] - rs.L[col]) * pp[i] : 0.f;
-    }
-    if (!ADD) st_c(sA, LD, 16 * w, 16 * ct, lane, pa);
-    st_c(sP, LD, 16 * w, 16 * ct, lane, pp);
+  for (int kb = 0; kb < 4; ++kb) {
+    const f4 xb = b_tr(sX, LD, 16 * kb, 16 * ct, lane);
+    if (!ADD) mma16(pa, a_rm(sX, LD, 16 * rt, 16 * kb, lane), xb);
+    mma16(pp, a_rm(sQ, LD, 16 * rt, 16 * kb, lane), xb);
   }
+  const int col = 16 * ct + cc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    pa[i] = col < row ? __expf(rs.Lm[row] - rs.L[col]) * pa[i] : 0.f;
+    pp[i] = col <= row ? __expf(rs.L[row] - rs.L[col]) * pp[i] : 0.f;
+  }
+  if (!ADD) st_c(sA, LD, 16 * rt, 16 * ct, lane, pa);
+  st_c(sP, LD, 16 * rt, 16 * ct, lane, pp);
 }
 
+// The 10 tiles on or below the diagonal of a 4x4 tiling, in row order (tiles above
+// the diagonal are never read).
+__device__ __forceinline__ void lower_tile(int k, int &rt, int &ct) {
+  rt = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
+  ct = k - rt * (rt + 1) / 2;
+}
 // Inverse of the unit lower-triangular diagonal block w of M = I + A diag(eta),
 // by forward substitution: lane j < 16 solves for column j.
 __device__ void diag_inverse(const float *sA, float *sT, const RowScalars &rs, int w, int lane) {
@@ -251,20 +255,28 @@ __device__ void solve_upper(f4 (&y)[4], const float *sA, const float *sT, const 
   }
 }
 
-// Rows 0..63 of a [C][64] input-typed array (rows past T are zero) into LDS as fp32.
-template <typename IT>
-__device__ void load_mat(const IT *base, size_t row_stride, int rows_live, float *dst) {
-  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
-  float v[16];
-  if (r < rows_live) load16(base + (size_t)r * row_stride + 16 * p, v);
-  else {
+// This thread's share of rows 0..63 of a [C][64] input-typed array (rows past
+// `rows_live` are zero), as fp32, and its store into LDS.
+template <int NTH>
+struct RowShare {
+  static constexpr int NP = NTH / 64, E = 64 / NP;
+  float v[E];
+  template <typename IT>
+  __device__ void load(const IT *base, size_t row_stride, int rows_live) {
+    const int r = threadIdx.x / NP, p = threadIdx.x % NP;
+    if (r < rows_live) load_e<IT, E>(base + (size_t)r * row_stride + E * p, v);
+    else {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = 0.f;
+      for (int j = 0; j < E; ++j) v[j] = 0.f;
+    }
   }
+  __device__ void store(float *dst) const {
+    const int r = threadIdx.x / NP, p = threadIdx.x % NP;
 #pragma unroll
-  for (int j = 0; j < 16; j += 4)
-    *reinterpret_cast<f4 *>(dst + r * LD + 16 * p + j) = f4{v[j], v[j + 1], v[j + 2], v[j + 3]};
-}
+    for (int j = 0; j < E; j += 4)
+      *reinterpret_cast<f4 *>(dst + r * LD + E * p + j) = f4{v[j], v[j + 1], v[j + 2], v[j + 3]};
+  }
+};
 
 // Workspace arrays of one chunk.
 struct WsPtr {
@@ -283,17 +295,20 @@ __device__ __forceinline__ WsPtr ws_of(const BwdArgs &a, size_t chunk_id) {
 }
 
 // ---- bwd_prep -------------------------------------------------------------------
+// 256 threads.  LDS: X, Qh (then do), A, P and the diagonal-block inverses, so
+// two workgroups share a compute unit.
 template <typename IT, bool ADD>
-__global__ __launch_bounds__(NT) void bwd_prep(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[MAT], sP[MAT], sO[MAT];
-  __shared__ __attribute__((aligned(16))) float sT[4 * 16 * TL];
+__global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[ADD ? 4 : MAT], sP[ADD ? 4 : MAT];
+  __shared__ __attribute__((aligned(16))) float sT[ADD ? 4 : 4 * 16 * TL];
   __shared__ RowScalars rs;
   const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
   const int b = n / a.H, h = n % a.H;
   const int live = min(C, a.T - c * C);
-  load_mat((const IT *)a.dO + ((size_t)(b * a.T + c * C) * a.H + h) * D, (size_t)a.H * D, live, sO);
-  load_rows<IT>(a, n, c, sX, sQ, rs);  // ends with a barrier
+  RowShare<256> dO;
+  dO.load((const IT *)a.dO + ((size_t)(b * a.T + c * C) * a.H + h) * D, (size_t)a.H * D, live);
+  load_rows<IT, 256>(a, n, c, sX, sQ, rs);  // ends with a barrier
   const WsPtr ws = ws_of(a, blockIdx.x);
   const float LC = rs.L[C - 1];
 
@@ -305,8 +320,15 @@ __global__ __launch_bounds__(NT) void bwd_prep(BwdArgs a) {
     for (int i = 0; i < 4; ++i) qe[rt][i] *= __expf(rs.L[16 * rt + 4 * g + i]);
   }
   if (!ADD) {
-    gram_tiles<false>(sX, sQ, sA, sP, rs, w, lane);
-    __syncthreads();
+    for (int k = w; k < 10; k += 4) {
+      int rt, ct;
+      lower_tile(k, rt, ct);
+      gram_tile<false>(sX, sQ, sA, sP, rs, rt, ct, lane);
+    }
+  }
+  __syncthreads();  // sQ is read: it takes do from here on
+  dO.store(sQ);
+  if (!ADD) {
     diag_inverse(sA, sT, rs, w, lane);
     __syncthreads();
     f4 W[4];
@@ -334,13 +356,15 @@ __global__ __launch_bounds__(NT) void bwd_prep(BwdArgs a) {
         ws.W[row * D + 16 * w + cc] = rs.eta[row] * __expf(LC - rs.L[row]) * W[rt][i];
       }
     }
+  } else {
+    __syncthreads();
   }
   // Z = do^T qe: value-channel rows, key-channel column tile w.
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     f4 z = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma16(z, a_tr(sO, LD, 16 * rt, 16 * kb, lane), qe[kb]);
+    for (int kb = 0; kb < 4; ++kb) mma16(z, a_tr(sQ, LD, 16 * rt, 16 * kb, lane), qe[kb]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ws.Z[(16 * rt + 4 * g + i) * D + 16 * w + cc] = z[i];
   }
@@ -354,10 +378,12 @@ __global__ __launch_bounds__(NT) void bwd_prep(BwdArgs a) {
 }
 
 // ---- bwd_scan -------------------------------------------------------------------
-// Workgroup (sequence n, value rows 16s..16s+15); wave w holds key columns 16w..+15.
+// Workgroup (sequence n, value rows 16s..16s+15); wave w holds key columns
+// 16w..16w+15.  The next chunk's X, diag(b) W, Z and decay are fetched into
+// registers while the current chunk is reduced.
 template <bool ADD>
-__global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float sX[MAT], sW[MAT], sG[16 * LD], sY[16 * LD];
+__global__ __launch_bounds__(256) void bwd_scan(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[ADD ? 4 : MAT], sW[ADD ? 4 : MAT], sG[16 * LD], sY[16 * LD];
   const int n = blockIdx.x >> 2, s = blockIdx.x & 3;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
   const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
@@ -367,24 +393,44 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) G[i] = a.dST[(size_t)n * D * D + tile + i * D];
   }
-  for (int c = a.NC - 1; c >= 0; --c) {
+  f4 nx[4], nw[4], nz;
+  float ndec;
+  auto fetch = [&](int c) {
     const WsPtr ws = ws_of(a, (size_t)n * a.NC + c);
-    f4 Z;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ws.G[tile + i * D] = G[i];  // gradient at the end of chunk c
-      Z[i] = ws.Z[tile + i * D];
+    for (int i = 0; i < 4; ++i) nz[i] = ws.Z[tile + i * D];
+    ndec = *ws.dec;
+    if (!ADD) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        nx[j] = *reinterpret_cast<const f4 *>(ws.X + r * D + 16 * p + 4 * j);
+        nw[j] = *reinterpret_cast<const f4 *>(ws.W + r * D + 16 * p + 4 * j);
+      }
     }
-    const float dec = *ws.dec;
+  };
+  fetch(a.NC - 1);
+  for (int c = a.NC - 1; c >= 0; --c) {
+    const f4 Z = nz;
+    const float dec = ndec;
+    f4 xr[4], wr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xr[j] = nx[j];
+      wr[j] = nw[j];
+    }
+    float *gout = ws_of(a, (size_t)n * a.NC + c).G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gout[tile + i * D] = G[i];  // gradient at the end of chunk c
+    if (c > 0) fetch(c - 1);
     if (ADD) {
       G = dec * G + Z;
       continue;
     }
     __syncthreads();  // the previous chunk's readers are done with sX, sW, sG, sY
 #pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-      *reinterpret_cast<f4 *>(sX + r * LD + 16 * p + j) = *reinterpret_cast<const f4 *>(ws.X + r * D + 16 * p + j);
-      *reinterpret_cast<f4 *>(sW + r * LD + 16 * p + j) = *reinterpret_cast<const f4 *>(ws.W + r * D + 16 * p + j);
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<f4 *>(sX + r * LD + 16 * p + 4 * j) = xr[j];
+      *reinterpret_cast<f4 *>(sW + r * LD + 16 * p + 4 * j) = wr[j];
     }
     st_c(sG, LD, 0, 16 * w, lane, G);
     __syncthreads();
@@ -405,95 +451,184 @@ __global__ __launch_bounds__(NT) void bwd_scan(BwdArgs a) {
 }
 
 // ---- bwd_chunk ------------------------------------------------------------------
+// 512 threads = 8 waves.  Wave w holds column tile ct = w % 4 of the C x 64
+// matrices for row tiles 2h, 2h+1 (h = w / 4); the triangular solves along the
+// chunk hand the first half's blocks to the second half through LDS (one
+// barrier each way).  The 10 lower tiles of the C x C products are spread over
+// all waves.  Per-wave partial sums of the row gradients (dL, d eta) are added
+// up in a fixed order at the end, so results are deterministic.
+constexpr int NTC = 512;
+constexpr int NWC = NTC / 64;
+
+// Adjoint of one lower tile (rt, ct) of A and P: from t = dR E^T and u = do E^T,
+// the tile's contributions to dL and d eta, and dAG = dA o Gamma, dPD = dP o D in
+// place of A and P.
+template <bool ADD>
+__device__ void adjoint_tile(float *sA, float *sP, const float *sG, const float *sO, const float *sE,
+                             const RowScalars &rs, float *pLw, float *pEw, int rt, int ct, int lane) {
+  const int g = lane >> 4, cc = lane & 15;
+  f4 t = zero4(), u = zero4();
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const f4 eb = b_tr(sE, LD, 16 * kb, 16 * ct, lane);
+    if (!ADD) mma16(t, a_rm(sG, LD, 16 * rt, 16 * kb, lane), eb);
+    mma16(u, a_rm(sO, LD, 16 * rt, 16 * kb, lane), eb);
+  }
+  const int col = 16 * ct + cc;
+  const float etac = rs.eta[col];
+  float colL = 0.f, colE = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    float rowL = 0.f, rowLm = 0.f;
+    if (!ADD) {
+      const float Aij = sA[row * LD + col];
+      const float dM = col < row ? -t[i] : 0.f;
+      colE += Aij * dM;  // d eta_j += A_ij dM_ij
+      const float dA = dM * etac;
+      const float H = dA * Aij;
+      rowLm += H;
+      colL -= H;
+      sA[row * LD + col] = col < row ? dA * __expf(rs.Lm[row] - rs.L[col]) : 0.f;
+    }
+    const float dP = col <= row ? u[i] * etac : 0.f;
+    const float HP = dP * sP[row * LD + col];
+    rowL += HP;
+    colL -= HP;
+    sP[row * LD + col] = col <= row ? dP * __expf(rs.L[row] - rs.L[col]) : 0.f;
+    rowL = sum16(rowL);
+    rowLm = sum16(rowLm);
+    if (cc == 0) {
+      pLw[row] += rowL;
+      if (row > 0) pLw[row - 1] += rowLm;
+    }
+  }
+  colL = sum4g(colL);
+  colE = sum4g(colE);
+  if (g == 0) {
+    pLw[col] += colL;
+    pEw[col] += colE;
+  }
+}
+
 template <typename IT, bool ADD>
-__global__ __launch_bounds__(NT) void bwd_chunk(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[MAT], sP[MAT], sE[MAT],
-      sO[MAT];
-  __shared__ __attribute__((aligned(16))) float sT[4 * 16 * TL];
+__global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[ADD ? 4 : MAT], sP[MAT],
+      sE[MAT], sO[MAT];
+  __shared__ __attribute__((aligned(16))) float sT[ADD ? 4 : 4 * 16 * TL];
   __shared__ RowScalars rs;
-  __shared__ float pL[4][C], pE[4][C], pC[4], sCoef[C];
+  __shared__ float pL[NWC][C], pE[NWC][C], pC[NWC], sCoef[C];
   const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
+  const int ct = w & 3, r0t = 2 * (w >> 2);  // column tile; first of the two row tiles
   const int b = n / a.H, h = n % a.H;
   const int live = min(C, a.T - c * C);
   const size_t row0 = (size_t)(b * a.T + c * C) * a.H + h;  // (b, t0, h)
   const WsPtr ws = ws_of(a, blockIdx.x);
 
-  // Phase 0: rows, the incoming state S0, the end-state gradient G, do.
-  load_mat((const IT *)a.dO + row0 * D, (size_t)a.H * D, live, sO);
+  // Phase 0: do, the incoming state S0, the end-state gradient G, v, the rows.
   {
-    const float *S0 = c ? a.chunk_states + ((size_t)n * a.NC + c - 1) * D * D : (a.S0 ? a.S0 + (size_t)n * D * D : nullptr);
-    const int r = tid >> 2, p = tid & 3;
+    RowShare<NTC> rO;
+    rO.load((const IT *)a.dO + row0 * D, (size_t)a.H * D, live);
+    const float *S0 = c ? a.chunk_states + ((size_t)n * a.NC + c - 1) * D * D
+                        : (a.S0 ? a.S0 + (size_t)n * D * D : nullptr);
+    const int r = tid >> 3, p = tid & 7;
 #pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-      *reinterpret_cast<f4 *>(sS + r * LD + 16 * p + j) =
-          S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 16 * p + j) : zero4();
-      *reinterpret_cast<f4 *>(sG + r * LD + 16 * p + j) = *reinterpret_cast<const f4 *>(ws.G + r * D + 16 * p + j);
+    for (int j = 0; j < 8; j += 4) {
+      *reinterpret_cast<f4 *>(sS + r * LD + 8 * p + j) =
+          S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 8 * p + j) : zero4();
+      *reinterpret_cast<f4 *>(sG + r * LD + 8 * p + j) = *reinterpret_cast<const f4 *>(ws.G + r * D + 8 * p + j);
     }
+    rO.store(sO);
     pL[w][lane] = 0.f;
     pE[w][lane] = 0.f;
   }
-  f4 V[4];
+  f4 V[2];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int j = 0; j < 2; ++j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 16 * rt + 4 * g + i;
-      V[rt][i] = row < live ? (float)((const IT *)a.v)[(row0 + (size_t)row * a.H) * D + 16 * w + cc] : 0.f;
+      const int row = 16 * (r0t + j) + 4 * g + i;
+      V[j][i] = row < live ? (float)((const IT *)a.v)[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] : 0.f;
     }
   }
-  load_rows<IT>(a, n, c, sX, sQ, rs);  // ends with a barrier
+  load_rows<IT, NTC>(a, n, c, sX, sQ, rs);  // ends with a barrier
   const float LC = rs.L[C - 1];
   float lc = 0.f;  // this lane's share of dL_C
-
-  {  // e^{L_C} <G, S0>
-    const int r = tid >> 2, p = tid & 3;
+  {
+    const int r = tid >> 3, p = tid & 7;
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s += sG[r * LD + 16 * p + j] * sS[r * LD + 16 * p + j];
-    lc += __expf(LC) * s;
+    for (int j = 0; j < 8; ++j) s += sG[r * LD + 8 * p + j] * sS[r * LD + 8 * p + j];
+    lc += __expf(LC) * s;  // e^{L_C} <G, S0>
   }
 
-  // Phase 1: A and P; R = V - diag(e^Lm) X S0^T; dQh from the first read term; Y = X G^T.
-  gram_tiles<ADD>(sX, sQ, sA, sP, rs, w, lane);
-  f4 dO[4], E[4], dQ[4], Y[4];
+  // Phase 1: A and P tiles; R = V - diag(e^Lm) X S0^T; dQh from the first read term; Y = X G^T.
+  for (int k = w; k < 10; k += NWC) {
+    int rt, ctt;
+    lower_tile(k, rt, ctt);
+    gram_tile<ADD>(sX, sQ, sA, sP, rs, rt, ctt, lane);
+  }
+  f4 E[2], dQ[2], Y[2];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) dO[rt] = b_rm(sO, LD, 16 * rt, 16 * w, lane);
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int j = 0; j < 2; ++j) {
+    const int rt = r0t + j;
     f4 xs = zero4(), dq = zero4(), y = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const f4 xa = a_rm(sX, LD, 16 * rt, 16 * kb, lane);
-      if (!ADD) mma16(xs, xa, b_tr(sS, LD, 16 * kb, 16 * w, lane));
-      mma16(y, xa, b_tr(sG, LD, 16 * kb, 16 * w, lane));
-      mma16(dq, a_rm(sO, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * w, lane));
+      if (!ADD) mma16(xs, xa, b_tr(sS, LD, 16 * kb, 16 * ct, lane));
+      mma16(y, xa, b_tr(sG, LD, 16 * kb, 16 * ct, lane));
+      mma16(dq, a_rm(sO, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rt + 4 * g + i;
-      E[rt][i] = ADD ? V[rt][i] : V[rt][i] - __expf(rs.Lm[row]) * xs[i];
-      dQ[rt][i] = __expf(rs.L[row]) * dq[i];
-      const float part = sum16(sQ[row * LD + 16 * w + cc] * dQ[rt][i]);  // qh_i . dQh_i
+      E[j][i] = ADD ? V[j][i] : V[j][i] - __expf(rs.Lm[row]) * xs[i];
+      dQ[j][i] = __expf(rs.L[row]) * dq[i];
+      const float part = sum16(sQ[row * LD + 16 * ct + cc] * dQ[j][i]);  // qh_i . dQh_i
       if (cc == 0) pL[w][row] += part;
     }
-    Y[rt] = y;
+    Y[j] = y;
   }
 
-  // Phase 2-3: E = M^-1 R.
+  // Phase 2-3: E = M^-1 R, blocks 0-1 by the first half, then blocks 2-3.
   if (!ADD) {
     __syncthreads();
-    diag_inverse(sA, sT, rs, w, lane);
+    if (w < 4) diag_inverse(sA, sT, rs, w, lane);
     __syncthreads();
-    solve_lower(E, sA, sT, rs, lane);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (2 * half == r0t) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int bb = r0t + j;
+          f4 s = zero4();
+          for (int bp = 0; bp < bb; ++bp) {
+            f4 af = a_rm(sA, LD, 16 * bb, 16 * bp, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] *= rs.eta[16 * bp + 4 * g + i];
+            mma16(s, af, bp == r0t ? E[0] : b_rm(sE, LD, 16 * bp, 16 * ct, lane));
+          }
+          const f4 rr = E[j] - s;
+          E[j] = zero4();
+          mma16(E[j], a_rm(sT + bb * 16 * TL, TL, 0, 0, lane), rr);
+          st_c(sE, LD, 16 * bb, 16 * ct, lane, E[j]);
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) st_c(sE, LD, 16 * (r0t + j), 16 * ct, lane, E[j]);
+    __syncthreads();
   }
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    st_c(sE, LD, 16 * rt, 16 * w, lane, E[rt]);
+  for (int j = 0; j < 2; ++j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // db_i = E_i . (G x_i): into d eta_i, dL_i and dL_C
-      const int row = 16 * rt + 4 * g + i;
-      const float db = sum16(E[rt][i] * Y[rt][i]);
+      const int row = 16 * (r0t + j) + 4 * g + i;
+      const float db = sum16(E[j][i] * Y[j][i]);
       const float f = __expf(LC - rs.L[row]);
       if (cc == 0) {
         pE[w][row] += db * f;
@@ -502,123 +637,99 @@ __global__ __launch_bounds__(NT) void bwd_chunk(BwdArgs a) {
       }
     }
   }
-  __syncthreads();
 
   // Phase 4: Z = P^T do; dE = diag(b) Y + diag(eta) Z; dX = diag(b) E G.
-  f4 dE[4], dX[4];
+  f4 dE[2], dX[2];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int j = 0; j < 2; ++j) {
+    const int rt = r0t + j;
     f4 z = zero4(), u = zero4();
+    for (int kb = rt; kb < 4; ++kb) mma16(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sO, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
-    for (int kb = rt; kb < 4; ++kb) mma16(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), dO[kb]);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma16(u, a_rm(sE, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * w, lane));
+    for (int kb = 0; kb < 4; ++kb) mma16(u, a_rm(sE, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rt + 4 * g + i;
       const float bb = rs.eta[row] * __expf(LC - rs.L[row]);
-      dE[rt][i] = bb * Y[rt][i] + rs.eta[row] * z[i];
-      dX[rt][i] = bb * u[i];
-      const float de = sum16(z[i] * E[rt][i]);
+      dE[j][i] = bb * Y[j][i] + rs.eta[row] * z[i];
+      dX[j][i] = bb * u[i];
+      const float de = sum16(z[i] * E[j][i]);
       if (cc == 0) pE[w][row] += de;
     }
   }
 
-  // Phase 5: dR = M^-T dE (= dv); F1A: dv = dE.
-  if (!ADD) solve_upper(dE, sA, sT, rs, lane);
+  // Phase 5: dR = M^-T dE (= dv), blocks 3-2 by the second half, then 1-0; F1A: dv = dE.
+  if (!ADD) {
+    __syncthreads();  // every wave is done reading G
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+    for (int half = 1; half >= 0; --half) {
+      if (2 * half == r0t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * rt + 4 * g + i;
-      if (row < live) a.dv[(row0 + (size_t)row * a.H) * D + 16 * w + cc] = dE[rt][i];
+        for (int j = 1; j >= 0; --j) {
+          const int bb = r0t + j;
+          f4 s = zero4();
+          for (int bp = bb + 1; bp < 4; ++bp) {
+            f4 af = a_tr(sA, LD, 16 * bb, 16 * bp, lane);
+            af *= rs.eta[16 * bb + cc];
+            mma16(s, af, bp == r0t + 1 ? dE[1] : b_rm(sG, LD, 16 * bp, 16 * ct, lane));
+          }
+          const f4 rr = dE[j] - s;
+          dE[j] = zero4();
+          mma16(dE[j], a_tr(sT + bb * 16 * TL, TL, 0, 0, lane), rr);
+          st_c(sG, LD, 16 * bb, 16 * ct, lane, dE[j]);  // sG now holds dR
+        }
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();  // every wave is done reading G and A
-  if (!ADD) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) st_c(sG, LD, 16 * rt, 16 * w, lane, dE[rt]);  // sG now holds dR
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * (r0t + j) + 4 * g + i;
+      if (row < live) a.dv[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] = dE[j][i];
+    }
   }
-  __syncthreads();
 
-  // Phase 6: dR S0 (into dX and dL_{i-1}); dA from dR E^T; dP from do (diag(eta) E)^T.
+  // Phase 6: dR S0 (into dX and dL_{i-1}); the C x C adjoints.
   if (!ADD) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int j = 0; j < 2; ++j) {
+      const int rt = r0t + j;
       f4 s = zero4();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma16(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * w, lane));
+      for (int kb = 0; kb < 4; ++kb) mma16(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * rt + 4 * g + i;
         const float am = __expf(rs.Lm[row]);
-        dX[rt][i] -= am * s[i];
-        const float part = sum16(sX[row * LD + 16 * w + cc] * s[i]);
+        dX[j][i] -= am * s[i];
+        const float part = sum16(sX[row * LD + 16 * ct + cc] * s[i]);
         if (cc == 0 && row > 0) pL[w][row - 1] -= am * part;
       }
     }
   }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    if (ct > w) continue;
-    f4 t = zero4(), u = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const f4 eb = b_tr(sE, LD, 16 * kb, 16 * ct, lane);
-      if (!ADD) mma16(t, a_rm(sG, LD, 16 * w, 16 * kb, lane), eb);
-      mma16(u, a_rm(sO, LD, 16 * w, 16 * kb, lane), eb);
-    }
-    const int col = 16 * ct + cc;
-    const float etac = rs.eta[col];
-    float colL = 0.f, colE = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * w + 4 * g + i;
-      float rowL = 0.f, rowLm = 0.f;
-      if (!ADD) {
-        const float Aij = sA[row * LD + col];
-        const float dM = col < row ? -t[i] : 0.f;
-        colE += Aij * dM;
-        const float dA = dM * etac;
-        const float H = dA * Aij;
-        rowLm += H;
-        colL -= H;
-        sA[row * LD + col] = col < row ? dA * __expf(rs.Lm[row] - rs.L[col]) : 0.f;
-      }
-      const float dP = col <= row ? u[i] * etac : 0.f;
-      const float HP = dP * sP[row * LD + col];
-      rowL += HP;
-      colL -= HP;
-      sP[row * LD + col] = col <= row ? dP * __expf(rs.L[row] - rs.L[col]) : 0.f;
-      rowL = sum16(rowL);
-      rowLm = sum16(rowLm);
-      if (cc == 0) {
-        pL[w][row] += rowL;
-        if (row > 0) pL[w][row - 1] += rowLm;
-      }
-    }
-    colL = sum4g(colL);
-    colE = sum4g(colE);
-    if (g == 0) {
-      pL[w][col] += colL;
-      pE[w][col] += colE;
-    }
+  for (int k = w; k < 10; k += NWC) {
+    int rt, ctt;
+    lower_tile(k, rt, ctt);
+    adjoint_tile<ADD>(sA, sP, sG, sO, sE, rs, pL[w], pE[w], rt, ctt, lane);
   }
   __syncthreads();
 
   // Phase 7: dQh += dPD X; dX += dPD^T Qh + dAG X + dAG^T X.
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int j = 0; j < 2; ++j) {
+    const int rt = r0t + j;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const f4 xb = b_rm(sX, LD, 16 * kb, 16 * w, lane);
+      const f4 xb = b_rm(sX, LD, 16 * kb, 16 * ct, lane);
       if (kb <= rt) {
-        mma16(dQ[rt], a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
-        if (!ADD) mma16(dX[rt], a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
+        mma16(dQ[j], a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
+        if (!ADD) mma16(dX[j], a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
       }
       if (kb >= rt) {
-        mma16(dX[rt], a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * w, lane));
-        if (!ADD) mma16(dX[rt], a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
+        mma16(dX[j], a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * ct, lane));
+        if (!ADD) mma16(dX[j], a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
       }
     }
   }
@@ -629,9 +740,16 @@ __global__ __launch_bounds__(NT) void bwd_chunk(BwdArgs a) {
   // Phase 8: per-row totals; dL -> d(log-decay) by a reverse sum; beta and the |x|^2 term.
   if (w == 0) {
     const int i = lane;
-    const float de = pE[0][i] + pE[1][i] + pE[2][i] + pE[3][i];
-    float dl = pL[0][i] + pL[1][i] + pL[2][i] + pL[3][i];
-    if (i == C - 1) dl += pC[0] + pC[1] + pC[2] + pC[3];
+    float de = 0.f, dl = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWC; ++v) {
+      de += pE[v][i];
+      dl += pL[v][i];
+    }
+    if (i == C - 1) {
+#pragma unroll
+      for (int v = 0; v < NWC; ++v) dl += pC[v];
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float y = __shfl_down(dl, o);
@@ -646,91 +764,90 @@ __global__ __launch_bounds__(NT) void bwd_chunk(BwdArgs a) {
   }
   __syncthreads();
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int j = 0; j < 2; ++j) {
+    const int rt = r0t + j;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rt + 4 * g + i;
-      dX[rt][i] += sCoef[row] * sX[row * LD + 16 * w + cc];
+      dX[j][i] += sCoef[row] * sX[row * LD + 16 * ct + cc];
     }
-    st_c(sO, LD, 16 * rt, 16 * w, lane, dQ[rt]);
-    st_c(sE, LD, 16 * rt, 16 * w, lane, dX[rt]);
+    st_c(sO, LD, 16 * rt, 16 * ct, lane, dQ[j]);
+    st_c(sE, LD, 16 * rt, 16 * ct, lane, dX[j]);
   }
   __syncthreads();
 
-  // Through the feature map: dq_t for t < T; dk of the key row i carries.
+  // Through the feature map: dq_t for t < T; dk of the key that row r carries.
   {
-    const int r = tid >> 2, p = tid & 3;
+    constexpr int NP = NTC / 64, EE = 64 / NP;
+    const int r = tid / NP, p = tid % NP;
     const int t = c * C + r;
-    float v[16], d[16];
+    float v[EE], d[EE];
     if (t < a.T) {
-      load16((const IT *)a.q + (row0 + (size_t)r * a.H) * D + 16 * p, v);
+      load_e<IT, EE>((const IT *)a.q + (row0 + (size_t)r * a.H) * D + EE * p, v);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) d[j] = sO[r * LD + 16 * p + j];
+      for (int j = 0; j < EE; ++j) d[j] = sO[r * LD + EE * p + j];
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = d[j] = 0.f;
+      for (int j = 0; j < EE; ++j) v[j] = d[j] = 0.f;
     }
     float nn = 0.f, dot = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < EE; ++j) {
       nn += v[j] * v[j];
       dot += v[j] * d[j];
     }
-    nn += __shfl_xor(nn, 1);
-    nn += __shfl_xor(nn, 2);
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
+    nn = sum_parts<NP>(nn);
+    dot = sum_parts<NP>(dot);
     float inv = 1.f / sqrtf(nn + a.eps_phi);
     float inv3 = inv * inv * inv;
     if (t < a.T) {
-      float *dst = a.dq + (row0 + (size_t)r * a.H) * D + 16 * p;
+      float *dst = a.dq + (row0 + (size_t)r * a.H) * D + EE * p;
 #pragma unroll
-      for (int j = 0; j < 16; j += 4)
+      for (int j = 0; j < EE; j += 4)
         *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
                                               d[j + 2] * inv - v[j + 2] * dot * inv3,
                                               d[j + 3] * inv - v[j + 3] * dot * inv3};
     }
-    // key of row r: k_{t-1+align}; rows at t == T (prefix) carry k_{T-1}, whose gradient is 0.
+    // key of row r: k_{t-1+align}; under the prefix pairing the row at t == T
+    // carries k_{T-1}, whose gradient is 0 (that row's dX is 0).
     const int kt = t - 1 + a.align;
     const bool key_row = kt >= 0 && kt < a.T && t <= a.T - a.align;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) d[j] = sE[r * LD + 16 * p + j];
-    if (key_row) load16((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + 16 * p, v);
+    for (int j = 0; j < EE; ++j) d[j] = sE[r * LD + EE * p + j];
+    if (key_row) load_e<IT, EE>((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + EE * p, v);
     else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0.f;
+      for (int j = 0; j < EE; ++j) v[j] = 0.f;
     }
     nn = 0.f;
     dot = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < EE; ++j) {
       nn += v[j] * v[j];
       dot += v[j] * d[j];
     }
-    nn += __shfl_xor(nn, 1);
-    nn += __shfl_xor(nn, 2);
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
+    nn = sum_parts<NP>(nn);
+    dot = sum_parts<NP>(dot);
     inv = 1.f / sqrtf(nn + a.eps_phi);
     inv3 = inv * inv * inv;
     if (key_row) {
-      float *dst = a.dk + ((size_t)(b * a.T + kt) * a.H + h) * D + 16 * p;
+      float *dst = a.dk + ((size_t)(b * a.T + kt) * a.H + h) * D + EE * p;
 #pragma unroll
-      for (int j = 0; j < 16; j += 4)
+      for (int j = 0; j < EE; j += 4)
         *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
                                               d[j + 2] * inv - v[j + 2] * dot * inv3,
                                               d[j + 3] * inv - v[j + 3] * dot * inv3};
     }
-    if (t == 0 && a.dxprev0) {  // the carried feature x_prev enters row 0 directly (prefix); unread (same step)
-      float *dst = a.dxprev0 + (size_t)n * D + 16 * p;
+    if (t == 0 && a.dxprev0) {  // the carried x_prev is row 0's key (prefix); unread under same-step pairs
+      float *dst = a.dxprev0 + (size_t)n * D + EE * p;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) dst[j] = a.align ? 0.f : d[j];
+      for (int j = 0; j < EE; ++j) dst[j] = a.align ? 0.f : d[j];
     }
     // Prefix pairing with T a multiple of C: k_{T-1} has no row here; its gradient is 0.
     if (!a.align && c == a.NC - 1 && a.T % C == 0 && r == 0) {
-      float *dst = a.dk + ((size_t)(b * a.T + a.T - 1) * a.H + h) * D + 16 * p;
+      float *dst = a.dk + ((size_t)(b * a.T + a.T - 1) * a.H + h) * D + EE * p;
 #pragma unroll
-      for (int j = 0; j < 16; j += 4) *reinterpret_cast<f4 *>(dst + j) = zero4();
+      for (int j = 0; j < EE; j += 4) *reinterpret_cast<f4 *>(dst + j) = zero4();
     }
   }
 }
@@ -738,13 +855,13 @@ __global__ __launch_bounds__(NT) void bwd_chunk(BwdArgs a) {
 template <typename IT, bool ADD>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   const unsigned nch = (unsigned)a.B * a.H * a.NC;
-  hipLaunchKernelGGL((bwd_prep<IT, ADD>), dim3(nch), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((bwd_prep<IT, ADD>), dim3(nch), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_scan<ADD>), dim3((unsigned)a.B * a.H * 4), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((bwd_scan<ADD>), dim3((unsigned)a.B * a.H * 4), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_chunk<IT, ADD>), dim3(nch), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((bwd_chunk<IT, ADD>), dim3(nch), dim3(NTC), 0, st, a);
   return hipGetLastError();
 }
 
