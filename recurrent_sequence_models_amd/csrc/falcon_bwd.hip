@@ -451,13 +451,13 @@ __global__ __launch_bounds__(256) void bwd_scan(BwdArgs a) {
 }
 
 // ---- bwd_chunk ------------------------------------------------------------------
-// 512 threads = 8 waves.  Wave w holds column tile ct = w % 4 of the C x 64
-// matrices for row tiles 2h, 2h+1 (h = w / 4); the triangular solves along the
-// chunk hand the first half's blocks to the second half through LDS (one
-// barrier each way).  The 10 lower tiles of the C x C products are spread over
-// all waves.  Per-wave partial sums of the row gradients (dL, d eta) are added
-// up in a fixed order at the end, so results are deterministic.
-constexpr int NTC = 512;
+// 1024 threads = 16 waves (four per SIMD).  Wave w owns the 16x16 tile (rt, ct) =
+// (w / 4, w % 4) of every C x 64 matrix.  The triangular solves run on four
+// solver waves, one per column tile, which read the right-hand side from LDS and
+// write the solution back (two barriers per solve).  The 10 lower tiles of the
+// C x C products go to waves 0..9.  Per-wave partial sums of the row gradients
+// (dL, d eta) are added in a fixed order at the end, so results are deterministic.
+constexpr int NTC = 1024;
 constexpr int NWC = NTC / 64;
 
 // Adjoint of one lower tile (rt, ct) of A and P: from t = dR E^T and u = do E^T,
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   __shared__ float pL[NWC][C], pE[NWC][C], pC[NWC], sCoef[C];
   const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
-  const int ct = w & 3, r0t = 2 * (w >> 2);  // column tile; first of the two row tiles
+  const int ct = w & 3, rt = w >> 2;  // this wave's tile of the C x 64 matrices
   const int b = n / a.H, h = n % a.H;
   const int live = min(C, a.T - c * C);
   const size_t row0 = (size_t)(b * a.T + c * C) * a.H + h;  // (b, t0, h)
@@ -532,47 +532,38 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
     rO.load((const IT *)a.dO + row0 * D, (size_t)a.H * D, live);
     const float *S0 = c ? a.chunk_states + ((size_t)n * a.NC + c - 1) * D * D
                         : (a.S0 ? a.S0 + (size_t)n * D * D : nullptr);
-    const int r = tid >> 3, p = tid & 7;
-#pragma unroll
-    for (int j = 0; j < 8; j += 4) {
-      *reinterpret_cast<f4 *>(sS + r * LD + 8 * p + j) =
-          S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 8 * p + j) : zero4();
-      *reinterpret_cast<f4 *>(sG + r * LD + 8 * p + j) = *reinterpret_cast<const f4 *>(ws.G + r * D + 8 * p + j);
-    }
+    const int r = tid >> 4, p = tid & 15;
+    *reinterpret_cast<f4 *>(sS + r * LD + 4 * p) = S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 4 * p) : zero4();
+    *reinterpret_cast<f4 *>(sG + r * LD + 4 * p) = *reinterpret_cast<const f4 *>(ws.G + r * D + 4 * p);
     rO.store(sO);
     pL[w][lane] = 0.f;
     pE[w][lane] = 0.f;
   }
-  f4 V[2];
+  f4 V;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * (r0t + j) + 4 * g + i;
-      V[j][i] = row < live ? (float)((const IT *)a.v)[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] : 0.f;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    V[i] = row < live ? (float)((const IT *)a.v)[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] : 0.f;
   }
   load_rows<IT, NTC>(a, n, c, sX, sQ, rs);  // ends with a barrier
   const float LC = rs.L[C - 1];
   float lc = 0.f;  // this lane's share of dL_C
   {
-    const int r = tid >> 3, p = tid & 7;
+    const int r = tid >> 4, p = tid & 15;
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s += sG[r * LD + 8 * p + j] * sS[r * LD + 8 * p + j];
+    for (int j = 0; j < 4; ++j) s += sG[r * LD + 4 * p + j] * sS[r * LD + 4 * p + j];
     lc += __expf(LC) * s;  // e^{L_C} <G, S0>
   }
 
   // Phase 1: A and P tiles; R = V - diag(e^Lm) X S0^T; dQh from the first read term; Y = X G^T.
-  for (int k = w; k < 10; k += NWC) {
-    int rt, ctt;
-    lower_tile(k, rt, ctt);
-    gram_tile<ADD>(sX, sQ, sA, sP, rs, rt, ctt, lane);
+  if (w < 10) {
+    int tr, tc;
+    lower_tile(w, tr, tc);
+    gram_tile<ADD>(sX, sQ, sA, sP, rs, tr, tc, lane);
   }
-  f4 E[2], dQ[2], Y[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rt = r0t + j;
+  f4 E, dQ, Y;
+  {
     f4 xs = zero4(), dq = zero4(), y = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -584,65 +575,46 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rt + 4 * g + i;
-      E[j][i] = ADD ? V[j][i] : V[j][i] - __expf(rs.Lm[row]) * xs[i];
-      dQ[j][i] = __expf(rs.L[row]) * dq[i];
-      const float part = sum16(sQ[row * LD + 16 * ct + cc] * dQ[j][i]);  // qh_i . dQh_i
+      E[i] = ADD ? V[i] : V[i] - __expf(rs.Lm[row]) * xs[i];
+      dQ[i] = __expf(rs.L[row]) * dq[i];
+      const float part = sum16(sQ[row * LD + 16 * ct + cc] * dQ[i]);  // qh_i . dQh_i
       if (cc == 0) pL[w][row] += part;
     }
-    Y[j] = y;
+    Y = y;
   }
 
-  // Phase 2-3: E = M^-1 R, blocks 0-1 by the first half, then blocks 2-3.
+  // Phase 2-3: E = M^-1 R on the solver waves (one per column tile).
+  st_c(sE, LD, 16 * rt, 16 * ct, lane, E);  // R (F1A: E = V)
+  __syncthreads();  // A, P and R are complete
   if (!ADD) {
-    __syncthreads();
     if (w < 4) diag_inverse(sA, sT, rs, w, lane);
-    __syncthreads();
+    __syncthreads();  // all four diagonal-block inverses
+    if (w < 4) {
+      f4 y4[4];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (2 * half == r0t) {
+      for (int bb = 0; bb < 4; ++bb) y4[bb] = b_rm(sE, LD, 16 * bb, 16 * w, lane);
+      solve_lower(y4, sA, sT, rs, lane);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int bb = r0t + j;
-          f4 s = zero4();
-          for (int bp = 0; bp < bb; ++bp) {
-            f4 af = a_rm(sA, LD, 16 * bb, 16 * bp, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] *= rs.eta[16 * bp + 4 * g + i];
-            mma16(s, af, bp == r0t ? E[0] : b_rm(sE, LD, 16 * bp, 16 * ct, lane));
-          }
-          const f4 rr = E[j] - s;
-          E[j] = zero4();
-          mma16(E[j], a_rm(sT + bb * 16 * TL, TL, 0, 0, lane), rr);
-          st_c(sE, LD, 16 * bb, 16 * ct, lane, E[j]);
-        }
-      }
-      __syncthreads();
+      for (int bb = 0; bb < 4; ++bb) st_c(sE, LD, 16 * bb, 16 * w, lane, y4[bb]);
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) st_c(sE, LD, 16 * (r0t + j), 16 * ct, lane, E[j]);
     __syncthreads();
+    E = b_rm(sE, LD, 16 * rt, 16 * ct, lane);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {  // db_i = E_i . (G x_i): into d eta_i, dL_i and dL_C
-      const int row = 16 * (r0t + j) + 4 * g + i;
-      const float db = sum16(E[j][i] * Y[j][i]);
-      const float f = __expf(LC - rs.L[row]);
-      if (cc == 0) {
-        pE[w][row] += db * f;
-        pL[w][row] -= db * rs.eta[row] * f;
-        lc += db * rs.eta[row] * f;
-      }
+  for (int i = 0; i < 4; ++i) {  // db_i = E_i . (G x_i): into d eta_i, dL_i and dL_C
+    const int row = 16 * rt + 4 * g + i;
+    const float db = sum16(E[i] * Y[i]);
+    const float f = __expf(LC - rs.L[row]);
+    if (cc == 0) {
+      pE[w][row] += db * f;
+      pL[w][row] -= db * rs.eta[row] * f;
+      lc += db * rs.eta[row] * f;
     }
   }
 
   // Phase 4: Z = P^T do; dE = diag(b) Y + diag(eta) Z; dX = diag(b) E G.
-  f4 dE[2], dX[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rt = r0t + j;
+  f4 dE, dX;
+  {
     f4 z = zero4(), u = zero4();
     for (int kb = rt; kb < 4; ++kb) mma16(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sO, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
@@ -651,86 +623,67 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rt + 4 * g + i;
       const float bb = rs.eta[row] * __expf(LC - rs.L[row]);
-      dE[j][i] = bb * Y[j][i] + rs.eta[row] * z[i];
-      dX[j][i] = bb * u[i];
-      const float de = sum16(z[i] * E[j][i]);
+      dE[i] = bb * Y[i] + rs.eta[row] * z[i];
+      dX[i] = bb * u[i];
+      const float de = sum16(z[i] * E[i]);
       if (cc == 0) pE[w][row] += de;
     }
   }
 
-  // Phase 5: dR = M^-T dE (= dv), blocks 3-2 by the second half, then 1-0; F1A: dv = dE.
+  // Phase 5: dR = M^-T dE (= dv) on the solver waves; F1A: dv = dE.
   if (!ADD) {
     __syncthreads();  // every wave is done reading G
+    st_c(sG, LD, 16 * rt, 16 * ct, lane, dE);
+    __syncthreads();
+    if (w < 4) {
+      f4 y4[4];
 #pragma unroll
-    for (int half = 1; half >= 0; --half) {
-      if (2 * half == r0t) {
+      for (int bb = 0; bb < 4; ++bb) y4[bb] = b_rm(sG, LD, 16 * bb, 16 * w, lane);
+      solve_upper(y4, sA, sT, rs, lane);
 #pragma unroll
-        for (int j = 1; j >= 0; --j) {
-          const int bb = r0t + j;
-          f4 s = zero4();
-          for (int bp = bb + 1; bp < 4; ++bp) {
-            f4 af = a_tr(sA, LD, 16 * bb, 16 * bp, lane);
-            af *= rs.eta[16 * bb + cc];
-            mma16(s, af, bp == r0t + 1 ? dE[1] : b_rm(sG, LD, 16 * bp, 16 * ct, lane));
-          }
-          const f4 rr = dE[j] - s;
-          dE[j] = zero4();
-          mma16(dE[j], a_tr(sT + bb * 16 * TL, TL, 0, 0, lane), rr);
-          st_c(sG, LD, 16 * bb, 16 * ct, lane, dE[j]);  // sG now holds dR
-        }
-      }
-      __syncthreads();
+      for (int bb = 0; bb < 4; ++bb) st_c(sG, LD, 16 * bb, 16 * w, lane, y4[bb]);  // sG now holds dR
     }
+    __syncthreads();
+    dE = b_rm(sG, LD, 16 * rt, 16 * ct, lane);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * (r0t + j) + 4 * g + i;
-      if (row < live) a.dv[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] = dE[j][i];
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    if (row < live) a.dv[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] = dE[i];
   }
 
   // Phase 6: dR S0 (into dX and dL_{i-1}); the C x C adjoints.
   if (!ADD) {
+    f4 s = zero4();
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rt = r0t + j;
-      f4 s = zero4();
+    for (int kb = 0; kb < 4; ++kb) mma16(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma16(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * rt + 4 * g + i;
-        const float am = __expf(rs.Lm[row]);
-        dX[j][i] -= am * s[i];
-        const float part = sum16(sX[row * LD + 16 * ct + cc] * s[i]);
-        if (cc == 0 && row > 0) pL[w][row - 1] -= am * part;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      const float am = __expf(rs.Lm[row]);
+      dX[i] -= am * s[i];
+      const float part = sum16(sX[row * LD + 16 * ct + cc] * s[i]);
+      if (cc == 0 && row > 0) pL[w][row - 1] -= am * part;
     }
   }
-  for (int k = w; k < 10; k += NWC) {
-    int rt, ctt;
-    lower_tile(k, rt, ctt);
-    adjoint_tile<ADD>(sA, sP, sG, sO, sE, rs, pL[w], pE[w], rt, ctt, lane);
+  if (w < 10) {
+    int tr, tc;
+    lower_tile(w, tr, tc);
+    adjoint_tile<ADD>(sA, sP, sG, sO, sE, rs, pL[w], pE[w], tr, tc, lane);
   }
   __syncthreads();
 
   // Phase 7: dQh += dPD X; dX += dPD^T Qh + dAG X + dAG^T X.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rt = r0t + j;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const f4 xb = b_rm(sX, LD, 16 * kb, 16 * ct, lane);
-      if (kb <= rt) {
-        mma16(dQ[j], a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
-        if (!ADD) mma16(dX[j], a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
-      }
-      if (kb >= rt) {
-        mma16(dX[j], a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * ct, lane));
-        if (!ADD) mma16(dX[j], a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
-      }
+  for (int kb = 0; kb < 4; ++kb) {
+    const f4 xb = b_rm(sX, LD, 16 * kb, 16 * ct, lane);
+    if (kb <= rt) {
+      mma16(dQ, a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
+      if (!ADD) mma16(dX, a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
+    }
+    if (kb >= rt) {
+      mma16(dX, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * ct, lane));
+      if (!ADD) mma16(dX, a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
     }
   }
   lc = sum64(lc);
@@ -764,16 +717,12 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rt = r0t + j;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * rt + 4 * g + i;
-      dX[j][i] += sCoef[row] * sX[row * LD + 16 * ct + cc];
-    }
-    st_c(sO, LD, 16 * rt, 16 * ct, lane, dQ[j]);
-    st_c(sE, LD, 16 * rt, 16 * ct, lane, dX[j]);
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    dX[i] += sCoef[row] * sX[row * LD + 16 * ct + cc];
   }
+  st_c(sO, LD, 16 * rt, 16 * ct, lane, dQ);
+  st_c(sE, LD, 16 * rt, 16 * ct, lane, dX);
   __syncthreads();
 
   // Through the feature map: dq_t for t < T; dk of the key that row r carries.
