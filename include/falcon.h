@@ -180,6 +180,35 @@ int falcon_chunk_fwd_varlen(const falcon_shape_t *shape, const int32_t *cu_seqle
                             const falcon_state_t *init, falcon_state_t *final_state,
                             void *o, void *stream);
 
+/* Bytes of device workspace falcon_chunk_fwd_segmented needs for this shape
+ * and segment count; 0 when the segmented form is not built for them: nseg
+ * must divide T, segments must hold at least Bw steps, the shape must have the
+ * two-kernel chunk-parallel path (see falcon_chunk_fwd_workspace), and F2 is
+ * excluded (its step differs per row of S, so a segment's map is not one
+ * matrix).  The workspace holds that path's scratch for B*nseg sequences of
+ * T/nseg steps plus six per-segment state arrays; it needs no initialisation. */
+size_t falcon_chunk_fwd_segmented_workspace(const falcon_shape_t *shape, int32_t nseg);
+
+/* The chunked forward pass with every sequence cut into nseg segments that run
+ * in parallel: the same function as falcon_chunk_fwd (up to rounding), for
+ * batches too small to fill the GPU.  A segment maps its incoming state S_0 to
+ * S_0 M + N ([P1] 三种等价形式: the chunk maps are affine and compose; [P2]
+ * 三种视角), so the call runs (1) the forward on all B*nseg segments from
+ * S_0 = 0 (giving N), (2) from S_0 = I (giving M + N), (3) the composition
+ * S_start[p] = S_start[p-1] M_{p-1} + N_{p-1} along each sequence, and (4) the
+ * forward from S_start, which writes o and the final state.  The carried key
+ * and window entering a segment come from the inputs.  The arrays are the same
+ * as falcon_chunk_fwd's ([B, T, H, d] is read as [B*nseg, T/nseg, H, d]); no
+ * per-chunk states.  init may alias final_state.  Errors: nseg < 1 or not
+ * dividing T -> FALCON_ERR_INVALID_ARG; NULL or misaligned workspace ->
+ * FALCON_ERR_INVALID_ARG; a shape or nseg the form is not built for ->
+ * FALCON_ERR_UNSUPPORTED; a short workspace -> FALCON_ERR_WORKSPACE. */
+int falcon_chunk_fwd_segmented(const falcon_shape_t *shape, int32_t nseg,
+                               const void *q, const void *k, const void *v,
+                               const float *beta, const float *log_lambda,
+                               const falcon_state_t *init, falcon_state_t *final_state,
+                               void *o, void *workspace, size_t workspace_bytes, void *stream);
+
 /* One token of the recurrent form ([P1] 三种等价形式 form A; [P2] 三种视角):
  * reads q, k [B, H, dk], v [B, H, dv], beta [B, H] (F2/F2A: [B, H, dv]) and
  * log_lambda [B, H]; updates `state` in place (S, x_prev and, for F3/F3A with

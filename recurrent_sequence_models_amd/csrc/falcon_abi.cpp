@@ -321,3 +321,142 @@ int falcon_chunk_bwd(const falcon_shape_t *s, const void *q, const void *k, cons
 }
 
 }  // extern "C"
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Byte offsets of the segment-parallel workspace: the two-kernel path's scratch
+// for B*P sequences of T/P steps, then the per-segment state arrays.
+struct SegLayout {
+  size_t split, S, N, MN, x, wx, wv, Sf, xf, wxf, wvf, total;
+};
+
+bool seg_layout(const falcon_shape_t *s, int nseg, SegLayout &L) {
+  if (check_shape(s, false) != FALCON_OK || nseg < 1 || s->seqlen % nseg != 0) return false;
+  if (s->variant == FALCON_2) return false;  // F2: a different state map for every row of S
+  const int Ts = s->seqlen / nseg;
+  const int window = windowed(s->variant) ? s->window : 1;
+  if (Ts < window) return false;
+  const int64_t bph = (int64_t)s->batch * nseg * s->heads;
+  if (bph * Ts > INT32_MAX || bph > INT32_MAX / 2) return false;
+  const size_t split = falcon::chunk_fwd_split_workspace(s->variant, s->dtype == FALCON_BF16, s->dk, s->dv, s->chunk,
+                                                         s->window, (int)bph, Ts);
+  if (split == 0) return false;
+  const size_t mat = (size_t)bph * s->dv * s->dk * 4, vec = (size_t)bph * s->dk * 4;
+  const size_t wx = (size_t)bph * (window - 1) * s->dk * 4, wv = (size_t)bph * (window - 1) * s->dv * 4;
+  size_t off = 0;
+  auto take = [&](size_t n) { const size_t o = off; off = align256(off + n); return o; };
+  L.split = take(split);
+  L.S = take(mat);
+  L.N = take(mat);
+  L.MN = take(mat);
+  L.x = take(vec);
+  L.wx = take(wx);
+  L.wv = take(wv);
+  L.Sf = take(mat);
+  L.xf = take(vec);
+  L.wxf = take(wx);
+  L.wvf = take(wv);
+  L.total = off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t falcon_chunk_fwd_segmented_workspace(const falcon_shape_t *s, int32_t nseg) {
+  SegLayout L;
+  return seg_layout(s, nseg, L) ? L.total : 0;
+}
+
+int falcon_chunk_fwd_segmented(const falcon_shape_t *s, int32_t nseg, const void *q, const void *k, const void *v,
+                               const float *beta, const float *log_lambda, const falcon_state_t *init,
+                               falcon_state_t *final_state, void *o, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  int st = check_shape(s, false);
+  if (st != FALCON_OK) return st;
+  if ((st = check_io(q, k, v, beta, log_lambda, o)) != FALCON_OK) return st;
+  if (init && (st = check_state(init, s)) != FALCON_OK) return st;
+  if (final_state && (st = check_state(final_state, s)) != FALCON_OK) return st;
+  if (nseg < 1 || s->seqlen % nseg != 0) return FALCON_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return FALCON_ERR_INVALID_ARG;
+  SegLayout L;
+  if (!seg_layout(s, nseg, L)) return FALCON_ERR_UNSUPPORTED;
+  if (workspace_bytes < L.total) return FALCON_ERR_WORKSPACE;
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  auto F = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
+  const bool bf16 = s->dtype == FALCON_BF16;
+  const bool win = windowed(s->variant) && s->window > 1;
+  const int window = windowed(s->variant) ? s->window : 1;
+  const int P = nseg, Ts = s->seqlen / nseg;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  falcon::SegArgs g{};
+  g.k = k; g.v = v;
+  g.S0 = init ? init->S : nullptr;
+  g.xprev0 = init ? init->x_prev : nullptr;
+  g.winx0 = (init && win) ? init->win_x : nullptr;
+  g.winv0 = (init && win) ? init->win_v : nullptr;
+  g.xseg = F(L.x); g.wxseg = F(L.wx); g.wvseg = F(L.wv);
+  g.Nseg = F(L.N); g.MNseg = F(L.MN); g.Sseg = F(L.S);
+  g.B = s->batch; g.T = s->seqlen; g.H = s->heads; g.P = P;
+  g.dk = s->dk; g.dv = s->dv; g.window = window; g.align = s->align;
+  g.eps_phi = s->eps_phi;
+
+  // One forward over all B*P segments, each a sequence of Ts steps (the arrays
+  // [B,T,H,d] read as [B*P,Ts,H,d]).
+  auto forward = [&](const float *S0, float *S_out, float *x_out, float *wx_out, float *wv_out, void *out) {
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = log_lambda;
+    a.S0 = S0;
+    a.xprev0 = F(L.x);
+    a.winx0 = win ? F(L.wx) : nullptr;
+    a.winv0 = win ? F(L.wv) : nullptr;
+    a.S_out = S_out; a.xprev_out = x_out; a.winx_out = wx_out; a.winv_out = wv_out;
+    a.o = out;
+    a.chunk_states = nullptr;
+    a.B = s->batch * P; a.T = Ts; a.H = s->heads;
+    a.nchunks = (Ts + s->chunk - 1) / s->chunk;
+    a.window = window;
+    a.align = s->align;
+    a.log_eps_gamma = std::log(s->eps_gamma);
+    a.eps_phi = s->eps_phi;
+    a.eps_eta = s->eps_eta;
+    a.write_tail = 1;
+    return falcon::launch_chunk_fwd_split(s->variant, bf16, s->dk, s->dv, s->chunk, window, a, ws + L.split, hs);
+  };
+  if (falcon::launch_seg_boundary(bf16, g, hs) != hipSuccess) return FALCON_ERR_HIP;
+  if (P > 1) {
+    if (forward(nullptr, F(L.N), nullptr, nullptr, nullptr, nullptr) != hipSuccess) return FALCON_ERR_HIP;
+    if (falcon::launch_seg_identity(F(L.S), s->batch * P * s->heads, s->dv, s->dk, hs) != hipSuccess)
+      return FALCON_ERR_HIP;
+    if (forward(F(L.S), F(L.MN), nullptr, nullptr, nullptr, nullptr) != hipSuccess) return FALCON_ERR_HIP;
+    if (falcon::launch_seg_combine(g, hs) != hipSuccess) return FALCON_ERR_HIP;
+  } else if (init) {
+    if (hipMemcpyAsync(F(L.S), init->S, (size_t)s->batch * s->heads * s->dv * s->dk * 4, hipMemcpyDeviceToDevice,
+                       hs) != hipSuccess)
+      return FALCON_ERR_HIP;
+  }
+  const float *S_in = (P > 1 || init) ? F(L.S) : nullptr;
+  if (forward(S_in, F(L.Sf), F(L.xf), win ? F(L.wxf) : nullptr, win ? F(L.wvf) : nullptr, o) != hipSuccess)
+    return FALCON_ERR_HIP;
+  if (final_state) {  // the last segment's final state is the sequence's
+    const size_t H = s->heads;
+    auto copy_last = [&](void *dst, const float *src, size_t per_bh) {
+      const size_t row = H * per_bh * 4;
+      return hipMemcpy2DAsync(dst, row, src + (size_t)(P - 1) * H * per_bh, (size_t)P * row, row, s->batch,
+                              hipMemcpyDeviceToDevice, hs);
+    };
+    if (copy_last(final_state->S, F(L.Sf), (size_t)s->dv * s->dk) != hipSuccess) return FALCON_ERR_HIP;
+    if (copy_last(final_state->x_prev, F(L.xf), (size_t)s->dk) != hipSuccess) return FALCON_ERR_HIP;
+    if (win) {
+      if (copy_last(final_state->win_x, F(L.wxf), (size_t)(window - 1) * s->dk) != hipSuccess) return FALCON_ERR_HIP;
+      if (copy_last(final_state->win_v, F(L.wvf), (size_t)(window - 1) * s->dv) != hipSuccess) return FALCON_ERR_HIP;
+    }
+  }
+  return FALCON_OK;
+}
+
+}  // extern "C"

@@ -54,6 +54,18 @@ struct BwdArgs {
   float log_eps_gamma, eps_phi, eps_eta;
 };
 
+// The segment-parallel forward: per-segment carried keys / windows and the
+// composition of the segments' state maps.
+struct SegArgs {
+  const void *k, *v;                          // [B,T,H,d] in the input dtype
+  const float *S0, *xprev0, *winx0, *winv0;   // the caller's incoming state, or null (zeros)
+  float *xseg, *wxseg, *wvseg;                // [B*P,H,dk], [B*P,H,Bw-1,dk|dv]: entering each segment
+  const float *Nseg, *MNseg;                  // [B*P,H,dv,dk]: segment end states from S0 = 0 and S0 = I
+  float *Sseg;                                // [B*P,H,dv,dk]: the state entering each segment
+  int B, T, H, P, dk, dv, window, align;
+  float eps_phi;
+};
+
 // Return hipSuccess or the launch error.  `variant` is falcon_variant_t,
 // `bf16` selects the input dtype.  Unsupported combinations return
 // hipErrorInvalidValue (the host validates first, so this is a safety net).
@@ -65,6 +77,10 @@ hipError_t launch_step(int variant, bool bf16, int dk, int dv, const StepArgs &a
 bool chunk_bwd_supported(int variant, int dk, int dv, int chunk, int window);
 size_t chunk_bwd_workspace(int B, int H, int T);
 hipError_t launch_chunk_bwd(int variant, bool bf16, const BwdArgs &a, hipStream_t stream);
+
+hipError_t launch_seg_boundary(bool bf16, const SegArgs &a, hipStream_t stream);
+hipError_t launch_seg_identity(float *S, int nmat, int dv, int dk, hipStream_t stream);
+hipError_t launch_seg_combine(const SegArgs &a, hipStream_t stream);
 
 // The per-shape d_v split of the forward kernel (channels per workgroup = dv / nsplit).
 int choose_nsplit(int variant, bool bf16, int dk, int dv, int chunk, int batch_heads);

@@ -967,7 +967,7 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
       for (int q = 0; q + 1 <= qm; q += 2) mmap(O, mkp(Eb[q], Eb[q + 1]), ldp(Pm + frag_off(S::pbase(ps), q, lane)));
       if (!(qm & 1)) mma16(O, Eb[qm], ld4(Pm + frag_off(S::pbase(ps), qm, lane)));
       const int srow = 16 * ps + cl, t = c0 + srow;
-      if (srow < CS && t < T)
+      if (op && srow < CS && t < T)  // no outputs when o is null (the segment-map passes)
         *reinterpret_cast<Frag *>(op + ((size_t)(tok0 + t) * H + h) * D + Z::DS * sp + 16 * cw + 4 * g4) = cvt<OpT>(O);
     }
   };

@@ -22,7 +22,8 @@ WINDOWED = ("F3", "F3A")
 
 EXPORTS = ("falcon_abi_version", "falcon_status_string", "falcon_chunk_fwd_workspace",
            "falcon_chunk_fwd", "falcon_chunk_fwd_varlen", "falcon_recurrent_step",
-           "falcon_chunk_bwd_workspace", "falcon_chunk_bwd")
+           "falcon_chunk_bwd_workspace", "falcon_chunk_bwd",
+           "falcon_chunk_fwd_segmented_workspace", "falcon_chunk_fwd_segmented")
 
 
 class Shape(ctypes.Structure):
@@ -68,6 +69,11 @@ def lib() -> ctypes.CDLL:
         L.falcon_chunk_fwd_varlen.argtypes = [P(Shape), V, V, V, V, V, V, P(State), P(State), V, V]
         L.falcon_recurrent_step.restype = I
         L.falcon_recurrent_step.argtypes = [P(Shape), V, V, V, V, V, P(State), V, V]
+        L.falcon_chunk_fwd_segmented_workspace.restype = S
+        L.falcon_chunk_fwd_segmented_workspace.argtypes = [P(Shape), ctypes.c_int32]
+        L.falcon_chunk_fwd_segmented.restype = I
+        L.falcon_chunk_fwd_segmented.argtypes = [P(Shape), ctypes.c_int32, V, V, V, V, V, P(State), P(State), V, V,
+                                                 S, V]
         L.falcon_chunk_bwd_workspace.restype = S
         L.falcon_chunk_bwd_workspace.argtypes = [P(Shape)]
         L.falcon_chunk_bwd.restype = I
@@ -336,3 +342,54 @@ def chunk_bwd(variant, q, k, v, beta, log_lambda, do, chunk_states, *, init=None
     res["dS0"] = d_init["S"] if d_init else None
     res["dx_prev0"] = d_init["x_prev"] if d_init else None
     return res
+
+
+def segmented_workspace_bytes(variant, dtype, batch, seqlen, heads, dk, dv, nseg, chunk=64, window=1,
+                              eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix"):
+    """falcon_chunk_fwd_segmented_workspace (0: not built for the shape or nseg)."""
+    shape = make_shape(variant, dtype, batch, seqlen, heads, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta,
+                       align)
+    return int(lib().falcon_chunk_fwd_segmented_workspace(ctypes.byref(shape), int(nseg)))
+
+
+def chunk_fwd_segmented(variant, q, k, v, beta, log_lambda, nseg, *, chunk=64, window=1, init=None, final=True,
+                        eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, out=None, workspace=None, stream=None,
+                        align="prefix"):
+    """falcon_chunk_fwd_segmented on torch tensors: the chunked forward with every
+    sequence cut into ``nseg`` segments run in parallel (T % nseg == 0).  Same
+    arguments as ``chunk_fwd``; ``workspace`` is None (allocate) or a uint8 device
+    tensor.  Returns (o, final_state)."""
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    dt = {torch.float32: "fp32", torch.bfloat16: "bf16"}.get(q.dtype)
+    if dt is None:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    _check_tensor("q", q, q.dtype, (B, T, H, dk), dev)
+    _check_tensor("k", k, q.dtype, (B, T, H, dk), dev)
+    _check_tensor("v", v, q.dtype, (B, T, H, dv), dev)
+    bshape = (B, T, H, dv) if variant in PER_CHANNEL else (B, T, H)
+    _check_tensor("beta", beta, torch.float32, bshape, dev)
+    _check_tensor("log_lambda", log_lambda, torch.float32, (B, T, H), dev)
+    if out is None:
+        out = torch.empty(B, T, H, dv, dtype=q.dtype, device=dev)
+    _check_tensor("o", out, q.dtype, (B, T, H, dv), dev)
+    if final is True:
+        final = new_state(B, H, dk, dv, window if variant in WINDOWED else 1, dev)
+    elif final is False:
+        final = None
+    shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
+    L = lib()
+    need = int(L.falcon_chunk_fwd_segmented_workspace(ctypes.byref(shape), int(nseg)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check_tensor("workspace", workspace, torch.uint8, (workspace.numel(),), dev)
+    st_in, st_out = _state(init), _state(final)
+    status = L.falcon_chunk_fwd_segmented(ctypes.byref(shape), int(nseg), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                          _ptr(log_lambda), ctypes.byref(st_in) if st_in else None,
+                                          ctypes.byref(st_out) if st_out else None, _ptr(out), _ptr(workspace),
+                                          workspace.numel(), _stream(stream))
+    if status != OK:
+        raise FalconError(status, "falcon_chunk_fwd_segmented")
+    return out, final

@@ -234,3 +234,45 @@ def test_bwd_rejects_on_host():
                dict(dk=128, dv=128)):
         assert call_bwd(good_shape(**kw)) == F.ERR_UNSUPPORTED, kw
     assert call_bwd(ok, wsb=bwd_workspace() - 1) == F.ERR_WORKSPACE
+
+
+def seg_workspace(nseg, **kw):
+    return F.lib().falcon_chunk_fwd_segmented_workspace(ctypes.byref(good_shape(**kw)), nseg)
+
+
+def call_seg(shape, nseg, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, init=None, final=None, o=FAKE, ws=FAKE,
+             wsb=1 << 40):
+    L = F.lib()
+    return L.falcon_chunk_fwd_segmented(ctypes.byref(shape) if shape is not None else None, nseg, q, k, v, beta,
+                                        g, ctypes.byref(init) if init else None,
+                                        ctypes.byref(final) if final else None, o, ws, wsb, None)
+
+
+def test_segmented_workspace_size():
+    """Built where the two-kernel path is, for nseg dividing T with segments of
+    at least Bw steps, except F2; grows with the segment count (per-segment states)."""
+    w1 = seg_workspace(1, seqlen=512)
+    w4 = seg_workspace(4, seqlen=512)
+    assert w1 > 0 and w4 > w1 and w4 % 256 == 0
+    assert seg_workspace(3, seqlen=512) == 0                       # 3 does not divide 512
+    assert seg_workspace(0, seqlen=512) == 0
+    assert seg_workspace(4, seqlen=512, variant="F2") == 0         # per-row maps
+    assert seg_workspace(4, seqlen=512, variant="F2A") > 0
+    assert seg_workspace(4, seqlen=512, variant="F3", window=4) > 0
+    assert seg_workspace(128, seqlen=256, variant="F3", window=4) == 0   # segments of 2 < Bw steps
+    assert seg_workspace(4, seqlen=512, dtype="fp32", dk=128, dv=128) == 0   # no two-kernel path
+
+
+@cpu_only
+def test_segmented_rejects_on_host():
+    ok = good_shape(seqlen=512)
+    assert call_seg(None, 4) == F.ERR_INVALID_ARG
+    assert call_seg(ok, 0) == F.ERR_INVALID_ARG
+    assert call_seg(ok, 3) == F.ERR_INVALID_ARG
+    assert call_seg(ok, 4, ws=None) == F.ERR_INVALID_ARG
+    assert call_seg(ok, 4, ws=ctypes.c_void_p(0x10008)) == F.ERR_INVALID_ARG
+    assert call_seg(ok, 4, o=None) == F.ERR_INVALID_ARG
+    assert call_seg(good_shape(seqlen=512, variant="F2"), 4) == F.ERR_UNSUPPORTED
+    assert call_seg(ok, 4, wsb=seg_workspace(4, seqlen=512) - 1) == F.ERR_WORKSPACE
+    for kw in INVALID_SHAPES:
+        assert call_seg(good_shape(**kw), 1) == F.ERR_INVALID_ARG, kw
