@@ -15,7 +15,8 @@ average device time of the forward path used for the roofline.  Paths
 built, else the fused kernel); "split" passes a workspace (allocated once
 outside the timed region): the prep kernel over all systems, then the state
 scan.  "auto" (default) takes the faster one measured per shape class: split
-for Falcon-3 windows and head dim 128, one-pass otherwise.
+for Falcon-3 windows and head dim 128, one-pass otherwise.  --segments P runs
+the segment-parallel form instead (every sequence cut into P segments).
 
 --backward times falcon_chunk_bwd instead (Falcon-1 or 1A at the 130M-layer
 shape): the gradients of every input from the forward's per-chunk states,
@@ -318,6 +319,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=("auto", "onepass", "split"), default="auto",
                     help="forward path: one-pass (no workspace), split (workspace), or auto")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="cut every sequence into this many segments run at once (segment-parallel form)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -336,8 +339,8 @@ def main():
 
     import torch
     import workloads as W
-    from recurrent_sequence_models_amd import chunk_fwd, new_state
-    from recurrent_sequence_models_amd.falcon import workspace_bytes
+    from recurrent_sequence_models_amd import chunk_fwd, chunk_fwd_segmented, new_state
+    from recurrent_sequence_models_amd.falcon import segmented_workspace_bytes, workspace_bytes
 
     w = W.WORKLOADS[args.workload]
     variant = args.variant
@@ -363,7 +366,22 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else False
     path = "split" if ws_bytes else "onepass"
 
+    if args.segments > 0:
+        ws_bytes = segmented_workspace_bytes(variant, w.dtype, w.batch, w.seqlen, w.heads, w.dk, w.dv, args.segments,
+                                             w.chunk, window)
+        if ws_bytes == 0:
+            print(f"the segmented form is not built for {variant} {w.name} with {args.segments} segments",
+                  file=sys.stderr)
+            sys.exit(2)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        path = f"segmented x{args.segments}"
+
     def call(d):
+        if args.segments > 0:
+            chunk_fwd_segmented(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], args.segments,
+                                chunk=w.chunk, window=window, final=d["final"], out=d["o"], stream=stream,
+                                workspace=ws)
+            return
         chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk, window=window,
                   final=d["final"], out=d["o"], stream=stream, workspace=ws)
 
@@ -404,7 +422,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
     roof["traffic"] = measured_traffic(f"{path} {variant} {w.name}")
-    roof["kernel"] = ("chunk_prep + chunk_scan" if path == "split" else
+    roof["kernel"] = ("seg_boundary + 3 x (chunk_prep + chunk_scan) + seg_combine" if path.startswith("segmented") else
+                      "chunk_prep + chunk_scan" if path == "split" else
                       "chunk_scan (one-pass)" if (w.dtype == "bf16" and w.dk <= 64 and w.chunk <= 64) else
                       "chunk_fwd_pipe" if w.dk <= 64 else "chunk_fwd_rows")
     roof["path"] = path
@@ -428,7 +447,7 @@ def main():
                                f"T{w.seqlen} d{w.dk} chunk {w.chunk}" + (f" window {window}" if window > 1 else "")
                                + f", {w.dtype} q/k/v/o, fp32 state",
                    "variant": variant, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
-                   "head_dim": w.dk, "chunk": w.chunk, "window": window},
+                   "head_dim": w.dk, "chunk": w.chunk, "window": window, "segments": max(args.segments, 1)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
