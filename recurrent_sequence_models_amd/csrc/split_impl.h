@@ -213,9 +213,15 @@ __device__ __forceinline__ uint4 scale_pack(const float *x, float f) {
 // diagonal blocks, finishes them with the decay / norm / step factors and
 // writes them, with the per-row factors (wave 3), into the image at img (global
 // memory for the prep kernel, LDS for the one-pass kernel).
-template <int VAR, typename IT, int D, int C, int BW>
-__device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const float *G, unsigned char *img, bool sep,
-                                             float Llast, int w, int lane) {
+// The products need only the rows, so they are issued first; `rows()` then
+// fills G (the one-pass kernel computes it there, while the products run) and
+// returns the system's total log-decay L_last.  The finishing code is built
+// twice, for separable (L_last >= -160) and per-element decay factors, so each
+// version is one straight-line block in which the diagonal solve and the
+// other tiles' finishing interleave.
+template <int VAR, typename IT, int D, int C, int BW, typename RowsFn>
+__device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const float *G, unsigned char *img, int w,
+                                             int lane, RowsFn &&rows) {
   using S = Split<VAR, IT, D, C, BW>;
   using OpT = IT;
   using Frag = typename Op<OpT>::frag;
@@ -244,10 +250,10 @@ __device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const flo
   // column 16q + 4g + i), the consumers' A-operand fragment.  Off-diagonal Gram
   // blocks are wholly visible (steps do not straddle blocks); score blocks see
   // the columns whose step is at most the row's.
-  auto finish = [&](const f4 &acc, int isP, int p, int q) {
+  auto finish = [&](auto sepc, const f4 &acc, int isP, int p, int q) {
     const int row = 16 * p + cl;
     f4 val;
-    if (sep) {
+    if constexpr (decltype(sepc)::value) {
       const f4 ec = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * q + 4 * g4);
       const float er = G[(isP ? R_EP : R_EA) * C + row];
 #pragma unroll
@@ -270,10 +276,10 @@ __device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const flo
     *reinterpret_cast<Frag *>(dst) = cvt<OpT>(val);
   };
   // diagonal block p: F1/F3 -> T_pp (A-layout); F2 -> the 4x4 diagonal coefficients and A_pp without them
-  auto diag = [&](const f4 &acc, int p) {   // acc: <x_{16p+4g+i}, x_{16p+c}> (symmetric)
+  auto diag = [&](auto sepc, const f4 &acc, int p) {   // acc: <x_{16p+4g+i}, x_{16p+c}> (symmetric)
     const int r0 = 4 * g4;
     f4 NA4, NC4;   // N[16p+c][16p+4g+i] (A-layout) and N[16p+4g+i][16p+c] (C-layout), strictly earlier steps
-    if (sep) {
+    if constexpr (decltype(sepc)::value) {
       const f4 ea4 = *reinterpret_cast<const f4 *>(G + R_EA * C + 16 * p + r0);
       const f4 ec4 = *reinterpret_cast<const f4 *>(G + R_EC * C + 16 * p + r0);
       const float ea1 = G[R_EA * C + 16 * p + cl], ec1 = G[R_EC * C + 16 * p + cl];
@@ -317,10 +323,13 @@ __device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const flo
         Y[0] = w[0] - Y[1] * n10 - Y[2] * n20 - Y[3] * n30;
       };
       local(Z);
+      // the sweeps run in the operand type: T_pp is stored in it, and a bf16
+      // sweep is one MFMA instead of four fp32 ones on this serial chain
+      const Frag NoCo = cvt<OpT>(NoC);
 #pragma unroll
       for (int it = 0; it < 3; ++it) {
         f4 cpl = zero4();
-        mma16(cpl, NoC, Y);   // fp32: C-layout of N_o^T Y^T = A-layout of Y N_o
+        mma16(cpl, NoCo, cvt<OpT>(Y));   // C-layout of N_o^T Y^T = A-layout of Y N_o
         local(Z - cpl);
       }
       *reinterpret_cast<Frag *>(gT + (p * 64 + lane) * 4) = cvt<OpT>(Y);
@@ -339,7 +348,7 @@ __device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const flo
       *reinterpret_cast<Frag *>(gT + (p * 64 + lane) * 4) = cvt<OpT>(NoA);
     }
   };
-  auto rowfac = [&]() {
+  auto rowfac = [&](float Llast) {
     if (lane < C) {
       const float L = G[R_LC * C + lane], Lm = G[R_LM * C + lane];
       gF[F_GAM * C + lane] = __expf(Lm) * G[R_IK * C + lane];
@@ -364,10 +373,15 @@ __device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const flo
     if constexpr (J.diag >= 0) dacc = tile(Dop, Dop);
 #pragma unroll
     for (int j = 0; j < J.n; ++j) acc[j] = tile(Aop[j], Bop[j]);
-    if constexpr (J.diag >= 0) diag(dacc, J.diag);
+    const float Llast = rows();
+    auto tail = [&](auto sepc) __attribute__((always_inline)) {
+      if constexpr (J.diag >= 0) diag(sepc, dacc, J.diag);
 #pragma unroll
-    for (int j = 0; j < J.n; ++j) finish(acc[j], J.isP[j], J.p[j], J.q[j]);
-    if constexpr (w == S::NPW - 1) rowfac();
+      for (int j = 0; j < J.n; ++j) finish(sepc, acc[j], J.isP[j], J.p[j], J.q[j]);
+      if constexpr (w == S::NPW - 1) rowfac(Llast);
+    };
+    if (Llast >= -160.f) tail(std::true_type());
+    else tail(std::false_type());
   };
   if (w == 0) run(std::integral_constant<int, 0>());
   else if (w == 1) run(std::integral_constant<int, 1>());
@@ -556,7 +570,7 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
   }
   __syncthreads();
 
-  derive_image<VAR, IT, D, C, BW>(sX, sQ, sR, img, sep, Llast, pw, lane);
+  derive_image<VAR, IT, D, C, BW>(sX, sQ, sR, img, pw, lane, [&]() { return Llast; });
 }
 
 // ============================== scan kernel ==============================
@@ -973,67 +987,70 @@ __global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdAr
   };
 
   // ================= derive waves (one-pass form) =================
-  // Per-row arrays of system c from the staged norms and gates (lane = row; each
-  // derive wave keeps its own copy), then the wave's share of the image tiles.
+  // The wave's share of the image tiles of system c; while its products run,
+  // the per-row arrays (lane = row; each derive wave keeps its own copy) are
+  // computed from the staged norms and gates, loaded first.
   auto derive = [&](int c) __attribute__((always_inline)) {
     const int si = c % 3, c0 = c * CS;
     float *G = sG[ONE ? dw : 0];
     const float *nk = sNrm[si][0], *nq = sNrm[si][1], *gg = sGB[si][0], *gb = sGB[si][1];
+    const int lr = lane < C ? lane : 0;
     const float g2 = lane < CSP ? gg[lane] : 0.f;     // lane = step
-    const float L = wave_inclusive_scan(g2);
-    const float Llast = __shfl(L, CS - 1);
-    const bool sep = Llast >= -160.f;
-    const float Lref = 0.5f * Llast;
-    if (lane >= C) {
-      // rows past the system: no per-row entries
-    } else if constexpr (BW == 1) {   // lane = row = step
-      const bool carried = c0 + lane - 1 + a.align < 0;
-      const float sk = nk[lane], sq = nq[lane];
-      const float ik = carried ? 1.f : safe_rsqrt(sk + a.eps_phi);
-      const float iq = safe_rsqrt(sq + a.eps_phi);
-      const float inv = fast_rcp(a.eps_eta + sk * ik * ik);
-      const float eta = PERCH ? inv : gb[lane] * inv;
-      const float cf = PERCH ? ik : ik * eta;
-      G[R_LC * C + lane] = L;
-      G[R_LM * C + lane] = L - g2;
-      G[R_IK * C + lane] = ik;
-      G[R_IQ * C + lane] = iq;
-      G[R_CF * C + lane] = cf;
-      G[R_ETA * C + lane] = eta;
-      if (sep) {
-        G[R_EP * C + lane] = __expf(L - Lref) * iq;
-        G[R_EA * C + lane] = __expf(L - g2 - Lref) * ik;
-        G[R_EC * C + lane] = __expf(Lref - L) * cf;
-      }
-    } else {   // lane = virtual row r (step r / BW); step values come from lane = step
-      const int st = lane / BW, j = c0 + st - BW + 1 + lane % BW;
-      const float sk = nk[lane];
-      const float ik = j - 1 + a.align < 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
-      const float e2 = sk * ik * ik;
-      const float e2new = __shfl(e2, st * BW + BW - 1);   // the step's own (newest) pair
-      const float bq = lane < CSP ? gb[lane] : 0.f;
-      const float Ls = __shfl(L, st), gs = __shfl(g2, st), bs = __shfl(bq, st);
-      const float w = bs * fast_rcp(a.eps_eta + e2new) * (1.f / BW);
-      const float cf = ik * w;
-      G[R_LC * C + lane] = Ls;
-      G[R_LM * C + lane] = Ls - gs;
-      G[R_IK * C + lane] = ik;
-      G[R_CF * C + lane] = cf;
-      G[R_ETA * C + lane] = w;
-      if (sep) {
-        G[R_EA * C + lane] = __expf(Ls - gs - Lref) * ik;
-        G[R_EC * C + lane] = __expf(Lref - Ls) * cf;
-      }
-      if (lane < CSP) {
-        const float iq = (lane < CS && c0 + lane < T) ? safe_rsqrt(nq[lane] + a.eps_phi) : 0.f;
+    const float sk = nk[lr], sqn = lane < CSP ? nq[lane] : 0.f, gbl = lane < CSP ? gb[lane] : 0.f;
+    auto rows = [&]() __attribute__((always_inline)) -> float {
+      const float L = wave_inclusive_scan(g2);
+      const float Llast = __shfl(L, CS - 1);
+      const bool sep = Llast >= -160.f;
+      const float Lref = 0.5f * Llast;
+      if (lane >= C) {
+        // rows past the system: no per-row entries
+      } else if constexpr (BW == 1) {   // lane = row = step
+        const bool carried = c0 + lane - 1 + a.align < 0;
+        const float ik = carried ? 1.f : safe_rsqrt(sk + a.eps_phi);
+        const float iq = safe_rsqrt(sqn + a.eps_phi);
+        const float inv = fast_rcp(a.eps_eta + sk * ik * ik);
+        const float eta = PERCH ? inv : gbl * inv;
+        const float cf = PERCH ? ik : ik * eta;
+        G[R_LC * C + lane] = L;
+        G[R_LM * C + lane] = L - g2;
+        G[R_IK * C + lane] = ik;
         G[R_IQ * C + lane] = iq;
-        G[R_LQ * C + lane] = L;
-        G[R_GQ * C + lane] = g2;
-        if (sep) G[R_EP * C + lane] = __expf(L - Lref) * iq;
+        G[R_CF * C + lane] = cf;
+        G[R_ETA * C + lane] = eta;
+        if (sep) {
+          G[R_EP * C + lane] = __expf(L - Lref) * iq;
+          G[R_EA * C + lane] = __expf(L - g2 - Lref) * ik;
+          G[R_EC * C + lane] = __expf(Lref - L) * cf;
+        }
+      } else {   // lane = virtual row r (step r / BW); step values come from lane = step
+        const int st = lane / BW, j = c0 + st - BW + 1 + lane % BW;
+        const float ik = j - 1 + a.align < 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
+        const float e2 = sk * ik * ik;
+        const float e2new = __shfl(e2, st * BW + BW - 1);   // the step's own (newest) pair
+        const float Ls = __shfl(L, st), gs = __shfl(g2, st), bs = __shfl(gbl, st);
+        const float w = bs * fast_rcp(a.eps_eta + e2new) * (1.f / BW);
+        const float cf = ik * w;
+        G[R_LC * C + lane] = Ls;
+        G[R_LM * C + lane] = Ls - gs;
+        G[R_IK * C + lane] = ik;
+        G[R_CF * C + lane] = cf;
+        G[R_ETA * C + lane] = w;
+        if (sep) {
+          G[R_EA * C + lane] = __expf(Ls - gs - Lref) * ik;
+          G[R_EC * C + lane] = __expf(Lref - Ls) * cf;
+        }
+        if (lane < CSP) {
+          const float iq = (lane < CS && c0 + lane < T) ? safe_rsqrt(sqn + a.eps_phi) : 0.f;
+          G[R_IQ * C + lane] = iq;
+          G[R_LQ * C + lane] = L;
+          G[R_GQ * C + lane] = g2;
+          if (sep) G[R_EP * C + lane] = __expf(L - Lref) * iq;
+        }
       }
-    }
-    wave_lds_sync();
-    derive_image<VAR, IT, D, C, BW>(sX[c % NXS], sQ[c % NQS], G, sImg[si], sep, Llast, dw, lane);
+      wave_lds_sync();
+      return Llast;
+    };
+    derive_image<VAR, IT, D, C, BW>(sX[c % NXS], sQ[c % NQS], G, sImg[si], dw, lane, rows);
   };
 
   // ---------------- scan: iteration i works on system i (state), i-1 (outputs), i+1 (staging) ----------------
