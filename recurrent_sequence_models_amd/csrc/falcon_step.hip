@@ -28,10 +28,22 @@ __device__ __forceinline__ float ld1(const float *p) { return *p; }
 __device__ __forceinline__ void st1(__bf16 *p, float x) { *p = (__bf16)x; }
 __device__ __forceinline__ void st1(float *p, float x) { *p = x; }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {  // x + x of the lane CTRL names (DPP, no LDS trip)
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// Sum over the LPR (4..64) lanes of one row, in every lane of it: butterflies
+// inside groups of 4, 8 and 16 lanes by DPP (quad permutations, half-row and
+// row mirrors), across 16-lane rows by lane shuffles.
 template <int LPR>
-__device__ __forceinline__ float row_sum(float x) {  // sum over the LPR lanes of one row
-#pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) x += __shfl_xor(x, off);
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(LPR >= 4 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "row of 4..64 lanes");
+  x = dpp_add<0xB1>(x);                                // quad_perm [1,0,3,2]
+  x = dpp_add<0x4E>(x);                                // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 8) x = dpp_add<0x141>(x);       // row_half_mirror
+  if constexpr (LPR >= 16) x = dpp_add<0x140>(x);      // row_mirror
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+  if constexpr (LPR >= 64) x += __shfl_xor(x, 32);
   return x;
 }
 
