@@ -107,6 +107,12 @@ def bench_decode(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_s = sum(a.elapsed_time(b) for a, b in ev) / K / 1e3
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     per_state = 2 * d * d * 4 + 2 * d * 4 + (2 * d + 2 * d) * 2 + 8 + (2 * (bw - 1) * 2 * d * 4 if bw > 1 else 0)
     nbytes = B * H * per_state
     ach = nbytes / kern_s / 1e9
@@ -118,7 +124,9 @@ def bench_decode(args):
         "config": {"workload": f"Falcon-{args.variant[1:]} recurrent step, B{B} H{H} d{d}, fp32 state, bf16 q/k/v/o",
                    "variant": args.variant, "window": bw},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "step_kernel",
+                     "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"decode {args.variant} b{B} h{H} d{d} w{bw}", DECODE_SOURCES),
+                     "kernel": "step_kernel",
                      "kernel_us": {"mean": round(kern_s * 1e6, 2)}, "alg_bytes": nbytes},
     }
 
@@ -262,7 +270,10 @@ KERNEL_SOURCES = ("split_impl.h", "falcon_fwd_split.hip", "falcon_fwd_split_win.
                   "chunk_common.h", "mfma_frag.h", "falcon_kernels.h")
 
 
-def measured_traffic(key):
+DECODE_SOURCES = ("falcon_step.hip", "falcon_kernels.h", "mfma_frag.h")
+
+
+def measured_traffic(key, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed counter record, or None when the
     kernel sources changed since the counters were taken."""
     import hashlib
@@ -272,7 +283,7 @@ def measured_traffic(key):
     except (OSError, KeyError, ValueError):
         return None
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "recurrent_sequence_models_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return round(rec["bytes_per_launch"]) if h.hexdigest() == rec["source_sha256"] else None
