@@ -127,15 +127,18 @@ struct Split {
 // key / query rows and the slice's value columns.  Two-kernel form (ONE =
 // false): 8 copy waves also stage the system image the prep kernel wrote.
 // One-pass form (ONE = true): 4 derive waves build each image in LDS one system
-// ahead (the prep kernel's tiles, from the staged rows), and 4 copy waves stage
-// rows, their squared norms and the gates.
+// ahead (the prep kernel's tiles, from the staged rows), and 4 or 8 copy waves
+// stage rows, their squared norms and the gates.
 template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false>
 struct Scan {
   using S = Split<VAR, IT, D, C, BW>;
   static constexpr int DS = D / NS;                          // value channels per workgroup
   // one-pass derive waves (8 measured slower than 4: every role shares the CU's SIMDs)
   static constexpr int NDW = ONE ? S::NPW : 0;
-  static constexpr int NCW = DS / 16, NSW = ONE ? 4 : 8;
+  // copy waves: 8 (two-kernel form: rows and images); one-pass form: 8 when the
+  // workgroup has two state waves and one step per channel set (1024 threads; the
+  // copy waves set the F1A period, and measured faster for F1 too), else 4
+  static constexpr int NCW = DS / 16, NSW = ONE ? (!S::PERCH && NCW == 2 ? 8 : 4) : 8;
   static constexpr int RG = BW == 1 ? R_EC + 1 : R_N;        // per-row arrays a derive wave uses
   static constexpr int NT = 64 * (2 * NCW + NDW + NSW), NST = 64 * NSW;
   static constexpr int LXV = DS + S::PADE;                   // V rows (this workgroup's channels)
@@ -575,10 +578,9 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
 
 // ============================== scan kernel ==============================
 template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE>
-__global__ __launch_bounds__(64 * (2 * (D / 16 / NS) + 8)) void chunk_scan(FwdArgs a, const unsigned char *ws) {
+__global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_scan(FwdArgs a, const unsigned char *ws) {
   using S = Split<VAR, IT, D, C, BW>;
   using Z = Scan<VAR, IT, D, C, BW, NS, ONE>;
-  static_assert(Z::NT == 64 * (2 * (D / 16 / NS) + 8), "launch bounds");
   using OpT = IT;
   using Frag = typename Op<OpT>::frag;
   using Pr = Pair<OpT>;
