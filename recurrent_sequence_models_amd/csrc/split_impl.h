@@ -838,14 +838,15 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
     for (int aa = 0; aa < NA; ++aa)
       sT[aa] = a.S0 ? *reinterpret_cast<const f4 *>(a.S0 + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) : zero4();
   }
+  // raw gains (rows clamped in bounds); the mask for rows past the end is applied
+  // where they are used, so nothing waits for these loads before the next system
   auto prefetch_beta = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < NB; ++p)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = c * CS + 16 * p + 4 * g4 + i;   // zero past the end: padded rows must not write
-        const float braw = a.beta[((size_t)(tok0 + min(t, T - 1)) * H + h) * D + chW];
-        rbeta[p][i] = t < T ? braw : 0.f;
+        const int t = c * CS + 16 * p + 4 * g4 + i;
+        rbeta[p][i] = a.beta[((size_t)(tok0 + min(t, T - 1)) * H + h) * D + chW];
       }
   };
 
@@ -889,7 +890,10 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
       if (PERCH) {
         const f4 inv = *reinterpret_cast<const f4 *>(F + F_ETA * C + 16 * p + 4 * g4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) eta4[i] = rbeta[p][i] * inv[i];
+        for (int i = 0; i < 4; ++i) {   // zero past the end: padded rows must not write
+          const int t = c * CS + 16 * p + 4 * g4 + i;
+          eta4[i] = (t < T ? rbeta[p][i] : 0.f) * inv[i];
+        }
       }
       if (DELTA) {   // R -= sum_{q<p} A_pq E_q   (E_q = eta (.) E for F2)
         f4 acc = zero4();
