@@ -136,9 +136,10 @@ struct Scan {
   // one-pass derive waves (8 measured slower than 4: every role shares the CU's SIMDs)
   static constexpr int NDW = ONE ? S::NPW : 0;
   // copy waves: 8 (two-kernel form: rows and images); one-pass form: 8 when the
-  // workgroup has two state waves and one step per channel set (1024 threads; the
-  // copy waves set the F1A period, and measured faster for F1 too), else 4
-  static constexpr int NCW = DS / 16, NSW = ONE ? (!S::PERCH && NCW == 2 ? 8 : 4) : 8;
+  // workgroup has two state waves (1024 threads; the copy waves set the F1A period,
+  // and F1 and F2A measured faster too), except Falcon-2, whose state waves need
+  // more registers than 16 waves leave (156 VGPRs), else 4
+  static constexpr int NCW = DS / 16, NSW = ONE ? (VAR != V_F2 && NCW == 2 ? 8 : 4) : 8;
   static constexpr int RG = BW == 1 ? R_EC + 1 : R_N;        // per-row arrays a derive wave uses
   static constexpr int NT = 64 * (2 * NCW + NDW + NSW), NST = 64 * NSW;
   static constexpr int LXV = DS + S::PADE;                   // V rows (this workgroup's channels)
