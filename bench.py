@@ -49,8 +49,14 @@ def alg_bytes(w, variant):
 
 
 def ref_flops(w, variant, window=1):
-    """Fixed reference flop count of the chunked form at the configured chunk C
-    (Falcon-3: per WY system of C/Bw steps and C virtual rows)."""
+    """Fixed reference flop count of the chunked form at the configured chunk C.
+
+    Falcon-3 with a window: per WY system of C/Bw steps and C virtual rows, since
+    every pair's residual enters the triangular system.  Falcon-3A keeps the
+    per-chunk count of the additive write: with no residual, the window average
+    folds into banded weights on a score matrix of C rows (the chunked formulas'
+    F3A form), so a window adds no products; the kernels' virtual rows are an
+    implementation choice and are not counted."""
     C, dk, dv = w.chunk, w.dk, w.dv
     if variant == "F3" and window > 1:
         cs, m = C // window, C
@@ -156,6 +162,14 @@ def bwd_bytes(w):
     return w.batch * w.heads * (w.seqlen * per_th + per_seq)
 
 
+def host_cores():
+    """Cores this process may run on (the oracle itself uses one)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline_bwd(w, variant, budget_s=20.0):
     """Time the oracle's backward (as it stands) on a prefix of the same workload,
     on one host core; scaled to tokens/s of the full batch."""
@@ -180,9 +194,11 @@ def cpu_baseline_bwd(w, variant, budget_s=20.0):
     dt = time.perf_counter() - t0
     if limiter is not None and hasattr(limiter, "unregister"):
         limiter.unregister()
-    return {"value": w.batch * T_s / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": w.batch * T_s / dt, "unit": "tokens/s", "cores": 1, "host_cores": host_cores(),
+            "kind": "oracle",
             "sample": f"fp64 NumPy reverse-time adjoint (with its forward) over all {w.batch * w.heads} "
-                      f"sequences of the workload, first {T_s} of {w.seqlen} steps ({dt:.1f} s on 1 host core)"}
+                      f"sequences of the workload, first {T_s} of {w.seqlen} steps ({dt:.1f} s on 1 of "
+                      f"{host_cores()} host cores)"}
 
 
 def bench_backward(args):
@@ -312,9 +328,10 @@ def cpu_baseline(w, variant, window=1, budget_s=20.0):
     dt = time.perf_counter() - t0
     if limiter is not None:
         limiter.unregister() if hasattr(limiter, "unregister") else None
-    return {"value": w.batch * T_s / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": w.batch * T_s / dt, "unit": "tokens/s", "cores": 1, "host_cores": host_cores(),
+            "kind": "oracle",
             "sample": f"fp64 NumPy step loop over all {w.batch * w.heads} sequences of the workload, "
-                      f"first {T_s} of {w.seqlen} steps ({dt:.1f} s on 1 host core)"}
+                      f"first {T_s} of {w.seqlen} steps ({dt:.1f} s on 1 of {host_cores()} host cores)"}
 
 
 def main():

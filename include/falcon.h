@@ -31,7 +31,10 @@
  *              q, k   [B, T, H, dk]   dtype (fp32 or bf16)
  *              v, o   [B, T, H, dv]   dtype
  *              beta   [B, T, H]  fp32, or [B, T, H, dv] for F2/F2A
- *              log_lambda (g) [B, T, H] fp32; any value <= 0 incl. -inf
+ *              log_lambda (g) [B, T, H] fp32; any value <= 0 incl. -inf.
+ *                     g > 0 (a decay above 1) is outside the contract and is
+ *                     not checked: the chunked kernels factor every decay
+ *                     exp(L_a - L_b), a >= b, as a number <= 1
  *              S      [B, H, dv, dk]  fp32, row i = value channel i
  *              x_prev [B, H, dk]      fp32
  *              win_x  [B, H, Bw-1, dk], win_v [B, H, Bw-1, dv] fp32, oldest first
@@ -98,13 +101,25 @@ typedef struct {
   int32_t batch;     /* B >= 1 */
   int32_t seqlen;    /* T >= 1 (ignored by falcon_recurrent_step) */
   int32_t heads;     /* H >= 1 */
-  int32_t dk;        /* key/query head dim: 32, 64 or 128 */
-  int32_t dv;        /* value head dim:     32, 64 or 128 (fp32: 32 or 64) */
+  int32_t dk;        /* key/query head dim: 32, 64 or 128 (fp32 inputs: 32 or 64).
+                        The kernels are built for square states only: dk must
+                        equal dv, else FALCON_ERR_UNSUPPORTED (every kernel tiles
+                        both axes of S with the same 16-wide blocks and one
+                        compile-time head dim).  fp32 at 128 is not built: its
+                        tiles and staged rows do not fit a compute unit's LDS. */
+  int32_t dv;        /* value head dim: equal to dk (see above) */
   int32_t chunk;     /* chunk length C: 16, 32 or 64; T need not be a multiple */
-  int32_t window;    /* Bw: 1..8 for F3/F3A (Bw divides 64), must be 1 otherwise */
+  int32_t window;    /* Bw for F3/F3A; must be 1 for the other variants.  The
+                        decode step takes 1..8.  The chunked forms take 1, 2, 4
+                        or 8 (Bw must divide 64: a system of 64 virtual rows
+                        holds 64/Bw whole steps, and a step's Bw rows must not
+                        straddle a 16-row MFMA block).  Larger windows (e.g. 16)
+                        return FALCON_ERR_UNSUPPORTED: they are not built. */
   float eps_gamma;   /* decay floor, in (0, 1]; the pages' workloads use 1e-3 */
   float eps_phi;     /* feature-map epsilon, >= 0 (1e-6) */
-  float eps_eta;     /* NLMS epsilon, >= 0 (1e-6) */
+  float eps_eta;     /* NLMS epsilon, > 0 (1e-6); 0 is FALCON_ERR_INVALID_ARG,
+                        since a fresh sequence's first key is zero and its step
+                        would divide by |x|^2 = 0 */
   int32_t align;     /* falcon_align_t */
 } falcon_shape_t;
 

@@ -65,6 +65,23 @@ int check_io(const void *q, const void *k, const void *v, const float *beta, con
   return FALCON_OK;
 }
 
+// Whether the one-pass kernel writes the outgoing x_prev / window itself (1) or
+// leaves it to the tail kernel (0).  The copy waves that write it run after the
+// kernel's last barrier, while other workgroups of the sequence (ns > 1 channel
+// slices) may still read the incoming state, and, for a window, the copy waves
+// of one workgroup read carried pairs (sequences shorter than the window) that
+// their neighbours overwrite.  So an outgoing state that aliases the incoming one
+// goes through the tail kernel, which reads everything before it writes, unless
+// a single workgroup per sequence writes only x_prev (which it never reads then:
+// x_prev = phi(k_{T-1}) comes from the inputs).
+int onepass_writes_tail(const falcon_state_t *init, const falcon_state_t *final_state, bool win, int ns) {
+  if (!final_state) return 0;
+  const bool alias = init && (init->x_prev == final_state->x_prev ||
+                              (win && (init->win_x == final_state->win_x || init->win_v == final_state->win_v)));
+  if (!alias) return 1;
+  return (ns == 1 && !win) ? 1 : 0;
+}
+
 }  // namespace
 
 namespace falcon {
@@ -175,10 +192,7 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   const int onepass = split ? 0 : falcon::chunk_fwd_onepass_ns(s->variant, bf16, s->dk, s->dv, s->chunk, a.window,
                                                                 s->batch * s->heads);
   if (onepass) {
-    const bool alias = init && final_state &&
-                       (init->x_prev == final_state->x_prev ||
-                        (win && (init->win_x == final_state->win_x || init->win_v == final_state->win_v)));
-    a.write_tail = (final_state && (onepass == 1 || !alias)) ? 1 : 0;
+    a.write_tail = onepass_writes_tail(init, final_state, win, onepass);
     if (falcon::launch_chunk_fwd_onepass(s->variant, bf16, s->dk, s->dv, s->chunk, a.window, a, hs) != hipSuccess)
       return FALCON_ERR_HIP;
     if (final_state && !a.write_tail) {
@@ -236,10 +250,7 @@ int falcon_chunk_fwd_varlen(const falcon_shape_t *s, const int32_t *cu_seqlens, 
   a.log_eps_gamma = std::log(s->eps_gamma);
   a.eps_phi = s->eps_phi;
   a.eps_eta = s->eps_eta;
-  const bool alias = init && final_state &&
-                     (init->x_prev == final_state->x_prev ||
-                      (win && (init->win_x == final_state->win_x || init->win_v == final_state->win_v)));
-  a.write_tail = (final_state && (ns == 1 || !alias)) ? 1 : 0;
+  a.write_tail = onepass_writes_tail(init, final_state, win, ns);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (falcon::launch_chunk_fwd_onepass(s->variant, bf16, s->dk, s->dv, s->chunk, window, a, hs) != hipSuccess)
     return FALCON_ERR_HIP;

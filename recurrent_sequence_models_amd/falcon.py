@@ -116,16 +116,38 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _check_tensor(name, t, dtype, shape, device):
-    import torch
+def _check_tensor(name, t, dtype, shape, device=None):
+    """dtype, shape and contiguity of a tensor, then (unless device is None) that
+    it lives on ``device``."""
     if t.dtype != dtype:
         raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
-    if t.device != device or not t.is_cuda:
-        raise ValueError(f"{name}: must live on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
+    if device is not None and (t.device != device or not t.is_cuda):
+        raise ValueError(f"{name}: must live on {device}")
+
+
+def _check_state(name, st, batch, heads, dk, dv, window, device):
+    """A state dict the kernels read or write: S [B,H,dv,dk], x_prev [B,H,dk] and,
+    for a window of Bw > 1 pairs, win_x [B,H,Bw-1,dk] and win_v [B,H,Bw-1,dv];
+    all float32, contiguous, on ``device``.  The library takes raw pointers, so a
+    state of another shape would be read or written out of bounds."""
+    import torch
+    if not isinstance(st, dict):
+        raise TypeError(f"{name}: expected a state dict (S, x_prev[, win_x, win_v])")
+    need = [("S", (batch, heads, dv, dk)), ("x_prev", (batch, heads, dk))]
+    if window > 1:
+        need += [("win_x", (batch, heads, window - 1, dk)), ("win_v", (batch, heads, window - 1, dv))]
+    for key, _ in need:
+        if st.get(key) is None:
+            raise ValueError(f"{name}: " + (f"a window of {window} pairs needs '{key}'" if key.startswith("win")
+                                            else f"'{key}' is required"))
+    for key, shp in need:    # every array's shape first, then where they live
+        _check_tensor(f"{name}['{key}']", st[key], torch.float32, shp)
+    for key, shp in need:
+        _check_tensor(f"{name}['{key}']", st[key], torch.float32, shp, device)
 
 
 def new_state(batch, heads, dk, dv, window=1, device="cuda"):
@@ -182,6 +204,11 @@ def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=No
         final = new_state(B, H, dk, dv, window if variant in WINDOWED else 1, dev)
     elif final is False:
         final = None
+    wst = window if variant in WINDOWED else 1
+    if init is not None:
+        _check_state("init", init, B, H, dk, dv, wst, dev)
+    if final is not None:
+        _check_state("final", final, B, H, dk, dv, wst, dev)
     nch = (T + chunk - 1) // chunk
     cs = torch.empty(B, H, nch, dv, dk, dtype=torch.float32, device=dev) if chunk_states else None
     shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
@@ -234,6 +261,11 @@ def chunk_fwd_varlen(variant, q, k, v, beta, log_lambda, cu_seqlens, *, chunk=64
         final = new_state(N, H, dk, dv, window if variant in WINDOWED else 1, dev)
     elif final is False:
         final = None
+    wst = window if variant in WINDOWED else 1
+    if init is not None:
+        _check_state("init", init, N, H, dk, dv, wst, dev)
+    if final is not None:
+        _check_state("final", final, N, H, dk, dv, wst, dev)
     shape = make_shape(variant, dt, N, total, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
     st_in, st_out = _state(init), _state(final)
     status = lib().falcon_chunk_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
@@ -264,10 +296,10 @@ def recurrent_step(variant, q, k, v, beta, log_lambda, state, *, window=1, eps_g
     _check_tensor("v", v, q.dtype, (B, H, dv), dev)
     _check_tensor("beta", beta, torch.float32, (B, H, dv) if variant in PER_CHANNEL else (B, H), dev)
     _check_tensor("log_lambda", log_lambda, torch.float32, (B, H), dev)
-    _check_tensor("S", state["S"], torch.float32, (B, H, dv, dk), dev)
-    _check_tensor("x_prev", state["x_prev"], torch.float32, (B, H, dk), dev)
+    _check_state("state", state, B, H, dk, dv, window if variant in WINDOWED else 1, dev)
     if out is None:
         out = torch.empty(B, H, dv, dtype=q.dtype, device=dev)
+    _check_tensor("o", out, q.dtype, (B, H, dv), dev)
     shape = make_shape(variant, dt, B, 1, H, dk, dv, 64, window, eps_gamma, eps_phi, eps_eta, align)
     st = _state(state)
     status = lib().falcon_recurrent_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
@@ -324,6 +356,10 @@ def chunk_bwd(variant, q, k, v, beta, log_lambda, do, chunk_states, *, init=None
         d_init = new_state(B, H, dk, dv, 1, dev)
     elif d_init is False:
         d_init = None
+    if init is not None:
+        _check_state("init", init, B, H, dk, dv, 1, dev)
+    if d_init is not None:
+        _check_state("d_init", d_init, B, H, dk, dv, 1, dev)
     shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, 1, eps_gamma, eps_phi, eps_eta, align)
     L = lib()
     need = int(L.falcon_chunk_bwd_workspace(ctypes.byref(shape)))
@@ -379,6 +415,11 @@ def chunk_fwd_segmented(variant, q, k, v, beta, log_lambda, nseg, *, chunk=64, w
         final = new_state(B, H, dk, dv, window if variant in WINDOWED else 1, dev)
     elif final is False:
         final = None
+    wst = window if variant in WINDOWED else 1
+    if init is not None:
+        _check_state("init", init, B, H, dk, dv, wst, dev)
+    if final is not None:
+        _check_state("final", final, B, H, dk, dv, wst, dev)
     shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
     L = lib()
     need = int(L.falcon_chunk_fwd_segmented_workspace(ctypes.byref(shape), int(nseg)))

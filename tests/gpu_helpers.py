@@ -15,6 +15,27 @@ def rel_l2(got, ref):
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
 
 
+def seq_errors(got, ref):
+    """Per-sequence diagnostics of an output o [B, T, H, dv]: the largest rel-L2
+    of one (b, h) sequence, and the largest error of one token row relative to
+    the RMS row norm of its sequence.  A whole-tensor rel-L2 dilutes one wrong
+    row of a long sequence by sqrt(T); these do not."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.linalg.norm(got - ref, axis=-1)               # [B, T, H]
+    rn = np.linalg.norm(ref, axis=-1)
+    seq_den = np.sqrt(np.sum(rn ** 2, axis=1))             # [B, H]
+    seq_num = np.sqrt(np.sum(err ** 2, axis=1))
+    head = np.where(seq_den > 0, seq_num / np.where(seq_den > 0, seq_den, 1.0), seq_num)
+    rms = np.sqrt(np.mean(rn ** 2, axis=1, keepdims=True))  # [B, 1, H]
+    row = np.where(rms > 0, err / np.where(rms > 0, rms, 1.0), err)
+    return float(head.max()), float(row.max())
+
+
+# a row may be worse than the whole sequence, but not by much: a wrong row is off by ~1
+ROW_FACTOR = 5.0
+
+
 def to_dev(inp, dtype, device="cuda"):
     import torch
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32

@@ -276,3 +276,67 @@ def test_segmented_rejects_on_host():
     assert call_seg(ok, 4, wsb=seg_workspace(4, seqlen=512) - 1) == F.ERR_WORKSPACE
     for kw in INVALID_SHAPES:
         assert call_seg(good_shape(**kw), 1) == F.ERR_INVALID_ARG, kw
+
+
+def _cpu_state(B=2, H=3, dk=64, dv=64, window=1, dtype=None, drop=()):
+    import torch
+    dt = dtype or torch.float32
+    st = dict(S=torch.zeros(B, H, dv, dk, dtype=dt), x_prev=torch.zeros(B, H, dk, dtype=dt))
+    if window > 1:
+        st["win_x"] = torch.zeros(B, H, window - 1, dk, dtype=dt)
+        st["win_v"] = torch.zeros(B, H, window - 1, dv, dtype=dt)
+    for k in drop:
+        st.pop(k)
+    return st
+
+
+def test_binding_checks_state_shapes():
+    """The binding passes raw state pointers, so it checks every state array's
+    shape, dtype and presence before the call (the device check comes last, so
+    on a CPU tensor of the right shape only the device is refused)."""
+    import torch
+    dev = torch.device("cuda:0")
+    chk = F._check_state
+    with pytest.raises(ValueError, match="must live on"):
+        chk("init", _cpu_state(), 2, 3, 64, 64, 1, dev)               # right shapes, wrong device
+    with pytest.raises(ValueError, match="shape"):
+        chk("init", _cpu_state(B=1), 2, 3, 64, 64, 1, dev)            # another batch
+    with pytest.raises(ValueError, match="shape"):
+        chk("init", _cpu_state(H=4), 2, 3, 64, 64, 1, dev)            # another head count
+    with pytest.raises(ValueError, match="shape"):
+        chk("init", _cpu_state(dk=32, dv=32), 2, 3, 64, 64, 1, dev)   # another head dim
+    with pytest.raises(TypeError, match="dtype"):
+        chk("init", _cpu_state(dtype=torch.float64), 2, 3, 64, 64, 1, dev)
+    with pytest.raises(ValueError, match="needs 'win_x'"):
+        chk("final", _cpu_state(window=4, drop=("win_x",)), 2, 3, 64, 64, 4, dev)
+    with pytest.raises(ValueError, match="shape"):
+        chk("final", _cpu_state(window=2), 2, 3, 64, 64, 4, dev)      # a window built for Bw = 2
+    with pytest.raises(ValueError, match="contiguous|shape"):
+        st = _cpu_state()
+        st["S"] = torch.zeros(2, 3, 64, 64).transpose(2, 3)
+        chk("init", st, 2, 3, 64, 64, 1, dev)
+    with pytest.raises(TypeError, match="state dict"):
+        chk("init", [1, 2], 2, 3, 64, 64, 1, dev)
+
+
+def test_bench_reference_counts():
+    """bench.py's algorithmic bytes and reference flops reproduce the
+    configurations' roofline table (bytes of inputs, outputs and final state; the
+    chunked form's fixed flop formula, per WY system of C/Bw steps for Falcon-3)."""
+    import bench
+    import workloads as W
+    c2, c3, c4, c5 = (W.WORKLOADS[n] for n in ("layer130m", "layer130m_f2", "window_t4096", "long_t65536"))
+    assert bench.alg_bytes(c2, "F1") / 1e6 == pytest.approx(103.83, abs=0.01)
+    assert bench.alg_bytes(c3, "F2") / 1e6 == pytest.approx(153.38, abs=0.01)
+    assert bench.alg_bytes(c5, "F1") / 1e6 == pytest.approx(1083.19, abs=0.01)
+    assert bench.ref_flops(c2, "F1") / 1e9 == pytest.approx(13.15, abs=0.01)
+    assert bench.ref_flops(c2, "F1A") / 1e9 == pytest.approx(6.44, abs=0.01)
+    assert bench.ref_flops(c3, "F2") / 1e9 == pytest.approx(10.47, abs=0.01)
+    assert bench.ref_flops(c4, "F3", 4) / 1e9 == pytest.approx(38.12, abs=0.01)
+    assert bench.ref_flops(c4, "F3", 8) / 1e9 == pytest.approx(71.40, abs=0.01)
+    assert bench.ref_flops(c4, "F3A", 4) / 1e9 == pytest.approx(6.44, abs=0.01)
+    assert bench.ref_flops(c4, "F3A", 8) == bench.ref_flops(c4, "F3A", 4)
+    assert bench.ref_flops(c5, "F1") / 1e9 == pytest.approx(190.41, abs=0.01)
+    assert bench.ref_flops(c5, "F1A") / 1e9 == pytest.approx(103.08, abs=0.01)
+    # Falcon-3 with one pair per step is Falcon-1
+    assert bench.ref_flops(c4, "F3", 1) == bench.ref_flops(c4, "F1")

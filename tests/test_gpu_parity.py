@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import TOL, oracle_subset, rel_l2, state_to_dev, to_dev, to_np
+from gpu_helpers import ROW_FACTOR, TOL, oracle_subset, rel_l2, seq_errors, state_to_dev, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -50,9 +50,13 @@ def check(variant, w, seed, window=1, init=False, chunk=None, chunk_states=False
         ends = [min(T, c0 + chunk) - 1 for c0 in range(0, T, chunk)]
         ref = np.moveaxis(r["states"][:, ends], 2, 1)           # [B,H,NC,dv,dk]
         errs["chunk_states"] = rel_l2(g["chunk_states"], ref)
-    print(variant, w.name, seed, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    head, row = seq_errors(g["o"], r["o"])
+    print(variant, w.name, seed, {k: f"{v:.2e}" for k, v in errs.items()},
+          f"o per-head max {head:.2e} row max {row:.2e}", flush=True)
     for k, e in errs.items():
         assert e <= tol, (k, e)
+    assert head <= tol, ("o per-head", head)
+    assert row <= ROW_FACTOR * tol, ("o per-row", row)
     return errs
 
 
