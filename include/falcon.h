@@ -174,6 +174,28 @@ int falcon_chunk_fwd(const falcon_shape_t *shape,
                      void *o, float *chunk_states,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The same computation as
+ * falcon_chunk_fwd on its chunk-parallel path (prep kernel + state scan), with
+ * the scratch that path needs taken from a fixed device array inside the library
+ * (FALCON_STATIC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends) instead of a caller's workspace.  The caller still
+ * passes every input and output; the call allocates and frees nothing.
+ *   Sizes  the shape must have that path (falcon_chunk_fwd_workspace(shape) > 0,
+ *          else FALCON_ERR_UNSUPPORTED) and need at most
+ *          FALCON_STATIC_SCRATCH_BYTES of it (else FALCON_ERR_WORKSPACE); e.g.
+ *          the 130M-layer shape (B 8, H 12, T 2048, d 64, chunk 64) needs 41 MB.
+ *   Races  every call on one GPU uses that GPU's one array: calls that overlap
+ *          on a GPU (other streams, other threads) race and give wrong results.
+ *          The scratch needs no initialisation; each call overwrites it.
+ * Other arguments, aliasing and errors as falcon_chunk_fwd. */
+#define FALCON_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int falcon_chunk_fwd_static(const falcon_shape_t *shape,
+                            const void *q, const void *k, const void *v,
+                            const float *beta, const float *log_lambda,
+                            const falcon_state_t *init, falcon_state_t *final_state,
+                            void *o, float *chunk_states, void *stream);
+
 /* Chunked forward pass over a packed batch of sequences of different lengths
  * (the same computation as falcon_chunk_fwd, one sequence per entry):
  *   shape->batch  = N, the number of sequences; shape->seqlen = the total

@@ -85,6 +85,7 @@ int onepass_writes_tail(const falcon_state_t *init, const falcon_state_t *final_
 }  // namespace
 
 namespace falcon {
+hipError_t static_scratch(void **out);   // falcon_static.hip
 hipError_t launch_chunk_fwd_rows(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
                                  const FwdArgs &a, hipStream_t s);
 hipError_t launch_chunk_fwd_window(int variant, bool bf16, int dk, int dv, int chunk, int nsplit,
@@ -214,6 +215,23 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
     if (falcon::launch_tail(s->variant, bf16, s->dk, s->dv, a, hs) != hipSuccess) return FALCON_ERR_HIP;
   }
   return FALCON_OK;
+}
+
+int falcon_chunk_fwd_static(const falcon_shape_t *s, const void *q, const void *k, const void *v,
+                            const float *beta, const float *log_lambda, const falcon_state_t *init,
+                            falcon_state_t *final_state, void *o, float *chunk_states, void *stream) {
+  int st = check_shape(s, false);
+  if (st != FALCON_OK) return st;
+  if ((st = check_io(q, k, v, beta, log_lambda, o)) != FALCON_OK) return st;
+  if (init && (st = check_state(init, s)) != FALCON_OK) return st;
+  if (final_state && (st = check_state(final_state, s)) != FALCON_OK) return st;
+  if (chunk_states && !aligned16(chunk_states)) return FALCON_ERR_INVALID_ARG;
+  const size_t need = falcon_chunk_fwd_workspace(s);
+  if (need == 0) return FALCON_ERR_UNSUPPORTED;
+  if (need > FALCON_STATIC_SCRATCH_BYTES) return FALCON_ERR_WORKSPACE;
+  void *scratch = nullptr;   // this device's copy of the library's scratch array
+  if (falcon::static_scratch(&scratch) != hipSuccess || !scratch) return FALCON_ERR_HIP;
+  return falcon_chunk_fwd(s, q, k, v, beta, log_lambda, init, final_state, o, chunk_states, scratch, need, stream);
 }
 
 int falcon_chunk_fwd_varlen(const falcon_shape_t *s, const int32_t *cu_seqlens, const void *q, const void *k,

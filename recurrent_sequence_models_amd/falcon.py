@@ -23,7 +23,7 @@ WINDOWED = ("F3", "F3A")
 EXPORTS = ("falcon_abi_version", "falcon_status_string", "falcon_chunk_fwd_workspace",
            "falcon_chunk_fwd", "falcon_chunk_fwd_varlen", "falcon_recurrent_step",
            "falcon_chunk_bwd_workspace", "falcon_chunk_bwd",
-           "falcon_chunk_fwd_segmented_workspace", "falcon_chunk_fwd_segmented")
+           "falcon_chunk_fwd_segmented_workspace", "falcon_chunk_fwd_segmented", "falcon_chunk_fwd_static")
 
 
 class Shape(ctypes.Structure):
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.falcon_chunk_fwd_segmented.restype = I
         L.falcon_chunk_fwd_segmented.argtypes = [P(Shape), ctypes.c_int32, V, V, V, V, V, P(State), P(State), V, V,
                                                  S, V]
+        L.falcon_chunk_fwd_static.restype = I
+        L.falcon_chunk_fwd_static.argtypes = [P(Shape), V, V, V, V, V, P(State), P(State), V, V, V]
         L.falcon_chunk_bwd_workspace.restype = S
         L.falcon_chunk_bwd_workspace.argtypes = [P(Shape)]
         L.falcon_chunk_bwd.restype = I

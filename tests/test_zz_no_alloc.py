@@ -1,0 +1,102 @@
+"""falcon_chunk_fwd_static (the entry point that allocates nothing) against
+falcon_chunk_fwd with a caller's workspace, through the C ABI.
+
+Both run the chunk-parallel path on the same kernels, so their outputs and
+states must be identical; they are also checked against the fp64 oracle on a
+sample.  Two calls in a row share the library's scratch array, the second on a
+smaller input, so stale contents of the array from the first call must not
+leak into the second."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import TOL, oracle_subset, rel_l2, state_to_dev, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _call(variant, w, inp, init, window, static):
+    """One forward through the C ABI; returns (status, o, final state, chunk states)."""
+    import torch
+    from recurrent_sequence_models_amd import falcon as F
+    L = F.lib()
+    d = to_dev(inp, w.dtype)
+    B, T, H, dk, dv = w.batch, w.seqlen, w.heads, w.dk, w.dv
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    o = torch.full((B, T, H, dv), float("nan"), dtype=tdt, device="cuda")
+    nch = -(-T // w.chunk)
+    cs = torch.full((B, H, nch, dv, dk), float("nan"), device="cuda")
+    fin = F.new_state(B, H, dk, dv, window)
+    init_dev = state_to_dev(init) if init is not None else None   # kept alive until after the call
+    st_in = F._state(init_dev)
+    st_out = F._state(fin)
+    shape = F.make_shape(variant, w.dtype, B, T, H, dk, dv, w.chunk, window)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    args = [ctypes.byref(shape), F._ptr(d["q"]), F._ptr(d["k"]), F._ptr(d["v"]), F._ptr(d["beta"]),
+            F._ptr(d["log_lambda"]), ctypes.byref(st_in) if st_in else None, ctypes.byref(st_out),
+            F._ptr(o), F._ptr(cs)]
+    if static:
+        status = L.falcon_chunk_fwd_static(*args, stream)
+    else:
+        nbytes = L.falcon_chunk_fwd_workspace(ctypes.byref(shape))
+        assert nbytes > 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        status = L.falcon_chunk_fwd(*args, F._ptr(ws), nbytes, stream)
+    torch.cuda.synchronize()
+    out = {"o": to_np(o), "chunk_states": to_np(cs)}
+    out.update({n: to_np(t) for n, t in fin.items()})
+    return status, out
+
+
+CASES = [
+    # (variant, window, first workload, second (smaller) workload)
+    ("F1", 1, W.WORKLOADS["layer130m"],
+     W.WORKLOADS["layer130m"].replace(batch=2, heads=3, seqlen=203)),
+    ("F2", 1, W.WORKLOADS["layer130m"].replace(batch=4, heads=12, seqlen=1024),
+     W.WORKLOADS["layer130m"].replace(batch=1, heads=2, seqlen=77, dk=128, dv=128)),
+    ("F3", 4, W.WORKLOADS["window_t4096"].replace(batch=2, heads=12, seqlen=2048),
+     W.WORKLOADS["window_t4096"].replace(batch=1, heads=3, seqlen=150, dk=32, dv=32, dtype="fp32")),
+]
+
+
+@pytest.mark.parametrize("variant,window,w1,w2", CASES, ids=[c[0] for c in CASES])
+def test_static_scratch_matches_workspace_path(variant, window, w1, w2):
+    from recurrent_sequence_models_amd import falcon as F
+    for n, w in enumerate((w1, w2)):
+        print(f"[call {n + 1}] {variant} Bw{window} {w.dtype} B{w.batch} H{w.heads} T{w.seqlen} d{w.dk}",
+              flush=True)
+        inp = W.make_inputs(w, variant, seed=w.seed + 50 + n, window=window)
+        init = W.make_state(w, w.seed + 60 + n, window) if n == 1 else None
+        s_ws, ref = _call(variant, w, inp, init, window, static=False)
+        s_st, got = _call(variant, w, inp, init, window, static=True)
+        assert s_ws == F.OK and s_st == F.OK, (F.status_string(s_ws), F.status_string(s_st))
+        for k in ref:
+            assert np.array_equal(got[k], ref[k], equal_nan=False), k   # same kernels, same arithmetic
+        # and the oracle's bar on a sample of sequences
+        seqs = [(0, 0), (w.batch - 1, w.heads - 1)]
+        refs = oracle_subset(variant, inp, seqs, window=window, state=init)
+        for (b, h), r in zip(seqs, refs):
+            eo = rel_l2(got["o"][b, :, h], r["o"][0, :, 0])
+            es = rel_l2(got["S"][b, h], r["S"][0, 0])
+            print(variant, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
+            assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+def test_static_scratch_rejects_oversized_shapes():
+    """A shape whose chunk-parallel scratch exceeds the array is refused on the
+    host (FALCON_ERR_WORKSPACE), as is a shape without that path."""
+    from recurrent_sequence_models_amd import falcon as F
+    L = F.lib()
+    big = F.make_shape("F1", "bf16", 64, 4096, 16, 64, 64, 64, 1)     # 64*16 sequences of 64 systems
+    assert L.falcon_chunk_fwd_workspace(ctypes.byref(big)) > (64 << 20)
+    fake = ctypes.c_void_p(0x10000)
+    st = L.falcon_chunk_fwd_static(ctypes.byref(big), fake, fake, fake, fake, fake, None, None, fake, None, None)
+    assert st == F.ERR_WORKSPACE, F.status_string(st)
+    nopath = F.make_shape("F1", "fp32", 1, 100, 2, 64, 64, 64, 1)     # fp32 at chunk 64: no two-kernel form
+    assert L.falcon_chunk_fwd_workspace(ctypes.byref(nopath)) == 0
+    st = L.falcon_chunk_fwd_static(ctypes.byref(nopath), fake, fake, fake, fake, fake, None, None, fake, None, None)
+    assert st == F.ERR_UNSUPPORTED, F.status_string(st)
