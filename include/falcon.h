@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define FALCON_ABI_VERSION 3
+#define FALCON_ABI_VERSION 4
 
 typedef enum {
   FALCON_1 = 1,   /* scalar NLMS step, residual write            */
@@ -196,6 +196,16 @@ int falcon_chunk_fwd_static(const falcon_shape_t *shape,
                             const falcon_state_t *init, falcon_state_t *final_state,
                             void *o, float *chunk_states, void *stream);
 
+/* Bytes of device workspace that enable the chunk-parallel path of
+ * falcon_chunk_fwd_varlen for this packed shape (shape->batch = N sequences,
+ * shape->seqlen = their total token count); 0 when that path does not apply
+ * (as for falcon_chunk_fwd_workspace).  Per head it holds one image slot per
+ * system the N sequences can have, at most total/S + N + 1 for systems of S
+ * steps (sequence n's images start at slot cu_seqlens[n] / S + n, so the layout
+ * follows from cu_seqlens on the device), plus each sequence's carried-state
+ * copy; no initialisation needed. */
+size_t falcon_chunk_fwd_varlen_workspace(const falcon_shape_t *shape);
+
 /* Chunked forward pass over a packed batch of sequences of different lengths
  * (the same computation as falcon_chunk_fwd, one sequence per entry):
  *   shape->batch  = N, the number of sequences; shape->seqlen = the total
@@ -206,16 +216,23 @@ int falcon_chunk_fwd_static(const falcon_shape_t *shape,
  *   q, k [total, H, dk], v, o [total, H, dv] in dtype; beta [total, H] (F2/F2A:
  *   [total, H, dv]) and log_lambda [total, H] fp32; the state arrays are per
  *   sequence ([N, H, ...]) as in falcon_chunk_fwd.
+ *   workspace     NULL: the one-pass kernel, where it is built for the shape
+ *                 (bf16 at d <= 64, fp32 at small chunks); a shape it does not
+ *                 build returns FALCON_ERR_WORKSPACE when the chunk-parallel path
+ *                 exists for it (pass a workspace) and FALCON_ERR_UNSUPPORTED
+ *                 otherwise.  Non-NULL: at least
+ *                 falcon_chunk_fwd_varlen_workspace(shape) bytes (else
+ *                 FALCON_ERR_WORKSPACE), 16-byte aligned, and the chunk-parallel
+ *                 path runs (this covers d = 128 in bf16).
  * Sequence n starts from init (its own S, x_prev and window) and ends in
  * final_state.  A sequence of length 0 is skipped: its final state is not
- * written.  No workspace and no per-chunk states; it runs on the one-pass
- * kernel, so shapes that kernel does not build return FALCON_ERR_UNSUPPORTED.
- * Same aliasing and stream rules as falcon_chunk_fwd. */
+ * written.  No per-chunk states.  Same aliasing and stream rules as
+ * falcon_chunk_fwd; calls sharing a workspace race. */
 int falcon_chunk_fwd_varlen(const falcon_shape_t *shape, const int32_t *cu_seqlens,
                             const void *q, const void *k, const void *v,
                             const float *beta, const float *log_lambda,
                             const falcon_state_t *init, falcon_state_t *final_state,
-                            void *o, void *stream);
+                            void *o, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace falcon_chunk_fwd_segmented needs for this shape
  * and segment count; 0 when the segmented form is not built for them: nseg

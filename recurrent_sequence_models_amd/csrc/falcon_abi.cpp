@@ -93,6 +93,8 @@ hipError_t launch_chunk_fwd_window(int variant, bool bf16, int dk, int dv, int c
 bool chunk_fwd_pipe_supported(int variant, bool bf16, int dk, int dv, int chunk);
 bool chunk_fwd_split_supported(int variant, bool bf16, int dk, int dv, int chunk, int window);
 size_t chunk_fwd_split_workspace(int variant, bool bf16, int dk, int dv, int chunk, int window, int bh, int T);
+size_t chunk_fwd_split_workspace_varlen(int variant, bool bf16, int dk, int dv, int chunk, int window, int N, int H,
+                                        int total);
 hipError_t launch_chunk_fwd_split(int variant, bool bf16, int dk, int dv, int chunk, int window, const FwdArgs &a,
                                   void *ws, hipStream_t s);
 int chunk_fwd_onepass_ns(int variant, bool bf16, int dk, int dv, int chunk, int window, int bh);
@@ -234,9 +236,18 @@ int falcon_chunk_fwd_static(const falcon_shape_t *s, const void *q, const void *
   return falcon_chunk_fwd(s, q, k, v, beta, log_lambda, init, final_state, o, chunk_states, scratch, need, stream);
 }
 
+size_t falcon_chunk_fwd_varlen_workspace(const falcon_shape_t *s) {
+  if (check_shape(s, false) != FALCON_OK) return 0;
+  // image slots per head must have int indices
+  if ((int64_t)s->heads * ((int64_t)s->seqlen + s->batch + 1) > INT32_MAX) return 0;
+  return falcon::chunk_fwd_split_workspace_varlen(s->variant, s->dtype == FALCON_BF16, s->dk, s->dv, s->chunk,
+                                                  s->window, s->batch, s->heads, s->seqlen);
+}
+
 int falcon_chunk_fwd_varlen(const falcon_shape_t *s, const int32_t *cu_seqlens, const void *q, const void *k,
                             const void *v, const float *beta, const float *log_lambda, const falcon_state_t *init,
-                            falcon_state_t *final_state, void *o, void *stream) {
+                            falcon_state_t *final_state, void *o, void *workspace, size_t workspace_bytes,
+                            void *stream) {
   int st = check_shape(s, false);
   if (st != FALCON_OK) return st;
   if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return FALCON_ERR_INVALID_ARG;
@@ -246,8 +257,13 @@ int falcon_chunk_fwd_varlen(const falcon_shape_t *s, const int32_t *cu_seqlens, 
   const bool bf16 = s->dtype == FALCON_BF16;
   const bool win = windowed(s->variant) && s->window > 1;
   const int window = windowed(s->variant) ? s->window : 1;
-  const int ns = falcon::chunk_fwd_onepass_ns(s->variant, bf16, s->dk, s->dv, s->chunk, window, s->batch * s->heads);
-  if (ns == 0) return FALCON_ERR_UNSUPPORTED;
+  const size_t ws_need = falcon_chunk_fwd_varlen_workspace(s);
+  const bool split = workspace != nullptr && ws_need > 0;
+  if (split && workspace_bytes < ws_need) return FALCON_ERR_WORKSPACE;
+  if (split && !aligned16(workspace)) return FALCON_ERR_INVALID_ARG;
+  const int ns =
+      split ? 0 : falcon::chunk_fwd_onepass_ns(s->variant, bf16, s->dk, s->dv, s->chunk, window, s->batch * s->heads);
+  if (!split && ns == 0) return ws_need > 0 ? FALCON_ERR_WORKSPACE : FALCON_ERR_UNSUPPORTED;
   FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = log_lambda;
   a.S0 = init ? init->S : nullptr;
@@ -268,8 +284,16 @@ int falcon_chunk_fwd_varlen(const falcon_shape_t *s, const int32_t *cu_seqlens, 
   a.log_eps_gamma = std::log(s->eps_gamma);
   a.eps_phi = s->eps_phi;
   a.eps_eta = s->eps_eta;
-  a.write_tail = onepass_writes_tail(init, final_state, win, ns);
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (split) {   // prep over every image slot, then the scan workgroups of each sequence; the scan
+                 // reads the prep's copy of the incoming x_prev / window, so it writes the outgoing ones
+    a.write_tail = final_state ? 1 : 0;
+    return falcon::launch_chunk_fwd_split(s->variant, bf16, s->dk, s->dv, s->chunk, window, a, workspace, hs) ==
+                   hipSuccess
+               ? FALCON_OK
+               : FALCON_ERR_HIP;
+  }
+  a.write_tail = onepass_writes_tail(init, final_state, win, ns);
   if (falcon::launch_chunk_fwd_onepass(s->variant, bf16, s->dk, s->dv, s->chunk, window, a, hs) != hipSuccess)
     return FALCON_ERR_HIP;
   if (final_state && !a.write_tail) {

@@ -8,6 +8,8 @@ namespace falcon {
 
 bool chunk_fwd_split_win_supported(int variant, bool bf16, int d, int chunk, int window);
 size_t chunk_fwd_split_win_workspace(int variant, bool bf16, int d, int chunk, int window, int bh, int T);
+size_t chunk_fwd_split_win_workspace_varlen(int variant, bool bf16, int d, int chunk, int window, int N, int H,
+                                            int total);
 hipError_t launch_chunk_fwd_split_win(int variant, bool bf16, int d, int chunk, int window, const FwdArgs &a,
                                       void *ws, hipStream_t st);
 int chunk_fwd_onepass_win_ns(int variant, bool bf16, int d, int chunk, int window, int bh);
@@ -72,6 +74,17 @@ size_t chunk_fwd_split_workspace(int variant, bool bf16, int dk, int dv, int chu
   return dispatch_split(one_pair(variant), bf16, dk, chunk, [bh, T](auto v, auto *t, auto dd, auto cc) -> size_t {
     using IT = std::remove_pointer_t<decltype(t)>;
     return Split<decltype(v)::value, IT, decltype(dd)::value, decltype(cc)::value, 1>::workspace(bh, T);
+  });
+}
+
+// Scratch of the two-kernel path for N packed sequences of `total` tokens over H heads.
+size_t chunk_fwd_split_workspace_varlen(int variant, bool bf16, int dk, int dv, int chunk, int window, int N, int H,
+                                        int total) {
+  if (!chunk_fwd_split_supported(variant, bf16, dk, dv, chunk, window)) return 0;
+  if (window > 1) return chunk_fwd_split_win_workspace_varlen(variant, bf16, dk, chunk, window, N, H, total);
+  return dispatch_split(one_pair(variant), bf16, dk, chunk, [N, H, total](auto v, auto *t, auto dd, auto cc) -> size_t {
+    using IT = std::remove_pointer_t<decltype(t)>;
+    return Split<decltype(v)::value, IT, decltype(dd)::value, decltype(cc)::value, 1>::workspace_varlen(N, H, total);
   });
 }
 

@@ -57,6 +57,14 @@ size_t chunk_fwd_split_win_workspace(int variant, bool bf16, int d, int chunk, i
   });
 }
 
+size_t chunk_fwd_split_win_workspace_varlen(int variant, bool bf16, int d, int chunk, int window, int N, int H,
+                                            int total) {
+  return dispatch_win(variant, bf16, d, chunk, window, [N, H, total](auto v, auto *t, auto dd, auto w) -> size_t {
+    using IT = std::remove_pointer_t<decltype(t)>;
+    return Split<decltype(v)::value, IT, decltype(dd)::value, 64, decltype(w)::value>::workspace_varlen(N, H, total);
+  });
+}
+
 hipError_t launch_chunk_fwd_split_win(int variant, bool bf16, int d, int chunk, int window, const FwdArgs &a,
                                       void *ws, hipStream_t st) {
   if (!chunk_fwd_split_win_supported(variant, bf16, d, chunk, window)) return hipErrorInvalidValue;

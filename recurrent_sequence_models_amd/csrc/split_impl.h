@@ -117,6 +117,15 @@ struct Split {
   static constexpr size_t prep_lds() { return (size_t)SZ * (C + CSP) * LX + 4 * R_N * C; }
   __host__ __device__ static int nsys(int T) { return (T + CS - 1) / CS; }
   static size_t workspace(int bh, int T) { return (size_t)bh * nsys(T) * IMG + (size_t)bh * CARRY; }
+  // Packed sequences (cu_seqlens): per head, sequence n's systems take image slots
+  // from cu[n] / CS + n on, which leaves room for its nsys(cu[n+1] - cu[n]) systems
+  // (floor(cu/CS) + ceil(T/CS) <= floor((cu + T)/CS) + 1), so the offsets follow from
+  // cu alone; `slots` per head bounds them all.
+  __host__ __device__ static int slot0(const int *cu, int n) { return cu[n] / CS + n; }
+  __host__ __device__ static int slots(int N, int total) { return total / CS + N + 1; }
+  static size_t workspace_varlen(int N, int H, int total) {
+    return (size_t)H * slots(N, total) * IMG + (size_t)N * H * CARRY;
+  }
 };
 
 // The scan of one sequence is split over NS workgroups by value channel (rows
@@ -410,14 +419,46 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
 
   const int tid = threadIdx.x, lane = tid & 63, pw = tid >> 6;
   const int g4 = lane >> 4, cl = lane & 15;
-  const int T = a.T, H = a.H, NSYS = S::nsys(T);
-  const int bh = blockIdx.x / NSYS, c = blockIdx.x % NSYS, b = bh / H, h = bh % H, c0 = c * CS;
+  const int H = a.H;
+  // the workgroup's sequence b, head h and system c: one per system of a dense
+  // [B, T] batch, or, for packed sequences, one per image slot of a head (slots
+  // past the end of their sequence's systems have nothing to do)
+  int T, b, h, c;
+  long long tok0;
+  unsigned char *img, *carry_base;
+  if (a.cu) {
+    const int SL = S::slots(a.B, a.T);
+    h = blockIdx.x / SL;
+    const int slot = blockIdx.x % SL;
+    int lo = 0, hi = a.B - 1;   // the last sequence whose first slot is <= slot
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (S::slot0(a.cu, mid) <= slot) lo = mid;
+      else hi = mid - 1;
+    }
+    b = lo;
+    tok0 = a.cu[b];
+    T = a.cu[b + 1] - a.cu[b];
+    c = slot - S::slot0(a.cu, b);
+    if (c >= S::nsys(T)) return;   // an unused slot (also every slot of an empty sequence)
+    img = ws + (size_t)blockIdx.x * S::IMG;
+    carry_base = ws + (size_t)H * SL * S::IMG;
+  } else {
+    T = a.T;
+    const int NSYS = S::nsys(T), bhd = blockIdx.x / NSYS;
+    c = blockIdx.x % NSYS;
+    b = bhd / H;
+    h = bhd % H;
+    tok0 = (long long)b * T;
+    img = ws + (size_t)blockIdx.x * S::IMG;
+    carry_base = ws + (size_t)a.B * H * NSYS * S::IMG;
+  }
+  const int bh = b * H + h, c0 = c * CS;
   const IT *qp = static_cast<const IT *>(a.q);
   const IT *kp = static_cast<const IT *>(a.k);
-  unsigned char *img = ws + (size_t)blockIdx.x * S::IMG;
 
   if (c == 0) {   // the sequence's carry block
-    float *carry = reinterpret_cast<float *>(ws + (size_t)a.B * H * NSYS * S::IMG + (size_t)bh * S::CARRY);
+    float *carry = reinterpret_cast<float *>(carry_base + (size_t)bh * S::CARRY);
     for (int e = tid; e < D; e += S::NPT) carry[e] = a.xprev0 ? a.xprev0[(size_t)bh * D + e] : 0.f;
     for (int e = tid; e < (BW - 1) * D; e += S::NPT) {
       carry[D + e] = a.winx0 ? a.winx0[(size_t)bh * (BW - 1) * D + e] : 0.f;
@@ -435,8 +476,8 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
         const int tk = c0 + r - 1 + a.align, tq = c0 + r;
         // loads use in-bounds (clamped) rows; rows outside the sequence are zeroed after the load
         const int tkc = min(max(tk, 0), T - 1), tqc = min(tq, T - 1);
-        const uint4 kraw = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tkc) * H + h) * D + part * VEC);
-        const uint4 qraw = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tqc) * H + h) * D + part * VEC);
+        const uint4 kraw = *reinterpret_cast<const uint4 *>(kp + ((size_t)(tok0 + tkc) * H + h) * D + part * VEC);
+        const uint4 qraw = *reinterpret_cast<const uint4 *>(qp + ((size_t)(tok0 + tqc) * H + h) * D + part * VEC);
         uint4 k4 = keep_or_zero(tk >= 0 && tk < T, kraw);
         const uint4 q4 = keep_or_zero(tq < T, qraw);
         float xv[VEC], qv[VEC];
@@ -459,7 +500,7 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
         const float ik = tk < 0 ? 1.f : safe_rsqrt(sk + a.eps_phi);
         const float iq = safe_rsqrt(sq + a.eps_phi);
         const float inv = fast_rcp(a.eps_eta + sk * ik * ik);
-        const float braw = PERCH ? 0.f : a.beta[(size_t)(b * T + tqc) * H + h];
+        const float braw = PERCH ? 0.f : a.beta[(size_t)(tok0 + tqc) * H + h];
         const float eta = PERCH ? inv : (tq < T ? braw : 0.f) * inv;
         put_perm(sX + r * LX, part * VEC, k4);
         put_perm(sQ + r * LX, part * VEC, q4);
@@ -480,7 +521,7 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
       if (r < C) {
         const int st = c0 + r / BW, j = st - BW + 1 + r % BW, tk = j - 1 + a.align;
         const int tkc = min(max(tk, 0), T - 1);
-        const uint4 kraw = *reinterpret_cast<const uint4 *>(kp + ((size_t)(b * T + tkc) * H + h) * D + part * VEC);
+        const uint4 kraw = *reinterpret_cast<const uint4 *>(kp + ((size_t)(tok0 + tkc) * H + h) * D + part * VEC);
         uint4 k4 = keep_or_zero(tk >= 0 && st < T, kraw);
         float sk = 0.f;
         if (tk < 0 && st < T) {   // carried feature (fp32, already normalised): x_prev (j = 0) or window
@@ -508,7 +549,7 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
         const int tq = c0 + r;
         const bool okq = r < CS && tq < T;
         const int tqc = min(tq, T - 1);
-        const uint4 qraw = *reinterpret_cast<const uint4 *>(qp + ((size_t)(b * T + tqc) * H + h) * D + part * VEC);
+        const uint4 qraw = *reinterpret_cast<const uint4 *>(qp + ((size_t)(tok0 + tqc) * H + h) * D + part * VEC);
         const uint4 q4 = keep_or_zero(okq, qraw);
         float qv[VEC], sq = 0.f;
         unpack(q4, IT(), qv);
@@ -517,7 +558,7 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
         sq = group_sum<TPR>(sq);
         put_perm(sQ + r * LX, part * VEC, q4);
         if (part == 0) {
-          const float braw = a.beta[(size_t)(b * T + tqc) * H + h];
+          const float braw = a.beta[(size_t)(tok0 + tqc) * H + h];
           sR[R_IQ * C + r] = okq ? safe_rsqrt(sq + a.eps_phi) : 0.f;
           sR[R_BQ * C + r] = okq ? braw : 0.f;
         }
@@ -526,7 +567,7 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
   }
   if (pw == S::NPW - 1) {   // clamp in log space, inclusive scan over the system's steps
     const bool ok = lane < CS && c0 + lane < T;
-    const float graw = a.g[(size_t)(b * T + min(c0 + lane, T - 1)) * H + h];
+    const float graw = a.g[(size_t)(tok0 + min(c0 + lane, T - 1)) * H + h];
     const float g2 = ok ? fmaxf(graw, a.log_eps_gamma) : 0.f;
     const float L = wave_inclusive_scan(g2);
     if (BW == 1) {
@@ -635,9 +676,20 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
   const IT *kp = static_cast<const IT *>(a.k);
   const IT *vp = static_cast<const IT *>(a.v);
   IT *op = static_cast<IT *>(a.o);
-  const unsigned char *wsq = ONE ? nullptr : ws + (size_t)bh * NSYS * S::IMG;
-  const float *carry =
-      ONE ? nullptr : reinterpret_cast<const float *>(ws + (size_t)a.B * H * NSYS * S::IMG + (size_t)bh * S::CARRY);
+  // two-kernel form: this sequence's images (consecutive systems) and its carry
+  // block, for a dense batch or packed sequences (image slots per head)
+  const unsigned char *wsq = nullptr;
+  const float *carry = nullptr;
+  if constexpr (!ONE) {
+    if (a.cu) {
+      const int SL = S::slots(a.B, a.T);
+      wsq = ws + ((size_t)h * SL + S::slot0(a.cu, b)) * S::IMG;
+      carry = reinterpret_cast<const float *>(ws + (size_t)H * SL * S::IMG + (size_t)bh * S::CARRY);
+    } else {
+      wsq = ws + (size_t)bh * NSYS * S::IMG;
+      carry = reinterpret_cast<const float *>(ws + (size_t)a.B * H * NSYS * S::IMG + (size_t)bh * S::CARRY);
+    }
+  }
   // carried features / window values: the prep kernel's copy (two-kernel form) or the
   // caller's incoming state (one-pass form; then the outgoing state is written by the
   // tail kernel when it may alias and other workgroups read it)
@@ -1221,9 +1273,11 @@ template <int VAR, typename IT, int D, int C, int BW>
 hipError_t launch_split(const FwdArgs &a, void *ws, hipStream_t st) {
   const int ns = pick_ns<VAR, IT, D, C, BW>(a.B * a.H);
   if (ns == 0) return hipErrorInvalidValue;
+  using Sp = Split<VAR, IT, D, C, BW>;
   unsigned char *w = static_cast<unsigned char *>(ws);
-  const int nsys = Split<VAR, IT, D, C, BW>::nsys(a.T);
-  hipLaunchKernelGGL((chunk_prep<VAR, IT, D, C, BW>), dim3(a.B * a.H * nsys), dim3(256), 0, st, a, w);
+  // packed sequences: one prep workgroup per image slot of each head (a.T is the total token count)
+  const long long nprep = a.cu ? (long long)a.H * Sp::slots(a.B, a.T) : (long long)a.B * a.H * Sp::nsys(a.T);
+  hipLaunchKernelGGL((chunk_prep<VAR, IT, D, C, BW>), dim3((unsigned)nprep), dim3(256), 0, st, a, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (ns) {

@@ -21,7 +21,7 @@ PER_CHANNEL = ("F2", "F2A")
 WINDOWED = ("F3", "F3A")
 
 EXPORTS = ("falcon_abi_version", "falcon_status_string", "falcon_chunk_fwd_workspace",
-           "falcon_chunk_fwd", "falcon_chunk_fwd_varlen", "falcon_recurrent_step",
+           "falcon_chunk_fwd", "falcon_chunk_fwd_varlen_workspace", "falcon_chunk_fwd_varlen", "falcon_recurrent_step",
            "falcon_chunk_bwd_workspace", "falcon_chunk_bwd",
            "falcon_chunk_fwd_segmented_workspace", "falcon_chunk_fwd_segmented", "falcon_chunk_fwd_static")
 
@@ -65,8 +65,10 @@ def lib() -> ctypes.CDLL:
         L.falcon_chunk_fwd_workspace.argtypes = [P(Shape)]
         L.falcon_chunk_fwd.restype = I
         L.falcon_chunk_fwd.argtypes = [P(Shape), V, V, V, V, V, P(State), P(State), V, V, V, S, V]
+        L.falcon_chunk_fwd_varlen_workspace.restype = S
+        L.falcon_chunk_fwd_varlen_workspace.argtypes = [P(Shape)]
         L.falcon_chunk_fwd_varlen.restype = I
-        L.falcon_chunk_fwd_varlen.argtypes = [P(Shape), V, V, V, V, V, V, P(State), P(State), V, V]
+        L.falcon_chunk_fwd_varlen.argtypes = [P(Shape), V, V, V, V, V, V, P(State), P(State), V, V, S, V]
         L.falcon_recurrent_step.restype = I
         L.falcon_recurrent_step.argtypes = [P(Shape), V, V, V, V, V, P(State), V, V]
         L.falcon_chunk_fwd_segmented_workspace.restype = S
@@ -235,13 +237,16 @@ def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=No
 
 def chunk_fwd_varlen(variant, q, k, v, beta, log_lambda, cu_seqlens, *, chunk=64, window=1, init=None,
                      final=True, eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, out=None, stream=None,
-                     align="prefix"):
+                     align="prefix", workspace=None):
     """falcon_chunk_fwd_varlen on torch tensors: N packed sequences.
 
     q, k [total,H,dk] and v [total,H,dv] (float32 or bfloat16); beta [total,H]
     (or [total,H,dv] for F2/F2A) and log_lambda [total,H] float32; cu_seqlens an
     int32 device tensor [N+1] of token offsets.  ``init`` / ``final`` as for
-    chunk_fwd, with N sequences.  Returns (o, final_state)."""
+    chunk_fwd, with N sequences.  ``workspace``: None (the one-pass kernel where
+    it is built for the shape, else the chunk-parallel path with a workspace
+    allocated here), True (allocate and take the chunk-parallel path), False
+    (one-pass only), or a uint8 device tensor.  Returns (o, final_state)."""
     import torch
     total, H, dk = q.shape
     dv = v.shape[-1]
@@ -269,12 +274,30 @@ def chunk_fwd_varlen(variant, q, k, v, beta, log_lambda, cu_seqlens, *, chunk=64
     if final is not None:
         _check_state("final", final, N, H, dk, dv, wst, dev)
     shape = make_shape(variant, dt, N, total, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
+    L = lib()
+    need = int(L.falcon_chunk_fwd_varlen_workspace(ctypes.byref(shape)))
     st_in, st_out = _state(init), _state(final)
-    status = lib().falcon_chunk_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
-                                           _ptr(beta), _ptr(log_lambda),
-                                           ctypes.byref(st_in) if st_in else None,
-                                           ctypes.byref(st_out) if st_out else None,
-                                           _ptr(out), _stream(stream))
+
+    def run(ws):
+        return L.falcon_chunk_fwd_varlen(ctypes.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(beta), _ptr(log_lambda),
+                                         ctypes.byref(st_in) if st_in else None,
+                                         ctypes.byref(st_out) if st_out else None,
+                                         _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+
+    if workspace is None:
+        # the one-pass kernel where it is built; a shape it does not build is refused
+        # on the host with FALCON_ERR_WORKSPACE, and then runs with a workspace
+        status = run(None)
+        if status == ERR_WORKSPACE and need:
+            status = run(torch.empty(need, dtype=torch.uint8, device=dev))
+    elif workspace is True:
+        status = run(torch.empty(need, dtype=torch.uint8, device=dev) if need else None)
+    elif workspace is False:
+        status = run(None)
+    else:
+        _check_tensor("workspace", workspace, torch.uint8, (workspace.numel(),), dev)
+        status = run(workspace)
     if status != OK:
         raise FalconError(status, "falcon_chunk_fwd_varlen")
     return out, final

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     L = F.lib()
-    assert L.falcon_abi_version() == 3
+    assert L.falcon_abi_version() == 4
     for code in range(5):
         s = F.status_string(code)
         assert s.startswith("FALCON_")
@@ -171,11 +171,16 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
         F.lib()
 
 
-def call_varlen(shape, cu=FAKE, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, init=None, final=None, o=FAKE):
+def call_varlen(shape, cu=FAKE, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, init=None, final=None, o=FAKE,
+                ws=None, wsb=0):
     L = F.lib()
     return L.falcon_chunk_fwd_varlen(ctypes.byref(shape) if shape is not None else None, cu, q, k, v, beta, g,
                                      ctypes.byref(init) if init else None, ctypes.byref(final) if final else None,
-                                     o, None)
+                                     o, ws, wsb, None)
+
+
+def varlen_workspace(**kw):
+    return F.lib().falcon_chunk_fwd_varlen_workspace(ctypes.byref(good_shape(**kw)))
 
 
 @cpu_only
@@ -186,9 +191,31 @@ def test_varlen_rejects_on_host():
     assert call_varlen(good_shape(seqlen=500), cu=ctypes.c_void_p(0x10002)) == F.ERR_INVALID_ARG
     assert call_varlen(good_shape(seqlen=500), q=None) == F.ERR_INVALID_ARG
     assert call_varlen(good_shape(seqlen=500, batch=0)) == F.ERR_INVALID_ARG
+    # no one-pass kernel and no chunk-parallel path either
     assert call_varlen(good_shape(seqlen=500, dtype="fp32", dk=64, dv=64, chunk=64)) == F.ERR_UNSUPPORTED
-    assert call_varlen(good_shape(seqlen=500, dk=128, dv=128)) == F.ERR_UNSUPPORTED
     assert call_varlen(good_shape(seqlen=500, variant="F3", window=4, chunk=32)) == F.ERR_UNSUPPORTED
+    # bf16 d = 128: only the chunk-parallel path, which needs the workspace
+    assert call_varlen(good_shape(seqlen=500, dk=128, dv=128)) == F.ERR_WORKSPACE
+    need = varlen_workspace(seqlen=500, dk=128, dv=128)
+    assert need > 0
+    assert call_varlen(good_shape(seqlen=500, dk=128, dv=128), ws=FAKE, wsb=need - 1) == F.ERR_WORKSPACE
+    assert call_varlen(good_shape(seqlen=500, dk=128, dv=128), ws=ctypes.c_void_p(0x10008), wsb=need) == \
+        F.ERR_INVALID_ARG
+
+
+def test_varlen_workspace_size():
+    """Per head, one image slot per system the packed sequences can have (at most
+    total/C + N + 1), plus one carried-state block per sequence and head."""
+    one = varlen_workspace(batch=1, seqlen=64, heads=1)
+    assert one > 0
+    # N sequences of total tokens: slots grow with total / C + N
+    a = varlen_workspace(batch=4, seqlen=1000, heads=3)
+    b = varlen_workspace(batch=8, seqlen=1000, heads=3)
+    c = varlen_workspace(batch=4, seqlen=2000, heads=3)
+    assert a < b and a < c
+    assert varlen_workspace(batch=4, seqlen=1000, heads=3, dtype="fp32", dk=64, dv=64, chunk=64) == 0
+    # at least the dense layout's size for equal-length sequences (that layout is packed tight)
+    assert varlen_workspace(batch=4, seqlen=4 * 256, heads=3) >= workspace(batch=4, seqlen=256, heads=3)
 
 
 def bwd_workspace(**kw):

@@ -316,7 +316,7 @@ def test_same_step_continuation_in_place(variant, bw, workspace):
 
 
 # ---- packed sequences of different lengths (cu_seqlens) ---------------------------
-def run_varlen(variant, lens, dtype, d, chunk, bw, seed, init=True, in_place=False, align="prefix"):
+def run_varlen(variant, lens, dtype, d, chunk, bw, seed, init=True, in_place=False, align="prefix", workspace=None):
     """Pack len(lens) independent sequences (H = 3), run falcon_chunk_fwd_varlen and
     the oracle per sequence; returns the rel-L2 errors per sequence and name."""
     import torch
@@ -339,7 +339,7 @@ def run_varlen(variant, lens, dtype, d, chunk, bw, seed, init=True, in_place=Fal
         st_dev = state_to_dev({k: np.concatenate([s[k] for s in states], axis=0) for k in states[0]})
     fin = st_dev if in_place else True
     o, fin = chunk_fwd_varlen(variant, d_in["q"], d_in["k"], d_in["v"], d_in["beta"], d_in["log_lambda"], cu,
-                              chunk=chunk, window=bw, init=st_dev, final=fin, align=align)
+                              chunk=chunk, window=bw, init=st_dev, final=fin, align=align, workspace=workspace)
     torch.cuda.synchronize()
     o = to_np(o)
     fin = {k: to_np(t) for k, t in fin.items()}
@@ -362,8 +362,34 @@ VARLEN_CASES = [(v, 1) for v in ROW_VARIANTS] + [("F3", 4), ("F3A", 8), ("F3", 2
 
 @pytest.mark.parametrize("variant,bw", VARLEN_CASES)
 @pytest.mark.parametrize("in_place", [False, True])
-def test_varlen_bf16(variant, bw, in_place):
-    errs = run_varlen(variant, [1, 17, 64, 65, 130, 200, 7], "bf16", 64, 64, bw, 91, in_place=in_place)
+@pytest.mark.parametrize("workspace", [False, True])
+def test_varlen_bf16(variant, bw, in_place, workspace):
+    """Without a workspace: the one-pass kernel; with one: prep over every image
+    slot of the packed layout, then the state scan."""
+    errs = run_varlen(variant, [1, 17, 64, 65, 130, 200, 7], "bf16", 64, 64, bw, 91, in_place=in_place,
+                      workspace=workspace)
+    for e in errs:
+        for k, x in e.items():
+            assert x <= TOL["bf16"], (k, x, e)
+
+
+@pytest.mark.parametrize("variant,bw", VARLEN_CASES)
+@pytest.mark.parametrize("in_place", [False, True])
+def test_varlen_d128(variant, bw, in_place):
+    """bf16 at d = 128, chunk 64 (the decode workload's head dim): packed sequences
+    on the chunk-parallel path (with a workspace), an empty one among them."""
+    errs = run_varlen(variant, [3, 64, 0, 150, 1, 90], "bf16", 128, 64, bw, 94, in_place=in_place)
+    assert len(errs) == 5
+    for e in errs:
+        for k, x in e.items():
+            assert x <= TOL["bf16"], (k, x, e)
+
+
+@pytest.mark.parametrize("variant,bw", [("F1", 1), ("F3", 4)])
+def test_varlen_workspace_same_step_and_small_chunks(variant, bw):
+    """Same-step pairs on the packed chunk-parallel path; fp32 at chunk 16 with a workspace."""
+    errs = run_varlen(variant, [40, 0, 90, 5], "bf16", 64, 64, bw, 95, align="same", workspace=True)
+    errs += run_varlen(variant if bw == 1 else "F1", [3, 50, 33, 1], "fp32", 32, 16, 1, 96, workspace=True)
     for e in errs:
         for k, x in e.items():
             assert x <= TOL["bf16"], (k, x, e)

@@ -250,16 +250,18 @@ def test_prefill_then_decode(variant, bw, T, workspace):
         assert rel_l2(to_np(st[n]), r[n]) <= TOL["bf16"], n
 
 
-@pytest.mark.parametrize("variant,bw", [("F1", 1), ("F3", 4)])
-def test_varlen_prefill_then_decode(variant, bw):
+@pytest.mark.parametrize("variant,bw", [("F1", 1), ("F3", 4), ("F1A", 1)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_prefill_then_decode(variant, bw, d):
     """Packed prefill of sequences of lengths 5, 70 and 2, then 4 decode steps of
-    the three together from the packed call's final states."""
+    the three together from the packed call's final states (d = 128: the packed
+    chunk-parallel path, as for the decode workload's head dim)."""
     import torch
     from recurrent_sequence_models_amd import chunk_fwd_varlen, recurrent_step
     lens, extra, H = [5, 70, 2], 4, 3
     seqs, refs, states = [], [], []
     for n, T in enumerate(lens):
-        w = W.WORKLOADS["layer130m"].replace(batch=1, heads=H, seqlen=T + extra)
+        w = W.WORKLOADS["layer130m"].replace(batch=1, heads=H, seqlen=T + extra, dk=d, dv=d)
         inp = W.make_inputs(w, variant, seed=151 + n, window=bw)
         st = W.make_state(w, 1151 + n, bw)
         seqs.append(inp)
