@@ -367,7 +367,7 @@ def main():
 
     import torch
     import workloads as W
-    from recurrent_sequence_models_amd import chunk_fwd, chunk_fwd_segmented, new_state
+    from recurrent_sequence_models_amd import ForwardCall, chunk_fwd_segmented, new_state
     from recurrent_sequence_models_amd.falcon import segmented_workspace_bytes, workspace_bytes
 
     w = W.WORKLOADS[args.workload]
@@ -404,14 +404,19 @@ def main():
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         path = f"segmented x{args.segments}"
 
+    # each input set's forward, validated once (ForwardCall): a step is then one C call
+    if args.segments == 0:
+        for d in sets:
+            d["fwd"] = ForwardCall(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk,
+                                   window=window, final=d["final"], out=d["o"], stream=stream, workspace=ws)
+
     def call(d):
         if args.segments > 0:
             chunk_fwd_segmented(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], args.segments,
                                 chunk=w.chunk, window=window, final=d["final"], out=d["o"], stream=stream,
                                 workspace=ws)
             return
-        chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk, window=window,
-                  final=d["final"], out=d["o"], stream=stream, workspace=ws)
+        d["fwd"]()
 
     for i in range(args.warmup):
         call(sets[i % 3])

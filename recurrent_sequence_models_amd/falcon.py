@@ -174,6 +174,75 @@ def workspace_bytes(variant, dtype, batch, seqlen, heads, dk, dv, chunk=64, wind
     return int(lib().falcon_chunk_fwd_workspace(ctypes.byref(shape)))
 
 
+class ForwardCall:
+    """One falcon_chunk_fwd call, validated once and issued as often as needed.
+
+    For loops that run the forward over the same buffers again and again (their
+    contents may change between calls): every argument check, allocation and
+    ctypes conversion happens here, and each call is one C call.  Arguments are
+    those of ``chunk_fwd``; ``stream`` (optional) is fixed for every call unless
+    one is passed to ``__call__``.  The object keeps every tensor it passes
+    alive: ``out``, ``final`` and ``chunk_states`` are its outputs."""
+
+    def __init__(self, variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=None,
+                 final=True, chunk_states=False, eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6,
+                 out=None, stream=None, workspace=True, align="prefix"):
+        import torch
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        dev = q.device
+        dt = {torch.float32: "fp32", torch.bfloat16: "bf16"}.get(q.dtype)
+        if dt is None:
+            raise TypeError("q/k/v must be float32 or bfloat16")
+        _check_tensor("q", q, q.dtype, (B, T, H, dk), dev)
+        _check_tensor("k", k, q.dtype, (B, T, H, dk), dev)
+        _check_tensor("v", v, q.dtype, (B, T, H, dv), dev)
+        bshape = (B, T, H, dv) if variant in PER_CHANNEL else (B, T, H)
+        _check_tensor("beta", beta, torch.float32, bshape, dev)
+        _check_tensor("log_lambda", log_lambda, torch.float32, (B, T, H), dev)
+        if out is None:
+            out = torch.empty(B, T, H, dv, dtype=q.dtype, device=dev)
+        _check_tensor("o", out, q.dtype, (B, T, H, dv), dev)
+        if final is True:
+            final = new_state(B, H, dk, dv, window if variant in WINDOWED else 1, dev)
+        elif final is False:
+            final = None
+        wst = window if variant in WINDOWED else 1
+        if init is not None:
+            _check_state("init", init, B, H, dk, dv, wst, dev)
+        if final is not None:
+            _check_state("final", final, B, H, dk, dv, wst, dev)
+        nch = (T + chunk - 1) // chunk
+        cs = torch.empty(B, H, nch, dv, dk, dtype=torch.float32, device=dev) if chunk_states else None
+        shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
+        L = lib()
+        if workspace is True:
+            ws_bytes = L.falcon_chunk_fwd_workspace(ctypes.byref(shape))
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        elif workspace is False or workspace is None:
+            ws, ws_bytes = None, 0
+        else:
+            _check_tensor("workspace", workspace, torch.uint8, (workspace.numel(),), dev)
+            ws, ws_bytes = workspace, workspace.numel()
+        self.out, self.final, self.chunk_states = out, final, cs
+        self._keep = (q, k, v, beta, log_lambda, init, ws)
+        self._shape = shape
+        self._st_in, self._st_out = _state(init), _state(final)
+        self._fn = L.falcon_chunk_fwd
+        self._args = (ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_lambda),
+                      ctypes.byref(self._st_in) if self._st_in else None,
+                      ctypes.byref(self._st_out) if self._st_out else None,
+                      _ptr(out), _ptr(cs), _ptr(ws), ws_bytes)
+        self._stream = None if stream is None else _stream(stream)
+
+    def __call__(self, stream=None):
+        st = _stream(stream) if stream is not None else (self._stream if self._stream is not None else _stream(None))
+        status = self._fn(*self._args, st)
+        if status != OK:
+            raise FalconError(status, "falcon_chunk_fwd")
+        return self.out, self.final, self.chunk_states
+
+
 def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=None,
               final=True, chunk_states=False, eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6,
               out=None, stream=None, workspace=True, align="prefix"):
@@ -187,52 +256,11 @@ def chunk_fwd(variant, q, k, v, beta, log_lambda, *, chunk=64, window=1, init=No
     has one, False runs the one-pass (or fused) kernel without scratch, or a
     uint8 device tensor to use.  ``align``: "prefix" (the pair written at step t
     is (phi(k_{t-1}), v_t)) or "same" ((phi(k_t), v_t)).
-    Returns (o, final_state, chunk_states)."""
-    import torch
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    dev = q.device
-    dt = {torch.float32: "fp32", torch.bfloat16: "bf16"}.get(q.dtype)
-    if dt is None:
-        raise TypeError("q/k/v must be float32 or bfloat16")
-    _check_tensor("q", q, q.dtype, (B, T, H, dk), dev)
-    _check_tensor("k", k, q.dtype, (B, T, H, dk), dev)
-    _check_tensor("v", v, q.dtype, (B, T, H, dv), dev)
-    bshape = (B, T, H, dv) if variant in PER_CHANNEL else (B, T, H)
-    _check_tensor("beta", beta, torch.float32, bshape, dev)
-    _check_tensor("log_lambda", log_lambda, torch.float32, (B, T, H), dev)
-    if out is None:
-        out = torch.empty(B, T, H, dv, dtype=q.dtype, device=dev)
-    _check_tensor("o", out, q.dtype, (B, T, H, dv), dev)
-    if final is True:
-        final = new_state(B, H, dk, dv, window if variant in WINDOWED else 1, dev)
-    elif final is False:
-        final = None
-    wst = window if variant in WINDOWED else 1
-    if init is not None:
-        _check_state("init", init, B, H, dk, dv, wst, dev)
-    if final is not None:
-        _check_state("final", final, B, H, dk, dv, wst, dev)
-    nch = (T + chunk - 1) // chunk
-    cs = torch.empty(B, H, nch, dv, dk, dtype=torch.float32, device=dev) if chunk_states else None
-    shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
-    L = lib()
-    if workspace is True:
-        ws_bytes = L.falcon_chunk_fwd_workspace(ctypes.byref(shape))
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    elif workspace is False or workspace is None:
-        ws, ws_bytes = None, 0
-    else:
-        _check_tensor("workspace", workspace, torch.uint8, (workspace.numel(),), dev)
-        ws, ws_bytes = workspace, workspace.numel()
-    st_in, st_out = _state(init), _state(final)
-    status = L.falcon_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_lambda),
-                                ctypes.byref(st_in) if st_in else None,
-                                ctypes.byref(st_out) if st_out else None,
-                                _ptr(out), _ptr(cs), _ptr(ws), ws_bytes, _stream(stream))
-    if status != OK:
-        raise FalconError(status, "falcon_chunk_fwd")
-    return out, final, cs
+    Returns (o, final_state, chunk_states).  For repeated calls over the same
+    buffers, ``ForwardCall`` does the checks once."""
+    return ForwardCall(variant, q, k, v, beta, log_lambda, chunk=chunk, window=window, init=init, final=final,
+                       chunk_states=chunk_states, eps_gamma=eps_gamma, eps_phi=eps_phi, eps_eta=eps_eta, out=out,
+                       workspace=workspace, align=align)(stream)
 
 
 def chunk_fwd_varlen(variant, q, k, v, beta, log_lambda, cu_seqlens, *, chunk=64, window=1, init=None,

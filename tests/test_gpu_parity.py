@@ -525,3 +525,25 @@ def test_window_full_size_sampled(variant, bw):
         es = rel_l2(g["S"][b, h], r["S"][0, 0])
         print(variant, bw, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("workspace", [False, True])
+def test_forward_call_reuse(workspace):
+    """A ForwardCall validated once and issued again after its input buffers were
+    refilled gives what a fresh chunk_fwd call gives on the new contents."""
+    import torch
+    from recurrent_sequence_models_amd import ForwardCall, chunk_fwd
+    w = W.WORKLOADS["layer130m"].replace(batch=2, heads=3, seqlen=150)
+    d1 = to_dev(W.make_inputs(w, "F1", seed=201), "bf16")
+    d2 = to_dev(W.make_inputs(w, "F1", seed=202), "bf16")
+    names = ("q", "k", "v", "beta", "log_lambda")
+    buf = {n: d1[n].clone() for n in names}
+    call = ForwardCall("F1", *(buf[n] for n in names), chunk_states=True, workspace=workspace)
+    for d in (d1, d2, d1):
+        for n in names:
+            buf[n].copy_(d[n])
+        o, fin, cs = call()
+        ro, rfin, rcs = chunk_fwd("F1", *(d[n] for n in names), chunk_states=True, workspace=workspace)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ro) and torch.equal(cs, rcs)
+        assert torch.equal(fin["S"], rfin["S"]) and torch.equal(fin["x_prev"], rfin["x_prev"])
