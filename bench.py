@@ -147,17 +147,19 @@ def bwd_flops(w, variant):
     F1A = 6.5 u (prep 1, adjoint 5.5)."""
     C, d = w.chunk, w.dk
     u = 2 * C * d * d
-    per_chunk = {"F1": 15 * u, "F1A": 6.5 * u}[variant]
+    per_chunk = {"F1": 15 * u, "F1A": 6.5 * u, "F2A": 6.5 * u}[variant]   # F2A: F1A on beta (.) v
     return w.batch * w.heads * (-(-w.seqlen // C)) * per_chunk
 
 
-def bwd_bytes(w):
+def bwd_bytes(w, variant="F1"):
     """Algorithmic HBM bytes of one backward call: q, k, v, do in the input
     dtype, beta and g, the per-chunk states, the fp32 gradients of q, k, v,
-    beta and g, and the final-state gradient and initial-state gradients."""
+    beta and g, and the final-state gradient and initial-state gradients
+    (F2A: beta and its gradient per value channel)."""
     e = 2 if w.dtype == "bf16" else 4
     nch = -(-w.seqlen // w.chunk)
-    per_th = 4 * w.dk * e + 8 + 3 * w.dk * 4 + 8
+    nb = w.dv if variant in ("F2", "F2A") else 1
+    per_th = 4 * w.dk * e + 4 * nb + 4 + 3 * w.dk * 4 + 4 * nb + 4
     per_seq = nch * w.dv * w.dk * 4 + 2 * w.dv * w.dk * 4 + w.dk * 4
     return w.batch * w.heads * (w.seqlen * per_th + per_seq)
 
@@ -226,7 +228,7 @@ def bench_backward(args):
         d["out"] = dict(dq=torch.empty(w.batch, w.seqlen, w.heads, w.dk, device=dev),
                         dk=torch.empty(w.batch, w.seqlen, w.heads, w.dk, device=dev),
                         dv=torch.empty(w.batch, w.seqlen, w.heads, w.dv, device=dev),
-                        dbeta=torch.empty(w.batch, w.seqlen, w.heads, device=dev),
+                        dbeta=torch.empty(*d["beta"].shape, device=dev),
                         dg=torch.empty(w.batch, w.seqlen, w.heads, device=dev))
         d["d_init"] = dict(S=torch.empty(w.batch, w.heads, w.dv, w.dk, device=dev),
                            x_prev=torch.empty(w.batch, w.heads, w.dk, device=dev))
@@ -254,7 +256,7 @@ def bench_backward(args):
     kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
     avg_s = sum(kern_ms) / K / 1e3
     flops = bwd_flops(w, variant)
-    nbytes = bwd_bytes(w)
+    nbytes = bwd_bytes(w, variant)
     tfs = flops / avg_s / 1e12
     line = {
         "metric": f"tokens/sec, Falcon-{variant[1:]} chunked backward (H={w.heads},d={w.dk},T={w.seqlen}) "

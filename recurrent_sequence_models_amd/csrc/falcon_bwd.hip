@@ -1,5 +1,11 @@
 // Backward pass of the chunk-parallel form for Falcon-1 / 1A (scalar NLMS step,
-// one pair per step), d_k = d_v = 64, chunks of 64 steps.
+// one pair per step) and Falcon-2A, d_k = d_v = 64, chunks of 64 steps.
+//
+// Falcon-2A writes diag(beta_t) v_t x_t^T / (eps_eta + |x_t|^2): it is Falcon-1A
+// with values beta (.) v and a unit gain ([P1] Falcon家族: only the step becomes a
+// vector over value channels).  So it runs the Falcon-1A kernels with those
+// values and eta_t = 1 / (eps_eta + |x_t|^2), and the gradient of the values dE
+// gives dv = beta (.) dE and the per-channel gain gradient dbeta = v (.) dE.
 //
 // It differentiates the scalar <do, o> + <dS_T, S_T> with respect to q, k, v,
 // beta, the log-decay g and the incoming state, reading the per-chunk states the
@@ -110,7 +116,7 @@ __device__ __forceinline__ void load_e(const IT *p, float (&v)[E]) {
   for (int j = 0; j < E; ++j) v[j] = (float)p[j];
 }
 
-template <typename IT, int NTH>
+template <typename IT, int NTH, bool UNIT = false>   // UNIT: eta = 1 / (eps_eta + |x|^2) (Falcon-2A)
 __device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, RowScalars &rs) {
   constexpr int NP = NTH / 64, E = 64 / NP;
   const int tid = threadIdx.x, r = tid / NP, p = tid % NP, lane = tid & 63;
@@ -152,7 +158,7 @@ __device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, 
     const size_t gi = (size_t)(b * a.T + t) * a.H + h;
     const float en = a.eps_eta + e;
     rs.en[r] = en;
-    rs.eta[r] = live ? a.beta[gi] / en : 0.f;
+    rs.eta[r] = live ? (UNIT ? 1.f : a.beta[gi]) / en : 0.f;
     rs.L[r] = live ? fmaxf(a.g[gi], a.log_eps_gamma) : 0.f;  // log-decay, summed below
   }
   __syncthreads();
@@ -511,7 +517,7 @@ __device__ void adjoint_tile(float *sA, float *sP, const float *sG, const float 
   }
 }
 
-template <typename IT, bool ADD>
+template <typename IT, bool ADD, bool PC = false>   // PC: Falcon-2A (ADD, per-channel gains)
 __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[ADD ? 4 : MAT], sP[MAT],
       sE[MAT], sO[MAT];
@@ -539,13 +545,16 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
     pL[w][lane] = 0.f;
     pE[w][lane] = 0.f;
   }
-  f4 V;
+  f4 V, Vraw, Bch;   // Falcon-2A: the value beta (.) v, and v and beta themselves
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 16 * rt + 4 * g + i;
-    V[i] = row < live ? (float)((const IT *)a.v)[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] : 0.f;
+    const size_t e = (row0 + (size_t)row * a.H) * D + 16 * ct + cc;
+    Vraw[i] = row < live ? (float)((const IT *)a.v)[e] : 0.f;
+    Bch[i] = (PC && row < live) ? a.beta[e] : 0.f;
+    V[i] = PC ? Bch[i] * Vraw[i] : Vraw[i];
   }
-  load_rows<IT, NTC>(a, n, c, sX, sQ, rs);  // ends with a barrier
+  load_rows<IT, NTC, PC>(a, n, c, sX, sQ, rs);  // ends with a barrier
   const float LC = rs.L[C - 1];
   float lc = 0.f;  // this lane's share of dL_C
   {
@@ -649,7 +658,11 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 16 * rt + 4 * g + i;
-    if (row < live) a.dv[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] = dE[i];
+    const size_t e = (row0 + (size_t)row * a.H) * D + 16 * ct + cc;
+    if (row < live) {
+      a.dv[e] = PC ? Bch[i] * dE[i] : dE[i];
+      if (PC) a.dbeta[e] = Vraw[i] * dE[i];   // per-channel gains: d beta = v (.) dE
+    }
   }
 
   // Phase 6: dR S0 (into dX and dL_{i-1}); the C x C adjoints.
@@ -710,7 +723,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
     }
     if (i < live) {
       const size_t gi = row0 + (size_t)i * a.H;
-      a.dbeta[gi] = de / rs.en[i];
+      if (!PC) a.dbeta[gi] = de / rs.en[i];   // Falcon-2A writes its per-channel d beta above
       a.dg[gi] = a.g[gi] > a.log_eps_gamma ? dl : 0.f;
     }
     sCoef[i] = -2.f * de * rs.eta[i] / rs.en[i];
@@ -801,7 +814,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   }
 }
 
-template <typename IT, bool ADD>
+template <typename IT, bool ADD, bool PC = false>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   const unsigned nch = (unsigned)a.B * a.H * a.NC;
   hipLaunchKernelGGL((bwd_prep<IT, ADD>), dim3(nch), dim3(256), 0, st, a);
@@ -810,14 +823,14 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_scan<ADD>), dim3((unsigned)a.B * a.H * 4), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_chunk<IT, ADD>), dim3(nch), dim3(NTC), 0, st, a);
+  hipLaunchKernelGGL((bwd_chunk<IT, ADD, PC>), dim3(nch), dim3(NTC), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool chunk_bwd_supported(int variant, int dk, int dv, int chunk, int window) {
-  return (variant == 1 || variant == 2) && dk == D && dv == D && chunk == C && window == 1;
+  return (variant == 1 || variant == 2 || variant == 4) && dk == D && dv == D && chunk == C && window == 1;
 }
 
 size_t chunk_bwd_workspace(int B, int H, int T) {
@@ -826,6 +839,7 @@ size_t chunk_bwd_workspace(int B, int H, int T) {
 }
 
 hipError_t launch_chunk_bwd(int variant, bool bf16, const BwdArgs &a, hipStream_t st) {
+  if (variant == 4) return bf16 ? launch_bwd_t<__bf16, true, true>(a, st) : launch_bwd_t<float, true, true>(a, st);
   const bool add = variant == 2;
   if (bf16) return add ? launch_bwd_t<__bf16, true>(a, st) : launch_bwd_t<__bf16, false>(a, st);
   return add ? launch_bwd_t<float, true>(a, st) : launch_bwd_t<float, false>(a, st);

@@ -392,7 +392,8 @@ def chunk_bwd(variant, q, k, v, beta, log_lambda, do, chunk_states, *, init=None
     _check_tensor("k", k, q.dtype, (B, T, H, dk), dev)
     _check_tensor("v", v, q.dtype, (B, T, H, dv), dev)
     _check_tensor("do", do, q.dtype, (B, T, H, dv), dev)
-    _check_tensor("beta", beta, torch.float32, (B, T, H), dev)
+    bshape = (B, T, H, dv) if variant in PER_CHANNEL else (B, T, H)
+    _check_tensor("beta", beta, torch.float32, bshape, dev)
     _check_tensor("log_lambda", log_lambda, torch.float32, (B, T, H), dev)
     nch = (T + chunk - 1) // chunk
     _check_tensor("chunk_states", chunk_states, torch.float32, (B, H, nch, dv, dk), dev)
@@ -400,10 +401,10 @@ def chunk_bwd(variant, q, k, v, beta, log_lambda, do, chunk_states, *, init=None
         _check_tensor("dS_T", dS_T, torch.float32, (B, H, dv, dk), dev)
     if out is None:
         out = dict(dq=torch.empty(B, T, H, dk, device=dev), dk=torch.empty(B, T, H, dk, device=dev),
-                   dv=torch.empty(B, T, H, dv, device=dev), dbeta=torch.empty(B, T, H, device=dev),
+                   dv=torch.empty(B, T, H, dv, device=dev), dbeta=torch.empty(*bshape, device=dev),
                    dg=torch.empty(B, T, H, device=dev))
     for name, shp in (("dq", (B, T, H, dk)), ("dk", (B, T, H, dk)), ("dv", (B, T, H, dv)),
-                      ("dbeta", (B, T, H)), ("dg", (B, T, H))):
+                      ("dbeta", bshape), ("dg", (B, T, H))):
         _check_tensor(name, out[name], torch.float32, shp, dev)
     if d_init is True:
         d_init = new_state(B, H, dk, dv, 1, dev)

@@ -233,12 +233,13 @@ def call_bwd(shape, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, init=None, cs=FAK
 def test_bwd_workspace_size():
     """Per chunk of 64 steps: keys, the scaled WY factor, the injected state
     gradient and the end-of-chunk state gradient (4 x 64 x 64 fp32) plus the
-    chunk's decay; F1 and F1A at d = 64, chunk 64 only."""
+    chunk's decay; F1, F1A and F2A at d = 64, chunk 64 only."""
     per_chunk = 4 * 64 * 64 * 4 + 4
     assert bwd_workspace(seqlen=64, batch=1, heads=1) == per_chunk
     assert bwd_workspace(seqlen=100) == 2 * 3 * 2 * per_chunk
     assert bwd_workspace(seqlen=129, variant="F1A", dtype="fp32") == 2 * 3 * 3 * per_chunk
-    for kw in (dict(variant="F2"), dict(variant="F2A"), dict(variant="F3", window=2), dict(variant="F3A"),
+    assert bwd_workspace(seqlen=100, variant="F2A") == 2 * 3 * 2 * per_chunk
+    for kw in (dict(variant="F2"), dict(variant="F3", window=2), dict(variant="F3A"),
                dict(dk=32, dv=32), dict(dk=128, dv=128), dict(chunk=32), dict(batch=0)):
         assert bwd_workspace(**kw) == 0, kw
 

@@ -60,7 +60,8 @@ def small(T, dtype, B=2, H=3, gates="floor5"):
     return W.WORKLOADS["layer130m"].replace(name=f"bwd_T{T}", batch=B, heads=H, seqlen=T, dtype=dtype, gates=gates)
 
 
-CASES = [(v, dt, al) for v in ("F1", "F1A") for dt in ("fp32", "bf16") for al in ("prefix", "same")]
+BWD_VARIANTS = ("F1", "F1A", "F2A")
+CASES = [(v, dt, al) for v in BWD_VARIANTS for dt in ("fp32", "bf16") for al in ("prefix", "same")]
 
 
 @pytest.mark.parametrize("variant,dtype,align", CASES)
@@ -77,21 +78,21 @@ def test_backward_fresh_no_final_gradient(variant, dtype, align):
     check_bwd(variant, small(100, dtype), 5, init=False, final_grad=False, align=align)
 
 
-@pytest.mark.parametrize("variant", ["F1", "F1A"])
+@pytest.mark.parametrize("variant", list(BWD_VARIANTS))
 @pytest.mark.parametrize("T", [1, 63, 64, 65])
 def test_backward_edge_lengths(variant, T):
     """One step, one step short of a chunk, exactly one chunk, one step past it."""
     check_bwd(variant, small(T, "fp32", B=1, H=2), 31 + T, init=True, final_grad=True)
 
 
-@pytest.mark.parametrize("variant", ["F1", "F1A"])
+@pytest.mark.parametrize("variant", list(BWD_VARIANTS))
 def test_backward_gates_clear_of_floor(variant):
     """Decays in (0.67, 1) only (no clamped step): every gate takes a gradient."""
     got, ref = check_bwd(variant, small(150, "fp32", gates="softplus"), 3)
     assert np.count_nonzero(got["dg"]) == got["dg"].size
 
 
-@pytest.mark.parametrize("variant", ["F1", "F1A"])
+@pytest.mark.parametrize("variant", list(BWD_VARIANTS))
 def test_backward_deterministic(variant):
     a, *_ = run_bwd(variant, small(200, "bf16"), 9)
     b, *_ = run_bwd(variant, small(200, "bf16"), 9)
@@ -99,7 +100,7 @@ def test_backward_deterministic(variant):
         assert np.array_equal(a[n], b[n]), n
 
 
-@pytest.mark.parametrize("variant", ["F1", "F1A"])
+@pytest.mark.parametrize("variant", list(BWD_VARIANTS))
 def test_backward_full_size_sampled(variant):
     """The full 130M-layer shape (B8 H12 T2048 d64, bf16, chunk 64); the oracle
     checks sampled sequences (sequences are independent, so their gradients are
