@@ -725,8 +725,61 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
   // masks or carried features.
   auto interior = [&](int c) { return c * CS >= BW - a.align && (c + 1) * CS <= T; };
   const long long rstride = (long long)H * D;   // elements between consecutive tokens
+  // Interior systems load through buffer resources based at this sequence's rows,
+  // with lane-constant byte offsets and the system's offset in an SGPR, so a
+  // load needs no per-lane address arithmetic.  The range check of a buffer load
+  // sees the lane offset alone, which must therefore be >= 0: the key and value
+  // resources start BW - 1 rows early, the oldest pair a virtual row can name.
+  // Used while every offset of the sequence fits 31 bits.
+  const bool bufok = (long long)(T + BW + 1) * rstride * S::SZ < 0x7fffffffLL;
+  const long long tokv = tok0 - (BW - 1);         // value row of the oldest pair of system 0
+  const long long tokb = tokv - 1 + a.align;      // its key row
+  const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(vp + tokv * rstride + (long long)h * D + Z::DS * sp), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(kp + tokb * rstride + (long long)h * D), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsq = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(qp + tok0 * rstride + (long long)h * D), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsg = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.g + tok0 * H + h), 0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.beta + (PERCH ? 0 : tok0 * H + h)), 0, 0x7fffffff, 0x00020000);
+  int vofs_v[Z::NPV], vofs_k[Z::NPK], vofs_q[Z::NPK];
+#pragma unroll
+  for (int ps = 0; ps < Z::NPV; ++ps) {
+    const int r = min(ps * RPV + ctid / TPV, C - 1), part = ctid % TPV;
+    vofs_v[ps] = (int)(((pair_of(0, r) + BW - 1) * rstride + part * VEC) * S::SZ);
+  }
+#pragma unroll
+  for (int ps = 0; ps < Z::NPK; ++ps) {
+    const int r = min(ps * RPC + ctid / TPR, C - 1), part = ctid % TPR;
+    vofs_k[ps] = (int)(((pair_of(0, r) + BW - 1) * rstride + part * VEC) * S::SZ);
+    vofs_q[ps] = (int)((min(r, CS - 1) * rstride + part * VEC) * S::SZ);
+  }
+  const int vofs_g = min(ctid, CS - 1) * H * 4;
   auto prefetch = [&](int c, Regs &R) __attribute__((always_inline)) {    // global -> registers, system c (rows clamped in bounds)
     const int c0 = c * CS;
+    if (bufok && interior(c)) {
+      const int so = (int)(c0 * rstride * S::SZ);   // the system's first row
+#pragma unroll
+      for (int ps = 0; ps < Z::NPV; ++ps)
+        R.v[ps] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsv, vofs_v[ps], so, 0));
+#pragma unroll
+      for (int ps = 0; ps < Z::NPK; ++ps) {
+        R.k[ps] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsk, vofs_k[ps], so, 0));
+        R.q[ps] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsq, vofs_q[ps], so, 0));
+      }
+      if constexpr (ONE) {
+        const int sg = c0 * H * 4;
+        R.g = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsg, vofs_g, sg, 0));
+        R.bt = PERCH ? 0.f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, vofs_g, sg, 0));
+      } else {
+        const uint4 *src = reinterpret_cast<const uint4 *>(wsq + (size_t)c * S::IMG);
+#pragma unroll
+        for (int j = 0; j < Z::NPI; ++j) R.img[j] = src[min(ctid + j * Z::NST, S::NU - 1)];
+      }
+      return;
+    }
     if (interior(c)) {
       const long long base = (tok0 + c0) * rstride + (long long)h * D;   // token c0 of the sequence
 #pragma unroll
