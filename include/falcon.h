@@ -274,11 +274,14 @@ int falcon_recurrent_step(const falcon_shape_t *shape,
                           falcon_state_t *state, void *o, void *stream);
 
 /* Bytes of device workspace falcon_chunk_bwd needs for this shape; 0 when the
- * backward pass is not built for it (or the shape is invalid).  Built: F1, F1A
- * and F2A, d_k = d_v = 64, chunk 64, fp32 or bf16 inputs, either pairing.  The
- * workspace holds, per chunk, the keys, the scaled WY factor, the state
+ * backward pass is not built for it (or the shape is invalid).  Built: F1, F1A,
+ * F2 and F2A, d_k = d_v = 64, chunk 64, fp32 or bf16 inputs, either pairing.
+ * The workspace holds, per chunk, the keys, the scaled WY factor, the state
  * gradient the chunk's outputs inject and the state gradient at the chunk's
- * end (4 x 16 KiB + 4 bytes); it needs no initialisation. */
+ * end (4 x 16 KiB + 4 bytes); for F2, whose solves are per value channel, the
+ * keys, the decayed Gram matrix, the injected gradient, the end gradient and
+ * the per-channel steps (5 x 16 KiB) plus 516 bytes of per-row factors.  It
+ * needs no initialisation. */
 size_t falcon_chunk_bwd_workspace(const falcon_shape_t *shape);
 
 /* Backward pass of the chunked form ([P1] 三种等价形式 form C / Figure 4-C: the
@@ -296,7 +299,7 @@ size_t falcon_chunk_bwd_workspace(const falcon_shape_t *shape);
  *   d_final_S    [B, H, 64, 64] fp32, or NULL for a zero gradient on S_T.
  *   dq, dk, dv   [B, T, H, 64] fp32, written whole (under the prefix pairing
  *                dk of the last token is 0).
- *   dbeta, dg    [B, T, H] fp32 (F2A: dbeta [B, T, H, dv], like its beta).
+ *   dbeta, dg    [B, T, H] fp32 (F2/F2A: dbeta [B, T, H, dv], like their beta).
  *   d_init       NULL, or S [B, H, 64, 64] and x_prev [B, H, 64] fp32 that
  *                receive the gradients w.r.t. the initial state (x_prev: 0
  *                under the same-step pairing, which does not read it).

@@ -332,7 +332,7 @@ int falcon_recurrent_step(const falcon_shape_t *s, const void *q, const void *k,
 size_t falcon_chunk_bwd_workspace(const falcon_shape_t *s) {
   if (check_shape(s, false) != FALCON_OK) return 0;
   if (!falcon::chunk_bwd_supported(s->variant, s->dk, s->dv, s->chunk, s->window)) return 0;
-  return falcon::chunk_bwd_workspace(s->batch, s->heads, s->seqlen);
+  return falcon::chunk_bwd_workspace(s->variant, s->batch, s->heads, s->seqlen);
 }
 
 int falcon_chunk_bwd(const falcon_shape_t *s, const void *q, const void *k, const void *v, const float *beta,
@@ -351,7 +351,7 @@ int falcon_chunk_bwd(const falcon_shape_t *s, const void *q, const void *k, cons
   if (init && (st = check_state(init, s)) != FALCON_OK) return st;
   if (d_init && (st = check_state(d_init, s)) != FALCON_OK) return st;
   if (!falcon::chunk_bwd_supported(s->variant, s->dk, s->dv, s->chunk, s->window)) return FALCON_ERR_UNSUPPORTED;
-  if (workspace_bytes < falcon::chunk_bwd_workspace(s->batch, s->heads, s->seqlen)) return FALCON_ERR_WORKSPACE;
+  if (workspace_bytes < falcon::chunk_bwd_workspace(s->variant, s->batch, s->heads, s->seqlen)) return FALCON_ERR_WORKSPACE;
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.dO = d_o; a.beta = beta; a.g = log_lambda;
   a.S0 = init ? init->S : nullptr;

@@ -1,5 +1,6 @@
 // Backward pass of the chunk-parallel form for Falcon-1 / 1A (scalar NLMS step,
-// one pair per step) and Falcon-2A, d_k = d_v = 64, chunks of 64 steps.
+// one pair per step), Falcon-2 and Falcon-2A (per-value-channel steps), d_k = d_v
+// = 64, chunks of 64 steps.
 //
 // Falcon-2A writes diag(beta_t) v_t x_t^T / (eps_eta + |x_t|^2): it is Falcon-1A
 // with values beta (.) v and a unit gain ([P1] Falcon家族: only the step becomes a
@@ -517,6 +518,86 @@ __device__ void adjoint_tile(float *sA, float *sP, const float *sG, const float 
   }
 }
 
+// The gradients of the rows' features taken through the feature map phi: dq_t
+// from dQh (sO) for t < T, and dk of the key row r carries from dX (sE), plus the
+// carried x_prev's gradient.  1024 threads, one chunk.
+template <typename IT>
+__device__ void through_phi(const BwdArgs &a, int n, int c, size_t row0, int b, int h, const float *sO,
+                            const float *sE) {
+  const int tid = threadIdx.x;
+  constexpr int NP = NTC / 64, EE = 64 / NP;
+  const int r = tid / NP, p = tid % NP;
+  const int t = c * C + r;
+  float v[EE], d[EE];
+  if (t < a.T) {
+    load_e<IT, EE>((const IT *)a.q + (row0 + (size_t)r * a.H) * D + EE * p, v);
+#pragma unroll
+    for (int j = 0; j < EE; ++j) d[j] = sO[r * LD + EE * p + j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < EE; ++j) v[j] = d[j] = 0.f;
+  }
+  float nn = 0.f, dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < EE; ++j) {
+    nn += v[j] * v[j];
+    dot += v[j] * d[j];
+  }
+  nn = sum_parts<NP>(nn);
+  dot = sum_parts<NP>(dot);
+  float inv = 1.f / sqrtf(nn + a.eps_phi);
+  float inv3 = inv * inv * inv;
+  if (t < a.T) {
+    float *dst = a.dq + (row0 + (size_t)r * a.H) * D + EE * p;
+#pragma unroll
+    for (int j = 0; j < EE; j += 4)
+      *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
+                                            d[j + 2] * inv - v[j + 2] * dot * inv3,
+                                            d[j + 3] * inv - v[j + 3] * dot * inv3};
+  }
+  // key of row r: k_{t-1+align}; under the prefix pairing the row at t == T
+  // carries k_{T-1}, whose gradient is 0 (that row's dX is 0).
+  const int kt = t - 1 + a.align;
+  const bool key_row = kt >= 0 && kt < a.T && t <= a.T - a.align;
+#pragma unroll
+  for (int j = 0; j < EE; ++j) d[j] = sE[r * LD + EE * p + j];
+  if (key_row) load_e<IT, EE>((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + EE * p, v);
+  else {
+#pragma unroll
+    for (int j = 0; j < EE; ++j) v[j] = 0.f;
+  }
+  nn = 0.f;
+  dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < EE; ++j) {
+    nn += v[j] * v[j];
+    dot += v[j] * d[j];
+  }
+  nn = sum_parts<NP>(nn);
+  dot = sum_parts<NP>(dot);
+  inv = 1.f / sqrtf(nn + a.eps_phi);
+  inv3 = inv * inv * inv;
+  if (key_row) {
+    float *dst = a.dk + ((size_t)(b * a.T + kt) * a.H + h) * D + EE * p;
+#pragma unroll
+    for (int j = 0; j < EE; j += 4)
+      *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
+                                            d[j + 2] * inv - v[j + 2] * dot * inv3,
+                                            d[j + 3] * inv - v[j + 3] * dot * inv3};
+  }
+  if (t == 0 && a.dxprev0) {  // the carried x_prev is row 0's key (prefix); unread under same-step pairs
+    float *dst = a.dxprev0 + (size_t)n * D + EE * p;
+#pragma unroll
+    for (int j = 0; j < EE; ++j) dst[j] = a.align ? 0.f : d[j];
+  }
+  // Prefix pairing with T a multiple of C: k_{T-1} has no row here; its gradient is 0.
+  if (!a.align && c == a.NC - 1 && a.T % C == 0 && r == 0) {
+    float *dst = a.dk + ((size_t)(b * a.T + a.T - 1) * a.H + h) * D + EE * p;
+#pragma unroll
+    for (int j = 0; j < EE; j += 4) *reinterpret_cast<f4 *>(dst + j) = zero4();
+  }
+}
+
 template <typename IT, bool ADD, bool PC = false>   // PC: Falcon-2A (ADD, per-channel gains)
 __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[ADD ? 4 : MAT], sP[MAT],
@@ -738,80 +819,541 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   st_c(sE, LD, 16 * rt, 16 * ct, lane, dX);
   __syncthreads();
 
-  // Through the feature map: dq_t for t < T; dk of the key that row r carries.
-  {
-    constexpr int NP = NTC / 64, EE = 64 / NP;
-    const int r = tid / NP, p = tid % NP;
-    const int t = c * C + r;
-    float v[EE], d[EE];
-    if (t < a.T) {
-      load_e<IT, EE>((const IT *)a.q + (row0 + (size_t)r * a.H) * D + EE * p, v);
+  through_phi<IT>(a, n, c, row0, b, h, sO, sE);
+}
+
+// ================= Falcon-2: per-value-channel steps =================
+// Falcon-2 gives every value channel (row of S) its own step eta_ch, so each
+// channel has its own chunk matrix M_ch = I + A diag(eta_ch) ([P1] Falcon家族;
+// the per-channel solve the forward pass also runs).  With F = eta (.) E and
+// c_i = e^{L_C - L_i}, the chunk's adjoint is
+//   Y = X G^T, Z = P^T do, dF = diag(c) Y + Z, dE = eta (.) dF,
+//   dR[:, ch] = M_ch^-T dE[:, ch]                 (a per-channel transposed solve)
+//   d eta = E (.) (dF - A^T dR),  dA = -strict-tril(dR F^T),  dP = tril(do F^T),
+//   dv = dR,  G0 = e^{L_C} G + do^T diag(e^L) Qh - dR^T diag(e^{Lm}) X,
+// the same as Falcon-1 with the solves per channel and F in place of diag(eta) E.
+// In the reverse recurrence dR splits into M^-T (eta (.) diag(c) X G^T), which
+// needs G and is solved inside the scan, and M^-T (eta (.) Z), which does not:
+// the prep kernel folds it into Zc = do^T diag(e^L) Qh - (e^{Lm} (.) M^-T(eta (.) Z))^T X.
+
+// Workspace arrays of one chunk (Falcon-2).
+struct WsF2 {
+  float *X, *A, *Zc, *G, *ETA, *RV, *dec;
+};
+__device__ __forceinline__ WsF2 ws_f2(const BwdArgs &a, size_t chunk_id) {
+  const size_t nch = (size_t)a.B * a.H * a.NC;
+  float *base = a.ws;
+  WsF2 p;
+  p.X = base + chunk_id * C * D;
+  p.A = base + nch * C * D + chunk_id * C * C;
+  p.Zc = base + nch * (C * D + C * C) + chunk_id * D * D;
+  p.G = base + nch * (C * D + C * C + D * D) + chunk_id * D * D;
+  p.ETA = base + nch * (C * D + C * C + 2 * D * D) + chunk_id * C * D;
+  p.RV = base + nch * (2 * C * D + C * C + 2 * D * D) + chunk_id * 2 * C;   // c_i, e^{Lm_i}
+  p.dec = base + nch * (2 * C * D + C * C + 2 * D * D + 2 * C) + chunk_id;
+  return p;
+}
+
+constexpr int SP = 17;                 // pitch of a wave's 16x16 scratch blocks
+constexpr int SCR = 2 * 16 * SP;       // floats of one wave's scratch: right-hand side, steps
+
+// The 16x16 diagonal block b of a per-channel solve, 16 channels (one per lane):
+// r (C-layout: rows 16b + 4g + i, channel c) goes through the wave's scratch,
+// lanes 0..15 substitute along the block's rows, and the solution comes back in
+// C-layout.  UPPER: (I + diag(eta) A_bb^T) y = r, else (I + A_bb diag(eta)) y = r.
+template <bool UPPER>
+__device__ __forceinline__ f4 pc_diag(const f4 &r, const f4 &et, const float *sA, int b, float *scr, int lane) {
+  st_c(scr, SP, 0, 0, lane, r);
+  st_c(scr + 16 * SP, SP, 0, 0, lane, et);
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane < 16) {
+    float y[16], e[16];
 #pragma unroll
-      for (int j = 0; j < EE; ++j) d[j] = sO[r * LD + EE * p + j];
+    for (int i = 0; i < 16; ++i) {
+      y[i] = scr[i * SP + lane];
+      e[i] = scr[16 * SP + i * SP + lane];
+    }
+    const float *Ab = sA + 16 * b * LD + 16 * b;
+    if constexpr (UPPER) {
+#pragma unroll
+      for (int i = 15; i >= 0; --i) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = i + 1; j < 16; ++j) s += Ab[j * LD + i] * y[j];
+        y[i] -= e[i] * s;
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < EE; ++j) v[j] = d[j] = 0.f;
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int j = 0; j < i; ++j) y[i] -= Ab[i * LD + j] * e[j] * y[j];
+      }
     }
-    float nn = 0.f, dot = 0.f;
 #pragma unroll
-    for (int j = 0; j < EE; ++j) {
-      nn += v[j] * v[j];
-      dot += v[j] * d[j];
+    for (int i = 0; i < 16; ++i) scr[i * SP + lane] = y[i];
+  }
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  return b_rm(scr, SP, 0, 0, lane);
+}
+
+// Y <- M_ch^-1 Y for the 16 channels of one wave (forward substitution).
+__device__ void solve_lower_pc(f4 (&y)[4], const f4 (&et)[4], const float *sA, float *scr, int lane) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f4 s = zero4();
+#pragma unroll
+    for (int bp = 0; bp < b; ++bp) mma16(s, a_rm(sA, LD, 16 * b, 16 * bp, lane), et[bp] * y[bp]);
+    y[b] = pc_diag<false>(y[b] - s, et[b], sA, b, scr, lane);
+  }
+}
+
+// Y <- M_ch^-T Y for the 16 channels of one wave (backward substitution).
+__device__ void solve_upper_pc(f4 (&y)[4], const f4 (&et)[4], const float *sA, float *scr, int lane) {
+#pragma unroll
+  for (int b = 3; b >= 0; --b) {
+    f4 s = zero4();
+#pragma unroll
+    for (int bp = b + 1; bp < 4; ++bp) mma16(s, a_tr(sA, LD, 16 * b, 16 * bp, lane), y[bp]);
+    y[b] = pc_diag<true>(y[b] - et[b] * s, et[b], sA, b, scr, lane);
+  }
+}
+
+// Steps eta[i][ch] = beta[t][ch] / (eps_eta + |x_i|^2) of the C-layout tile
+// (rows 16rt + 4g + i, channels 16ct + c); zero past the sequence.
+__device__ __forceinline__ f4 eta_tile(const BwdArgs &a, size_t row0, int live, const RowScalars &rs, int rt, int ct,
+                                       int lane) {
+  const int g = lane >> 4, cc = lane & 15;
+  f4 e;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    e[i] = row < live ? a.beta[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] * rs.eta[row] : 0.f;
+  }
+  return e;
+}
+
+// ---- bwd_prep_f2 ------------------------------------------------------------------
+// 256 threads; wave w takes value channels 16w..16w+15 for the solve and key
+// columns 16w..16w+15 for Zc.  Writes X, A, Zc, eta, (c, e^{Lm}) and e^{L_C}.
+template <typename IT>
+__global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[MAT], sP[MAT], sD[MAT];
+  __shared__ __attribute__((aligned(16))) float sScr[4][SCR];
+  __shared__ RowScalars rs;
+  const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
+  const int b = n / a.H, h = n % a.H;
+  const int live = min(C, a.T - c * C);
+  const size_t row0 = (size_t)(b * a.T + c * C) * a.H + h;
+  RowShare<256> dO;
+  dO.load((const IT *)a.dO + row0 * D, (size_t)a.H * D, live);
+  load_rows<IT, 256, true>(a, n, c, sX, sQ, rs);  // rs.eta = 1 / (eps_eta + |x|^2); ends with a barrier
+  const WsF2 ws = ws_f2(a, blockIdx.x);
+  const float LC = rs.L[C - 1];
+
+  f4 qe[4];  // diag(e^L) Qh, key column tile w
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    qe[rt] = b_rm(sQ, LD, 16 * rt, 16 * w, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qe[rt][i] *= __expf(rs.L[16 * rt + 4 * g + i]);
+  }
+  for (int k = w; k < 10; k += 4) {
+    int rt, ct;
+    lower_tile(k, rt, ct);
+    gram_tile<false>(sX, sQ, sA, sP, rs, rt, ct, lane);
+  }
+  __syncthreads();  // A, P complete; sQ is read: it takes do from here on
+  dO.store(sQ);
+  __syncthreads();
+  // B = eta (.) P^T do for value channels 16w.., then M^-T B per channel
+  f4 y[4], et[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f4 z = zero4();
+    for (int kb = rt; kb < 4; ++kb) mma16(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * w, lane));
+    et[rt] = eta_tile(a, row0, live, rs, rt, w, lane);
+    y[rt] = et[rt] * z;
+  }
+  solve_upper_pc(y, et, sA, sScr[w], lane);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f4 d = y[rt];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] *= __expf(rs.Lm[16 * rt + 4 * g + i]);
+    st_c(sD, LD, 16 * rt, 16 * w, lane, d);   // e^{Lm} (.) M^-T (eta (.) Z)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.ETA[(16 * rt + 4 * g + i) * D + 16 * w + cc] = et[rt][i];
+  }
+  __syncthreads();
+  // Zc = do^T diag(e^L) Qh - D^T X: value-channel rows, key-column tile w
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f4 z = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      mma16(z, a_tr(sQ, LD, 16 * rt, 16 * kb, lane), qe[kb]);
+      mma16(z, -a_tr(sD, LD, 16 * rt, 16 * kb, lane), b_rm(sX, LD, 16 * kb, 16 * w, lane));
     }
-    nn = sum_parts<NP>(nn);
-    dot = sum_parts<NP>(dot);
-    float inv = 1.f / sqrtf(nn + a.eps_phi);
-    float inv3 = inv * inv * inv;
-    if (t < a.T) {
-      float *dst = a.dq + (row0 + (size_t)r * a.H) * D + EE * p;
 #pragma unroll
-      for (int j = 0; j < EE; j += 4)
-        *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
-                                              d[j + 2] * inv - v[j + 2] * dot * inv3,
-                                              d[j + 3] * inv - v[j + 3] * dot * inv3};
-    }
-    // key of row r: k_{t-1+align}; under the prefix pairing the row at t == T
-    // carries k_{T-1}, whose gradient is 0 (that row's dX is 0).
-    const int kt = t - 1 + a.align;
-    const bool key_row = kt >= 0 && kt < a.T && t <= a.T - a.align;
+    for (int i = 0; i < 4; ++i) ws.Zc[(16 * rt + 4 * g + i) * D + 16 * w + cc] = z[i];
+  }
+  {
+    const int r = threadIdx.x >> 2, p = threadIdx.x & 3;
 #pragma unroll
-    for (int j = 0; j < EE; ++j) d[j] = sE[r * LD + EE * p + j];
-    if (key_row) load_e<IT, EE>((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + EE * p, v);
-    else {
-#pragma unroll
-      for (int j = 0; j < EE; ++j) v[j] = 0.f;
-    }
-    nn = 0.f;
-    dot = 0.f;
-#pragma unroll
-    for (int j = 0; j < EE; ++j) {
-      nn += v[j] * v[j];
-      dot += v[j] * d[j];
-    }
-    nn = sum_parts<NP>(nn);
-    dot = sum_parts<NP>(dot);
-    inv = 1.f / sqrtf(nn + a.eps_phi);
-    inv3 = inv * inv * inv;
-    if (key_row) {
-      float *dst = a.dk + ((size_t)(b * a.T + kt) * a.H + h) * D + EE * p;
-#pragma unroll
-      for (int j = 0; j < EE; j += 4)
-        *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
-                                              d[j + 2] * inv - v[j + 2] * dot * inv3,
-                                              d[j + 3] * inv - v[j + 3] * dot * inv3};
-    }
-    if (t == 0 && a.dxprev0) {  // the carried x_prev is row 0's key (prefix); unread under same-step pairs
-      float *dst = a.dxprev0 + (size_t)n * D + EE * p;
-#pragma unroll
-      for (int j = 0; j < EE; ++j) dst[j] = a.align ? 0.f : d[j];
-    }
-    // Prefix pairing with T a multiple of C: k_{T-1} has no row here; its gradient is 0.
-    if (!a.align && c == a.NC - 1 && a.T % C == 0 && r == 0) {
-      float *dst = a.dk + ((size_t)(b * a.T + a.T - 1) * a.H + h) * D + EE * p;
-#pragma unroll
-      for (int j = 0; j < EE; j += 4) *reinterpret_cast<f4 *>(dst + j) = zero4();
+    for (int j = 0; j < 16; j += 4) {
+      *reinterpret_cast<f4 *>(ws.X + r * D + 16 * p + j) = *reinterpret_cast<const f4 *>(sX + r * LD + 16 * p + j);
+      *reinterpret_cast<f4 *>(ws.A + r * C + 16 * p + j) = *reinterpret_cast<const f4 *>(sA + r * LD + 16 * p + j);
     }
   }
+  if (threadIdx.x < C) {
+    const int i = threadIdx.x;
+    ws.RV[i] = __expf(LC - rs.L[i]);
+    ws.RV[C + i] = __expf(rs.Lm[i]);
+  }
+  if (threadIdx.x == 0) *ws.dec = __expf(LC);
+}
+
+// ---- bwd_scan_f2 -------------------------------------------------------------------
+// Workgroup (sequence n, value rows 16s..16s+15), chunks in reverse; wave w holds
+// key columns 16w..16w+15 of G.  Per chunk: Y^T = G X^T, B = eta (.) c (.) Y, the
+// per-channel solve dR = M^-T B on wave 0, then G <- e^{L_C} G - (e^{Lm} (.) dR)^T X + Zc.
+__global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[MAT], sA[MAT], sG[16 * LD], sB[C * SP], sE[C * SP];
+  __shared__ __attribute__((aligned(16))) float sScr[SCR];
+  __shared__ float sRV[2 * C];
+  const int n = blockIdx.x >> 2, s = blockIdx.x & 3;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
+  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
+  const size_t tile = (size_t)(16 * s + 4 * g) * D + 16 * w + cc;  // + i * D
+  f4 G = zero4();
+  if (a.dST) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) G[i] = a.dST[(size_t)n * D * D + tile + i * D];
+  }
+  for (int c = a.NC - 1; c >= 0; --c) {
+    const WsF2 ws = ws_f2(a, (size_t)n * a.NC + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws.G[tile + i * D] = G[i];  // gradient at the end of chunk c
+    __syncthreads();  // the previous chunk's readers are done
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<f4 *>(sX + r * LD + 16 * p + 4 * j) = *reinterpret_cast<const f4 *>(ws.X + r * D + 16 * p + 4 * j);
+      *reinterpret_cast<f4 *>(sA + r * LD + 16 * p + 4 * j) = *reinterpret_cast<const f4 *>(ws.A + r * C + 16 * p + 4 * j);
+    }
+    for (int e = tid; e < C * 16; e += 256) sE[(e >> 4) * SP + (e & 15)] = ws.ETA[(e >> 4) * D + 16 * s + (e & 15)];
+    if (tid < 2 * C) sRV[tid] = ws.RV[tid];
+    st_c(sG, LD, 0, 16 * w, lane, G);
+    __syncthreads();
+    {  // (G X^T) tile: channels 16s.., chunk rows 16w..; B = eta (.) c (.) Y into sB [row][channel]
+      f4 y = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma16(y, a_rm(sG, LD, 0, 16 * kb, lane), b_tr(sX, LD, 16 * kb, 16 * w, lane));
+      const int row = 16 * w + cc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = 4 * g + i;
+        sB[row * SP + ch] = sE[row * SP + ch] * sRV[row] * y[i];
+      }
+    }
+    __syncthreads();
+    if (w == 0) {  // dR = M^-T B for the 16 channels; e^{Lm} (.) dR back into sB
+      f4 yy[4], et[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        yy[bb] = b_rm(sB, SP, 16 * bb, 0, lane);
+        et[bb] = b_rm(sE, SP, 16 * bb, 0, lane);
+      }
+      solve_upper_pc(yy, et, sA, sScr, lane);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yy[bb][i] *= sRV[C + 16 * bb + 4 * g + i];
+        st_c(sB, SP, 16 * bb, 0, lane, yy[bb]);
+      }
+    }
+    __syncthreads();
+    f4 u = zero4();  // (e^{Lm} (.) dR)^T X: channels 16s.., key columns 16w..
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mma16(u, a_tr(sB, SP, 0, 16 * kb, lane), b_rm(sX, LD, 16 * kb, 16 * w, lane));
+    f4 Zc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Zc[i] = ws.Zc[tile + i * D];
+    G = *ws.dec * G - u + Zc;
+  }
+  if (a.dS0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a.dS0[(size_t)n * D * D + tile + i * D] = G[i];
+  }
+}
+
+// ---- bwd_chunk_f2 ------------------------------------------------------------------
+// 16 waves, wave w owns tile (rt, ct) = (w / 4, w % 4) of every C x 64 matrix; the
+// per-channel solves run on waves 0..3 (one 16-channel column tile each).
+template <typename IT>
+__global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[MAT], sP[MAT], sE[MAT],
+      sO[MAT];
+  __shared__ __attribute__((aligned(16))) float sScr[4][SCR];
+  __shared__ RowScalars rs;
+  __shared__ float pL[NWC][C], pE[NWC][C], pC[NWC], sCoef[C];
+  const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
+  const int ct = w & 3, rt = w >> 2;
+  const int b = n / a.H, h = n % a.H;
+  const int live = min(C, a.T - c * C);
+  const size_t row0 = (size_t)(b * a.T + c * C) * a.H + h;
+  const WsF2 ws = ws_f2(a, blockIdx.x);
+
+  // Phase 0: do, the incoming state S0, the end-state gradient G, v, the rows.
+  {
+    RowShare<NTC> rO;
+    rO.load((const IT *)a.dO + row0 * D, (size_t)a.H * D, live);
+    const float *S0 = c ? a.chunk_states + ((size_t)n * a.NC + c - 1) * D * D
+                        : (a.S0 ? a.S0 + (size_t)n * D * D : nullptr);
+    const int r = tid >> 4, p = tid & 15;
+    *reinterpret_cast<f4 *>(sS + r * LD + 4 * p) = S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 4 * p) : zero4();
+    *reinterpret_cast<f4 *>(sG + r * LD + 4 * p) = *reinterpret_cast<const f4 *>(ws.G + r * D + 4 * p);
+    rO.store(sO);
+    pL[w][lane] = 0.f;
+    pE[w][lane] = 0.f;
+  }
+  f4 V;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    V[i] = row < live ? (float)((const IT *)a.v)[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] : 0.f;
+  }
+  load_rows<IT, NTC, true>(a, n, c, sX, sQ, rs);  // rs.eta = 1 / (eps_eta + |x|^2); ends with a barrier
+  const f4 ET = eta_tile(a, row0, live, rs, rt, ct, lane);   // this tile's per-channel steps
+  const float LC = rs.L[C - 1];
+  float lc = 0.f;
+  {
+    const int r = tid >> 4, p = tid & 15;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += sG[r * LD + 4 * p + j] * sS[r * LD + 4 * p + j];
+    lc += __expf(LC) * s;  // e^{L_C} <G, S0>
+  }
+
+  // Phase 1: A and P tiles; R = V - diag(e^Lm) X S0^T; dQh from the first read term; Y = X G^T.
+  if (w < 10) {
+    int tr, tc;
+    lower_tile(w, tr, tc);
+    gram_tile<false>(sX, sQ, sA, sP, rs, tr, tc, lane);
+  }
+  f4 E, dQ, Y;
+  {
+    f4 xs = zero4(), dq = zero4(), y = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f4 xa = a_rm(sX, LD, 16 * rt, 16 * kb, lane);
+      mma16(xs, xa, b_tr(sS, LD, 16 * kb, 16 * ct, lane));
+      mma16(y, xa, b_tr(sG, LD, 16 * kb, 16 * ct, lane));
+      mma16(dq, a_rm(sO, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      E[i] = V[i] - __expf(rs.Lm[row]) * xs[i];
+      dQ[i] = __expf(rs.L[row]) * dq[i];
+      const float part = sum16(sQ[row * LD + 16 * ct + cc] * dQ[i]);  // qh_i . dQh_i
+      if (cc == 0) pL[w][row] += part;
+    }
+    Y = y;
+  }
+
+  // Phase 2-3: E[:, ch] = M_ch^-1 R[:, ch] on waves 0..3 (one per column tile).
+  st_c(sE, LD, 16 * rt, 16 * ct, lane, E);  // R
+  __syncthreads();                           // A, P and R are complete
+  if (w < 4) {
+    f4 y4[4], e4[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      y4[bb] = b_rm(sE, LD, 16 * bb, 16 * w, lane);
+      e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
+    }
+    solve_lower_pc(y4, e4, sA, sScr[w], lane);
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) st_c(sE, LD, 16 * bb, 16 * w, lane, y4[bb]);
+  }
+  __syncthreads();
+  E = b_rm(sE, LD, 16 * rt, 16 * ct, lane);
+  const f4 F = ET * E;   // eta (.) E
+
+  // Phase 4: Z = P^T do; dF = c (.) Y + Z; d eta = E (.) dF; dE = eta (.) dF; dX = c (.) F G.
+  f4 dE, dX, deta;
+  {
+    f4 z = zero4();
+    for (int kb = rt; kb < 4; ++kb) mma16(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sO, LD, 16 * kb, 16 * ct, lane));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      const float cf = __expf(LC - rs.L[row]);
+      const float fy = F[i] * Y[i] * cf;   // the c_i term of S_C: into dL_i and dL_C
+      const float part = sum16(fy);
+      if (cc == 0) {
+        pL[w][row] -= part;
+        lc += part;
+      }
+      const float dF = cf * Y[i] + z[i];
+      deta[i] = E[i] * dF;
+      dE[i] = ET[i] * dF;
+    }
+  }
+  __syncthreads();                           // every wave has read E from sE
+  st_c(sE, LD, 16 * rt, 16 * ct, lane, F);   // sE holds F from here on
+  __syncthreads();
+  {
+    f4 u = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mma16(u, a_rm(sE, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * ct, lane));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dX[i] = __expf(LC - rs.L[16 * rt + 4 * g + i]) * u[i];
+  }
+
+  // Phase 5: dR = M_ch^-T dE on waves 0..3 (= dv).
+  __syncthreads();  // every wave is done reading G
+  st_c(sG, LD, 16 * rt, 16 * ct, lane, dE);
+  __syncthreads();
+  if (w < 4) {
+    f4 y4[4], e4[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      y4[bb] = b_rm(sG, LD, 16 * bb, 16 * w, lane);
+      e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
+    }
+    solve_upper_pc(y4, e4, sA, sScr[w], lane);
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) st_c(sG, LD, 16 * bb, 16 * w, lane, y4[bb]);  // sG now holds dR
+  }
+  __syncthreads();
+  const f4 dR = b_rm(sG, LD, 16 * rt, 16 * ct, lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    if (row < live) a.dv[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] = dR[i];
+  }
+
+  // Phase 6: dR S0 (into dX and dL_{i-1}); d eta -= E (.) A^T dR; the C x C adjoints.
+  {
+    f4 s = zero4(), t2 = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mma16(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
+    for (int kb = rt; kb < 4; ++kb) mma16(t2, a_tr(sA, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * ct, lane));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      const float am = __expf(rs.Lm[row]);
+      dX[i] -= am * s[i];
+      const float part = sum16(sX[row * LD + 16 * ct + cc] * s[i]);
+      if (cc == 0 && row > 0) pL[w][row - 1] -= am * part;
+      deta[i] -= E[i] * t2[i];
+    }
+  }
+  __syncthreads();  // every wave has read A (A^T dR): the adjoint tiles overwrite it
+  if (w < 10) {   // dA = -strict-tril(dR F^T), dP = tril(do F^T), with their decays
+    int tr, tc;
+    lower_tile(w, tr, tc);
+    const int tg = lane >> 4, tcc = lane & 15;
+    f4 t = zero4(), u = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f4 fb = b_tr(sE, LD, 16 * kb, 16 * tc, lane);
+      mma16(t, a_rm(sG, LD, 16 * tr, 16 * kb, lane), fb);
+      mma16(u, a_rm(sO, LD, 16 * tr, 16 * kb, lane), fb);
+    }
+    const int col = 16 * tc + tcc;
+    float colL = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * tr + 4 * tg + i;
+      float rowL = 0.f, rowLm = 0.f;
+      const float Aij = sA[row * LD + col];
+      const float dA = col < row ? -t[i] : 0.f;
+      const float H = dA * Aij;
+      rowLm += H;
+      colL -= H;
+      sA[row * LD + col] = col < row ? dA * __expf(rs.Lm[row] - rs.L[col]) : 0.f;
+      const float dP = col <= row ? u[i] : 0.f;
+      const float HP = dP * sP[row * LD + col];
+      rowL += HP;
+      colL -= HP;
+      sP[row * LD + col] = col <= row ? dP * __expf(rs.L[row] - rs.L[col]) : 0.f;
+      rowL = sum16(rowL);
+      rowLm = sum16(rowLm);
+      if (tcc == 0) {
+        pL[w][row] += rowL;
+        if (row > 0) pL[w][row - 1] += rowLm;
+      }
+    }
+    colL = sum4g(colL);
+    if (tg == 0) pL[w][col] += colL;
+  }
+  {  // d beta = d eta / (eps + |x|^2); sum over this tile's channels of d eta (.) eta, for |x|^2
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      if (row < live) a.dbeta[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] = deta[i] * rs.eta[row];
+      const float part = sum16(deta[i] * ET[i]);
+      if (cc == 0) pE[w][row] += part;
+    }
+  }
+  __syncthreads();
+
+  // Phase 7: dQh += dPD X; dX += dPD^T Qh + dAG X + dAG^T X.
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const f4 xb = b_rm(sX, LD, 16 * kb, 16 * ct, lane);
+    if (kb <= rt) {
+      mma16(dQ, a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
+      mma16(dX, a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
+    }
+    if (kb >= rt) {
+      mma16(dX, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * ct, lane));
+      mma16(dX, a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
+    }
+  }
+  lc = sum64(lc);
+  if (lane == 0) pC[w] = lc;
+  __syncthreads();
+
+  // Phase 8: per-row totals; dL -> d(log-decay) by a reverse sum; the |x|^2 term.
+  if (w == 0) {
+    const int i = lane;
+    float de = 0.f, dl = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWC; ++v) {
+      de += pE[v][i];
+      dl += pL[v][i];
+    }
+    if (i == C - 1) {
+#pragma unroll
+      for (int v = 0; v < NWC; ++v) dl += pC[v];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_down(dl, o);
+      if (i + o < 64) dl += y;
+    }
+    if (i < live) {
+      const size_t gi = row0 + (size_t)i * a.H;
+      a.dg[gi] = a.g[gi] > a.log_eps_gamma ? dl : 0.f;
+    }
+    sCoef[i] = -2.f * de * rs.eta[i];   // -2 sum_ch d eta eta / (eps + |x|^2)
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    dX[i] += sCoef[row] * sX[row * LD + 16 * ct + cc];
+  }
+  st_c(sO, LD, 16 * rt, 16 * ct, lane, dQ);
+  st_c(sE, LD, 16 * rt, 16 * ct, lane, dX);
+  __syncthreads();
+  through_phi<IT>(a, n, c, row0, b, h, sO, sE);
 }
 
 template <typename IT, bool ADD, bool PC = false>
@@ -827,18 +1369,34 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename IT>
+hipError_t launch_bwd_f2(const BwdArgs &a, hipStream_t st) {
+  const unsigned nch = (unsigned)a.B * a.H * a.NC;
+  hipLaunchKernelGGL((bwd_prep_f2<IT>), dim3(nch), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scan_f2, dim3((unsigned)a.B * a.H * 4), dim3(256), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_chunk_f2<IT>), dim3(nch), dim3(NTC), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool chunk_bwd_supported(int variant, int dk, int dv, int chunk, int window) {
-  return (variant == 1 || variant == 2 || variant == 4) && dk == D && dv == D && chunk == C && window == 1;
+  return variant >= 1 && variant <= 4 && dk == D && dv == D && chunk == C && window == 1;
 }
 
-size_t chunk_bwd_workspace(int B, int H, int T) {
+size_t chunk_bwd_workspace(int variant, int B, int H, int T) {
   const size_t nch = (size_t)B * H * ((T + C - 1) / C);
+  if (variant == 3)   // Falcon-2: keys, A, Zc, G, eta, (c, e^{Lm}) and the decay per chunk
+    return nch * (2 * C * D + C * C + 2 * D * D + 2 * C + 1) * sizeof(float);
   return (4 * nch * C * D + nch) * sizeof(float);
 }
 
 hipError_t launch_chunk_bwd(int variant, bool bf16, const BwdArgs &a, hipStream_t st) {
+  if (variant == 3) return bf16 ? launch_bwd_f2<__bf16>(a, st) : launch_bwd_f2<float>(a, st);
   if (variant == 4) return bf16 ? launch_bwd_t<__bf16, true, true>(a, st) : launch_bwd_t<float, true, true>(a, st);
   const bool add = variant == 2;
   if (bf16) return add ? launch_bwd_t<__bf16, true>(a, st) : launch_bwd_t<__bf16, false>(a, st);

@@ -75,7 +75,7 @@ hipError_t launch_tail(int variant, bool bf16, int dk, int dv, const FwdArgs &a,
 hipError_t launch_step(int variant, bool bf16, int dk, int dv, const StepArgs &a, hipStream_t stream);
 
 bool chunk_bwd_supported(int variant, int dk, int dv, int chunk, int window);
-size_t chunk_bwd_workspace(int B, int H, int T);
+size_t chunk_bwd_workspace(int variant, int B, int H, int T);
 hipError_t launch_chunk_bwd(int variant, bool bf16, const BwdArgs &a, hipStream_t stream);
 
 hipError_t launch_seg_boundary(bool bf16, const SegArgs &a, hipStream_t stream);

@@ -60,7 +60,7 @@ def small(T, dtype, B=2, H=3, gates="floor5"):
     return W.WORKLOADS["layer130m"].replace(name=f"bwd_T{T}", batch=B, heads=H, seqlen=T, dtype=dtype, gates=gates)
 
 
-BWD_VARIANTS = ("F1", "F1A", "F2A")
+BWD_VARIANTS = ("F1", "F1A", "F2", "F2A")
 CASES = [(v, dt, al) for v in BWD_VARIANTS for dt in ("fp32", "bf16") for al in ("prefix", "same")]
 
 
