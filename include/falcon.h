@@ -275,7 +275,9 @@ int falcon_recurrent_step(const falcon_shape_t *shape,
 
 /* Bytes of device workspace falcon_chunk_bwd needs for this shape; 0 when the
  * backward pass is not built for it (or the shape is invalid).  Built: F1, F1A,
- * F2 and F2A, d_k = d_v = 64, chunk 64, fp32 or bf16 inputs, either pairing.
+ * F2 and F2A, d_k = d_v = 64, chunk 16, 32 or 64 (the chunk of the forward call
+ * that wrote the per-chunk states; the kernels work in 64-step chunks and read
+ * the states at 64-step boundaries), fp32 or bf16 inputs, either pairing.
  * The workspace holds, per chunk, the keys, the scaled WY factor, the state
  * gradient the chunk's outputs inject and the state gradient at the chunk's
  * end (4 x 16 KiB + 4 bytes); for F2, whose solves are per value channel, the
@@ -293,8 +295,8 @@ size_t falcon_chunk_bwd_workspace(const falcon_shape_t *shape);
  * exp(g) <= eps_gamma (there the decay does not depend on g).
  *   init         as given to the forward pass (NULL = fresh sequences); S and
  *                x_prev are read.
- *   chunk_states [B, H, ceil(T/64), 64, 64] fp32: the per-chunk states the
- *                forward pass wrote for these inputs (chunk 64).
+ *   chunk_states [B, H, ceil(T/C), 64, 64] fp32: the per-chunk states the
+ *                forward pass wrote for these inputs at shape->chunk = C.
  *   d_o          [B, T, H, 64] in dtype.
  *   d_final_S    [B, H, 64, 64] fp32, or NULL for a zero gradient on S_T.
  *   dq, dk, dv   [B, T, H, 64] fp32, written whole (under the prefix pairing

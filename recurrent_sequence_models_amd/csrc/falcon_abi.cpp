@@ -363,7 +363,9 @@ int falcon_chunk_bwd(const falcon_shape_t *s, const void *q, const void *k, cons
   a.dxprev0 = d_init ? d_init->x_prev : nullptr;
   a.ws = static_cast<float *>(workspace);
   a.B = s->batch; a.T = s->seqlen; a.H = s->heads;
-  a.NC = (s->seqlen + s->chunk - 1) / s->chunk;
+  a.NC = (s->seqlen + 63) / 64;                        // the kernels' chunks of 64 steps
+  a.cs_nc = (s->seqlen + s->chunk - 1) / s->chunk;      // the forward's per-chunk states
+  a.cs_step = s->chunk;
   a.align = s->align;
   a.log_eps_gamma = std::log(s->eps_gamma);
   a.eps_phi = s->eps_phi;

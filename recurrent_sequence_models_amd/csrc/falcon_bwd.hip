@@ -617,7 +617,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   {
     RowShare<NTC> rO;
     rO.load((const IT *)a.dO + row0 * D, (size_t)a.H * D, live);
-    const float *S0 = c ? a.chunk_states + ((size_t)n * a.NC + c - 1) * D * D
+    const float *S0 = c ? a.chunk_states + ((size_t)n * a.cs_nc + (size_t)c * (C / a.cs_step) - 1) * D * D
                         : (a.S0 ? a.S0 + (size_t)n * D * D : nullptr);
     const int r = tid >> 4, p = tid & 15;
     *reinterpret_cast<f4 *>(sS + r * LD + 4 * p) = S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 4 * p) : zero4();
@@ -1111,7 +1111,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   {
     RowShare<NTC> rO;
     rO.load((const IT *)a.dO + row0 * D, (size_t)a.H * D, live);
-    const float *S0 = c ? a.chunk_states + ((size_t)n * a.NC + c - 1) * D * D
+    const float *S0 = c ? a.chunk_states + ((size_t)n * a.cs_nc + (size_t)c * (C / a.cs_step) - 1) * D * D
                         : (a.S0 ? a.S0 + (size_t)n * D * D : nullptr);
     const int r = tid >> 4, p = tid & 15;
     *reinterpret_cast<f4 *>(sS + r * LD + 4 * p) = S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 4 * p) : zero4();
@@ -1384,8 +1384,12 @@ hipError_t launch_bwd_f2(const BwdArgs &a, hipStream_t st) {
 
 }  // namespace
 
+// The kernels work in chunks of 64 steps whatever the forward's chunk: the
+// gradient does not depend on the chunking, and a forward at chunk 16 or 32
+// wrote the state at every 64-step boundary among its per-chunk states.
 bool chunk_bwd_supported(int variant, int dk, int dv, int chunk, int window) {
-  return variant >= 1 && variant <= 4 && dk == D && dv == D && chunk == C && window == 1;
+  return variant >= 1 && variant <= 4 && dk == D && dv == D && (chunk == 16 || chunk == 32 || chunk == C) &&
+         window == 1;
 }
 
 size_t chunk_bwd_workspace(int variant, int B, int H, int T) {

@@ -43,13 +43,16 @@ struct BwdArgs {
   const void *q, *k, *v, *dO;    // [B,T,H,64] in the input dtype
   const float *beta, *g;         // [B,T,H]
   const float *S0, *xprev0;      // incoming S [B,H,64,64] and x_prev [B,H,64], or null (zeros)
-  const float *chunk_states;     // [B,H,NC,64,64]: S at the end of every chunk (the forward's)
+  const float *chunk_states;     // [B,H,cs_nc,64,64]: S at the end of every forward chunk
   const float *dST;              // [B,H,64,64] gradient w.r.t. S_T, or null (zero)
   float *dq, *dk, *dv;           // [B,T,H,64] fp32
   float *dbeta, *dg;             // [B,T,H] fp32
   float *dS0, *dxprev0;          // [B,H,64,64], [B,H,64] or null
-  float *ws;                     // chunk_bwd_workspace(B, H, T) bytes
-  int B, T, H, NC;
+  float *ws;                     // chunk_bwd_workspace(variant, B, H, T) bytes
+  int B, T, H, NC;               // NC: chunks of 64 steps
+  int cs_nc, cs_step;            // chunk_states holds cs_nc states per sequence, one every cs_step
+                                 // steps (the forward's chunk: 16, 32 or 64); the kernels read
+                                 // those at 64-step boundaries
   int align;
   float log_eps_gamma, eps_phi, eps_eta;
 };

@@ -242,8 +242,10 @@ def test_bwd_workspace_size():
     # Falcon-2: keys, A, Zc, G and the per-channel steps (5 x 64 x 64), (c, e^{Lm}) and the decay
     assert bwd_workspace(seqlen=100, variant="F2") == 2 * 3 * 2 * (5 * 64 * 64 + 2 * 64 + 1) * 4
     for kw in (dict(variant="F3", window=2), dict(variant="F3A"),
-               dict(dk=32, dv=32), dict(dk=128, dv=128), dict(chunk=32), dict(batch=0)):
+               dict(dk=32, dv=32), dict(dk=128, dv=128), dict(batch=0)):
         assert bwd_workspace(**kw) == 0, kw
+    # the kernels work in 64-step chunks whatever the forward's chunk
+    assert bwd_workspace(seqlen=100, chunk=32) == bwd_workspace(seqlen=100, chunk=16) == 2 * 3 * 2 * per_chunk
 
 
 @cpu_only
@@ -260,7 +262,7 @@ def test_bwd_rejects_on_host():
         assert call_bwd(ok, **{name: ctypes.c_void_p(0x10002)}) == F.ERR_INVALID_ARG, name
     assert call_bwd(ok, d_init=F.State(FAKE.value, None, None, None)) == F.ERR_INVALID_ARG
     assert call_bwd(ok, init=F.State(None, FAKE.value, None, None)) == F.ERR_INVALID_ARG
-    for kw in (dict(variant="F3", window=2), dict(dk=32, dv=32), dict(chunk=32),
+    for kw in (dict(variant="F3", window=2), dict(dk=32, dv=32),
                dict(dk=128, dv=128)):
         assert call_bwd(good_shape(**kw)) == F.ERR_UNSUPPORTED, kw
     assert call_bwd(ok, wsb=bwd_workspace() - 1) == F.ERR_WORKSPACE

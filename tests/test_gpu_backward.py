@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 GRADS = ("dq", "dk", "dv", "dbeta", "dg", "dS0", "dx_prev0")
 
 
-def run_bwd(variant, w, seed, init=True, final_grad=True, align="prefix"):
+def run_bwd(variant, w, seed, init=True, final_grad=True, align="prefix", chunk=64):
     import torch
     from recurrent_sequence_models_amd import chunk_bwd, chunk_fwd
     inp = W.make_inputs(w, variant, seed=seed)
@@ -32,21 +32,21 @@ def run_bwd(variant, w, seed, init=True, final_grad=True, align="prefix"):
     sd = state_to_dev(st) if st is not None else None
     # The library's fp32 forward at d 64 pairs same-step keys at chunk 32 only: take
     # the states at every second boundary of the chunk-32 forward (the chunk-64 ends).
-    fc = 32 if (w.dtype == "fp32" and align == "same") else 64
+    fc = 32 if (w.dtype == "fp32" and align == "same" and chunk == 64) else chunk
     _, _, cs = chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=fc, init=sd,
                          final=False, chunk_states=True, align=align)
-    if fc == 32:
+    if fc != chunk:
         n32 = cs.shape[2]
         idx = [min(2 * c + 1, n32 - 1) for c in range(-(-w.seqlen // 64))]
         cs = cs[:, :, idx].contiguous()
     g = chunk_bwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], do, cs, init=sd, dS_T=dST,
-                  align=align)
+                  align=align, chunk=chunk)
     torch.cuda.synchronize()
     return {n: to_np(g[n]) for n in GRADS}, inp, st, cot
 
 
-def check_bwd(variant, w, seed, init=True, final_grad=True, align="prefix"):
-    got, inp, st, cot = run_bwd(variant, w, seed, init, final_grad, align)
+def check_bwd(variant, w, seed, init=True, final_grad=True, align="prefix", chunk=64):
+    got, inp, st, cot = run_bwd(variant, w, seed, init, final_grad, align, chunk)
     ref = oracle.recurrent_backward(variant, **inp, do=cot["do"], state=st, dS_T=cot["dS_T"], align=align)
     errs = {n: rel_l2(got[n], ref[n]) for n in GRADS}
     print(variant, w.name, w.dtype, w.seqlen, align, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
@@ -120,3 +120,12 @@ def test_backward_full_size_sampled(variant):
             e = rel_l2(gn, ref[n])
             print(variant, (b, h), n, f"{e:.2e}", flush=True)
             assert e <= TOL["bf16"], (b, h, n, e)
+
+
+@pytest.mark.parametrize("variant", list(BWD_VARIANTS))
+@pytest.mark.parametrize("chunk,dtype,align", [(16, "fp32", "prefix"), (32, "bf16", "prefix"), (32, "fp32", "same"),
+                                               (16, "bf16", "same")])
+def test_backward_from_smaller_chunks(variant, chunk, dtype, align):
+    """Per-chunk states written by a forward at chunk 16 or 32: the backward reads
+    the ones at 64-step boundaries (T = 150: a ragged last chunk)."""
+    check_bwd(variant, small(150, dtype), 51 + chunk, init=True, final_grad=True, align=align, chunk=chunk)
