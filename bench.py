@@ -143,11 +143,13 @@ MFMA_FP32_PEAK_TFS = 157.3    # MI355X dense fp32 MFMA
 def bwd_flops(w, variant):
     """Algorithmic flops of one backward call, per chunk of C steps: the chunked
     products of the adjoint (a triangular C x C product counts half).  With
-    u = 2 C d^2 (C = d): F1 = 15 u (prep 3, scan 2, per-chunk adjoint 10);
-    F1A = 6.5 u (prep 1, adjoint 5.5)."""
+    u = 2 C d^2 (C = d): F1 and F2 = 15 u (prep 3, scan 2, per-chunk adjoint 10);
+    F1A and F2A = 6.5 u (prep 1, adjoint 5.5)."""
     C, d = w.chunk, w.dk
     u = 2 * C * d * d
-    per_chunk = {"F1": 15 * u, "F1A": 6.5 * u, "F2A": 6.5 * u}[variant]   # F2A: F1A on beta (.) v
+    # F2: the products of F1 with F = eta (.) E in place of diag(eta) E (its per-channel
+    # diagonal-block substitutions are not counted); F2A: F1A on beta (.) v
+    per_chunk = {"F1": 15 * u, "F1A": 6.5 * u, "F2": 15 * u, "F2A": 6.5 * u}[variant]
     return w.batch * w.heads * (-(-w.seqlen // C)) * per_chunk
 
 
@@ -456,7 +458,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
-    roof["traffic"] = measured_traffic(f"{path} {variant} {w.name}")
+    roof["traffic"] = measured_traffic(f"{path} {variant} {w.name}" + (f" w{window}" if window > 1 else ""))
     roof["kernel"] = ("seg_boundary + 3 x (chunk_prep + chunk_scan) + seg_combine" if path.startswith("segmented") else
                       "chunk_prep + chunk_scan" if path == "split" else
                       "chunk_scan (one-pass)" if (w.dtype == "bf16" and w.dk <= 64 and w.chunk <= 64) else

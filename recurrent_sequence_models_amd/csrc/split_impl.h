@@ -725,13 +725,16 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
   // masks or carried features.
   auto interior = [&](int c) { return c * CS >= BW - a.align && (c + 1) * CS <= T; };
   const long long rstride = (long long)H * D;   // elements between consecutive tokens
-  // Interior systems load through buffer resources based at this sequence's rows,
-  // with lane-constant byte offsets and the system's offset in an SGPR, so a
-  // load needs no per-lane address arithmetic.  The range check of a buffer load
-  // sees the lane offset alone, which must therefore be >= 0: the key and value
-  // resources start BW - 1 rows early, the oldest pair a virtual row can name.
-  // Used while every offset of the sequence fits 31 bits.
-  const bool bufok = (long long)(T + BW + 1) * rstride * S::SZ < 0x7fffffffLL;
+  // One-pass form: interior systems load through buffer resources based at this
+  // sequence's rows, with lane-constant byte offsets and the system's offset in an
+  // SGPR, so a load needs no per-lane address arithmetic (-7 % VALU instructions,
+  // -1 to -2 % time at the 130M-layer shape).  The two-kernel scan keeps plain
+  // global loads: buffer loads measured 5-20 % slower there (at d = 128 most).
+  // The range check of a buffer load sees the lane offset alone, which must
+  // therefore be >= 0: the key and value resources start BW - 1 rows early, the
+  // oldest pair a virtual row can name.  Used while every offset of the sequence
+  // fits 31 bits.
+  const bool bufok = ONE && (long long)(T + BW + 1) * rstride * S::SZ < 0x7fffffffLL;
   const long long tokv = tok0 - (BW - 1);         // value row of the oldest pair of system 0
   const long long tokb = tokv - 1 + a.align;      // its key row
   const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
@@ -759,7 +762,7 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
   const int vofs_g = min(ctid, CS - 1) * H * 4;
   auto prefetch = [&](int c, Regs &R) __attribute__((always_inline)) {    // global -> registers, system c (rows clamped in bounds)
     const int c0 = c * CS;
-    if (bufok && interior(c)) {
+    if (ONE && bufok && interior(c)) {
       const int so = (int)(c0 * rstride * S::SZ);   // the system's first row
 #pragma unroll
       for (int ps = 0; ps < Z::NPV; ++ps)
