@@ -295,18 +295,29 @@ DECODE_SOURCES = ("falcon_step.hip", "falcon_kernels.h", "mfma_frag.h")
 
 def measured_traffic(key, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed counter record, or None when the
-    kernel sources changed since the counters were taken."""
-    import hashlib
+    kernel code changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         rec = json.load(open(path))[key]
     except (OSError, KeyError, ValueError):
         return None
+    return round(rec["bytes_per_launch"]) if code_digest(sources) == rec["source_sha256"] else None
+
+
+def code_digest(sources):
+    """sha256 over the kernel sources with comments and blank lines removed, so
+    that a comment edit keeps the counter record while any code change drops it."""
+    import hashlib
+    import re
     h = hashlib.sha256()
     for f in sources:
-        with open(os.path.join(ROOT, "recurrent_sequence_models_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return round(rec["bytes_per_launch"]) if h.hexdigest() == rec["source_sha256"] else None
+        with open(os.path.join(ROOT, "recurrent_sequence_models_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
+    return h.hexdigest()
 
 
 def cpu_baseline(w, variant, window=1, budget_s=20.0):

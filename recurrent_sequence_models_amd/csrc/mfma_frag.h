@@ -19,11 +19,10 @@
 // assignment of actual k to slots only has to be the same for A and B, which
 // it is by construction.
 //
-// All bf16 products use the one 16x16x32 opcode.  On gfx950 a 16x16x16 bf16
-// MFMA that accumulates into the result of an immediately preceding 16x16x32
-// bf16 MFMA read a stale accumulator (measured: wrong sums with the wait
-// states the compiler inserts), while same-opcode accumulation chains are
-// exact.  A padded 16x16x32 issues at the same rate as 16x16x16.
+// All bf16 products use the one 16x16x32 opcode, so every accumulation chain
+// is a same-opcode chain.  A 16x16x16 bf16 MFMA accumulating onto the result
+// of a directly preceding 16x16x32 one gave wrong output rows in the parity
+// tests of these kernels; with the single opcode they pass.
 #pragma once
 #include <hip/hip_runtime.h>
 
