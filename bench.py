@@ -260,25 +260,36 @@ def bench_backward(args):
     flops = bwd_flops(w, variant)
     nbytes = bwd_bytes(w, variant)
     tfs = flops / avg_s / 1e12
+    gbs = nbytes / avg_s / 1e9
+    # bf16 inputs run the products on bf16 MFMA, fp32 inputs on fp32 MFMA; the
+    # roofline is whichever of that MFMA peak and HBM bounds the call
+    bf = w.dtype == "bf16"
+    mpeak = MFMA_BF16_PEAK_TFS if bf else MFMA_FP32_PEAK_TFS
+    if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (mpeak * 1e12):
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": mpeak, "unit": "TFLOP/s",
+                "frac": round(tfs / mpeak, 4)}
     line = {
         "metric": f"tokens/sec, Falcon-{variant[1:]} chunked backward (H={w.heads},d={w.dk},T={w.seqlen}) "
-                  "+ % fp32 MFMA roofline",
+                  "+ % MFMA/HBM roofline",
         "value": round(w.batch * w.seqlen / (wall / K), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall / K * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "bf16" if bf else "f32", "data": "synthetic",
         "config": {"workload": f"Falcon-{variant[1:]} chunked backward, {w.name}: B{w.batch} H{w.heads} "
                                f"T{w.seqlen} d{w.dk} chunk {w.chunk}, {w.dtype} q/k/v/do, fp32 gradients",
                    "variant": variant, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
                    "head_dim": w.dk, "chunk": w.chunk},
-        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_FP32_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": round(tfs / MFMA_FP32_PEAK_TFS, 4), "traffic": None,
+        "roofline": {**roof, "traffic": None,
                      "kernel": "bwd_prep + bwd_scan + bwd_chunk",
                      "kernel_us": {"mean": round(avg_s * 1e6, 2), "p10": round(kern_ms[K // 10] * 1e3, 2),
                                    "p50": round(kern_ms[K // 2] * 1e3, 2),
                                    "p90": round(kern_ms[(9 * K) // 10] * 1e3, 2)},
                      "alg_flops": flops, "alg_bytes": nbytes,
-                     "hbm_frac": round(nbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "mfma_frac": round(tfs / mpeak, 4), "mfma_peak": mpeak,
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                      "workspace_bytes": ws_bytes},
     }
     if not args.no_cpu_baseline:

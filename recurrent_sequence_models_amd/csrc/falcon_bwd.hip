@@ -25,7 +25,10 @@
 //   W = M^-1 diag(e^{Lm}) X   (F1A: W = 0),
 // a reverse recurrence of the same shape as the forward state recurrence.
 //
-// Three launches, all fp32 MFMA (v_mfma_f32_16x16x4f32, mfma_frag.h layouts):
+// Three launches (mfma_frag.h fragment layouts).  The per-chunk kernels run their
+// products on bf16 MFMA with fp32 accumulation for bf16 inputs (every operand is
+// rounded to bf16 once, as in the forward pass) and on fp32 MFMA for fp32 inputs;
+// the two reverse-time scans carry G through fp32 MFMA for both:
 //   bwd_prep   one workgroup per chunk: X, Wb = diag(b) W and
 //              Z = do^T (diag(e^L) Qh - P diag(eta) W) into the workspace.
 //   bwd_scan   one workgroup per 16 value channels of a sequence (rows of G are
@@ -79,6 +82,15 @@ __device__ __forceinline__ void st_c(float *m, int ld, int r0, int c0, int lane,
   p[ld] = v[1];
   p[2 * ld] = v[2];
   p[3 * ld] = v[3];
+}
+
+// One 16x16x16 product of fp32 fragments, d += a b: four fp32 MFMAs, or (BF, for
+// bf16 inputs) both operands rounded to bf16 on one bf16 MFMA with fp32
+// accumulation.  The reverse-time scans stay on fp32 MFMA.
+template <bool BF>
+__device__ __forceinline__ void mmx(f4 &d, const f4 &a, const f4 &b) {
+  if constexpr (BF) mma16(d, to_op(a, __bf16()), to_op(b, __bf16()));
+  else mma16(d, a, b);
 }
 
 // Sum over the 16 lanes that share a row of a C-layout tile.
@@ -179,7 +191,7 @@ __device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, 
 
 // One 16x16 tile (rt, ct <= rt) of A (skipped for F1A) and P into LDS, with
 // their masks (strict / causal) and decays.
-template <bool ADD>
+template <bool ADD, bool BF>
 __device__ void gram_tile(const float *sX, const float *sQ, float *sA, float *sP, const RowScalars &rs, int rt,
                           int ct, int lane) {
   const int g = lane >> 4, cc = lane & 15;
@@ -187,8 +199,8 @@ __device__ void gram_tile(const float *sX, const float *sQ, float *sA, float *sP
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const f4 xb = b_tr(sX, LD, 16 * kb, 16 * ct, lane);
-    if (!ADD) mma16(pa, a_rm(sX, LD, 16 * rt, 16 * kb, lane), xb);
-    mma16(pp, a_rm(sQ, LD, 16 * rt, 16 * kb, lane), xb);
+    if (!ADD) mmx<BF>(pa, a_rm(sX, LD, 16 * rt, 16 * kb, lane), xb);
+    mmx<BF>(pp, a_rm(sQ, LD, 16 * rt, 16 * kb, lane), xb);
   }
   const int col = 16 * ct + cc;
 #pragma unroll
@@ -226,6 +238,7 @@ __device__ void diag_inverse(const float *sA, float *sT, const RowScalars &rs, i
 }
 
 // Y <- M^-1 Y for one 16-column tile held by a wave (blocked forward substitution).
+template <bool BF>
 __device__ void solve_lower(f4 (&y)[4], const float *sA, const float *sT, const RowScalars &rs, int lane) {
   const int g = lane >> 4;
 #pragma unroll
@@ -236,15 +249,16 @@ __device__ void solve_lower(f4 (&y)[4], const float *sA, const float *sT, const 
       f4 af = a_rm(sA, LD, 16 * b, 16 * bp, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) af[i] *= rs.eta[16 * bp + 4 * g + i];
-      mma16(s, af, y[bp]);
+      mmx<BF>(s, af, y[bp]);
     }
     const f4 r = y[b] - s;
     y[b] = zero4();
-    mma16(y[b], a_rm(sT + b * 16 * TL, TL, 0, 0, lane), r);
+    mmx<BF>(y[b], a_rm(sT + b * 16 * TL, TL, 0, 0, lane), r);
   }
 }
 
 // Y <- M^-T Y (blocked backward substitution).
+template <bool BF>
 __device__ void solve_upper(f4 (&y)[4], const float *sA, const float *sT, const RowScalars &rs, int lane) {
   const int cc = lane & 15;
 #pragma unroll
@@ -254,11 +268,11 @@ __device__ void solve_upper(f4 (&y)[4], const float *sA, const float *sT, const 
     for (int bp = b + 1; bp < 4; ++bp) {
       f4 af = a_tr(sA, LD, 16 * b, 16 * bp, lane);
       af *= rs.eta[16 * b + cc];
-      mma16(s, af, y[bp]);
+      mmx<BF>(s, af, y[bp]);
     }
     const f4 r = y[b] - s;
     y[b] = zero4();
-    mma16(y[b], a_tr(sT + b * 16 * TL, TL, 0, 0, lane), r);
+    mmx<BF>(y[b], a_tr(sT + b * 16 * TL, TL, 0, 0, lane), r);
   }
 }
 
@@ -306,6 +320,7 @@ __device__ __forceinline__ WsPtr ws_of(const BwdArgs &a, size_t chunk_id) {
 // two workgroups share a compute unit.
 template <typename IT, bool ADD>
 __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
+  constexpr bool BF = std::is_same_v<IT, __bf16>;   // bf16 inputs: products on bf16 MFMA
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[ADD ? 4 : MAT], sP[ADD ? 4 : MAT];
   __shared__ __attribute__((aligned(16))) float sT[ADD ? 4 : 4 * 16 * TL];
   __shared__ RowScalars rs;
@@ -330,7 +345,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
     for (int k = w; k < 10; k += 4) {
       int rt, ct;
       lower_tile(k, rt, ct);
-      gram_tile<false>(sX, sQ, sA, sP, rs, rt, ct, lane);
+      gram_tile<false, BF>(sX, sQ, sA, sP, rs, rt, ct, lane);
     }
   }
   __syncthreads();  // sQ is read: it takes do from here on
@@ -345,7 +360,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) W[rt][i] *= __expf(rs.Lm[16 * rt + 4 * g + i]);
     }
-    solve_lower(W, sA, sT, rs, lane);
+    solve_lower<BF>(W, sA, sT, rs, lane);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       f4 s = zero4();
@@ -354,7 +369,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
         f4 af = a_rm(sP, LD, 16 * rt, 16 * kb, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i) af[i] *= rs.eta[16 * kb + 4 * g + i];
-        mma16(s, af, W[kb]);
+        mmx<BF>(s, af, W[kb]);
       }
       qe[rt] -= s;
 #pragma unroll
@@ -371,7 +386,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
   for (int rt = 0; rt < 4; ++rt) {
     f4 z = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma16(z, a_tr(sQ, LD, 16 * rt, 16 * kb, lane), qe[kb]);
+    for (int kb = 0; kb < 4; ++kb) mmx<BF>(z, a_tr(sQ, LD, 16 * rt, 16 * kb, lane), qe[kb]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ws.Z[(16 * rt + 4 * g + i) * D + 16 * w + cc] = z[i];
   }
@@ -470,7 +485,7 @@ constexpr int NWC = NTC / 64;
 // Adjoint of one lower tile (rt, ct) of A and P: from t = dR E^T and u = do E^T,
 // the tile's contributions to dL and d eta, and dAG = dA o Gamma, dPD = dP o D in
 // place of A and P.
-template <bool ADD>
+template <bool ADD, bool BF>
 __device__ void adjoint_tile(float *sA, float *sP, const float *sG, const float *sO, const float *sE,
                              const RowScalars &rs, float *pLw, float *pEw, int rt, int ct, int lane) {
   const int g = lane >> 4, cc = lane & 15;
@@ -478,8 +493,8 @@ __device__ void adjoint_tile(float *sA, float *sP, const float *sG, const float 
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const f4 eb = b_tr(sE, LD, 16 * kb, 16 * ct, lane);
-    if (!ADD) mma16(t, a_rm(sG, LD, 16 * rt, 16 * kb, lane), eb);
-    mma16(u, a_rm(sO, LD, 16 * rt, 16 * kb, lane), eb);
+    if (!ADD) mmx<BF>(t, a_rm(sG, LD, 16 * rt, 16 * kb, lane), eb);
+    mmx<BF>(u, a_rm(sO, LD, 16 * rt, 16 * kb, lane), eb);
   }
   const int col = 16 * ct + cc;
   const float etac = rs.eta[col];
@@ -600,6 +615,7 @@ __device__ void through_phi(const BwdArgs &a, int n, int c, size_t row0, int b, 
 
 template <typename IT, bool ADD, bool PC = false>   // PC: Falcon-2A (ADD, per-channel gains)
 __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
+  constexpr bool BF = std::is_same_v<IT, __bf16>;   // bf16 inputs: products on bf16 MFMA
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[ADD ? 4 : MAT], sP[MAT],
       sE[MAT], sO[MAT];
   __shared__ __attribute__((aligned(16))) float sT[ADD ? 4 : 4 * 16 * TL];
@@ -650,7 +666,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   if (w < 10) {
     int tr, tc;
     lower_tile(w, tr, tc);
-    gram_tile<ADD>(sX, sQ, sA, sP, rs, tr, tc, lane);
+    gram_tile<ADD, BF>(sX, sQ, sA, sP, rs, tr, tc, lane);
   }
   f4 E, dQ, Y;
   {
@@ -658,9 +674,9 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const f4 xa = a_rm(sX, LD, 16 * rt, 16 * kb, lane);
-      if (!ADD) mma16(xs, xa, b_tr(sS, LD, 16 * kb, 16 * ct, lane));
-      mma16(y, xa, b_tr(sG, LD, 16 * kb, 16 * ct, lane));
-      mma16(dq, a_rm(sO, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
+      if (!ADD) mmx<BF>(xs, xa, b_tr(sS, LD, 16 * kb, 16 * ct, lane));
+      mmx<BF>(y, xa, b_tr(sG, LD, 16 * kb, 16 * ct, lane));
+      mmx<BF>(dq, a_rm(sO, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -683,7 +699,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
       f4 y4[4];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) y4[bb] = b_rm(sE, LD, 16 * bb, 16 * w, lane);
-      solve_lower(y4, sA, sT, rs, lane);
+      solve_lower<BF>(y4, sA, sT, rs, lane);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) st_c(sE, LD, 16 * bb, 16 * w, lane, y4[bb]);
     }
@@ -706,9 +722,9 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   f4 dE, dX;
   {
     f4 z = zero4(), u = zero4();
-    for (int kb = rt; kb < 4; ++kb) mma16(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sO, LD, 16 * kb, 16 * ct, lane));
+    for (int kb = rt; kb < 4; ++kb) mmx<BF>(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sO, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma16(u, a_rm(sE, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * ct, lane));
+    for (int kb = 0; kb < 4; ++kb) mmx<BF>(u, a_rm(sE, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rt + 4 * g + i;
@@ -729,7 +745,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
       f4 y4[4];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) y4[bb] = b_rm(sG, LD, 16 * bb, 16 * w, lane);
-      solve_upper(y4, sA, sT, rs, lane);
+      solve_upper<BF>(y4, sA, sT, rs, lane);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) st_c(sG, LD, 16 * bb, 16 * w, lane, y4[bb]);  // sG now holds dR
     }
@@ -750,7 +766,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   if (!ADD) {
     f4 s = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma16(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
+    for (int kb = 0; kb < 4; ++kb) mmx<BF>(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rt + 4 * g + i;
@@ -763,7 +779,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   if (w < 10) {
     int tr, tc;
     lower_tile(w, tr, tc);
-    adjoint_tile<ADD>(sA, sP, sG, sO, sE, rs, pL[w], pE[w], tr, tc, lane);
+    adjoint_tile<ADD, BF>(sA, sP, sG, sO, sE, rs, pL[w], pE[w], tr, tc, lane);
   }
   __syncthreads();
 
@@ -772,12 +788,12 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   for (int kb = 0; kb < 4; ++kb) {
     const f4 xb = b_rm(sX, LD, 16 * kb, 16 * ct, lane);
     if (kb <= rt) {
-      mma16(dQ, a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
-      if (!ADD) mma16(dX, a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
+      mmx<BF>(dQ, a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
+      if (!ADD) mmx<BF>(dX, a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
     }
     if (kb >= rt) {
-      mma16(dX, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * ct, lane));
-      if (!ADD) mma16(dX, a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
+      mmx<BF>(dX, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * ct, lane));
+      if (!ADD) mmx<BF>(dX, a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
     }
   }
   lc = sum64(lc);
@@ -899,23 +915,25 @@ __device__ __forceinline__ f4 pc_diag(const f4 &r, const f4 &et, const float *sA
 }
 
 // Y <- M_ch^-1 Y for the 16 channels of one wave (forward substitution).
+template <bool BF>
 __device__ void solve_lower_pc(f4 (&y)[4], const f4 (&et)[4], const float *sA, float *scr, int lane) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     f4 s = zero4();
 #pragma unroll
-    for (int bp = 0; bp < b; ++bp) mma16(s, a_rm(sA, LD, 16 * b, 16 * bp, lane), et[bp] * y[bp]);
+    for (int bp = 0; bp < b; ++bp) mmx<BF>(s, a_rm(sA, LD, 16 * b, 16 * bp, lane), et[bp] * y[bp]);
     y[b] = pc_diag<false>(y[b] - s, et[b], sA, b, scr, lane);
   }
 }
 
 // Y <- M_ch^-T Y for the 16 channels of one wave (backward substitution).
+template <bool BF>
 __device__ void solve_upper_pc(f4 (&y)[4], const f4 (&et)[4], const float *sA, float *scr, int lane) {
 #pragma unroll
   for (int b = 3; b >= 0; --b) {
     f4 s = zero4();
 #pragma unroll
-    for (int bp = b + 1; bp < 4; ++bp) mma16(s, a_tr(sA, LD, 16 * b, 16 * bp, lane), y[bp]);
+    for (int bp = b + 1; bp < 4; ++bp) mmx<BF>(s, a_tr(sA, LD, 16 * b, 16 * bp, lane), y[bp]);
     y[b] = pc_diag<true>(y[b] - et[b] * s, et[b], sA, b, scr, lane);
   }
 }
@@ -939,6 +957,7 @@ __device__ __forceinline__ f4 eta_tile(const BwdArgs &a, size_t row0, int live, 
 // columns 16w..16w+15 for Zc.  Writes X, A, Zc, eta, (c, e^{Lm}) and e^{L_C}.
 template <typename IT>
 __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
+  constexpr bool BF = std::is_same_v<IT, __bf16>;   // bf16 inputs: products on bf16 MFMA
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[MAT], sP[MAT], sD[MAT];
   __shared__ __attribute__((aligned(16))) float sScr[4][SCR];
   __shared__ RowScalars rs;
@@ -963,7 +982,7 @@ __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
   for (int k = w; k < 10; k += 4) {
     int rt, ct;
     lower_tile(k, rt, ct);
-    gram_tile<false>(sX, sQ, sA, sP, rs, rt, ct, lane);
+    gram_tile<false, BF>(sX, sQ, sA, sP, rs, rt, ct, lane);
   }
   __syncthreads();  // A, P complete; sQ is read: it takes do from here on
   dO.store(sQ);
@@ -973,11 +992,11 @@ __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     f4 z = zero4();
-    for (int kb = rt; kb < 4; ++kb) mma16(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * w, lane));
+    for (int kb = rt; kb < 4; ++kb) mmx<BF>(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * w, lane));
     et[rt] = eta_tile(a, row0, live, rs, rt, w, lane);
     y[rt] = et[rt] * z;
   }
-  solve_upper_pc(y, et, sA, sScr[w], lane);
+  solve_upper_pc<BF>(y, et, sA, sScr[w], lane);
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     f4 d = y[rt];
@@ -994,8 +1013,8 @@ __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
     f4 z = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      mma16(z, a_tr(sQ, LD, 16 * rt, 16 * kb, lane), qe[kb]);
-      mma16(z, -a_tr(sD, LD, 16 * rt, 16 * kb, lane), b_rm(sX, LD, 16 * kb, 16 * w, lane));
+      mmx<BF>(z, a_tr(sQ, LD, 16 * rt, 16 * kb, lane), qe[kb]);
+      mmx<BF>(z, -a_tr(sD, LD, 16 * rt, 16 * kb, lane), b_rm(sX, LD, 16 * kb, 16 * w, lane));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) ws.Zc[(16 * rt + 4 * g + i) * D + 16 * w + cc] = z[i];
@@ -1066,7 +1085,7 @@ __global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
         yy[bb] = b_rm(sB, SP, 16 * bb, 0, lane);
         et[bb] = b_rm(sE, SP, 16 * bb, 0, lane);
       }
-      solve_upper_pc(yy, et, sA, sScr, lane);
+      solve_upper_pc<false>(yy, et, sA, sScr, lane);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
 #pragma unroll
@@ -1094,6 +1113,7 @@ __global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
 // per-channel solves run on waves 0..3 (one 16-channel column tile each).
 template <typename IT>
 __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
+  constexpr bool BF = std::is_same_v<IT, __bf16>;   // bf16 inputs: products on bf16 MFMA
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[MAT], sP[MAT], sE[MAT],
       sO[MAT];
   __shared__ __attribute__((aligned(16))) float sScr[4][SCR];
@@ -1142,7 +1162,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   if (w < 10) {
     int tr, tc;
     lower_tile(w, tr, tc);
-    gram_tile<false>(sX, sQ, sA, sP, rs, tr, tc, lane);
+    gram_tile<false, BF>(sX, sQ, sA, sP, rs, tr, tc, lane);
   }
   f4 E, dQ, Y;
   {
@@ -1150,9 +1170,9 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const f4 xa = a_rm(sX, LD, 16 * rt, 16 * kb, lane);
-      mma16(xs, xa, b_tr(sS, LD, 16 * kb, 16 * ct, lane));
-      mma16(y, xa, b_tr(sG, LD, 16 * kb, 16 * ct, lane));
-      mma16(dq, a_rm(sO, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
+      mmx<BF>(xs, xa, b_tr(sS, LD, 16 * kb, 16 * ct, lane));
+      mmx<BF>(y, xa, b_tr(sG, LD, 16 * kb, 16 * ct, lane));
+      mmx<BF>(dq, a_rm(sO, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1175,7 +1195,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
       y4[bb] = b_rm(sE, LD, 16 * bb, 16 * w, lane);
       e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
     }
-    solve_lower_pc(y4, e4, sA, sScr[w], lane);
+    solve_lower_pc<BF>(y4, e4, sA, sScr[w], lane);
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) st_c(sE, LD, 16 * bb, 16 * w, lane, y4[bb]);
   }
@@ -1187,7 +1207,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   f4 dE, dX, deta;
   {
     f4 z = zero4();
-    for (int kb = rt; kb < 4; ++kb) mma16(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sO, LD, 16 * kb, 16 * ct, lane));
+    for (int kb = rt; kb < 4; ++kb) mmx<BF>(z, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sO, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rt + 4 * g + i;
@@ -1209,7 +1229,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   {
     f4 u = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma16(u, a_rm(sE, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * ct, lane));
+    for (int kb = 0; kb < 4; ++kb) mmx<BF>(u, a_rm(sE, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
     for (int i = 0; i < 4; ++i) dX[i] = __expf(LC - rs.L[16 * rt + 4 * g + i]) * u[i];
   }
@@ -1225,7 +1245,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
       y4[bb] = b_rm(sG, LD, 16 * bb, 16 * w, lane);
       e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
     }
-    solve_upper_pc(y4, e4, sA, sScr[w], lane);
+    solve_upper_pc<BF>(y4, e4, sA, sScr[w], lane);
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) st_c(sG, LD, 16 * bb, 16 * w, lane, y4[bb]);  // sG now holds dR
   }
@@ -1241,8 +1261,8 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   {
     f4 s = zero4(), t2 = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma16(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
-    for (int kb = rt; kb < 4; ++kb) mma16(t2, a_tr(sA, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * ct, lane));
+    for (int kb = 0; kb < 4; ++kb) mmx<BF>(s, a_rm(sG, LD, 16 * rt, 16 * kb, lane), b_rm(sS, LD, 16 * kb, 16 * ct, lane));
+    for (int kb = rt; kb < 4; ++kb) mmx<BF>(t2, a_tr(sA, LD, 16 * rt, 16 * kb, lane), b_rm(sG, LD, 16 * kb, 16 * ct, lane));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rt + 4 * g + i;
@@ -1262,8 +1282,8 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const f4 fb = b_tr(sE, LD, 16 * kb, 16 * tc, lane);
-      mma16(t, a_rm(sG, LD, 16 * tr, 16 * kb, lane), fb);
-      mma16(u, a_rm(sO, LD, 16 * tr, 16 * kb, lane), fb);
+      mmx<BF>(t, a_rm(sG, LD, 16 * tr, 16 * kb, lane), fb);
+      mmx<BF>(u, a_rm(sO, LD, 16 * tr, 16 * kb, lane), fb);
     }
     const int col = 16 * tc + tcc;
     float colL = 0.f;
@@ -1308,12 +1328,12 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   for (int kb = 0; kb < 4; ++kb) {
     const f4 xb = b_rm(sX, LD, 16 * kb, 16 * ct, lane);
     if (kb <= rt) {
-      mma16(dQ, a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
-      mma16(dX, a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
+      mmx<BF>(dQ, a_rm(sP, LD, 16 * rt, 16 * kb, lane), xb);
+      mmx<BF>(dX, a_rm(sA, LD, 16 * rt, 16 * kb, lane), xb);
     }
     if (kb >= rt) {
-      mma16(dX, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * ct, lane));
-      mma16(dX, a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
+      mmx<BF>(dX, a_tr(sP, LD, 16 * rt, 16 * kb, lane), b_rm(sQ, LD, 16 * kb, 16 * ct, lane));
+      mmx<BF>(dX, a_tr(sA, LD, 16 * rt, 16 * kb, lane), xb);
     }
   }
   lc = sum64(lc);

@@ -51,7 +51,9 @@ __device__ __forceinline__ float dot4(const f4 &a, const f4 &b) {
   return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
-template <int VAR, typename IT, int DK, int DV>
+// BW: the window size (compile time, so a window holds only the registers it uses;
+// 1 for every variant but Falcon-3 / 3A).
+template <int VAR, typename IT, int DK, int DV, int BW>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   constexpr int LPR = DK / 4;          // lanes per row of S (float4 per lane)
   constexpr int RPW = 64 / LPR;        // rows per wave pass
@@ -61,7 +63,6 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int part = lane % LPR, rsub = lane / LPR;
   const int bh = blockIdx.x;
-  const int BW = WIN ? a.window : 1;
   const IT *qp = static_cast<const IT *>(a.q);
   const IT *kp = static_cast<const IT *>(a.k);
   const IT *vp = static_cast<const IT *>(a.v);
@@ -86,18 +87,22 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
   const float etas = PERCH ? 0.f : a.beta[bh] / (a.eps_eta + xn2);
   const float inv_e = 1.f / (a.eps_eta + xn2);
 
-  f4 wx[MAXW - 1];
-  float wxq[MAXW - 1];
-  if (WIN) {
+  // Falcon-3: the window's values are staged in LDS once per sequence (one
+  // coalesced read), so the per-row loop reads them without a global load whose
+  // address the compiler cannot separate from the state rows it stores.
+  constexpr int NW = BW > 1 ? BW - 1 : 1;   // window slots held (1 when unused)
+  __shared__ float swv[NW][DV];
+  if (WIN && BW > 1) {
+    for (int i = tid; i < (BW - 1) * DV; i += 256) swv[i / DV][i % DV] = a.winv[(size_t)bh * (BW - 1) * DV + i];
+    __syncthreads();
+  }
+  f4 wx[NW];
+  float wxq[NW];
+  if (WIN && BW > 1) {
 #pragma unroll
-    for (int j = 0; j < MAXW - 1; ++j) {
-      if (j < BW - 1) {
-        wx[j] = *reinterpret_cast<const f4 *>(a.winx + ((size_t)bh * (BW - 1) + j) * DK + 4 * part);
-        wxq[j] = row_sum<LPR>(dot4(wx[j], qh));
-      } else {
-        wx[j] = zero4();
-        wxq[j] = 0.f;
-      }
+    for (int j = 0; j < BW - 1; ++j) {
+      wx[j] = *reinterpret_cast<const f4 *>(a.winx + ((size_t)bh * (BW - 1) + j) * DK + 4 * part);
+      wxq[j] = row_sum<LPR>(dot4(wx[j], qh));
     }
   }
 
@@ -133,13 +138,11 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
       const float w = eta / (float)BW;
       float acc_o = 0.f;
 #pragma unroll
-      for (int j = 0; j < MAXW - 1; ++j) {
-        if (j < BW - 1) {
-          const float vj = ok ? a.winv[((size_t)bh * (BW - 1) + j) * DV + row] : 0.f;
-          const float e = DELTA ? vj - row_sum<LPR>(dot4(s, wx[j])) : vj;
-          snew += wx[j] * (w * e);
-          acc_o += e * wxq[j];
-        }
+      for (int j = 0; j < BW - 1; ++j) {
+        const float vj = ok ? swv[j][row] : 0.f;
+        const float e = DELTA ? vj - row_sum<LPR>(dot4(s, wx[j])) : vj;
+        snew += wx[j] * (w * e);
+        acc_o += e * wxq[j];
       }
       const float e = DELTA ? vi - row_sum<LPR>(dot4(s, x)) : vi;
       snew += x * (w * e);
@@ -159,18 +162,17 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     if (WIN && BW > 1) {
       // shift the window: drop the oldest pair, append (x, v)
 #pragma unroll
-      for (int j = 0; j < MAXW - 2; ++j)
-        if (j < BW - 2) *reinterpret_cast<f4 *>(a.winx + ((size_t)bh * (BW - 1) + j) * DK + 4 * part) = wx[j + 1];
+      for (int j = 0; j < BW - 2; ++j)
+        *reinterpret_cast<f4 *>(a.winx + ((size_t)bh * (BW - 1) + j) * DK + 4 * part) = wx[j + 1];
       *reinterpret_cast<f4 *>(a.winx + ((size_t)bh * (BW - 1) + BW - 2) * DK + 4 * part) = x;
     }
     *reinterpret_cast<f4 *>(a.xprev + (size_t)bh * DK + 4 * part) = xn;
   }
   if (WIN && BW > 1) {
-    // value window: each thread moves whole columns (oldest first, so no overwrite before read)
-    for (int row = tid; row < DV; row += 256) {
-      float* wvp = a.winv + (size_t)bh * (BW - 1) * DV + row;
-      for (int j = 0; j + 1 < BW - 1; ++j) wvp[(size_t)j * DV] = wvp[(size_t)(j + 1) * DV];
-      wvp[(size_t)(BW - 2) * DV] = ld1(vp + (size_t)bh * DV + row);
+    // value window, shifted from the staged copy: drop the oldest value, append v_t
+    for (int i = tid; i < (BW - 1) * DV; i += 256) {
+      const int j = i / DV, row = i % DV;
+      a.winv[(size_t)bh * (BW - 1) * DV + i] = j + 1 < BW - 1 ? swv[j + 1][row] : ld1(vp + (size_t)bh * DV + row);
     }
   }
 }
@@ -236,12 +238,12 @@ __global__ __launch_bounds__(256) void tail_kernel(FwdArgs a) {
   }
 }
 
-template <int VAR, typename IT>
+template <int VAR, typename IT, int BW>
 hipError_t step_dims(int dk, int dv, const StepArgs &a, hipStream_t s) {
   const int nblk = a.B * a.H;
 #define FALCON_STEP(DK_, DV_)                                                                  \
   if (dk == DK_ && dv == DV_) {                                                                \
-    hipLaunchKernelGGL((step_kernel<VAR, IT, DK_, DV_>), dim3(nblk), dim3(256), 0, s, a);      \
+    hipLaunchKernelGGL((step_kernel<VAR, IT, DK_, DV_, BW>), dim3(nblk), dim3(256), 0, s, a);  \
     return hipGetLastError();                                                                  \
   }
   FALCON_STEP(32, 32)
@@ -266,17 +268,28 @@ hipError_t tail_dims(int dk, int dv, const FwdArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int VAR>
+hipError_t step_window(bool bf16, int dk, int dv, const StepArgs &a, hipStream_t s) {
+#define FALCON_W(W_) \
+  case W_: return bf16 ? step_dims<VAR, __bf16, W_>(dk, dv, a, s) : step_dims<VAR, float, W_>(dk, dv, a, s)
+  switch (a.window) {
+    FALCON_W(1); FALCON_W(2); FALCON_W(3); FALCON_W(4); FALCON_W(5); FALCON_W(6); FALCON_W(7); FALCON_W(8);
+  }
+#undef FALCON_W
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_step(int variant, bool bf16, int dk, int dv, const StepArgs &a, hipStream_t s) {
-#define FALCON_V(VV) return bf16 ? step_dims<VV, __bf16>(dk, dv, a, s) : step_dims<VV, float>(dk, dv, a, s)
+#define FALCON_V(VV) return bf16 ? step_dims<VV, __bf16, 1>(dk, dv, a, s) : step_dims<VV, float, 1>(dk, dv, a, s)
   switch (variant) {
     case V_F1: FALCON_V(V_F1);
     case V_F1A: FALCON_V(V_F1A);
     case V_F2: FALCON_V(V_F2);
     case V_F2A: FALCON_V(V_F2A);
-    case V_F3: FALCON_V(V_F3);
-    case V_F3A: FALCON_V(V_F3A);
+    case V_F3: return step_window<V_F3>(bf16, dk, dv, a, s);
+    case V_F3A: return step_window<V_F3A>(bf16, dk, dv, a, s);
   }
 #undef FALCON_V
   return hipErrorInvalidValue;
