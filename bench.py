@@ -15,8 +15,10 @@ average device time of the forward path used for the roofline.  Paths
 built, else the fused kernel); "split" passes a workspace (allocated once
 outside the timed region): the prep kernel over all systems, then the state
 scan.  "auto" (default) takes the faster one measured per shape class: split
-for Falcon-3 windows and head dim 128, one-pass otherwise.  --segments P runs
-the segment-parallel form instead (every sequence cut into P segments).
+for Falcon-3 windows and head dim 128, one-pass otherwise, and for long
+sequences too few to fill the device (B*H*dv/16 <= 128 scan workgroups, T >=
+16384, one pair per step) the segment-parallel form with 16 segments.
+--segments P runs the segment-parallel form with P segments.
 
 --backward times falcon_chunk_bwd instead (Falcon-1 or 1A at the 130M-layer
 shape): the gradients of every input from the forward's per-chunk states,
@@ -419,6 +421,9 @@ def main():
     ws_bytes = split_bytes if want == "split" else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else False
     path = "split" if ws_bytes else "onepass"
+    if (args.path == "auto" and args.segments == 0 and window == 1 and variant != "F2"
+            and w.batch * w.heads * (w.dv // 16) <= 128 and w.seqlen >= 16384 and w.seqlen % 16 == 0):
+        args.segments = 16
 
     if args.segments > 0:
         ws_bytes = segmented_workspace_bytes(variant, w.dtype, w.batch, w.seqlen, w.heads, w.dk, w.dv, args.segments,
@@ -481,7 +486,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
     roof["traffic"] = measured_traffic(f"{path} {variant} {w.name}" + (f" w{window}" if window > 1 else ""))
-    roof["kernel"] = ("seg_boundary + 3 x (chunk_prep + chunk_scan) + seg_combine" if path.startswith("segmented") else
+    roof["kernel"] = ("seg_boundary + chunk_prep + 2 x chunk_scan (map form) + seg_combine + chunk_scan"
+                      if path.startswith("segmented") else
                       "chunk_prep + chunk_scan" if path == "split" else
                       "chunk_scan (one-pass)" if (w.dtype == "bf16" and w.dk <= 64 and w.chunk <= 64) else
                       "chunk_fwd_pipe" if w.dk <= 64 else "chunk_fwd_rows")

@@ -247,10 +247,11 @@ size_t falcon_chunk_fwd_segmented_workspace(const falcon_shape_t *shape, int32_t
  * in parallel: the same function as falcon_chunk_fwd (up to rounding), for
  * batches too small to fill the GPU.  A segment maps its incoming state S_0 to
  * S_0 M + N ([P1] 三种等价形式: the chunk maps are affine and compose; [P2]
- * 三种视角), so the call runs (1) the forward on all B*nseg segments from
- * S_0 = 0 (giving N), (2) from S_0 = I (giving M + N), (3) the composition
+ * 三种视角), so the call builds the key-side images of all B*nseg segments
+ * once, then runs (1) the scan from S_0 = 0 (giving N) and (2) from S_0 = I
+ * (giving M + N), both keeping end states only, (3) the composition
  * S_start[p] = S_start[p-1] M_{p-1} + N_{p-1} along each sequence, and (4) the
- * forward from S_start, which writes o and the final state.  The carried key
+ * scan from S_start, which writes o and the final state.  The carried key
  * and window entering a segment come from the inputs.  The arrays are the same
  * as falcon_chunk_fwd's ([B, T, H, d] is read as [B*nseg, T/nseg, H, d]); no
  * per-chunk states.  init may alias final_state.  Errors: nseg < 1 or not

@@ -462,8 +462,14 @@ int falcon_chunk_fwd_segmented(const falcon_shape_t *s, int32_t nseg, const void
 
   // One forward over all B*P segments, each a sequence of Ts steps (the arrays
   // [B,T,H,d] read as [B*P,Ts,H,d]).
+  // The three passes share one set of images (they depend on the inputs, not on
+  // S0): the first pass builds them, the later ones only scan.
+  bool images = false;
   auto forward = [&](const float *S0, float *S_out, float *x_out, float *wx_out, float *wv_out, void *out) {
     FwdArgs a{};
+    a.reuse_images = images ? 1 : 0;
+    a.maps_only = out ? 0 : 1;   // the map passes want the end states alone
+    images = true;
     a.q = q; a.k = k; a.v = v; a.beta = beta; a.g = log_lambda;
     a.S0 = S0;
     a.xprev0 = F(L.x);

@@ -25,6 +25,8 @@ struct FwdArgs {
   int align;                     // 0: pair (phi(k_{t-1}), v_t); 1: pair (phi(k_t), v_t)
   float log_eps_gamma, eps_phi, eps_eta;
   int write_tail;                // 1: the main kernel writes x_prev / window itself
+  int reuse_images;              // two-kernel path: the workspace already holds this call's images
+  int maps_only;                 // two-kernel path: only S_out is wanted (no o, x_prev or window)
 };
 
 struct StepArgs {

@@ -69,55 +69,78 @@ __global__ __launch_bounds__(256) void seg_identity(float *S, int dv, int dk) {
 }
 
 // S_start[b, 0] = the caller's S (or 0); S_start[b, p] = S_start[b, p-1] (MN - N)[p-1] + N[p-1].
-// Workgroup (b, h, 16 value rows); rows of S are independent.  Wave w computes
-// key-column tiles w, w+4, ... of the slab on fp32 MFMA; the slab is kept in LDS
-// as the left operand of the next product.
+// Workgroup (b, h, 16 value rows); rows of S are independent.  The segment maps
+// do not depend on the chain, so each step's M = MN - N is read into registers
+// (coalesced 16-byte loads) while the previous product runs, then staged in LDS;
+// wave w computes key-column tiles w, w+4, ... of the slab on fp32 MFMA, and the
+// slab stays in LDS as the left operand of the next product.
 template <int D>
 __global__ __launch_bounds__(256) void seg_combine(SegArgs a) {
   constexpr int LDS_ = D + 4;
-  constexpr int NCT = D / 16;  // key-column tiles
+  constexpr int NCT = D / 16;            // key-column tiles
+  constexpr int NT = (NCT + 3) / 4;      // tiles per wave
+  constexpr int NV = D * D / 4 / 256;    // 16-byte vectors of M per thread
   __shared__ __attribute__((aligned(16))) float sS[16 * LDS_];
+  __shared__ __attribute__((aligned(16))) float sM[D * LDS_];
   const int nslab = a.dv / 16;
   const int slab = blockIdx.x % nslab, bh = blockIdx.x / nslab;
   const int h = bh % a.H, b = bh / a.H;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, cc = lane & 15;
   const int r0 = 16 * slab;
   auto seg_off = [&](int p) { return ((size_t)(b * a.P + p) * a.H + h) * a.dv * D; };
   // start: the caller's S
-  for (int e = threadIdx.x; e < 16 * D; e += 256) {
+  for (int e = tid; e < 16 * D; e += 256) {
     const int r = e / D, cidx = e % D;
     const float v = a.S0 ? a.S0[((size_t)bh * a.dv + r0 + r) * D + cidx] : 0.f;
     sS[r * LDS_ + cidx] = v;
     a.Sseg[seg_off(0) + (size_t)(r0 + r) * D + cidx] = v;
   }
-  for (int p = 1; p < a.P; ++p) {
-    __syncthreads();
-    const float *N = a.Nseg + seg_off(p - 1);
-    const float *MN = a.MNseg + seg_off(p - 1);
-    f4 acc[(NCT + 3) / 4];
+  f4 mreg[NV];   // M of the next step, this thread's vectors
+  f4 nreg[NT];   // N of the next step at this lane's output elements
+  auto fetch = [&](int p) {   // the maps of segment p
+    const float *N = a.Nseg + seg_off(p), *MN = a.MNseg + seg_off(p);
 #pragma unroll
-    for (int j = 0; j < (NCT + 3) / 4; ++j) {
+    for (int j = 0; j < NV; ++j) {
+      const int e = 4 * (tid + 256 * j);
+      mreg[j] = *reinterpret_cast<const f4 *>(MN + e) - *reinterpret_cast<const f4 *>(N + e);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
       const int ct = w + 4 * j;
-      acc[j] = zero4();
-      if (ct < NCT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][i] = N[(size_t)(r0 + 4 * g + i) * D + 16 * ct + cc];
+      for (int i = 0; i < 4; ++i) nreg[j][i] = ct < NCT ? N[(size_t)(r0 + 4 * g + i) * D + 16 * ct + cc] : 0.f;
+    }
+  };
+  if (a.P > 1) fetch(0);
+  for (int p = 1; p < a.P; ++p) {
+    __syncthreads();   // the previous product is done with sM; the slab in sS is complete
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = 4 * (tid + 256 * j);
+      *reinterpret_cast<f4 *>(sM + (e / D) * LDS_ + e % D) = mreg[j];
+    }
+    f4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = nreg[j];
+    if (p + 1 < a.P) fetch(p);   // in flight during this step's product
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int ct = w + 4 * j;
+      if (ct < NCT) {
 #pragma unroll
         for (int kb = 0; kb < NCT; ++kb) {
           const f4 sa = *reinterpret_cast<const f4 *>(sS + cc * LDS_ + 16 * kb + 4 * g);  // S[c][16kb+4g+i]
-          f4 mb;  // M[16kb+4g+i][16ct+c] = (MN - N)
+          f4 mb;  // M[16kb+4g+i][16ct+c]
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const size_t off = (size_t)(16 * kb + 4 * g + i) * D + 16 * ct + cc;
-            mb[i] = MN[off] - N[off];
-          }
+          for (int i = 0; i < 4; ++i) mb[i] = sM[(16 * kb + 4 * g + i) * LDS_ + 16 * ct + cc];
           mma16(acc[j], sa, mb);
         }
       }
     }
     __syncthreads();  // every wave is done reading the previous slab
 #pragma unroll
-    for (int j = 0; j < (NCT + 3) / 4; ++j) {
+    for (int j = 0; j < NT; ++j) {
       const int ct = w + 4 * j;
       if (ct < NCT) {
 #pragma unroll

@@ -138,8 +138,13 @@ struct Split {
 // One-pass form (ONE = true): 4 derive waves build each image in LDS one system
 // ahead (the prep kernel's tiles, from the staged rows), and 4 or 8 copy waves
 // stage rows, their squared norms and the gates.
-template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false>
+// Map form (MAPS = true, two-kernel only): the state at the end of each
+// sequence and nothing else, for the segment-map passes of the two-level scan:
+// no output waves, no query rows and no fragments handed to output waves, so
+// wider channel slices fit.
+template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false, bool MAPS = false>
 struct Scan {
+  static_assert(!(ONE && MAPS), "the map form is a two-kernel scan");
   using S = Split<VAR, IT, D, C, BW>;
   static constexpr int DS = D / NS;                          // value channels per workgroup
   // one-pass derive waves (8 measured slower than 4: every role shares the CU's SIMDs)
@@ -149,18 +154,19 @@ struct Scan {
   // and F1 and F2A measured faster too), except Falcon-2, whose state waves need
   // more registers than 16 waves leave (156 VGPRs), else 4
   static constexpr int NCW = DS / 16, NSW = ONE ? (VAR != V_F2 && NCW == 2 ? 8 : 4) : 8;
+  static constexpr int NOW = MAPS ? 0 : NCW;                 // output waves
   static constexpr int RG = BW == 1 ? R_EC + 1 : R_N;        // per-row arrays a derive wave uses
-  static constexpr int NT = 64 * (2 * NCW + NDW + NSW), NST = 64 * NSW;
+  static constexpr int NT = 64 * (NCW + NOW + NDW + NSW), NST = 64 * NSW;
   static constexpr int LXV = DS + S::PADE;                   // V rows (this workgroup's channels)
   static constexpr int RPC = NST / S::TPR, NPK = (C + RPC - 1) / RPC;   // key / query rows per copy pass
   static constexpr int TPV = DS / S::VEC, RPV = NST / TPV, NPV = (C + RPV - 1) / RPV;
   static constexpr int NPI = ONE ? 1 : (S::NU + NST - 1) / NST;
   // LDS slots: keys and values 2 (3 one-pass: derive waves read one system ahead),
   // queries 3 (4), images 3 (output waves lag one system); S and E' fragments 2
-  static constexpr int NXS = ONE ? 3 : 2, NQS = ONE ? 4 : 3;
+  static constexpr int NXS = ONE ? 3 : 2, NQS = MAPS ? 0 : ONE ? 4 : 3;
   static constexpr size_t lds() {
     return (size_t)S::SZ * (NXS * C * S::LX + NQS * S::CSP * S::LX + NXS * C * LXV) + 3 * (size_t)S::IMG +
-           2 * (size_t)NCW * 64 * S::SZ * (8 * (S::NA / 2) + 4 * S::NB) +
+           2 * (size_t)NOW * 64 * S::SZ * (8 * (S::NA / 2) + 4 * S::NB) +
            (ONE ? (size_t)4 * (3 * 4 * C + NDW * RG * C) : 0);
   }
   static constexpr bool fits() {
@@ -619,27 +625,29 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
 }
 
 // ============================== scan kernel ==============================
-template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE>
-__global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_scan(FwdArgs a, const unsigned char *ws) {
+template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE, bool MAPS>
+__global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE, MAPS>::NT)) void chunk_scan(FwdArgs a,
+                                                                                          const unsigned char *ws) {
   using S = Split<VAR, IT, D, C, BW>;
-  using Z = Scan<VAR, IT, D, C, BW, NS, ONE>;
+  using Z = Scan<VAR, IT, D, C, BW, NS, ONE, MAPS>;
   using OpT = IT;
   using Frag = typename Op<OpT>::frag;
   using Pr = Pair<OpT>;
   constexpr int NB = S::NB, NA = S::NA, NCW = Z::NCW, LX = S::LX, VEC = S::VEC, TPR = S::TPR, RPC = Z::RPC;
   constexpr int LXV = Z::LXV, TPV = Z::TPV, RPV = Z::RPV;
-  constexpr int CS = S::CS, CSP = S::CSP, NBS = S::NBS, NXS = Z::NXS, NQS = Z::NQS, NDW = Z::NDW;
+  constexpr int CS = S::CS, CSP = S::CSP, NBS = S::NBS, NXS = Z::NXS, NDW = Z::NDW, NOW = Z::NOW;
+  constexpr int NQS = Z::NQS > 0 ? Z::NQS : 1;   // query slots (one unused slot in the map form)
   constexpr bool PERCH = S::PERCH, DELTA = S::DELTA;
 
   // Raw operands (dk permuted); the per-row factors are applied to the products,
   // so copy waves only move bytes and take few issue slots from the other waves:
   __shared__ __attribute__((aligned(16))) OpT sX[NXS][C * LX];     // key of each virtual row
   __shared__ __attribute__((aligned(16))) IT sV[NXS][C * LXV];     // raw v of each virtual row, this workgroup's channels
-  __shared__ __attribute__((aligned(16))) OpT sQ[NQS][CSP * LX];   // q of each step row
+  __shared__ __attribute__((aligned(16))) OpT sQ[NQS][MAPS ? 8 : CSP * LX];   // q of each step row
   __shared__ __attribute__((aligned(16))) unsigned char sImg[3][S::IMG];
   // handed from each state wave to its output wave: S at the system's start, E'
-  __shared__ Pr sSp[2][NCW][NA / 2][64];
-  __shared__ Frag sEb[2][NCW][NB][64];
+  __shared__ Pr sSp[MAPS ? 1 : 2][MAPS ? 1 : NCW][NA / 2][MAPS ? 1 : 64];
+  __shared__ Frag sEb[MAPS ? 1 : 2][MAPS ? 1 : NCW][NB][MAPS ? 1 : 64];
   // one-pass: squared norms of key / query rows, clamped log-decays and gains of
   // the steps (staged with the rows), and each derive wave's per-row arrays
   __shared__ float sNrm[ONE ? 3 : 1][2][ONE ? C : 1];
@@ -666,10 +674,10 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
   const int T = a.cu ? a.cu[b + 1] - a.cu[b] : a.T;
   if (T <= 0) return;
   const int H = a.H, NC = a.nchunks, NSYS = S::nsys(T);
-  const int role = wv < NCW ? 0 : wv < 2 * NCW ? 1 : wv < 2 * NCW + NDW ? 3 : 2;   // state, output, derive, copy
+  const int role = wv < NCW ? 0 : wv < NCW + NOW ? 1 : wv < NCW + NOW + NDW ? 3 : 2;   // state, output, derive, copy
   const int cw = role == 1 ? wv - NCW : wv;                // channel group of a state / output wave
-  const int dw = wv - 2 * NCW;                             // derive wave index
-  const int ctid = tid - 64 * (2 * NCW + NDW);             // copy thread index
+  const int dw = wv - NCW - NOW;                           // derive wave index
+  const int ctid = tid - 64 * (NCW + NOW + NDW);           // copy thread index
   const int chW = Z::DS * sp + 16 * cw + cl;               // the lane's value channel
 
   const IT *qp = static_cast<const IT *>(a.q);
@@ -794,7 +802,7 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
       for (int ps = 0; ps < Z::NPK; ++ps) {
         const int r = min(ps * RPC + ctid / TPR, C - 1), part = ctid % TPR;
         R.k[ps] = *reinterpret_cast<const uint4 *>(kp + base + (pair_of(0, r) - 1 + a.align) * rstride + part * VEC);
-        R.q[ps] = *reinterpret_cast<const uint4 *>(qp + base + min(r, CS - 1) * rstride + part * VEC);
+        if constexpr (!MAPS) R.q[ps] = *reinterpret_cast<const uint4 *>(qp + base + min(r, CS - 1) * rstride + part * VEC);
       }
       if constexpr (ONE) {
         const size_t gi = ((size_t)(tok0 + c0 + min(ctid, CS - 1))) * H + h;
@@ -818,7 +826,7 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
       const int r = min(ps * RPC + ctid / TPR, C - 1), part = ctid % TPR;
       const int tk = min(max(pair_of(c0, r) - 1 + a.align, 0), T - 1), tq = min(c0 + r, T - 1);
       R.k[ps] = *reinterpret_cast<const uint4 *>(kp + ((size_t)(tok0 + tk) * H + h) * D + part * VEC);
-      R.q[ps] = *reinterpret_cast<const uint4 *>(qp + ((size_t)(tok0 + tq) * H + h) * D + part * VEC);
+      if constexpr (!MAPS) R.q[ps] = *reinterpret_cast<const uint4 *>(qp + ((size_t)(tok0 + tq) * H + h) * D + part * VEC);
     }
     if constexpr (ONE) {
       const int t = min(c0 + min(ctid, CSP - 1), T - 1);
@@ -847,7 +855,7 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
             const float sk = group_sum<TPR>(sumsq(R.k[ps], IT()));
             if (part == 0) sNrm[si][0][r] = sk;
           }
-          if (r < CSP) {
+          if (!MAPS && r < CSP) {
             const uint4 qq = CSP > CS ? keep_or_zero(r < CS, R.q[ps]) : R.q[ps];
             put_perm(sQ[s3] + r * LX, part * VEC, qq);
             if constexpr (ONE) {
@@ -914,7 +922,7 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
           sk = group_sum<TPR>(sk);
           if (ctid % TPR == 0) sNrm[si][0][r] = sk;
         }
-        if (r < CSP) {
+        if (!MAPS && r < CSP) {
           const uint4 qq = keep_or_zero(r < CS && c0 + r < T, R.q[ps]);
           put_perm(sQ[s3] + r * LX, part * VEC, qq);
           if constexpr (ONE) {
@@ -970,7 +978,7 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
 #pragma unroll
     for (int a2 = 0; a2 < NA / 2; ++a2) {
       Sp[a2] = mkp(cvt<OpT>(sT[2 * a2]), cvt<OpT>(sT[2 * a2 + 1]));
-      sSp[s2][cw][a2][lane] = Sp[a2];
+      if constexpr (!MAPS) sSp[s2][cw][a2][lane] = Sp[a2];
     }
     // XS = diag(GAM) X S0^T: C-layout (virtual rows 16p+4g+i, channel c), the row
     // factor applied to the product
@@ -1045,7 +1053,7 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
         Ef = R;
       }
       Eb[p] = cvt<OpT>(Ef);
-      sEb[s2][cw][p][lane] = Eb[p];
+      if constexpr (!MAPS) sEb[s2][cw][p][lane] = Eb[p];
       Ec[p] = cvt<OpT>(Ef * *reinterpret_cast<const f4 *>(F + F_CST * C + 16 * p + 4 * g4));
       // a finished pair of row blocks (or the last, unpaired one) goes into the state
       if ((p & 1) || p == NB - 1) {
@@ -1190,12 +1198,12 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
       for (int aa = 0; aa < NA; ++aa)
         *reinterpret_cast<f4 *>(a.S_out + ((size_t)bh * D + chW) * D + 16 * aa + 4 * g4) = sT[aa];
     }
-  } else if (role == 1) {
+  } else if (!MAPS && role == 1) {
     __syncthreads();
     if (ONE) __syncthreads();
     __syncthreads();
     for (int i = 1; i <= NSYS; ++i) {
-      output(i - 1);
+      if (op) output(i - 1);   // the segment-map passes store no outputs and skip their products
       __syncthreads();
     }
   } else if (role == 3) {
@@ -1232,7 +1240,7 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
     if (a.write_tail) {
       // outgoing x_prev = phi(k_{T-1}) and, for windows, the last Bw-1 pairs
       // j = T-Bw+1..T-1 (keys phi(k_{j-1}), values v_j; carried ones for j <= 0)
-      const int w8 = wv - 2 * NCW - NDW;
+      const int w8 = wv - NCW - NOW - NDW;
       // normalised key k_t (t >= 0) or carried key of pair j (t = j - 1 + align < 0) into dst[0..D)
       auto key_row = [&](int t, int j, float *dst) {
         float xv[2] = {0.f, 0.f};
@@ -1279,13 +1287,17 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE>::NT)) void chunk_
 
 // Channel splits built per shape: fp32 keeps whole sequences; bf16 takes 1 or
 // 2 slices at d <= 64 and 2, 4 or 8 at d = 128 (whose values do not fit whole).
+// The map form takes whole sequences, or 2 slices at d = 128.
 template <typename IT, int D>
-constexpr bool ns_built(int ns) {
+constexpr bool ns_built(int ns, bool maps = false) {
+  if (maps) return sizeof(IT) == 2 && D == 128 ? (ns == 1 || ns == 2) : ns == 1;
   if (sizeof(IT) == 4) return ns == 1;
   return D <= 64 ? (ns == 1 || ns == 2) : (ns == 2 || ns == 4 || ns == 8);
 }
-template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false>
-constexpr bool scan_ok() { return ns_built<IT, D>(NS) && Scan<VAR, IT, D, C, BW, NS, ONE>::fits(); }
+template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false, bool MAPS = false>
+constexpr bool scan_ok() {
+  return ns_built<IT, D>(NS, MAPS) && Scan<VAR, IT, D, C, BW, NS, ONE, MAPS>::fits();
+}
 
 // Smallest built split that fits and gives at least 128 scan workgroups (else
 // the largest that fits); 0 when none fits.
@@ -1302,11 +1314,29 @@ int pick_ns(int bh) {
   return best;
 }
 
-template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false>
+// Map form: the smallest split that fits and gives at least 256 workgroups (one
+// per compute unit; these scans are chain-bound), else the largest; 0 if none.
+template <int VAR, typename IT, int D, int C, int BW>
+int pick_ns_maps(int bh) {
+  if constexpr (VAR == V_F2) {   // per-channel steps: no single segment map
+    return 0;
+  } else {
+    const bool ok[2] = {scan_ok<VAR, IT, D, C, BW, 1, false, true>(), scan_ok<VAR, IT, D, C, BW, 2, false, true>()};
+    int best = 0;
+    for (int i = 0; i < 2; ++i) {
+      if (!ok[i]) continue;
+      best = 1 << i;
+      if (bh * best >= 256) break;
+    }
+    return best;
+  }
+}
+
+template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false, bool MAPS = false>
 hipError_t launch_scan(const FwdArgs &a, const unsigned char *w, hipStream_t st) {
-  if constexpr (scan_ok<VAR, IT, D, C, BW, NS, ONE>()) {
-    hipLaunchKernelGGL((chunk_scan<VAR, IT, D, C, BW, NS, ONE>), dim3(a.B * a.H * NS),
-                       dim3(Scan<VAR, IT, D, C, BW, NS, ONE>::NT), 0, st, a, w);
+  if constexpr (scan_ok<VAR, IT, D, C, BW, NS, ONE, MAPS>()) {
+    hipLaunchKernelGGL((chunk_scan<VAR, IT, D, C, BW, NS, ONE, MAPS>), dim3(a.B * a.H * NS),
+                       dim3(Scan<VAR, IT, D, C, BW, NS, ONE, MAPS>::NT), 0, st, a, w);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
@@ -1333,9 +1363,17 @@ hipError_t launch_split(const FwdArgs &a, void *ws, hipStream_t st) {
   unsigned char *w = static_cast<unsigned char *>(ws);
   // packed sequences: one prep workgroup per image slot of each head (a.T is the total token count)
   const long long nprep = a.cu ? (long long)a.H * Sp::slots(a.B, a.T) : (long long)a.B * a.H * Sp::nsys(a.T);
-  hipLaunchKernelGGL((chunk_prep<VAR, IT, D, C, BW>), dim3((unsigned)nprep), dim3(256), 0, st, a, w);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!a.reuse_images) {   // the images depend on keys, queries and gates only, not on S0
+    hipLaunchKernelGGL((chunk_prep<VAR, IT, D, C, BW>), dim3((unsigned)nprep), dim3(256), 0, st, a, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.maps_only) {   // the end state alone, on the map form where it is built
+    switch (pick_ns_maps<VAR, IT, D, C, BW>(a.B * a.H)) {
+      case 1: return launch_scan<VAR, IT, D, C, BW, 1, false, true>(a, w, st);
+      case 2: return launch_scan<VAR, IT, D, C, BW, 2, false, true>(a, w, st);
+    }
+  }
   switch (ns) {
     case 1: return launch_scan<VAR, IT, D, C, BW, 1>(a, w, st);
     case 2: return launch_scan<VAR, IT, D, C, BW, 2>(a, w, st);
