@@ -22,3 +22,18 @@ def _flush_name(item):
 def pytest_runtest_setup(item):
     if item.get_closest_marker("gpu") is not None:
         _flush_name(item)
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The largest rel-L2 against the fp64 oracle per test family, quantity and
+    input dtype over the tests that ran (GPU runs only)."""
+    try:
+        from gpu_helpers import MAXIMA
+    except ImportError:
+        return
+    if not MAXIMA:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "largest rel-L2 against the oracle (family / quantity / inputs)")
+    for (fam, name, dtype), e in sorted(MAXIMA.items()):
+        tr.write_line(f"{fam:52s} {name:20s} {dtype:5s} {e:.2e}")

@@ -7,6 +7,16 @@ import workloads as W
 
 TOL = {"fp32": 1e-4, "bf16": 2e-2}   # rel-L2 bar of the parity tests
 
+# Largest error seen per (test family, quantity, input dtype) in this session;
+# tests/conftest.py prints the table at the end of a run.
+MAXIMA = {}
+
+
+def record(family, errs, dtype):
+    for name, e in errs.items():
+        key = (family, name, dtype)
+        MAXIMA[key] = max(MAXIMA.get(key, 0.0), float(e))
+
 
 def rel_l2(got, ref):
     got = np.asarray(got, np.float64)

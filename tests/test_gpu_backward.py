@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import TOL, rel_l2, state_to_dev, to_dev, to_np
+from gpu_helpers import TOL, record, rel_l2, state_to_dev, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,7 @@ def check_bwd(variant, w, seed, init=True, final_grad=True, align="prefix", chun
     ref = oracle.recurrent_backward(variant, **inp, do=cot["do"], state=st, dS_T=cot["dS_T"], align=align)
     errs = {n: rel_l2(got[n], ref[n]) for n in GRADS}
     print(variant, w.name, w.dtype, w.seqlen, align, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    record("backward", errs, w.dtype)
     for n, e in errs.items():
         assert np.all(np.isfinite(got[n])), n
         assert e <= TOL[w.dtype], (n, e)
@@ -119,6 +120,7 @@ def test_backward_full_size_sampled(variant):
                 gn = got[n][b:b + 1, :, h:h + 1]
             e = rel_l2(gn, ref[n])
             print(variant, (b, h), n, f"{e:.2e}", flush=True)
+            record("backward, full size sampled", {n: e}, "bf16")
             assert e <= TOL["bf16"], (b, h, n, e)
 
 

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import TOL, rel_l2, state_to_dev, to_dev, to_np
+from gpu_helpers import TOL, record, rel_l2, state_to_dev, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -40,9 +40,11 @@ def test_decode_steps(variant, window, d, dtype):
         o = step_gpu(variant, x, st_dev, window, dtype)
         r = oracle.decode_step(variant, x["q"], x["k"], x["v"], x["beta"], x["log_lambda"], st_ref, window=window)
         st_ref = {n: r[n] for n in st0}
+        record("decode step (10-step chains)", {"o": rel_l2(o, r["o"])}, dtype)
         assert rel_l2(o, r["o"]) <= TOL[dtype], (t, rel_l2(o, r["o"]))
     for n in st0:
         e = rel_l2(to_np(st_dev[n]), st_ref[n])
+        record("decode step (10-step chains)", {n: e}, dtype)
         assert e <= TOL[dtype], (n, e)
 
 

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import ROW_FACTOR, TOL, oracle_subset, rel_l2, seq_errors, state_to_dev, to_dev, to_np
+from gpu_helpers import ROW_FACTOR, TOL, oracle_subset, record, rel_l2, seq_errors, state_to_dev, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,7 @@ def check(variant, w, seed, window=1, init=False, chunk=None, chunk_states=False
     head, row = seq_errors(g["o"], r["o"])
     print(variant, w.name, seed, {k: f"{v:.2e}" for k, v in errs.items()},
           f"o per-head max {head:.2e} row max {row:.2e}", flush=True)
+    record("chunked forward", {**errs, "o, worst sequence": head, "o, worst row": row}, w.dtype)
     for k, e in errs.items():
         assert e <= tol, (k, e)
     assert head <= tol, ("o per-head", head)
@@ -203,6 +204,7 @@ def test_full_size_sampled(name, variant):
         eo = rel_l2(g["o"][b, :, h], r["o"][0, :, 0])
         es = rel_l2(g["S"][b, h], r["S"][0, 0])
         print(variant, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
+        record("full-size workloads, sampled", {"o": eo, "S": es}, "bf16")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
     assert np.all(np.isfinite(g["o"]))
 
@@ -267,6 +269,7 @@ def test_onepass_full_size_sampled(variant):
         eo = rel_l2(g["o"][b, :, h], r["o"][0, :, 0])
         es = rel_l2(g["S"][b, h], r["S"][0, 0])
         print(variant, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
+        record("full-size workloads, sampled", {"o": eo, "S": es}, "bf16")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
     assert np.all(np.isfinite(g["o"]))
 
@@ -524,6 +527,7 @@ def test_window_full_size_sampled(variant, bw):
         eo = rel_l2(g["o"][b, :, h], r["o"][0, :, 0])
         es = rel_l2(g["S"][b, h], r["S"][0, 0])
         print(variant, bw, (b, h), f"o {eo:.2e} S {es:.2e}", flush=True)
+        record("full-size workloads, sampled", {"o": eo, "S": es}, "bf16")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import TOL, rel_l2, state_to_dev, to_dev, to_np
+from gpu_helpers import TOL, record, rel_l2, state_to_dev, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,7 @@ def check_seg(variant, w, nseg, seed, window=1, init=False, align="prefix", inpl
     errs = {k: rel_l2(got[k], ref[k]) for k in keys}
     print(variant, w.name, w.dtype, w.seqlen, nseg, window, align, {k: f"{v:.2e}" for k, v in errs.items()},
           flush=True)
+    record("segment-parallel forward", errs, w.dtype)
     for k, e in errs.items():
         assert e <= TOL[w.dtype], (k, e)
     return errs
@@ -84,6 +85,12 @@ def test_segmented_d128():
     check_seg("F1", shape(1024, d=128, B=1, H=2), 8, 19, init=True)
 
 
+@pytest.mark.parametrize("variant,nseg", [("F3", 8), ("F3A", 4)])
+def test_segmented_windows_d128(variant, nseg):
+    """Windows at head dim 128: the map passes take two 64-channel slices."""
+    check_seg(variant, shape(1024, d=128, B=1, H=2), nseg, 37, window=4, init=True)
+
+
 def test_segmented_matches_plain_forward():
     """Same function as falcon_chunk_fwd on the same inputs (bf16 outputs: the two
     differ only by rounding)."""
@@ -112,4 +119,5 @@ def test_segmented_long_sampled(variant):
             g = got[k][:, :, h:h + 1] if k == "o" else got[k][:, h:h + 1]
             e = rel_l2(g, ref[k])
             print(variant, h, k, f"{e:.2e}", flush=True)
+            record("segment-parallel forward, long context sampled", {k: e}, "bf16")
             assert e <= TOL["bf16"], (h, k, e)

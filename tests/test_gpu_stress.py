@@ -25,7 +25,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import ROW_FACTOR, TOL, oracle_subset, rel_l2, seq_errors, state_to_dev, to_dev, to_np
+from gpu_helpers import ROW_FACTOR, TOL, oracle_subset, record, rel_l2, seq_errors, state_to_dev, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,8 @@ def compare(variant, inp, dtype, chunk, window=1, init=None, chunk_states=False,
         errs["chunk_states"] = rel_l2(g["chunk_states"], np.moveaxis(r["states"][:, ends], 2, 1))
     head, row = seq_errors(g["o"], r["o"])
     print(variant, label, {k: f"{v:.2e}" for k, v in errs.items()}, f"head {head:.2e} row {row:.2e}", flush=True)
+    record("stress (deep decay, correlated keys, fallbacks)", {**errs, "o, worst sequence": head, "o, worst row": row},
+           dtype)
     for k, e in errs.items():
         assert e <= tol, (k, e)
     assert head <= tol and row <= ROW_FACTOR * tol, (head, row)
@@ -212,6 +214,7 @@ def test_long_context_full_length(variant):
         es = rel_l2(g["S"][b, h], r["S"][0, 0])
         head, row = seq_errors(g["o"][b:b + 1, :, h:h + 1], r["o"])
         print(variant, (b, h), f"o {eo:.2e} S {es:.2e} row max {row:.2e}", flush=True)
+        record("long context, full length, sampled", {"o": eo, "S": es, "o, worst row": row}, "bf16")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"] and row <= ROW_FACTOR * TOL["bf16"]
     assert np.all(np.isfinite(g["o"]))
 
