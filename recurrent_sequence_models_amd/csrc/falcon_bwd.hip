@@ -54,7 +54,6 @@ namespace {
 constexpr int D = 64;    // d_k = d_v
 constexpr int C = 64;    // steps per chunk
 constexpr int LD = 68;   // LDS pitch of a 64-wide matrix (floats)
-constexpr int TL = 20;   // LDS pitch of a 16x16 diagonal-block inverse
 constexpr int MAT = C * LD;
 
 // ---- fragments (lane l = 16g + c) ---------------------------------------------
@@ -219,27 +218,56 @@ __device__ __forceinline__ void lower_tile(int k, int &rt, int &ct) {
   rt = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3;
   ct = k - rt * (rt + 1) / 2;
 }
-// Inverse of the unit lower-triangular diagonal block w of M = I + A diag(eta),
-// by forward substitution: lane j < 16 solves for column j.
-__device__ void diag_inverse(const float *sA, float *sT, const RowScalars &rs, int w, int lane) {
-  if (lane < 16) {
-    const int base = 16 * w;
-    float t[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = r == lane ? 1.f : 0.f;
-#pragma unroll
-      for (int q = 0; q < r; ++q) s -= sA[(base + r) * LD + base + q] * rs.eta[base + q] * t[q];
-      t[r] = s;
+// Diagonal block b of a chunk solve, for the 16 columns of one wave (value or
+// key channels; C-layout: lane (g, c) holds rows 16b+4g..16b+4g+3 of column c),
+// with steps eta per row and column (the same for every column but Falcon-2's):
+//   lower (UPPER = false): y = (I + A_bb diag(eta))^-1 r,
+//   upper (UPPER = true):  y = (I + diag(eta) A_bb^T)^-1 r.
+// Each lane solves its own 4 rows exactly with the 6 coefficients of its 4x4
+// diagonal sub-block; the coupling between the four row groups (A_bb without
+// those sub-blocks) is strictly block-triangular, so three sweeps of it on MFMA
+// make the solution exact.
+template <bool UPPER, bool BF>
+__device__ __forceinline__ f4 pc_diag(const f4 &r, const f4 &et, const float *sA, int b, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  const float *Ag = sA + (16 * b + 4 * g) * LD + 16 * b + 4 * g;   // this row group's 4x4 sub-block
+  const float a10 = Ag[LD], a20 = Ag[2 * LD], a21 = Ag[2 * LD + 1];
+  const float a30 = Ag[3 * LD], a31 = Ag[3 * LD + 1], a32 = Ag[3 * LD + 2];
+  f4 an = UPPER ? a_tr(sA, LD, 16 * b, 16 * b, lane) : a_rm(sA, LD, 16 * b, 16 * b, lane);
+  if ((c >> 2) == g) an = zero4();   // A-layout row c lies in group c / 4
+  auto local = [&](const f4 &z) {
+    f4 y;
+    if constexpr (UPPER) {
+      y[3] = z[3];
+      y[2] = z[2] - et[2] * (a32 * y[3]);
+      y[1] = z[1] - et[1] * (a21 * y[2] + a31 * y[3]);
+      y[0] = z[0] - et[0] * (a10 * y[1] + a20 * y[2] + a30 * y[3]);
+    } else {
+      y[0] = z[0];
+      y[1] = z[1] - a10 * (et[0] * y[0]);
+      y[2] = z[2] - a20 * (et[0] * y[0]) - a21 * (et[1] * y[1]);
+      y[3] = z[3] - a30 * (et[0] * y[0]) - a31 * (et[1] * y[1]) - a32 * (et[2] * y[2]);
     }
+    return y;
+  };
+  f4 y = local(r);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sT[w * 16 * TL + r * TL + lane] = t[r];
+  for (int it = 0; it < 3; ++it) {
+    f4 cpl = zero4();
+    if constexpr (UPPER) {
+      mmx<BF>(cpl, an, y);
+      y = local(r - et * cpl);
+    } else {
+      mmx<BF>(cpl, an, et * y);
+      y = local(r - cpl);
+    }
   }
+  return y;
 }
 
 // Y <- M^-1 Y for one 16-column tile held by a wave (blocked forward substitution).
 template <bool BF>
-__device__ void solve_lower(f4 (&y)[4], const float *sA, const float *sT, const RowScalars &rs, int lane) {
+__device__ void solve_lower(f4 (&y)[4], const float *sA, const RowScalars &rs, int lane) {
   const int g = lane >> 4;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -251,16 +279,16 @@ __device__ void solve_lower(f4 (&y)[4], const float *sA, const float *sT, const 
       for (int i = 0; i < 4; ++i) af[i] *= rs.eta[16 * bp + 4 * g + i];
       mmx<BF>(s, af, y[bp]);
     }
-    const f4 r = y[b] - s;
-    y[b] = zero4();
-    mmx<BF>(y[b], a_rm(sT + b * 16 * TL, TL, 0, 0, lane), r);
+    const float *eb = rs.eta + 16 * b + 4 * g;
+    const f4 et = {eb[0], eb[1], eb[2], eb[3]};
+    y[b] = pc_diag<false, BF>(y[b] - s, et, sA, b, lane);
   }
 }
 
 // Y <- M^-T Y (blocked backward substitution).
 template <bool BF>
-__device__ void solve_upper(f4 (&y)[4], const float *sA, const float *sT, const RowScalars &rs, int lane) {
-  const int cc = lane & 15;
+__device__ void solve_upper(f4 (&y)[4], const float *sA, const RowScalars &rs, int lane) {
+  const int g = lane >> 4, cc = lane & 15;
 #pragma unroll
   for (int b = 3; b >= 0; --b) {
     f4 s = zero4();
@@ -270,9 +298,9 @@ __device__ void solve_upper(f4 (&y)[4], const float *sA, const float *sT, const 
       af *= rs.eta[16 * b + cc];
       mmx<BF>(s, af, y[bp]);
     }
-    const f4 r = y[b] - s;
-    y[b] = zero4();
-    mmx<BF>(y[b], a_tr(sT + b * 16 * TL, TL, 0, 0, lane), r);
+    const float *eb = rs.eta + 16 * b + 4 * g;
+    const f4 et = {eb[0], eb[1], eb[2], eb[3]};
+    y[b] = pc_diag<true, BF>(y[b] - s, et, sA, b, lane);
   }
 }
 
@@ -322,7 +350,6 @@ template <typename IT, bool ADD>
 __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
   constexpr bool BF = std::is_same_v<IT, __bf16>;   // bf16 inputs: products on bf16 MFMA
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[ADD ? 4 : MAT], sP[ADD ? 4 : MAT];
-  __shared__ __attribute__((aligned(16))) float sT[ADD ? 4 : 4 * 16 * TL];
   __shared__ RowScalars rs;
   const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
@@ -351,8 +378,6 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
   __syncthreads();  // sQ is read: it takes do from here on
   dO.store(sQ);
   if (!ADD) {
-    diag_inverse(sA, sT, rs, w, lane);
-    __syncthreads();
     f4 W[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -360,7 +385,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) W[rt][i] *= __expf(rs.Lm[16 * rt + 4 * g + i]);
     }
-    solve_lower<BF>(W, sA, sT, rs, lane);
+    solve_lower<BF>(W, sA, rs, lane);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       f4 s = zero4();
@@ -378,9 +403,8 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
         ws.W[row * D + 16 * w + cc] = rs.eta[row] * __expf(LC - rs.L[row]) * W[rt][i];
       }
     }
-  } else {
-    __syncthreads();
   }
+  __syncthreads();  // every thread's rows of do are in sQ
   // Z = do^T qe: value-channel rows, key-channel column tile w.
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
@@ -618,7 +642,6 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   constexpr bool BF = std::is_same_v<IT, __bf16>;   // bf16 inputs: products on bf16 MFMA
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[ADD ? 4 : MAT], sP[MAT],
       sE[MAT], sO[MAT];
-  __shared__ __attribute__((aligned(16))) float sT[ADD ? 4 : 4 * 16 * TL];
   __shared__ RowScalars rs;
   __shared__ float pL[NWC][C], pE[NWC][C], pC[NWC], sCoef[C];
   const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
@@ -693,13 +716,11 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   st_c(sE, LD, 16 * rt, 16 * ct, lane, E);  // R (F1A: E = V)
   __syncthreads();  // A, P and R are complete
   if (!ADD) {
-    if (w < 4) diag_inverse(sA, sT, rs, w, lane);
-    __syncthreads();  // all four diagonal-block inverses
     if (w < 4) {
       f4 y4[4];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) y4[bb] = b_rm(sE, LD, 16 * bb, 16 * w, lane);
-      solve_lower<BF>(y4, sA, sT, rs, lane);
+      solve_lower<BF>(y4, sA, rs, lane);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) st_c(sE, LD, 16 * bb, 16 * w, lane, y4[bb]);
     }
@@ -745,7 +766,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
       f4 y4[4];
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) y4[bb] = b_rm(sG, LD, 16 * bb, 16 * w, lane);
-      solve_upper<BF>(y4, sA, sT, rs, lane);
+      solve_upper<BF>(y4, sA, rs, lane);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) st_c(sG, LD, 16 * bb, 16 * w, lane, y4[bb]);  // sG now holds dR
     }
@@ -870,71 +891,29 @@ __device__ __forceinline__ WsF2 ws_f2(const BwdArgs &a, size_t chunk_id) {
   return p;
 }
 
-constexpr int SP = 17;                 // pitch of a wave's 16x16 scratch blocks
-constexpr int SCR = 2 * 16 * SP;       // floats of one wave's scratch: right-hand side, steps
-
-// The 16x16 diagonal block b of a per-channel solve, 16 channels (one per lane):
-// r (C-layout: rows 16b + 4g + i, channel c) goes through the wave's scratch,
-// lanes 0..15 substitute along the block's rows, and the solution comes back in
-// C-layout.  UPPER: (I + diag(eta) A_bb^T) y = r, else (I + A_bb diag(eta)) y = r.
-template <bool UPPER>
-__device__ __forceinline__ f4 pc_diag(const f4 &r, const f4 &et, const float *sA, int b, float *scr, int lane) {
-  st_c(scr, SP, 0, 0, lane, r);
-  st_c(scr + 16 * SP, SP, 0, 0, lane, et);
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  if (lane < 16) {
-    float y[16], e[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      y[i] = scr[i * SP + lane];
-      e[i] = scr[16 * SP + i * SP + lane];
-    }
-    const float *Ab = sA + 16 * b * LD + 16 * b;
-    if constexpr (UPPER) {
-#pragma unroll
-      for (int i = 15; i >= 0; --i) {
-        float s = 0.f;
-#pragma unroll
-        for (int j = i + 1; j < 16; ++j) s += Ab[j * LD + i] * y[j];
-        y[i] -= e[i] * s;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-#pragma unroll
-        for (int j = 0; j < i; ++j) y[i] -= Ab[i * LD + j] * e[j] * y[j];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) scr[i * SP + lane] = y[i];
-  }
-  __builtin_amdgcn_wave_barrier();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  return b_rm(scr, SP, 0, 0, lane);
-}
+constexpr int SP = 17;                 // pitch of the scan's C x 16 arrays (one 16-channel slice)
 
 // Y <- M_ch^-1 Y for the 16 channels of one wave (forward substitution).
 template <bool BF>
-__device__ void solve_lower_pc(f4 (&y)[4], const f4 (&et)[4], const float *sA, float *scr, int lane) {
+__device__ void solve_lower_pc(f4 (&y)[4], const f4 (&et)[4], const float *sA, int lane) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     f4 s = zero4();
 #pragma unroll
     for (int bp = 0; bp < b; ++bp) mmx<BF>(s, a_rm(sA, LD, 16 * b, 16 * bp, lane), et[bp] * y[bp]);
-    y[b] = pc_diag<false>(y[b] - s, et[b], sA, b, scr, lane);
+    y[b] = pc_diag<false, BF>(y[b] - s, et[b], sA, b, lane);
   }
 }
 
 // Y <- M_ch^-T Y for the 16 channels of one wave (backward substitution).
 template <bool BF>
-__device__ void solve_upper_pc(f4 (&y)[4], const f4 (&et)[4], const float *sA, float *scr, int lane) {
+__device__ void solve_upper_pc(f4 (&y)[4], const f4 (&et)[4], const float *sA, int lane) {
 #pragma unroll
   for (int b = 3; b >= 0; --b) {
     f4 s = zero4();
 #pragma unroll
     for (int bp = b + 1; bp < 4; ++bp) mmx<BF>(s, a_tr(sA, LD, 16 * b, 16 * bp, lane), y[bp]);
-    y[b] = pc_diag<true>(y[b] - et[b] * s, et[b], sA, b, scr, lane);
+    y[b] = pc_diag<true, BF>(y[b] - et[b] * s, et[b], sA, b, lane);
   }
 }
 
@@ -959,7 +938,6 @@ template <typename IT>
 __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
   constexpr bool BF = std::is_same_v<IT, __bf16>;   // bf16 inputs: products on bf16 MFMA
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[MAT], sP[MAT], sD[MAT];
-  __shared__ __attribute__((aligned(16))) float sScr[4][SCR];
   __shared__ RowScalars rs;
   const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
@@ -996,7 +974,7 @@ __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
     et[rt] = eta_tile(a, row0, live, rs, rt, w, lane);
     y[rt] = et[rt] * z;
   }
-  solve_upper_pc<BF>(y, et, sA, sScr[w], lane);
+  solve_upper_pc<BF>(y, et, sA, lane);
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     f4 d = y[rt];
@@ -1041,7 +1019,6 @@ __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
 // per-channel solve dR = M^-T B on wave 0, then G <- e^{L_C} G - (e^{Lm} (.) dR)^T X + Zc.
 __global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sX[MAT], sA[MAT], sG[16 * LD], sB[C * SP], sE[C * SP];
-  __shared__ __attribute__((aligned(16))) float sScr[SCR];
   __shared__ float sRV[2 * C];
   const int n = blockIdx.x >> 2, s = blockIdx.x & 3;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
@@ -1085,7 +1062,7 @@ __global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
         yy[bb] = b_rm(sB, SP, 16 * bb, 0, lane);
         et[bb] = b_rm(sE, SP, 16 * bb, 0, lane);
       }
-      solve_upper_pc<false>(yy, et, sA, sScr, lane);
+      solve_upper_pc<false>(yy, et, sA, lane);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
 #pragma unroll
@@ -1116,7 +1093,6 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   constexpr bool BF = std::is_same_v<IT, __bf16>;   // bf16 inputs: products on bf16 MFMA
   __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sS[MAT], sG[MAT], sA[MAT], sP[MAT], sE[MAT],
       sO[MAT];
-  __shared__ __attribute__((aligned(16))) float sScr[4][SCR];
   __shared__ RowScalars rs;
   __shared__ float pL[NWC][C], pE[NWC][C], pC[NWC], sCoef[C];
   const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
@@ -1195,7 +1171,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
       y4[bb] = b_rm(sE, LD, 16 * bb, 16 * w, lane);
       e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
     }
-    solve_lower_pc<BF>(y4, e4, sA, sScr[w], lane);
+    solve_lower_pc<BF>(y4, e4, sA, lane);
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) st_c(sE, LD, 16 * bb, 16 * w, lane, y4[bb]);
   }
@@ -1245,7 +1221,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
       y4[bb] = b_rm(sG, LD, 16 * bb, 16 * w, lane);
       e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
     }
-    solve_upper_pc<BF>(y4, e4, sA, sScr[w], lane);
+    solve_upper_pc<BF>(y4, e4, sA, lane);
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) st_c(sG, LD, 16 * bb, 16 * w, lane, y4[bb]);  // sG now holds dR
   }
