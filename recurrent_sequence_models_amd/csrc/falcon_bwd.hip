@@ -937,7 +937,9 @@ __device__ __forceinline__ f4 eta_tile(const BwdArgs &a, size_t row0, int live, 
 template <typename IT>
 __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
   constexpr bool BF = std::is_same_v<IT, __bf16>;   // bf16 inputs: products on bf16 MFMA
-  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[MAT], sP[MAT], sD[MAT];
+  // LDS: X, Qh (then do), A and P (then D): 70.7 KB, two workgroups per compute unit
+  __shared__ __attribute__((aligned(16))) float sX[MAT], sQ[MAT], sA[MAT], sP[MAT];
+  float *const sD = sP;
   __shared__ RowScalars rs;
   const int n = blockIdx.x / a.NC, c = blockIdx.x % a.NC;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
@@ -975,6 +977,7 @@ __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
     y[rt] = et[rt] * z;
   }
   solve_upper_pc<BF>(y, et, sA, lane);
+  __syncthreads();  // every wave is done reading P: D takes its place
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     f4 d = y[rt];
@@ -1017,6 +1020,10 @@ __global__ __launch_bounds__(256) void bwd_prep_f2(BwdArgs a) {
 // Workgroup (sequence n, value rows 16s..16s+15), chunks in reverse; wave w holds
 // key columns 16w..16w+15 of G.  Per chunk: Y^T = G X^T, B = eta (.) c (.) Y, the
 // per-channel solve dR = M^-T B on wave 0, then G <- e^{L_C} G - (e^{Lm} (.) dR)^T X + Zc.
+// The next chunk's X, A, steps, row factors and Zc are fetched into registers
+// while the current chunk is reduced.  G and its two products stay on fp32 MFMA;
+// BF (bf16 inputs) puts the solve's coupling sweeps on bf16 MFMA, as in bwd_chunk_f2.
+template <bool BF>
 __global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sX[MAT], sA[MAT], sG[16 * LD], sB[C * SP], sE[C * SP];
   __shared__ float sRV[2 * C];
@@ -1029,6 +1036,26 @@ __global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) G[i] = a.dST[(size_t)n * D * D + tile + i * D];
   }
+  f4 nx[4], na[4], nz;
+  float ne[4], nrv, ndec;
+  auto fetch = [&](int c) {
+    const WsF2 ws = ws_f2(a, (size_t)n * a.NC + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      nx[j] = *reinterpret_cast<const f4 *>(ws.X + r * D + 16 * p + 4 * j);
+      na[j] = *reinterpret_cast<const f4 *>(ws.A + r * C + 16 * p + 4 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid + 256 * j;   // C x 16 steps of this slice's channels
+      ne[j] = ws.ETA[(e >> 4) * D + 16 * s + (e & 15)];
+    }
+    nrv = tid < 2 * C ? ws.RV[tid] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nz[i] = ws.Zc[tile + i * D];
+    ndec = *ws.dec;
+  };
+  fetch(a.NC - 1);
   for (int c = a.NC - 1; c >= 0; --c) {
     const WsF2 ws = ws_f2(a, (size_t)n * a.NC + c);
 #pragma unroll
@@ -1036,13 +1063,20 @@ __global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
     __syncthreads();  // the previous chunk's readers are done
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<f4 *>(sX + r * LD + 16 * p + 4 * j) = *reinterpret_cast<const f4 *>(ws.X + r * D + 16 * p + 4 * j);
-      *reinterpret_cast<f4 *>(sA + r * LD + 16 * p + 4 * j) = *reinterpret_cast<const f4 *>(ws.A + r * C + 16 * p + 4 * j);
+      *reinterpret_cast<f4 *>(sX + r * LD + 16 * p + 4 * j) = nx[j];
+      *reinterpret_cast<f4 *>(sA + r * LD + 16 * p + 4 * j) = na[j];
     }
-    for (int e = tid; e < C * 16; e += 256) sE[(e >> 4) * SP + (e & 15)] = ws.ETA[(e >> 4) * D + 16 * s + (e & 15)];
-    if (tid < 2 * C) sRV[tid] = ws.RV[tid];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid + 256 * j;
+      sE[(e >> 4) * SP + (e & 15)] = ne[j];
+    }
+    if (tid < 2 * C) sRV[tid] = nrv;
+    const f4 Zc = nz;
+    const float dec = ndec;
     st_c(sG, LD, 0, 16 * w, lane, G);
     __syncthreads();
+    if (c > 0) fetch(c - 1);   // in flight during this chunk's products
     {  // (G X^T) tile: channels 16s.., chunk rows 16w..; B = eta (.) c (.) Y into sB [row][channel]
       f4 y = zero4();
 #pragma unroll
@@ -1062,7 +1096,7 @@ __global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
         yy[bb] = b_rm(sB, SP, 16 * bb, 0, lane);
         et[bb] = b_rm(sE, SP, 16 * bb, 0, lane);
       }
-      solve_upper_pc<false>(yy, et, sA, lane);
+      solve_upper_pc<BF>(yy, et, sA, lane);
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
 #pragma unroll
@@ -1074,10 +1108,7 @@ __global__ __launch_bounds__(256) void bwd_scan_f2(BwdArgs a) {
     f4 u = zero4();  // (e^{Lm} (.) dR)^T X: channels 16s.., key columns 16w..
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) mma16(u, a_tr(sB, SP, 0, 16 * kb, lane), b_rm(sX, LD, 16 * kb, 16 * w, lane));
-    f4 Zc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Zc[i] = ws.Zc[tile + i * D];
-    G = *ws.dec * G - u + Zc;
+    G = dec * G - u + Zc;
   }
   if (a.dS0) {
 #pragma unroll
@@ -1371,7 +1402,7 @@ hipError_t launch_bwd_f2(const BwdArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_prep_f2<IT>), dim3(nch), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_scan_f2, dim3((unsigned)a.B * a.H * 4), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_scan_f2<std::is_same_v<IT, __bf16>>), dim3((unsigned)a.B * a.H * 4), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_chunk_f2<IT>), dim3(nch), dim3(NTC), 0, st, a);
