@@ -113,6 +113,7 @@ __device__ __forceinline__ float sum64(float x) { return sum4g(sum16(x)); }
 // 64 / NP channels, NP = NTH / 64.
 struct RowScalars {
   float L[C], Lm[C], eta[C], en[C];  // L_i, L_{i-1}, eta_i, eps_eta + |x_i|^2
+  float ik[C], iq[C];                // 1/|k| of row i's key (0 unless it is one) and 1/|q_i| (0 past T)
 };
 
 template <int NP>
@@ -170,6 +171,8 @@ __device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, 
     const size_t gi = (size_t)(b * a.T + t) * a.H + h;
     const float en = a.eps_eta + e;
     rs.en[r] = en;
+    rs.ik[r] = key_row ? ix : 0.f;
+    rs.iq[r] = live ? iq : 0.f;
     rs.eta[r] = live ? (UNIT ? 1.f : a.beta[gi]) / en : 0.f;
     rs.L[r] = live ? fmaxf(a.g[gi], a.log_eps_gamma) : 0.f;  // log-decay, summed below
   }
@@ -559,70 +562,54 @@ __device__ void adjoint_tile(float *sA, float *sP, const float *sG, const float 
 
 // The gradients of the rows' features taken through the feature map phi: dq_t
 // from dQh (sO) for t < T, and dk of the key row r carries from dX (sE), plus the
-// carried x_prev's gradient.  1024 threads, one chunk.
-template <typename IT>
+// carried x_prev's gradient.  With u^ = u / sqrt(|u|^2 + eps) the normalised row
+// (sQ, sX) and s = 1 / sqrt(|u|^2 + eps) (rs.iq, rs.ik), the adjoint of
+// phi is s (d - u^ (u^ . d)), so nothing is read back from memory.  1024 threads,
+// one chunk.
 __device__ void through_phi(const BwdArgs &a, int n, int c, size_t row0, int b, int h, const float *sO,
-                            const float *sE) {
+                            const float *sE, const float *sX, const float *sQ, const RowScalars &rs) {
   const int tid = threadIdx.x;
   constexpr int NP = NTC / 64, EE = 64 / NP;
   const int r = tid / NP, p = tid % NP;
   const int t = c * C + r;
-  float v[EE], d[EE];
-  if (t < a.T) {
-    load_e<IT, EE>((const IT *)a.q + (row0 + (size_t)r * a.H) * D + EE * p, v);
-#pragma unroll
-    for (int j = 0; j < EE; ++j) d[j] = sO[r * LD + EE * p + j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < EE; ++j) v[j] = d[j] = 0.f;
-  }
-  float nn = 0.f, dot = 0.f;
+  float u[EE], d[EE];
 #pragma unroll
   for (int j = 0; j < EE; ++j) {
-    nn += v[j] * v[j];
-    dot += v[j] * d[j];
+    u[j] = sQ[r * LD + EE * p + j];
+    d[j] = sO[r * LD + EE * p + j];
   }
-  nn = sum_parts<NP>(nn);
+  float dot = 0.f;
+#pragma unroll
+  for (int j = 0; j < EE; ++j) dot += u[j] * d[j];
   dot = sum_parts<NP>(dot);
-  float inv = 1.f / sqrtf(nn + a.eps_phi);
-  float inv3 = inv * inv * inv;
   if (t < a.T) {
+    const float s = rs.iq[r];
     float *dst = a.dq + (row0 + (size_t)r * a.H) * D + EE * p;
 #pragma unroll
     for (int j = 0; j < EE; j += 4)
-      *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
-                                            d[j + 2] * inv - v[j + 2] * dot * inv3,
-                                            d[j + 3] * inv - v[j + 3] * dot * inv3};
+      *reinterpret_cast<f4 *>(dst + j) = f4{s * (d[j] - u[j] * dot), s * (d[j + 1] - u[j + 1] * dot),
+                                            s * (d[j + 2] - u[j + 2] * dot), s * (d[j + 3] - u[j + 3] * dot)};
   }
   // key of row r: k_{t-1+align}; under the prefix pairing the row at t == T
-  // carries k_{T-1}, whose gradient is 0 (that row's dX is 0).
+  // carries k_{T-1}, whose gradient is 0 (that row's dX is 0; rs.ik is 0 there).
   const int kt = t - 1 + a.align;
   const bool key_row = kt >= 0 && kt < a.T && t <= a.T - a.align;
 #pragma unroll
-  for (int j = 0; j < EE; ++j) d[j] = sE[r * LD + EE * p + j];
-  if (key_row) load_e<IT, EE>((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + EE * p, v);
-  else {
-#pragma unroll
-    for (int j = 0; j < EE; ++j) v[j] = 0.f;
+  for (int j = 0; j < EE; ++j) {
+    u[j] = sX[r * LD + EE * p + j];
+    d[j] = sE[r * LD + EE * p + j];
   }
-  nn = 0.f;
   dot = 0.f;
 #pragma unroll
-  for (int j = 0; j < EE; ++j) {
-    nn += v[j] * v[j];
-    dot += v[j] * d[j];
-  }
-  nn = sum_parts<NP>(nn);
+  for (int j = 0; j < EE; ++j) dot += u[j] * d[j];
   dot = sum_parts<NP>(dot);
-  inv = 1.f / sqrtf(nn + a.eps_phi);
-  inv3 = inv * inv * inv;
   if (key_row) {
+    const float s = rs.ik[r];
     float *dst = a.dk + ((size_t)(b * a.T + kt) * a.H + h) * D + EE * p;
 #pragma unroll
     for (int j = 0; j < EE; j += 4)
-      *reinterpret_cast<f4 *>(dst + j) = f4{d[j] * inv - v[j] * dot * inv3, d[j + 1] * inv - v[j + 1] * dot * inv3,
-                                            d[j + 2] * inv - v[j + 2] * dot * inv3,
-                                            d[j + 3] * inv - v[j + 3] * dot * inv3};
+      *reinterpret_cast<f4 *>(dst + j) = f4{s * (d[j] - u[j] * dot), s * (d[j + 1] - u[j + 1] * dot),
+                                            s * (d[j + 2] - u[j + 2] * dot), s * (d[j + 3] - u[j + 3] * dot)};
   }
   if (t == 0 && a.dxprev0) {  // the carried x_prev is row 0's key (prefix); unread under same-step pairs
     float *dst = a.dxprev0 + (size_t)n * D + EE * p;
@@ -856,7 +843,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   st_c(sE, LD, 16 * rt, 16 * ct, lane, dX);
   __syncthreads();
 
-  through_phi<IT>(a, n, c, row0, b, h, sO, sE);
+  through_phi(a, n, c, row0, b, h, sO, sE, sX, sQ, rs);
 }
 
 // ================= Falcon-2: per-value-channel steps =================
@@ -1155,6 +1142,11 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   }
   load_rows<IT, NTC, true>(a, n, c, sX, sQ, rs);  // rs.eta = 1 / (eps_eta + |x|^2); ends with a barrier
   const f4 ET = eta_tile(a, row0, live, rs, rt, ct, lane);   // this tile's per-channel steps
+  f4 e4[4];   // solver waves: the steps of their column tile, loaded ahead of both solves
+  if (w < 4) {
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
+  }
   const float LC = rs.L[C - 1];
   float lc = 0.f;
   {
@@ -1196,12 +1188,9 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   st_c(sE, LD, 16 * rt, 16 * ct, lane, E);  // R
   __syncthreads();                           // A, P and R are complete
   if (w < 4) {
-    f4 y4[4], e4[4];
+    f4 y4[4];
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      y4[bb] = b_rm(sE, LD, 16 * bb, 16 * w, lane);
-      e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
-    }
+    for (int bb = 0; bb < 4; ++bb) y4[bb] = b_rm(sE, LD, 16 * bb, 16 * w, lane);
     solve_lower_pc<BF>(y4, e4, sA, lane);
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) st_c(sE, LD, 16 * bb, 16 * w, lane, y4[bb]);
@@ -1246,12 +1235,9 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   st_c(sG, LD, 16 * rt, 16 * ct, lane, dE);
   __syncthreads();
   if (w < 4) {
-    f4 y4[4], e4[4];
+    f4 y4[4];
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      y4[bb] = b_rm(sG, LD, 16 * bb, 16 * w, lane);
-      e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
-    }
+    for (int bb = 0; bb < 4; ++bb) y4[bb] = b_rm(sG, LD, 16 * bb, 16 * w, lane);
     solve_upper_pc<BF>(y4, e4, sA, lane);
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) st_c(sG, LD, 16 * bb, 16 * w, lane, y4[bb]);  // sG now holds dR
@@ -1380,7 +1366,7 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   st_c(sO, LD, 16 * rt, 16 * ct, lane, dQ);
   st_c(sE, LD, 16 * rt, 16 * ct, lane, dX);
   __syncthreads();
-  through_phi<IT>(a, n, c, row0, b, h, sO, sE);
+  through_phi(a, n, c, row0, b, h, sO, sE, sX, sQ, rs);
 }
 
 template <typename IT, bool ADD, bool PC = false>
