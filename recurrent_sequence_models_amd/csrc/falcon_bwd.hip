@@ -129,26 +129,49 @@ __device__ __forceinline__ void load_e(const IT *p, float (&v)[E]) {
   for (int j = 0; j < E; ++j) v[j] = (float)p[j];
 }
 
-template <typename IT, int NTH, bool UNIT = false>   // UNIT: eta = 1 / (eps_eta + |x|^2) (Falcon-2A)
-__device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, RowScalars &rs) {
+// One thread's share of a chunk's key and query rows and of its per-row gain and
+// log-decay, read from global memory ahead of their use (fetch_rows), so that a
+// kernel can issue these loads together with its others before waiting on any.
+template <int NTH>
+struct Rows {
+  static constexpr int NP = NTH / 64, E = 64 / NP;
+  float x[E], q[E], beta, g;
+};
+
+template <typename IT, int NTH>
+__device__ void fetch_rows(const BwdArgs &a, int n, int c, Rows<NTH> &R) {
   constexpr int NP = NTH / 64, E = 64 / NP;
-  const int tid = threadIdx.x, r = tid / NP, p = tid % NP, lane = tid & 63;
+  const int tid = threadIdx.x, r = tid / NP, p = tid % NP;
   const int b = n / a.H, h = n % a.H;
   const int t = c * C + r;
   const int kt = t - 1 + a.align;  // key index of the pair written at step t
   const bool live = t < a.T;
-  float x[E], q[E];
 #pragma unroll
-  for (int j = 0; j < E; ++j) x[j] = q[j] = 0.f;
+  for (int j = 0; j < E; ++j) R.x[j] = R.q[j] = 0.f;
   const bool key_row = live && kt >= 0;
-  if (key_row) load_e<IT, E>((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + E * p, x);
-  else if (live && a.xprev0) load_e<float, E>(a.xprev0 + (size_t)n * D + E * p, x);  // the carried feature
-  if (live) load_e<IT, E>((const IT *)a.q + ((size_t)(b * a.T + t) * a.H + h) * D + E * p, q);
+  if (key_row) load_e<IT, E>((const IT *)a.k + ((size_t)(b * a.T + kt) * a.H + h) * D + E * p, R.x);
+  else if (live && a.xprev0) load_e<float, E>(a.xprev0 + (size_t)n * D + E * p, R.x);  // the carried feature
+  if (live) load_e<IT, E>((const IT *)a.q + ((size_t)(b * a.T + t) * a.H + h) * D + E * p, R.q);
+  const size_t gi = (size_t)(b * a.T + t) * a.H + h;
+  R.beta = (live && p == 0) ? a.beta[gi] : 0.f;
+  R.g = (live && p == 0) ? a.g[gi] : 0.f;
+}
+
+// The rows into LDS: normalised keys X and queries Qh, and the per-row scalars
+// (the log-decays summed along the chunk).  Ends with a barrier.
+template <int NTH, bool UNIT = false>   // UNIT: eta = 1 / (eps_eta + |x|^2) (Falcon-2A)
+__device__ void stage_rows(const BwdArgs &a, int c, Rows<NTH> &R, float *sX, float *sQ, RowScalars &rs) {
+  constexpr int NP = NTH / 64, E = 64 / NP;
+  const int tid = threadIdx.x, r = tid / NP, p = tid % NP, lane = tid & 63;
+  const int t = c * C + r;
+  const int kt = t - 1 + a.align;
+  const bool live = t < a.T;
+  const bool key_row = live && kt >= 0;
   float sx = 0.f, sq = 0.f;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    sx += x[j] * x[j];
-    sq += q[j] * q[j];
+    sx += R.x[j] * R.x[j];
+    sq += R.q[j] * R.q[j];
   }
   sx = sum_parts<NP>(sx);
   sq = sum_parts<NP>(sq);
@@ -157,24 +180,23 @@ __device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, 
   float e = 0.f;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    x[j] *= ix;
-    q[j] = live ? q[j] * iq : 0.f;
-    e += x[j] * x[j];
+    R.x[j] *= ix;
+    R.q[j] = live ? R.q[j] * iq : 0.f;
+    e += R.x[j] * R.x[j];
   }
   e = sum_parts<NP>(e);
 #pragma unroll
   for (int j = 0; j < E; j += 4) {
-    *reinterpret_cast<f4 *>(sX + r * LD + E * p + j) = f4{x[j], x[j + 1], x[j + 2], x[j + 3]};
-    *reinterpret_cast<f4 *>(sQ + r * LD + E * p + j) = f4{q[j], q[j + 1], q[j + 2], q[j + 3]};
+    *reinterpret_cast<f4 *>(sX + r * LD + E * p + j) = f4{R.x[j], R.x[j + 1], R.x[j + 2], R.x[j + 3]};
+    *reinterpret_cast<f4 *>(sQ + r * LD + E * p + j) = f4{R.q[j], R.q[j + 1], R.q[j + 2], R.q[j + 3]};
   }
   if (p == 0) {
-    const size_t gi = (size_t)(b * a.T + t) * a.H + h;
     const float en = a.eps_eta + e;
     rs.en[r] = en;
     rs.ik[r] = key_row ? ix : 0.f;
     rs.iq[r] = live ? iq : 0.f;
-    rs.eta[r] = live ? (UNIT ? 1.f : a.beta[gi]) / en : 0.f;
-    rs.L[r] = live ? fmaxf(a.g[gi], a.log_eps_gamma) : 0.f;  // log-decay, summed below
+    rs.eta[r] = live ? (UNIT ? 1.f : R.beta) / en : 0.f;
+    rs.L[r] = live ? fmaxf(R.g, a.log_eps_gamma) : 0.f;  // log-decay, summed below
   }
   __syncthreads();
   if (tid < 64) {  // inclusive prefix sum of the log-decays along the chunk
@@ -189,6 +211,13 @@ __device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, 
     rs.Lm[lane] = lane ? lm : 0.f;
   }
   __syncthreads();
+}
+
+template <typename IT, int NTH, bool UNIT = false>
+__device__ void load_rows(const BwdArgs &a, int n, int c, float *sX, float *sQ, RowScalars &rs) {
+  Rows<NTH> R;
+  fetch_rows<IT, NTH>(a, n, c, R);
+  stage_rows<NTH, UNIT>(a, c, R, sX, sQ, rs);
 }
 
 // One 16x16 tile (rt, ct <= rt) of A (skipped for F1A) and P into LDS, with
@@ -639,29 +668,35 @@ __global__ __launch_bounds__(NTC) void bwd_chunk(BwdArgs a) {
   const size_t row0 = (size_t)(b * a.T + c * C) * a.H + h;  // (b, t0, h)
   const WsPtr ws = ws_of(a, blockIdx.x);
 
-  // Phase 0: do, the incoming state S0, the end-state gradient G, v, the rows.
+  // Phase 0: the rows, do, the incoming state S0, the end-state gradient G and v.
+  // Every global read is issued before the first is used, so they share one
+  // round trip.
+  Rows<NTC> rows;
+  fetch_rows<IT, NTC>(a, n, c, rows);
+  f4 V, Vraw, Bch;   // Falcon-2A: the value beta (.) v, and v and beta themselves
   {
     RowShare<NTC> rO;
     rO.load((const IT *)a.dO + row0 * D, (size_t)a.H * D, live);
     const float *S0 = c ? a.chunk_states + ((size_t)n * a.cs_nc + (size_t)c * (C / a.cs_step) - 1) * D * D
                         : (a.S0 ? a.S0 + (size_t)n * D * D : nullptr);
     const int r = tid >> 4, p = tid & 15;
-    *reinterpret_cast<f4 *>(sS + r * LD + 4 * p) = S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 4 * p) : zero4();
-    *reinterpret_cast<f4 *>(sG + r * LD + 4 * p) = *reinterpret_cast<const f4 *>(ws.G + r * D + 4 * p);
+    const f4 s0v = S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 4 * p) : zero4();
+    const f4 gv = *reinterpret_cast<const f4 *>(ws.G + r * D + 4 * p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      const size_t e = (row0 + (size_t)row * a.H) * D + 16 * ct + cc;
+      Vraw[i] = row < live ? (float)((const IT *)a.v)[e] : 0.f;
+      Bch[i] = (PC && row < live) ? a.beta[e] : 0.f;
+      V[i] = PC ? Bch[i] * Vraw[i] : Vraw[i];
+    }
+    *reinterpret_cast<f4 *>(sS + r * LD + 4 * p) = s0v;
+    *reinterpret_cast<f4 *>(sG + r * LD + 4 * p) = gv;
     rO.store(sO);
     pL[w][lane] = 0.f;
     pE[w][lane] = 0.f;
   }
-  f4 V, Vraw, Bch;   // Falcon-2A: the value beta (.) v, and v and beta themselves
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * rt + 4 * g + i;
-    const size_t e = (row0 + (size_t)row * a.H) * D + 16 * ct + cc;
-    Vraw[i] = row < live ? (float)((const IT *)a.v)[e] : 0.f;
-    Bch[i] = (PC && row < live) ? a.beta[e] : 0.f;
-    V[i] = PC ? Bch[i] * Vraw[i] : Vraw[i];
-  }
-  load_rows<IT, NTC, PC>(a, n, c, sX, sQ, rs);  // ends with a barrier
+  stage_rows<NTC, PC>(a, c, rows, sX, sQ, rs);  // ends with a barrier
   const float LC = rs.L[C - 1];
   float lc = 0.f;  // this lane's share of dL_C
   {
@@ -904,6 +939,23 @@ __device__ void solve_upper_pc(f4 (&y)[4], const f4 (&et)[4], const float *sA, i
   }
 }
 
+// Gains beta[t][ch] of the C-layout tile (rows 16rt + 4g + i, channels 16ct + c);
+// zero past the sequence.  steps_of turns them into eta = beta / (eps_eta + |x|^2).
+__device__ __forceinline__ f4 beta_tile(const BwdArgs &a, size_t row0, int live, int rt, int ct, int lane) {
+  const int g = lane >> 4, cc = lane & 15;
+  f4 e;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * rt + 4 * g + i;
+    e[i] = row < live ? a.beta[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] : 0.f;
+  }
+  return e;
+}
+__device__ __forceinline__ f4 steps_of(const f4 &beta, const RowScalars &rs, int rt, int lane) {
+  const float *er = rs.eta + 16 * rt + 4 * (lane >> 4);
+  return f4{beta[0] * er[0], beta[1] * er[1], beta[2] * er[2], beta[3] * er[3]};
+}
+
 // Steps eta[i][ch] = beta[t][ch] / (eps_eta + |x_i|^2) of the C-layout tile
 // (rows 16rt + 4g + i, channels 16ct + c); zero past the sequence.
 __device__ __forceinline__ f4 eta_tile(const BwdArgs &a, size_t row0, int live, const RowScalars &rs, int rt, int ct,
@@ -1121,31 +1173,41 @@ __global__ __launch_bounds__(NTC) void bwd_chunk_f2(BwdArgs a) {
   const size_t row0 = (size_t)(b * a.T + c * C) * a.H + h;
   const WsF2 ws = ws_f2(a, blockIdx.x);
 
-  // Phase 0: do, the incoming state S0, the end-state gradient G, v, the rows.
+  // Phase 0: the rows, the gains, do, the incoming state S0, the end-state
+  // gradient G and v.  Every global read is issued before the first is used.
+  Rows<NTC> R;
+  fetch_rows<IT, NTC>(a, n, c, R);
+  f4 ET = beta_tile(a, row0, live, rt, ct, lane);   // this tile's gains (steps below)
+  f4 e4[4];   // solver waves: the gains, then the steps, of their column tile
+  if (w < 4) {
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) e4[bb] = beta_tile(a, row0, live, bb, w, lane);
+  }
+  f4 V;
   {
     RowShare<NTC> rO;
     rO.load((const IT *)a.dO + row0 * D, (size_t)a.H * D, live);
     const float *S0 = c ? a.chunk_states + ((size_t)n * a.cs_nc + (size_t)c * (C / a.cs_step) - 1) * D * D
                         : (a.S0 ? a.S0 + (size_t)n * D * D : nullptr);
     const int r = tid >> 4, p = tid & 15;
-    *reinterpret_cast<f4 *>(sS + r * LD + 4 * p) = S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 4 * p) : zero4();
-    *reinterpret_cast<f4 *>(sG + r * LD + 4 * p) = *reinterpret_cast<const f4 *>(ws.G + r * D + 4 * p);
+    const f4 s0v = S0 ? *reinterpret_cast<const f4 *>(S0 + r * D + 4 * p) : zero4();
+    const f4 gv = *reinterpret_cast<const f4 *>(ws.G + r * D + 4 * p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * rt + 4 * g + i;
+      V[i] = row < live ? (float)((const IT *)a.v)[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] : 0.f;
+    }
+    *reinterpret_cast<f4 *>(sS + r * LD + 4 * p) = s0v;
+    *reinterpret_cast<f4 *>(sG + r * LD + 4 * p) = gv;
     rO.store(sO);
     pL[w][lane] = 0.f;
     pE[w][lane] = 0.f;
   }
-  f4 V;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * rt + 4 * g + i;
-    V[i] = row < live ? (float)((const IT *)a.v)[(row0 + (size_t)row * a.H) * D + 16 * ct + cc] : 0.f;
-  }
-  load_rows<IT, NTC, true>(a, n, c, sX, sQ, rs);  // rs.eta = 1 / (eps_eta + |x|^2); ends with a barrier
-  const f4 ET = eta_tile(a, row0, live, rs, rt, ct, lane);   // this tile's per-channel steps
-  f4 e4[4];   // solver waves: the steps of their column tile, loaded ahead of both solves
+  stage_rows<NTC, true>(a, c, R, sX, sQ, rs);  // rs.eta = 1 / (eps_eta + |x|^2); ends with a barrier
+  ET = steps_of(ET, rs, rt, lane);
   if (w < 4) {
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) e4[bb] = eta_tile(a, row0, live, rs, bb, w, lane);
+    for (int bb = 0; bb < 4; ++bb) e4[bb] = steps_of(e4[bb], rs, bb, lane);
   }
   const float LC = rs.L[C - 1];
   float lc = 0.f;
