@@ -31,10 +31,12 @@
 //
 // Image of one system (bytes, tiles in the input dtype, fragment pairs of 64
 // lanes x 8 elements; slots hold only the tiles that exist):
-//   A   : A_pq, q < p (F1 / F2 / F3)  -- pair slot aslot_base(p) + q/2, half q&1
+//   A   : A_pq, q < p (F1 / F2 / F3)  -- pair slot aslot_base(p) + q/2, half q&1;
+//         in the prep kernel's F1 / F3 images the blocks T_pq of T = (I + A)^{-1}
+//         instead, with T_pp also in the free upper half of odd p's last slot
 //   P   : P_pq (step block p, virtual-row block q <= qmax(p))
 //                                      -- pair slot pbase(p) + q/2, half q&1
-//   T   : F1 / F3: T_pp = (I + A_pp)^{-1}; F2: A_pp without its 4x4 diagonal
+//   T   : F1 / F3: T_pp = (I + A_pp)^{-1} (the diagonal blocks of T); F2: A_pp without its 4x4 diagonal
 //         sub-blocks; one fragment per diagonal block
 //   AD  : F2 only, the 6 coefficients of each 4x4 diagonal sub-block (8 floats)
 //   F   : per-row GAM, EL, CST, ETA (fp32, C each) and e^{L_last}
@@ -114,7 +116,11 @@ struct Split {
   // prep kernel: 4 waves, one system
   static constexpr int NPW = 4, NPT = 256;
   static constexpr int RPP = NPT / TPR, NPASS = (C + RPP - 1) / RPP;
-  static constexpr size_t prep_lds() { return (size_t)SZ * (C + CSP) * LX + 4 * R_N * C; }
+  // the prep kernel of F1 / F3 also keeps the Gram blocks and T_pp in LDS to
+  // complete the inverse of the system matrix (complete_inverse), over the rows
+  static constexpr int LAT = SDELTA ? NSA * FRAG + NB * 256 : 1;
+  static constexpr int PXQ = (C + CSP) * LX > LAT ? (C + CSP) * LX : LAT;   // rows X, Q (then the tiles)
+  static constexpr size_t prep_lds() { return (size_t)SZ * PXQ + 4 * R_N * C; }
   __host__ __device__ static int nsys(int T) { return (T + CS - 1) / CS; }
   static size_t workspace(int bh, int T) { return (size_t)bh * nsys(T) * IMG + (size_t)bh * CARRY; }
   // Packed sequences (cu_seqlens): per head, sequence n's systems take image slots
@@ -238,9 +244,9 @@ __device__ __forceinline__ uint4 scale_pack(const float *x, float f) {
 // twice, for separable (L_last >= -160) and per-element decay factors, so each
 // version is one straight-line block in which the diagonal solve and the
 // other tiles' finishing interleave.
-template <int VAR, typename IT, int D, int C, int BW, typename RowsFn>
+template <int VAR, typename IT, int D, int C, int BW, bool LA = false, typename RowsFn>
 __device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const float *G, unsigned char *img, int w,
-                                             int lane, RowsFn &&rows) {
+                                             int lane, RowsFn &&rows, IT *lat = nullptr) {
   using S = Split<VAR, IT, D, C, BW>;
   using OpT = IT;
   using Frag = typename Op<OpT>::frag;
@@ -248,9 +254,13 @@ __device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const flo
   constexpr int NB = S::NB, NA = S::NA, LX = S::LX, CS = S::CS, CSP = S::CSP, RLQ = S::RLQ;
   constexpr bool DELTA = S::DELTA;
   const int g4 = lane >> 4, cl = lane & 15;
-  OpT *gA = reinterpret_cast<OpT *>(img + S::OFF_A);
+  // LA: the Gram blocks and the diagonal-block inverses go to `lat` (LDS, the A
+  // slots followed by the T fragments) for complete_inverse instead of the image;
+  // it is written only after a workgroup barrier that follows the tile products
+  // (all NPW waves call this once), so it may overlay the rows X and Q
+  OpT *gA = LA ? lat : reinterpret_cast<OpT *>(img + S::OFF_A);
   OpT *gP = reinterpret_cast<OpT *>(img + S::OFF_P);
-  OpT *gT = reinterpret_cast<OpT *>(img + S::OFF_T);
+  OpT *gT = LA ? lat + S::NSA * S::FRAG : reinterpret_cast<OpT *>(img + S::OFF_T);
   float *gAd = reinterpret_cast<float *>(img + S::OFF_AD);
   float *gF = reinterpret_cast<float *>(img + S::OFF_F);
   (void)CS;
@@ -393,6 +403,8 @@ __device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const flo
 #pragma unroll
     for (int j = 0; j < J.n; ++j) acc[j] = tile(Aop[j], Bop[j]);
     const float Llast = rows();
+    // LA: `lat` may share LDS with the rows; every wave's products are done
+    if constexpr (LA) __syncthreads();
     auto tail = [&](auto sepc) __attribute__((always_inline)) {
       if constexpr (J.diag >= 0) diag(sepc, dacc, J.diag);
 #pragma unroll
@@ -408,6 +420,57 @@ __device__ __forceinline__ void derive_image(const IT *X, const IT *Q, const flo
   else run(std::integral_constant<int, 3>());
 }
 
+// Whole inverse of a system's matrix M = I + A (F1 / F3: A holds the decayed,
+// step-weighted Gram blocks, so E = M^{-1} R is the WY solve of [P1] 三种等价形式
+// form C), from the Gram blocks and the diagonal-block inverses T_pp that
+// derive_image left in LDS (`lat`).  Block column q of T = M^{-1} follows by
+// forward substitution down the column,
+//   T_pq = -T_pp sum_{r=q}^{p-1} A_pr T_rq,   p > q,
+// so wave q takes column q on its own, with no exchange between waves.  Each
+// block is formed twice from the same operands: in C-layout (the right operand
+// of the next block's products) and transposed, whose C-layout is the A-layout
+// fragment the scan reads.  The image then holds T_pq in the A slots, and T_pp
+// in T and, for odd p, in the free upper half of the slot of A_{p,p-1}, so that
+// the scan forms E = T R with every product independent of the others.
+template <int VAR, typename IT, int D, int C, int BW>
+__device__ __forceinline__ void complete_inverse(const IT *lat, unsigned char *img, int w, int lane) {
+  using S = Split<VAR, IT, D, C, BW>;
+  using OpT = IT;
+  using Frag = typename Op<OpT>::frag;
+  constexpr int NB = S::NB;
+  const int g4 = lane >> 4, cl = lane & 15;
+  const OpT *lA = lat, *lT = lat + S::NSA * S::FRAG;
+  OpT *gA = reinterpret_cast<OpT *>(img + S::OFF_A);
+  OpT *gT = reinterpret_cast<OpT *>(img + S::OFF_T);
+  auto column = [&](auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    const Frag tqq = ld4(lT + (q * 64 + lane) * 4);
+    *reinterpret_cast<Frag *>(gT + (q * 64 + lane) * 4) = tqq;
+    if constexpr (q & 1) *reinterpret_cast<Frag *>(gA + frag_off(aslot_base(q), q, lane)) = tqq;
+    // C-layout of T_qq: element (4g+i, c) sits in lane 16(c/4) + 4g + i, entry c%4, of the A-layout
+    f4 Tc[NB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Tc[q][i] = (float)lT[(q * 64 + 16 * (cl >> 2) + 4 * g4 + i) * 4 + (cl & 3)];
+#pragma unroll
+    for (int p = q + 1; p < NB; ++p) {
+      f4 sacc = zero4();   // sum_{r=q}^{p-1} A_pr T_rq, C-layout
+#pragma unroll
+      for (int r = q; r < p; ++r) mma16(sacc, ld4(lA + frag_off(aslot_base(p), r, lane)), cvt<OpT>(Tc[r]));
+      const Frag sb = cvt<OpT>(sacc);
+      const Frag tpp = ld4(lT + (p * 64 + lane) * 4);
+      f4 tc = zero4(), tt = zero4();
+      mma16(tc, tpp, sb);   // T_pp S: C-layout of -T_pq
+      mma16(tt, sb, tpp);   // S^T T_pp^T: C-layout of -T_pq^T = A-layout of -T_pq
+      Tc[p] = -tc;
+      *reinterpret_cast<Frag *>(gA + frag_off(aslot_base(p), q, lane)) = cvt<OpT>(-tt);
+    }
+  };
+  if (w == 0) column(std::integral_constant<int, 0>());
+  if constexpr (NB > 1) if (w == 1) column(std::integral_constant<int, 1>());
+  if constexpr (NB > 2) if (w == 2) column(std::integral_constant<int, 2>());
+  if constexpr (NB > 3) if (w == 3) column(std::integral_constant<int, 3>());
+}
+
 // ============================== prep kernel ==============================
 template <int VAR, typename IT, int D, int C, int BW>
 __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) {
@@ -419,8 +482,9 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
   constexpr int CS = S::CS, CSP = S::CSP, RLQ = S::RLQ;
   constexpr bool PERCH = S::PERCH, DELTA = S::DELTA;
 
-  __shared__ __attribute__((aligned(16))) OpT sX[C * LX];     // raw key of each virtual row, dk permuted
-  __shared__ __attribute__((aligned(16))) OpT sQ[CSP * LX];   // raw q of each step row, dk permuted
+  __shared__ __attribute__((aligned(16))) OpT sXQ[S::PXQ];
+  OpT *const sX = sXQ;              // raw key of each virtual row, dk permuted
+  OpT *const sQ = sXQ + C * LX;     // raw q of each step row, dk permuted
   __shared__ __attribute__((aligned(16))) float sR[R_N * C];
 
   const int tid = threadIdx.x, lane = tid & 63, pw = tid >> 6;
@@ -621,7 +685,13 @@ __global__ __launch_bounds__(256) void chunk_prep(FwdArgs a, unsigned char *ws) 
   }
   __syncthreads();
 
-  derive_image<VAR, IT, D, C, BW>(sX, sQ, sR, img, pw, lane, [&]() { return Llast; });
+  if constexpr (S::SDELTA) {   // Gram blocks and T_pp of the system over the rows, then T
+    derive_image<VAR, IT, D, C, BW, true>(sX, sQ, sR, img, pw, lane, [&]() { return Llast; }, sXQ);
+    __syncthreads();
+    complete_inverse<VAR, IT, D, C, BW>(sXQ, img, pw, lane);
+  } else {
+    derive_image<VAR, IT, D, C, BW>(sX, sQ, sR, img, pw, lane, [&]() { return Llast; });
+  }
 }
 
 // ============================== scan kernel ==============================
@@ -638,6 +708,7 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE, MAPS>::NT)) void 
   constexpr int CS = S::CS, CSP = S::CSP, NBS = S::NBS, NXS = Z::NXS, NDW = Z::NDW, NOW = Z::NOW;
   constexpr int NQS = Z::NQS > 0 ? Z::NQS : 1;   // query slots (one unused slot in the map form)
   constexpr bool PERCH = S::PERCH, DELTA = S::DELTA;
+  constexpr bool FULLT = S::SDELTA && !ONE;   // the image holds the blocks of M^{-1} (complete_inverse)
 
   // Raw operands (dk permuted); the per-row factors are applied to the products,
   // so copy waves only move bytes and take few issue slots from the other waves:
@@ -999,58 +1070,73 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE, MAPS>::NT)) void 
     auto vcol = [&](int j4) { return 16 * cw + 4 * j4; };
     Frag Eb[NB];               // E' = E (F1/F3), eta (.) E (F2), V (F1A/F3A), eta (.) V (F2A)
     Frag Ec[NB];               // diag(CST) E', the state update's right operand
+    // F1 / F3 from a prep-made image: its A slots hold the blocks of T = M^{-1}
+    // (complete_inverse), so E = T R needs every residual block first and then
+    // no block waits for another
+    Frag Rb[FULLT ? NB : 1];
+    if constexpr (FULLT) {
+#pragma unroll
+      for (int p = 0; p < NB; ++p) Rb[p] = cvt<OpT>(to_f4(ldT(V, LXV, 16 * p, vcol, lane)) - XS[p]);
+    }
 #pragma unroll
     for (int p = 0; p < NB; ++p) {
-      f4 R = to_f4(ldT(V, LXV, 16 * p, vcol, lane));  // C-layout values of this wave's channels
-      if (DELTA) R -= XS[p];
-      f4 eta4;
-      if (PERCH) {
-        const f4 inv = *reinterpret_cast<const f4 *>(F + F_ETA * C + 16 * p + 4 * g4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {   // zero past the end: padded rows must not write
-          const int t = c * CS + 16 * p + 4 * g4 + i;
-          eta4[i] = (t < T ? rbeta[p][i] : 0.f) * inv[i];
-        }
-      }
-      if (DELTA) {   // R -= sum_{q<p} A_pq E_q   (E_q = eta (.) E for F2)
-        f4 acc = zero4();
-#pragma unroll
-        for (int q = 0; q + 1 < p; q += 2) mmap(acc, ldp(Ao + frag_off(aslot_base(p), q, lane)), mkp(Eb[q], Eb[q + 1]));
-        if (p & 1) mma16(acc, ld4(Ao + frag_off(aslot_base(p), p - 1, lane)), Eb[p - 1]);
-        R -= acc;
-      }
       f4 Ef;                   // E' in fp32
-      if constexpr (S::SDELTA) {
+      if constexpr (FULLT) {
         Ef = zero4();
-        mma16(Ef, ld4(Tb + (p * 64 + lane) * 4), cvt<OpT>(R));
-      } else if constexpr (VAR == V_F2) {
-        // rows 4g4..4g4+3 of block p: exact 4x4 solves, coupled by A_pp minus its 4x4 diagonal
-        const float *Ad = reinterpret_cast<const float *>(sImg[s3] + S::OFF_AD) + (p * 4 + g4) * 8;
-        const f4 c0v = *reinterpret_cast<const f4 *>(Ad), c1v = *reinterpret_cast<const f4 *>(Ad + 4);
-        const float a10 = c0v[0], a20 = c0v[1], a21 = c0v[2], a30 = c0v[3], a31 = c1v[0], a32 = c1v[1];
-        const Frag Ain = ld4(Tb + (p * 64 + lane) * 4);
-        f4 E;
-        auto local = [&](const f4 &zz) {
-          E[0] = zz[0];
-          Ef[0] = eta4[0] * E[0];
-          E[1] = zz[1] - a10 * Ef[0];
-          Ef[1] = eta4[1] * E[1];
-          E[2] = zz[2] - a20 * Ef[0] - a21 * Ef[1];
-          Ef[2] = eta4[2] * E[2];
-          E[3] = zz[3] - a30 * Ef[0] - a31 * Ef[1] - a32 * Ef[2];
-          Ef[3] = eta4[3] * E[3];
-        };
-        local(R);
 #pragma unroll
-        for (int it = 0; it < 3; ++it) {
-          f4 cpl = zero4();
-          mma16(cpl, Ain, cvt<OpT>(Ef));
-          local(R - cpl);
-        }
-      } else if constexpr (VAR == V_F2A) {
-        Ef = eta4 * R;
+        for (int q = 0; q + 1 <= p; q += 2) mmap(Ef, ldp(Ao + frag_off(aslot_base(p), q, lane)), mkp(Rb[q], Rb[q + 1]));
+        if (!(p & 1)) mma16(Ef, ld4(Tb + (p * 64 + lane) * 4), Rb[p]);
       } else {
-        Ef = R;
+        f4 R = to_f4(ldT(V, LXV, 16 * p, vcol, lane));  // C-layout values of this wave's channels
+        if (DELTA) R -= XS[p];
+        f4 eta4;
+        if (PERCH) {
+          const f4 inv = *reinterpret_cast<const f4 *>(F + F_ETA * C + 16 * p + 4 * g4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {   // zero past the end: padded rows must not write
+            const int t = c * CS + 16 * p + 4 * g4 + i;
+            eta4[i] = (t < T ? rbeta[p][i] : 0.f) * inv[i];
+          }
+        }
+        if (DELTA) {   // R -= sum_{q<p} A_pq E_q   (E_q = eta (.) E for F2)
+          f4 acc = zero4();
+#pragma unroll
+          for (int q = 0; q + 1 < p; q += 2) mmap(acc, ldp(Ao + frag_off(aslot_base(p), q, lane)), mkp(Eb[q], Eb[q + 1]));
+          if (p & 1) mma16(acc, ld4(Ao + frag_off(aslot_base(p), p - 1, lane)), Eb[p - 1]);
+          R -= acc;
+        }
+        if constexpr (S::SDELTA) {
+          Ef = zero4();
+          mma16(Ef, ld4(Tb + (p * 64 + lane) * 4), cvt<OpT>(R));
+        } else if constexpr (VAR == V_F2) {
+          // rows 4g4..4g4+3 of block p: exact 4x4 solves, coupled by A_pp minus its 4x4 diagonal
+          const float *Ad = reinterpret_cast<const float *>(sImg[s3] + S::OFF_AD) + (p * 4 + g4) * 8;
+          const f4 c0v = *reinterpret_cast<const f4 *>(Ad), c1v = *reinterpret_cast<const f4 *>(Ad + 4);
+          const float a10 = c0v[0], a20 = c0v[1], a21 = c0v[2], a30 = c0v[3], a31 = c1v[0], a32 = c1v[1];
+          const Frag Ain = ld4(Tb + (p * 64 + lane) * 4);
+          f4 E;
+          auto local = [&](const f4 &zz) {
+            E[0] = zz[0];
+            Ef[0] = eta4[0] * E[0];
+            E[1] = zz[1] - a10 * Ef[0];
+            Ef[1] = eta4[1] * E[1];
+            E[2] = zz[2] - a20 * Ef[0] - a21 * Ef[1];
+            Ef[2] = eta4[2] * E[2];
+            E[3] = zz[3] - a30 * Ef[0] - a31 * Ef[1] - a32 * Ef[2];
+            Ef[3] = eta4[3] * E[3];
+          };
+          local(R);
+#pragma unroll
+          for (int it = 0; it < 3; ++it) {
+            f4 cpl = zero4();
+            mma16(cpl, Ain, cvt<OpT>(Ef));
+            local(R - cpl);
+          }
+        } else if constexpr (VAR == V_F2A) {
+          Ef = eta4 * R;
+        } else {
+          Ef = R;
+        }
       }
       Eb[p] = cvt<OpT>(Ef);
       if constexpr (!MAPS) sEb[s2][cw][p][lane] = Eb[p];
