@@ -302,7 +302,7 @@ def chunked(variant, q, k, v, beta, log_lambda, *, chunk, window=1, state=None,
     return res
 
 
-_BACKWARD_VARIANTS = ("F1", "F1A", "F2", "F2A")
+_BACKWARD_VARIANTS = VARIANTS
 
 
 def _phi_backward(a, da, eps_phi):
@@ -311,7 +311,7 @@ def _phi_backward(a, da, eps_phi):
     return da / n - a * np.sum(a * da, axis=-1, keepdims=True) / n ** 3
 
 
-def recurrent_backward(variant, q, k, v, beta, log_lambda, do, *, state=None, dS_T=None,
+def recurrent_backward(variant, q, k, v, beta, log_lambda, do, *, window=1, state=None, dS_T=None,
                        eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix"):
     """Gradients of the recurrent form by reverse-time accumulation (the adjoint of
     the step written out), for the chunked form's use in training ([P1] 三种等价形式:
@@ -331,15 +331,27 @@ def recurrent_backward(variant, q, k, v, beta, log_lambda, do, *, state=None, dS
             dx_t = G^T (eta e) - S_{t-1}^T (eta u),  G <- lam G - (eta u) x_t^T
         additive (F1A/F2A): e = v_t, same deta/dv_t, dx_t = G^T (eta v_t),  G <- lam G
     (``eta * u`` is a scalar times a vector for F1/F1A and elementwise for F2/F2A.)
+    Windows (F3/F3A, [P1] Falcon家族, [P2] 六个变体): the step writes the B_w pairs
+    j of its window with weight w = eta_t / B_w, so every pair j gets
+        u_j = G x_j,  e_j = v_j - S_{t-1} x_j (F3) or v_j (F3A),  dv_j += w u_j,
+        dx_j += w (G^T e_j - S_{t-1}^T u_j) (the second term F3 only),
+    deta_t = sum_j <e_j, u_j> / B_w and G <- lam G - w sum_j u_j x_j^T (F3) or lam G;
+    pairs before the sequence start are the carried window, whose gradients are
+    dwin_x0 / dwin_v0.
     Then dx_t gains -2 x_t sum(deta * eta)/(eps_eta + |x_t|^2), dbeta_t = deta/(eps_eta + |x_t|^2),
     and dx_t flows through phi to k_{t-1} (prefix; x_1 of the prefix form is the
     carried x_prev, so its gradient is dx_prev0) or to k_t (same step).
 
     Returns dict(dq, dk, dv [B,T,H,d], dbeta (shape of beta), dg [B,T,H],
-    dS0 [B,H,dv,dk], dx_prev0 [B,H,dk])."""
-    _check(variant, 1, align)
+    dS0 [B,H,dv,dk], dx_prev0 [B,H,dk]) and, for windows of B_w > 1,
+    dwin_x0 [B,H,B_w-1,dk] and dwin_v0 [B,H,B_w-1,dv]."""
+    _check(variant, window, align)
     if variant not in _BACKWARD_VARIANTS:
-        raise ValueError("the backward covers F1, F1A, F2, F2A")
+        raise ValueError(f"no backward for {variant}")
+    if variant in _WINDOWED:
+        return _window_backward(variant, q, k, v, beta, log_lambda, do, window=window, state=state,
+                                dS_T=dS_T, eps_gamma=eps_gamma, eps_phi=eps_phi, eps_eta=eps_eta,
+                                align=align)
     q = np.asarray(q)
     B, T, H, dk = q.shape
     dv = np.asarray(v).shape[-1]
@@ -411,4 +423,82 @@ def recurrent_backward(variant, q, k, v, beta, log_lambda, do, *, state=None, dS
     out = dict(dq=_from_seq(dQ, B, H), dk=_from_seq(dK, B, H), dv=_from_seq(dV, B, H),
                dbeta=_from_seq(dBt, B, H), dg=_from_seq(dGl, B, H),
                dS0=G.reshape(B, H, dv, dk), dx_prev0=dxp0.reshape(B, H, dk))
+    return out
+
+
+def _window_backward(variant, q, k, v, beta, log_lambda, do, *, window, state, dS_T, eps_gamma,
+                     eps_phi, eps_eta, align):
+    """recurrent_backward for F3/F3A: the reverse-time adjoint of the window step
+    (see there), one step at a time."""
+    q = np.asarray(q)
+    B, T, H, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    N = B * H
+    Bw = window
+    Q, K, V = _to_seq(q), _to_seq(k), _to_seq(v)
+    Bt, G_in, dO = _to_seq(beta), _to_seq(log_lambda), _to_seq(do)
+    S0, xp0, wx0, wv0 = _initial(state, N, B, H, dk, dv, Bw)
+    fwd = recurrent(variant, q, k, v, beta, log_lambda, window=Bw, state=state, eps_gamma=eps_gamma,
+                    eps_phi=eps_phi, eps_eta=eps_eta, return_states=True, align=align)
+    states = _to_seq(fwd["states"])
+    Kh = phi(K, eps_phi)
+    Qh = phi(Q, eps_phi)
+    if align == "prefix":
+        X = np.concatenate([xp0[:, None, :], Kh[:, :-1]], axis=1)
+    else:
+        X = Kh.copy()
+    # every pair of the sequence, the carried window first: pair j sits at j + Bw - 1
+    XA = np.concatenate([wx0, X], axis=1)
+    VA = np.concatenate([wv0, V], axis=1)
+    dXA = np.zeros_like(XA)
+    dVA = np.zeros_like(VA)
+    dQh = np.zeros_like(Qh)
+    dBt = np.zeros_like(Bt)
+    dGl = np.zeros((N, T))
+    G = np.zeros((N, dv, dk)) if dS_T is None else np.asarray(dS_T, np.float64).reshape(N, dv, dk).copy()
+    for t in range(T - 1, -1, -1):
+        S_prev = states[:, t - 1] if t > 0 else S0
+        S_t = states[:, t]
+        x = X[:, t]
+        energy = eps_eta + np.sum(x * x, axis=-1)
+        eta = Bt[:, t] / energy
+        w = eta / Bw
+        lam = np.maximum(np.exp(G_in[:, t]), eps_gamma)
+        keys = XA[:, t:t + Bw]                                            # pairs t-Bw+1 .. t
+        vals = VA[:, t:t + Bw]
+        G = G + dO[:, t][:, :, None] * Qh[:, t][:, None, :]
+        dQh[:, t] = np.einsum("nij,ni->nj", S_t, dO[:, t])
+        dlam = np.einsum("nij,nij->n", G, S_prev)
+        U = np.einsum("nij,nbj->nbi", G, keys)                            # G x_j
+        if variant == "F3":
+            E = vals - np.einsum("nij,nbj->nbi", S_prev, keys)            # v_j - S_{t-1} x_j
+        else:
+            E = vals
+        dVA[:, t:t + Bw] += w[:, None, None] * U
+        dXA[:, t:t + Bw] += w[:, None, None] * np.einsum("nij,nbi->nbj", G, E)
+        if variant == "F3":
+            dXA[:, t:t + Bw] -= w[:, None, None] * np.einsum("nij,nbi->nbj", S_prev, U)
+            G = lam[:, None, None] * G - w[:, None, None] * np.einsum("nbi,nbj->nij", U, keys)
+        else:
+            G = lam[:, None, None] * G
+        deta = np.sum(E * U, axis=(1, 2)) / Bw
+        dBt[:, t] = deta / energy
+        dXA[:, t + Bw - 1] += 2.0 * (-deta * eta / energy)[:, None] * x
+        dGl[:, t] = np.where(np.exp(G_in[:, t]) > eps_gamma, dlam * lam, 0.0)
+
+    dX = dXA[:, Bw - 1:]
+    dQ = _phi_backward(Q, dQh, eps_phi)
+    dK = np.zeros_like(K)
+    dxp0 = np.zeros((N, dk))
+    if align == "prefix":
+        dK[:, :-1] = _phi_backward(K[:, :-1], dX[:, 1:], eps_phi)
+        dxp0 = dX[:, 0]
+    else:
+        dK = _phi_backward(K, dX, eps_phi)
+    out = dict(dq=_from_seq(dQ, B, H), dk=_from_seq(dK, B, H), dv=_from_seq(dVA[:, Bw - 1:], B, H),
+               dbeta=_from_seq(dBt, B, H), dg=_from_seq(dGl, B, H),
+               dS0=G.reshape(B, H, dv, dk), dx_prev0=dxp0.reshape(B, H, dk))
+    if Bw > 1:
+        out["dwin_x0"] = dXA[:, :Bw - 1].reshape(B, H, Bw - 1, dk)
+        out["dwin_v0"] = dVA[:, :Bw - 1].reshape(B, H, Bw - 1, dv)
     return out
