@@ -20,9 +20,11 @@ sequences too few to fill the device (B*H*dv/16 <= 128 scan workgroups, T >=
 16384, one pair per step) the segment-parallel form with 16 segments.
 --segments P runs the segment-parallel form with P segments.
 
---backward times falcon_chunk_bwd instead (Falcon-1 or 1A at the 130M-layer
-shape): the gradients of every input from the forward's per-chunk states,
-which are computed once outside the timed region.
+--backward times falcon_chunk_bwd instead: the gradients of every input from
+the forward's per-chunk states, which are computed once outside the timed
+region.  Falcon-1 / 1A / 2 / 2A at head dim 64 run the chunk-parallel kernels;
+windows (--variant F3 / F3A --window B_w) and other head dims the recurrent
+form.
 """
 
 from __future__ import annotations
@@ -140,6 +142,7 @@ def bench_decode(args):
 
 
 MFMA_FP32_PEAK_TFS = 157.3    # MI355X dense fp32 MFMA
+VALU_FP32_PEAK_TFS = 157.3    # MI355X fp32 vector ALUs
 
 
 def bwd_flops(w, variant):
@@ -153,6 +156,20 @@ def bwd_flops(w, variant):
     # diagonal-block substitutions are not counted); F2A: F1A on beta (.) v
     per_chunk = {"F1": 15 * u, "F1A": 6.5 * u, "F2": 15 * u, "F2A": 6.5 * u}[variant]
     return w.batch * w.heads * (-(-w.seqlen // C)) * per_chunk
+
+
+def bwd_rows_path(w, variant, window):
+    """True where the backward runs in the recurrent form (windows of more than
+    one pair, head dims other than 64); the chunk-parallel kernels elsewhere."""
+    return (variant in ("F3", "F3A") and window > 1) or w.dk != 64
+
+
+def bwd_rows_flops(w, variant, window):
+    """Algorithmic flops of the recurrent-form backward: per step and sequence,
+    one forward step, (1 + 4 B_w) d^2, and its adjoint, (7 + 10 B_w) d^2 (B_w = 1
+    outside Falcon-3 / 3A).  They run on the vector ALUs in fp32."""
+    bw = window if variant in ("F3", "F3A") else 1
+    return w.batch * w.heads * w.seqlen * (8 + 14 * bw) * w.dk * w.dv
 
 
 def bwd_bytes(w, variant="F1"):
@@ -176,7 +193,7 @@ def host_cores():
         return os.cpu_count() or 1
 
 
-def cpu_baseline_bwd(w, variant, budget_s=20.0):
+def cpu_baseline_bwd(w, variant, window=1, budget_s=20.0):
     """Time the oracle's backward (as it stands) on a prefix of the same workload,
     on one host core; scaled to tokens/s of the full batch."""
     try:
@@ -186,17 +203,17 @@ def cpu_baseline_bwd(w, variant, budget_s=20.0):
         limiter = None
     import oracle
     import workloads as W
-    inp = W.make_inputs(w, variant, seed=w.seed)
+    inp = W.make_inputs(w, variant, seed=w.seed, window=window)
     cot = W.make_cotangents(w, w.seed + 1)
     t_probe = 16
     t0 = time.perf_counter()
     oracle.recurrent_backward(variant, **{n: a[:, :t_probe] for n, a in inp.items()}, do=cot["do"][:, :t_probe],
-                              dS_T=cot["dS_T"])
+                              dS_T=cot["dS_T"], window=window)
     per_step = (time.perf_counter() - t0) / t_probe
     T_s = int(max(t_probe, min(w.seqlen, budget_s / max(per_step, 1e-9))))
     t0 = time.perf_counter()
     oracle.recurrent_backward(variant, **{n: a[:, :T_s] for n, a in inp.items()}, do=cot["do"][:, :T_s],
-                              dS_T=cot["dS_T"])
+                              dS_T=cot["dS_T"], window=window)
     dt = time.perf_counter() - t0
     if limiter is not None and hasattr(limiter, "unregister"):
         limiter.unregister()
@@ -216,11 +233,13 @@ def bench_backward(args):
     from recurrent_sequence_models_amd.falcon import bwd_workspace_bytes
     w = W.WORKLOADS[args.workload]
     variant = args.variant
+    win = args.window if variant in ("F3", "F3A") else 1
+    rows = bwd_rows_path(w, variant, win)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     sets = []
     for i in range(3):
-        inp = W.make_inputs(w, variant, seed=w.seed + i)
+        inp = W.make_inputs(w, variant, seed=w.seed + i, window=win)
         cot = W.make_cotangents(w, w.seed + 10 + i)
         d = {n: torch.from_numpy(a).to(dev) for n, a in inp.items()}
         for n in ("q", "k", "v"):
@@ -228,7 +247,7 @@ def bench_backward(args):
         d["do"] = torch.from_numpy(cot["do"]).to(dev).to(tdt).contiguous()
         d["dS_T"] = torch.from_numpy(cot["dS_T"]).to(dev)
         _, _, d["cs"] = chunk_fwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], chunk=w.chunk,
-                                  final=False, chunk_states=True)
+                                  window=win, final=False, chunk_states=True)
         d["out"] = dict(dq=torch.empty(w.batch, w.seqlen, w.heads, w.dk, device=dev),
                         dk=torch.empty(w.batch, w.seqlen, w.heads, w.dk, device=dev),
                         dv=torch.empty(w.batch, w.seqlen, w.heads, w.dv, device=dev),
@@ -236,14 +255,17 @@ def bench_backward(args):
                         dg=torch.empty(w.batch, w.seqlen, w.heads, device=dev))
         d["d_init"] = dict(S=torch.empty(w.batch, w.heads, w.dv, w.dk, device=dev),
                            x_prev=torch.empty(w.batch, w.heads, w.dk, device=dev))
+        if win > 1:
+            d["d_init"]["win_x"] = torch.empty(w.batch, w.heads, win - 1, w.dk, device=dev)
+            d["d_init"]["win_v"] = torch.empty(w.batch, w.heads, win - 1, w.dv, device=dev)
         sets.append(d)
-    ws_bytes = bwd_workspace_bytes(variant, w.dtype, w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk)
+    ws_bytes = bwd_workspace_bytes(variant, w.dtype, w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk, window=win)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def call(d):
         chunk_bwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], d["do"], d["cs"], dS_T=d["dS_T"],
-                  chunk=w.chunk, d_init=d["d_init"], out=d["out"], workspace=ws, stream=stream)
+                  chunk=w.chunk, window=win, d_init=d["d_init"], out=d["out"], workspace=ws, stream=stream)
 
     for i in range(args.warmup):
         call(sets[i % 3])
@@ -259,43 +281,45 @@ def bench_backward(args):
     wall = time.perf_counter() - t0
     kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
     avg_s = sum(kern_ms) / K / 1e3
-    flops = bwd_flops(w, variant)
+    flops = bwd_rows_flops(w, variant, win) if rows else bwd_flops(w, variant)
     nbytes = bwd_bytes(w, variant)
     tfs = flops / avg_s / 1e12
     gbs = nbytes / avg_s / 1e9
-    # bf16 inputs run the products on bf16 MFMA, fp32 inputs on fp32 MFMA; the
-    # roofline is whichever of that MFMA peak and HBM bounds the call
+    # bf16 inputs run the chunk-parallel products on bf16 MFMA, fp32 inputs on fp32
+    # MFMA; the recurrent form runs on the fp32 vector ALUs.  The roofline is
+    # whichever of that peak and HBM bounds the call
     bf = w.dtype == "bf16"
-    mpeak = MFMA_BF16_PEAK_TFS if bf else MFMA_FP32_PEAK_TFS
+    mpeak = VALU_FP32_PEAK_TFS if rows else MFMA_BF16_PEAK_TFS if bf else MFMA_FP32_PEAK_TFS
     if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (mpeak * 1e12):
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
     else:
-        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": mpeak, "unit": "TFLOP/s",
+        roof = {"bound": "alu" if rows else "mfma", "achieved": round(tfs, 2), "peak": mpeak, "unit": "TFLOP/s",
                 "frac": round(tfs / mpeak, 4)}
     line = {
-        "metric": f"tokens/sec, Falcon-{variant[1:]} chunked backward (H={w.heads},d={w.dk},T={w.seqlen}) "
-                  "+ % MFMA/HBM roofline",
+        "metric": f"tokens/sec, Falcon-{variant[1:]} {'recurrent-form' if rows else 'chunked'} backward "
+                  f"(H={w.heads},d={w.dk},T={w.seqlen}{f',B_w={win}' if win > 1 else ''}) + % roofline",
         "value": round(w.batch * w.seqlen / (wall / K), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(wall / K * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf else "f32", "data": "synthetic",
-        "config": {"workload": f"Falcon-{variant[1:]} chunked backward, {w.name}: B{w.batch} H{w.heads} "
-                               f"T{w.seqlen} d{w.dk} chunk {w.chunk}, {w.dtype} q/k/v/do, fp32 gradients",
+        "config": {"workload": f"Falcon-{variant[1:]} backward, {w.name}: B{w.batch} H{w.heads} "
+                               f"T{w.seqlen} d{w.dk} chunk {w.chunk}{f' window {win}' if win > 1 else ''}, "
+                               f"{w.dtype} q/k/v/do, fp32 gradients",
                    "variant": variant, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
-                   "head_dim": w.dk, "chunk": w.chunk},
+                   "head_dim": w.dk, "chunk": w.chunk, "window": win},
         "roofline": {**roof, "traffic": None,
-                     "kernel": "bwd_prep + bwd_scan + bwd_chunk",
+                     "kernel": "bwd_rows + bwd_rows_finish" if rows else "bwd_prep + bwd_scan + bwd_chunk",
                      "kernel_us": {"mean": round(avg_s * 1e6, 2), "p10": round(kern_ms[K // 10] * 1e3, 2),
                                    "p50": round(kern_ms[K // 2] * 1e3, 2),
                                    "p90": round(kern_ms[(9 * K) // 10] * 1e3, 2)},
                      "alg_flops": flops, "alg_bytes": nbytes,
-                     "mfma_frac": round(tfs / mpeak, 4), "mfma_peak": mpeak,
+                     "mfma_frac": None if rows else round(tfs / mpeak, 4), "mfma_peak": None if rows else mpeak,
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                      "workspace_bytes": ws_bytes},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_bwd(w, variant)
+        line["cpu_baseline"] = cpu_baseline_bwd(w, variant, win)
     return line
 
 

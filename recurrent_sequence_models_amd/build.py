@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libfalcon.so")
 
 SOURCES = ["falcon_abi.cpp", "falcon_fwd.hip", "falcon_fwd_pipe.hip", "falcon_fwd_split.hip", "falcon_fwd_split_win.hip",
            "falcon_fwd3.hip",
-           "falcon_step.hip", "falcon_bwd.hip", "falcon_segment.hip", "falcon_static.hip"]
+           "falcon_step.hip", "falcon_bwd.hip", "falcon_bwd_rows.hip", "falcon_segment.hip", "falcon_static.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

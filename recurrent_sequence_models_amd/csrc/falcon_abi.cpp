@@ -329,10 +329,39 @@ int falcon_recurrent_step(const falcon_shape_t *s, const void *q, const void *k,
   return FALCON_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The chunk-parallel backward where it is built (F1 / F1A / F2 / F2A, and
+// F3 / F3A with one pair, which are F1 / F1A; d = 64), else the recurrent-form
+// one (every variant and window, d = 32 / 64 / 128).
+int bwd_variant(const falcon_shape_t *s) {
+  if (windowed(s->variant) && s->window == 1) return s->variant == FALCON_3 ? FALCON_1 : FALCON_1A;
+  return s->variant;
+}
+bool bwd_chunk_parallel(const falcon_shape_t *s) {
+  return falcon::chunk_bwd_supported(bwd_variant(s), s->dk, s->dv, s->chunk, windowed(s->variant) ? s->window : 1);
+}
+bool bwd_rows(const falcon_shape_t *s) {
+  return falcon::rows_bwd_supported(s->variant, s->dtype == FALCON_BF16, s->dk, s->dv, s->chunk,
+                                    windowed(s->variant) ? s->window : 1);
+}
+size_t bwd_workspace(const falcon_shape_t *s) {
+  if (bwd_chunk_parallel(s)) return falcon::chunk_bwd_workspace(bwd_variant(s), s->batch, s->heads, s->seqlen);
+  if (bwd_rows(s))
+    return falcon::rows_bwd_workspace(s->variant, s->batch, s->heads, s->seqlen, s->dk,
+                                      windowed(s->variant) ? s->window : 1);
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t falcon_chunk_bwd_workspace(const falcon_shape_t *s) {
   if (check_shape(s, false) != FALCON_OK) return 0;
-  if (!falcon::chunk_bwd_supported(s->variant, s->dk, s->dv, s->chunk, s->window)) return 0;
-  return falcon::chunk_bwd_workspace(s->variant, s->batch, s->heads, s->seqlen);
+  return bwd_workspace(s);
 }
 
 int falcon_chunk_bwd(const falcon_shape_t *s, const void *q, const void *k, const void *v, const float *beta,
@@ -350,17 +379,23 @@ int falcon_chunk_bwd(const falcon_shape_t *s, const void *q, const void *k, cons
   if (d_final_S && !aligned16(d_final_S)) return FALCON_ERR_INVALID_ARG;
   if (init && (st = check_state(init, s)) != FALCON_OK) return st;
   if (d_init && (st = check_state(d_init, s)) != FALCON_OK) return st;
-  if (!falcon::chunk_bwd_supported(s->variant, s->dk, s->dv, s->chunk, s->window)) return FALCON_ERR_UNSUPPORTED;
-  if (workspace_bytes < falcon::chunk_bwd_workspace(s->variant, s->batch, s->heads, s->seqlen)) return FALCON_ERR_WORKSPACE;
+  const bool wy = bwd_chunk_parallel(s);
+  if (!wy && !bwd_rows(s)) return FALCON_ERR_UNSUPPORTED;
+  if (workspace_bytes < bwd_workspace(s)) return FALCON_ERR_WORKSPACE;
+  const bool win = windowed(s->variant) && s->window > 1;
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.dO = d_o; a.beta = beta; a.g = log_lambda;
   a.S0 = init ? init->S : nullptr;
   a.xprev0 = init ? init->x_prev : nullptr;
+  a.winx0 = init && win ? init->win_x : nullptr;
+  a.winv0 = init && win ? init->win_v : nullptr;
   a.chunk_states = chunk_states;
   a.dST = d_final_S;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dbeta = dbeta; a.dg = dg;
   a.dS0 = d_init ? d_init->S : nullptr;
   a.dxprev0 = d_init ? d_init->x_prev : nullptr;
+  a.dwinx0 = d_init && win ? d_init->win_x : nullptr;
+  a.dwinv0 = d_init && win ? d_init->win_v : nullptr;
   a.ws = static_cast<float *>(workspace);
   a.B = s->batch; a.T = s->seqlen; a.H = s->heads;
   a.NC = (s->seqlen + 63) / 64;                        // the kernels' chunks of 64 steps
@@ -370,9 +405,11 @@ int falcon_chunk_bwd(const falcon_shape_t *s, const void *q, const void *k, cons
   a.log_eps_gamma = std::log(s->eps_gamma);
   a.eps_phi = s->eps_phi;
   a.eps_eta = s->eps_eta;
-  if (falcon::launch_chunk_bwd(s->variant, s->dtype == FALCON_BF16, a, static_cast<hipStream_t>(stream)) != hipSuccess)
-    return FALCON_ERR_HIP;
-  return FALCON_OK;
+  const hipError_t e =
+      wy ? falcon::launch_chunk_bwd(bwd_variant(s), s->dtype == FALCON_BF16, a, static_cast<hipStream_t>(stream))
+         : falcon::launch_rows_bwd(s->variant, s->dtype == FALCON_BF16, s->dk, win ? s->window : 1, a,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
 }
 
 }  // extern "C"

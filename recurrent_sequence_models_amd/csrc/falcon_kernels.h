@@ -39,22 +39,25 @@ struct StepArgs {
   float log_eps_gamma, eps_phi, eps_eta;
 };
 
-// Everything the backward pass of the chunked form needs (F1 / F1A, d = 64,
-// chunk 64), already validated by the host.
+// Everything a backward pass needs, already validated by the host: the
+// chunk-parallel kernels (falcon_bwd.hip: F1 / F1A / F2 / F2A, d = 64) or the
+// recurrent-form kernels (falcon_bwd_rows.hip: every variant, d = 32 / 64 / 128).
 struct BwdArgs {
-  const void *q, *k, *v, *dO;    // [B,T,H,64] in the input dtype
-  const float *beta, *g;         // [B,T,H]
-  const float *S0, *xprev0;      // incoming S [B,H,64,64] and x_prev [B,H,64], or null (zeros)
-  const float *chunk_states;     // [B,H,cs_nc,64,64]: S at the end of every forward chunk
-  const float *dST;              // [B,H,64,64] gradient w.r.t. S_T, or null (zero)
-  float *dq, *dk, *dv;           // [B,T,H,64] fp32
-  float *dbeta, *dg;             // [B,T,H] fp32
-  float *dS0, *dxprev0;          // [B,H,64,64], [B,H,64] or null
-  float *ws;                     // chunk_bwd_workspace(variant, B, H, T) bytes
-  int B, T, H, NC;               // NC: chunks of 64 steps
+  const void *q, *k, *v, *dO;    // [B,T,H,d] in the input dtype
+  const float *beta, *g;         // [B,T,H] (F2 / F2A: beta [B,T,H,d])
+  const float *S0, *xprev0;      // incoming S [B,H,d,d] and x_prev [B,H,d], or null (zeros)
+  const float *winx0, *winv0;    // incoming window [B,H,Bw-1,d], or null (zeros)
+  const float *chunk_states;     // [B,H,cs_nc,d,d]: S at the end of every forward chunk
+  const float *dST;              // [B,H,d,d] gradient w.r.t. S_T, or null (zero)
+  float *dq, *dk, *dv;           // [B,T,H,d] fp32
+  float *dbeta, *dg;             // [B,T,H] fp32 (F2 / F2A: dbeta [B,T,H,d])
+  float *dS0, *dxprev0;          // [B,H,d,d], [B,H,d] or null
+  float *dwinx0, *dwinv0;        // [B,H,Bw-1,d] or null
+  float *ws;                     // the backward workspace
+  int B, T, H, NC;               // NC: chunks of 64 steps (chunk-parallel kernels)
   int cs_nc, cs_step;            // chunk_states holds cs_nc states per sequence, one every cs_step
-                                 // steps (the forward's chunk: 16, 32 or 64); the kernels read
-                                 // those at 64-step boundaries
+                                 // steps (the forward's chunk: 16, 32 or 64); the chunk-parallel
+                                 // kernels read those at 64-step boundaries
   int align;
   float log_eps_gamma, eps_phi, eps_eta;
 };
@@ -82,6 +85,9 @@ hipError_t launch_step(int variant, bool bf16, int dk, int dv, const StepArgs &a
 bool chunk_bwd_supported(int variant, int dk, int dv, int chunk, int window);
 size_t chunk_bwd_workspace(int variant, int B, int H, int T);
 hipError_t launch_chunk_bwd(int variant, bool bf16, const BwdArgs &a, hipStream_t stream);
+bool rows_bwd_supported(int variant, bool bf16, int dk, int dv, int chunk, int window);
+size_t rows_bwd_workspace(int variant, int B, int H, int T, int d, int window);
+hipError_t launch_rows_bwd(int variant, bool bf16, int d, int window, const BwdArgs &a, hipStream_t stream);
 
 hipError_t launch_seg_boundary(bool bf16, const SegArgs &a, hipStream_t stream);
 hipError_t launch_seg_identity(float *S, int nmat, int dv, int dk, hipStream_t stream);

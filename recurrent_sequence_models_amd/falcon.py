@@ -363,24 +363,26 @@ def recurrent_step(variant, q, k, v, beta, log_lambda, state, *, window=1, eps_g
 
 
 def bwd_workspace_bytes(variant, dtype, batch, seqlen, heads, dk, dv, chunk=64, eps_gamma=1e-3, eps_phi=1e-6,
-                        eps_eta=1e-6, align="prefix"):
+                        eps_eta=1e-6, align="prefix", window=1):
     """falcon_chunk_bwd_workspace for a shape (0: the backward pass is not built for it)."""
-    shape = make_shape(variant, dtype, batch, seqlen, heads, dk, dv, chunk, 1, eps_gamma, eps_phi, eps_eta, align)
+    shape = make_shape(variant, dtype, batch, seqlen, heads, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta,
+                       align)
     return int(lib().falcon_chunk_bwd_workspace(ctypes.byref(shape)))
 
 
 def chunk_bwd(variant, q, k, v, beta, log_lambda, do, chunk_states, *, init=None, dS_T=None, chunk=64,
-              eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix", d_init=True, out=None,
+              window=1, eps_gamma=1e-3, eps_phi=1e-6, eps_eta=1e-6, align="prefix", d_init=True, out=None,
               workspace=None, stream=None):
     """falcon_chunk_bwd on torch tensors: gradients of <do, o> + <dS_T, S_T>.
 
     ``chunk_states`` is what ``chunk_fwd(..., chunk_states=True)`` returned for
-    the same inputs and ``init``.  ``do`` has the dtype of q; ``dS_T`` is None or
-    [B,H,dv,dk] float32.  ``d_init``: True (allocate), a state dict to write, or
-    False.  ``out``: None or a dict of preallocated dq, dk, dv, dbeta, dg.
-    ``workspace``: None (allocate) or a uint8 device tensor.
-    Returns dict(dq, dk, dv, dbeta, dg, dS0, dx_prev0) (the last two None when
-    ``d_init`` is False)."""
+    the same inputs, ``init`` and ``window``.  ``do`` has the dtype of q; ``dS_T``
+    is None or [B,H,dv,dk] float32.  ``d_init``: True (allocate), a state dict to
+    write, or False.  ``out``: None or a dict of preallocated dq, dk, dv, dbeta,
+    dg.  ``workspace``: None (allocate) or a uint8 device tensor.
+    Returns dict(dq, dk, dv, dbeta, dg, dS0, dx_prev0) and, for a window of
+    B_w > 1 pairs, dwin_x0 and dwin_v0 (the state entries None when ``d_init``
+    is False)."""
     import torch
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -406,15 +408,16 @@ def chunk_bwd(variant, q, k, v, beta, log_lambda, do, chunk_states, *, init=None
     for name, shp in (("dq", (B, T, H, dk)), ("dk", (B, T, H, dk)), ("dv", (B, T, H, dv)),
                       ("dbeta", bshape), ("dg", (B, T, H))):
         _check_tensor(name, out[name], torch.float32, shp, dev)
+    wst = window if variant in WINDOWED else 1
     if d_init is True:
-        d_init = new_state(B, H, dk, dv, 1, dev)
+        d_init = new_state(B, H, dk, dv, wst, dev)
     elif d_init is False:
         d_init = None
     if init is not None:
-        _check_state("init", init, B, H, dk, dv, 1, dev)
+        _check_state("init", init, B, H, dk, dv, wst, dev)
     if d_init is not None:
-        _check_state("d_init", d_init, B, H, dk, dv, 1, dev)
-    shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, 1, eps_gamma, eps_phi, eps_eta, align)
+        _check_state("d_init", d_init, B, H, dk, dv, wst, dev)
+    shape = make_shape(variant, dt, B, T, H, dk, dv, chunk, window, eps_gamma, eps_phi, eps_eta, align)
     L = lib()
     need = int(L.falcon_chunk_bwd_workspace(ctypes.byref(shape)))
     if workspace is None:
@@ -431,6 +434,9 @@ def chunk_bwd(variant, q, k, v, beta, log_lambda, do, chunk_states, *, init=None
     res = dict(out)
     res["dS0"] = d_init["S"] if d_init else None
     res["dx_prev0"] = d_init["x_prev"] if d_init else None
+    if wst > 1:
+        res["dwin_x0"] = d_init["win_x"] if d_init else None
+        res["dwin_v0"] = d_init["win_v"] if d_init else None
     return res
 
 

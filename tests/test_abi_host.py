@@ -241,11 +241,24 @@ def test_bwd_workspace_size():
     assert bwd_workspace(seqlen=100, variant="F2A") == 2 * 3 * 2 * per_chunk
     # Falcon-2: keys, A, Zc, G and the per-channel steps (5 x 64 x 64), (c, e^{Lm}) and the decay
     assert bwd_workspace(seqlen=100, variant="F2") == 2 * 3 * 2 * (5 * 64 * 64 + 2 * 64 + 1) * 4
-    for kw in (dict(variant="F3", window=2), dict(variant="F3A"),
-               dict(dk=32, dv=32), dict(dk=128, dv=128), dict(batch=0)):
+    for kw in (dict(dtype="fp32", dk=128, dv=128), dict(dk=64, dv=32), dict(batch=0)):
         assert bwd_workspace(**kw) == 0, kw
     # the kernels work in 64-step chunks whatever the forward's chunk
     assert bwd_workspace(seqlen=100, chunk=32) == bwd_workspace(seqlen=100, chunk=16) == 2 * 3 * 2 * per_chunk
+    # a window of one pair is Falcon-1 / 1A
+    assert bwd_workspace(variant="F3") == bwd_workspace(variant="F1")
+    assert bwd_workspace(variant="F3A") == bwd_workspace(variant="F1A")
+
+
+def test_bwd_rows_workspace_size():
+    """The recurrent-form backward (windows, head dims 32 and 128): per workgroup
+    of 16 value rows, for every token the row sums dqh and dx (d each) and two
+    scalars, then d floats per carried window pair of each sequence."""
+    bth, bh = 2 * 100 * 3, 2 * 3
+    for kw, d, bw in ((dict(variant="F3", window=2), 64, 2), (dict(variant="F3A", window=8), 64, 8),
+                      (dict(dk=32, dv=32), 32, 1), (dict(dk=128, dv=128, variant="F2"), 128, 1),
+                      (dict(dk=128, dv=128, variant="F3", window=4, chunk=16), 128, 4)):
+        assert bwd_workspace(**kw) == (d // 16) * (bth * (2 * d + 2) + bh * (bw - 1) * d) * 4, kw
 
 
 @cpu_only
@@ -262,9 +275,12 @@ def test_bwd_rejects_on_host():
         assert call_bwd(ok, **{name: ctypes.c_void_p(0x10002)}) == F.ERR_INVALID_ARG, name
     assert call_bwd(ok, d_init=F.State(FAKE.value, None, None, None)) == F.ERR_INVALID_ARG
     assert call_bwd(ok, init=F.State(None, FAKE.value, None, None)) == F.ERR_INVALID_ARG
-    for kw in (dict(variant="F3", window=2), dict(dk=32, dv=32),
-               dict(dk=128, dv=128)):
+    for kw in (dict(dtype="fp32", dk=128, dv=128), dict(dk=64, dv=32)):
         assert call_bwd(good_shape(**kw)) == F.ERR_UNSUPPORTED, kw
+    win = good_shape(variant="F3", window=4)
+    assert call_bwd(win, wsb=bwd_workspace(variant="F3", window=4) - 1) == F.ERR_WORKSPACE
+    # a window's carried state comes with its pairs
+    assert call_bwd(win, init=F.State(FAKE.value, FAKE.value, None, None)) == F.ERR_INVALID_ARG
     assert call_bwd(ok, wsb=bwd_workspace() - 1) == F.ERR_WORKSPACE
 
 
