@@ -275,16 +275,23 @@ int falcon_recurrent_step(const falcon_shape_t *shape,
                           falcon_state_t *state, void *o, void *stream);
 
 /* Bytes of device workspace falcon_chunk_bwd needs for this shape; 0 when the
- * backward pass is not built for it (or the shape is invalid).  Built: F1, F1A,
- * F2 and F2A, d_k = d_v = 64, chunk 16, 32 or 64 (the chunk of the forward call
- * that wrote the per-chunk states; the kernels work in 64-step chunks and read
- * the states at 64-step boundaries), fp32 or bf16 inputs, either pairing.
- * The workspace holds, per chunk, the keys, the scaled WY factor, the state
- * gradient the chunk's outputs inject and the state gradient at the chunk's
- * end (4 x 16 KiB + 4 bytes); for F2, whose solves are per value channel, the
- * keys, the decayed Gram matrix, the injected gradient, the end gradient and
- * the per-channel steps (5 x 16 KiB) plus 516 bytes of per-row factors.  It
- * needs no initialisation. */
+ * backward pass is not built for it (or the shape is invalid).  Built for every
+ * shape the chunked forward pass builds with d_k = d_v: chunk 16, 32 or 64 (the
+ * chunk of the forward call that wrote the per-chunk states), fp32 or bf16
+ * inputs, either pairing, by one of two paths:
+ *  - chunk-parallel (F1, F1A, F2, F2A, and F3 / F3A with one pair; d = 64): the
+ *    kernels work in 64-step chunks and read the states at 64-step boundaries.
+ *    The workspace holds, per chunk, the keys, the scaled WY factor, the state
+ *    gradient the chunk's outputs inject and the state gradient at the chunk's
+ *    end (4 x 16 KiB + 4 bytes); for F2, whose solves are per value channel,
+ *    the keys, the decayed Gram matrix, the injected gradient, the end gradient
+ *    and the per-channel steps (5 x 16 KiB) plus 516 bytes of per-row factors.
+ *  - recurrent form (F3 / F3A windows of 2, 4 or 8 pairs; d = 32, or 128 with
+ *    bf16 inputs; every variant): the states at every forward chunk are the
+ *    checkpoints.  The workspace holds, per 16 value rows of every sequence,
+ *    the row sums of each token (2 d + 2 floats) and of each carried window
+ *    pair (d floats): d/16 x (B T H (2 d + 2) + B H (Bw - 1) d) x 4 bytes.
+ * It needs no initialisation. */
 size_t falcon_chunk_bwd_workspace(const falcon_shape_t *shape);
 
 /* Backward pass of the chunked form ([P1] 三种等价形式 form C / Figure 4-C: the
@@ -294,18 +301,23 @@ size_t falcon_chunk_bwd_workspace(const falcon_shape_t *shape);
  * with respect to q, k, v, beta, log_lambda and the initial state.  The
  * outgoing x_prev takes no gradient.  The decay clamp passes no gradient where
  * exp(g) <= eps_gamma (there the decay does not depend on g).
- *   init         as given to the forward pass (NULL = fresh sequences); S and
- *                x_prev are read.
- *   chunk_states [B, H, ceil(T/C), 64, 64] fp32: the per-chunk states the
+ * Windows ([P1] Falcon家族, [P2] 六个变体): every pair of a step's window takes
+ * its share of the gradient, the carried window's pairs included.
+ *   init         as given to the forward pass (NULL = fresh sequences); S,
+ *                x_prev and, for F3/F3A with Bw > 1, the window are read.
+ *   chunk_states [B, H, ceil(T/C), d, d] fp32: the per-chunk states the
  *                forward pass wrote for these inputs at shape->chunk = C.
- *   d_o          [B, T, H, 64] in dtype.
- *   d_final_S    [B, H, 64, 64] fp32, or NULL for a zero gradient on S_T.
- *   dq, dk, dv   [B, T, H, 64] fp32, written whole (under the prefix pairing
+ *   d_o          [B, T, H, d] in dtype.
+ *   d_final_S    [B, H, d, d] fp32, or NULL for a zero gradient on S_T.
+ *   dq, dk, dv   [B, T, H, d] fp32, written whole (under the prefix pairing
  *                dk of the last token is 0).
  *   dbeta, dg    [B, T, H] fp32 (F2/F2A: dbeta [B, T, H, dv], like their beta).
- *   d_init       NULL, or S [B, H, 64, 64] and x_prev [B, H, 64] fp32 that
+ *   d_init       NULL, or S [B, H, d, d] and x_prev [B, H, d] fp32 (and, for
+ *                F3/F3A with Bw > 1, win_x and win_v [B, H, Bw-1, d]) that
  *                receive the gradients w.r.t. the initial state (x_prev: 0
- *                under the same-step pairing, which does not read it).
+ *                under the same-step pairing, which does not read it; the
+ *                window's keys are features, so win_x takes their gradient
+ *                as they are).
  *   workspace    at least falcon_chunk_bwd_workspace(shape) bytes, else
  *                FALCON_ERR_WORKSPACE; calls sharing a workspace race.
  * Outputs must not alias inputs.  Other shapes return FALCON_ERR_UNSUPPORTED.
