@@ -21,8 +21,8 @@
 // the checkpoints: the chunks run in reverse, each one first forward, keeping the
 // state every SUB steps in LDS, then stretch by stretch backward: the stretch's
 // SUB states are recomputed into registers and the adjoint steps run in reverse.
-// Every step's row sums are reduced over the workgroup's 16 rows (shuffles within
-// a wave, then LDS over the four waves) and written to the workspace, one record
+// Every step's row sums are reduced over the workgroup's 16 rows (lane shuffles
+// within a wave, then LDS over the four waves) and written to the workspace, one record
 // per workgroup, so the result does not depend on scheduling.
 // bwd_rows_finish: one wave per token adds the records of the D/16 workgroups of
 // its sequence and takes the gradients through eta's norm, the decay clamp and
@@ -64,14 +64,8 @@ inline size_t row_ws_floats(int B, int H, int T, int D, int BW) {
   return nsl * (bth * (2 * (size_t)D + 2) + (size_t)B * H * (BW - 1) * D);
 }
 
-// Sum over the 16 lanes of a row group.
-__device__ __forceinline__ float rsum16(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  return x;
-}
+// Sum over the 16 lanes of a row group (DPP butterflies, no LDS trip).
+__device__ __forceinline__ float rsum16(float x) { return group_sum<16>(x); }
 // Sum over the four row groups of a wave.
 __device__ __forceinline__ float rsum4(float x) {
   x += __shfl_xor(x, 16);
