@@ -21,7 +21,7 @@
 // the checkpoints: the chunks run in reverse, each one first forward, keeping the
 // state every SUB steps in LDS, then stretch by stretch backward: the stretch's
 // SUB states are recomputed into registers and the adjoint steps run in reverse.
-// Every step's row sums are reduced over the workgroup's 16 rows (lane shuffles
+// Every step's row sums are reduced over the workgroup's 16 rows (lane swaps
 // within a wave, then LDS over the four waves) and written to the workspace, one record
 // per workgroup, so the result does not depend on scheduling.
 // bwd_rows_finish: one wave per token adds the records of the D/16 workgroups of
@@ -40,8 +40,10 @@ constexpr int RNT = 256;     // threads per workgroup: 16 rows x 16 lanes
 template <int D>
 struct RowGeom {
   static constexpr int E = D / 16;                // columns per lane
-  static constexpr int SUB = D == 128 ? 8 : 16;   // steps whose states stay in registers
-  static constexpr int MAXCK = 64 / SUB;          // stretches per forward chunk (chunk <= 64)
+  static constexpr int SUB = D == 128 ? 8 : 16;   // steps whose states stay in registers (a stretch)
+  static constexpr int STG = D == 128 ? 32 : 64;  // steps whose inputs are staged in LDS at once (a unit)
+  static constexpr int MAXCK = STG / SUB;         // stretches per unit
+  static constexpr int MAXNU = 64 / STG;          // units per forward chunk (chunk <= 64)
 };
 
 // Workspace records (floats): per workgroup slice sl of a sequence, for every
@@ -66,12 +68,24 @@ inline size_t row_ws_floats(int B, int H, int T, int D, int BW) {
 
 // Sum over the 16 lanes of a row group (DPP butterflies, no LDS trip).
 __device__ __forceinline__ float rsum16(float x) { return group_sum<16>(x); }
-// Sum over the four row groups of a wave.
-__device__ __forceinline__ float rsum4(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// x plus the value of lane l ^ 16 (resp. l ^ 32), by gfx950's lane swaps of two
+// registers a, b: v_permlane16_swap exchanges the odd 16-lane rows of a with the
+// even rows of b, v_permlane32_swap the upper 32 lanes of a with the lower 32 of b.
+// With a = b = x the two registers then hold the two partners' values in every
+// lane.  Written out (the two copies must be distinct registers; the nops cover
+// the VALU-write-to-permlane-read wait).
+__device__ __forceinline__ float add_xor16(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return a + b;
 }
+__device__ __forceinline__ float add_xor32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return a + b;
+}
+// Sum over the four row groups of a wave.
+__device__ __forceinline__ float rsum4(float x) { return add_xor32(add_xor16(x)); }
 
 template <typename IT, int E>
 __device__ __forceinline__ void load_cols(const IT *p, float (&v)[E]) {
@@ -82,19 +96,22 @@ __device__ __forceinline__ void load_cols(const IT *p, float (&v)[E]) {
 template <int VAR, typename IT, int D, int BW>
 __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
   using Gm = RowGeom<D>;
-  constexpr int E = Gm::E, SUB = Gm::SUB, NP = SUB + BW - 1;
+  constexpr int E = Gm::E, SUB = Gm::SUB, STG = Gm::STG, NP = STG + BW - 1;
   constexpr bool DELTA = VAR == V_F1 || VAR == V_F2 || VAR == V_F3;
   constexpr bool PERCH = VAR == V_F2 || VAR == V_F2A;
   static_assert(SUB % BW == 0, "a stretch holds whole windows");
   static_assert(!PERCH || BW == 1, "per-channel steps have one pair per step");
 
-  __shared__ __attribute__((aligned(16))) float sK[NP * D];         // keys of pairs s0-BW+1 .. s0+SUB-1
-  __shared__ __attribute__((aligned(16))) float sQ[SUB * D];        // qh of steps s0 .. s0+SUB-1
-  __shared__ float sV[NP * RROWS];                                  // the rows' values of those pairs
-  __shared__ float sDO[SUB * RROWS];                                // the rows' do
-  __shared__ float sW[SUB * (PERCH ? RROWS : 1)];                   // w_t (per row for F2 / F2A)
-  __shared__ float sLam[SUB], sEn[SUB];                             // lam_t, eps_eta + |x_t|^2
-  __shared__ __attribute__((aligned(16))) float sCk[Gm::MAXCK * RNT * E];   // state at each stretch start
+  // one unit of up to STG steps u0 ..: the keys of its pairs u0-BW+1 .., its queries,
+  // the rows' values and do, and the per-step factors
+  __shared__ __attribute__((aligned(16))) float sK[NP * D];
+  __shared__ __attribute__((aligned(16))) float sQ[STG * D];
+  __shared__ float sV[NP * RROWS];
+  __shared__ float sDO[STG * RROWS];
+  __shared__ float sW[STG * (PERCH ? RROWS : 1)];                   // w_t (per row for F2 / F2A)
+  __shared__ float sLam[STG], sEn[STG];                             // lam_t, eps_eta + |x_t|^2
+  __shared__ __attribute__((aligned(16))) float sCk[Gm::MAXCK * RNT * E];   // state at each stretch start of the unit
+  __shared__ __attribute__((aligned(16))) float sUS[Gm::MAXNU * RNT * E];   // state at each unit start of the chunk
   __shared__ __attribute__((aligned(16))) float sRq[4 * SUB * D], sRx[4 * SUB * D];   // per-wave row sums
   __shared__ float sRs[4 * SUB * 2];
 
@@ -102,8 +119,8 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
   const int rr = 4 * w + (lane >> 4);     // row of the workgroup
   const int p = lane & 15, c0 = p * E;    // this lane's columns c0 .. c0+E-1
   constexpr int NSL = D / RROWS;
-  const int n = blockIdx.x / NSL, sl = blockIdx.x % NSL;
-  const int b = n / a.H, h = n % a.H, T = a.T, H = a.H;
+  const int n_seq = blockIdx.x / NSL, sl = blockIdx.x % NSL;
+  const int b = n_seq / a.H, h = n_seq % a.H, T = a.T, H = a.H;
   const int ch = sl * RROWS + rr;         // value channel of this row
   const size_t bth = (size_t)a.B * T * H;
   const RowWs ws = row_ws(a.ws, a.B, H, T, D, BW);
@@ -113,26 +130,32 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
   const IT *dop = static_cast<const IT *>(a.dO);
   auto tok = [&](int t) { return ((size_t)b * T + t) * H + h; };
 
-  // The inputs of the stretch of steps s0 .. s0+SUB-1 into LDS (steps past T are
-  // identity steps: no pair written, no output read).  Two barriers.
-  auto stage = [&](int s0) {
-    for (int r = tid >> 4; r < NP; r += RNT / 16) {   // pair keys, 16 lanes per pair
-      const int j = s0 - BW + 1 + r;                  // pair index; pairs j < 0 are the carried window
-      const int kt = j - 1 + a.align;                 // token of the pair's raw key
+  // The inputs of the unit of steps u0 .. u0+n-1 into LDS (steps past T are
+  // identity steps: no pair written, no output read).  Every global read of the
+  // unit is issued in one pass; one barrier.
+  auto stage = [&](int u0, int n) {
+    for (int r = tid >> 4; r < n + BW - 1; r += RNT / 16) {   // pair keys, 16 lanes per pair
+      const int j = u0 - BW + 1 + r;                          // pair index; pairs j < 0 are the carried window
+      const int kt = j - 1 + a.align;                         // token of the pair's raw key
+      const int i = r - (BW - 1);                             // the step whose newest pair this is
       float x[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) x[e] = 0.f;
       bool raw = false;
       if (j < T) {
         if (j < 0) {
-          if (a.winx0) load_cols<float, E>(a.winx0 + ((size_t)n * (BW - 1) + j + BW - 1) * D + c0, x);
+          if (a.winx0) load_cols<float, E>(a.winx0 + ((size_t)n_seq * (BW - 1) + j + BW - 1) * D + c0, x);
         } else if (kt < 0) {
-          if (a.xprev0) load_cols<float, E>(a.xprev0 + (size_t)n * D + c0, x);
+          if (a.xprev0) load_cols<float, E>(a.xprev0 + (size_t)n_seq * D + c0, x);
         } else {
           load_cols<IT, E>(kp + tok(kt) * D + c0, x);
           raw = true;
         }
       }
+      // the step's gain, read with its key: 16 channels (one per lane) for F2 / F2A
+      float beta = 0.f;
+      if (i >= 0 && j < T)
+        beta = PERCH ? a.beta[tok(j) * D + sl * RROWS + p] : a.beta[tok(j)];
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) ss += x[e] * x[e];
@@ -140,10 +163,15 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
       const float sc = raw ? 1.f / sqrtf(ss + a.eps_phi) : 1.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) sK[r * D + c0 + e] = x[e] * sc;
-      if (p == 0 && r >= BW - 1) sEn[r - (BW - 1)] = a.eps_eta + ss * sc * sc;   // the step's newest pair
+      if (i >= 0) {
+        const float en = a.eps_eta + ss * sc * sc;
+        if (p == 0) sEn[i] = en;
+        if (PERCH) sW[i * RROWS + p] = beta / en;
+        else if (p == 0) sW[i] = beta / en * (1.f / BW);
+      }
     }
-    for (int r = tid >> 4; r < SUB; r += RNT / 16) {  // queries
-      const int t = s0 + r;
+    for (int r = tid >> 4; r < n; r += RNT / 16) {  // queries
+      const int t = u0 + r;
       float x[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) x[e] = 0.f;
@@ -156,36 +184,26 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) sQ[r * D + c0 + e] = x[e] * sc;
     }
-    for (int e = tid; e < NP * RROWS; e += RNT) {   // the rows' values of every staged pair
-      const int r = e / RROWS, c = sl * RROWS + e % RROWS, j = s0 - BW + 1 + r;
+    for (int e = tid; e < (n + BW - 1) * RROWS; e += RNT) {   // the rows' values of every staged pair
+      const int r = e / RROWS, c = sl * RROWS + e % RROWS, j = u0 - BW + 1 + r;
       float v = 0.f;
       if (j >= 0 && j < T) v = (float)vp[tok(j) * D + c];
-      else if (j < 0 && a.winv0) v = a.winv0[((size_t)n * (BW - 1) + j + BW - 1) * D + c];
+      else if (j < 0 && a.winv0) v = a.winv0[((size_t)n_seq * (BW - 1) + j + BW - 1) * D + c];
       sV[e] = v;
     }
-    for (int e = tid; e < SUB * RROWS; e += RNT) {
-      const int t = s0 + e / RROWS;
+    for (int e = tid; e < n * RROWS; e += RNT) {
+      const int t = u0 + e / RROWS;
       sDO[e] = t < T ? (float)dop[tok(t) * D + sl * RROWS + e % RROWS] : 0.f;
     }
-    if (tid < SUB) {
-      const int t = s0 + tid;
-      sLam[tid] = t < T ? __expf(fmaxf(a.g[tok(t)], a.log_eps_gamma)) : 1.f;
-    }
-    __syncthreads();
-    if (PERCH) {
-      for (int e = tid; e < SUB * RROWS; e += RNT) {
-        const int i = e / RROWS, t = s0 + i;
-        sW[e] = t < T ? a.beta[tok(t) * D + sl * RROWS + e % RROWS] / sEn[i] : 0.f;
-      }
-    } else if (tid < SUB) {
-      const int t = s0 + tid;
-      sW[tid] = t < T ? a.beta[tok(t)] / sEn[tid] * (1.f / BW) : 0.f;
+    for (int i = tid; i < n; i += RNT) {
+      const int t = u0 + i;
+      sLam[i] = t < T ? __expf(fmaxf(a.g[tok(t)], a.log_eps_gamma)) : 1.f;
     }
     __syncthreads();
   };
   auto wstep = [&](int i) { return PERCH ? sW[i * RROWS + rr] : sW[i]; };
 
-  // One forward step i of the staged stretch on this lane's columns of S.
+  // One forward step on this lane's columns of S: step i of the staged unit.
   auto fwd = [&](const float (&S)[E], float (&Sn)[E], int i) __attribute__((always_inline)) {
     const float lam = sLam[i], wt = wstep(i);
     float eb[BW];
@@ -213,7 +231,7 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
   };
 
   float G[E];
-  if (a.dST) load_cols<float, E>(a.dST + ((size_t)n * D + ch) * D + c0, G);
+  if (a.dST) load_cols<float, E>(a.dST + ((size_t)n_seq * D + ch) * D + c0, G);
   else {
 #pragma unroll
     for (int e = 0; e < E; ++e) G[e] = 0.f;
@@ -228,24 +246,24 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
   }
 
   const int K = a.cs_step;                  // the forward's chunk: 16, 32 or 64 steps
-  const int NCK = (T + K - 1) / K, NST = K / SUB;
+  const int U = K < STG ? K : STG;          // steps per unit
+  const int NCK = (T + K - 1) / K, NU = K / U, NSU = U / SUB;
   for (int c = NCK - 1; c >= 0; --c) {
     // the state entering chunk c: the forward's end state of chunk c-1, or the initial state
     float S[E];
-    const float *ck = c ? a.chunk_states + (((size_t)n * a.cs_nc + c - 1) * D + ch) * D + c0
-                        : (a.S0 ? a.S0 + ((size_t)n * D + ch) * D + c0 : nullptr);
+    const float *ck = c ? a.chunk_states + (((size_t)n_seq * a.cs_nc + c - 1) * D + ch) * D + c0
+                        : (a.S0 ? a.S0 + ((size_t)n_seq * D + ch) * D + c0 : nullptr);
     if (ck) load_cols<float, E>(ck, S);
     else {
 #pragma unroll
       for (int e = 0; e < E; ++e) S[e] = 0.f;
     }
-    for (int st = 0; st < NST; ++st) {      // forward through the chunk, keeping each stretch's start
+    for (int u = 0; u < NU; ++u) {          // forward to each unit's start (own elements only)
 #pragma unroll
-      for (int e = 0; e < E; ++e) sCk[(st * RNT + tid) * E + e] = S[e];
-      if (st + 1 == NST) break;
-      stage(c * K + st * SUB);
-#pragma unroll
-      for (int i = 0; i < SUB; ++i) {
+      for (int e = 0; e < E; ++e) sUS[(u * RNT + tid) * E + e] = S[e];
+      if (u + 1 == NU) break;
+      stage(c * K + u * U, U);
+      for (int i = 0; i < U; ++i) {
         float Sn[E];
         fwd(S, Sn, i);
 #pragma unroll
@@ -253,123 +271,141 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
       }
       __syncthreads();   // the next stage overwrites the inputs
     }
-    for (int st = NST - 1; st >= 0; --st) {
-      const int s0 = c * K + st * SUB;
-      stage(s0);
-      float hs[SUB + 1][E];   // hs[i] = S_{s0+i-1}
+    for (int u = NU - 1; u >= 0; --u) {
+      const int u0 = c * K + u * U;
+      stage(u0, U);
 #pragma unroll
-      for (int e = 0; e < E; ++e) hs[0][e] = sCk[(st * RNT + tid) * E + e];
+      for (int e = 0; e < E; ++e) S[e] = sUS[(u * RNT + tid) * E + e];
+      for (int st = 0; st < NSU; ++st) {    // forward through the unit, keeping each stretch's start
 #pragma unroll
-      for (int i = 0; i < SUB; ++i) fwd(hs[i], hs[i + 1], i);
+        for (int e = 0; e < E; ++e) sCk[(st * RNT + tid) * E + e] = S[e];
+        if (st + 1 == NSU) break;
 #pragma unroll
-      for (int i = SUB - 1; i >= 0; --i) {
-        const int t = s0 + i;
-        const float dot = sDO[i * RROWS + rr], lam = sLam[i], wt = wstep(i);
-        float qv[E];
+        for (int i = 0; i < SUB; ++i) {
+          float Sn[E];
+          fwd(S, Sn, st * SUB + i);
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          G[e] += dot * sQ[i * D + c0 + e];
-          qv[e] = dot * hs[i + 1][e];
+          for (int e = 0; e < E; ++e) S[e] = Sn[e];
         }
-        // row dot products: G.S_{t-1}, G.x_j and S_{t-1}.x_j
-        float dl = 0.f, u[BW], dd[BW];
+      }
+      for (int st = NSU - 1; st >= 0; --st) {
+        const int b0 = st * SUB, s0 = u0 + b0;   // the stretch within the unit, and its first step
+        float hs[SUB + 1][E];   // hs[i] = S_{s0+i-1}
 #pragma unroll
-        for (int bb = 0; bb < BW; ++bb) u[bb] = dd[bb] = 0.f;
+        for (int e = 0; e < E; ++e) hs[0][e] = sCk[(st * RNT + tid) * E + e];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          dl += G[e] * hs[i][e];
+        for (int i = 0; i < SUB; ++i) fwd(hs[i], hs[i + 1], b0 + i);
+#pragma unroll
+        for (int i = SUB - 1; i >= 0; --i) {
+          const int t = s0 + i, iu = b0 + i;
+          const float dot = sDO[iu * RROWS + rr], lam = sLam[iu], wt = wstep(iu);
+          float qv[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            G[e] += dot * sQ[iu * D + c0 + e];
+            qv[e] = dot * hs[i + 1][e];
+          }
+          // row dot products: G.S_{t-1}, G.x_j and S_{t-1}.x_j
+          float dl = 0.f, u[BW], dd[BW];
+#pragma unroll
+          for (int bb = 0; bb < BW; ++bb) u[bb] = dd[bb] = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            dl += G[e] * hs[i][e];
+#pragma unroll
+            for (int bb = 0; bb < BW; ++bb) {
+              const float xk = sK[(iu + bb) * D + c0 + e];
+              u[bb] += G[e] * xk;
+              if (DELTA) dd[bb] += hs[i][e] * xk;
+            }
+          }
+          dl = rsum16(dl);
+          float deta = 0.f;
 #pragma unroll
           for (int bb = 0; bb < BW; ++bb) {
-            const float xk = sK[(i + bb) * D + c0 + e];
-            u[bb] += G[e] * xk;
-            if (DELTA) dd[bb] += hs[i][e] * xk;
-          }
-        }
-        dl = rsum16(dl);
-        float deta = 0.f;
+            u[bb] = rsum16(u[bb]);
+            const float ev = sV[(iu + bb) * RROWS + rr] - (DELTA ? rsum16(dd[bb]) : 0.f);
+            deta += ev * u[bb];
+            const int slot = (i + 1 + bb) % BW;   // pair t-BW+1+bb; s0 is a multiple of BW
+            dva[slot] += wt * u[bb];
 #pragma unroll
-        for (int bb = 0; bb < BW; ++bb) {
-          u[bb] = rsum16(u[bb]);
-          const float ev = sV[(i + bb) * RROWS + rr] - (DELTA ? rsum16(dd[bb]) : 0.f);
-          deta += ev * u[bb];
-          const int slot = (i + 1 + bb) % BW;   // pair t-BW+1+bb; s0 is a multiple of BW
-          dva[slot] += wt * u[bb];
+            for (int e = 0; e < E; ++e) {
+              dxa[slot][e] += wt * ev * G[e];
+              if (DELTA) dxa[slot][e] -= wt * u[bb] * hs[i][e];
+            }
+          }
 #pragma unroll
           for (int e = 0; e < E; ++e) {
-            dxa[slot][e] += wt * ev * G[e];
-            if (DELTA) dxa[slot][e] -= wt * u[bb] * hs[i][e];
+            float gn = lam * G[e];
+            if (DELTA) {
+#pragma unroll
+              for (int bb = 0; bb < BW; ++bb) gn -= wt * u[bb] * sK[(iu + bb) * D + c0 + e];
+            }
+            G[e] = gn;
           }
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          float gn = lam * G[e];
-          if (DELTA) {
-#pragma unroll
-            for (int bb = 0; bb < BW; ++bb) gn -= wt * u[bb] * sK[(i + bb) * D + c0 + e];
+          // pair t has all its contributions: its value gradient, and its dx into the row sums
+          const int sl_t = (i + BW) % BW;
+          if (p == 0 && t < T) {
+            a.dv[tok(t) * D + ch] = dva[sl_t];
+            if (PERCH) a.dbeta[tok(t) * D + ch] = deta / sEn[iu];
           }
-          G[e] = gn;
-        }
-        // pair t has all its contributions: its value gradient, and its dx into the row sums
-        const int sl_t = (i + BW) % BW;
-        if (p == 0 && t < T) {
-          a.dv[tok(t) * D + ch] = dva[sl_t];
-          if (PERCH) a.dbeta[tok(t) * D + ch] = deta / sEn[i];
-        }
-        dva[sl_t] = 0.f;
-        float es = PERCH ? deta * wt : deta;   // F2 / F2A: sum over rows of d eta_i eta_i
-        es = rsum4(es);
-        dl = rsum4(dl);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          qv[e] = rsum4(qv[e]);
-          dxa[sl_t][e] = rsum4(dxa[sl_t][e]);
-        }
-        if (lane < 16) {
+          dva[sl_t] = 0.f;
+          float es = PERCH ? deta * wt : deta;   // F2 / F2A: sum over rows of d eta_i eta_i
+          es = rsum4(es);
+          dl = rsum4(dl);
 #pragma unroll
           for (int e = 0; e < E; ++e) {
-            sRq[(w * SUB + i) * D + c0 + e] = qv[e];
-            sRx[(w * SUB + i) * D + c0 + e] = dxa[sl_t][e];
+            qv[e] = rsum4(qv[e]);
+            dxa[sl_t][e] = rsum4(dxa[sl_t][e]);
           }
-          if (p == 0) {
-            sRs[(w * SUB + i) * 2] = dl;
-            sRs[(w * SUB + i) * 2 + 1] = es;
-          }
-        }
+          if (lane < 16) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) dxa[sl_t][e] = 0.f;
-      }
-      __syncthreads();
-      // the stretch's row sums over the four waves, one record per workgroup
-      for (int e = tid; e < SUB * D; e += RNT) {
-        const int i = e / D, col = e % D, t = s0 + i;
-        if (t < T) {
-          const size_t o = ((size_t)sl * bth + tok(t)) * D + col;
-          ws.q[o] = sRq[i * D + col] + sRq[(SUB + i) * D + col] + sRq[(2 * SUB + i) * D + col] +
-                    sRq[(3 * SUB + i) * D + col];
-          ws.x[o] = sRx[i * D + col] + sRx[(SUB + i) * D + col] + sRx[(2 * SUB + i) * D + col] +
-                    sRx[(3 * SUB + i) * D + col];
+            for (int e = 0; e < E; ++e) {
+              sRq[(w * SUB + i) * D + c0 + e] = qv[e];
+              sRx[(w * SUB + i) * D + c0 + e] = dxa[sl_t][e];
+            }
+            if (p == 0) {
+              sRs[(w * SUB + i) * 2] = dl;
+              sRs[(w * SUB + i) * 2 + 1] = es;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < E; ++e) dxa[sl_t][e] = 0.f;
         }
-      }
-      if (tid < SUB * 2) {
-        const int i = tid >> 1, t = s0 + i;
-        if (t < T)
-          ws.s[((size_t)sl * bth + tok(t)) * 2 + (tid & 1)] =
-              sRs[i * 2 + (tid & 1)] + sRs[(SUB + i) * 2 + (tid & 1)] + sRs[(2 * SUB + i) * 2 + (tid & 1)] +
-              sRs[(3 * SUB + i) * 2 + (tid & 1)];
+        __syncthreads();
+        // the stretch's row sums over the four waves, one record per workgroup
+        for (int e = tid; e < SUB * D; e += RNT) {
+          const int i = e / D, col = e % D, t = s0 + i;
+          if (t < T) {
+            const size_t o = ((size_t)sl * bth + tok(t)) * D + col;
+            ws.q[o] = sRq[i * D + col] + sRq[(SUB + i) * D + col] + sRq[(2 * SUB + i) * D + col] +
+                      sRq[(3 * SUB + i) * D + col];
+            ws.x[o] = sRx[i * D + col] + sRx[(SUB + i) * D + col] + sRx[(2 * SUB + i) * D + col] +
+                      sRx[(3 * SUB + i) * D + col];
+          }
+        }
+        if (tid < SUB * 2) {
+          const int i = tid >> 1, t = s0 + i;
+          if (t < T)
+            ws.s[((size_t)sl * bth + tok(t)) * 2 + (tid & 1)] =
+                sRs[i * 2 + (tid & 1)] + sRs[(SUB + i) * 2 + (tid & 1)] + sRs[(2 * SUB + i) * 2 + (tid & 1)] +
+                sRs[(3 * SUB + i) * 2 + (tid & 1)];
+        }
+        __syncthreads();   // the next stretch writes its row sums
       }
     }
   }
   // the gradient at the initial state, and the carried window pairs (j = -BW+1 .. -1)
   if (a.dS0) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) a.dS0[((size_t)n * D + ch) * D + c0 + e] = G[e];
+    for (int e = 0; e < E; ++e) a.dS0[((size_t)n_seq * D + ch) * D + c0 + e] = G[e];
   }
   if constexpr (BW > 1) {
     __syncthreads();
 #pragma unroll
     for (int j = -BW + 1; j < 0; ++j) {
       const int s = (j + BW) % BW;
-      if (p == 0 && a.dwinv0) a.dwinv0[((size_t)n * (BW - 1) + j + BW - 1) * D + ch] = dva[s];
+      if (p == 0 && a.dwinv0) a.dwinv0[((size_t)n_seq * (BW - 1) + j + BW - 1) * D + ch] = dva[s];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float x = rsum4(dxa[s][e]);
@@ -379,7 +415,7 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
     __syncthreads();
     for (int e = tid; e < (BW - 1) * D; e += RNT) {
       const int jj = e / D, col = e % D;
-      ws.w[(((size_t)sl * a.B * H + n) * (BW - 1) + jj) * D + col] =
+      ws.w[(((size_t)sl * a.B * H + n_seq) * (BW - 1) + jj) * D + col] =
           sRx[jj * D + col] + sRx[(SUB + jj) * D + col] + sRx[(2 * SUB + jj) * D + col] + sRx[(3 * SUB + jj) * D + col];
     }
   }
