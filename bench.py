@@ -315,6 +315,7 @@ def bench_backward(args):
                                    "p90": round(kern_ms[(9 * K) // 10] * 1e3, 2)},
                      "alg_flops": flops, "alg_bytes": nbytes,
                      "mfma_frac": None if rows else round(tfs / mpeak, 4), "mfma_peak": None if rows else mpeak,
+                     "measured_busy": None if rows else measured_busy(f"backward {variant} {w.name}", BWD_SOURCES),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                      "workspace_bytes": ws_bytes},
     }
@@ -328,6 +329,7 @@ KERNEL_SOURCES = ("split_impl.h", "falcon_fwd_split.hip", "falcon_fwd_split_win.
 
 
 DECODE_SOURCES = ("falcon_step.hip", "falcon_kernels.h", "mfma_frag.h")
+BWD_SOURCES = ("falcon_bwd.hip", "falcon_kernels.h", "mfma_frag.h")
 
 
 def measured_traffic(key, sources=KERNEL_SOURCES):
@@ -339,6 +341,23 @@ def measured_traffic(key, sources=KERNEL_SOURCES):
     except (OSError, KeyError, ValueError):
         return None
     return round(rec["bytes_per_launch"]) if code_digest(sources) == rec["source_sha256"] else None
+
+
+def measured_busy(key, sources=KERNEL_SOURCES):
+    """Unit busy fractions from the committed SQ-counter record (rocprofv3, the
+    dominant kernel), or None when the kernel code changed since they were taken:
+    mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES), the share
+    of the MFMA pipes' cycles in use while the kernel held its compute units, and
+    valu_issue = SQ_INSTS_VALU / SQ_BUSY_CU_CYCLES (MFMA included; a compute unit
+    issues at most one wave64 VALU instruction per cycle)."""
+    path = os.path.join(ROOT, "profiles", "sq_counters.json")
+    try:
+        rec = json.load(open(path))[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if code_digest(sources) != rec["source_sha256"]:
+        return None
+    return {"kernel": rec["kernel"], "mfma_busy": round(rec["mfma_busy"], 4), "valu_issue": round(rec["valu_issue"], 4)}
 
 
 def code_digest(sources):
@@ -509,7 +528,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
-    roof["traffic"] = measured_traffic(f"{path} {variant} {w.name}" + (f" w{window}" if window > 1 else ""))
+    key = f"{path} {variant} {w.name}" + (f" w{window}" if window > 1 else "")
+    roof["traffic"] = measured_traffic(key)
+    roof["measured_busy"] = measured_busy(key)
     roof["kernel"] = ("seg_boundary + chunk_prep + 2 x chunk_scan (map form) + seg_combine + chunk_scan"
                       if path.startswith("segmented") else
                       "chunk_prep + chunk_scan" if path == "split" else
