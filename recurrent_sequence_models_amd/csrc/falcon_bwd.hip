@@ -45,6 +45,7 @@
 // which makes both the 16-byte row reads and the 4-byte column reads of the
 // fragment loads free of bank conflicts.
 #include "falcon_kernels.h"
+#include "lane_ops.h"
 #include "mfma_frag.h"
 
 namespace falcon {
@@ -93,28 +94,9 @@ __device__ __forceinline__ void mmx(f4 &d, const f4 &a, const f4 &b) {
 }
 
 // Sum over the 16 lanes that share a row of a C-layout tile.
-// x of the lane a DPP control names within the lane's 16-lane row (no LDS trip).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-// Sum over aligned groups of N = 2, 4, 8 or 16 lanes: quad permutations, then the
-// half-row and row mirrors, which pair the groups' halves as xor 4 and xor 8 would.
-template <int N>
-__device__ __forceinline__ float lane_sum(float x) {
-  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
-  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
-  if constexpr (N >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror
-  if constexpr (N >= 16) x += dpp_mov<0x140>(x);  // row_mirror
-  return x;
-}
 __device__ __forceinline__ float sum16(float x) { return lane_sum<16>(x); }
 // Sum over the 4 lane groups that share a column of a C-layout tile.
-__device__ __forceinline__ float sum4g(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
+__device__ __forceinline__ float sum4g(float x) { return add_xor32(add_xor16(x)); }
 __device__ __forceinline__ float sum64(float x) { return sum4g(sum16(x)); }
 
 // The chunk's rows in LDS: keys x_i (features), queries qh_i and the per-row
@@ -126,10 +108,7 @@ struct RowScalars {
 };
 
 template <int NP>
-__device__ __forceinline__ float sum_parts(float x) {
-  static_assert(NP == 1 || NP == 2 || NP == 4 || NP == 8 || NP == 16, "parts of one row within a DPP row");
-  return lane_sum<NP>(x);
-}
+__device__ __forceinline__ float sum_parts(float x) { return lane_sum<NP>(x); }
 
 template <typename IT, int E>
 __device__ __forceinline__ void load_e(const IT *p, float (&v)[E]) {

@@ -29,6 +29,7 @@
 // the feature map phi (adjoint s (d - u^ (u^.d)) of u^ = u s, s = 1/sqrt(|u|^2 + eps)).
 #include "chunk_common.h"
 #include "falcon_kernels.h"
+#include "lane_ops.h"
 
 namespace falcon {
 
@@ -68,22 +69,6 @@ inline size_t row_ws_floats(int B, int H, int T, int D, int BW) {
 
 // Sum over the 16 lanes of a row group (DPP butterflies, no LDS trip).
 __device__ __forceinline__ float rsum16(float x) { return group_sum<16>(x); }
-// x plus the value of lane l ^ 16 (resp. l ^ 32), by gfx950's lane swaps of two
-// registers a, b: v_permlane16_swap exchanges the odd 16-lane rows of a with the
-// even rows of b, v_permlane32_swap the upper 32 lanes of a with the lower 32 of b.
-// With a = b = x the two registers then hold the two partners' values in every
-// lane.  Written out (the two copies must be distinct registers; the nops cover
-// the VALU-write-to-permlane-read wait).
-__device__ __forceinline__ float add_xor16(float x) {
-  float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  return a + b;
-}
-__device__ __forceinline__ float add_xor32(float x) {
-  float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  return a + b;
-}
 // Sum over the four row groups of a wave.
 __device__ __forceinline__ float rsum4(float x) { return add_xor32(add_xor16(x)); }
 
