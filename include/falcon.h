@@ -281,11 +281,12 @@ int falcon_recurrent_step(const falcon_shape_t *shape,
  * inputs, either pairing, by one of two paths:
  *  - chunk-parallel (F1, F1A, F2, F2A, and F3 / F3A with one pair; d = 64): the
  *    kernels work in 64-step chunks and read the states at 64-step boundaries.
- *    The workspace holds, per chunk, the keys, the scaled WY factor, the state
- *    gradient the chunk's outputs inject and the state gradient at the chunk's
- *    end (4 x 16 KiB + 4 bytes); for F2, whose solves are per value channel,
- *    the keys, the decayed Gram matrix, the injected gradient, the end gradient
- *    and the per-channel steps (5 x 16 KiB) plus 516 bytes of per-row factors.
+ *    The workspace holds, per chunk, the chunk's transition of the reverse
+ *    recurrence (d x d), the state gradient the chunk's outputs inject and the
+ *    state gradient at the chunk's end (3 x 16 KiB + 4 bytes); for F2, whose
+ *    solves are per value channel, the keys, the decayed Gram matrix, the
+ *    injected gradient, the end gradient and the per-channel steps (5 x 16 KiB)
+ *    plus 516 bytes of per-row factors.
  *  - recurrent form (F3 / F3A windows of 2, 4 or 8 pairs; d = 32, or 128 with
  *    bf16 inputs; every variant): the states at every forward chunk are the
  *    checkpoints.  The workspace holds, per 16 value rows of every sequence,

@@ -28,12 +28,14 @@
 // Three launches (mfma_frag.h fragment layouts).  The per-chunk kernels run their
 // products on bf16 MFMA with fp32 accumulation for bf16 inputs (every operand is
 // rounded to bf16 once, as in the forward pass) and on fp32 MFMA for fp32 inputs;
-// the two reverse-time scans carry G through fp32 MFMA for both:
-//   bwd_prep   one workgroup per chunk: X, Wb = diag(b) W and
+// the reverse-time scans carry G in fp32:
+//   bwd_prep   one workgroup per chunk: the chunk's transition of the reverse
+//              recurrence, M = e^{L_C} I - X^T diag(b) W (so G0 = G M + Z), and
 //              Z = do^T (diag(e^L) Qh - P diag(eta) W) into the workspace.
-//   bwd_scan   one workgroup per 16 value channels of a sequence (rows of G are
-//              independent), chunks in reverse: writes G at every chunk end and
-//              the gradient of the initial S.
+//   bwd_scan   one workgroup per sequence, one compute wave per 16 value
+//              channels (rows of G are independent) and four loader waves,
+//              chunks in reverse: writes G at every chunk end and the gradient
+//              of the initial S (Falcon-1A / 2A: bwd_scan_add, elementwise).
 //   bwd_chunk  one workgroup per chunk: recomputes A, P, E from the chunk's
 //              incoming state and takes the adjoint of every product above.
 //
@@ -347,18 +349,24 @@ struct RowShare {
 };
 
 // Workspace arrays of one chunk.
+// Workspace arrays of one chunk: the transition M = e^{L_C} I - X^T diag(b) W of
+// the reverse recurrence, stored as the A-operand fragments of its transpose
+// (fp32 inputs: fragment (kt, kb) of M^T at ((4 kt + kb) 64 + lane) 4 floats;
+// bf16 inputs: the pairs (kt, kb / 2) of Mh at ((2 kt + kb / 2) 64 + lane) 8 +
+// (kb & 1) 4 bf16 elements, Ml 4096 elements later), the injected
+// gradient Z and the gradient G at the chunk's end (row-major, value rows), and
+// the chunk's decay e^{L_C}.
 struct WsPtr {
-  float *X, *W, *Z, *G, *dec;
+  float *M, *Z, *G, *dec;
 };
 __device__ __forceinline__ WsPtr ws_of(const BwdArgs &a, size_t chunk_id) {
   const size_t nch = (size_t)a.B * a.H * a.NC;
   float *base = a.ws;
   WsPtr p;
-  p.X = base + chunk_id * C * D;
-  p.W = base + nch * C * D + chunk_id * C * D;
-  p.Z = base + 2 * nch * C * D + chunk_id * D * D;
-  p.G = base + 3 * nch * C * D + chunk_id * D * D;
-  p.dec = base + 4 * nch * C * D + chunk_id;
+  p.M = base + chunk_id * D * D;
+  p.Z = base + nch * D * D + chunk_id * D * D;
+  p.G = base + 2 * nch * D * D + chunk_id * D * D;
+  p.dec = base + 3 * nch * D * D + chunk_id;
   return p;
 }
 
@@ -416,10 +424,34 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
         mmx<BF>(s, af, W[kb]);
       }
       qe[rt] -= s;
+    }
+    // M = e^{L_C} I - X^T diag(b) W, b_i = eta_i e^{L_C - L_i}, on fp32 MFMA (the
+    // reverse recurrence carries G in fp32): key rows 16kt.., key columns 16w..,
+    // which is the A-operand fragment (w, kt) of M^T; for bf16 inputs stored as
+    // its two bf16 parts for the scan's split products
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * rt + 4 * g + i;
-        ws.W[row * D + 16 * w + cc] = rs.eta[row] * __expf(LC - rs.L[row]) * W[rt][i];
+        W[rt][i] *= rs.eta[row] * __expf(LC - rs.L[row]);
+      }
+    }
+    const float dec = __expf(LC);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f4 m = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma16(m, a_tr(sX, LD, 16 * kt, 16 * kb, lane), W[kb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m[i] = (16 * kt + 4 * g + i == 16 * w + cc ? dec : 0.f) - m[i];
+      if constexpr (BF) {   // Mh then Ml, each as k-block pairs (w, kt / 2) of bf16
+        const bf4 mh = to_op(m, __bf16()), ml = to_op(m - to_f4(mh), __bf16());
+        __bf16 *dst = reinterpret_cast<__bf16 *>(ws.M) + ((2 * w + kt / 2) * 64 + lane) * 8 + (kt & 1) * 4;
+        *reinterpret_cast<bf4 *>(dst) = mh;
+        *reinterpret_cast<bf4 *>(dst + 8 * 64 * 8) = ml;
+      } else {
+        *reinterpret_cast<f4 *>(ws.M + ((4 * w + kt) * 64 + lane) * 4) = m;
       }
     }
   }
@@ -433,86 +465,178 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ws.Z[(16 * rt + 4 * g + i) * D + 16 * w + cc] = z[i];
   }
-  if (!ADD) {
-    const int r = threadIdx.x >> 2, p = threadIdx.x & 3;
-#pragma unroll
-    for (int j = 0; j < 16; j += 4)
-      *reinterpret_cast<f4 *>(ws.X + r * D + 16 * p + j) = *reinterpret_cast<const f4 *>(sX + r * LD + 16 * p + j);
-  }
   if (threadIdx.x == 0) *ws.dec = __expf(LC);
 }
 
 // ---- bwd_scan -------------------------------------------------------------------
-// Workgroup (sequence n, value rows 16s..16s+15); wave w holds key columns
-// 16w..16w+15.  The next chunk's X, diag(b) W, Z and decay are fetched into
-// registers while the current chunk is reduced.
-template <bool ADD>
-__global__ __launch_bounds__(256) void bwd_scan(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float sX[ADD ? 4 : MAT], sW[ADD ? 4 : MAT], sG[16 * LD], sY[16 * LD];
-  const int n = blockIdx.x >> 2, s = blockIdx.x & 3;
+// Falcon-1: workgroup = one sequence.  Compute wave w (0..3) carries the rows
+// 16w..16w+15 of G (value channels; rows of G evolve independently) transposed,
+// as four C-layout tiles of G^T (key rows 16kt.., value columns).  Per chunk, in
+// reverse,
+//   G^T <- M^T G^T + Z^T,
+// so each product's result is the next chunk's right operand and no lane
+// exchange is needed.  Loader waves (4..7) copy each chunk's M fragments and Z
+// into a ring of LDS slots, NR - 1 chunks ahead of the compute waves, with their
+// own global reads a further KL chunks ahead in registers; the compute waves read
+// only LDS, so their chain never waits on memory.  One barrier per chunk.
+// fp32 inputs: fp32 MFMA.  bf16 inputs (BF): M arrives split as Mh + Ml (two
+// bf16 parts, Mh = bf16(M), Ml = bf16(M - Mh)) and G is split the same way each
+// chunk; G M = Gh Mh + Gh Ml + Gl Mh up to a relative 2^-16 (the dropped Gl Ml
+// and the rounding of the low parts), on bf16 MFMA with fp32 accumulation.
+constexpr int SCAN_NR = 4;                       // LDS ring slots
+constexpr int SCAN_ZP = 68;                      // LDS pitch of Z's rows (floats)
+constexpr int SCAN_SLOT = D * D + D * SCAN_ZP;   // floats: M fragments, then Z
+
+template <bool BF>
+__global__ __launch_bounds__(512) void bwd_scan(BwdArgs a) {
+  constexpr int NR = SCAN_NR, KL = 4;
+  __shared__ __attribute__((aligned(16))) float ring[NR * SCAN_SLOT];
+  const int n = blockIdx.x;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, cc = lane & 15;
-  const int tid = threadIdx.x, r = tid >> 2, p = tid & 3;
-  const size_t tile = (size_t)(16 * s + 4 * g) * D + 16 * w + cc;  // + i * D
-  f4 G = zero4();
-  if (a.dST) {
+  const int NC = a.NC;
+  if (w >= 4) {
+    // ---- loader waves: chunk NC-1-j goes to slot j % NR, written in iteration j - (NR-1)
+    const int t = threadIdx.x - 256;
+    f4 r[KL][8];
+    auto load = [&](int j, f4 (&dst)[8]) {   // chunk NC-1-j, clamped: the last loads are spare
+      const WsPtr ws = ws_of(a, (size_t)n * NC + max(NC - 1 - j, 0));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) G[i] = a.dST[(size_t)n * D * D + tile + i * D];
-  }
-  f4 nx[4], nw[4], nz;
-  float ndec;
-  auto fetch = [&](int c) {
-    const WsPtr ws = ws_of(a, (size_t)n * a.NC + c);
+      for (int q = 0; q < 4; ++q) dst[q] = *reinterpret_cast<const f4 *>(ws.M + (q * 256 + t) * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nz[i] = ws.Z[tile + i * D];
-    ndec = *ws.dec;
-    if (!ADD) {
+      for (int q = 0; q < 4; ++q) dst[4 + q] = *reinterpret_cast<const f4 *>(ws.Z + (q * 256 + t) * 4);
+    };
+    auto put = [&](int j, const f4 (&src)[8]) {
+      float *slot = ring + (j % NR) * SCAN_SLOT;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        nx[j] = *reinterpret_cast<const f4 *>(ws.X + r * D + 16 * p + 4 * j);
-        nw[j] = *reinterpret_cast<const f4 *>(ws.W + r * D + 16 * p + 4 * j);
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<f4 *>(slot + (q * 256 + t) * 4) = src[q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = (q * 256 + t) * 4;   // Z[e / 64][e % 64 ..]
+        *reinterpret_cast<f4 *>(slot + D * D + (e >> 6) * SCAN_ZP + (e & 63)) = src[4 + q];
+      }
+    };
+    // register set k holds chunk NC-1-j for j = k (mod KL)
+#pragma unroll
+    for (int k = 0; k < KL; ++k) load(k, r[k]);
+    // prologue: slots of chunks j = 0..NR-2
+    int j = 0;
+#pragma unroll
+    for (int k = 0; k < NR - 1; ++k, ++j) {
+      put(j, r[k % KL]);
+      load(j + KL, r[k % KL]);
+    }
+    __syncthreads();
+    // iteration i writes chunk jj = i + NR - 1 from register set jj % KL (i is a
+    // multiple of KL at the top of the unrolled body)
+    int i = 0;
+    for (; i + KL <= NC; i += KL) {
+#pragma unroll
+      for (int k = 0; k < KL; ++k) {
+        const int jj = i + k + NR - 1;
+        put(jj, r[(k + NR - 1) % KL]);
+        load(jj + KL, r[(k + NR - 1) % KL]);
+        __syncthreads();
       }
     }
-  };
-  fetch(a.NC - 1);
-  for (int c = a.NC - 1; c >= 0; --c) {
-    const f4 Z = nz;
-    const float dec = ndec;
-    f4 xr[4], wr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xr[j] = nx[j];
-      wr[j] = nw[j];
+    for (int k = 0; k < KL - 1; ++k) {
+      if (i + k < NC) {
+        const int jj = i + k + NR - 1;
+        put(jj, r[(k + NR - 1) % KL]);
+        __syncthreads();
+      }
     }
-    float *gout = ws_of(a, (size_t)n * a.NC + c).G;
+    return;
+  }
+  // ---- compute waves
+  // lane (g, cc) of tile kt holds G[16w + cc][16kt + 4g + i], i = 0..3
+  const size_t row = (size_t)(16 * w + cc) * D + 4 * g;   // + 16 kt
+  f4 G[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gout[tile + i * D] = G[i];  // gradient at the end of chunk c
-    if (c > 0) fetch(c - 1);
-    if (ADD) {
-      G = dec * G + Z;
-      continue;
+  for (int kt = 0; kt < 4; ++kt)
+    G[kt] = a.dST ? *reinterpret_cast<const f4 *>(a.dST + (size_t)n * D * D + row + 16 * kt) : zero4();
+  __syncthreads();   // the loaders' prologue
+  for (int i = 0; i < NC; ++i) {
+    const int c = NC - 1 - i;
+    const float *slot = ring + (i % NR) * SCAN_SLOT;
+    float *gout = ws_of(a, (size_t)n * NC + c).G;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) *reinterpret_cast<f4 *>(gout + row + 16 * kt) = G[kt];  // at the end of chunk c
+    f4 Gn[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      Gn[kt] = *reinterpret_cast<const f4 *>(slot + D * D + (16 * w + cc) * SCAN_ZP + 16 * kt + 4 * g);
+    if constexpr (BF) {
+      const bf8 *mh = reinterpret_cast<const bf8 *>(slot), *ml = mh + 8 * 64;
+      bf8 gh[2], gl[2];
+#pragma unroll
+      for (int kbp = 0; kbp < 2; ++kbp) {
+        const bf4 h0 = to_op(G[2 * kbp], __bf16()), h1 = to_op(G[2 * kbp + 1], __bf16());
+        const bf4 l0 = to_op(G[2 * kbp] - to_f4(h0), __bf16()), l1 = to_op(G[2 * kbp + 1] - to_f4(h1), __bf16());
+        gh[kbp] = bf8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        gl[kbp] = bf8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int kbp = 0; kbp < 2; ++kbp) {
+          const int j = 2 * kt + kbp;
+          Gn[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ml[j * 64 + lane], gh[kbp], Gn[kt], 0, 0, 0);
+          Gn[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh[j * 64 + lane], gl[kbp], Gn[kt], 0, 0, 0);
+          Gn[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh[j * 64 + lane], gh[kbp], Gn[kt], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          mma16(Gn[kt], *reinterpret_cast<const f4 *>(slot + ((4 * kt + kb) * 64 + lane) * 4), G[kb]);
+      }
     }
-    __syncthreads();  // the previous chunk's readers are done with sX, sW, sG, sY
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<f4 *>(sX + r * LD + 16 * p + 4 * j) = xr[j];
-      *reinterpret_cast<f4 *>(sW + r * LD + 16 * p + 4 * j) = wr[j];
-    }
-    st_c(sG, LD, 0, 16 * w, lane, G);
-    __syncthreads();
-    f4 y = zero4();  // (G X^T) tile: chunk rows 16w..16w+15
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma16(y, a_rm(sG, LD, 0, 16 * kb, lane), b_tr(sX, LD, 16 * kb, 16 * w, lane));
-    st_c(sY, LD, 0, 16 * w, lane, y);
-    __syncthreads();
-    f4 u = zero4();  // (G X^T) diag(b) W
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) mma16(u, a_rm(sY, LD, 0, 16 * kb, lane), b_rm(sW, LD, 16 * kb, 16 * w, lane));
-    G = dec * G - u + Z;
+    for (int kt = 0; kt < 4; ++kt) G[kt] = Gn[kt];
+    __syncthreads();   // slot i % NR is free for the loaders
   }
   if (a.dS0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a.dS0[(size_t)n * D * D + tile + i * D] = G[i];
+    for (int kt = 0; kt < 4; ++kt) *reinterpret_cast<f4 *>(a.dS0 + (size_t)n * D * D + row + 16 * kt) = G[kt];
   }
+}
+
+// Falcon-1A / 2A: G <- e^{L_C} G + Z elementwise.  Four workgroups per sequence,
+// one 16-byte column group of G per thread; a ring of the next PF chunks' Z and
+// decay is in flight (slot j holds chunk c - j; the loop body has no branch).
+__global__ __launch_bounds__(256) void bwd_scan_add(BwdArgs a) {
+  constexpr int PF = 8;
+  const int n = blockIdx.x >> 2;
+  const size_t e = ((size_t)(blockIdx.x & 3) * 256 + threadIdx.x) * 4;
+  f4 G = a.dST ? *reinterpret_cast<const f4 *>(a.dST + (size_t)n * D * D + e) : zero4();
+  f4 z[PF];
+  float dc[PF];
+  auto fetch = [&](int c, int j) {   // c clamped to 0: the ring's last loads are spare
+    const WsPtr ws = ws_of(a, (size_t)n * a.NC + max(c, 0));
+    z[j] = *reinterpret_cast<const f4 *>(ws.Z + e);
+    dc[j] = *ws.dec;
+  };
+  auto step = [&](int c, int j) {
+    *reinterpret_cast<f4 *>(ws_of(a, (size_t)n * a.NC + c).G + e) = G;   // at the end of chunk c
+    G = dc[j] * G + z[j];
+  };
+#pragma unroll
+  for (int j = 0; j < PF; ++j) fetch(a.NC - 1 - j, j);
+  int c = a.NC - 1;
+  for (; c >= PF - 1; c -= PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      step(c - j, j);
+      fetch(c - j - PF, j);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PF - 1; ++j)
+    if (j <= c) step(c - j, j);
+  if (a.dS0) *reinterpret_cast<f4 *>(a.dS0 + (size_t)n * D * D + e) = G;
 }
 
 // ---- bwd_chunk ------------------------------------------------------------------
@@ -1424,7 +1548,8 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_prep<IT, ADD>), dim3(nch), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_scan<ADD>), dim3((unsigned)a.B * a.H * 4), dim3(256), 0, st, a);
+  if (ADD) hipLaunchKernelGGL(bwd_scan_add, dim3((unsigned)a.B * a.H * 4), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((bwd_scan<std::is_same_v<IT, __bf16>>), dim3((unsigned)a.B * a.H), dim3(512), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_chunk<IT, ADD, PC>), dim3(nch), dim3(NTC), 0, st, a);
@@ -1458,7 +1583,7 @@ size_t chunk_bwd_workspace(int variant, int B, int H, int T) {
   const size_t nch = (size_t)B * H * ((T + C - 1) / C);
   if (variant == 3)   // Falcon-2: keys, A, Zc, G, eta, (c, e^{Lm}) and the decay per chunk
     return nch * (2 * C * D + C * C + 2 * D * D + 2 * C + 1) * sizeof(float);
-  return (4 * nch * C * D + nch) * sizeof(float);
+  return (3 * nch * D * D + nch) * sizeof(float);
 }
 
 hipError_t launch_chunk_bwd(int variant, bool bf16, const BwdArgs &a, hipStream_t st) {

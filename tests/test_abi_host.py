@@ -231,10 +231,10 @@ def call_bwd(shape, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, init=None, cs=FAK
 
 
 def test_bwd_workspace_size():
-    """Per chunk of 64 steps: keys, the scaled WY factor, the injected state
-    gradient and the end-of-chunk state gradient (4 x 64 x 64 fp32) plus the
-    chunk's decay; F1, F1A and F2A at d = 64, chunk 64 only."""
-    per_chunk = 4 * 64 * 64 * 4 + 4
+    """Per chunk of 64 steps: the chunk's transition of the reverse recurrence,
+    the injected state gradient and the end-of-chunk state gradient (3 x 64 x 64
+    fp32) plus the chunk's decay; F1, F1A and F2A at d = 64, chunk 64 only."""
+    per_chunk = 3 * 64 * 64 * 4 + 4
     assert bwd_workspace(seqlen=64, batch=1, heads=1) == per_chunk
     assert bwd_workspace(seqlen=100) == 2 * 3 * 2 * per_chunk
     assert bwd_workspace(seqlen=129, variant="F1A", dtype="fp32") == 2 * 3 * 3 * per_chunk
