@@ -86,6 +86,16 @@ def test_backward_edge_lengths(variant, T):
     check_bwd(variant, small(T, "fp32", B=1, H=2), 31 + T, init=True, final_grad=True)
 
 
+# The reverse scans hold the next chunks in a ring (four slots for Falcon-1, eight
+# for the additive variants) and run whole turns of it, then a tail: chunk counts
+# 3, 5, 7, 9 and 11 take the tail after zero, one or two whole turns.
+@pytest.mark.parametrize("variant", list(BWD_VARIANTS))
+@pytest.mark.parametrize("T,dtype", [(150, "bf16"), (300, "fp32"), (420, "bf16"), (560, "bf16"), (700, "fp32")])
+def test_backward_scan_ring_tails(variant, T, dtype):
+    """Sequences of 3, 5, 7, 9 and 11 chunks of 64 steps (ragged last chunks)."""
+    check_bwd(variant, small(T, dtype, B=1, H=2), 71 + T, init=True, final_grad=True)
+
+
 @pytest.mark.parametrize("variant", list(BWD_VARIANTS))
 def test_backward_gates_clear_of_floor(variant):
     """Decays in (0.67, 1) only (no clamped step): every gate takes a gradient."""
