@@ -1375,14 +1375,15 @@ __global__ __launch_bounds__((Scan<VAR, IT, D, C, BW, NS, ONE, MAPS>::NT)) void 
 // 2 slices at d <= 64 and 2, 4 or 8 at d = 128 (whose values do not fit whole).
 // The map form takes whole sequences, or 2 slices at d = 128.
 template <typename IT, int D>
-constexpr bool ns_built(int ns, bool maps = false) {
+constexpr bool ns_built(int ns, bool maps = false, bool one = false) {
   if (maps) return sizeof(IT) == 2 && D == 128 ? (ns == 1 || ns == 2) : ns == 1;
   if (sizeof(IT) == 4) return ns == 1;
+  if (D == 64 && !one && ns == 4) return true;   // two-kernel form: one state wave per workgroup
   return D <= 64 ? (ns == 1 || ns == 2) : (ns == 2 || ns == 4 || ns == 8);
 }
 template <int VAR, typename IT, int D, int C, int BW, int NS, bool ONE = false, bool MAPS = false>
 constexpr bool scan_ok() {
-  return ns_built<IT, D>(NS, MAPS) && Scan<VAR, IT, D, C, BW, NS, ONE, MAPS>::fits();
+  return ns_built<IT, D>(NS, MAPS, ONE) && Scan<VAR, IT, D, C, BW, NS, ONE, MAPS>::fits();
 }
 
 // Smallest built split that fits and gives at least 128 scan workgroups (else

@@ -114,8 +114,10 @@ def test_fused_and_split_paths_agree(variant):
 # shapes reach every built split and both workgroup mappings.
 SPLIT_SHAPES = [
     (64, 8, 16, 130),    # B*H = 128: NS = 1
-    (64, 4, 8, 130),     # B*H = 32: NS = 2, XCD-grouped
-    (64, 1, 5, 130),     # B*H = 5: NS = 2, plain mapping
+    (64, 8, 8, 130),     # B*H = 64: NS = 2, XCD-grouped
+    (64, 1, 66, 130),    # B*H = 66: NS = 2, plain mapping
+    (64, 4, 8, 130),     # B*H = 32: NS = 4 (two-kernel form; the one-pass form takes 2), XCD-grouped
+    (64, 1, 5, 130),     # B*H = 5: NS = 4 (one-pass: 2), plain mapping
     (128, 2, 32, 100),   # NS = 2, XCD-grouped
     (128, 4, 8, 100),    # NS = 4
     (128, 1, 6, 100),    # NS = 8, plain mapping
