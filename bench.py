@@ -329,7 +329,9 @@ KERNEL_SOURCES = ("split_impl.h", "falcon_fwd_split.hip", "falcon_fwd_split_win.
 
 
 DECODE_SOURCES = ("falcon_step.hip", "falcon_kernels.h", "mfma_frag.h")
-BWD_SOURCES = ("falcon_bwd.hip", "falcon_kernels.h", "mfma_frag.h")
+BWD_SOURCES = ("falcon_bwd.hip", "falcon_kernels.h", "mfma_frag.h", "lane_ops.h")
+# the segment-parallel forward also runs the boundary and combine kernels
+SEG_SOURCES = KERNEL_SOURCES + ("falcon_segment.hip",)
 
 
 def measured_traffic(key, sources=KERNEL_SOURCES):
@@ -529,8 +531,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
     key = f"{path} {variant} {w.name}" + (f" w{window}" if window > 1 else "")
-    roof["traffic"] = measured_traffic(key)
-    roof["measured_busy"] = measured_busy(key)
+    sources = SEG_SOURCES if path.startswith("segmented") else KERNEL_SOURCES
+    roof["traffic"] = measured_traffic(key, sources)
+    roof["measured_busy"] = measured_busy(key, sources)
     roof["kernel"] = ("seg_boundary + chunk_prep + 2 x chunk_scan (map form) + seg_combine + chunk_scan"
                       if path.startswith("segmented") else
                       "chunk_prep + chunk_scan" if path == "split" else

@@ -16,13 +16,13 @@
 //   d eta: sum_i sum_j e_j[i] u_j[i] (scalar step) or per row (F2 / F2A),
 // while dv_j[i] = sum over the steps using pair j of w_t u_j[i] stays in its row.
 //
-// bwd_rows: one workgroup per (sequence, 16 value rows), one group of 16 lanes
-// per row with D/16 columns per lane.  The forward pass's per-chunk states are
+// bwd_rows: one workgroup per (sequence, 16 value rows), LP = 16 or 32 lanes per
+// row with D/LP columns per lane (4 or 8 waves).  The forward pass's per-chunk states are
 // the checkpoints: the chunks run in reverse, each one first forward, keeping the
 // state every SUB steps in LDS, then stretch by stretch backward: the stretch's
 // SUB states are recomputed into registers and the adjoint steps run in reverse.
 // Every step's row sums are reduced over the workgroup's 16 rows (lane swaps
-// within a wave, then LDS over the four waves) and written to the workspace, one record
+// within a wave, then LDS over the waves) and written to the workspace, one record
 // per workgroup, so the result does not depend on scheduling.
 // bwd_rows_finish: one wave per token adds the records of the D/16 workgroups of
 // its sequence and takes the gradients through eta's norm, the decay clamp and
@@ -35,12 +35,20 @@ namespace falcon {
 
 namespace {
 
-constexpr int RROWS = 16;    // value rows per workgroup
-constexpr int RNT = 256;     // threads per workgroup: 16 rows x 16 lanes
+constexpr int RROWS = 16;             // value rows per workgroup
 
-template <int D>
+// A value row is spread over LP = 16 or 32 lanes (D / LP columns each): 16 rows
+// per workgroup of 4 or 8 waves (one or two per SIMD).
+template <int LP>
+struct RowLanes {
+  static constexpr int RPW = 64 / LP;          // rows per wave
+  static constexpr int NW = RROWS / RPW;       // waves per workgroup
+  static constexpr int NT = 64 * NW;           // threads per workgroup
+};
+
+template <int D, int LP>
 struct RowGeom {
-  static constexpr int E = D / 16;                // columns per lane
+  static constexpr int E = D / LP;                // columns per lane
   static constexpr int SUB = D == 128 ? 8 : 16;   // steps whose states stay in registers (a stretch)
   static constexpr int STG = D == 128 ? 32 : 64;  // steps whose inputs are staged in LDS at once (a unit)
   static constexpr int MAXCK = STG / SUB;         // stretches per unit
@@ -67,10 +75,32 @@ inline size_t row_ws_floats(int B, int H, int T, int D, int BW) {
   return nsl * (bth * (2 * (size_t)D + 2) + (size_t)B * H * (BW - 1) * D);
 }
 
-// Sum over the 16 lanes of a row group (DPP butterflies, no LDS trip).
-__device__ __forceinline__ float rsum16(float x) { return group_sum<16>(x); }
-// Sum over the four row groups of a wave.
-__device__ __forceinline__ float rsum4(float x) { return add_xor32(add_xor16(x)); }
+// Sum over the LP lanes of a row: DPP butterflies within each 16-lane row of the
+// wave, then (LP = 32) the lane swap of the two halves; no LDS trip.  Every lane
+// of the wave must run these.
+template <int LP>
+__device__ __forceinline__ float rsumL(float x) {
+  x = lane_sum<16>(x);
+  if constexpr (LP == 32) x = add_xor16(x);
+  return x;
+}
+template <int LP, int N>
+__device__ __forceinline__ void rsumL_all(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = lane_sum<16>(x[i]);
+  if constexpr (LP == 32) add_xor16_all(x);
+}
+// Sum over the 64 / LP rows of a wave.
+template <int LP>
+__device__ __forceinline__ float rsumW(float x) {
+  if constexpr (LP == 16) x = add_xor16(x);
+  return add_xor32(x);
+}
+template <int LP, int N>
+__device__ __forceinline__ void rsumW_all(float (&x)[N]) {
+  if constexpr (LP == 16) add_xor16_all(x);
+  add_xor32_all(x);
+}
 
 template <typename IT, int E>
 __device__ __forceinline__ void load_cols(const IT *p, float (&v)[E]) {
@@ -78,9 +108,10 @@ __device__ __forceinline__ void load_cols(const IT *p, float (&v)[E]) {
   for (int e = 0; e < E; ++e) v[e] = (float)p[e];
 }
 
-template <int VAR, typename IT, int D, int BW>
-__global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
-  using Gm = RowGeom<D>;
+template <int VAR, typename IT, int D, int BW, int LP>
+__global__ __launch_bounds__(RowLanes<LP>::NT) void bwd_rows(BwdArgs a) {
+  using Gm = RowGeom<D, LP>;
+  constexpr int LPR = LP, RPW = RowLanes<LP>::RPW, NWR = RowLanes<LP>::NW, RNT = RowLanes<LP>::NT;
   constexpr int E = Gm::E, SUB = Gm::SUB, STG = Gm::STG, NP = STG + BW - 1;
   constexpr bool DELTA = VAR == V_F1 || VAR == V_F2 || VAR == V_F3;
   constexpr bool PERCH = VAR == V_F2 || VAR == V_F2A;
@@ -97,12 +128,12 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
   __shared__ float sLam[STG], sEn[STG];                             // lam_t, eps_eta + |x_t|^2
   __shared__ __attribute__((aligned(16))) float sCk[Gm::MAXCK * RNT * E];   // state at each stretch start of the unit
   __shared__ __attribute__((aligned(16))) float sUS[Gm::MAXNU * RNT * E];   // state at each unit start of the chunk
-  __shared__ __attribute__((aligned(16))) float sRq[4 * SUB * D], sRx[4 * SUB * D];   // per-wave row sums
-  __shared__ float sRs[4 * SUB * 2];
+  __shared__ __attribute__((aligned(16))) float sRq[NWR * SUB * D], sRx[NWR * SUB * D];   // per-wave row sums
+  __shared__ float sRs[NWR * SUB * 2];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int rr = 4 * w + (lane >> 4);     // row of the workgroup
-  const int p = lane & 15, c0 = p * E;    // this lane's columns c0 .. c0+E-1
+  const int rr = RPW * w + lane / LPR;    // row of the workgroup
+  const int p = lane % LPR, c0 = p * E;   // this lane's columns c0 .. c0+E-1
   constexpr int NSL = D / RROWS;
   const int n_seq = blockIdx.x / NSL, sl = blockIdx.x % NSL;
   const int b = n_seq / a.H, h = n_seq % a.H, T = a.T, H = a.H;
@@ -119,7 +150,11 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
   // identity steps: no pair written, no output read).  Every global read of the
   // unit is issued in one pass; one barrier.
   auto stage = [&](int u0, int n) {
-    for (int r = tid >> 4; r < n + BW - 1; r += RNT / 16) {   // pair keys, 16 lanes per pair
+    // rows of LPR lanes; the loop bounds are wave-uniform (rsumL needs the whole
+    // wave), rows past the end load nothing and store nothing
+    for (int rb = RPW * w; rb < n + BW - 1; rb += RNT / LPR) {   // pair keys
+      const int r = rb + lane / LPR;
+      const bool row_ok = r < n + BW - 1;
       const int j = u0 - BW + 1 + r;                          // pair index; pairs j < 0 are the carried window
       const int kt = j - 1 + a.align;                         // token of the pair's raw key
       const int i = r - (BW - 1);                             // the step whose newest pair this is
@@ -127,7 +162,7 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) x[e] = 0.f;
       bool raw = false;
-      if (j < T) {
+      if (row_ok && j < T) {
         if (j < 0) {
           if (a.winx0) load_cols<float, E>(a.winx0 + ((size_t)n_seq * (BW - 1) + j + BW - 1) * D + c0, x);
         } else if (kt < 0) {
@@ -139,32 +174,37 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
       }
       // the step's gain, read with its key: 16 channels (one per lane) for F2 / F2A
       float beta = 0.f;
-      if (i >= 0 && j < T)
+      if (row_ok && i >= 0 && j < T && (!PERCH || p < RROWS))
         beta = PERCH ? a.beta[tok(j) * D + sl * RROWS + p] : a.beta[tok(j)];
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) ss += x[e] * x[e];
-      ss = rsum16(ss);
+      ss = rsumL<LP>(ss);
+      if (!row_ok) continue;
       const float sc = raw ? 1.f / sqrtf(ss + a.eps_phi) : 1.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) sK[r * D + c0 + e] = x[e] * sc;
       if (i >= 0) {
         const float en = a.eps_eta + ss * sc * sc;
         if (p == 0) sEn[i] = en;
-        if (PERCH) sW[i * RROWS + p] = beta / en;
+        if (PERCH) {
+          if (p < RROWS) sW[i * RROWS + p] = beta / en;
+        }
         else if (p == 0) sW[i] = beta / en * (1.f / BW);
       }
     }
-    for (int r = tid >> 4; r < n; r += RNT / 16) {  // queries
+    for (int rb = RPW * w; rb < n; rb += RNT / LPR) {  // queries
+      const int r = rb + lane / LPR;
       const int t = u0 + r;
       float x[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) x[e] = 0.f;
-      if (t < T) load_cols<IT, E>(qp + tok(t) * D + c0, x);
+      if (r < n && t < T) load_cols<IT, E>(qp + tok(t) * D + c0, x);
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) ss += x[e] * x[e];
-      ss = rsum16(ss);
+      ss = rsumL<LP>(ss);
+      if (r >= n) continue;
       const float sc = 1.f / sqrtf(ss + a.eps_phi);
 #pragma unroll
       for (int e = 0; e < E; ++e) sQ[r * D + c0 + e] = x[e] * sc;
@@ -201,9 +241,9 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
       }
       eb[bb] = d;
     }
+    if (DELTA) rsumL_all<LP>(eb);
 #pragma unroll
     for (int bb = 0; bb < BW; ++bb) {
-      if (DELTA) eb[bb] = rsum16(eb[bb]);
       eb[bb] = wt * (sV[(i + bb) * RROWS + rr] - eb[bb]);
     }
 #pragma unroll
@@ -304,12 +344,27 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
               if (DELTA) dd[bb] += hs[i][e] * xk;
             }
           }
-          dl = rsum16(dl);
+          {   // the row sums of this step, reduced together
+            constexpr int NR = 1 + (DELTA ? 2 : 1) * BW;
+            float red[NR];
+            red[0] = dl;
+#pragma unroll
+            for (int bb = 0; bb < BW; ++bb) {
+              red[1 + bb] = u[bb];
+              if constexpr (DELTA) red[1 + BW + bb] = dd[bb];
+            }
+            rsumL_all<LP>(red);
+            dl = red[0];
+#pragma unroll
+            for (int bb = 0; bb < BW; ++bb) {
+              u[bb] = red[1 + bb];
+              if constexpr (DELTA) dd[bb] = red[1 + BW + bb];
+            }
+          }
           float deta = 0.f;
 #pragma unroll
           for (int bb = 0; bb < BW; ++bb) {
-            u[bb] = rsum16(u[bb]);
-            const float ev = sV[(iu + bb) * RROWS + rr] - (DELTA ? rsum16(dd[bb]) : 0.f);
+            const float ev = sV[(iu + bb) * RROWS + rr] - (DELTA ? dd[bb] : 0.f);
             deta += ev * u[bb];
             const int slot = (i + 1 + bb) % BW;   // pair t-BW+1+bb; s0 is a multiple of BW
             dva[slot] += wt * u[bb];
@@ -336,14 +391,25 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
           }
           dva[sl_t] = 0.f;
           float es = PERCH ? deta * wt : deta;   // F2 / F2A: sum over rows of d eta_i eta_i
-          es = rsum4(es);
-          dl = rsum4(dl);
+          {   // over the wave's rows, reduced together
+            float red[2 + 2 * E];
+            red[0] = es;
+            red[1] = dl;
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            qv[e] = rsum4(qv[e]);
-            dxa[sl_t][e] = rsum4(dxa[sl_t][e]);
+            for (int e = 0; e < E; ++e) {
+              red[2 + e] = qv[e];
+              red[2 + E + e] = dxa[sl_t][e];
+            }
+            rsumW_all<LP>(red);
+            es = red[0];
+            dl = red[1];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              qv[e] = red[2 + e];
+              dxa[sl_t][e] = red[2 + E + e];
+            }
           }
-          if (lane < 16) {
+          if (lane < LPR) {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
               sRq[(w * SUB + i) * D + c0 + e] = qv[e];
@@ -363,18 +429,24 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
           const int i = e / D, col = e % D, t = s0 + i;
           if (t < T) {
             const size_t o = ((size_t)sl * bth + tok(t)) * D + col;
-            ws.q[o] = sRq[i * D + col] + sRq[(SUB + i) * D + col] + sRq[(2 * SUB + i) * D + col] +
-                      sRq[(3 * SUB + i) * D + col];
-            ws.x[o] = sRx[i * D + col] + sRx[(SUB + i) * D + col] + sRx[(2 * SUB + i) * D + col] +
-                      sRx[(3 * SUB + i) * D + col];
+            float sq = 0.f, sx = 0.f;
+#pragma unroll
+            for (int v = 0; v < NWR; ++v) {   // fixed order over the waves
+              sq += sRq[(v * SUB + i) * D + col];
+              sx += sRx[(v * SUB + i) * D + col];
+            }
+            ws.q[o] = sq;
+            ws.x[o] = sx;
           }
         }
         if (tid < SUB * 2) {
           const int i = tid >> 1, t = s0 + i;
-          if (t < T)
-            ws.s[((size_t)sl * bth + tok(t)) * 2 + (tid & 1)] =
-                sRs[i * 2 + (tid & 1)] + sRs[(SUB + i) * 2 + (tid & 1)] + sRs[(2 * SUB + i) * 2 + (tid & 1)] +
-                sRs[(3 * SUB + i) * 2 + (tid & 1)];
+          if (t < T) {
+            float ss = 0.f;
+#pragma unroll
+            for (int v = 0; v < NWR; ++v) ss += sRs[(v * SUB + i) * 2 + (tid & 1)];
+            ws.s[((size_t)sl * bth + tok(t)) * 2 + (tid & 1)] = ss;
+          }
         }
         __syncthreads();   // the next stretch writes its row sums
       }
@@ -393,15 +465,17 @@ __global__ __launch_bounds__(RNT) void bwd_rows(BwdArgs a) {
       if (p == 0 && a.dwinv0) a.dwinv0[((size_t)n_seq * (BW - 1) + j + BW - 1) * D + ch] = dva[s];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float x = rsum4(dxa[s][e]);
-        if (lane < 16) sRx[(w * SUB + j + BW - 1) * D + c0 + e] = x;
+        const float x = rsumW<LP>(dxa[s][e]);
+        if (lane < LPR) sRx[(w * SUB + j + BW - 1) * D + c0 + e] = x;
       }
     }
     __syncthreads();
     for (int e = tid; e < (BW - 1) * D; e += RNT) {
       const int jj = e / D, col = e % D;
-      ws.w[(((size_t)sl * a.B * H + n_seq) * (BW - 1) + jj) * D + col] =
-          sRx[jj * D + col] + sRx[(SUB + jj) * D + col] + sRx[(2 * SUB + jj) * D + col] + sRx[(3 * SUB + jj) * D + col];
+      float sx = 0.f;
+#pragma unroll
+      for (int v = 0; v < NWR; ++v) sx += sRx[(v * SUB + jj) * D + col];
+      ws.w[(((size_t)sl * a.B * H + n_seq) * (BW - 1) + jj) * D + col] = sx;
     }
   }
 }
@@ -518,9 +592,22 @@ __global__ __launch_bounds__(256) void bwd_rows_finish(BwdArgs a) {
   }
 }
 
+// Lanes per value row: 32 (two waves per SIMD, D / 32 columns per lane), except
+// for windows of residual pairs (Falcon-3 with Bw > 1), whose steps reduce 2 Bw + 1
+// row sums and B_w more per recomputed step: there the swaps between the 16-lane
+// halves cost more than the second wave per SIMD gains (window 4: 16 lanes 4.6 ms,
+// 32 lanes 5.3 ms; F3A window 4 and Falcon-1 at d = 128 are 14-19 % faster on 32),
+// and at Bw = 8 the registers of 32 would spill.
+template <int VAR, int D, int BW>
+constexpr int rows_lanes() {
+  return (VAR == V_F3 && BW > 1) ? 16 : 32;
+}
+
 template <int VAR, typename IT, int D, int BW>
 hipError_t launch_rows_t(const BwdArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_rows<VAR, IT, D, BW>), dim3((unsigned)(a.B * a.H * (D / RROWS))), dim3(RNT), 0, st, a);
+  constexpr int LP = rows_lanes<VAR, D, BW>();
+  hipLaunchKernelGGL((bwd_rows<VAR, IT, D, BW, LP>), dim3((unsigned)(a.B * a.H * (D / RROWS))),
+                     dim3(RowLanes<LP>::NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long waves = (long long)a.B * a.T * a.H + (long long)a.B * a.H * (BW - 1);

@@ -41,4 +41,43 @@ __device__ __forceinline__ float add_xor32(float x) {
   return a + b;
 }
 
+// The same over N values: the lane swaps of four values at a time issued back to
+// back between one pair of nops (the swaps of one block are independent).
+__device__ __forceinline__ void add_xor16_4(float &x0, float &x1, float &x2, float &x3) {
+  float a0 = x0, b0 = x0, a1 = x1, b1 = x1, a2 = x2, b2 = x2, a3 = x3, b3 = x3;
+  asm volatile(
+      "s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\t"
+      "v_permlane16_swap_b32 %4, %5\n\tv_permlane16_swap_b32 %6, %7\n\ts_nop 1"
+      : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "+v"(a2), "+v"(b2), "+v"(a3), "+v"(b3));
+  x0 = a0 + b0;
+  x1 = a1 + b1;
+  x2 = a2 + b2;
+  x3 = a3 + b3;
+}
+__device__ __forceinline__ void add_xor32_4(float &x0, float &x1, float &x2, float &x3) {
+  float a0 = x0, b0 = x0, a1 = x1, b1 = x1, a2 = x2, b2 = x2, a3 = x3, b3 = x3;
+  asm volatile(
+      "s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\t"
+      "v_permlane32_swap_b32 %4, %5\n\tv_permlane32_swap_b32 %6, %7\n\ts_nop 1"
+      : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "+v"(a2), "+v"(b2), "+v"(a3), "+v"(b3));
+  x0 = a0 + b0;
+  x1 = a1 + b1;
+  x2 = a2 + b2;
+  x3 = a3 + b3;
+}
+template <int N>
+__device__ __forceinline__ void add_xor16_all(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i + 4 <= N; i += 4) add_xor16_4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+#pragma unroll
+  for (int i = N - N % 4; i < N; ++i) x[i] = add_xor16(x[i]);
+}
+template <int N>
+__device__ __forceinline__ void add_xor32_all(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i + 4 <= N; i += 4) add_xor32_4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+#pragma unroll
+  for (int i = N - N % 4; i < N; ++i) x[i] = add_xor32(x[i]);
+}
+
 }  // namespace falcon
