@@ -8,9 +8,14 @@ synthetic N(0,1) inputs.  One step = one falcon_chunk_fwd call over one batch
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant V]
 
 Timing: three rotating input sets (more bytes than the 256 MB MALL), W untimed
-calls, then K timed calls bracketed by torch.cuda.synchronize().  Each call is
-also bracketed by HIP events on the stream it is launched on, which gives the
-average device time of the forward path used for the roofline.  Paths
+calls, then K timed calls bracketed by torch.cuda.synchronize() and by one pair of
+HIP events on the stream they are launched on: the wall time gives the
+throughput, the event time over K each call's average device time, used for the
+roofline.  Before the warmup steps, about --settle-ms (300) of untimed calls let
+the GPU's clocks settle.  A second, untimed pass brackets each call by events of its own for the
+p10 / p50 / p90 of the durations (per-call events cost the stream a few
+microseconds each, so they stay out of the timed loop), and a third reuses one
+input set (the warm figure).  Paths
 (--path): "onepass" calls without a workspace (the one-pass kernel where it is
 built, else the fused kernel); "split" passes a workspace (allocated once
 outside the timed region): the prep kernel over all systems, then the state
@@ -72,6 +77,62 @@ class TimingEvent:
     def __del__(self):
         if TimingEvent._hip is not None and self.handle:
             TimingEvent._hip.hipEventDestroy(self.handle)
+
+
+def settle(call, sets, ms):
+    """Untimed, before the warmup steps: calls for about `ms` milliseconds, so the
+    GPU's clocks reach their steady state (20 warmup calls of the 130M-layer
+    forward are about 1 ms, after which the same loop still ran 15 % slower than
+    after 2000).  Synchronises every 64 calls to keep the queue short."""
+    import torch
+    t_end = time.perf_counter() + ms / 1e3
+    i = 0
+    while time.perf_counter() < t_end:
+        call(sets[i % len(sets)])
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def with_settle(line, args):
+    """The settle phase's length, stated in the line's roofline object."""
+    line["roofline"]["settle_ms"] = args.settle_ms
+    return line
+
+
+def time_loop(call, sets, K, stream):
+    """The timed region: K calls, input sets rotating, bracketed by device
+    synchronisations and by one pair of timing events on the launch stream, with
+    nothing else in the loop.  Returns (wall seconds, event seconds); the event
+    time over K is each launch's average duration."""
+    import torch
+    start, end = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        call(sets[i % len(sets)])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) / 1e3
+
+
+def per_call_ms(call, sets, K, stream, rotate=True):
+    """Outside the timed region: each of K calls bracketed by events of its own,
+    the distribution of launch durations (ms, sorted).  Recording two events per
+    call costs the stream a few microseconds per call, so these run apart from
+    the timed loop.  rotate=False reuses one input set (the warm figure)."""
+    import torch
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        call(sets[i % len(sets)] if rotate else sets[0])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
 
 
 METRIC = "tokens/sec, Falcon-1 chunked fwd (H=12,d=64,T=2048) + % MFMA/HBM roofline"
@@ -140,19 +201,14 @@ def bench_decode(args):
         recurrent_step(args.variant, dd["q"], dd["k"], dd["v"], dd["beta"], dd["log_lambda"], dd,
                        window=bw, stream=stream)
 
+    settle(call, sets, args.settle_ms)
     for i in range(args.warmup):
         call(sets[i % 3])
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(TimingEvent(), TimingEvent()) for _ in range(K)]
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        call(sets[i % 3])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_s = sum(a.elapsed_time(b) for a, b in ev) / K / 1e3
+    wall, ev_s = time_loop(call, sets, K, stream)
+    kern_s = ev_s / K
+    per_ms = per_call_ms(call, sets, K, stream)
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -173,7 +229,9 @@ def bench_decode(args):
                      "frac": round(ach / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(f"decode {args.variant} b{B} h{H} d{d} w{bw}", DECODE_SOURCES),
                      "kernel": "step_kernel",
-                     "kernel_us": {"mean": round(kern_s * 1e6, 2)}, "alg_bytes": nbytes},
+                     "kernel_us": {"mean": round(kern_s * 1e6, 2), "per_call_mean": round(sum(per_ms) / K * 1e3, 2),
+                                   "p10": round(per_ms[K // 10] * 1e3, 2), "p50": round(per_ms[K // 2] * 1e3, 2),
+                                   "p90": round(per_ms[(9 * K) // 10] * 1e3, 2)}, "alg_bytes": nbytes},
     }
 
 
@@ -303,20 +361,14 @@ def bench_backward(args):
         chunk_bwd(variant, d["q"], d["k"], d["v"], d["beta"], d["log_lambda"], d["do"], d["cs"], dS_T=d["dS_T"],
                   chunk=w.chunk, window=win, d_init=d["d_init"], out=d["out"], workspace=ws, stream=stream)
 
+    settle(call, sets, args.settle_ms)
     for i in range(args.warmup):
         call(sets[i % 3])
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(TimingEvent(), TimingEvent()) for _ in range(K)]
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        call(sets[i % 3])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    avg_s = sum(kern_ms) / K / 1e3
+    wall, ev_s = time_loop(call, sets, K, stream)
+    avg_s = ev_s / K
+    kern_ms = per_call_ms(call, sets, K, stream)
     flops = bwd_rows_flops(w, variant, win) if rows else bwd_flops(w, variant)
     nbytes = bwd_bytes(w, variant)
     tfs = flops / avg_s / 1e12
@@ -346,7 +398,8 @@ def bench_backward(args):
                    "head_dim": w.dk, "chunk": w.chunk, "window": win},
         "roofline": {**roof, "traffic": None,
                      "kernel": "bwd_rows + bwd_rows_finish" if rows else "bwd_prep + bwd_scan + bwd_chunk",
-                     "kernel_us": {"mean": round(avg_s * 1e6, 2), "p10": round(kern_ms[K // 10] * 1e3, 2),
+                     "kernel_us": {"mean": round(avg_s * 1e6, 2), "per_call_mean": round(sum(kern_ms) / K * 1e3, 2),
+                                   "p10": round(kern_ms[K // 10] * 1e3, 2),
                                    "p50": round(kern_ms[K // 2] * 1e3, 2),
                                    "p90": round(kern_ms[(9 * K) // 10] * 1e3, 2)},
                      "alg_flops": flops, "alg_bytes": nbytes,
@@ -448,6 +501,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed calls before the warmup steps, in ms of wall time (clock settling)")
     ap.add_argument("--workload", default="layer130m")
     ap.add_argument("--variant", default="F1")
     ap.add_argument("--window", type=int, default=4, help="Falcon-3/3A window (pairs)")
@@ -468,10 +523,10 @@ def main():
         sys.exit(2)
 
     if args.decode:
-        print(json.dumps(bench_decode(args)), flush=True)
+        print(json.dumps(with_settle(bench_decode(args), args)), flush=True)
         return
     if args.backward:
-        print(json.dumps(bench_backward(args)), flush=True)
+        print(json.dumps(with_settle(bench_backward(args), args)), flush=True)
         return
 
     import torch
@@ -530,32 +585,20 @@ def main():
             return
         d["fwd"]()
 
+    settle(call, sets, args.settle_ms)
     for i in range(args.warmup):
         call(sets[i % 3])
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(TimingEvent(), TimingEvent()) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        call(sets[i % 3])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    avg_kernel_s = sum(kern_ms) / K / 1e3
+    wall, ev_s = time_loop(call, sets, K, stream)
+    avg_kernel_s = ev_s / K
     ms_per_step = wall / K * 1e3
     tokens = w.batch * w.seqlen
-    # outside the timed region: the warm figure, one input set reused (104 MB stays
-    # in the 256 MB MALL), reported beside the rotating-input one
-    for i in range(K):
-        ev[i][0].record(stream)
-        call(sets[0])
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    warm_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    # outside the timed region: each call's duration (p10 / p50 / p90), and the warm
+    # figure, one input set reused (104 MB stays in the 256 MB MALL)
+    kern_ms = per_call_ms(call, sets, K, stream)
+    warm_ms = per_call_ms(call, sets, K, stream, rotate=False)
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -585,7 +628,9 @@ def main():
                       "chunk_fwd_pipe" if w.dk <= 64 else "chunk_fwd_rows")
     roof["path"] = path
     roof["workspace_bytes"] = ws_bytes
-    roof["kernel_us"] = {"mean": round(avg_kernel_s * 1e6, 2), "p10": round(kern_ms[K // 10] * 1e3, 2),
+    # mean: the timed region's event pair over K; the rest from each call's own events
+    roof["kernel_us"] = {"mean": round(avg_kernel_s * 1e6, 2), "per_call_mean": round(sum(kern_ms) / K * 1e3, 2),
+                         "p10": round(kern_ms[K // 10] * 1e3, 2),
                          "p50": round(kern_ms[K // 2] * 1e3, 2), "p90": round(kern_ms[(9 * K) // 10] * 1e3, 2)}
     roof["kernel_us_warm"] = {"mean": round(sum(warm_ms) / K * 1e3, 2), "p50": round(warm_ms[K // 2] * 1e3, 2)}
     roof["alg_bytes"] = nbytes
@@ -610,7 +655,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, variant, window)
-    print(json.dumps(line), flush=True)
+    print(json.dumps(with_settle(line, args)), flush=True)
 
 
 if __name__ == "__main__":
