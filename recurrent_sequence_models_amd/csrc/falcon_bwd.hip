@@ -425,8 +425,7 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
       }
       qe[rt] -= s;
     }
-    // M = e^{L_C} I - X^T diag(b) W, b_i = eta_i e^{L_C - L_i}, on fp32 MFMA (the
-    // reverse recurrence carries G in fp32): key rows 16kt.., key columns 16w..,
+    // M = e^{L_C} I - X^T diag(b) W, b_i = eta_i e^{L_C - L_i}: key rows 16kt.., key columns 16w..,
     // which is the A-operand fragment (w, kt) of M^T; for bf16 inputs stored as
     // its two bf16 parts for the scan's split products
 #pragma unroll
@@ -438,11 +437,34 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdArgs a) {
       }
     }
     const float dec = __expf(LC);
+    // bf16 inputs: X^T diag(b) W as three bf16 products of the split parts (x = xh + xl,
+    // xh = bf16(x), xl = bf16(x - xh)), Xl Wh + Xh Wl + Xh Wh, exact to a relative 2^-16
+    // (the dropped Xl Wl and the rounding of the low parts); fp32 inputs: fp32 MFMA
+    bf4 wh[4], wl[4];
+    if constexpr (BF) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        wh[kb] = to_op(W[kb], __bf16());
+        wl[kb] = to_op(W[kb] - to_f4(wh[kb]), __bf16());
+      }
+    }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       f4 m = zero4();
+      if constexpr (BF) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) mma16(m, a_tr(sX, LD, 16 * kt, 16 * kb, lane), W[kb]);
+        for (int kp = 0; kp < 2; ++kp) {
+          const f4 x0 = a_tr(sX, LD, 16 * kt, 32 * kp, lane), x1 = a_tr(sX, LD, 16 * kt, 32 * kp + 16, lane);
+          const bf4 xh0 = to_op(x0, __bf16()), xh1 = to_op(x1, __bf16());
+          const bf4 xl0 = to_op(x0 - to_f4(xh0), __bf16()), xl1 = to_op(x1 - to_f4(xh1), __bf16());
+          mma32(m, xl0, xl1, wh[2 * kp], wh[2 * kp + 1]);
+          mma32(m, xh0, xh1, wl[2 * kp], wl[2 * kp + 1]);
+          mma32(m, xh0, xh1, wh[2 * kp], wh[2 * kp + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma16(m, a_tr(sX, LD, 16 * kt, 16 * kb, lane), W[kb]);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) m[i] = (16 * kt + 4 * g + i == 16 * w + cc ? dec : 0.f) - m[i];
       if constexpr (BF) {   // Mh then Ml, each as k-block pairs (w, kt / 2) of bf16
