@@ -22,7 +22,7 @@ outside the timed region): the prep kernel over all systems, then the state
 scan.  "auto" (default) takes the faster one measured per shape class: split
 for Falcon-3 windows and head dim 128, one-pass otherwise, and for long
 sequences too few to fill the device (B*H*dv/16 <= 128 scan workgroups, T >=
-16384, one pair per step) the segment-parallel form with 16 segments.
+16384, one pair per step) the segment-parallel form with 8 segments.
 --segments P runs the segment-parallel form with P segments.
 
 --backward times falcon_chunk_bwd instead: the gradients of every input from
@@ -559,7 +559,7 @@ def main():
     path = "split" if ws_bytes else "onepass"
     if (args.path == "auto" and args.segments == 0 and window == 1 and variant != "F2"
             and w.batch * w.heads * (w.dv // 16) <= 128 and w.seqlen >= 16384 and w.seqlen % 16 == 0):
-        args.segments = 16
+        args.segments = 8
 
     if args.segments > 0:
         ws_bytes = segmented_workspace_bytes(variant, w.dtype, w.batch, w.seqlen, w.heads, w.dk, w.dv, args.segments,

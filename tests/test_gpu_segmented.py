@@ -106,12 +106,13 @@ def test_segmented_matches_plain_forward():
     assert rel_l2(got["S"], to_np(fin["S"])) <= 1e-3
 
 
-@pytest.mark.parametrize("variant", ["F1", "F1A"])
-def test_segmented_long_sampled(variant):
-    """The long-context shape (B1 H16 T65536 d128, bf16, chunk 64) in 16 segments;
-    the oracle checks two sampled heads over the whole sequence."""
+@pytest.mark.parametrize("variant,nseg", [("F1", 8), ("F1A", 8), ("F1", 16)])
+def test_segmented_long_sampled(variant, nseg):
+    """The long-context shape (B1 H16 T65536 d128, bf16, chunk 64) in 8 segments (the
+    benchmark's launch) and 16; the oracle checks two sampled heads over the whole
+    sequence."""
     w = W.WORKLOADS["long_t65536"]
-    got, inp, _ = run_seg(variant, w, 16, 29)
+    got, inp, _ = run_seg(variant, w, nseg, 29)
     for h in (0, 11):
         sub = {n: a[:, :, h:h + 1] for n, a in inp.items()}
         ref = oracle.recurrent(variant, **sub)
