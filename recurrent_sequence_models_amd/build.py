@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfalcon.so")
 
 SOURCES = ["falcon_abi.cpp", "falcon_fwd.hip", "falcon_fwd_pipe.hip", "falcon_fwd_split.hip", "falcon_fwd_split_win.hip",
-           "falcon_fwd3.hip",
+           "falcon_fwd3.hip", "falcon_fwd_band.hip",
            "falcon_step.hip", "falcon_bwd.hip", "falcon_bwd_rows.hip", "falcon_segment.hip", "falcon_static.hip"]
 ARCH = "gfx950"
 FLAGS = [

@@ -5,6 +5,7 @@
 // kernels live in falcon_fwd.hip, falcon_fwd3.hip and falcon_step.hip.
 #include "falcon.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -98,6 +99,9 @@ size_t chunk_fwd_split_workspace_varlen(int variant, bool bf16, int dk, int dv, 
 hipError_t launch_chunk_fwd_split(int variant, bool bf16, int dk, int dv, int chunk, int window, const FwdArgs &a,
                                   void *ws, hipStream_t s);
 int chunk_fwd_onepass_ns(int variant, bool bf16, int dk, int dv, int chunk, int window, int bh);
+bool chunk_fwd_band_supported(int variant, int dk, int dv, int chunk, int window);   // falcon_fwd_band.hip
+size_t chunk_fwd_band_workspace(int bh, int T);
+hipError_t launch_chunk_fwd_band(bool bf16, const FwdArgs &a, void *ws, hipStream_t s);
 hipError_t launch_chunk_fwd_onepass(int variant, bool bf16, int dk, int dv, int chunk, int window, const FwdArgs &a,
                                     hipStream_t s);
 
@@ -142,8 +146,13 @@ size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape) {
   // one image per system of rows (at least one step each) must have an int index
   const int64_t bhs = (int64_t)shape->batch * shape->heads * shape->seqlen;
   if (bhs > INT32_MAX) return 0;
-  return falcon::chunk_fwd_split_workspace(shape->variant, shape->dtype == FALCON_BF16, shape->dk, shape->dv,
-                                           shape->chunk, shape->window, shape->batch * shape->heads, shape->seqlen);
+  const size_t split = falcon::chunk_fwd_split_workspace(shape->variant, shape->dtype == FALCON_BF16, shape->dk,
+                                                        shape->dv, shape->chunk, shape->window,
+                                                        shape->batch * shape->heads, shape->seqlen);
+  // Falcon-3A windows at d = 64, chunk 64 run the banded-weight kernels, which need less
+  if (split && falcon::chunk_fwd_band_supported(shape->variant, shape->dk, shape->dv, shape->chunk, shape->window))
+    return std::max(split, falcon::chunk_fwd_band_workspace(shape->batch * shape->heads, shape->seqlen));
+  return split;
 }
 
 int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, const void *v,
@@ -205,6 +214,8 @@ int falcon_chunk_fwd(const falcon_shape_t *s, const void *q, const void *k, cons
   }
   // same-step pairs run only on the chunk-parallel kernels
   if (!split && s->align != FALCON_ALIGN_PREFIX) return FALCON_ERR_UNSUPPORTED;
+  if (split && falcon::chunk_fwd_band_supported(s->variant, s->dk, s->dv, s->chunk, a.window))
+    return falcon::launch_chunk_fwd_band(bf16, a, workspace, hs) == hipSuccess ? FALCON_OK : FALCON_ERR_HIP;
   if (split) {   // prep over all systems, then the scan workgroups of each sequence
     return falcon::launch_chunk_fwd_split(s->variant, bf16, s->dk, s->dv, s->chunk, a.window, a, workspace, hs) ==
                    hipSuccess

@@ -553,3 +553,30 @@ def test_forward_call_reuse(workspace):
         torch.cuda.synchronize()
         assert torch.equal(o, ro) and torch.equal(cs, rcs)
         assert torch.equal(fin["S"], rfin["S"]) and torch.equal(fin["x_prev"], rfin["x_prev"])
+
+
+# ---- Falcon-3A windows at d = 64, chunk 64: the banded-weight kernels ----------------
+# (band_state / band_scan / band_out; the window's earlier pairs enter each chunk as a
+# halo block, so sequences shorter than the window and chunk edges are the cases.)
+@pytest.mark.parametrize("bw", [2, 4, 8])
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 9, 63, 64, 65, 130])
+@pytest.mark.parametrize("align", ["prefix", "same"])
+def test_band_short_and_ragged(bw, T, align):
+    w = W.WORKLOADS["window_t4096"].replace(batch=1, heads=3, seqlen=T)
+    check("F3A", w, 71, window=bw, init=True, chunk_states=True, align=align)
+
+
+@pytest.mark.parametrize("bw", [2, 4, 8])
+@pytest.mark.parametrize("init", [False, True])
+def test_band_fp32(bw, init):
+    w = TINY.replace(batch=2, heads=2, seqlen=200, dk=64, dv=64, chunk=64)
+    check("F3A", w, 72, window=bw, init=init, chunk_states=True)
+
+
+@pytest.mark.parametrize("bw", [4, 8])
+@pytest.mark.parametrize("gates", ["floor5", "softplus"])
+def test_band_decay_regimes(bw, gates):
+    """Steps at the eps_gamma floor (a window's weights then span e^{-7 |log eps|})
+    and softplus gates, several chunks."""
+    w = W.WORKLOADS["window_t4096"].replace(batch=2, heads=2, seqlen=333, gates=gates)
+    check("F3A", w, 73, window=bw, init=True, chunk_states=True)
