@@ -19,7 +19,8 @@ input set (the warm figure).  Paths
 (--path): "onepass" calls without a workspace (the one-pass kernel where it is
 built, else the fused kernel); "split" passes a workspace (allocated once
 outside the timed region): the prep kernel over all systems, then the state
-scan.  "auto" (default) takes the faster one measured per shape class: split
+scan (for Falcon-3A windows at head dim 64: the banded-weight kernels, the
+chunks' state increments, their scan and the outputs).  "auto" (default) takes the faster one measured per shape class: split
 for Falcon-3 windows and head dim 128, one-pass otherwise, and for long
 sequences too few to fill the device (B*H*dv/16 <= 128 scan workgroups, T >=
 16384, one pair per step) the segment-parallel form with 8 segments.
@@ -421,6 +422,13 @@ DECODE_SOURCES = ("falcon_step.hip", "falcon_kernels.h", "mfma_frag.h")
 BWD_SOURCES = ("falcon_bwd.hip", "falcon_kernels.h", "mfma_frag.h", "lane_ops.h")
 # the segment-parallel forward also runs the boundary and combine kernels
 SEG_SOURCES = KERNEL_SOURCES + ("falcon_segment.hip",)
+# Falcon-3A windows at d = 64, chunk 64: the banded-weight kernels
+BAND_SOURCES = ("falcon_fwd_band.hip", "chunk_common.h", "mfma_frag.h", "falcon_kernels.h")
+
+
+def band_path(w, variant, window, path):
+    """True where the two-kernel request runs the banded-weight kernels."""
+    return path == "split" and variant == "F3A" and window > 1 and w.dk == 64 and w.dv == 64 and w.chunk == 64
 
 
 def measured_traffic(key, sources=KERNEL_SOURCES):
@@ -618,11 +626,13 @@ def main():
         roof = {"bound": "mfma", "achieved": round(mfma_tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4)}
     key = f"{path} {variant} {w.name}" + (f" w{window}" if window > 1 else "")
-    sources = SEG_SOURCES if path.startswith("segmented") else KERNEL_SOURCES
+    band = band_path(w, variant, window, path)
+    sources = SEG_SOURCES if path.startswith("segmented") else BAND_SOURCES if band else KERNEL_SOURCES
     roof["traffic"] = measured_traffic(key, sources)
     roof["measured_busy"] = measured_busy(key, sources)
     roof["kernel"] = ("seg_boundary + chunk_prep + 2 x chunk_scan (map form) + seg_combine + chunk_scan"
                       if path.startswith("segmented") else
+                      "band_state + band_scan + band_out" if band else
                       "chunk_prep + chunk_scan" if path == "split" else
                       "chunk_scan (one-pass)" if (w.dtype == "bf16" and w.dk <= 64 and w.chunk <= 64) else
                       "chunk_fwd_pipe" if w.dk <= 64 else "chunk_fwd_rows")

@@ -106,8 +106,7 @@ __device__ inline void unpack16(const Raw16<IT> &r, float *o) {
 template <typename IT>
 struct alignas(16) BandTile {
   static constexpr int LD = band_ld<IT>();
-  IT X[BNR * LD];      // keys of pairs j = row - 16
-  IT V[BNR * LD];      // values of the same pairs (band_state: scaled by omega(63, j))
+  IT X[BNR * LD];      // keys of pairs j = row - 16 (band_out: then their values)
   float L[BC];         // cumulative clamped log-decay
   float lam[BC];       // lambda_s
   float eta[BC];       // eta_s (already divided by the window)
@@ -221,6 +220,7 @@ template <typename IT>
 __global__ __launch_bounds__(BNT) void band_state(FwdArgs a, BandWs ws) {
   constexpr int LD = BandTile<IT>::LD;
   __shared__ BandTile<IT> s;
+  __shared__ alignas(16) IT Vs[BNR * LD];   // values scaled by omega(63, j)
   const int nc = a.nchunks, seq = blockIdx.x / nc, c = blockIdx.x % nc;
   const int b = seq / a.H, h = seq % a.H, Hw = a.window - 1;
   const int t0 = c * BC, n = min(BC, a.T - t0);
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(BNT) void band_state(FwdArgs a, BandWs ws) {
     const float om = s.w[r];
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[j] *= om;
-    store16(s.V + r * LD + 16 * (tid & 3), x);
+    store16(Vs + r * LD + 16 * (tid & 3), x);
   }
   __syncthreads();
 
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(BNT) void band_state(FwdArgs a, BandWs ws) {
   f4 u[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
   for (int q = 0; q < BNR / 16; ++q) {
-    const auto bv = ldT(s.V, LD, 16 * q, [&](int i) { return 16 * w + 4 * i; }, lane);
+    const auto bv = ldT(Vs, LD, 16 * q, [&](int i) { return 16 * w + 4 * i; }, lane);
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) mma16(u[bb], ldT(s.X, LD, 16 * q, [&](int i) { return 16 * bb + 4 * i; }, lane), bv);
   }
@@ -371,14 +371,6 @@ __global__ __launch_bounds__(BNT) void band_out(FwdArgs a, BandWs ws) {
   ChunkFetch<IT> f;
   fetch_chunk<IT, true>(f, a, b, h, t0, n);
   keys_to_lds<IT>(s, f, a, t0, n, Hw, cy + CX, cy + CWX);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (tid >> 2) + 64 * i;
-    if (r >= BNR) break;   // wave-uniform
-    float x[16];
-    value_row<IT>(f, i, a, t0 + r - BHALO, Hw, cy + CWV, x);
-    store16(s.V + r * LD + 16 * qd, x);
-  }
   {
     const int r = tid >> 2;   // query rows: one per group of four lanes
     float x[16];
@@ -416,10 +408,20 @@ __global__ __launch_bounds__(BNT) void band_out(FwdArgs a, BandWs ws) {
     Wt[k * 64 + lane] = cvt<IT>(wt);
   }
   __syncthreads();
+  // the keys are no longer needed: the values take their place
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (tid >> 2) + 64 * i;
+    if (r >= BNR) break;   // wave-uniform
+    float x[16];
+    value_row<IT>(f, i, a, t0 + r - BHALO, Hw, cy + CWV, x);
+    store16(s.X + r * LD + 16 * qd, x);
+  }
+  __syncthreads();
 
   Frag vf[5];   // V^T blocks (channels 16w.., pair block q)
 #pragma unroll
-  for (int q = 0; q < 5; ++q) vf[q] = ldT(s.V, LD, 16 * q, [&](int i) { return 16 * w + 4 * i; }, lane);
+  for (int q = 0; q < 5; ++q) vf[q] = ldT(s.X, LD, 16 * q, [&](int i) { return 16 * w + 4 * i; }, lane);
   Frag sh[4], sl[4];   // S_c rows; bf16: high and low parts, about 16 bits of S in the product
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
