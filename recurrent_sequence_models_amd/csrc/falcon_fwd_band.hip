@@ -259,11 +259,15 @@ __global__ __launch_bounds__(BNT) void band_state(FwdArgs a, BandWs ws) {
   // wave w: U^T tiles of value channels 16w.. (so a lane holds four consecutive
   // key channels of one row of U), all four key-channel blocks
   f4 u[4] = {zero4(), zero4(), zero4(), zero4()};
+  typename Op<IT>::frag bv[5];
 #pragma unroll
-  for (int q = 0; q < BNR / 16; ++q) {
-    const auto bv = ldT(Vs, LD, 16 * q, [&](int i) { return 16 * w + 4 * i; }, lane);
+  for (int q = 0; q < BNR / 16; ++q) bv[q] = ldT(Vs, LD, 16 * q, [&](int i) { return 16 * w + 4 * i; }, lane);
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) mma16(u[bb], ldT(s.X, LD, 16 * q, [&](int i) { return 16 * bb + 4 * i; }, lane), bv);
+  for (int bb = 0; bb < 4; ++bb) {
+    auto xa = [&](int q) { return ldT(s.X, LD, 16 * q, [&](int i) { return 16 * bb + 4 * i; }, lane); };
+    mma32(u[bb], xa(0), xa(1), bv[0], bv[1]);
+    mma32(u[bb], xa(2), xa(3), bv[2], bv[3]);
+    mma16(u[bb], xa(4), bv[4]);
   }
   float *U = ws.U + ((size_t)seq * nc + c) * BD * BD + (16 * w + cc) * BD + 4 * g;
 #pragma unroll
@@ -391,9 +395,9 @@ __global__ __launch_bounds__(BNT) void band_out(FwdArgs a, BandWs ws) {
   for (int k = w; k < NTILE; k += 4) {   // wave-uniform
     const int p = tile_p(k), q = k - p * (p + 3) / 2, st = 16 * p + cc;
     f4 sc = zero4();   // <x_j, q_s> at j = 16q - 16 + 4g + i, s = st
+    const IT *xr = s.X + (16 * q + cc) * LD + 4 * g, *qr = Q + st * LD + 4 * g;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      mma16(sc, ld4(s.X + (16 * q + cc) * LD + 16 * kb + 4 * g), ld4(Q + st * LD + 16 * kb + 4 * g));
+    for (int kb = 0; kb < 4; kb += 2) mma32(sc, ld4(xr + 16 * kb), ld4(xr + 16 * kb + 16), ld4(qr + 16 * kb), ld4(qr + 16 * kb + 16));
     f4 wt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -413,9 +417,16 @@ __global__ __launch_bounds__(BNT) void band_out(FwdArgs a, BandWs ws) {
   for (int i = 0; i < 2; ++i) {
     const int r = (tid >> 2) + 64 * i;
     if (r >= BNR) break;   // wave-uniform
-    float x[16];
-    value_row<IT>(f, i, a, t0 + r - BHALO, Hw, cy + CWV, x);
-    store16(s.X + r * LD + 16 * qd, x);
+    const int t = t0 + r - BHALO;
+    if (t >= 0 && t < a.T) {   // input rows go in as they are
+#pragma unroll
+      for (int j = 0; j < (int)(sizeof(IT) * 16 / 16); ++j)
+        reinterpret_cast<uint4 *>(s.X + r * LD + 16 * qd)[j] = f.v[i].u[j];
+    } else {
+      float x[16];
+      value_row<IT>(f, i, a, t, Hw, cy + CWV, x);
+      store16(s.X + r * LD + 16 * qd, x);
+    }
   }
   __syncthreads();
 
@@ -432,14 +443,18 @@ __global__ __launch_bounds__(BNT) void band_out(FwdArgs a, BandWs ws) {
   for (int p = 0; p < 4; ++p) {
     const int st = 16 * p + cc;
     f4 o = zero4();
+    const Frag *wp = Wt + (p * (p + 3) / 2) * 64 + lane;
 #pragma unroll
-    for (int q = 0; q <= p + 1; ++q) mma16(o, vf[q], Wt[(p * (p + 3) / 2 + q) * 64 + lane]);
+    for (int q = 0; q + 1 <= p + 1; q += 2) mma32(o, vf[q], vf[q + 1], wp[64 * q], wp[64 * q + 64]);
+    if (p % 2 == 1) mma16(o, vf[p + 1], wp[64 * (p + 1)]);   // odd count p + 2 of pair blocks: the last one
     f4 in = zero4();
+    Frag qf[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const Frag qf = ld4(Q + st * LD + 16 * kb + 4 * g);
-      mma16(in, sh[kb], qf);
-      if constexpr (std::is_same_v<IT, __bf16>) mma16(in, sl[kb], qf);
+    for (int kb = 0; kb < 4; ++kb) qf[kb] = ld4(Q + st * LD + 16 * kb + 4 * g);
+#pragma unroll
+    for (int kb = 0; kb < 4; kb += 2) {
+      mma32(in, sh[kb], sh[kb + 1], qf[kb], qf[kb + 1]);
+      if constexpr (std::is_same_v<IT, __bf16>) mma32(in, sl[kb], sl[kb + 1], qf[kb], qf[kb + 1]);
     }
     if (st < n) {
       o += __expf(s.L[st]) * in;
