@@ -146,6 +146,11 @@ const char *falcon_status_string(int status);
  * incoming x_prev and window; its contents are scratch and need no
  * initialisation.  The path covers F1/F1A/F2/F2A (chunk 16, 32, 64) and
  * F3/F3A with Bw = 2, 4, 8 at chunk 64; d = 32, 64 (fp32, bf16), 128 (bf16).
+ * F3A with Bw = 2, 4, 8 at d = 64, chunk 64 uses the same workspace for its
+ * banded-weight form (additive windows as decayed score weights, the Falcon
+ * paper's windowed variant): each chunk's state increment, then the state
+ * entering it, 16 KiB per chunk and sequence, plus the carried-state copy; the
+ * returned size covers both.
  * Returns 0 for an invalid shape as well; validation is the forward call's job. */
 size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape);
 
