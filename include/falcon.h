@@ -147,8 +147,8 @@ const char *falcon_status_string(int status);
  * initialisation.  The path covers F1/F1A/F2/F2A (chunk 16, 32, 64) and
  * F3/F3A with Bw = 2, 4, 8 at chunk 64; d = 32, 64 (fp32, bf16), 128 (bf16).
  * F3A with Bw = 2, 4, 8 at d = 64, chunk 64 uses the same workspace for its
- * banded-weight form (additive windows as decayed score weights, the Falcon
- * paper's windowed variant): each chunk's state increment, then the state
+ * banded-weight form (the window-averaged additive write of [P1] Falcon家族
+ * as decayed score weights): each chunk's state increment, then the state
  * entering it, 16 KiB per chunk and sequence, plus the carried-state copy; the
  * returned size covers both.
  * Returns 0 for an invalid shape as well; validation is the forward call's job. */

@@ -1,6 +1,7 @@
 // Falcon-3A with a window of 2, 4 or 8 pairs, head dim 64, chunks of 64 steps:
-// the banded-weight chunk form (Falcon paper, the windowed variant of the
-// additive update and its chunkwise-parallel form).
+// the banded-weight chunk form.  The window-averaged additive write is [P1]
+// Falcon家族 (window average); the chunked form it rearranges is [P1] 三种等价形式
+// (form C).
 //
 // Falcon-3A never reads S in its write, so each step adds a fixed rank-B_w term
 // and S is a decayed sum of them.  Inside a chunk, with L_s the cumulative
