@@ -60,6 +60,9 @@ CASES = [
      W.WORKLOADS["layer130m"].replace(batch=1, heads=2, seqlen=77, dk=128, dv=128)),
     ("F3", 4, W.WORKLOADS["window_t4096"].replace(batch=2, heads=12, seqlen=2048),
      W.WORKLOADS["window_t4096"].replace(batch=1, heads=3, seqlen=150, dk=32, dv=32, dtype="fp32")),
+    # the banded Falcon-3A kernels (d = 64, chunk 64) in the library's scratch, twice
+    ("F3A", 8, W.WORKLOADS["window_t4096"].replace(batch=2, heads=12, seqlen=2048),
+     W.WORKLOADS["window_t4096"].replace(batch=1, heads=3, seqlen=150)),
 ]
 
 
