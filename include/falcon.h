@@ -146,7 +146,7 @@ const char *falcon_status_string(int status);
  * incoming x_prev and window; its contents are scratch and need no
  * initialisation.  The path covers F1/F1A/F2/F2A (chunk 16, 32, 64) and
  * F3/F3A with Bw = 2, 4, 8 at chunk 64; d = 32, 64 (fp32, bf16), 128 (bf16).
- * F3A with Bw = 2, 4, 8 at d = 64, chunk 64 uses the same workspace for its
+ * F3A with Bw = 2, 4, 8 at d = 64, chunk 64 (fp32 and bf16 inputs) uses a workspace for its
  * banded-weight form (the window-averaged additive write of [P1] Falcon家族
  * as decayed score weights): each chunk's state increment, then the state
  * entering it, 16 KiB per chunk and sequence, plus the carried-state copy; the

@@ -149,8 +149,9 @@ size_t falcon_chunk_fwd_workspace(const falcon_shape_t *shape) {
   const size_t split = falcon::chunk_fwd_split_workspace(shape->variant, shape->dtype == FALCON_BF16, shape->dk,
                                                         shape->dv, shape->chunk, shape->window,
                                                         shape->batch * shape->heads, shape->seqlen);
-  // Falcon-3A windows at d = 64, chunk 64 run the banded-weight kernels, which need less
-  if (split && falcon::chunk_fwd_band_supported(shape->variant, shape->dk, shape->dv, shape->chunk, shape->window))
+  // Falcon-3A windows at d = 64, chunk 64 run the banded-weight kernels (fp32 and bf16 inputs); the
+  // size covers both paths
+  if (falcon::chunk_fwd_band_supported(shape->variant, shape->dk, shape->dv, shape->chunk, shape->window))
     return std::max(split, falcon::chunk_fwd_band_workspace(shape->batch * shape->heads, shape->seqlen));
   return split;
 }

@@ -113,7 +113,7 @@ def test_deep_decay_rows(variant, dtype, d, chunk, workspace, eps_gamma):
 @pytest.mark.parametrize("variant", ("F3", "F3A"))
 @pytest.mark.parametrize("bw", (2, 4, 8))
 @pytest.mark.parametrize("dtype,d,workspace", [("bf16", 64, False), ("bf16", 64, True), ("bf16", 128, True),
-                                               ("fp32", 32, True), ("fp32", 64, False)])
+                                               ("fp32", 32, True), ("fp32", 64, False), ("fp32", 64, True)])
 def test_deep_decay_windows(variant, bw, dtype, d, workspace):
     w = W.WORKLOADS["window_t4096"].replace(batch=1, heads=2, seqlen=200, dk=d, dv=d, dtype=dtype)
     inp = deep_decay_inputs(w, variant, 112, window=bw)
